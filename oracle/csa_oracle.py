@@ -1,0 +1,350 @@
+"""CPU oracle for one compressed-sparse-attention (CSA) layer step.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference that the
+HIP path is checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it; the library and its
+Python binding never do.  It shares no code, header, table or helper with the
+HIP sources.
+
+Arithmetic is float64 NumPy, row by row, in the order the pages state it.
+Integer dot products of the indexer are formed with a float64 matrix product
+of INT8-valued operands, which is exact: every partial sum is an integer of
+magnitude at most 128 * 127 * 127 < 2**53.
+
+Sources (the pages are cited by title and section):
+
+* [V41]  pypto-lib "DeepSeek V4.1 Flash" -- sections "Serving-owned full RoPE
+  tables", "Compressor state ownership" (metadata contract, index checks
+  before table indexing), "Decode composition" (Top-K checks, -1 padding).
+* [HP]   gitcode hyper-parallel issue #2, "Hyper-Parallel 支持 MindFormers
+  DeepSeek V4 CP 并行方案" -- Stage-2 operator calls (sinks, softmax scale,
+  ori_win_left=127 / ori_win_right=0), section 7.1 (window example), 8.2
+  (causal compressed visibility, worked example p=300), 9.1 (kv_full is the
+  window KV followed by the compressed KV; indices are the union), 10.2
+  (indexer indices are compressed slot ids), 10.3 (causal mask).
+* [MTP]  pypto-lib "DeepSeek V4-Flash, MTP point" -- section "What is
+  quantized" (INT8 index-key cache with an FP32 per-row scale; BF16 KV;
+  FP32 attn_sink).
+* [ATOM] ROCm ATOM "DeepSeek-V4.1 native paged runtime" -- section "Current
+  execution scope" (per-row bounds, 128-token PAGE, padding sentinels).
+
+Readings where the pages are silent (listed with reasons in the design notes):
+
+* the score is sum_h w[t,h] * relu(qs[t,h] * ks[c] * <q8[t,h], k8[c]>): ReLU on
+  each dequantised head dot, weights after the ReLU, no extra 1/sqrt scaling;
+* top-k ties break toward the lower position; the output is ascending by
+  position, padded with -1 (value -inf) when fewer than k positions are visible;
+* the window of a query at position p is raw positions [max(0, p-W+1), p];
+  window rows and selected compressed rows are concatenated with no dedup;
+* the sink is one unscaled logit per head in the softmax denominator with no
+  value row; lse includes it; an empty key set gives out = 0, lse = sink;
+* only the query is rotated (adjacent pairs (2i, 2i+1) of channels
+  [rope_offset, rope_offset + rope_dim) by rope row t); cached rows are used as
+  stored.
+
+Device-error flags mirror the library's documented bit values (restated here,
+not shared): rows that violate the metadata contract are handled as listed in
+each function.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 128
+
+EFLAG_POS_RANGE = 1     # position past a table / a row's visible span past its storage
+EFLAG_BLOCK_RANGE = 2   # block id outside the pool (or page outside the table)
+EFLAG_TOPK_RANGE = 4    # selected index not visible to the row
+EFLAG_META = 8          # active row that no request owns
+
+
+# ----------------------------------------------------------------------------
+# small exact helpers
+# ----------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of BF16 bit patterns: the top 16 bits of an IEEE float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def visible_count(pos: int, ratio: int) -> int:
+    """Compressed slots a query at absolute position ``pos`` may see.
+
+    [HP] 8.2 / 10.3: slot c is visible to position p iff c < (p + 1) // ratio
+    (worked example: p = 300, ratio = 128 sees slots 0 and 1, not 2).
+    A negative position sees nothing."""
+    return max(0, (int(pos) + 1) // int(ratio))
+
+
+def window_positions(pos: int, window: int) -> range:
+    """Raw positions in the sliding window of a query at ``pos``:
+    [max(0, p - W + 1), p] -- ori_win_left = W - 1 tokens to the left, none to
+    the right ([HP] Stage-2 calls; worked example in section 7.1: with W = 4,
+    token 4 sees tokens 1..4)."""
+    p = int(pos)
+    if p < 0:
+        return range(0)
+    return range(max(0, p - window + 1), p + 1)
+
+
+def owner_request(t: int, query_start_loc: np.ndarray) -> int:
+    """Request b with query_start_loc[b] <= t < query_start_loc[b+1]; -1 if none.
+    [V41] "Compressor state ownership": packed, nondecreasing query starts;
+    equal neighbours are an empty request."""
+    qsl = np.asarray(query_start_loc)
+    for b in range(len(qsl) - 1):
+        if qsl[b] <= t < qsl[b + 1]:
+            return b
+    return -1
+
+
+def rotate_adjacent_pairs(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotate channel pairs (2i, 2i+1) of ``x`` by the angle whose cosine and
+    sine are cos[i], sin[i] (multiplication by e^{i theta} with x[2i] the real
+    part).  [V41] "Serving-owned full RoPE tables": FP32 half-width tables are
+    kept for adjacent-pair rotation."""
+    x = np.asarray(x, dtype=np.float64)
+    c = np.asarray(cos, dtype=np.float64)
+    s = np.asarray(sin, dtype=np.float64)
+    re = x[..., 0::2]
+    im = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = re * c - im * s
+    out[..., 1::2] = re * s + im * c
+    return out
+
+
+# ----------------------------------------------------------------------------
+# a1: RoPE rows
+# ----------------------------------------------------------------------------
+
+def materialize_rope_rows(freqs_cos, freqs_sin, position_ids, num_tokens,
+                          rope_cos, rope_sin) -> int:
+    """[V41] "Serving-owned full RoPE tables": for each active row t < num_tokens
+    copy row position_ids[t] of the FP32 half-width tables; a negative position
+    writes the identity rotation (cos 1, sin +0); rows >= num_tokens are left
+    untouched.  A nonnegative position at or past the table capacity is a
+    contract violation: the row is left untouched and POS_RANGE is flagged.
+
+    Writes ``rope_cos`` / ``rope_sin`` (float32 [T, R/2]) in place; returns the
+    error flags."""
+    cap = freqs_cos.shape[0]
+    err = 0
+    for t in range(int(num_tokens)):
+        p = int(position_ids[t])
+        if p < 0:
+            rope_cos[t, :] = np.float32(1.0)
+            rope_sin[t, :] = np.float32(0.0)
+        elif p < cap:
+            rope_cos[t, :] = freqs_cos[p, :]
+            rope_sin[t, :] = freqs_sin[p, :]
+        else:
+            err |= EFLAG_POS_RANGE
+    return err
+
+
+# ----------------------------------------------------------------------------
+# a2 + a4: lightning-indexer scores
+# ----------------------------------------------------------------------------
+
+def _physical_rows(block_table_row, num_blocks, positions):
+    """Translate request-local positions to flat pool rows through a 128-token
+    block table ([V41] cache ABI; [ATOM] "Current execution scope").  Returns
+    (rows, ok) where ok marks positions whose page and block id are valid."""
+    positions = np.asarray(positions, dtype=np.int64)
+    page = positions // PAGE
+    in_table = page < len(block_table_row)
+    blk = np.full(positions.shape, -1, dtype=np.int64)
+    blk[in_table] = np.asarray(block_table_row, dtype=np.int64)[page[in_table]]
+    ok = in_table & (blk >= 0) & (blk < num_blocks)
+    rows = np.where(ok, blk * PAGE + positions % PAGE, 0)
+    return rows, ok
+
+
+def index_scores(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table,
+                 query_start_loc, positions, num_tokens, ratio, score_stride,
+                 key_chunk: int = 1 << 16):
+    """Lightning-indexer score of every causally visible compressed position.
+
+    For active row t of request b at position p, and c < (p + 1) // ratio:
+
+        score[t, c] = sum_h w[t,h] * relu( qs[t,h] * ks[c] * <q8[t,h,:], k8[c,:]> )
+
+    with k8 / ks the INT8 key row and FP32 scale of compressed position c,
+    found through the request's block table ([MTP] "What is quantized": INT8
+    index keys with an FP32 per-row scale; [HP] 10.2: scores over compressed
+    slot ids; 10.3: causal mask).  Positions c >= (p + 1) // ratio score -inf.
+
+    Contract checks (flags; never an out-of-range read):
+      * a row no request owns: META, the whole row is -inf;
+      * visible span larger than score_stride or than the block table covers:
+        POS_RANGE, the span is cut to what fits;
+      * a visible position whose page holds an invalid block id: BLOCK_RANGE,
+        that position scores -inf.
+
+    Returns (scores float64 [num_tokens, score_stride], err)."""
+    qsl = np.asarray(query_start_loc)
+    num_blocks = idx_kv.shape[0]
+    Di = idx_kv.shape[2]
+    keys_flat = idx_kv.reshape(num_blocks * PAGE, Di)
+    scales_flat = np.asarray(idx_scale, dtype=np.float64).reshape(-1)
+    scores = np.full((int(num_tokens), int(score_stride)), -np.inf, dtype=np.float64)
+    err = 0
+    max_blocks = block_table.shape[1]
+    for t in range(int(num_tokens)):
+        b = owner_request(t, qsl)
+        if b < 0:
+            err |= EFLAG_META
+            continue
+        n = visible_count(positions[t], ratio)
+        if n > score_stride or n > PAGE * max_blocks:
+            err |= EFLAG_POS_RANGE
+            n = min(n, int(score_stride), PAGE * max_blocks)
+        q = np.asarray(q_idx[t], dtype=np.float64)          # [Hi, Di], integer valued
+        qs = np.asarray(q_scale[t], dtype=np.float64)        # [Hi]
+        w = np.asarray(head_w[t], dtype=np.float64)          # [Hi]
+        for c0 in range(0, n, key_chunk):
+            cs = np.arange(c0, min(n, c0 + key_chunk))
+            rows, ok = _physical_rows(block_table[b], num_blocks, cs)
+            if not ok.all():
+                err |= EFLAG_BLOCK_RANGE
+            k8 = keys_flat[rows].astype(np.float64)         # [n_c, Di]
+            ks = scales_flat[rows]                           # [n_c]
+            dots = q @ k8.T                                  # [Hi, n_c], exact integers
+            per_head = qs[:, None] * ks[None, :] * dots
+            s = (w[:, None] * np.maximum(per_head, 0.0)).sum(axis=0)
+            s[~ok] = -np.inf
+            scores[t, cs] = s
+    return scores, err
+
+
+# ----------------------------------------------------------------------------
+# a3: top-k
+# ----------------------------------------------------------------------------
+
+def topk(scores, positions, ratio, num_tokens, k):
+    """Per active row, the k best visible positions.
+
+    The visible span of row t is n = (p + 1) // ratio ([HP] 10.3), cut to the
+    score row width (flag POS_RANGE if cut); the width of the selection is
+    m = min(k, n) ([HP] 7.4: top-k width capped by the key length).  Order:
+    score descending, ties toward the lower position, NaN below everything.
+    Output ([V41] "Decode composition": eligibility, uniqueness, logical
+    position order, trailing -1): the m chosen positions ascending, then -1 up
+    to k; values are the chosen scores, -inf for padding.
+
+    Returns (idx int32 [num_tokens, k], val float64 [num_tokens, k], err)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    nt = int(num_tokens)
+    idx = np.full((nt, int(k)), -1, dtype=np.int32)
+    val = np.full((nt, int(k)), -np.inf, dtype=np.float64)
+    err = 0
+    width = scores.shape[1]
+    for t in range(nt):
+        n = visible_count(positions[t], ratio)
+        if n > width:
+            err |= EFLAG_POS_RANGE
+            n = width
+        m = min(int(k), n)
+        if m == 0:
+            continue
+        s = scores[t, :n]
+        nan = np.isnan(s)
+        primary = np.where(nan, np.inf, -s)          # ascending sort = descending score
+        order = np.lexsort((np.arange(n), nan, primary))
+        chosen = np.sort(order[:m])
+        idx[t, :m] = chosen
+        val[t, :m] = s[chosen]
+    return idx, val, err
+
+
+# ----------------------------------------------------------------------------
+# a5 + a6/a7: shared-KV sparse attention with sink
+# ----------------------------------------------------------------------------
+
+def kv_rows_for_query(t, b, p, topk_row, ratio, window, cmp_block_table, num_cmp_blocks,
+                      win_block_table, num_win_blocks):
+    """The key/value rows of one query, window first then selected compressed
+    rows, as (pool, flat_row) pairs -- [HP] 9.1: kv_full = [window KV,
+    compressed KV], topk_idxs = [window_idxs, compressed_idxs]; the two caches
+    are separate, so nothing is deduplicated.  Returns (win_rows, cmp_rows, err)."""
+    err = 0
+    wpos = np.asarray(list(window_positions(p, window)), dtype=np.int64)
+    wrows, wok = _physical_rows(win_block_table[b], num_win_blocks, wpos)
+    if not wok.all():
+        err |= EFLAG_BLOCK_RANGE
+    n = visible_count(p, ratio)
+    sel = np.asarray([int(c) for c in topk_row if int(c) >= 0], dtype=np.int64)
+    if np.any(sel >= n):
+        err |= EFLAG_TOPK_RANGE
+    sel = sel[sel < n]
+    crows, cok = _physical_rows(cmp_block_table[b], num_cmp_blocks, sel)
+    if not cok.all():
+        err |= EFLAG_BLOCK_RANGE
+    return wrows[wok], crows[cok], err
+
+
+def sparse_attn(q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table,
+                topk_idx, ratio, win_kv, win_block_table, window, attn_sink,
+                softmax_scale, query_start_loc, positions, num_tokens):
+    """Shared-KV multi-head attention over the window rows and the selected
+    compressed rows, with one sink logit per head.
+
+    [HP] Stage-2 call (sinks = attn_sink, softmax_scale, ori_win_left = 127,
+    ori_win_right = 0) and 9.1 (union of window and compressed rows); all
+    heads share one KV row, which serves as both key and value ([MTP]: one
+    BF16 KV cache per layer).  For each head h of active row t:
+
+        q      = BF16 query with channels [off, off + R) rotated by rope row t
+        l_j    = softmax_scale * <q, K_j>          for each row j of the set
+        M      = max(sink_h, max_j l_j)
+        Z      = exp(sink_h - M) + sum_j exp(l_j - M)
+        out    = sum_j exp(l_j - M) / Z * K_j
+        lse    = M + log Z
+
+    Contract checks: an active row that no request owns flags META and is
+    treated as having no keys; window pages with invalid block ids, and
+    selected entries that are not visible (TOPK_RANGE) or sit on invalid
+    pages (BLOCK_RANGE), are flagged and left out; negative selected entries
+    are padding.
+
+    Returns (out float64 [num_tokens, H, D], lse float64 [num_tokens, H], err)."""
+    nt = int(num_tokens)
+    T, H, D = q.shape
+    half = rope_cos.shape[1]
+    qsl = np.asarray(query_start_loc)
+    ncb = cmp_kv.shape[0]
+    nwb = win_kv.shape[0]
+    cmp_flat = cmp_kv.reshape(ncb * PAGE, D)
+    win_flat = win_kv.reshape(nwb * PAGE, D)
+    sink = np.asarray(attn_sink, dtype=np.float64)
+    out = np.zeros((nt, H, D), dtype=np.float64)
+    lse = np.zeros((nt, H), dtype=np.float64)
+    err = 0
+    for t in range(nt):
+        b = owner_request(t, qsl)
+        if b < 0:
+            err |= EFLAG_META
+            out[t] = 0.0
+            lse[t] = sink
+            continue
+        p = int(positions[t])
+        wrows, crows, e = kv_rows_for_query(t, b, p, topk_idx[t], ratio, window,
+                                            cmp_block_table, ncb, win_block_table, nwb)
+        err |= e
+        kv = np.concatenate([bf16_to_f64(win_flat[wrows]), bf16_to_f64(cmp_flat[crows])], axis=0)
+        qt = bf16_to_f64(q[t])                                          # [H, D]
+        qt[:, rope_offset:rope_offset + 2 * half] = rotate_adjacent_pairs(
+            qt[:, rope_offset:rope_offset + 2 * half], rope_cos[t], rope_sin[t])
+        if kv.shape[0] == 0:
+            out[t] = 0.0
+            lse[t] = sink
+            continue
+        logits = softmax_scale * (qt @ kv.T)                            # [H, n]
+        m = np.maximum(sink, logits.max(axis=1))                        # [H]
+        e_kv = np.exp(logits - m[:, None])
+        z = np.exp(sink - m) + e_kv.sum(axis=1)
+        out[t] = (e_kv / z[:, None]) @ kv
+        lse[t] = m + np.log(z)
+    return out, lse, err

@@ -1,0 +1,136 @@
+"""Workload shapes for one compressed-sparse-attention (CSA) layer step.
+
+Each config is a synthetic stand-in for a V4/V4.1-Flash attention layer as the
+pages describe it (pypto-lib "DeepSeek V4.1 Flash", checkpoint-shape table: 64
+heads of width 512, maximum position 1,048,576; pypto-lib "DeepSeek V4-Flash,
+MTP point", deployment table: 4 requests x S=2 decode rows per card, prefill up
+to 8,192 tokens walked in 128-token tiles).  No dataset is involved.
+
+This module holds shapes only; no arithmetic of the method lives here.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Tuple
+
+PAGE = 128  # tokens per cache block (the pages' 128-token scheduler block)
+
+
+@dataclasses.dataclass(frozen=True)
+class CsaConfig:
+    name: str
+    description: str
+    # query side
+    rows_per_request: Tuple[int, ...]   # decode/prefill rows of each request
+    positions: Tuple[Tuple[int, ...], ...]  # causal position of every row, per request
+    rope_neg_rows: Tuple[int, ...] = ()  # row offsets (within each request) whose rope position is -1
+    H: int = 64
+    D: int = 512
+    R: int = 64                 # rope_dim (rotated channels, adjacent pairs)
+    Hi: int = 64                # indexer heads
+    Di: int = 128               # indexer head dim
+    W: int = 128                # sliding window
+    ratio: int = 2
+    k: int = 512
+    context: int = 32768        # raw tokens per request already in the caches
+    rope_capacity: int = 1 << 20
+    theta: float = 10000.0
+    outlier_frac: float = 0.0   # fraction of compressed positions whose key scale is x4
+    shared_pool: bool = False   # all requests page into one pool (C5)
+
+    # ---- derived sizes -------------------------------------------------
+    @property
+    def B(self) -> int:
+        return len(self.rows_per_request)
+
+    @property
+    def T(self) -> int:
+        return int(sum(self.rows_per_request))
+
+    @property
+    def query_start_loc(self) -> List[int]:
+        out = [0]
+        for r in self.rows_per_request:
+            out.append(out[-1] + r)
+        return out
+
+    @property
+    def flat_positions(self) -> List[int]:
+        return [p for req in self.positions for p in req]
+
+    @property
+    def n_cmp_per_request(self) -> int:
+        """Compressed rows each request holds: context // ratio."""
+        return self.context // self.ratio
+
+    @property
+    def cmp_pages_per_request(self) -> int:
+        return -(-self.n_cmp_per_request // PAGE)
+
+    @property
+    def win_pages_per_request(self) -> int:
+        return -(-self.context // PAGE)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def rope_offset(self) -> int:
+        return self.D - self.R
+
+    @property
+    def score_stride(self) -> int:
+        return self.cmp_pages_per_request * PAGE
+
+
+def _decode(name, desc, n_req, s, context, **kw) -> CsaConfig:
+    pos = tuple(tuple(range(context - s, context)) for _ in range(n_req))
+    return CsaConfig(name=name, description=desc, rows_per_request=(s,) * n_req,
+                     positions=pos, context=context, **kw)
+
+
+C1 = _decode(
+    "c1_tiny_decode",
+    "tiny decode: 2 rows, 8 heads x 64, rope 16, 512 raw tokens at ratio 2 -> 256 "
+    "compressed rows, window 16, indexer 4x32, top-k 32, positions 510/511",
+    n_req=1, s=2, context=512, H=8, D=64, R=16, Hi=4, Di=32, W=16, ratio=2, k=32,
+    rope_capacity=1024)
+
+C2 = _decode(
+    "c2_ratio2_decode",
+    "V4.1 ratio-2 decode: 8 rows (4 requests x S=2), 64x512 heads, 32,768 tokens "
+    "-> 16,384 compressed rows per request, window 128, indexer 64x128, top-k 512",
+    n_req=4, s=2, context=32768, ratio=2, k=512)
+
+C3 = _decode(
+    "c3_ratio1_decode",
+    "V4.1 ratio-1 decode: 8 rows (4 x 2), 131,072 compressed rows per request, "
+    "window 128, indexer 64x128, top-k 2048, first row of each request at rope "
+    "position -1",
+    n_req=4, s=2, context=131072, ratio=1, k=2048, rope_neg_rows=(0,))
+
+C4 = CsaConfig(
+    name="c4_ratio2_prefill",
+    description="V4.1 ratio-2 prefill: 1 request, 8,192 causal queries at positions "
+                "0..8191, 4,096 compressed rows, window 128, indexer 64x128, top-k 512",
+    rows_per_request=(8192,), positions=(tuple(range(8192)),), context=8192,
+    ratio=2, k=512)
+
+C5 = _decode(
+    "c5_maxctx_ratio1_decode",
+    "max-context ratio-1 decode: 8 rows (2 requests x 4), 1,048,576 positions per "
+    "request in 8,192 pages of one shared pool, window 128, top-k 2048, 5% of "
+    "positions carry x4 key scales",
+    n_req=2, s=4, context=1 << 20, ratio=1, k=2048, outlier_frac=0.05,
+    shared_pool=True)
+
+CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5)}
+SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+
+
+def get(name: str) -> CsaConfig:
+    if name in SHORT:
+        return SHORT[name]
+    return CONFIGS[name]
