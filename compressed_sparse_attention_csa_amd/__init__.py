@@ -1,0 +1,15 @@
+"""MI355X-native compressed-sparse-attention (CSA) layer step.
+
+The hot path lives in libcsa.so (hand-written HIP for gfx950 behind the C ABI
+declared in include/csa.h).  This package is its thin binding: ``_lib`` has one
+function per C entry point, ``runner.CsaStep`` holds device buffers for a
+whole step.  There is no CPU fallback: without the built library every call
+raises.
+"""
+from ._lib import (  # noqa: F401
+    CsaError, EXPORTS, LIB_PATH, load,
+    csa_status_string, csa_materialize_rope_rows, csa_index_score, csa_topk,
+    csa_topk_workspace_bytes, csa_sparse_attn_decode, csa_sparse_attn_prefill,
+    csa_sparse_attn_workspace_bytes,
+)
+from .runner import CsaStep, step_for_config  # noqa: F401

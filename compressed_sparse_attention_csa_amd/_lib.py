@@ -1,0 +1,180 @@
+"""ctypes binding of libcsa.so (argument marshalling only).
+
+Every function keeps the C entry point's name and semantics (see
+``include/csa.h``); tensor arguments are torch tensors on the GPU, whose
+shapes give the sizes the C call takes.  All arithmetic runs in the HIP
+kernels; if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+PAGE = 128
+EFLAG_POS_RANGE = 1
+EFLAG_BLOCK_RANGE = 2
+EFLAG_TOPK_RANGE = 4
+EFLAG_META = 8
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F32 = ctypes.c_float
+
+_SIGS = {
+    "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "csa_materialize_rope_rows": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _I32, _I32, _P, _P, _P, _P]),
+    "csa_index_score": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I32, _I32,
+                                       _I32, _I32, _I32, _I32, _P, _I64, _P, _P]),
+    "csa_topk_workspace_bytes": (_SZ, [_I32, _I64, _I32]),
+    "csa_topk": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P, _P]),
+    "csa_sparse_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "csa_sparse_attn_decode": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32,
+                                              _I32, _P, _I32, _P, _I32, _I32, _P, _F32, _P, _P,
+                                              _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P,
+                                              _P]),
+}
+_SIGS["csa_sparse_attn_prefill"] = _SIGS["csa_sparse_attn_decode"]
+
+EXPORTS = tuple(_SIGS)
+
+
+class CsaError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libcsa.so; raises when it is missing (the HIP path has no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise CsaError(f"{path} is missing: build it with __graft_entry__.build() "
+                       "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CsaError("tensor arguments must live on the GPU")
+    if not t.is_contiguous():
+        raise CsaError("tensor arguments must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = load().csa_status_string(status).decode()
+        raise CsaError(f"{what}: {msg} ({status})")
+
+
+def _need(t: torch.Tensor, dtypes, ndim: int, name: str):
+    if t.dtype not in dtypes:
+        raise CsaError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.dim() != ndim:
+        raise CsaError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def csa_status_string(status: int) -> str:
+    return load().csa_status_string(status).decode()
+
+
+def csa_materialize_rope_rows(freqs_cos, freqs_sin, position_ids, num_tokens, rope_cos,
+                              rope_sin, err=None, stream=None) -> None:
+    _need(freqs_cos, (torch.float32,), 2, "freqs_cos")
+    _need(rope_cos, (torch.float32,), 2, "rope_cos")
+    st = load().csa_materialize_rope_rows(
+        _ptr(freqs_cos), _ptr(freqs_sin), freqs_cos.shape[0], freqs_cos.shape[1],
+        _ptr(position_ids), position_ids.shape[0], int(num_tokens), _ptr(rope_cos),
+        _ptr(rope_sin), _ptr(err), _stream(stream))
+    _check(st, "csa_materialize_rope_rows")
+
+
+def csa_index_score(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table, query_start_loc,
+                    positions, num_tokens, ratio, scores, err=None, stream=None) -> None:
+    _need(q_idx, (torch.int8,), 3, "q_idx")
+    _need(idx_kv, (torch.int8,), 3, "idx_kv")
+    _need(scores, (torch.float32,), 2, "scores")
+    T, Hi, Di = q_idx.shape
+    st = load().csa_index_score(
+        _ptr(q_idx), _ptr(q_scale), _ptr(head_w), _ptr(idx_kv), _ptr(idx_scale),
+        idx_kv.shape[0], _ptr(block_table), block_table.shape[1], _ptr(query_start_loc),
+        _ptr(positions), query_start_loc.shape[0] - 1, T, int(num_tokens), Hi, Di, int(ratio),
+        _ptr(scores), scores.shape[1], _ptr(err), _stream(stream))
+    _check(st, "csa_index_score")
+
+
+def csa_topk_workspace_bytes(T: int, score_stride: int, k: int) -> int:
+    return int(load().csa_topk_workspace_bytes(T, score_stride, k))
+
+
+def csa_topk(scores, positions, ratio, num_tokens, k, topk_idx, topk_val=None, workspace=None,
+             err=None, stream=None) -> None:
+    _need(scores, (torch.float32,), 2, "scores")
+    _need(topk_idx, (torch.int32,), 2, "topk_idx")
+    T = scores.shape[0]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().csa_topk(_ptr(scores), scores.shape[1], _ptr(positions), int(ratio), T,
+                         int(num_tokens), int(k), _ptr(topk_idx), _ptr(topk_val),
+                         _ptr(workspace), wsb, _ptr(err), _stream(stream))
+    _check(st, "csa_topk")
+
+
+def csa_sparse_attn_workspace_bytes(T: int, H: int, D: int, k: int, window: int) -> int:
+    return int(load().csa_sparse_attn_workspace_bytes(T, H, D, k, window))
+
+
+def _attn(fn_name, q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table, topk_idx, ratio,
+          win_kv, win_block_table, window, attn_sink, softmax_scale, query_start_loc, positions,
+          num_tokens, out, lse=None, workspace=None, err=None, stream=None):
+    _need(q, _BF16, 3, "q")
+    _need(out, _BF16, 3, "out")
+    T, H, D = q.shape
+    k = topk_idx.shape[1]
+    rope_dim = 2 * rope_cos.shape[1]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(load(), fn_name)(
+        _ptr(q), _ptr(rope_cos), _ptr(rope_sin), rope_dim, int(rope_offset), _ptr(cmp_kv),
+        cmp_kv.shape[0], _ptr(cmp_block_table), cmp_block_table.shape[1], _ptr(topk_idx), k,
+        int(ratio), _ptr(win_kv), win_kv.shape[0], _ptr(win_block_table),
+        win_block_table.shape[1], int(window), _ptr(attn_sink), float(softmax_scale),
+        _ptr(query_start_loc), _ptr(positions), query_start_loc.shape[0] - 1, T,
+        int(num_tokens), H, D, _ptr(out), _ptr(lse), _ptr(workspace), wsb, _ptr(err),
+        _stream(stream))
+    _check(st, fn_name)
+
+
+def csa_sparse_attn_decode(*args, **kw) -> None:
+    _attn("csa_sparse_attn_decode", *args, **kw)
+
+
+def csa_sparse_attn_prefill(*args, **kw) -> None:
+    _attn("csa_sparse_attn_prefill", *args, **kw)

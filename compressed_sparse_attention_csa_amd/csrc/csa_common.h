@@ -1,0 +1,68 @@
+// Device helpers shared by the CSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+constexpr int kPage = CSA_PAGE;  // tokens per cache block
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef unsigned short v4us __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Compressed slots visible to a query at absolute position p: c < (p+1)/ratio.
+__device__ __forceinline__ int visible_count(int p, int ratio) {
+  return p < 0 ? 0 : (p + 1) / ratio;
+}
+
+// Request owning packed row t (query_start_loc is nondecreasing, B+1 long);
+// -1 when no request owns it.
+__device__ __forceinline__ int owner_request(const int32_t* __restrict__ qsl, int B, int t) {
+  if (B <= 0 || t < qsl[0] || t >= qsl[B]) return -1;
+  int lo = 0, hi = B;  // invariant: qsl[lo] <= t < qsl[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void flag_error(int32_t* err, int bits) {
+  if (err != nullptr && bits) atomicOr(err, bits);
+}
+
+// Pool row of request-local position c through a 128-token block table;
+// -1 when the page lies past the table or names an invalid block.
+__device__ __forceinline__ long long page_row(const int32_t* __restrict__ bt_row,
+                                              int max_blocks, int num_blocks, int c) {
+  int page = c / kPage;
+  if (page >= max_blocks) return -1;
+  int blk = bt_row[page];
+  if (blk < 0 || blk >= num_blocks) return -1;
+  return static_cast<long long>(blk) * kPage + (c % kPage);
+}
+
+// Wave-wide xor shuffle (wave64).
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace csa

@@ -1,0 +1,99 @@
+"""Device buffers for one CSA layer step and the calls that run it.
+
+``CsaStep`` uploads host arrays (NumPy) once, allocates every output and
+workspace up front, and then runs the path as four library calls on one
+stream: RoPE rows -> indexer scores -> top-k -> sparse attention.  It only
+moves memory and passes pointers; all arithmetic runs in libcsa.so.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+
+PAGE = _lib.PAGE
+
+_INT_KEYS = ("query_start_loc", "positions", "position_ids", "cmp_block_table",
+             "win_block_table")
+
+
+def _to_dev(a: np.ndarray, device) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:  # BF16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+class CsaStep:
+    def __init__(self, arrays: Dict[str, np.ndarray], *, ratio: int, k: int, window: int,
+                 rope_offset: int, softmax_scale: float, num_tokens: Optional[int] = None,
+                 prefill: bool = False, device: str = "cuda", with_values: bool = True,
+                 with_lse: bool = True):
+        self.ratio, self.k, self.window = int(ratio), int(k), int(window)
+        self.rope_offset, self.softmax_scale = int(rope_offset), float(softmax_scale)
+        self.prefill = prefill
+        dev = torch.device(device)
+        self.t: Dict[str, torch.Tensor] = {}
+        for name, a in arrays.items():
+            self.t[name] = _to_dev(a, dev)
+        q = self.t["q"]
+        T, H, D = q.shape
+        self.T, self.H, self.D = T, H, D
+        self.num_tokens = T if num_tokens is None else int(num_tokens)
+        half = self.t["freqs_cos"].shape[1]
+        self.score_stride = self.t["cmp_block_table"].shape[1] * PAGE
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.rope_cos = torch.empty((T, half), **f32)
+        self.rope_sin = torch.empty((T, half), **f32)
+        self.scores = torch.empty((T, self.score_stride), **f32)
+        self.topk_idx = torch.empty((T, self.k), dtype=torch.int32, device=dev)
+        self.topk_val = torch.empty((T, self.k), **f32) if with_values else None
+        self.out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((T, H), **f32) if with_lse else None
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        tw = _lib.csa_topk_workspace_bytes(T, self.score_stride, self.k)
+        self.topk_ws = torch.empty(max(tw, 1), dtype=torch.uint8, device=dev) if tw else None
+        aw = 0 if prefill else _lib.csa_sparse_attn_workspace_bytes(T, H, D, self.k, self.window)
+        self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=dev) if aw else None
+
+    # ---- the four stages -------------------------------------------------
+    def rope(self, stream=None):
+        _lib.csa_materialize_rope_rows(self.t["freqs_cos"], self.t["freqs_sin"],
+                                       self.t["position_ids"], self.num_tokens, self.rope_cos,
+                                       self.rope_sin, err=self.err, stream=stream)
+
+    def index(self, stream=None):
+        t = self.t
+        _lib.csa_index_score(t["q_idx"], t["q_scale"], t["head_w"], t["idx_kv"], t["idx_scale"],
+                             t["cmp_block_table"], t["query_start_loc"], t["positions"],
+                             self.num_tokens, self.ratio, self.scores, err=self.err,
+                             stream=stream)
+
+    def topk(self, stream=None):
+        _lib.csa_topk(self.scores, self.t["positions"], self.ratio, self.num_tokens, self.k,
+                      self.topk_idx, self.topk_val, workspace=self.topk_ws, err=self.err,
+                      stream=stream)
+
+    def attn(self, stream=None, topk_idx: Optional[torch.Tensor] = None):
+        t = self.t
+        fn = _lib.csa_sparse_attn_prefill if self.prefill else _lib.csa_sparse_attn_decode
+        fn(t["q"], self.rope_cos, self.rope_sin, self.rope_offset, t["cmp_kv"],
+           t["cmp_block_table"], self.topk_idx if topk_idx is None else topk_idx, self.ratio,
+           t["win_kv"], t["win_block_table"], self.window, t["attn_sink"], self.softmax_scale,
+           t["query_start_loc"], t["positions"], self.num_tokens, self.out, lse=self.lse,
+           workspace=self.attn_ws, err=self.err, stream=stream)
+
+    def run(self, stream=None):
+        self.rope(stream)
+        self.index(stream)
+        self.topk(stream)
+        self.attn(stream)
+
+
+def step_for_config(cfg, arrays: Dict[str, np.ndarray], **kw) -> CsaStep:
+    """CsaStep with the scalar parameters of a workload config."""
+    return CsaStep(arrays, ratio=cfg.ratio, k=cfg.k, window=cfg.W, rope_offset=cfg.rope_offset,
+                   softmax_scale=cfg.softmax_scale, prefill=(cfg.T > 256), **kw)

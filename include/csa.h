@@ -1,0 +1,233 @@
+/*
+ * csa.h -- C ABI of libcsa.so: one compressed-sparse-attention (CSA) layer
+ * step on AMD Instinct MI355X (gfx950).
+ *
+ * The step, per query row:
+ *   1. csa_materialize_rope_rows  -- gather FP32 half-width RoPE rows
+ *   2. csa_index_score            -- INT8 lightning-indexer scores over the
+ *                                    causally visible compressed positions
+ *   3. csa_topk                   -- the k best positions, ascending, -1 padded
+ *   4. csa_sparse_attn_decode /   -- shared-KV attention over the 128-token
+ *      csa_sparse_attn_prefill       window and the selected compressed rows,
+ *                                    with one sink logit per head
+ *
+ * Pages the contracts follow (cited by title and section):
+ *   [V41]  pypto-lib "DeepSeek V4.1 Flash": "Serving-owned full RoPE tables",
+ *          "Compressor state ownership" (query_start_loc / positions /
+ *          num_tokens contract; indices checked before table indexing),
+ *          "Decode composition" (top-k checks, -1 padding, 128-token block
+ *          tables, padding rows).
+ *   [HP]   gitcode hyper-parallel issue #2 (DeepSeek V4 CP notes): Stage-2
+ *          operator calls (sinks, softmax_scale, ori_win_left = 127,
+ *          ori_win_right = 0), sections 8.2 / 10.3 (causal compressed
+ *          visibility c < (p+1)//ratio), 9.1 (window KV and compressed KV
+ *          joined, indices are the union), 10.2 (indexer indices are
+ *          compressed slot ids).
+ *   [MTP]  pypto-lib "DeepSeek V4-Flash, MTP point": "What is quantized"
+ *          (INT8 index keys with FP32 per-row scale, BF16 KV, FP32 sinks),
+ *          "Deployment configuration" (4 requests x S=2 decode rows, 128-token
+ *          pages, work scales with the visible context).
+ *   [ATOM] ROCm ATOM "DeepSeek-V4.1 native paged runtime": "Current execution
+ *          scope" (per-row bounds read on the device; padding sentinels).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or retains them; scratch space is a caller
+ *     workspace whose size a *_workspace_bytes helper returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream). Sizes are host scalars. Per-row bounds (visible span, window,
+ *     owning request) are derived on the device, so the same launch serves any
+ *     batch contents (graph-capturable; [ATOM]).
+ *   - Tensors are dense, row-major (C order) with the shapes given below. BF16
+ *     values are passed as their uint16 bit patterns.
+ *   - PAGE = 128: row c of a request lives at pool row
+ *       block_table[b * max_blocks + c / 128] * 128 + c % 128.
+ *   - Active rows are t < num_tokens; rows t >= num_tokens of every output are
+ *     never read or written ([V41]). num_tokens == 0 returns CSA_OK with no
+ *     launch. Row t belongs to the request b with
+ *     query_start_loc[b] <= t < query_start_loc[b+1] (equal neighbours are an
+ *     empty request).
+ *   - Return value: a csa_status. A negative status means nothing was
+ *     launched (host-checkable argument errors). Device-detected contract
+ *     violations OR a CSA_EFLAG_* bit into *err (if err != NULL; the caller
+ *     zeroes it) and are handled as each function states -- never by an
+ *     out-of-range access.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_PAGE 128
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  CSA_ERR_SHAPE = -2,       /* a size is negative or inconsistent                */
+  CSA_ERR_RANGE = -3,       /* num_tokens outside [0, T], k > width, ratio < 1   */
+  CSA_ERR_UNSUPPORTED = -4, /* a shape this build has no kernel for              */
+  CSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the helper's size  */
+  CSA_ERR_LAUNCH = -6       /* the HIP runtime refused a launch                  */
+} csa_status;
+
+/* device error word bits, OR-ed into *err */
+#define CSA_EFLAG_POS_RANGE 1   /* position >= table capacity, or a visible span past its storage */
+#define CSA_EFLAG_BLOCK_RANGE 2 /* a needed page lies past the block table or names an invalid block */
+#define CSA_EFLAG_TOPK_RANGE 4  /* a selected index is not visible to its row                  */
+#define CSA_EFLAG_META 8        /* an active row that no request owns                          */
+
+/* Human-readable name of a csa_status. */
+const char* csa_status_string(int status);
+
+/*
+ * csa_materialize_rope_rows -- [V41] "Serving-owned full RoPE tables".
+ *
+ *   freqs_cos, freqs_sin  FP32 [table_capacity, half_rope_dim], read only
+ *   position_ids          INT32 [T]
+ *   rope_cos, rope_sin    FP32 [T, half_rope_dim], written for t < num_tokens
+ *
+ * Row t < num_tokens: position p = position_ids[t]; p < 0 writes the identity
+ * (cos = 1.0, sin = +0.0); 0 <= p < table_capacity copies table row p bit for
+ * bit; p >= table_capacity flags CSA_EFLAG_POS_RANGE and leaves the row
+ * untouched.
+ */
+int csa_materialize_rope_rows(const float* freqs_cos, const float* freqs_sin,
+                              int32_t table_capacity, int32_t half_rope_dim,
+                              const int32_t* position_ids, int32_t T, int32_t num_tokens,
+                              float* rope_cos, float* rope_sin, int32_t* err, void* stream);
+
+/*
+ * csa_index_score -- lightning-indexer scores ([HP] 10.2 / 10.3; [MTP] INT8
+ * index keys with an FP32 per-row scale; per-row bounds as in [ATOM]).
+ *
+ *   q_idx        INT8 [T, Hi, Di]   quantised indexer query
+ *   q_scale      FP32 [T, Hi]       its per-(row, head) scale, > 0
+ *   head_w       FP32 [T, Hi]       per-head weights
+ *   idx_kv       INT8 [num_blocks, 128, Di]  index keys (one per position)
+ *   idx_scale    FP32 [num_blocks, 128]      key scales, > 0
+ *   block_table  INT32 [B, max_blocks]
+ *   query_start_loc INT32 [B + 1], positions INT32 [T] (causal positions)
+ *   scores       FP32 [T, score_stride], written for t < num_tokens
+ *
+ * For active row t of request b at position p and c < n = (p + 1) / ratio:
+ *   scores[t][c] = sum_h head_w[t][h] * relu(q_scale[t][h] * idx_scale[c]
+ *                                            * <q_idx[t][h], idx_kv[c]>)
+ * with exact INT32 dots and an FP32 epilogue (evaluated as
+ * idx_scale[c] * sum_h (head_w * q_scale)[t][h] * relu(dot), which equals the
+ * formula for positive scales); -0.0 results are written as +0.0. Entries
+ * c in [n, score_stride) are set to -inf.
+ * Violations: a row no request owns -> CSA_EFLAG_META, whole row -inf; n past
+ * score_stride or past 128 * max_blocks -> CSA_EFLAG_POS_RANGE, n is cut;
+ * a visible position on a page with an invalid block id ->
+ * CSA_EFLAG_BLOCK_RANGE, that position scores -inf.
+ * Supported: 1 <= Hi <= 64, Di in {32, 64, 96, 128}, ratio >= 1.
+ */
+int csa_index_score(const int8_t* q_idx, const float* q_scale, const float* head_w,
+                    const int8_t* idx_kv, const float* idx_scale, int32_t num_blocks,
+                    const int32_t* block_table, int32_t max_blocks,
+                    const int32_t* query_start_loc, const int32_t* positions,
+                    int32_t B, int32_t T, int32_t num_tokens, int32_t Hi, int32_t Di,
+                    int32_t ratio, float* scores, int64_t score_stride, int32_t* err,
+                    void* stream);
+
+/*
+ * csa_topk -- per active row, the k best of its visible positions
+ * ([V41] "Decode composition": eligibility, uniqueness, logical-position
+ * order, trailing -1; [HP] 7.4: width capped by the key length).
+ *
+ *   scores     FP32 [T, score_stride]
+ *   positions  INT32 [T]; the visible span of row t is n = (p + 1) / ratio,
+ *              cut to score_stride (CSA_EFLAG_POS_RANGE if cut)
+ *   topk_idx   INT32 [T, k]: the m = min(k, n) chosen positions ascending,
+ *              then -1
+ *   topk_val   FP32 [T, k] or NULL: the chosen scores, -inf for padding
+ *   workspace  device scratch of csa_topk_workspace_bytes(T, score_stride, k)
+ *              bytes (may be NULL when that size is 0)
+ *
+ * Ranking: score descending, ties to the lower position; -0.0 equals +0.0;
+ * NaN ranks below every number. Supported: 1 <= k <= 4096.
+ */
+size_t csa_topk_workspace_bytes(int32_t T, int64_t score_stride, int32_t k);
+int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions,
+             int32_t ratio, int32_t T, int32_t num_tokens, int32_t k, int32_t* topk_idx,
+             float* topk_val, void* workspace, size_t workspace_bytes, int32_t* err,
+             void* stream);
+
+/*
+ * csa_sparse_attn_decode -- shared-KV sparse attention with sink
+ * ([HP] Stage-2 calls and 9.1; [MTP] BF16 KV, FP32 attn_sink).
+ *
+ *   q            BF16 [T, H, D]
+ *   rope_cos/sin FP32 [T, rope_dim / 2]: rope rows of each query row
+ *                (csa_materialize_rope_rows); channels
+ *                [rope_offset, rope_offset + rope_dim) of q are rotated in
+ *                adjacent pairs (2i, 2i+1) by angle i before use
+ *   cmp_kv       BF16 [num_cmp_blocks, 128, D]  compressed KV (K = V)
+ *   cmp_block_table INT32 [B, max_cmp_blocks]
+ *   topk_idx     INT32 [T, k]: request-local compressed positions; negative
+ *                entries are padding
+ *   win_kv       BF16 [num_win_blocks, 128, D]  raw-token (window) KV
+ *   win_block_table INT32 [B, max_win_blocks], indexed by raw position
+ *   attn_sink    FP32 [H]
+ *   out          BF16 [T, H, D]  (round to nearest even of the FP32 result)
+ *   lse          FP32 [T, H] or NULL
+ *   workspace    csa_sparse_attn_workspace_bytes(T, H, D, k, window) bytes
+ *
+ * Row t of request b at position p attends, with every head, over the window
+ * rows at raw positions [max(0, p - window + 1), p] followed by the selected
+ * compressed rows (no deduplication between the two caches):
+ *   l_j = softmax_scale * <rot(q[t][h]), K_j>,  M = max(sink_h, max_j l_j),
+ *   Z = exp(sink_h - M) + sum_j exp(l_j - M),
+ *   out = sum_j exp(l_j - M) / Z * K_j,  lse = M + log Z.
+ * An empty set gives out = 0, lse = sink. Violations: a row no request owns
+ * -> CSA_EFLAG_META, treated as empty; a selected entry >= (p + 1) / ratio ->
+ * CSA_EFLAG_TOPK_RANGE, left out; a window or selected row whose page is past
+ * the table or names an invalid block -> CSA_EFLAG_BLOCK_RANGE, left out.
+ * Supported: 1 <= H <= 64, D in {64, 128, 256, 512}, rope_dim even,
+ * rope_offset + rope_dim <= D, window >= 0, 0 <= k <= 4096.
+ * Arithmetic: the rotated query and the probabilities are rounded to BF16 as
+ * MFMA operands; logits, softmax and accumulation are FP32.
+ */
+size_t csa_sparse_attn_workspace_bytes(int32_t T, int32_t H, int32_t D, int32_t k,
+                                       int32_t window);
+int csa_sparse_attn_decode(const uint16_t* q, const float* rope_cos, const float* rope_sin,
+                           int32_t rope_dim, int32_t rope_offset, const uint16_t* cmp_kv,
+                           int32_t num_cmp_blocks, const int32_t* cmp_block_table,
+                           int32_t max_cmp_blocks, const int32_t* topk_idx, int32_t k,
+                           int32_t ratio, const uint16_t* win_kv, int32_t num_win_blocks,
+                           const int32_t* win_block_table, int32_t max_win_blocks,
+                           int32_t window, const float* attn_sink, float softmax_scale,
+                           const int32_t* query_start_loc, const int32_t* positions,
+                           int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
+                           uint16_t* out, float* lse, void* workspace,
+                           size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * csa_sparse_attn_prefill -- the same operation and arguments as
+ * csa_sparse_attn_decode, scheduled for many query rows (a prefill walk in
+ * 128-token tiles, [MTP] "Deployment configuration"): one work-group per
+ * query row, consecutive rows kept on one XCD so their shared window rows and
+ * popular compressed rows stay in that XCD's L2. Needs no workspace
+ * (csa_sparse_attn_workspace_bytes is still accepted).
+ */
+int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const float* rope_sin,
+                            int32_t rope_dim, int32_t rope_offset, const uint16_t* cmp_kv,
+                            int32_t num_cmp_blocks, const int32_t* cmp_block_table,
+                            int32_t max_cmp_blocks, const int32_t* topk_idx, int32_t k,
+                            int32_t ratio, const uint16_t* win_kv, int32_t num_win_blocks,
+                            const int32_t* win_block_table, int32_t max_win_blocks,
+                            int32_t window, const float* attn_sink, float softmax_scale,
+                            const int32_t* query_start_loc, const int32_t* positions,
+                            int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
+                            uint16_t* out, float* lse, void* workspace,
+                            size_t workspace_bytes, int32_t* err, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

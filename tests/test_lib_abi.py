@@ -1,0 +1,107 @@
+"""The C ABI library loads and exports every entry point include/csa.h declares,
+and its host-side argument checks reject bad calls before any launch.  No
+compute call is made here (no GPU needed): every call below fails validation
+on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import compressed_sparse_attention_csa_amd as csa
+    try:
+        return csa.load()
+    except csa.CsaError as e:  # pragma: no cover - build first
+        pytest.fail(f"libcsa.so not built: {e}")
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"csa_materialize_rope_rows", "csa_index_score", "csa_topk",
+            "csa_sparse_attn_decode", "csa_sparse_attn_prefill"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_header():
+    import compressed_sparse_attention_csa_amd as csa
+    assert set(csa.EXPORTS) == set(_declared())
+    for n in _declared():
+        assert callable(getattr(csa, n))
+
+
+def test_status_strings(lib):
+    for s in range(-6, 1):
+        assert lib.csa_status_string(s).decode().startswith("CSA_")
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call fails on the host
+
+
+def test_rope_rows_host_checks(lib):
+    f = lib.csa_materialize_rope_rows
+    assert f(FAKE, FAKE, 8, 4, FAKE, 4, 5, FAKE, FAKE, None, None) == -3   # num_tokens > T
+    assert f(FAKE, FAKE, 8, 4, FAKE, 4, -1, FAKE, FAKE, None, None) == -3
+    assert f(None, FAKE, 8, 4, FAKE, 4, 2, FAKE, FAKE, None, None) == -1
+    assert f(None, None, 8, 4, None, 4, 0, None, None, None, None) == 0    # no work, no launch
+
+
+def test_index_score_host_checks(lib):
+    f = lib.csa_index_score
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, FAKE, FAKE, 1, 2, 2, 64, 128, 1, FAKE,
+            256, None, None]
+    bad = list(args); bad[15] = 0                     # ratio < 1
+    assert f(*bad) == -3
+    bad = list(args); bad[13] = 65                    # Hi > 64
+    assert f(*bad) == -4
+    bad = list(args); bad[14] = 100                   # Di not a multiple of 16
+    assert f(*bad) == -4
+    bad = list(args); bad[0] = None                   # q_idx NULL
+    assert f(*bad) == -1
+    bad = list(args); bad[0] = ctypes.c_void_p(0x1001)  # misaligned INT8 query
+    assert f(*bad) == -4
+    bad = list(args); bad[12] = 0                     # num_tokens 0: nothing to do
+    assert f(*bad) == 0
+
+
+def test_topk_host_checks(lib):
+    f = lib.csa_topk
+    assert lib.csa_topk_workspace_bytes(8, 1 << 20, 2048) >= 0
+    assert f(FAKE, 100, FAKE, 1, 2, 2, 0, FAKE, None, None, 0, None, None) == -3     # k < 1
+    assert f(FAKE, 100, FAKE, 1, 2, 2, 5000, FAKE, None, None, 0, None, None) == -3  # k too big
+    assert f(None, 100, FAKE, 1, 2, 2, 4, FAKE, None, None, 0, None, None) == -1
+    assert f(None, 100, None, 1, 2, 0, 4, None, None, None, 0, None, None) == 0
+
+
+def test_attention_host_checks(lib):
+    for f in (lib.csa_sparse_attn_decode, lib.csa_sparse_attn_prefill):
+        base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
+                FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, None, 0, None, None]
+        bad = list(base); bad[25] = 320               # D without a kernel
+        assert f(*bad) == -4
+        bad = list(base); bad[24] = 65                # H > 64
+        assert f(*bad) == -4
+        bad = list(base); bad[4] = 450                # rope span past D
+        assert f(*bad) == -4
+        bad = list(base); bad[0] = None               # q NULL
+        assert f(*bad) == -1
+        bad = list(base); bad[23] = 0                 # no active rows
+        assert f(*bad) == 0
+    # decode with several splits needs the workspace the helper reports
+    need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 512, 128)
+    assert need > 0
+    base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
+            FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, None, 0, None, None]
+    assert lib.csa_sparse_attn_decode(*base) == -5
