@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Throughput of one CSA layer step on one MI355X.
+
+A step is the whole hot path on one batch: RoPE rows -> INT8 indexer scores ->
+top-k -> shared-KV sparse attention (four library calls on one stream).  The
+default workload is the V4.1 ratio-2 decode layer (8 rows = 4 requests x S=2,
+64 heads x 512, 16,384 compressed rows per request, top-k 512, window 128).
+
+Timing: W untimed warmup steps, then exactly K steps bracketed by
+torch.cuda.synchronize(); inputs are resident in HBM.  To keep the layer's
+working set out of the 256 MB Infinity Cache (as it would be when 40 layers
+run between two steps of this one), successive steps rotate through enough
+independent copies of the inputs to exceed 512 MiB.  Per-stage HIP events on
+the launch stream give each kernel's live duration for the roofline.
+
+Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits: this build runs on
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense BF16 MFMA
+INT8_PEAK_TOPS = 5000.0        # dense INT8 MFMA
+
+KERNEL_SOURCES = {
+    "rope": "csa_rope.hip", "index": "csa_index.hip", "topk": "csa_topk.hip",
+    "attn": "csa_attn.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c2", help="c1..c5 (default c2: ratio-2 decode)")
+    ap.add_argument("--copies", type=int, default=0, help="input copies (0 = auto, cold L2/MALL)")
+    ap.add_argument("--warm", action="store_true", help="one input copy (cache-warm timing)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes / flops (counting only; the pages' data movement per unit)
+# ---------------------------------------------------------------------------
+
+def visible(p, ratio):
+    return max(0, (int(p) + 1) // ratio)
+
+
+def work_model(cfg, x, topk_idx: np.ndarray):
+    """Bytes each stage must move once, and the step total (decode formula:
+    index keys of every visible position once per request, every unique
+    gathered KV row once per request, Q, O, lse and small metadata)."""
+    T, H, D, R, Hi, Di, k = cfg.T, cfg.H, cfg.D, cfg.R, cfg.Hi, cfg.Di, cfg.k
+    qsl = np.asarray(x["query_start_loc"])
+    pos = np.asarray(x["positions"])
+    nv = np.array([visible(p, cfg.ratio) for p in pos])
+    idx_keys = 0
+    kv_rows = 0
+    pairs = 0
+    for b in range(len(qsl) - 1):
+        rows = range(qsl[b], qsl[b + 1])
+        if not len(rows):
+            continue
+        idx_keys += int(max(nv[t] for t in rows))
+        win, sel = set(), set()
+        for t in rows:
+            p = int(pos[t])
+            w = list(range(max(0, p - cfg.W + 1), p + 1))
+            s = [int(c) for c in topk_idx[t] if c >= 0]
+            win.update(w)
+            sel.update(s)
+            pairs += len(w) + len(s)
+        kv_rows += len(win) + len(sel)
+    q_side = T * Hi * (Di + 8)
+    st = {
+        "rope": 8 * T * R + 4 * T,   # read + write cos and sin rows (R/2 FP32 each), positions
+        "index": idx_keys * (Di + 4) + q_side + 4 * T * cfg.score_stride,
+        "topk": 4 * int(nv.clip(max=cfg.score_stride).sum()) + 8 * T * k,
+        "attn": kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + 4 * T * k + 4 * T * R,
+    }
+    step = (idx_keys * (Di + 4) + kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + q_side
+            + 8 * T * k + 4 * T * R)
+    flops = {"attn": pairs * H * D * 4,
+             "index": int(sum(nv[t] for t in range(T))) * Hi * Di * 2}
+    return dict(stage_bytes=st, step_bytes=step, flops=flops, kv_rows=kv_rows,
+                idx_keys=idx_keys, pairs=pairs)
+
+
+def source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "compressed_sparse_attention_csa_amd", "csrc", KERNEL_SOURCES[name])
+    h = hashlib.sha256()
+    for q in (p, os.path.join(ROOT, "compressed_sparse_attention_csa_amd", "csrc",
+                              "csa_common.h")):
+        h.update(open(q, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("source_hash") != source_hash(stage):
+        return None
+    return d.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on host cores
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(cfg, x, budget_s: float):
+    import oracle  # the cpu_baseline leg is the one place bench.py uses the oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = min(blas_threads, len(os.sched_getaffinity(0)))
+    T = cfg.T
+    # sample: whole rows of the workload; all of them when they fit the budget
+    rows_per_call = T if T <= 16 else 16
+    done_rows = 0
+    t0 = time.perf_counter()
+    stage = dict(rope=0.0, index=0.0, topk=0.0, attn=0.0)
+    rng = np.random.default_rng(0)
+    while True:
+        rows = np.arange(T) if rows_per_call == T else np.sort(rng.choice(T, rows_per_call, False))
+        qsl = np.asarray(x["query_start_loc"])
+        owner = np.searchsorted(qsl, rows, side="right") - 1
+        cnt = np.bincount(owner, minlength=len(qsl) - 1)
+        sub = dict(x)
+        sub["query_start_loc"] = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+        for key in ("q_idx", "q_scale", "head_w", "positions", "position_ids", "q"):
+            sub[key] = np.ascontiguousarray(np.asarray(x[key])[rows])
+        n = len(rows)
+        a = time.perf_counter()
+        rc = np.zeros((n, cfg.R // 2), np.float32)
+        rs = np.zeros_like(rc)
+        oracle.materialize_rope_rows(sub["freqs_cos"], sub["freqs_sin"], sub["position_ids"], n,
+                                     rc, rs)
+        b_ = time.perf_counter()
+        s, _ = oracle.index_scores(sub["q_idx"], sub["q_scale"], sub["head_w"], sub["idx_kv"],
+                                   sub["idx_scale"], sub["cmp_block_table"],
+                                   sub["query_start_loc"], sub["positions"], n, cfg.ratio,
+                                   cfg.score_stride)
+        c_ = time.perf_counter()
+        idx, _, _ = oracle.topk(s, sub["positions"], cfg.ratio, n, cfg.k)
+        d_ = time.perf_counter()
+        oracle.sparse_attn(sub["q"], rc, rs, cfg.rope_offset, sub["cmp_kv"],
+                           sub["cmp_block_table"], idx, cfg.ratio, sub["win_kv"],
+                           sub["win_block_table"], cfg.W, sub["attn_sink"], cfg.softmax_scale,
+                           sub["query_start_loc"], sub["positions"], n)
+        e_ = time.perf_counter()
+        stage["rope"] += b_ - a
+        stage["index"] += c_ - b_
+        stage["topk"] += d_ - c_
+        stage["attn"] += e_ - d_
+        done_rows += n
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done_rows / el, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done_rows} query rows of this workload ({rows_per_call} per oracle call, "
+                      f"all four stages, float64 NumPy) in {el:.1f} s",
+            "stage_seconds": {k: round(v, 3) for k, v in stage.items()}}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs the CSA step on one GPU; --gpus {args.gpus} is not "
+              "supported (the multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synthetic
+    import compressed_sparse_attention_csa_amd as csa
+
+    cfg = synthetic.get(args.config)
+    x = synthetic.make_inputs(cfg, seed=0).t
+    shared_names = ("freqs_cos", "freqs_sin")
+    first = csa.step_for_config(cfg, x)
+    shared = {n: first.t[n] for n in shared_names}
+    per_copy_touch = (cfg.B * cfg.n_cmp_per_request * (cfg.Di + 4) +
+                      cfg.T * (cfg.k + cfg.W) * 2 * cfg.D + 4 * cfg.T * cfg.H * cfg.D)
+    if args.warm:
+        copies = 1
+    elif args.copies > 0:
+        copies = args.copies
+    else:
+        copies = int(min(48, max(1, -(-(512 << 20) // max(per_copy_touch, 1)))))
+    steps = [first] + [csa.step_for_config(cfg, x, shared=shared) for _ in range(copies - 1)]
+
+    stream = torch.cuda.current_stream()
+    stages = ("rope", "index", "topk", "attn")
+
+    def one(step, ev=None):
+        if ev is None:
+            step.run()
+            return
+        ev[0].record(stream)
+        step.rope()
+        ev[1].record(stream)
+        step.index()
+        ev[2].record(stream)
+        step.topk()
+        ev[3].record(stream)
+        step.attn()
+        ev[4].record(stream)
+
+    for i in range(args.warmup):
+        one(steps[i % copies])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(steps[i % copies], evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {s: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
+                                  for i in range(args.steps)]))
+                for j, s in enumerate(stages)}
+    errs = [int(s.err.item()) for s in steps]
+    topk_host = first.topk_idx.cpu().numpy()
+
+    wm = work_model(cfg, x, topk_host)
+    rows = cfg.T
+    value = rows / (ms_per_step / 1e3)
+    step_gbs = wm["step_bytes"] / (ms_per_step / 1e3) / 1e9
+
+    # dominant kernel: the stage with the largest share of the step
+    dom = max(stages, key=lambda s: stage_ms[s])
+    if dom == "attn" and cfg.T > 256:
+        ach = wm["flops"]["attn"] / (stage_ms[dom] / 1e3) / 1e12
+        roof = {"kernel": "attn_kernel (csa_sparse_attn_prefill)", "bound": "mfma",
+                "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(dom, cfg.name),
+                "algorithmic_per_launch": wm["flops"]["attn"], "avg_launch_ms": stage_ms[dom]}
+    else:
+        names = {"rope": "rope_rows_kernel", "index": "index_score_kernel",
+                 "topk": "topk_kernel", "attn": "attn_kernel + attn_merge_kernel"}
+        ach = wm["stage_bytes"][dom] / (stage_ms[dom] / 1e3) / 1e9
+        roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, cfg.name),
+                "algorithmic_per_launch": wm["stage_bytes"][dom], "avg_launch_ms": stage_ms[dom]}
+
+    rec = {
+        "metric": "CSA decode rows/s per layer + achieved HBM GB/s (% of MI355X peak)",
+        "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8+bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": cfg.T, "requests": cfg.B, "heads": cfg.H,
+                   "head_dim": cfg.D, "ratio": cfg.ratio, "top_k": cfg.k, "window": cfg.W,
+                   "compressed_rows_per_request": cfg.n_cmp_per_request,
+                   "indexer": f"{cfg.Hi}x{cfg.Di}", "input_copies": copies,
+                   "cache": "warm" if copies == 1 else "cold (rotating copies > 512 MiB)"},
+        "step_hbm": {"algorithmic_bytes": wm["step_bytes"], "achieved_gbs": round(step_gbs, 1),
+                     "frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "roofline": roof,
+        "device_errors": errs[0],
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,10 +16,6 @@ from . import _lib
 
 PAGE = _lib.PAGE
 
-_INT_KEYS = ("query_start_loc", "positions", "position_ids", "cmp_block_table",
-             "win_block_table")
-
-
 def _to_dev(a: np.ndarray, device) -> torch.Tensor:
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:  # BF16 bit patterns
@@ -31,14 +27,17 @@ class CsaStep:
     def __init__(self, arrays: Dict[str, np.ndarray], *, ratio: int, k: int, window: int,
                  rope_offset: int, softmax_scale: float, num_tokens: Optional[int] = None,
                  prefill: bool = False, device: str = "cuda", with_values: bool = True,
-                 with_lse: bool = True):
+                 with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None):
         self.ratio, self.k, self.window = int(ratio), int(k), int(window)
         self.rope_offset, self.softmax_scale = int(rope_offset), float(softmax_scale)
         self.prefill = prefill
         dev = torch.device(device)
         self.t: Dict[str, torch.Tensor] = {}
         for name, a in arrays.items():
-            self.t[name] = _to_dev(a, dev)
+            if shared is not None and name in shared:
+                self.t[name] = shared[name]   # e.g. read-only RoPE tables reused by copies
+            else:
+                self.t[name] = _to_dev(a, dev)
         q = self.t["q"]
         T, H, D = q.shape
         self.T, self.H, self.D = T, H, D
