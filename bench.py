@@ -7,11 +7,13 @@ default workload is the V4.1 ratio-2 decode layer (8 rows = 4 requests x S=2,
 64 heads x 512, 16,384 compressed rows per request, top-k 512, window 128).
 
 Timing: W untimed warmup steps, then exactly K steps bracketed by
-torch.cuda.synchronize(); inputs are resident in HBM.  To keep the layer's
-working set out of the 256 MB Infinity Cache (as it would be when 40 layers
-run between two steps of this one), successive steps rotate through enough
-independent copies of the inputs to exceed 512 MiB.  Per-stage HIP events on
-the launch stream give each kernel's live duration for the roofline.
+torch.cuda.synchronize(); inputs are resident in HBM.  A step is one replay of
+a captured HIP graph of the four calls.  To keep the layer's working set out
+of the 256 MB Infinity Cache (as it would be when 40 layers run between two
+steps of this one), successive steps rotate through enough independent copies
+of the inputs to exceed 512 MiB.  Each stage's per-launch duration (for the
+roofline) comes from HIP events around a graph of back-to-back launches of
+that stage over the same rotating copies.
 
 Prints ONE JSON line (rank 0).  --gpus N with N > 1 exits: this build runs on
 one GPU.
@@ -213,37 +215,53 @@ def main():
         copies = int(min(48, max(1, -(-(512 << 20) // max(per_copy_touch, 1)))))
     steps = [first] + [csa.step_for_config(cfg, x, shared=shared) for _ in range(copies - 1)]
 
-    stream = torch.cuda.current_stream()
     stages = ("rope", "index", "topk", "attn")
-
-    def one(step, ev=None):
-        if ev is None:
-            step.run()
-            return
-        ev[0].record(stream)
-        step.rope()
-        ev[1].record(stream)
-        step.index()
-        ev[2].record(stream)
-        step.topk()
-        ev[3].record(stream)
-        step.attn()
-        ev[4].record(stream)
-
     for i in range(args.warmup):
-        one(steps[i % copies])
+        steps[i % copies].run()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    # one captured graph per input copy: a step is one graph replay, so host
+    # launch overhead stays out of the step time (as under decode graph capture)
+    cap = torch.cuda.Stream()
+    graphs = []
+    for st in steps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            st.run()
+        graphs.append(g)
+    for i in range(max(2, args.warmup)):
+        graphs[i % copies].replay()
     torch.cuda.synchronize()
+
     t0 = time.perf_counter()
     for i in range(args.steps):
-        one(steps[i % copies], evs[i])
+        graphs[i % copies].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_ms = {s: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1])
-                                  for i in range(args.steps)]))
-                for j, s in enumerate(stages)}
+
+    # per-launch duration of each stage: a graph of back-to-back launches of
+    # that stage over the rotating copies, timed with HIP events on the stream
+    # the graph runs on
+    stage_ms = {}
+    reps = max(8, copies)
+    for s in stages:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(reps):
+                getattr(steps[i % copies], s)()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        n_rep = 5
+        for _ in range(n_rep):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stage_ms[s] = e0.elapsed_time(e1) / (n_rep * reps)
     errs = [int(s.err.item()) for s in steps]
     topk_host = first.topk_idx.cpu().numpy()
 

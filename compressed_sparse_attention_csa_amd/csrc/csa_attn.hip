@@ -8,22 +8,30 @@
 // "Serving-owned full RoPE tables": the query is rotated with FP32 half-width
 // rows in adjacent pairs.
 //
-// Mapping.  A work-group (4 waves) owns one query row and one contiguous span
-// (a "split") of its key list; wave w owns heads 16w..16w+15.  The key list is
-// virtual -- entry i < W_len is window position w_lo + i, later entries are
-// topk_idx[t][i - W_len] -- and is resolved through the block tables one
-// 32-row tile at a time.  Each tile is gathered (1 KiB rows, coalesced) into
-// LDS twice: row-major K (MFMA A operand of S^T = K Q^T) and transposed V
-// (A operand of O^T = V^T P^T).  S^T puts one head per lane, so the online
-// softmax needs only two cross-lane steps per tile, and P^T leaves the MFMA
-// already laid out as the B operand of the P*V product (the key order inside
-// the MFMA is permuted identically on both operands).  The rotated query
-// stays in registers as the B operand of S^T for the whole walk.
+// Two schedules share the same tile code.
 //
-// With one split per row the kernel writes BF16 output and lse directly
-// (prefill, many rows); with several it writes FP32 partials (unnormalised O,
-// running max and sum, base-2 domain) that a merge kernel combines with the
-// sink.
+// Ring kernel (prefill, large decode batches): a work-group (4 waves) owns
+// one query row and walks its whole key list; wave w owns heads 16w..16w+15.
+// The key list is virtual -- entry i < W_len is window position w_lo + i,
+// later entries are topk_idx[t][i - W_len] -- and the work-group resolves it
+// through the block tables in one parallel pass into LDS, compacting the
+// valid rows to the front.  Rows then stream into a four-tile LDS ring (32
+// rows per tile) with gfx950's direct global->LDS loads -- one wave-wide
+// 16-byte-per-lane load moves a whole 1 KiB row, no registers involved --
+// keeping three tiles in flight behind the one being multiplied.
+//
+// Decode kernel (small batches): a work-group owns one (row, 16-head group,
+// 128-entry span); each wave gathers and multiplies its own 32-row tile, so a
+// span costs one memory latency and every key byte is read from LDS once.
+// Partials of the spans are merged with the sink by a third kernel.
+//
+// Tile code.  Rows sit at a 16-byte-padded stride so the K operand reads
+// (A of S^T = K Q^T) and the transposed V reads (A of O^T = V^T P^T) spread
+// over the LDS banks.  S^T puts one head per lane, so the softmax needs only
+// two cross-lane steps per tile, and P^T leaves the MFMA already laid out as
+// the B operand of the P*V product (the key order inside the MFMA is permuted
+// identically on both operands).  The rotated query stays in registers as the
+// B operand of S^T.
 #include "csa_common.h"
 
 namespace csa {
@@ -33,7 +41,6 @@ namespace {
 constexpr int kTile = 32;       // key rows per LDS tile
 constexpr int kAttnWaves = 4;   // 16 heads per wave
 constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kVtStride = 36;   // bf16 elements per transposed row (32 + pad)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -67,28 +74,81 @@ struct AttnArgs {
   float* part_o;     // [T][splits][H][D]
   float2* part_ml;   // [T][splits][H]
   int splits;
-  int split_len;
   int items_per_xcd;
   int32_t* err;
 };
 
 __device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
+constexpr int kMaxSplit = 4224;  // longest key list: window + k
+constexpr uint32_t kWinBit = 0x80000000u;
+constexpr uint32_t kNoRow = 0xffffffffu;
+constexpr int kRing = 4;          // key tiles resident in LDS (in flight or in use)
+constexpr float kSlack = 8.0f;    // log2 headroom before the running max is moved
+
+// s_waitcnt immediate that waits until at most n vector-memory ops are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Exclusive scan over the 256-thread work-group (scratch: one int per wave).
+__device__ int block_excl_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) {
+    const int s = wsum[w];
+    if (w < wave) before += s;
+    tot += s;
+  }
+  *total = tot;
+  return before + incl - v;
+}
+
+template <int LPW>
+__device__ __forceinline__ void wait_tiles_behind(int behind) {
+  // at most `behind` later tiles (LPW loads each) may still be in flight
+  switch (behind) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<LPW>(); break;
+    case 2: wait_vmcnt<2 * LPW>(); break;
+    default: wait_vmcnt<3 * LPW>(); break;
+  }
+}
+
 template <int D>
-__global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnArgs a) {
-  constexpr int KS = D / 32;   // K steps of S^T
-  constexpr int DT = D / 16;   // d tiles of O^T
-  constexpr int KROW = D + 8;  // padded bf16 elements per K row
-  __shared__ __attribute__((aligned(16))) uint16_t k_s[kTile * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_s[D * kVtStride];
-  __shared__ const uint16_t* rowptr_s[kTile];
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;                 // K steps of S^T
+  constexpr int DT = D / 16;                 // d tiles of O^T
+  constexpr int RB = 2 * D;                  // bytes per key row
+  constexpr int NC = D / 8;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / NC;               // rows one wave-wide load moves
+  constexpr int LPW = kTile / RPI / kAttnWaves;  // loads per wave per tile
+  constexpr int GS = RPI * RB + 16;          // LDS stride of one load's rows (+16 B pad)
+  constexpr int TS = (kTile / RPI) * GS;     // LDS bytes per tile
+  static_assert(kRing == 4, "wait_tiles_behind assumes a ring of 4");
+  __shared__ __attribute__((aligned(16))) uint8_t kv_s[kRing * TS];
+  __shared__ uint32_t row_s[kMaxSplit];   // pool row of each valid entry (bit 31: window pool)
+  __shared__ int scan_s[kAttnWaves];
   __shared__ int err_s;
 
-  // XCD-aware work mapping: consecutive items (row, split) land on one XCD.
+  // XCD-aware work mapping: consecutive rows land on one XCD.
   const int L = blockIdx.x;
-  const int item = (L & 7) * a.items_per_xcd + (L >> 3);
-  const int t = item / a.splits;
-  const int split = item % a.splits;
+  const int t = (L & 7) * a.items_per_xcd + (L >> 3);
   if (t >= a.num_tokens) return;
 
   const int tid = threadIdx.x;
@@ -110,8 +170,83 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnArgs a) {
     w_len = p - w_lo + 1;
   }
   const int list_len = (b >= 0) ? (w_len + a.k) : 0;
-  const int i_begin = split * a.split_len;
-  const int i_end = min(list_len, i_begin + a.split_len);
+  const int n_my = list_len;
+  __syncthreads();
+
+  // ---- resolve every entry of the key list through the block tables at once;
+  //      valid rows are compacted to the front (softmax does not depend on
+  //      their order), so a tile's mask is just j < n_valid
+  const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
+  int n_valid = 0;
+  {
+    int ebits = 0;
+    for (int j0 = 0; j0 < n_my; j0 += kAttnThreads) {
+      const int j = j0 + tid;
+      const int i = j;
+      uint32_t rr = kNoRow;
+      if (j >= n_my) {
+        // past the list: nothing to resolve
+      } else if (i < w_len) {
+        const long long r = page_row(a.win_bt + static_cast<long long>(b) * a.max_win_blocks,
+                                     a.max_win_blocks, a.num_win_blocks, w_lo + i);
+        if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
+      } else {
+        const int c = topk_row[i - w_len];
+        if (c >= 0) {
+          if (c >= nv) {
+            ebits |= CSA_EFLAG_TOPK_RANGE;
+          } else {
+            const long long r = page_row(a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks,
+                                         a.max_cmp_blocks, a.num_cmp_blocks, c);
+            if (r >= 0) rr = static_cast<uint32_t>(r); else ebits |= CSA_EFLAG_BLOCK_RANGE;
+          }
+        }
+      }
+      int total = 0;
+      const int slot = n_valid + block_excl_scan(rr != kNoRow ? 1 : 0, scan_s, &total);
+      if (rr != kNoRow) row_s[slot] = rr;
+      n_valid += total;
+    }
+    if (ebits) atomicOr(&err_s, ebits);
+  }
+
+  __syncthreads();  // row_s ready
+
+  // ---- direct-to-LDS gather of one 32-row tile into ring slot tt % kRing.
+  //      Lane l of a wave-wide load moves chunk l % NC of row l / NC; each
+  //      load's rows start 16 bytes past the previous load's, which spreads the
+  //      K and V^T operand reads over the LDS banks.  Masked rows read finite
+  //      dummy bytes (the query) so every wave issues exactly LPW loads per
+  //      tile; P = 0 keeps them out of the result.
+  const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
+  auto issue = [&](int tt) {
+    uint8_t* slot = kv_s + (tt % kRing) * TS;
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int ins = wave * LPW + u;
+      const int j = tt * kTile + ins * RPI + lane / NC;   // compacted entry
+      const uint32_t rr = (j < n_valid) ? row_s[j] : kNoRow;
+      const uint8_t* src = dummy;
+      if (rr != kNoRow)
+        src = reinterpret_cast<const uint8_t*>(
+            (rr & kWinBit) ? a.win_kv + static_cast<long long>(rr & ~kWinBit) * D
+                           : a.cmp_kv + static_cast<long long>(rr) * D);
+      __builtin_amdgcn_global_load_lds(
+          src + (lane % NC) * 16, (__attribute__((address_space(3))) void*)(slot + ins * GS), 16,
+          0, 0);
+    }
+  };
+  auto row_off = [](int r) { return (r / RPI) * GS + (r % RPI) * RB; };
+
+  const float neg_inf = -__builtin_huge_valf();
+  float m_run = neg_inf;  // running max of this lane's head (base-2 logits)
+  float l_run = 0.0f;     // running sum
+  v4f o_acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int ntiles = (n_valid + kTile - 1) / kTile;
+  for (int tt = 0; tt < min(kRing, ntiles); ++tt) issue(tt);
 
   // ---- query fragments (B operand of S^T): lane (head col, group grp) holds
   //      channels ks*32 + grp*8 .. +8, rotated where they fall in the rope span.
@@ -146,92 +281,57 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnArgs a) {
     }
   }
 
-  const float neg_inf = -__builtin_huge_valf();
-  float m_run = neg_inf;  // running max of this lane's head (base-2 logits)
-  float l_run = 0.0f;     // running sum
-  v4f o_acc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
-  for (int i0 = i_begin; i0 < i_end; i0 += kTile) {
-    // resolve this tile's rows through the block tables
-    if (tid < kTile) {
-      const int i = i0 + tid;
-      const uint16_t* ptr = nullptr;
-      int ebits = 0;
-      if (i < i_end) {
-        if (i < w_len) {
-          const long long r = page_row(a.win_bt + static_cast<long long>(b) * a.max_win_blocks,
-                                       a.max_win_blocks, a.num_win_blocks, w_lo + i);
-          if (r >= 0) ptr = a.win_kv + r * D; else ebits |= CSA_EFLAG_BLOCK_RANGE;
-        } else {
-          const int c = topk_row[i - w_len];
-          if (c >= 0) {
-            if (c >= nv) {
-              ebits |= CSA_EFLAG_TOPK_RANGE;
-            } else {
-              const long long r = page_row(a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks,
-                                           a.max_cmp_blocks, a.num_cmp_blocks, c);
-              if (r >= 0) ptr = a.cmp_kv + r * D; else ebits |= CSA_EFLAG_BLOCK_RANGE;
-            }
-          }
-        }
-      }
-      rowptr_s[tid] = ptr;
-      if (ebits) atomicOr(&err_s, ebits);
-    }
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int issued = min(ntiles, tt + kRing);
+    wait_tiles_behind<LPW>(issued - tt - 1);
     __syncthreads();
-    // gather: lane (c4 = lane&3, rp = lane>>2) moves two rows' 16-byte chunk
-    {
-      const int c4 = lane & 3;
-      const int rp = lane >> 2;
-      const int r0 = 2 * rp, r1 = r0 + 1;
-      const uint16_t* p0 = rowptr_s[r0];
-      const uint16_t* p1 = rowptr_s[r1];
-      for (int cg = wave; cg < D / 32; cg += kAttnWaves) {
-        const int cc = cg * 4 + c4;  // 16-byte chunk index within the row
-        v4i x0 = p0 ? *reinterpret_cast<const v4i*>(p0 + cc * 8) : v4i{0, 0, 0, 0};
-        v4i x1 = p1 ? *reinterpret_cast<const v4i*>(p1 + cc * 8) : v4i{0, 0, 0, 0};
-        *reinterpret_cast<v4i*>(k_s + r0 * KROW + cc * 8) = x0;
-        *reinterpret_cast<v4i*>(k_s + r1 * KROW + cc * 8) = x1;
-        const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&x0);
-        const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&x1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t pair = static_cast<uint32_t>(e0[e]) | (static_cast<uint32_t>(e1[e]) << 16);
-          *reinterpret_cast<uint32_t*>(vt_s + (cc * 8 + e) * kVtStride + r0) = pair;
-        }
-      }
-    }
-    __syncthreads();
+    const uint8_t* tile = kv_s + (tt % kRing) * TS;
 
     if (wave_active) {
-      // S^T tile: rows = 32 keys (two 16-row M tiles), columns = 16 heads
+      // S^T tile: rows = 32 keys (two 16-row M tiles), columns = 16 heads.
+      // M-tile mt row i holds key mt*16 + i/4 + 4*(i%4), so the four keys a
+      // lane group later needs for one transposed V read are 4 rows apart.
       v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
+      const int krow = (col >> 2) + 4 * (col & 3);
+      const uint8_t* k0p = tile + row_off(krow) + grp * 16;
+      const uint8_t* k1p = tile + row_off(16 + krow) + grp * 16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const v8bf a0 = as_v8bf(*reinterpret_cast<const v4i*>(k_s + col * KROW + ks * 32 + grp * 8));
-        const v8bf a1 = as_v8bf(*reinterpret_cast<const v4i*>(k_s + (16 + col) * KROW + ks * 32 + grp * 8));
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+      for (int kg = 0; kg < KS; kg += 4) {
+#pragma unroll
+        for (int ks = kg; ks < kg + 4 && ks < KS; ++ks) {
+          const v8bf a0 = as_v8bf(*reinterpret_cast<const v4i*>(k0p + ks * 64));
+          const v8bf a1 = as_v8bf(*reinterpret_cast<const v4i*>(k1p + ks * 64));
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // lane holds keys grp*4 + r (s0) and 16 + grp*4 + r (s1) of head col
+      // lane (head col, group grp) now holds keys grp + 4r (s0[r]) and
+      // 16 + grp + 4r (s1[r]) of the tile
       float lg[8];
       float tmax = neg_inf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool v0 = rowptr_s[grp * 4 + r] != nullptr;
-        const bool v1 = rowptr_s[16 + grp * 4 + r] != nullptr;
-        lg[r] = v0 ? s0[r] * a.scale_log2 : neg_inf;
-        lg[4 + r] = v1 ? s1[r] * a.scale_log2 : neg_inf;
+        const int ja = tt * kTile + grp + 4 * r, jb = ja + 16;
+        lg[r] = ja < n_valid ? s0[r] * a.scale_log2 : neg_inf;
+        lg[4 + r] = jb < n_valid ? s1[r] * a.scale_log2 : neg_inf;
         tmax = fmaxf(tmax, fmaxf(lg[r], lg[4 + r]));
       }
       tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
       tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == neg_inf) ? 0.0f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      // the reference max only moves when the tile max passes it by more than
+      // kSlack (probabilities then stay <= 2^kSlack), so the accumulator is
+      // rescaled on few tiles
+      const bool grow = tmax > m_run + kSlack;
+      if (__ballot(grow) != 0ull) {
+        const float m_new = grow ? tmax : m_run;
+        const float alpha = (m_run == neg_inf) ? 0.0f : exp2f(m_run - m_new);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o_acc[dt] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == neg_inf) ? 0.0f : m_run;
       float psum = 0.0f;
       uint16_t pb[8];
 #pragma unroll
@@ -242,30 +342,41 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnArgs a) {
       }
       psum += shfl_xor_f(psum, 16);
       psum += shfl_xor_f(psum, 32);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run += psum;
       const v8bf pf = as_v8bf(*reinterpret_cast<v4i*>(pb));
+      // V^T operand with transposed LDS reads: in lane group g, source lane
+      // 4e + q points at 8 bytes of key row (g + 4e) [then 16 + g + 4e],
+      // channels n0 + 4q .. +3; lane i of the group receives those rows'
+      // channel n0 + i -- the keys P^T holds in elements e and 4 + e.
+      const int e_src = (lane & 15) >> 2, q_src = lane & 3;
+      const uint8_t* v0p = tile + row_off(grp + 4 * e_src) + q_src * 8;
+      const uint8_t* v1p = tile + row_off(16 + grp + 4 * e_src) + q_src * 8;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        o_acc[dt] *= alpha;
-        const uint16_t* vrow = vt_s + (dt * 16 + col) * kVtStride + grp * 4;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const v4i va = v4i{static_cast<int>(lo.x), static_cast<int>(lo.y),
-                           static_cast<int>(hi.x), static_cast<int>(hi.y)};
-        o_acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(va), pf, o_acc[dt], 0, 0, 0);
+      for (int dg = 0; dg < DT; dg += 8) {
+#pragma unroll
+        for (int dt = dg; dt < dg + 8 && dt < DT; ++dt) {
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(v0p + dt * 32));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(v1p + dt * 32));
+          const v8s va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o_acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, va), pf,
+                                                               o_acc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();
+    __syncthreads();               // every wave is done with this slot
+    if (tt + kRing < ntiles) issue(tt + kRing);
   }
 
   if (tid == 0 && err_s) flag_error(a.err, err_s);
-  if (b < 0 && split == 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
+  if (b < 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
   if (!wave_active) return;
   const int h = h0 + col;
   if (h >= a.H) return;
 
-  if (a.splits == 1) {
+  {
     const float sink2 = a.sink[h] * kLog2e;
     const float M = fmaxf(m_run, sink2);
     const float corr = (m_run == neg_inf) ? 0.0f : exp2f(m_run - M);
@@ -284,87 +395,380 @@ __global__ void __launch_bounds__(kAttnThreads, 2) attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint2*>(orow + d) = w;
     }
     if (a.lse && grp == 0) a.lse[static_cast<long long>(t) * a.H + h] = (M + log2f(Z)) * kLn2;
-  } else {
-    const long long slot = (static_cast<long long>(t) * a.splits + split) * a.H + h;
-    float* po = a.part_o + slot * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<v4f*>(po + dt * 16 + grp * 4) = o_acc[dt];
-    if (grp == 0) a.part_ml[slot] = make_float2(m_run, l_run);
   }
 }
 
-// Combine split partials with the sink: one work-group per (row, head).
+// ---------------------------------------------------------------------------
+// Decode schedule: a work-group owns one (row, 16-head group, 128-entry span of
+// the key list).  Each of its four waves gathers its own 32 rows into a private
+// LDS slot with direct-to-LDS loads -- all at once, so a work-group pays one
+// memory latency -- and runs one 32-key tile (S^T, softmax, P*V) for the
+// group's 16 heads; no key byte is read from LDS by more than one wave.  The
+// four per-wave softmax states are then combined in LDS.  With one span the
+// work-group writes the output rows directly; with several it writes an FP32
+// partial (16 heads x D, relative to its own max) for the merge kernel.
+constexpr int kSpan = kAttnWaves * kTile;   // list entries per decode work-group
+
+template <int D>
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int RB = 2 * D;
+  constexpr int NC = D / 8;
+  constexpr int RPI = 64 / NC;
+  constexpr int GS = RPI * RB + 16;
+  constexpr int TS = (kTile / RPI) * GS;     // one wave's slot: 32 rows
+  constexpr int OSTR = D + 4;                // padded FP32 row of the per-wave output
+  constexpr int SS = (TS > 16 * OSTR * 4) ? TS : 16 * OSTR * 4;   // slot bytes
+  __shared__ __attribute__((aligned(16))) uint8_t slot_s[kAttnWaves * SS];
+  __shared__ uint32_t row_s[kSpan];
+  __shared__ float ml_s[kAttnWaves][2][16];
+  __shared__ int scan_s[kAttnWaves];
+  __shared__ int err_s;
+
+  const int HG = (a.H + 15) / 16;
+  const int L = blockIdx.x;
+  const int item = (L & 7) * a.items_per_xcd + (L >> 3);
+  const int hg = item % HG;
+  const int ts = item / HG;                 // t * splits + split
+  const int t = ts / a.splits;
+  const int split = ts % a.splits;
+  if (t >= a.num_tokens) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int h = hg * 16 + col;
+  const bool hv = h < a.H;
+  if (tid == 0) err_s = 0;
+
+  const int b = owner_request(a.qsl, a.B, t);
+  const int p = a.positions[t];
+  const int nv = visible_count(p, a.ratio);
+  int w_len = 0, w_lo = 0;
+  if (b >= 0 && p >= 0 && a.window > 0) {
+    w_lo = max(0, p - a.window + 1);
+    w_len = p - w_lo + 1;
+  }
+  const int list_len = (b >= 0) ? (w_len + a.k) : 0;
+  const int i_begin = split * kSpan;
+  const int n_my = max(0, min(list_len, i_begin + kSpan) - i_begin);
+  __syncthreads();
+
+  // ---- resolve this span through the block tables; compact valid rows
+  int n_valid = 0;
+  {
+    const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
+    int ebits = 0;
+    uint32_t rr = kNoRow;
+    const int j = tid;
+    if (j < n_my) {
+      const int i = i_begin + j;
+      if (i < w_len) {
+        const long long r = page_row(a.win_bt + static_cast<long long>(b) * a.max_win_blocks,
+                                     a.max_win_blocks, a.num_win_blocks, w_lo + i);
+        if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
+      } else {
+        const int c = topk_row[i - w_len];
+        if (c >= 0) {
+          if (c >= nv) {
+            ebits |= CSA_EFLAG_TOPK_RANGE;
+          } else {
+            const long long r = page_row(a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks,
+                                         a.max_cmp_blocks, a.num_cmp_blocks, c);
+            if (r >= 0) rr = static_cast<uint32_t>(r); else ebits |= CSA_EFLAG_BLOCK_RANGE;
+          }
+        }
+      }
+    }
+    if (ebits && hg == 0) atomicOr(&err_s, ebits);
+    int total = 0;
+    const int slot = block_excl_scan(rr != kNoRow ? 1 : 0, scan_s, &total);
+    if (rr != kNoRow) row_s[slot] = rr;
+    n_valid = total;
+  }
+  __syncthreads();
+
+  // ---- this wave's 32 rows straight into its LDS slot (masked rows read the
+  //      query: finite bytes that P = 0 keeps out)
+  uint8_t* myslot = slot_s + wave * SS;
+  const int j0 = wave * kTile;
+  {
+    const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
+#pragma unroll
+    for (int ins = 0; ins < kTile / RPI; ++ins) {
+      const int j = j0 + ins * RPI + lane / NC;
+      const uint32_t rr = (j < n_valid) ? row_s[j] : kNoRow;
+      const uint8_t* src = dummy;
+      if (rr != kNoRow)
+        src = reinterpret_cast<const uint8_t*>(
+            (rr & kWinBit) ? a.win_kv + static_cast<long long>(rr & ~kWinBit) * D
+                           : a.cmp_kv + static_cast<long long>(rr) * D);
+      if (j0 < n_valid)
+        __builtin_amdgcn_global_load_lds(
+            src + (lane % NC) * 16, (__attribute__((address_space(3))) void*)(myslot + ins * GS),
+            16, 0, 0);
+    }
+  }
+  auto row_off = [](int r) { return (r / RPI) * GS + (r % RPI) * RB; };
+
+  // ---- query fragments of head h (B operand of S^T), rotated on the rope span
+  v8bf qf[KS];
+  {
+    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
+    const float* rc = a.rope_cos + static_cast<long long>(t) * a.half_rope;
+    const float* rs = a.rope_sin + static_cast<long long>(t) * a.half_rope;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = ks * 32 + grp * 8;
+      v4i raw = hv ? *reinterpret_cast<const v4i*>(qrow + d0) : v4i{0, 0, 0, 0};
+      const int r0 = d0 - a.rope_offset;
+      if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
+        uint16_t e[8];
+        *reinterpret_cast<v4i*>(e) = raw;
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          const int rr = r0 + 2 * pr;
+          if (rr >= 0 && rr < 2 * a.half_rope) {
+            const float c = rc[rr >> 1], sn = rs[rr >> 1];
+            const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
+            e[2 * pr] = f32_to_bf16(x * c - y * sn);
+            e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
+          }
+        }
+        raw = *reinterpret_cast<v4i*>(e);
+      }
+      qf[ks] = as_v8bf(raw);
+    }
+  }
+
+  const float neg_inf = -__builtin_huge_valf();
+  float m_w = neg_inf, l_w = 0.0f;
+  v4f o_acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's rows have landed in its slot
+
+  if (j0 < n_valid) {
+    const uint8_t* tile = myslot;
+    v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
+    v4f s2 = v4f{0.f, 0.f, 0.f, 0.f}, s3 = v4f{0.f, 0.f, 0.f, 0.f};
+    const int krow = (col >> 2) + 4 * (col & 3);
+    const uint8_t* k0p = tile + row_off(krow) + grp * 16;
+    const uint8_t* k1p = tile + row_off(16 + krow) + grp * 16;
+#pragma unroll
+    for (int kg = 0; kg < KS; kg += 4) {
+#pragma unroll
+      for (int ks = kg; ks < kg + 4 && ks < KS; ks += 2) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_v8bf(*reinterpret_cast<const v4i*>(k0p + ks * 64)), qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_v8bf(*reinterpret_cast<const v4i*>(k1p + ks * 64)), qf[ks], s1, 0, 0, 0);
+        if (ks + 1 < KS) {
+          s2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_v8bf(*reinterpret_cast<const v4i*>(k0p + (ks + 1) * 64)), qf[ks + 1], s2, 0, 0, 0);
+          s3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              as_v8bf(*reinterpret_cast<const v4i*>(k1p + (ks + 1) * 64)), qf[ks + 1], s3, 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    s0 += s2;
+    s1 += s3;
+    float lg[8];
+    float tmax = neg_inf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ja = j0 + grp + 4 * r, jb = ja + 16;
+      lg[r] = ja < n_valid ? s0[r] * a.scale_log2 : neg_inf;
+      lg[4 + r] = jb < n_valid ? s1[r] * a.scale_log2 : neg_inf;
+      tmax = fmaxf(tmax, fmaxf(lg[r], lg[4 + r]));
+    }
+    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+    m_w = tmax;   // finite: the wave has at least one valid row
+    float psum = 0.0f;
+    uint16_t pb[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float pj = exp2f(lg[jj] - m_w);
+      psum += pj;
+      pb[jj] = f32_to_bf16(pj);
+    }
+    psum += shfl_xor_f(psum, 16);
+    psum += shfl_xor_f(psum, 32);
+    l_w = psum;
+    const v8bf pf = as_v8bf(*reinterpret_cast<v4i*>(pb));
+    const int e_src = (lane & 15) >> 2, q_src = lane & 3;
+    const uint8_t* v0p = tile + row_off(grp + 4 * e_src) + q_src * 8;
+    const uint8_t* v1p = tile + row_off(16 + grp + 4 * e_src) + q_src * 8;
+#pragma unroll
+    for (int dg = 0; dg < DT; dg += 8) {
+#pragma unroll
+      for (int dt = dg; dt < dg + 8 && dt < DT; ++dt) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(v0p + dt * 32));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(v1p + dt * 32));
+        const v8s va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o_acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, va), pf,
+                                                             o_acc[dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // ---- combine the four waves: each parks (m, l, O) in LDS (its own slot)
+  {
+    float* ow = reinterpret_cast<float*>(myslot);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<v4f*>(ow + col * OSTR + dt * 16 + grp * 4) = o_acc[dt];
+    if (grp == 0) {
+      ml_s[wave][0][col] = m_w;
+      ml_s[wave][1][col] = l_w;
+    }
+  }
+  __syncthreads();
+  if (tid == 0 && err_s) flag_error(a.err, err_s);
+  if (b < 0 && split == 0 && hg == 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
+  {
+    // thread (head hh, lane c4) combines channels c4*4 + 64m: consecutive
+    // lanes touch consecutive 16-byte LDS words and output bytes
+    const int hh = tid >> 4;
+    const int c4 = (tid & 15) * 4;
+    const int head = hg * 16 + hh;
+    if (head < a.H) {
+      float mw[kAttnWaves], e[kAttnWaves];
+      float M = neg_inf;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        mw[w] = ml_s[w][0][hh];
+        M = fmaxf(M, mw[w]);
+      }
+      float Lsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        e[w] = (mw[w] == neg_inf) ? 0.0f : exp2f(mw[w] - M);
+        Lsum += ml_s[w][1][hh] * e[w];
+      }
+      float scale = 1.0f;
+      if (a.splits == 1) {
+        const float sink2 = a.sink[head] * kLog2e;
+        const float Mt = fmaxf(M, sink2);
+        const float corr = (M == neg_inf) ? 0.0f : exp2f(M - Mt);
+        const float Z = Lsum * corr + exp2f(sink2 - Mt);
+        scale = corr / Z;
+        if (a.lse && c4 == 0) a.lse[static_cast<long long>(t) * a.H + head] = (Mt + log2f(Z)) * kLn2;
+      } else if (c4 == 0) {
+        a.part_ml[static_cast<long long>(ts) * a.H + head] = make_float2(M, Lsum);
+      }
+#pragma unroll
+      for (int c = c4; c < D; c += 64) {
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w)
+          acc += *reinterpret_cast<const v4f*>(
+                     reinterpret_cast<const float*>(slot_s + w * SS) + hh * OSTR + c) * e[w];
+        if (a.splits == 1) {
+          acc *= scale;
+          uint2 pk;
+          pk.x = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+          pk.y = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+          *reinterpret_cast<uint2*>(a.out + (static_cast<long long>(t) * a.H + head) * D + c) = pk;
+        } else {
+          *reinterpret_cast<v4f*>(a.part_o + (static_cast<long long>(ts) * a.H + head) * D + c) = acc;
+        }
+      }
+    }
+  }
+}
+
+// Combine split partials with the sink: one work-group per (row, head) over
+// partials laid out [t][split][head][D]; the split weights are formed once in
+// LDS so the partial reads pipeline.
+constexpr int kMaxSplits = 64;
+
 template <int D>
 __global__ void __launch_bounds__(128) attn_merge_kernel(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const float* __restrict__ sink, int splits, int H, int num_tokens,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float mz_s[2];
   const int t = blockIdx.x / H;
   const int h = blockIdx.x % H;
   if (t >= num_tokens) return;
   const float neg_inf = -__builtin_huge_valf();
-  const long long base = static_cast<long long>(t) * splits * H + h;
-  float M = sink[h] * kLog2e;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[base + static_cast<long long>(s) * H].x);
-  float Z = exp2f(sink[h] * kLog2e - M);
-  for (int s = 0; s < splits; ++s) {
-    const float2 ml = part_ml[base + static_cast<long long>(s) * H];
-    if (ml.x != neg_inf) Z += ml.y * exp2f(ml.x - M);
+  const long long base = static_cast<long long>(t) * splits;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float2 ml = make_float2(neg_inf, 0.0f);
+    if (lane < splits) ml = part_ml[(base + lane) * H + h];
+    const float sink2 = sink[h] * kLog2e;
+    float M = ml.x;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    M = fmaxf(M, sink2);
+    const float e = (ml.x == neg_inf) ? 0.0f : exp2f(ml.x - M);
+    float z = ml.y * e;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+    z += exp2f(sink2 - M);
+    if (lane < splits) w_s[lane] = e / z;
+    if (lane == 0) {
+      mz_s[0] = M;
+      mz_s[1] = z;
+    }
   }
-  const float invZ = 1.0f / Z;
+  __syncthreads();
   for (int d = threadIdx.x * 4; d < D; d += 128 * 4) {
     v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-      const long long slot = base + static_cast<long long>(s) * H;
-      const float mx = part_ml[slot].x;
-      if (mx == neg_inf) continue;
-      const float w = exp2f(mx - M) * invZ;
-      const v4f v = *reinterpret_cast<const v4f*>(part_o + slot * D + d);
-      acc += v * w;
-    }
+    for (int s = 0; s < splits; ++s)
+      acc += *reinterpret_cast<const v4f*>(part_o + ((base + s) * H + h) * D + d) * w_s[s];
     uint2 pk;
     pk.x = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
     pk.y = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
     *reinterpret_cast<uint2*>(out + (static_cast<long long>(t) * H + h) * D + d) = pk;
   }
-  if (lse && threadIdx.x == 0) lse[static_cast<long long>(t) * H + h] = (M + log2f(Z)) * kLn2;
+  if (lse && threadIdx.x == 0) lse[static_cast<long long>(t) * H + h] = (mz_s[0] + log2f(mz_s[1])) * kLn2;
 }
 
-// Split plan shared by the launcher and the workspace helper: enough
-// work-groups to spread a small decode batch over the chip, spans long enough
-// (>= 128 rows) that FP32 partials stay smaller than the rows they replace.
+// Schedule shared by the launcher and the workspace helper.  Prefill and
+// large decode batches walk each row's whole key list in one work-group (the
+// ring kernel, no partials); small decode batches split the list into
+// kSpan-entry spans per 16-head group (the decode kernel) and merge.
 struct SplitPlan {
+  bool ring;
   int splits;
-  int split_len;
 };
 
 SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   const int lmax = max(1, window + k);
-  if (prefill || T >= 256) return SplitPlan{1, ((lmax + kTile - 1) / kTile) * kTile};
-  int by_len = (lmax + 127) / 128;
-  int want = (512 + T - 1) / max(T, 1);
-  int splits = max(1, min(by_len, want));
-  int len = (lmax + splits - 1) / splits;
-  len = ((len + kTile - 1) / kTile) * kTile;
-  splits = (lmax + len - 1) / len;
-  return SplitPlan{splits, len};
+  if (prefill || T >= 256) return SplitPlan{true, 1};
+  return SplitPlan{false, (lmax + kSpan - 1) / kSpan};
 }
 
 template <int D>
-int launch_attn(const AttnArgs& in, hipStream_t st) {
+int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
   AttnArgs a = in;
-  const long long items = static_cast<long long>(a.num_tokens) * a.splits;
+  const long long items = static_cast<long long>(a.num_tokens) * a.splits *
+                          (ring ? 1 : (a.H + 15) / 16);
   a.items_per_xcd = static_cast<int>((items + 7) / 8);
   const long long grid = static_cast<long long>(a.items_per_xcd) * 8;
   if (grid > 0x7fffffffll) return CSA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0, st,
-                     a);
+  if (ring)
+    hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(static_cast<unsigned>(grid)),
+                       dim3(kAttnThreads), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   if (a.splits > 1) {
-    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3(static_cast<unsigned>(a.num_tokens * a.H)),
-                       dim3(128), 0, st, a.part_o, a.part_ml, a.sink, a.splits, a.H, a.num_tokens,
-                       a.out, a.lse);
+    const long long mgrid = static_cast<long long>(a.num_tokens) * a.H;
+    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3(static_cast<unsigned>(mgrid)), dim3(128), 0, st,
+                       a.part_o, a.part_ml, a.sink, a.splits, a.H, a.num_tokens, a.out, a.lse);
     if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   }
   return CSA_OK;
@@ -395,6 +799,11 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
        reinterpret_cast<uintptr_t>(cmp_kv) | reinterpret_cast<uintptr_t>(win_kv)) & 15)
     return CSA_ERR_UNSUPPORTED;
+  // the key list lives in LDS; pool rows are packed in 31 bits
+  if (window + k > kMaxSplit) return CSA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(num_cmp_blocks) * kPage >= (1ll << 31) ||
+      static_cast<long long>(num_win_blocks) * kPage >= (1ll << 31))
+    return CSA_ERR_UNSUPPORTED;
   const SplitPlan plan = plan_splits(num_tokens, k, window, prefill);
   AttnArgs a{};
   a.q = q;
@@ -424,7 +833,6 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   a.out = out;
   a.lse = lse;
   a.splits = plan.splits;
-  a.split_len = plan.split_len;
   a.err = err;
   if (plan.splits > 1) {
     const size_t need = static_cast<size_t>(num_tokens) * plan.splits * H * (D + 2) * sizeof(float);
@@ -436,10 +844,10 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (D) {
-    case 64: return launch_attn<64>(a, st);
-    case 128: return launch_attn<128>(a, st);
-    case 256: return launch_attn<256>(a, st);
-    default: return launch_attn<512>(a, st);
+    case 64: return launch_attn<64>(a, plan.ring, st);
+    case 128: return launch_attn<128>(a, plan.ring, st);
+    case 256: return launch_attn<256>(a, plan.ring, st);
+    default: return launch_attn<512>(a, plan.ring, st);
   }
 }
 

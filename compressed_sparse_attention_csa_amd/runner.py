@@ -54,7 +54,8 @@ class CsaStep:
         self.lse = torch.empty((T, H), **f32) if with_lse else None
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         tw = _lib.csa_topk_workspace_bytes(T, self.score_stride, self.k)
-        self.topk_ws = torch.empty(max(tw, 1), dtype=torch.uint8, device=dev) if tw else None
+        # zero-filled once; the library leaves it zero-filled after every call
+        self.topk_ws = torch.zeros(tw, dtype=torch.uint8, device=dev) if tw else None
         aw = 0 if prefill else _lib.csa_sparse_attn_workspace_bytes(T, H, D, self.k, self.window)
         self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=dev) if aw else None
 

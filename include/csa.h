@@ -147,10 +147,18 @@ int csa_index_score(const int8_t* q_idx, const float* q_scale, const float* head
  *              then -1
  *   topk_val   FP32 [T, k] or NULL: the chosen scores, -inf for padding
  *   workspace  device scratch of csa_topk_workspace_bytes(T, score_stride, k)
- *              bytes (may be NULL when that size is 0)
+ *              bytes (may be NULL when that size is 0). It must be zero-filled
+ *              before its first use; every call restores the zero state it
+ *              relies on (histograms and counters), so one workspace serves any
+ *              number of calls on one stream (calls that overlap on different
+ *              streams need separate workspaces).
  *
  * Ranking: score descending, ties to the lower position; -0.0 equals +0.0;
- * NaN ranks below every number. Supported: 1 <= k <= 4096.
+ * NaN ranks below every number. Supported: 1 <= k <= 4096, score_stride a
+ * multiple of 4, scores 16-byte aligned. Rows whose span exceeds 32,768 use a
+ * multi-work-group path (histogram, candidate filter, final select); with more
+ * than 8,192 candidates in the threshold bin (massive exact ties) that row
+ * falls back to an exact whole-row pass.
  */
 size_t csa_topk_workspace_bytes(int32_t T, int64_t score_stride, int32_t k);
 int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions,
@@ -188,8 +196,9 @@ int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions
  * -> CSA_EFLAG_META, treated as empty; a selected entry >= (p + 1) / ratio ->
  * CSA_EFLAG_TOPK_RANGE, left out; a window or selected row whose page is past
  * the table or names an invalid block -> CSA_EFLAG_BLOCK_RANGE, left out.
- * Supported: 1 <= H <= 64, D in {64, 128, 256, 512}, rope_dim even,
- * rope_offset + rope_dim <= D, window >= 0, 0 <= k <= 4096.
+ * Supported: 1 <= H <= 64, D in {64, 128, 256, 512}, rope_dim and rope_offset
+ * even, rope_offset + rope_dim <= D, window >= 0, 0 <= k <= 4096,
+ * window + k <= 4224, pools of fewer than 2^31 rows.
  * Arithmetic: the rotated query and the probabilities are rounded to BF16 as
  * MFMA operands; logits, softmax and accumulation are FP32.
  */
