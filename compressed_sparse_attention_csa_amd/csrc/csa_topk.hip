@@ -6,26 +6,37 @@
 // by the number of visible keys).  Ranking is score descending, ties to the
 // lower position, NaN last (scores map to order-preserving 32-bit keys).
 //
-// Short rows (visible span <= 32,768): one work-group of 1024 threads per row.
-// Each thread holds a contiguous run of up to 32 keys in registers; an
-// MSB-first radix select (8-bit digits, per-wave LDS histograms, stopping as
-// soon as the threshold digit holds exactly the count still needed) finds the
-// cut; a block scan in position order then writes the chosen positions
+// Selection core (one work-group over keys held in registers): refine a
+// histogram whose bins are linear in score VALUE over the range [min, max] of
+// the keys still in play, so the bins spread the keys whatever the shape of
+// the score distribution (bit-prefix bins pile a bell-shaped row into a few
+// exponent bins and serialise the LDS atomics).  Each pass finds the bin that
+// holds the m-th best key; keys above it are chosen, keys below it drop out,
+// and the pass repeats inside that bin until its count is exactly what is
+// still needed or all of its keys are equal (then the lowest positions win).
+// NaN, -inf and +inf get bins of their own at the ends, and a pass whose value
+// bins would not separate its min from its max bins the keys' integer codes
+// instead, so every pass shrinks the set in play.  Each thread holds a
+// contiguous run of positions, so a block scan writes the chosen positions
 // already ascending -- no sort.
 //
-// Long rows (up to the 1,048,576-position context): three kernels over the
-// row, which the indexer has just left in L2 / Infinity Cache.
-//   hist:   work-groups over 8,192-score chunks add a 4,096-bin histogram of
-//           the top 12 key bits into the row's global histogram; the last
-//           work-group of a row (device-scope counter) finds the 12-bit bin
-//           that holds the k-th key, records it, and clears the histogram.
-//   filter: work-groups over chunks append every key in or above that bin
-//           (typically ~k + a few hundred) to the row's candidate list.
-//   final:  one work-group per row loads the candidates into LDS, radix
-//           selects the exact cut (ties by position), bitonic-sorts the chosen
-//           positions and clears the row's counters.
-// The histogram and counters of the workspace are zero on first use and every
-// call leaves them zero again; candidate slots are always written before read.
+// Rows with span <= 32,768: one work-group per row, keys straight from the
+// score row.  Longer rows (up to the 1,048,576-position context): four
+// kernels over the row, which the indexer has just left in L2 / MALL:
+//   range:  work-groups over 8,192-score chunks fold the row's finite min and
+//           max into two counters;
+//   hist:   they add a 4,096-bin value histogram into the row's global one;
+//   filter: each work-group finds the bin of the m-th key from that histogram
+//           and keeps every key in or above it (typically m plus a handful),
+//           each wave writing one position-ordered segment;
+//   final:  one work-group per row gathers the segments in position order
+//           into LDS, runs the selection core on them and clears the row's
+//           histogram and counters.
+// No work-group waits on another inside a kernel, so no device-scope fences.
+// Rows of a long launch with span <= 8,192 skip the first three kernels; the
+// final kernel selects on the row itself.  If more than 8,192 keys tie into
+// the threshold bin, the final kernel falls back to an exact radix select
+// over the whole row.
 #include "csa_common.h"
 
 namespace csa {
@@ -33,32 +44,52 @@ namespace csa {
 namespace {
 
 constexpr int kMaxK = 4096;
-constexpr int kSmallMax = 32768;     // rows up to this span take the one-group path
-constexpr int kSThreads = 1024;
-constexpr int kSPer = kSmallMax / kSThreads;  // keys per thread
-constexpr int kBins = 4096;          // 12-bit first-level histogram
-constexpr int kChunk = 8192;         // scores per work-group in hist / filter
+constexpr int kSmallMax = 32768;     // spans up to this use the one-group kernel
+constexpr int kSBins = 2048;         // selection-core histogram bins
+constexpr int kChunk = 8192;         // scores per work-group in the long-row kernels
 constexpr int kLThreads = 256;
+constexpr int kLWaves = kLThreads / 64;
+constexpr int kSub = kChunk / kLWaves;   // contiguous positions per wave
+constexpr int kLLoads = kSub / 256;      // 16-byte loads per lane
+constexpr int kLBins = 512;          // long-row histogram bins
+constexpr int kLCap = 2048;          // threshold-bin keys compacted into LDS
+constexpr int kRankMax = 256;        // up to this many are ranked directly
 constexpr int kCap = 8192;           // candidate slots per row
-constexpr int kMetaWords = 8;        // done counter, candidate count, bin, above, ...
-constexpr int kPerThread4 = kChunk / (4 * kLThreads);  // float4 loads per thread
+constexpr int kFThreads = 1024;      // final kernel
+constexpr int kFPer = kCap / kFThreads;
+constexpr long long kMaxStride = 1ll << 24;   // long rows: <= 8,192 segments
+constexpr int kMetaWords = 8;
+constexpr int kMetaMax = 0;          // max finite key
+constexpr int kMetaMinInv = 1;       // max of ~(finite key)
+constexpr int kMetaCount = 2;        // candidates appended
+constexpr uint32_t kKeyNegInf = 0x007fffffu;
+constexpr uint32_t kKeyPosInf = 0xff800000u;
 
 struct Workspace {
-  uint32_t* hist;   // [T][kBins]
+  uint32_t* hist;   // [T][kLBins]
   uint32_t* meta;   // [T][kMetaWords]
+  uint2* seg;       // [T][nseg] (first candidate slot, count)
   uint2* cand;      // [T][kCap] (key, position)
+  int nseg;         // segments per row: chunks * waves
 };
 
-__host__ __device__ inline size_t ws_bytes(int T) {
-  return static_cast<size_t>(T) * (kBins + kMetaWords) * sizeof(uint32_t) +
+inline int segs_for(long long stride) {
+  return static_cast<int>(((stride + kChunk - 1) / kChunk) * kLWaves);
+}
+
+inline size_t ws_bytes(int T, long long stride) {
+  return static_cast<size_t>(T) * (kLBins + kMetaWords) * sizeof(uint32_t) +
+         static_cast<size_t>(T) * segs_for(stride) * sizeof(uint2) +
          static_cast<size_t>(T) * kCap * sizeof(uint2);
 }
 
-__host__ __device__ inline Workspace ws_layout(void* base, int T) {
+inline Workspace ws_layout(void* base, int T, long long stride) {
   Workspace w;
+  w.nseg = segs_for(stride);
   w.hist = static_cast<uint32_t*>(base);
-  w.meta = w.hist + static_cast<size_t>(T) * kBins;
-  w.cand = reinterpret_cast<uint2*>(w.meta + static_cast<size_t>(T) * kMetaWords);
+  w.meta = w.hist + static_cast<size_t>(T) * kLBins;
+  w.seg = reinterpret_cast<uint2*>(w.meta + static_cast<size_t>(T) * kMetaWords);
+  w.cand = w.seg + static_cast<size_t>(T) * w.nseg;
   return w;
 }
 
@@ -67,6 +98,367 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN: below everything
   if (u == 0x80000000u) u = 0u;                      // -0.0 ranks as +0.0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ bool key_finite(uint32_t k) { return k > kKeyNegInf && k < kKeyPosInf; }
+
+// Monotone map from keys to nb bins: NaN -> 0, -inf -> 1, +inf -> nb - 1,
+// finite keys -> 2 .. nb - 2, linear in value over [lo, hi] (or, when that
+// does not separate lo from hi in float arithmetic, linear in key code).
+struct Binner {
+  bool by_value;
+  float lo_h;      // lo / 2 (halved so hi - lo cannot overflow)
+  float scale;
+  uint32_t klo;
+  float kscale;
+  int nb;
+  __device__ __forceinline__ int operator()(uint32_t key) const {
+    // branch-free: non-finite keys produce a finite d (clamped) and are then
+    // overridden by their own bins
+    const float dv = fmaf(key_value(key), 0.5f, -lo_h) * scale;
+    const float dk = static_cast<float>(key - klo) * kscale;
+    const float d = fminf(fmaxf(by_value ? dv : dk, 0.0f), static_cast<float>(nb - 4));
+    int b = 2 + static_cast<int>(d);
+    b = key == kKeyPosInf ? nb - 1 : b;
+    b = key == kKeyNegInf ? 1 : b;
+    b = key == 0u ? 0 : b;
+    return b;
+  }
+};
+
+// kfmin / kfmax: smallest and largest finite key in play (kfmin > kfmax when
+// there is none).
+__device__ __forceinline__ Binner make_binner(uint32_t kfmin, uint32_t kfmax, int nb) {
+  Binner b;
+  b.nb = nb;
+  b.by_value = false;
+  b.lo_h = 0.0f;
+  b.scale = 0.0f;
+  b.klo = kfmin;
+  b.kscale = 0.0f;
+  if (kfmin >= kfmax) return b;   // at most one finite value: one finite bin
+  // any positive scale keeps the map monotone, so approximate reciprocals do
+  const float top = static_cast<float>(nb - 4);
+  b.kscale = top * __builtin_amdgcn_rcpf(static_cast<float>(kfmax - kfmin));
+  const float lo = key_value(kfmin), hi = key_value(kfmax);
+  b.lo_h = lo * 0.5f;
+  const float range_h = fmaf(hi, 0.5f, -b.lo_h);
+  const float sc = top * __builtin_amdgcn_rcpf(range_h);
+  if (range_h > 0.0f && sc < 3.0e38f) {
+    b.scale = sc;
+    b.by_value = true;
+    if (b(kfmin) == b(kfmax)) b.by_value = false;
+  }
+  return b;
+}
+
+// Wave-wide primitives on DPP row shifts and row broadcasts (gfx9 family):
+// a few dependent VALU ops instead of a chain of LDS permutes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = min(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(-1, static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// Exclusive scan over a work-group of NW waves.  `wsum` holds 2 * NW + 1
+// ints; wave 0 scans the wave totals, so every thread reads one prefix.
+// Back-to-back calls are safe: a call's writes to wsum are ordered after the
+// previous call's reads by its own barriers.
+template <int NW>
+__device__ int block_excl_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int tw = lane < NW ? wsum[lane] : 0;
+    const int pw = wave_incl_scan(tw);
+    if (lane < NW) wsum[NW + lane] = pw - tw;
+    if (lane == NW - 1) wsum[2 * NW] = pw;
+  }
+  __syncthreads();
+  if (total) *total = wsum[2 * NW];
+  return wsum[NW + wave] + incl - v;
+}
+
+// The work-group scans an NB-bin histogram from the top: thread t sums bins
+// [NB - (t+1)*PER, NB - t*PER) (consecutive threads, consecutive words), a
+// block scan orders the sums, and the one thread whose range holds the
+// need-th key writes that bin and the count strictly above it.
+template <int NB, int THREADS>
+__device__ void find_bin(const uint32_t* hist, int need, int* wsum, int* bin_out,
+                         int* above_out) {
+  constexpr int PER = NB / THREADS;
+  static_assert(PER >= 1 && NB % THREADS == 0, "bins per thread");
+  const int lo = NB - (static_cast<int>(threadIdx.x) + 1) * PER;
+  int h[PER];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    h[i] = static_cast<int>(hist[lo + i]);
+    s += h[i];
+  }
+  int run = block_excl_scan<THREADS / 64>(s, wsum, nullptr);
+  if (run < need && run + s >= need) {
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (run < need && run + h[i] >= need) {
+        *bin_out = lo + i;
+        *above_out = run;
+      }
+      run += h[i];
+    }
+  }
+  __syncthreads();
+}
+
+template <int THREADS>
+struct SelShared {
+  alignas(16) uint32_t hist[kSBins + 64];   // + one dummy bin per lane
+  // threshold-bin keys then their positions (position order); the whole-row
+  // path uses it as its selection buffer (kMaxK entries)
+  uint32_t list[2 * kLCap];
+  uint32_t red[4][THREADS / 64];
+  int wsum[2 * (THREADS / 64) + 1];
+  uint32_t mm[4];                           // block min / max results
+  int bsel[2];
+  uint32_t cut[2];                          // key and position of the m-th best
+  int sel_count;
+};
+static_assert(2 * kLCap >= kMaxK, "whole-row selection buffer");
+
+__device__ __forceinline__ uint32_t uniform_u(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
+// Block min / max of one u32 per thread (result uniform in every thread):
+// wave partials go to red[0..1], wave 0 combines them into res[0..1].
+template <int NW>
+__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t (*red)[NW],
+                                             uint32_t* res) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  lo = wave_min_u(lo);
+  hi = wave_max_u(hi);
+  if (lane == 0) {
+    red[0][wave] = lo;
+    red[1][wave] = hi;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t a = wave_min_u(lane < NW ? red[0][lane] : 0xffffffffu);
+    const uint32_t b = wave_max_u(lane < NW ? red[1][lane] : 0u);
+    if (lane == 0) {
+      res[0] = a;
+      res[1] = b;
+    }
+  }
+  __syncthreads();
+  lo = uniform_u(res[0]);
+  hi = uniform_u(res[1]);
+}
+
+// Refinement select (the path for a threshold bin too large for the LDS
+// list).  Thread-local keys key[0..nmine), positions ascending within the
+// thread and threads in position order; the m best over the work-group are
+// the `chosen` bits plus, of the `tie` bits (equal keys), the thread's first
+// `take`.
+template <int THREADS, int KPT>
+__device__ void block_select(const uint32_t (&key)[KPT], int nmine, int m, SelShared<THREADS>& sh,
+                             uint32_t& chosen, uint32_t& tie, int& take) {
+  static_assert(KPT <= 32, "one bit per key");
+  constexpr int NW = THREADS / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t live = nmine >= 32 ? 0xffffffffu : ((1u << nmine) - 1u);
+  chosen = 0u;
+  tie = 0u;
+  take = 0;
+  int rem = m;
+  for (;;) {
+    uint32_t kmin = 0xffffffffu, kmax = 0u, fmin = 0xffffffffu, fmax = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool lv = (live >> j) & 1u;
+      const uint32_t kk = key[j];
+      kmin = min(kmin, lv ? kk : 0xffffffffu);
+      kmax = max(kmax, lv ? kk : 0u);
+      const bool fin = lv && key_finite(kk);
+      fmin = min(fmin, fin ? kk : 0xffffffffu);
+      fmax = max(fmax, fin ? kk : 0u);
+    }
+    for (int i = tid; i < kSBins + 64; i += THREADS) sh.hist[i] = 0u;
+    block_minmax<NW>(kmin, kmax, sh.red, sh.mm);
+    block_minmax<NW>(fmin, fmax, sh.red + 2, sh.mm + 2);
+    if (kmin == kmax) {
+      // every key in play is equal: the rem lowest positions among them
+      const int eq = __popc(live);
+      const int eq_before = block_excl_scan<NW>(eq, sh.wsum, nullptr);
+      take = max(0, min(eq, rem - eq_before));
+      tie = live;
+      return;
+    }
+    const Binner bn = make_binner(fmin, fmax, kSBins);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      atomicAdd(&sh.hist[((live >> j) & 1u) ? bn(key[j]) : kSBins + lane], 1u);
+    __syncthreads();
+    find_bin<kSBins, THREADS>(sh.hist, rem, sh.wsum, &sh.bsel[0], &sh.bsel[1]);
+    const int b = sh.bsel[0];
+    rem -= sh.bsel[1];
+    const int cnt = static_cast<int>(sh.hist[b]);
+    uint32_t in_b = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int bb = bn(key[j]);
+      const bool lv = (live >> j) & 1u;
+      chosen |= (lv && bb > b) ? (1u << j) : 0u;
+      in_b |= (lv && bb == b) ? (1u << j) : 0u;
+    }
+    live = in_b;
+    if (cnt == rem) {
+      chosen |= live;
+      return;
+    }
+    __syncthreads();   // hist, bsel and red are rewritten by the next pass
+  }
+}
+
+// The cut of a refinement select: key and position of its worst winner.
+template <int THREADS, int KPT, typename PosFn>
+__device__ void cut_of_selection(const uint32_t (&key)[KPT], uint32_t chosen, uint32_t tie,
+                                 int take, SelShared<THREADS>& sh, PosFn pos) {
+  constexpr int NW = THREADS / 64;
+  uint32_t kmin = 0xffffffffu, dummy = 0u;
+  uint32_t win = chosen;
+  int taken = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (((tie >> j) & 1u) && taken < take) {
+      win |= 1u << j;
+      ++taken;
+    }
+    kmin = min(kmin, ((win >> j) & 1u) ? key[j] : 0xffffffffu);
+  }
+  block_minmax<NW>(kmin, dummy, sh.red, sh.mm);
+  uint32_t pmin = 0xffffffffu, pmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (((win >> j) & 1u) && key[j] == kmin) pmax = max(pmax, static_cast<uint32_t>(pos(j)));
+  __syncthreads();   // red is reused
+  block_minmax<NW>(pmin, pmax, sh.red + 2, sh.mm + 2);
+  if (threadIdx.x == 0) {
+    sh.cut[0] = kmin;
+    sh.cut[1] = pmax;
+  }
+  __syncthreads();
+}
+
+// Selection core: leaves in sh.cut the key and position of the m-th best
+// (score descending, position ascending) of the work-group's keys
+// key[0..nmine), whose positions pos(j) ascend within a thread and across
+// threads.  One value-histogram pass over every key finds the bin holding the
+// m-th best; that bin's keys are compacted into LDS in position order and,
+// when few, ranked directly, else refined as a list.
+template <int THREADS, int KPT, typename PosFn>
+__device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared<THREADS>& sh,
+                         PosFn pos) {
+  constexpr int NW = THREADS / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t fmin = 0xffffffffu, fmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool fin = j < nmine && key_finite(key[j]);
+    fmin = min(fmin, fin ? key[j] : 0xffffffffu);
+    fmax = max(fmax, fin ? key[j] : 0u);
+  }
+  for (int i = tid; i < kSBins + 64; i += THREADS) sh.hist[i] = 0u;
+  block_minmax<NW>(fmin, fmax, sh.red, sh.mm);
+  const Binner bn = make_binner(fmin, fmax, kSBins);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) atomicAdd(&sh.hist[j < nmine ? bn(key[j]) : kSBins + lane], 1u);
+  __syncthreads();
+  find_bin<kSBins, THREADS>(sh.hist, m, sh.wsum, &sh.bsel[0], &sh.bsel[1]);
+  const int b0 = sh.bsel[0];
+  const int rem = m - sh.bsel[1];
+  const int cnt = static_cast<int>(sh.hist[b0]);
+  if (cnt > kLCap) return false;   // massive ties: the caller selects on the whole row
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) c += (j < nmine && bn(key[j]) == b0) ? 1 : 0;
+  int o = block_excl_scan<NW>(c, sh.wsum, nullptr);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (j < nmine && bn(key[j]) == b0) {
+      sh.list[o] = key[j];
+      sh.list[kLCap + o] = static_cast<uint32_t>(pos(j));
+      ++o;
+    }
+  }
+  __syncthreads();
+  if (cnt <= kRankMax) {
+    // rank of element i among the bin: how many are better (larger key, or
+    // the same key at a lower position); the one of rank rem - 1 is the cut
+    if (tid < cnt) {
+      const uint32_t ki = sh.list[tid], pi = sh.list[kLCap + tid];
+      int r = 0;
+      for (int q = 0; q < cnt; ++q) {
+        const uint32_t kq = sh.list[q], pq = sh.list[kLCap + q];
+        r += (kq > ki || (kq == ki && pq < pi)) ? 1 : 0;
+      }
+      if (r == rem - 1) {
+        sh.cut[0] = ki;
+        sh.cut[1] = pi;
+      }
+    }
+    __syncthreads();
+    return true;
+  }
+  // a larger bin: refine on the list, LPT elements per thread in order
+  constexpr int LPT = kLCap / THREADS;
+  const int lbase = tid * LPT;
+  uint32_t lk[LPT];
+#pragma unroll
+  for (int j = 0; j < LPT; ++j) lk[j] = lbase + j < cnt ? sh.list[lbase + j] : 0u;
+  const int nl = max(0, min(LPT, cnt - lbase));
+  uint32_t chosen, tie;
+  int take;
+  block_select<THREADS, LPT>(lk, nl, rem, sh, chosen, tie, take);
+  cut_of_selection<THREADS, LPT>(lk, chosen, tie, take, sh,
+                                 [&](int j) { return static_cast<int>(sh.list[kLCap + lbase + j]); });
+  return true;
 }
 
 __device__ __forceinline__ int row_span(const int32_t* positions, int t, int ratio,
@@ -79,436 +471,146 @@ __device__ __forceinline__ int row_span(const int32_t* positions, int t, int rat
   return static_cast<int>(nv);
 }
 
-// Wave 0 finds the digit d such that, scanning `nb` bins (4 per lane) from the
-// top (descending) or bottom, the running count first reaches `need`; writes
-// d and the count strictly before it.
-__device__ void find_digit(const uint32_t* hist, int need, bool descending, int* d_out,
-                           int* before_out) {
-  const int lane = threadIdx.x & 63;
-  const int b0 = descending ? (255 - 4 * lane) : (4 * lane);
-  const int step = descending ? -1 : 1;
-  int h[4];
-  int s = 0;
+// Writes, in position order, every key better than or equal to the cut
+// (exactly m of them), then the -1 / -inf padding.
+template <int THREADS, int KPT, typename PosFn>
+__device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, const float* row,
+                         int32_t* out_i, float* out_v, SelShared<THREADS>& sh, PosFn pos) {
+  const uint32_t ck = sh.cut[0], cp = sh.cut[1];
+  uint32_t pick = 0u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = static_cast<int>(hist[b0 + step * i]);
-    s += h[i];
+  for (int j = 0; j < KPT; ++j) {
+    const bool in = j < nmine &&
+                    (key[j] > ck || (key[j] == ck && static_cast<uint32_t>(pos(j)) <= cp));
+    pick |= in ? (1u << j) : 0u;
   }
-  int incl = s;
+  int o = block_excl_scan<THREADS / 64>(__popc(pick), sh.wsum, nullptr);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  int run = incl - s;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (run < need && run + h[i] >= need) {
-      *d_out = b0 + step * i;
-      *before_out = run;
+  for (int j = 0; j < KPT; ++j) {
+    if ((pick >> j) & 1u) {
+      const int c = pos(j);
+      out_i[o] = c;
+      if (out_v) out_v[o] = row[c];
+      ++o;
     }
-    run += h[i];
   }
-}
-
-// Exclusive scan over a work-group of nwaves*64 threads; `wsum` holds nwaves ints.
-__device__ int block_excl_scan(int v, int* wsum, int nwaves, int* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  __syncthreads();
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
-  for (int w = 0; w < nwaves; ++w) {
-    const int s = wsum[w];
-    if (w < wave) before += s;
-    tot += s;
-  }
-  if (total) *total = tot;
-  return before + incl - v;
-}
-
-// ----------------------------------------------------------------------------
-// short rows: one work-group, keys in registers
-// ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(kSThreads) topk_small_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_val, int32_t* err, int skip_long) {
-  __shared__ uint32_t hist[kSThreads / 64][256];
-  __shared__ uint32_t total[256];
-  __shared__ int wsum[kSThreads / 64];
-  __shared__ int dig_s, before_s;
-
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, err, tid == 0);
-  if (skip_long && n > kSmallMax) return;
-  const float* row = scores + static_cast<long long>(t) * stride;
-  int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
-  float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
-  const int m = min(k, n);
   const float neg_inf = -__builtin_huge_valf();
-  if (m == n) {  // every visible position is chosen, already ascending
-    for (int i = tid; i < k; i += kSThreads) {
-      out_i[i] = i < n ? i : -1;
-      if (out_v) out_v[i] = i < n ? row[i] : neg_inf;
-    }
-    return;
-  }
-
-  // contiguous run per thread, a multiple of 4 keys so loads are 16 bytes
-  const int per = 4 * ((n + 4 * kSThreads - 1) / (4 * kSThreads));
-  const int base = tid * per;
-  uint32_t key[kSPer];
-#pragma unroll
-  for (int j = 0; j < kSPer; j += 4) {
-    if (j < per) {
-      const int c = base + j;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c + 3 < n) {
-        v = *reinterpret_cast<const float4*>(row + c);
-      } else {
-        if (c < n) v.x = row[c];
-        if (c + 1 < n) v.y = row[c + 1];
-        if (c + 2 < n) v.z = row[c + 2];
-      }
-      key[j] = order_key(v.x);
-      key[j + 1] = order_key(v.y);
-      key[j + 2] = order_key(v.z);
-      key[j + 3] = order_key(v.w);
-    }
-  }
-  const int nmine = max(0, min(per, n - base));
-
-  for (int i = tid; i < (kSThreads / 64) * 256; i += kSThreads) (&hist[0][0])[i] = 0;
-  __syncthreads();
-
-  uint32_t prefix = 0, mask = 0;
-  int rem = m;
-  bool exact = false;   // threshold digit holds exactly the needed count
-  int cnt_d = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-#pragma unroll
-    for (int j = 0; j < kSPer; ++j)
-      if (j < nmine && (key[j] & mask) == prefix) atomicAdd(&hist[wave][(key[j] >> shift) & 255], 1u);
-    __syncthreads();
-    if (tid < 256) {
-      uint32_t s = 0;
-#pragma unroll
-      for (int w = 0; w < kSThreads / 64; ++w) {
-        s += hist[w][tid];
-        hist[w][tid] = 0;
-      }
-      total[tid] = s;
-    }
-    __syncthreads();
-    if (tid < 64) find_digit(total, rem, true, &dig_s, &before_s);
-    __syncthreads();
-    const int d = dig_s;
-    rem -= before_s;
-    cnt_d = static_cast<int>(total[d]);
-    prefix |= static_cast<uint32_t>(d) << shift;
-    mask |= 0xffu << shift;
-    if (cnt_d == rem) {
-      exact = true;
-      break;
-    }
-  }
-  // chosen: (key & mask) > prefix, plus keys equal to the threshold -- all of
-  // them when exact, else the rem lowest positions among them
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int j = 0; j < kSPer; ++j) {
-    if (j < nmine) {
-      const uint32_t km = key[j] & mask;
-      gt += km > prefix;
-      eq += km == prefix;
-    }
-  }
-  int take = eq;
-  if (!exact) {
-    const int eq_before = block_excl_scan(eq, wsum, kSThreads / 64, nullptr);
-    take = max(0, min(eq, rem - eq_before));
-  }
-  const int off = block_excl_scan(gt + take, wsum, kSThreads / 64, nullptr);
-  int o = off, taken = 0;
-#pragma unroll
-  for (int j = 0; j < kSPer; ++j) {
-    if (j < nmine) {
-      const uint32_t km = key[j] & mask;
-      bool pick = km > prefix;
-      if (km == prefix && taken < take) {
-        pick = true;
-        ++taken;
-      }
-      if (pick) {
-        const int c = base + j;
-        out_i[o] = c;
-        if (out_v) out_v[o] = row[c];
-        ++o;
-      }
-    }
-  }
-  for (int i = m + tid; i < k; i += kSThreads) {
+  for (int i = m + static_cast<int>(threadIdx.x); i < k; i += THREADS) {
     out_i[i] = -1;
     if (out_v) out_v[i] = neg_inf;
   }
 }
 
-// ----------------------------------------------------------------------------
-// long rows: histogram + threshold bin
-// ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(kLThreads) topk_hist_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, int k, Workspace ws, int32_t* err) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ int last_s;
-  __shared__ int wsum[kLThreads / 64];
-  const int t = blockIdx.y;
-  const int tid = threadIdx.x;
-  if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, err, blockIdx.x == 0 && tid == 0);
-  if (n <= kSmallMax) return;
-  const float* row = scores + static_cast<long long>(t) * stride;
-  for (int i = tid; i < kBins; i += kLThreads) hist[i] = 0;
-  // issue all of this thread's loads before touching the histogram
-  const int c0 = blockIdx.x * kChunk;
-  const int c1 = min(n, c0 + kChunk);
-  float4 v[kPerThread4];
-#pragma unroll
-  for (int i = 0; i < kPerThread4; ++i) {
-    const int c = c0 + 4 * (tid + kLThreads * i);
-    if (c + 3 < c1) {
-      v[i] = *reinterpret_cast<const float4*>(row + c);
-    } else {
-      v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c < c1) v[i].x = row[c];
-      if (c + 1 < c1) v[i].y = row[c + 1];
-      if (c + 2 < c1) v[i].z = row[c + 2];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kPerThread4; ++i) {
-    const int c = c0 + 4 * (tid + kLThreads * i);
-    if (c < c1) atomicAdd(&hist[order_key(v[i].x) >> 20], 1u);
-    if (c + 1 < c1) atomicAdd(&hist[order_key(v[i].y) >> 20], 1u);
-    if (c + 2 < c1) atomicAdd(&hist[order_key(v[i].z) >> 20], 1u);
-    if (c + 3 < c1) atomicAdd(&hist[order_key(v[i].w) >> 20], 1u);
-  }
-  __syncthreads();
-  uint32_t* gh = ws.hist + static_cast<size_t>(t) * kBins;
-  uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
-  for (int i = tid; i < kBins; i += kLThreads)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last_s = (atomicAdd(&meta[0], 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!last_s) return;
-  __threadfence();
-  // this work-group is the row's last: find the bin holding the m-th key
-  const int m = min(k, n);
-  constexpr int kPerT = kBins / kLThreads;  // 16 bins per thread, from the top
-  uint32_t h[kPerT];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < kPerT; ++i) {
-    const int b = kBins - 1 - (tid * kPerT + i);
-    h[i] = __hip_atomic_load(&gh[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s += static_cast<int>(h[i]);
-  }
-  const int before = block_excl_scan(s, wsum, kLThreads / 64, nullptr);
-  int run = before;
-#pragma unroll
-  for (int i = 0; i < kPerT; ++i) {
-    if (run < m && run + static_cast<int>(h[i]) >= m) {
-      meta[2] = static_cast<uint32_t>(kBins - 1 - (tid * kPerT + i));  // threshold bin
-      meta[3] = static_cast<uint32_t>(run);                            // keys above it
-    }
-    run += static_cast<int>(h[i]);
-  }
-  for (int i = tid; i < kBins; i += kLThreads) gh[i] = 0;
-  if (tid == 0) meta[0] = 0;
-}
-
-// ----------------------------------------------------------------------------
-// long rows: keep every key in or above the threshold bin
-// ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, Workspace ws) {
-  const int t = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, nullptr, false);
-  if (n <= kSmallMax) return;
-  const int c0 = blockIdx.x * kChunk;
-  if (c0 >= n) return;
-  const int c1 = min(n, c0 + kChunk);
-  const float* row = scores + static_cast<long long>(t) * stride;
-  uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
-  uint2* cand = ws.cand + static_cast<size_t>(t) * kCap;
-  const uint32_t bin = meta[2];
-  uint32_t key[4 * kPerThread4];
-  int keep = 0;
-#pragma unroll
-  for (int i = 0; i < kPerThread4; ++i) {
-    const int c = c0 + 4 * (tid + kLThreads * i);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (c + 3 < c1) {
-      v = *reinterpret_cast<const float4*>(row + c);
-    } else {
-      if (c < c1) v.x = row[c];
-      if (c + 1 < c1) v.y = row[c + 1];
-      if (c + 2 < c1) v.z = row[c + 2];
-    }
-    key[4 * i] = order_key(v.x);
-    key[4 * i + 1] = order_key(v.y);
-    key[4 * i + 2] = order_key(v.z);
-    key[4 * i + 3] = order_key(v.w);
-  }
-#pragma unroll
-  for (int j = 0; j < 4 * kPerThread4; ++j) {
-    const int c = c0 + 4 * (tid + kLThreads * (j >> 2)) + (j & 3);
-    keep += (c < c1 && (key[j] >> 20) >= bin) ? 1 : 0;
-  }
-  // one device atomic per wave: in-wave exclusive prefix of the keep counts
-  int incl = keep;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  const int wave_total = __shfl(incl, 63, 64);
-  if (wave_total == 0) return;
-  uint32_t base = 0;
-  if (lane == 63) base = atomicAdd(&meta[1], static_cast<uint32_t>(wave_total));
-  base = __shfl(base, 63, 64);
-  uint32_t slot = base + static_cast<uint32_t>(incl - keep);
-#pragma unroll
-  for (int j = 0; j < 4 * kPerThread4; ++j) {
-    const int c = c0 + 4 * (tid + kLThreads * (j >> 2)) + (j & 3);
-    if (c < c1 && (key[j] >> 20) >= bin) {
-      if (slot < static_cast<uint32_t>(kCap)) cand[slot] = make_uint2(key[j], static_cast<uint32_t>(c));
-      ++slot;
-    }
+// Every visible position is chosen: 0 .. n-1 ascending, then padding.
+template <int THREADS>
+__device__ void write_all(int n, int k, const float* row, int32_t* out_i, float* out_v) {
+  const float neg_inf = -__builtin_huge_valf();
+  for (int i = threadIdx.x; i < k; i += THREADS) {
+    out_i[i] = i < n ? i : -1;
+    if (out_v) out_v[i] = i < n ? row[i] : neg_inf;
   }
 }
 
-// ----------------------------------------------------------------------------
-// long rows: exact cut among the candidates (or the whole row if they overflowed)
-// ----------------------------------------------------------------------------
-__global__ void __launch_bounds__(kSThreads) topk_final_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_val, Workspace ws) {
-  __shared__ uint32_t ckey[kCap];
-  __shared__ uint32_t cpos[kCap];
-  __shared__ uint32_t hist[256];
-  __shared__ int sel[kMaxK];
-  __shared__ int sel_count;
-  __shared__ int dig_s, before_s;
-
-  const int t = blockIdx.x;
+// Exact radix select over a whole row from global memory (8-bit digits on the
+// key, then on the position for ties) and a bitonic sort of the chosen
+// positions: the path for rows whose threshold bin held too many keys.
+template <int THREADS>
+__device__ void select_whole_row(const float* row, int n, int m, int k, int32_t* out_i,
+                                 float* out_v, SelShared<THREADS>& sh) {
   const int tid = threadIdx.x;
-  if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, nullptr, false);
-  if (n <= kSmallMax) return;
-  const float* row = scores + static_cast<long long>(t) * stride;
-  int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
-  float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
-  uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
-  const uint2* cand = ws.cand + static_cast<size_t>(t) * kCap;
-  const int m = min(k, n);
-  const int ncand = static_cast<int>(meta[1]);
-  const bool in_lds = ncand <= kCap;
-  const int nc = in_lds ? ncand : n;   // candidates, or the whole row on overflow
-  if (in_lds) {
-    for (int i = tid; i < nc; i += kSThreads) {
-      const uint2 e = cand[i];
-      ckey[i] = e.x;
-      cpos[i] = e.y;
+  int* sel = reinterpret_cast<int*>(sh.list);
+  int* sel_count = &sh.sel_count;
+  __syncthreads();   // the caller's last reads of the shared state are done
+  uint32_t* hist = sh.hist;   // first 256 bins
+  // wave 0: the digit where the running count from the top (or the bottom)
+  // first reaches need, and the count before it
+  auto digit = [&](bool descending, int need) {
+    if (tid < 64) {
+      const int lane = tid;
+      const int b0 = descending ? (255 - 4 * lane) : (4 * lane);
+      const int step = descending ? -1 : 1;
+      int hh[4];
+      int s = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hh[i] = static_cast<int>(hist[b0 + step * i]);
+        s += hh[i];
+      }
+      const int incl = wave_incl_scan(s);
+      int run = incl - s;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (run < need && run + hh[i] >= need) {
+          sh.bsel[0] = b0 + step * i;
+          sh.bsel[1] = run;
+        }
+        run += hh[i];
+      }
     }
-  }
-  __syncthreads();
-  auto key_at = [&](int i) -> uint32_t { return in_lds ? ckey[i] : order_key(row[i]); };
-  auto pos_at = [&](int i) -> uint32_t { return in_lds ? cpos[i] : static_cast<uint32_t>(i); };
-
-  uint32_t prefix = 0, mask = 0;
-  int rem = m, cnt_d = 0;
+  };
+  uint32_t prefix = 0u, mask = 0u;
+  int rem = m;
   bool exact = false;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0u;
     __syncthreads();
-    for (int i = tid; i < nc; i += kSThreads) {
-      const uint32_t kk = key_at(i);
+    for (int i = tid; i < n; i += THREADS) {
+      const uint32_t kk = order_key(row[i]);
       if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1u);
     }
     __syncthreads();
-    if (tid < 64) find_digit(hist, rem, true, &dig_s, &before_s);
+    digit(true, rem);
     __syncthreads();
-    const int d = dig_s;
-    rem -= before_s;
-    cnt_d = static_cast<int>(hist[d]);
+    const int d = sh.bsel[0];
+    rem -= sh.bsel[1];
+    const int cnt = static_cast<int>(hist[d]);
     prefix |= static_cast<uint32_t>(d) << shift;
     mask |= 0xffu << shift;
     __syncthreads();
-    if (cnt_d == rem) {
+    if (cnt == rem) {
       exact = true;
       break;
     }
   }
-  // ties beyond the need: keep the rem lowest positions among them
   uint32_t pos_limit = 0xffffffffu;
   if (!exact) {
-    uint32_t pprefix = 0, pmask = 0;
+    uint32_t pprefix = 0u, pmask = 0u;
     int prem = rem;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
+      if (tid < 256) hist[tid] = 0u;
       __syncthreads();
-      for (int i = tid; i < nc; i += kSThreads) {
-        const uint32_t p = pos_at(i);
-        if ((key_at(i) & mask) == prefix && (p & pmask) == pprefix)
+      for (int i = tid; i < n; i += THREADS) {
+        const uint32_t p = static_cast<uint32_t>(i);
+        if ((order_key(row[i]) & mask) == prefix && (p & pmask) == pprefix)
           atomicAdd(&hist[(p >> shift) & 255], 1u);
       }
       __syncthreads();
-      if (tid < 64) find_digit(hist, prem, false, &dig_s, &before_s);
+      digit(false, prem);
       __syncthreads();
-      prem -= before_s;
-      pprefix |= static_cast<uint32_t>(dig_s) << shift;
+      prem -= sh.bsel[1];
+      pprefix |= static_cast<uint32_t>(sh.bsel[0]) << shift;
       pmask |= 0xffu << shift;
       __syncthreads();
     }
     pos_limit = pprefix;
   }
-  if (tid == 0) sel_count = 0;
+  if (tid == 0) *sel_count = 0;
   __syncthreads();
-  for (int i = tid; i < nc; i += kSThreads) {
-    const uint32_t km = key_at(i) & mask;
-    if (km > prefix || (km == prefix && pos_at(i) <= pos_limit)) {
-      const int slot = atomicAdd(&sel_count, 1);
-      if (slot < kMaxK) sel[slot] = static_cast<int>(pos_at(i));
+  for (int i = tid; i < n; i += THREADS) {
+    const uint32_t km = order_key(row[i]) & mask;
+    if (km > prefix || (km == prefix && static_cast<uint32_t>(i) <= pos_limit)) {
+      const int slot = atomicAdd(sel_count, 1);
+      if (slot < kMaxK) sel[slot] = i;
     }
   }
   __syncthreads();
   int P = 1;
   while (P < m) P <<= 1;
-  for (int i = m + tid; i < P; i += kSThreads) sel[i] = 0x7fffffff;
+  for (int i = m + tid; i < P; i += THREADS) sel[i] = 0x7fffffff;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int j = size >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < (P >> 1); i += kSThreads) {
+      for (int i = tid; i < (P >> 1); i += THREADS) {
         const int lo = 2 * i - (i & (j - 1));
         const int hi = lo + j;
         const bool up = ((lo & size) == 0);
@@ -522,16 +624,395 @@ __global__ void __launch_bounds__(kSThreads) topk_final_kernel(
     }
   }
   const float neg_inf = -__builtin_huge_valf();
-  for (int i = tid; i < k; i += kSThreads) {
+  for (int i = tid; i < k; i += THREADS) {
     const int c = i < m ? sel[i] : -1;
     out_i[i] = c;
     if (out_v) out_v[i] = c >= 0 ? row[c] : neg_inf;
   }
-  if (tid == 0) {
-    meta[1] = 0;
-    meta[2] = 0;
-    meta[3] = 0;
+}
+
+// ----------------------------------------------------------------------------
+// short rows: one work-group, keys in registers
+// ----------------------------------------------------------------------------
+template <int THREADS, int KPT>
+__global__ void __launch_bounds__(THREADS) topk_small_kernel(
+    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
+    int ratio, int num_tokens, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_val, int32_t* err) {
+  constexpr int kSmallCand = THREADS >= 1024 ? 4096 : 8 * THREADS;
+  __shared__ SelShared<THREADS> sh;
+  __shared__ uint32_t cand_k[kSmallCand];
+  __shared__ uint32_t cand_p[kSmallCand];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (t >= num_tokens) return;
+  const float* row = scores + static_cast<long long>(t) * stride;
+  // the whole allocated row is loaded before the span is known (one memory
+  // latency instead of two); per is a multiple of 4 and stride is too, so a
+  // 16-byte load starting below stride stays inside the row
+  const int span = static_cast<int>(stride);
+  const int per = 4 * ((span + 4 * THREADS - 1) / (4 * THREADS));
+  const int base = tid * per;
+  float4 v[KPT / 4];
+#pragma unroll
+  for (int i = 0; i < KPT / 4; ++i) {
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (4 * i < per && base + 4 * i < span)
+      v[i] = *reinterpret_cast<const float4*>(row + base + 4 * i);
   }
+  const int n = row_span(positions, t, ratio, stride, err, tid == 0);
+  int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
+  float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
+  const int m = min(k, n);
+  if (m == n) {
+    write_all<THREADS>(n, k, row, out_i, out_v);
+    return;
+  }
+  uint32_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT / 4; ++i) {
+    key[4 * i] = order_key(v[i].x);
+    key[4 * i + 1] = order_key(v[i].y);
+    key[4 * i + 2] = order_key(v[i].z);
+    key[4 * i + 3] = order_key(v[i].w);
+  }
+  const int nmine = max(0, min(per, n - base));
+  auto pos = [&](int j) { return base + j; };
+  constexpr int NW = THREADS / 64;
+  constexpr int CPT = kSmallCand / THREADS;
+  bool done = false;
+  // Sampled threshold: every thread's first key is a sample (S of them,
+  // evenly spaced); the key tau of the r-th best sample, with r a little above
+  // m * S / n, leaves in expectation slightly more than m keys >= tau.  Those
+  // candidates are compacted in position order and selected exactly; when the
+  // sample misleads (fewer than m or too many candidates) the row takes the
+  // full path below.
+  const int S = (n + per - 1) / per;
+  const float expect = static_cast<float>(m) * static_cast<float>(S) / static_cast<float>(n);
+  const int r = static_cast<int>(ceilf(expect + 2.0f * sqrtf(expect) + 2.0f));
+  if (S >= 64 && r < S) {
+    {
+      // histogram of the samples' top 11 key bits; tau is the lower edge of
+      // the bin holding the r-th best sample
+      for (int i = tid; i < kSBins + 64; i += THREADS) sh.hist[i] = 0u;
+      __syncthreads();
+      atomicAdd(&sh.hist[nmine > 0 ? (key[0] >> 21) : kSBins + (tid & 63)], 1u);
+      __syncthreads();
+      find_bin<kSBins, THREADS>(sh.hist, r, sh.wsum, &sh.bsel[0], &sh.bsel[1]);
+      const uint32_t tau = static_cast<uint32_t>(sh.bsel[0]) << 21;
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) c += (j < nmine && key[j] >= tau) ? 1 : 0;
+      int total = 0;
+      int o = block_excl_scan<NW>(c, sh.wsum, &total);
+      if (total >= m && total <= kSmallCand) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          if (j < nmine && key[j] >= tau) {
+            cand_k[o] = key[j];
+            cand_p[o] = static_cast<uint32_t>(base + j);
+            ++o;
+          }
+        }
+        __syncthreads();
+        const int cper = (total + THREADS - 1) / THREADS;
+        const int cbase = tid * cper;
+        uint32_t ck[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) ck[j] = (j < cper && cbase + j < total) ? cand_k[cbase + j] : 0u;
+        const int cn = max(0, min(cper, total - cbase));
+        auto cpos = [&](int j) { return static_cast<int>(cand_p[cbase + j]); };
+        if (find_cut<THREADS, CPT>(ck, cn, m, sh, cpos)) {
+          emit_cut<THREADS, CPT>(ck, cn, m, k, row, out_i, out_v, sh, cpos);
+          done = true;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (done) return;
+  if (find_cut<THREADS, KPT>(key, nmine, m, sh, pos))
+    emit_cut<THREADS, KPT>(key, nmine, m, k, row, out_i, out_v, sh, pos);
+  else
+    select_whole_row<THREADS>(row, n, m, k, out_i, out_v, sh);
+}
+
+// ----------------------------------------------------------------------------
+// long rows
+// ----------------------------------------------------------------------------
+// Lane `lane` of wave `wave` loads kLLoads 16-byte groups of the chunk at c0:
+// positions c0 + wave*kSub + 256*i + 4*lane, so each wave owns a contiguous
+// kSub-position run and position order is (i, lane, component).
+struct ChunkKeys {
+  uint32_t key[4 * kLLoads];
+  int first;   // position of key[0]
+};
+
+__device__ __forceinline__ void load_chunk(const float* row, long long stride, int n, int c0,
+                                           ChunkKeys& ck) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  ck.first = c0 + wave * kSub + 4 * lane;
+  float4 v[kLLoads];
+#pragma unroll
+  for (int i = 0; i < kLLoads; ++i) {
+    const int c = ck.first + 256 * i;
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < stride) v[i] = *reinterpret_cast<const float4*>(row + c);
+  }
+#pragma unroll
+  for (int i = 0; i < kLLoads; ++i) {
+    const int c = ck.first + 256 * i;
+    // keys past the span get the NaN code; callers mask them by position
+    ck.key[4 * i] = c < n ? order_key(v[i].x) : 0u;
+    ck.key[4 * i + 1] = c + 1 < n ? order_key(v[i].y) : 0u;
+    ck.key[4 * i + 2] = c + 2 < n ? order_key(v[i].z) : 0u;
+    ck.key[4 * i + 3] = c + 3 < n ? order_key(v[i].w) : 0u;
+  }
+}
+
+__device__ __forceinline__ bool in_span(const ChunkKeys& ck, int j, int n) {
+  return ck.first + 256 * (j >> 2) + (j & 3) < n;
+}
+
+__global__ void __launch_bounds__(kLThreads) topk_range_kernel(
+    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
+    int ratio, int num_tokens, Workspace ws) {
+  __shared__ uint32_t red[2][kLWaves];
+  const int t = blockIdx.y;
+  if (t >= num_tokens) return;
+  const int n = row_span(positions, t, ratio, stride, nullptr, false);
+  const int c0 = blockIdx.x * kChunk;
+  if (n <= kCap || c0 >= n) return;
+  ChunkKeys ck;
+  load_chunk(scores + static_cast<long long>(t) * stride, stride, n, c0, ck);
+  uint32_t fmin = 0xffffffffu, fmax = 0u;
+#pragma unroll
+  for (int j = 0; j < 4 * kLLoads; ++j) {
+    if (key_finite(ck.key[j])) {   // keys past the span carry the NaN code
+      fmin = min(fmin, ck.key[j]);
+      fmax = max(fmax, ck.key[j]);
+    }
+  }
+  fmin = wave_min_u(fmin);
+  fmax = wave_max_u(fmax);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[0][wave] = fmin;
+    red[1][wave] = fmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 0; w < kLWaves; ++w) {
+      fmin = min(fmin, red[0][w]);
+      fmax = max(fmax, red[1][w]);
+    }
+    uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
+    if (fmax != 0u) atomicMax(&meta[kMetaMax], fmax);
+    if (fmin != 0xffffffffu) atomicMax(&meta[kMetaMinInv], ~fmin);
+  }
+}
+
+__device__ __forceinline__ Binner row_binner(const uint32_t* meta) {
+  const uint32_t kfmax = meta[kMetaMax];
+  const uint32_t kfmin = ~meta[kMetaMinInv];   // no finite key: 0xffffffff > kfmax
+  return make_binner(kfmin, kfmax, kLBins);
+}
+
+__global__ void __launch_bounds__(kLThreads) topk_hist_kernel(
+    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
+    int ratio, int num_tokens, Workspace ws) {
+  __shared__ uint32_t hist[kLBins + 64];   // + one dummy bin per lane
+  const int t = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (t >= num_tokens) return;
+  const int n = row_span(positions, t, ratio, stride, nullptr, false);
+  const int c0 = blockIdx.x * kChunk;
+  if (n <= kCap || c0 >= n) return;
+  ChunkKeys ck;
+  load_chunk(scores + static_cast<long long>(t) * stride, stride, n, c0, ck);
+  const Binner bn = row_binner(ws.meta + static_cast<size_t>(t) * kMetaWords);
+  for (int i = tid; i < kLBins + 64; i += kLThreads) hist[i] = 0u;
+  __syncthreads();
+  const int dummy = kLBins + (tid & 63);
+#pragma unroll
+  for (int j = 0; j < 4 * kLLoads; ++j)
+    atomicAdd(&hist[in_span(ck, j, n) ? bn(ck.key[j]) : dummy], 1u);
+  __syncthreads();
+  uint32_t* gh = ws.hist + static_cast<size_t>(t) * kLBins;
+  for (int i = tid; i < kLBins; i += kLThreads)
+    if (hist[i]) atomicAdd(&gh[i], hist[i]);
+}
+
+__global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
+    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
+    int ratio, int num_tokens, int k, Workspace ws) {
+  __shared__ int wsum[2 * kLWaves + 1];
+  __shared__ int bsel;
+  const int t = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  if (t >= num_tokens) return;
+  const int n = row_span(positions, t, ratio, stride, nullptr, false);
+  const int c0 = blockIdx.x * kChunk;
+  if (n <= kCap || c0 >= n) return;
+  ChunkKeys ck;
+  load_chunk(scores + static_cast<long long>(t) * stride, stride, n, c0, ck);
+  uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
+  const Binner bn = row_binner(meta);
+
+  // bin of the m-th key, from the row histogram (every work-group of the row
+  // computes the same answer): thread tid sums bins [lo, lo + kPer) from the top
+  const uint32_t* gh = ws.hist + static_cast<size_t>(t) * kLBins;
+  constexpr int kPer = kLBins / kLThreads;
+  const int lo = kLBins - (tid + 1) * kPer;
+  uint32_t h[kPer];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    h[i] = gh[lo + i];
+    s += static_cast<int>(h[i]);
+  }
+  const int m = min(k, n);
+  int run = block_excl_scan<kLWaves>(s, wsum, nullptr);
+  if (run < m && run + s >= m) {
+    for (int i = kPer - 1; i >= 0; --i) {
+      if (run + static_cast<int>(h[i]) >= m) {
+        bsel = lo + i;
+        break;
+      }
+      run += static_cast<int>(h[i]);
+    }
+  }
+  __syncthreads();
+  const int b = bsel;
+
+  // keep keys in or above bin b; the wave's kept keys form one segment in
+  // position order (i, lane, component)
+  int cnt[kLLoads];
+  int off[kLLoads];
+  int wave_total = 0;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int i = 0; i < kLLoads; ++i) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool keep = in_span(ck, 4 * i + q, n) && bn(ck.key[4 * i + q]) >= b;
+      c += keep ? 1 : 0;
+    }
+    cnt[i] = c;
+    const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
+    off[i] = wave_total + __popcll(b0 & below) + 2 * __popcll(b1 & below) +
+             4 * __popcll(b2 & below);
+    wave_total += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+  }
+  uint32_t slot0 = 0u;
+  if (lane == 0 && wave_total > 0)
+    slot0 = atomicAdd(&meta[kMetaCount], static_cast<uint32_t>(wave_total));
+  slot0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slot0), 0));
+  if (lane == 0)
+    ws.seg[static_cast<size_t>(t) * ws.nseg + blockIdx.x * kLWaves + wave] =
+        make_uint2(slot0, static_cast<uint32_t>(wave_total));
+  uint2* cand = ws.cand + static_cast<size_t>(t) * kCap;
+#pragma unroll
+  for (int i = 0; i < kLLoads; ++i) {
+    if (cnt[i] == 0) continue;
+    uint32_t slot = slot0 + static_cast<uint32_t>(off[i]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = 4 * i + q;
+      if (in_span(ck, j, n) && bn(ck.key[j]) >= b) {
+        if (slot < static_cast<uint32_t>(kCap))
+          cand[slot] = make_uint2(ck.key[j], static_cast<uint32_t>(ck.first + 256 * i + q));
+        ++slot;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kFThreads) topk_final_kernel(
+    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
+    int ratio, int num_tokens, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_val, Workspace ws, int32_t* err) {
+  __shared__ SelShared<kFThreads> sh;
+  __shared__ uint32_t ckey[kCap];
+  __shared__ uint32_t cpos[kCap];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (t >= num_tokens) return;
+  const int n = row_span(positions, t, ratio, stride, err, tid == 0);
+  const float* row = scores + static_cast<long long>(t) * stride;
+  int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
+  float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
+  uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
+  uint32_t* gh = ws.hist + static_cast<size_t>(t) * kLBins;
+  const int m = min(k, n);
+  if (m == n) {
+    write_all<kFThreads>(n, k, row, out_i, out_v);
+  } else {
+    int total = 0;
+    bool whole_row = false;
+    if (n <= kCap) {
+      // short row: the row itself is the candidate list
+      for (int i = tid; i < n; i += kFThreads) {
+        ckey[i] = order_key(row[i]);
+        cpos[i] = static_cast<uint32_t>(i);
+      }
+      total = n;
+    } else {
+      total = static_cast<int>(meta[kMetaCount]);
+      if (total > kCap) {
+        whole_row = true;
+      } else {
+        // segments in position order: scan their counts, copy each into place
+        const int nseg = ((n + kChunk - 1) / kChunk) * kLWaves;
+        const int spt = (nseg + kFThreads - 1) / kFThreads;
+        const uint2* seg = ws.seg + static_cast<size_t>(t) * ws.nseg;
+        const uint2* cand = ws.cand + static_cast<size_t>(t) * kCap;
+        int mine = 0;
+        for (int i = 0; i < spt; ++i) {
+          const int sidx = tid * spt + i;
+          if (sidx < nseg) mine += static_cast<int>(seg[sidx].y);
+        }
+        int dst = block_excl_scan<kFThreads / 64>(mine, sh.wsum, nullptr);
+        for (int i = 0; i < spt; ++i) {
+          const int sidx = tid * spt + i;
+          if (sidx < nseg) {
+            const uint2 sg = seg[sidx];
+            for (uint32_t q = 0; q < sg.y; ++q) {
+              const uint2 e = cand[sg.x + q];
+              ckey[dst] = e.x;
+              cpos[dst] = e.y;
+              ++dst;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (whole_row) {
+      select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh);
+    } else {
+      const int per = (total + kFThreads - 1) / kFThreads;   // <= kFPer
+      const int base = tid * per;
+      uint32_t key[kFPer];
+#pragma unroll
+      for (int j = 0; j < kFPer; ++j) key[j] = (j < per && base + j < total) ? ckey[base + j] : 0u;
+      const int nmine = max(0, min(per, total - base));
+      auto pos = [&](int j) { return static_cast<int>(cpos[base + j]); };
+      if (find_cut<kFThreads, kFPer>(key, nmine, m, sh, pos))
+        emit_cut<kFThreads, kFPer>(key, nmine, m, k, row, out_i, out_v, sh, pos);
+      else
+        select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh);
+    }
+  }
+  // leave the row's histogram and counters zero for the next call
+  if (n > kCap)
+    for (int i = tid; i < kLBins; i += kFThreads) gh[i] = 0u;
+  if (tid < kMetaWords) meta[tid] = 0u;
 }
 
 }  // namespace
@@ -541,7 +1022,7 @@ __global__ void __launch_bounds__(kSThreads) topk_final_kernel(
 extern "C" size_t csa_topk_workspace_bytes(int32_t T, int64_t score_stride, int32_t k) {
   (void)k;
   if (T <= 0 || score_stride <= csa::kSmallMax) return 0;
-  return csa::ws_bytes(T);
+  return csa::ws_bytes(T, score_stride);
 }
 
 extern "C" int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions,
@@ -555,24 +1036,32 @@ extern "C" int csa_topk(const float* scores, int64_t score_stride, const int32_t
   if (!scores || !positions || !topk_idx) return CSA_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(scores) & 15 || (score_stride & 3)) return CSA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool long_rows = score_stride > csa::kSmallMax;
-  if (long_rows) {
-    if (!workspace || workspace_bytes < csa::ws_bytes(T)) return CSA_ERR_WORKSPACE;
-    const csa::Workspace ws = csa::ws_layout(workspace, T);
-    const long long chunks = (score_stride + csa::kChunk - 1) / csa::kChunk;
-    if (chunks > 0x7fffffffll || num_tokens > 65535) return CSA_ERR_UNSUPPORTED;
-    const dim3 grid(static_cast<unsigned>(chunks), static_cast<unsigned>(num_tokens));
-    hipLaunchKernelGGL(csa::topk_hist_kernel, grid, dim3(csa::kLThreads), 0, st, scores,
-                       static_cast<long long>(score_stride), positions, ratio, num_tokens, k, ws,
-                       err);
+  const long long stride = score_stride;
+  if (stride <= 4096) {
+    hipLaunchKernelGGL((csa::topk_small_kernel<256, 16>), dim3(num_tokens), dim3(256), 0, st,
+                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, err);
+  } else if (stride <= 16384) {
+    hipLaunchKernelGGL((csa::topk_small_kernel<1024, 16>), dim3(num_tokens), dim3(1024), 0, st,
+                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, err);
+  } else if (stride <= csa::kSmallMax) {
+    hipLaunchKernelGGL((csa::topk_small_kernel<1024, 32>), dim3(num_tokens), dim3(1024), 0, st,
+                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, err);
+  } else {
+    if (stride > csa::kMaxStride || num_tokens > 65535) return CSA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < csa::ws_bytes(T, stride)) return CSA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
+    const csa::Workspace ws = csa::ws_layout(workspace, T, stride);
+    const dim3 grid(static_cast<unsigned>((stride + csa::kChunk - 1) / csa::kChunk),
+                    static_cast<unsigned>(num_tokens));
+    hipLaunchKernelGGL(csa::topk_range_kernel, grid, dim3(csa::kLThreads), 0, st, scores, stride,
+                       positions, ratio, num_tokens, ws);
+    hipLaunchKernelGGL(csa::topk_hist_kernel, grid, dim3(csa::kLThreads), 0, st, scores, stride,
+                       positions, ratio, num_tokens, ws);
     hipLaunchKernelGGL(csa::topk_filter_kernel, grid, dim3(csa::kLThreads), 0, st, scores,
-                       static_cast<long long>(score_stride), positions, ratio, num_tokens, ws);
-    hipLaunchKernelGGL(csa::topk_final_kernel, dim3(num_tokens), dim3(csa::kSThreads), 0, st,
-                       scores, static_cast<long long>(score_stride), positions, ratio,
-                       num_tokens, k, topk_idx, topk_val, ws);
+                       stride, positions, ratio, num_tokens, k, ws);
+    hipLaunchKernelGGL(csa::topk_final_kernel, dim3(num_tokens), dim3(csa::kFThreads), 0, st,
+                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, ws,
+                       err);
   }
-  hipLaunchKernelGGL(csa::topk_small_kernel, dim3(num_tokens), dim3(csa::kSThreads), 0, st,
-                     scores, static_cast<long long>(score_stride), positions, ratio, num_tokens,
-                     k, topk_idx, topk_val, long_rows ? nullptr : err, long_rows ? 1 : 0);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
