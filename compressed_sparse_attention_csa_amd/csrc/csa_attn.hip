@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
 
   if (tid == 0) err_s = 0;
 
-  const int b = owner_request(a.qsl, a.B, t);
+  const int b = owner_request_wave(a.qsl, a.B, t);
   const int p = a.positions[t];
   const int nv = visible_count(p, a.ratio);
   int w_len = 0, w_lo = 0;
@@ -423,6 +423,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   __shared__ __attribute__((aligned(16))) uint8_t slot_s[kAttnWaves * SS];
   __shared__ uint32_t row_s[kSpan];
   __shared__ float ml_s[kAttnWaves][2][16];
+  __shared__ float rope_s[2 * kAttnThreads];   // rope row of t: cos, then sin
   __shared__ int scan_s[kAttnWaves];
   __shared__ int err_s;
 
@@ -443,9 +444,27 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   const int h = hg * 16 + col;
   const bool hv = h < a.H;
   if (tid == 0) err_s = 0;
-
-  const int b = owner_request(a.qsl, a.B, t);
+  // metadata loads first, then the query and rope loads, then the first use
+  // of the metadata (vector memory returns in order)
+  const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
+  // the query and the rope row: in flight during the row resolution, and
+  // complete before the gather is issued (a load issued after the gather
+  // would wait for it)
+  v4i qraw[KS];
+  {
+    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = hv ? *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8) : v4i{0, 0, 0, 0};
+  }
+  float rcv = 0.0f, rsv = 0.0f;
+  if (tid < a.half_rope) {
+    rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + tid];
+    rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + tid];
+  }
+
+  const int b = owner_from_lanes(qsl_v, a.qsl, a.B, t);
   const int nv = visible_count(p, a.ratio);
   int w_len = 0, w_lo = 0;
   if (b >= 0 && p >= 0 && a.window > 0) {
@@ -489,59 +508,63 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
     if (rr != kNoRow) row_s[slot] = rr;
     n_valid = total;
   }
+  if (tid < a.half_rope) {
+    rope_s[tid] = rcv;
+    rope_s[kAttnThreads + tid] = rsv;
+  }
   __syncthreads();
 
   // ---- this wave's 32 rows straight into its LDS slot (masked rows read the
-  //      query: finite bytes that P = 0 keeps out)
+  //      query: finite bytes that P = 0 keeps out).  All row indices are read
+  //      from LDS first, so the direct-to-LDS loads issue back to back.
   uint8_t* myslot = slot_s + wave * SS;
   const int j0 = wave * kTile;
-  {
+  if (j0 < n_valid) {
+    constexpr int NI = kTile / RPI;
+    uint32_t rr[NI];
+#pragma unroll
+    for (int ins = 0; ins < NI; ++ins) {
+      const int j = j0 + ins * RPI + lane / NC;
+      rr[ins] = (j < n_valid) ? row_s[j] : kNoRow;
+    }
     const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
 #pragma unroll
-    for (int ins = 0; ins < kTile / RPI; ++ins) {
-      const int j = j0 + ins * RPI + lane / NC;
-      const uint32_t rr = (j < n_valid) ? row_s[j] : kNoRow;
-      const uint8_t* src = dummy;
-      if (rr != kNoRow)
-        src = reinterpret_cast<const uint8_t*>(
-            (rr & kWinBit) ? a.win_kv + static_cast<long long>(rr & ~kWinBit) * D
-                           : a.cmp_kv + static_cast<long long>(rr) * D);
-      if (j0 < n_valid)
-        __builtin_amdgcn_global_load_lds(
-            src + (lane % NC) * 16, (__attribute__((address_space(3))) void*)(myslot + ins * GS),
-            16, 0, 0);
+    for (int ins = 0; ins < NI; ++ins) {
+      const uint32_t r = rr[ins];
+      const uint16_t* pool = (r & kWinBit) ? a.win_kv : a.cmp_kv;
+      const uint8_t* row = reinterpret_cast<const uint8_t*>(
+          pool + static_cast<long long>(r & ~kWinBit) * D);
+      const uint8_t* src = (r == kNoRow) ? dummy : row;
+      __builtin_amdgcn_global_load_lds(
+          src + (lane % NC) * 16, (__attribute__((address_space(3))) void*)(myslot + ins * GS),
+          16, 0, 0);
     }
   }
   auto row_off = [](int r) { return (r / RPI) * GS + (r % RPI) * RB; };
 
-  // ---- query fragments of head h (B operand of S^T), rotated on the rope span
+  // ---- query fragments of head h (B operand of S^T), rotated on the rope
+  //      span while the gather is in flight
   v8bf qf[KS];
-  {
-    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
-    const float* rc = a.rope_cos + static_cast<long long>(t) * a.half_rope;
-    const float* rs = a.rope_sin + static_cast<long long>(t) * a.half_rope;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = ks * 32 + grp * 8;
-      v4i raw = hv ? *reinterpret_cast<const v4i*>(qrow + d0) : v4i{0, 0, 0, 0};
-      const int r0 = d0 - a.rope_offset;
-      if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
-        uint16_t e[8];
-        *reinterpret_cast<v4i*>(e) = raw;
+  for (int ks = 0; ks < KS; ++ks) {
+    v4i raw = qraw[ks];
+    const int r0 = ks * 32 + grp * 8 - a.rope_offset;
+    if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
+      uint16_t e[8];
+      *reinterpret_cast<v4i*>(e) = raw;
 #pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const int rr = r0 + 2 * pr;
-          if (rr >= 0 && rr < 2 * a.half_rope) {
-            const float c = rc[rr >> 1], sn = rs[rr >> 1];
-            const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
-            e[2 * pr] = f32_to_bf16(x * c - y * sn);
-            e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
-          }
+      for (int pr = 0; pr < 4; ++pr) {
+        const int rr = r0 + 2 * pr;
+        if (rr >= 0 && rr < 2 * a.half_rope) {
+          const float c = rope_s[rr >> 1], sn = rope_s[kAttnThreads + (rr >> 1)];
+          const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
+          e[2 * pr] = f32_to_bf16(x * c - y * sn);
+          e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
         }
-        raw = *reinterpret_cast<v4i*>(e);
       }
-      qf[ks] = as_v8bf(raw);
+      raw = *reinterpret_cast<v4i*>(e);
     }
+    qf[ks] = as_v8bf(raw);
   }
 
   const float neg_inf = -__builtin_huge_valf();
@@ -685,54 +708,79 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   }
 }
 
-// Combine split partials with the sink: one work-group per (row, head) over
-// partials laid out [t][split][head][D]; the split weights are formed once in
-// LDS so the partial reads pipeline.
-constexpr int kMaxSplits = 64;
+// Combine the span partials of each (row, head) with the sink: one wave per
+// (row, head).  Lane l owns channels [8l, 8l + 8) of every partial (D = 512;
+// D / 64 channels in general).  The (max, sum) pairs and the first eight
+// partials are loaded together, so a merge costs one memory latency.
+constexpr int kMergeChunk = 8;
 
 template <int D>
-__global__ void __launch_bounds__(128) attn_merge_kernel(
+__global__ void __launch_bounds__(64) attn_merge_kernel(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const float* __restrict__ sink, int splits, int H, int num_tokens,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float w_s[kMaxSplits];
-  __shared__ float mz_s[2];
+  constexpr int CPL = D / 64;            // channels per lane
+  constexpr int V4 = CPL >= 4 ? CPL / 4 : 1;
+  static_assert(CPL % 4 == 0 || CPL == 1 || CPL == 2, "channels per lane");
   const int t = blockIdx.x / H;
   const int h = blockIdx.x % H;
   if (t >= num_tokens) return;
+  const int lane = threadIdx.x;
   const float neg_inf = -__builtin_huge_valf();
-  const long long base = static_cast<long long>(t) * splits;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    float2 ml = make_float2(neg_inf, 0.0f);
-    if (lane < splits) ml = part_ml[(base + lane) * H + h];
-    const float sink2 = sink[h] * kLog2e;
-    float M = ml.x;
+  const long long tbase = static_cast<long long>(t) * splits;
+  const float2 ml = lane < splits ? part_ml[(tbase + lane) * H + h] : make_float2(neg_inf, 0.0f);
+  float acc[CPL];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    M = fmaxf(M, sink2);
-    const float e = (ml.x == neg_inf) ? 0.0f : exp2f(ml.x - M);
-    float z = ml.y * e;
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
+  float chunk[kMergeChunk][CPL];
+  auto load_chunk = [&](int s0) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
-    z += exp2f(sink2 - M);
-    if (lane < splits) w_s[lane] = e / z;
-    if (lane == 0) {
-      mz_s[0] = M;
-      mz_s[1] = z;
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const int sp = s0 + u;
+      const float* po = part_o + ((tbase + (sp < splits ? sp : 0)) * H + h) * D + lane * CPL;
+      if constexpr (CPL >= 4) {
+#pragma unroll
+        for (int v = 0; v < V4; ++v) {
+          const v4f x = sp < splits ? *reinterpret_cast<const v4f*>(po + 4 * v) : v4f{0.f, 0.f, 0.f, 0.f};
+          chunk[u][4 * v] = x[0];
+          chunk[u][4 * v + 1] = x[1];
+          chunk[u][4 * v + 2] = x[2];
+          chunk[u][4 * v + 3] = x[3];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) chunk[u][i] = sp < splits ? po[i] : 0.0f;
+      }
+    }
+  };
+  load_chunk(0);
+  // running max and denominator over the spans, with the sink
+  const float sink2 = sink[h] * kLog2e;
+  float M = ml.x;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  M = fmaxf(M, sink2);
+  const float w_l = (ml.x == neg_inf) ? 0.0f : exp2f(ml.x - M);
+  float z = ml.y * w_l;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+  z += exp2f(sink2 - M);
+  for (int s0 = 0; s0 < splits; s0 += kMergeChunk) {
+    if (s0 > 0) load_chunk(s0);
+#pragma unroll
+    for (int u = 0; u < kMergeChunk; ++u) {
+      const float w = __shfl(w_l, (s0 + u) & 63, 64);
+      if (s0 + u < splits) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) acc[i] += chunk[u][i] * w;
+      }
     }
   }
-  __syncthreads();
-  for (int d = threadIdx.x * 4; d < D; d += 128 * 4) {
-    v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s)
-      acc += *reinterpret_cast<const v4f*>(part_o + ((base + s) * H + h) * D + d) * w_s[s];
-    uint2 pk;
-    pk.x = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-    pk.y = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-    *reinterpret_cast<uint2*>(out + (static_cast<long long>(t) * H + h) * D + d) = pk;
-  }
-  if (lse && threadIdx.x == 0) lse[static_cast<long long>(t) * H + h] = (mz_s[0] + log2f(mz_s[1])) * kLn2;
+  const float f = 1.0f / z;
+  uint16_t* orow = out + (static_cast<long long>(t) * H + h) * D + lane * CPL;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) orow[i] = f32_to_bf16(acc[i] * f);
+  if (lse && lane == 0) lse[static_cast<long long>(t) * H + h] = (M + log2f(z)) * kLn2;
 }
 
 // Schedule shared by the launcher and the workspace helper.  Prefill and
@@ -748,6 +796,12 @@ SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   const int lmax = max(1, window + k);
   if (prefill || T >= 256) return SplitPlan{true, 1};
   return SplitPlan{false, (lmax + kSpan - 1) / kSpan};
+}
+
+// Decode workspace: the FP32 partials [T][splits][H][D] and their (max, sum)
+// pairs [T][splits][H].
+inline size_t attn_ws_bytes(int T, int splits, int H, int D) {
+  return static_cast<size_t>(T) * splits * H * (D + 2) * sizeof(float);
 }
 
 template <int D>
@@ -767,7 +821,7 @@ int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
   if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   if (a.splits > 1) {
     const long long mgrid = static_cast<long long>(a.num_tokens) * a.H;
-    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3(static_cast<unsigned>(mgrid)), dim3(128), 0, st,
+    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3(static_cast<unsigned>(mgrid)), dim3(64), 0, st,
                        a.part_o, a.part_ml, a.sink, a.splits, a.H, a.num_tokens, a.out, a.lse);
     if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   }
@@ -835,12 +889,13 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   a.splits = plan.splits;
   a.err = err;
   if (plan.splits > 1) {
-    const size_t need = static_cast<size_t>(num_tokens) * plan.splits * H * (D + 2) * sizeof(float);
+    const size_t need = attn_ws_bytes(num_tokens, plan.splits, H, D);
     if (!workspace || workspace_bytes < need) return CSA_ERR_WORKSPACE;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                          static_cast<size_t>(num_tokens) * plan.splits * H * D *
-                                              sizeof(float));
+    if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
+    char* w = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(w);
+    a.part_ml = reinterpret_cast<float2*>(w + static_cast<size_t>(num_tokens) * plan.splits * H *
+                                                  D * sizeof(float));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (D) {
@@ -860,7 +915,7 @@ extern "C" size_t csa_sparse_attn_workspace_bytes(int32_t T, int32_t H, int32_t 
   if (T <= 0 || H <= 0 || D <= 0 || k < 0 || window < 0) return 0;
   const csa::SplitPlan plan = csa::plan_splits(T, k, window, false);
   if (plan.splits <= 1) return 0;
-  return static_cast<size_t>(T) * plan.splits * H * (D + 2) * sizeof(float);
+  return csa::attn_ws_bytes(T, plan.splits, H, D);
 }
 
 extern "C" int csa_sparse_attn_decode(

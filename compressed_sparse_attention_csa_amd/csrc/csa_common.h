@@ -46,6 +46,31 @@ __device__ __forceinline__ int owner_request(const int32_t* __restrict__ qsl, in
   return lo;
 }
 
+// owner_request with one memory round trip when B < 64, in two halves so
+// other loads can be issued between them: every lane of the wave loads one
+// entry of query_start_loc, then a ballot counts the entries <= t.  Both
+// halves must be called by all 64 lanes of a wave with the same t.
+__device__ __forceinline__ int qsl_lane_load(const int32_t* __restrict__ qsl, int B) {
+  const int lane = threadIdx.x & 63;
+  return (B < 64 && lane <= B) ? qsl[lane] : 0x7fffffff;
+}
+
+__device__ __forceinline__ int owner_from_lanes(int v, const int32_t* __restrict__ qsl, int B,
+                                                int t) {
+  if (B >= 64) return owner_request(qsl, B, t);
+  if (B <= 0) return -1;
+  const int lane = threadIdx.x & 63;
+  const uint64_t le = __ballot(v <= t);
+  const int first = __builtin_amdgcn_readfirstlane(lane == 0 ? v : 0);
+  const int last = __builtin_amdgcn_readlane(v, B);
+  if (t < first || t >= last) return -1;
+  return __popcll(le) - 1;   // qsl is nondecreasing: the entries <= t are a prefix
+}
+
+__device__ __forceinline__ int owner_request_wave(const int32_t* __restrict__ qsl, int B, int t) {
+  return owner_from_lanes(qsl_lane_load(qsl, B), qsl, B, t);
+}
+
 __device__ __forceinline__ void flag_error(int32_t* err, int bits) {
   if (err != nullptr && bits) atomicOr(err, bits);
 }

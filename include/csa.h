@@ -184,7 +184,10 @@ int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions
  *   attn_sink    FP32 [H]
  *   out          BF16 [T, H, D]  (round to nearest even of the FP32 result)
  *   lse          FP32 [T, H] or NULL
- *   workspace    csa_sparse_attn_workspace_bytes(T, H, D, k, window) bytes
+ *   workspace    csa_sparse_attn_workspace_bytes(T, H, D, k, window) bytes,
+ *                16-byte aligned (NULL when that size is 0); scratch for the
+ *                split partials, always written before it is read (calls
+ *                that overlap on different streams need separate workspaces).
  *
  * Row t of request b at position p attends, with every head, over the window
  * rows at raw positions [max(0, p - window + 1), p] followed by the selected

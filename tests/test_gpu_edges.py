@@ -225,7 +225,7 @@ def test_attention_shapes(H_, D, R, off):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     for fn in ("decode", "prefill"):
         ws_n = csa.csa_sparse_attn_workspace_bytes(cfg.T, H_, D, cfg.k, cfg.W)
-        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
         getattr(csa, "csa_sparse_attn_" + fn)(
             q, dev(rc), dev(rs), off, torch.from_numpy(x["cmp_kv"].view(np.int16)).cuda(),
             dev(x["cmp_block_table"]), dev(sel), cfg.ratio,
@@ -239,3 +239,14 @@ def test_attention_shapes(H_, D, R, off):
                                         x["positions"], cfg.T)
         assert int(err.item()) == oe == 0
         H.check_attn(H.bf16_to_f64(out), oo, lse.cpu().numpy(), ol, f"{fn} H{H_} D{D}")
+        if ws_n:
+            # the same workspace, dirty from the first call, serves a second
+            first = out.clone()
+            getattr(csa, "csa_sparse_attn_" + fn)(
+                q, dev(rc), dev(rs), off, torch.from_numpy(x["cmp_kv"].view(np.int16)).cuda(),
+                dev(x["cmp_block_table"]), dev(sel), cfg.ratio,
+                torch.from_numpy(x["win_kv"].view(np.int16)).cuda(), dev(x["win_block_table"]),
+                cfg.W, dev(x["attn_sink"]), cfg.softmax_scale, dev(x["query_start_loc"]),
+                dev(x["positions"]), cfg.T, out, lse=lse, workspace=ws, err=err)
+            torch.cuda.synchronize()
+            assert torch.equal(first, out), "second call on the same workspace differs"
