@@ -52,7 +52,25 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="one input copy (cache-warm timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy five times (the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counts)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """Five plain device-to-device copies of 256 MiB: each reads and writes
+    exactly 268,435,456 bytes, so FETCH_SIZE / WRITE_SIZE per dispatch of this
+    copy give the counters' scale factor."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -192,6 +210,9 @@ def cpu_baseline(cfg, x, budget_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs the CSA step on one GPU; --gpus {args.gpus} is not "
               "supported (the multi-GPU sharding is a design note only).", file=sys.stderr)
@@ -280,8 +301,11 @@ def main():
                 "traffic": measured_traffic(dom, cfg.name),
                 "algorithmic_per_launch": wm["flops"]["attn"], "avg_launch_ms": stage_ms[dom]}
     else:
+        long_rows = cfg.score_stride > 32768
         names = {"rope": "rope_rows_kernel", "index": "index_score_kernel",
-                 "topk": "topk_kernel", "attn": "attn_kernel + attn_merge_kernel"}
+                 "topk": ("topk_range + topk_hist + topk_filter + topk_final" if long_rows
+                          else "topk_small_kernel"),
+                 "attn": "attn_decode_kernel + attn_merge_kernel"}
         ach = wm["stage_bytes"][dom] / (stage_ms[dom] / 1e3) / 1e9
         roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
