@@ -119,6 +119,19 @@ __device__ int block_excl_scan(int v, int* wsum, int* total) {
   return before + incl - v;
 }
 
+// Work-group barrier for LDS ordering only.  __syncthreads() is a
+// work-group release/acquire: with direct-to-LDS loads in flight it waits for
+// ALL of them (vmcnt(0)), which would drain the tile ring at every barrier.
+// Here each wave first waits for its own LDS operations (lgkmcnt(0)); the
+// caller waits explicitly (vmcnt) for exactly the tiles the next phase reads.
+// The signal fences keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int LPW>
 __device__ __forceinline__ void wait_tiles_behind(int behind) {
   // at most `behind` later tiles (LPW loads each) may still be in flight
@@ -145,6 +158,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   __shared__ uint32_t row_s[kMaxSplit];   // pool row of each valid entry (bit 31: window pool)
   __shared__ int scan_s[kAttnWaves];
   __shared__ int err_s;
+  __shared__ float rope_s[2 * kAttnThreads];   // rope row of t: cos, then sin
 
   // XCD-aware work mapping: consecutive rows land on one XCD.
   const int L = blockIdx.x;
@@ -161,8 +175,26 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
 
   if (tid == 0) err_s = 0;
 
-  const int b = owner_request_wave(a.qsl, a.B, t);
+  // metadata loads first, then the query and the rope row (vector memory
+  // returns in order: these complete during the row resolution, and nothing
+  // that depends on them is loaded after the tile gathers start)
+  const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
+  const int h = h0 + col;
+  const bool hv = wave_active && h < a.H;
+  v4i qraw[KS];
+  {
+    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = hv ? *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8) : v4i{0, 0, 0, 0};
+  }
+  float rcv = 0.0f, rsv = 0.0f;
+  if (tid < a.half_rope) {
+    rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + tid];
+    rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + tid];
+  }
+  const int b = owner_from_lanes(qsl_v, a.qsl, a.B, t);
   const int nv = visible_count(p, a.ratio);
   int w_len = 0, w_lo = 0;
   if (b >= 0 && p >= 0 && a.window > 0) {
@@ -210,7 +242,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
     if (ebits) atomicOr(&err_s, ebits);
   }
 
-  __syncthreads();  // row_s ready
+  if (tid < a.half_rope) {
+    rope_s[tid] = rcv;
+    rope_s[kAttnThreads + tid] = rsv;
+  }
+  __syncthreads();  // row_s and rope_s ready
 
   // ---- direct-to-LDS gather of one 32-row tile into ring slot tt % kRing.
   //      Lane l of a wave-wide load moves chunk l % NC of row l / NC; each
@@ -221,16 +257,20 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
   auto issue = [&](int tt) {
     uint8_t* slot = kv_s + (tt % kRing) * TS;
+    uint32_t rr[LPW];
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int j = tt * kTile + (wave * LPW + u) * RPI + lane / NC;   // compacted entry
+      rr[u] = (j < n_valid) ? row_s[j] : kNoRow;
+    }
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int ins = wave * LPW + u;
-      const int j = tt * kTile + ins * RPI + lane / NC;   // compacted entry
-      const uint32_t rr = (j < n_valid) ? row_s[j] : kNoRow;
-      const uint8_t* src = dummy;
-      if (rr != kNoRow)
-        src = reinterpret_cast<const uint8_t*>(
-            (rr & kWinBit) ? a.win_kv + static_cast<long long>(rr & ~kWinBit) * D
-                           : a.cmp_kv + static_cast<long long>(rr) * D);
+      const uint32_t r = rr[u];
+      const uint16_t* pool = (r & kWinBit) ? a.win_kv : a.cmp_kv;
+      const uint8_t* row = reinterpret_cast<const uint8_t*>(
+          pool + static_cast<long long>(r & ~kWinBit) * D);
+      const uint8_t* src = (r == kNoRow) ? dummy : row;
       __builtin_amdgcn_global_load_lds(
           src + (lane % NC) * 16, (__attribute__((address_space(3))) void*)(slot + ins * GS), 16,
           0, 0);
@@ -249,42 +289,35 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   for (int tt = 0; tt < min(kRing, ntiles); ++tt) issue(tt);
 
   // ---- query fragments (B operand of S^T): lane (head col, group grp) holds
-  //      channels ks*32 + grp*8 .. +8, rotated where they fall in the rope span.
+  //      channels ks*32 + grp*8 .. +8, rotated where they fall in the rope span
+  //      (rope values from LDS, so nothing here waits on the gathers).
   v8bf qf[KS];
-  {
-    const int h = h0 + col;
-    const bool hv = wave_active && h < a.H;
-    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
-    const float* rc = a.rope_cos + static_cast<long long>(t) * a.half_rope;
-    const float* rs = a.rope_sin + static_cast<long long>(t) * a.half_rope;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = ks * 32 + grp * 8;
-      v4i raw = hv ? *reinterpret_cast<const v4i*>(qrow + d0) : v4i{0, 0, 0, 0};
-      const int r0 = d0 - a.rope_offset;
-      if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
-        uint16_t e[8];
-        *reinterpret_cast<v4i*>(e) = raw;
+  for (int ks = 0; ks < KS; ++ks) {
+    v4i raw = qraw[ks];
+    const int r0 = ks * 32 + grp * 8 - a.rope_offset;
+    if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
+      uint16_t e[8];
+      *reinterpret_cast<v4i*>(e) = raw;
 #pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const int rr = r0 + 2 * pr;
-          if (rr >= 0 && rr < 2 * a.half_rope) {
-            const float c = rc[rr >> 1], s = rs[rr >> 1];
-            const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
-            e[2 * pr] = f32_to_bf16(x * c - y * s);
-            e[2 * pr + 1] = f32_to_bf16(x * s + y * c);
-          }
+      for (int pr = 0; pr < 4; ++pr) {
+        const int rr = r0 + 2 * pr;
+        if (rr >= 0 && rr < 2 * a.half_rope) {
+          const float c = rope_s[rr >> 1], sn = rope_s[kAttnThreads + (rr >> 1)];
+          const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
+          e[2 * pr] = f32_to_bf16(x * c - y * sn);
+          e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
         }
-        raw = *reinterpret_cast<v4i*>(e);
       }
-      qf[ks] = as_v8bf(raw);
+      raw = *reinterpret_cast<v4i*>(e);
     }
+    qf[ks] = as_v8bf(raw);
   }
 
   for (int tt = 0; tt < ntiles; ++tt) {
     const int issued = min(ntiles, tt + kRing);
     wait_tiles_behind<LPW>(issued - tt - 1);
-    __syncthreads();
+    lds_barrier();   // every wave's share of tile tt has landed
     const uint8_t* tile = kv_s + (tt % kRing) * TS;
 
     if (wave_active) {
@@ -366,15 +399,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __syncthreads();               // every wave is done with this slot
+    lds_barrier();                 // every wave is done with this slot
     if (tt + kRing < ntiles) issue(tt + kRing);
   }
 
   if (tid == 0 && err_s) flag_error(a.err, err_s);
   if (b < 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
-  if (!wave_active) return;
-  const int h = h0 + col;
-  if (h >= a.H) return;
+  if (!wave_active || h >= a.H) return;
 
   {
     const float sink2 = a.sink[h] * kLog2e;
