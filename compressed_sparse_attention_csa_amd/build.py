@@ -24,6 +24,9 @@ ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
+# per-source flags: the indexer's MFMA results feed a per-element VALU
+# epilogue, so they are kept in VGPRs (AGPR results would need a copy each)
+SOURCE_FLAGS = {"csa_index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -35,7 +38,8 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    extra = SOURCE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *COMMON, *DEVICE_FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

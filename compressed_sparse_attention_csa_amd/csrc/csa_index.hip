@@ -9,14 +9,18 @@
 // Mapping.  Work-groups are (request, up to 4 of its rows) x (a run of
 // 128-key pages); wave w owns one query row and computes its heads as 16-row
 // MFMA tiles (M = heads, N = keys, K = Di), so a key page staged once in LDS
-// feeds every row of the group.  The block ids of the run's pages are read up
-// front, and while a page is scored from LDS the next page is already on its
-// way into registers (software pipelining), so HBM latency overlaps the MFMA
-// and epilogue work.  LDS rows are 128 bytes with XOR-swizzled 16-byte chunks
-// (conflict-free MFMA operand reads).  INT32 accumulators stay in registers:
-// the epilogue applies ReLU, the folded weight w*qs, reduces the heads (16 in
-// lane, then across the four 16-lane groups) and scales by ks.  Pages past
-// every row's visible span only receive -inf.
+// feeds every row of the group.  Pages stream through a 3-stage LDS ring
+// filled by direct-to-LDS loads (two pages in flight behind the one being
+// scored, three work-groups per CU); the barriers between pages order LDS only, so the loads stay in
+// flight across them.  LDS rows are 128 bytes with XOR-swizzled 16-byte
+// chunks (conflict-free operand reads), the swizzle applied by choosing each
+// lane's source chunk.  INT32 accumulators stay in registers: the epilogue
+// applies ReLU and the folded weight w*qs per head, the head sums of eight
+// 16-key subtiles are finished together with two rounds of cross-lane swaps
+// (gfx950 permlane32/permlane16), and each lane scales its two keys by ks and
+// stores them.  Pages past every row's visible span only receive -inf.
+#include <type_traits>
+
 #include "csa_common.h"
 
 namespace csa {
@@ -25,9 +29,11 @@ namespace {
 
 constexpr int kRowsPerWG = 4;
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;   // LDS bytes per key (Di <= 128, zero padded)
-constexpr int kMaxPPW = 16;      // pages per work-group
-constexpr int kChunksPerThread = (kPage * 8) / kThreads;  // 16-byte chunks staged per thread
+constexpr int kRowBytes = 128;   // LDS bytes per key (Di <= 128, padded)
+constexpr int kMaxPPW = 64;      // pages per work-group
+constexpr int kStages = 3;       // key pages resident in LDS (in flight or in use)
+constexpr int kLoadsPerWave = kPage * kRowBytes / (64 * 16) / (kThreads / 64);  // per page
+constexpr int kVmPerPage = kLoadsPerWave + 1;   // + one load of 32 key scales
 
 __device__ __forceinline__ int swz_chunk(int key, int chunk) {
   return chunk ^ ((key >> 1) & 7);
@@ -81,6 +87,55 @@ __device__ int locate_group(const int32_t* __restrict__ qsl, int B, int num_toke
   return -1;
 }
 
+// s_waitcnt for "at most n vector-memory operations outstanding", n known at
+// run time (small): one case per immediate.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vm_rt(int n) {
+  switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    case 6: wait_vm<6>(); break;
+    case 7: wait_vm<7>(); break;
+    case 8: wait_vm<8>(); break;
+    case 9: wait_vm<9>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 12: wait_vm<12>(); break;
+    case 13: wait_vm<13>(); break;
+    case 14: wait_vm<14>(); break;
+    case 15: wait_vm<15>(); break;
+    case 16: wait_vm<16>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
+
+// Work-group barrier that orders LDS only (see the attention kernels: a
+// __syncthreads() would wait for every direct-to-LDS load in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ float lane_add_swap32(float x, float y) {
+  // lanes 0-31: x[l] + x[l+32]; lanes 32-63: y[l-32] + y[l]
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lane_add_swap16(float x, float y) {
+  // per 32-lane half: lanes 0-15: x[l] + x[l+16]; lanes 16-31: y[l-16] + y[l]
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int KK>
 __global__ void __launch_bounds__(kThreads) index_score_kernel(
     const int8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
@@ -89,8 +144,15 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
     int max_blocks, const int32_t* __restrict__ qsl, const int32_t* __restrict__ positions,
     int B, int num_tokens, int Hi, int Di, int ratio, float* __restrict__ scores,
     long long stride, int pages_per_wg, int32_t* err) {
-  __shared__ __attribute__((aligned(16))) int8_t keys_s[2][kPage * kRowBytes];
-  __shared__ float ks_s[2][kPage];
+  // one array per ring stage: with a single array indexed by a run-time
+  // stage, the compiler cannot tell which stage a direct-to-LDS load writes
+  // and drains every load in flight before each LDS read of keys
+  __shared__ __attribute__((aligned(16))) int8_t keys0[kPage * kRowBytes];
+  __shared__ __attribute__((aligned(16))) int8_t keys1[kPage * kRowBytes];
+  __shared__ __attribute__((aligned(16))) int8_t keys2[kPage * kRowBytes];
+  __shared__ __attribute__((aligned(16))) float ks0[kPage];
+  __shared__ __attribute__((aligned(16))) float ks1[kPage];
+  __shared__ __attribute__((aligned(16))) float ks2[kPage];
   __shared__ int blk_s[kMaxPPW];
   __shared__ int nvis_s[kRowsPerWG];
   __shared__ int scratch[kThreads / 64 + 2];
@@ -103,6 +165,7 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
   const int npages = static_cast<int>(min(static_cast<long long>(pages_per_wg),
                                           stride_pages - page0));
   if (npages <= 0) return;
+  const float neg_inf = -__builtin_huge_valf();
 
   int row0 = 0, nrows = 0;
   const int b = locate_group(qsl, B, num_tokens, blockIdx.y, &row0, &nrows, scratch);
@@ -110,7 +173,6 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
     // rows that no request owns: the first groups past the owned ones cover them
     const int owned_end = (B > 0) ? min(max(qsl[B], 0), num_tokens) : 0;
     const int owned_begin = (B > 0) ? min(max(qsl[0], 0), num_tokens) : 0;
-    // enumerate unowned rows in blocks of 4 after the owned groups
     int gfirst = 0;
     for (int bb = 0; bb < B; ++bb) {
       const int lo = min(max(qsl[bb], 0), num_tokens);
@@ -120,7 +182,6 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
     const int u = blockIdx.y - gfirst;  // index among unowned 4-row blocks
     const int n_unowned = owned_begin + (num_tokens - owned_end);
     if (u < 0 || u * kRowsPerWG >= n_unowned) return;
-    const float neg_inf = -__builtin_huge_valf();
     for (int r = 0; r < kRowsPerWG; ++r) {
       const int j = u * kRowsPerWG + r;
       if (j >= n_unowned) break;
@@ -194,84 +255,120 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
       }
     }
   }
-  __syncthreads();  // blk_s ready
+  __syncthreads();  // blk_s ready (no direct-to-LDS load is in flight yet)
 
-  // staging helpers: thread -> (key, chunk) pairs of one page
-  v4i pre[kChunksPerThread];
-  float pre_ks = 0.0f;
-  auto fetch = [&](int pi) {
+  // ---- page pi -> LDS stage pi % kStages with direct-to-LDS loads.  LDS
+  //      slot q of a page holds 16-byte chunk (q & 7) ^ ((key >> 1) & 7) of key
+  //      q >> 3 (the XOR swizzle that makes the operand reads conflict-free),
+  //      so each lane picks its source chunk.  Every wave issues exactly
+  //      kLoadsPerWave + 1 loads per page (pages with nothing to stage read a
+  //      dummy 16 bytes), which keeps the vmcnt bookkeeping uniform.
+  auto keys_of = [&](auto stg) -> int8_t* {
+    constexpr int S = decltype(stg)::value;
+    if constexpr (S == 0) return keys0;
+    else if constexpr (S == 1) return keys1;
+    else return keys2;
+  };
+  auto ks_of = [&](auto stg) -> float* {
+    constexpr int S = decltype(stg)::value;
+    if constexpr (S == 0) return ks0;
+    else if constexpr (S == 1) return ks1;
+    else return ks2;
+  };
+  auto issue = [&](int pi, auto stg) {
+    int8_t* keys = keys_of(stg);
+    float* ksd = ks_of(stg);
     const int blk = blk_s[pi];
-    if (blk < 0) return;
-    const int8_t* src = idx_kv + static_cast<long long>(blk) * kPage * Di;
+    const int8_t* pbase = idx_kv + static_cast<long long>(blk < 0 ? 0 : blk) * kPage * Di;
 #pragma unroll
-    for (int u = 0; u < kChunksPerThread; ++u) {
-      const int ch = tid + u * kThreads;
-      const int key = ch >> 3, c = ch & 7;
-      pre[u] = (c * 16 < Di) ? *reinterpret_cast<const v4i*>(src + key * Di + c * 16)
-                             : v4i{0, 0, 0, 0};
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      const int ins = wave * kLoadsPerWave + u;
+      const int q = ins * 64 + lane;
+      const int key = q >> 3;
+      int c = (q & 7) ^ ((key >> 1) & 7);
+      if (c * 16 >= Di) c = 0;   // padding slot: any bytes of the same key
+      const int8_t* src = blk >= 0 ? pbase + key * Di + c * 16 : q_idx;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(keys + ins * 1024), 16, 0, 0);
     }
-    if (tid < kPage) pre_ks = idx_scale[static_cast<long long>(blk) * kPage + tid];
-  };
-  auto store = [&](int pi, int buf) {
-    if (blk_s[pi] < 0) return;
-#pragma unroll
-    for (int u = 0; u < kChunksPerThread; ++u) {
-      const int ch = tid + u * kThreads;
-      const int key = ch >> 3, c = ch & 7;
-      *reinterpret_cast<v4i*>(&keys_s[buf][key * kRowBytes + swz_chunk(key, c) * 16]) = pre[u];
+    if (lane < 8) {   // key scales: wave w brings keys 32w .. 32w+31
+      const float* ssrc = blk >= 0
+                              ? idx_scale + static_cast<long long>(blk) * kPage + wave * 32 + lane * 4
+                              : reinterpret_cast<const float*>(q_idx);
+      __builtin_amdgcn_global_load_lds(
+          ssrc, (__attribute__((address_space(3))) void*)(ksd + wave * 32), 16, 0, 0);
     }
-    if (tid < kPage) ks_s[buf][tid] = pre_ks;
   };
 
-  const float neg_inf = -__builtin_huge_valf();
-  fetch(0);
-  store(0, 0);
-  if (npages > 1) fetch(1);
-  __syncthreads();
-  for (int pi = 0; pi < npages; ++pi) {
-    const int buf = pi & 1;
+  const int key_lo = (((grp & 1) << 1) | (grp >> 1)) * 16 + col;   // subtile order 0, 2, 1, 3
+  // one page: wait for it, barrier, refill the stage freed by the previous
+  // page, score this one
+  auto step = [&](int pi, auto stg) {
+    constexpr int S = decltype(stg)::value;
+    // page pi has landed once only the newer pages and the score stores
+    // issued since may still be in flight (vector memory completes in issue
+    // order).  Only the first of a page's two stores is sure to be issued
+    // (its lane for key 0 is always inside the row), so only it is counted:
+    // counting too few ops just waits a little longer.
+    const int newer = min(kStages - 2, npages - 1 - pi);
+    wait_vm_rt(__builtin_amdgcn_readfirstlane(kVmPerPage * newer +
+                                              (active ? min(kStages - 1, pi) : 0)));
+    lds_barrier();
+    if (pi + kStages - 1 < npages)
+      issue(pi + kStages - 1, std::integral_constant<int, (S + kStages - 1) % kStages>{});
+    if (!active) return;
+    const int8_t* keys = keys_of(stg);
+    const float* ksd = ks_of(stg);
     const int c0 = (page0 + pi) * kPage;
-    const bool staged = blk_s[pi] >= 0;
-    if (active) {
-      float* out_row = scores + static_cast<long long>(my_t) * stride;
-#pragma unroll 2
-      for (int s = 0; s < kPage / 16; ++s) {
-        const int kj = s * 16 + col;
-        const int c = c0 + kj;
-        float sc = neg_inf;
-        if (staged && c0 + s * 16 < my_n) {
-          v4i bk[KK];
+    float* out_row = scores + static_cast<long long>(my_t) * stride + c0;
+    float w0 = neg_inf, w1 = neg_inf;
+    if (blk_s[pi] >= 0 && c0 < my_n) {
+      float x[8];
+#pragma unroll
+      for (int sb = 0; sb < 8; ++sb) {
+        const int kj = sb * 16 + col;
+        v4i bk[KK];
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          bk[kk] = *reinterpret_cast<const v4i*>(
+              keys + kj * kRowBytes + swz_chunk(kj, kk * 4 + grp) * 16);
+        float xs = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          v4i acc = v4i{0, 0, 0, 0};
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk)
-            bk[kk] = *reinterpret_cast<const v4i*>(
-                &keys_s[buf][kj * kRowBytes + swz_chunk(kj, kk * 4 + grp) * 16]);
-          float x = 0.0f;
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][kk], bk[kk], acc, 0, 0, 0);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            v4i acc = v4i{0, 0, 0, 0};
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-              acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][kk], bk[kk], acc, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              x = fmaf(ww[mt][r], static_cast<float>(max(acc[r], 0)), x);
-          }
-          x += shfl_xor_f(x, 16);
-          x += shfl_xor_f(x, 32);
-          if (c < my_n) {
-            sc = ks_s[buf][kj] * x;
-            if (sc == 0.0f) sc = 0.0f;  // one zero: +0.0
-          }
+          for (int r = 0; r < 4; ++r)
+            xs = fmaf(ww[mt][r], static_cast<float>(max(acc[r], 0)), xs);
         }
-        if (grp == 0 && c < stride) out_row[c] = sc;
+        x[sb] = xs;
       }
+      // head sums over the four lane groups, 8 subtiles at once: lane l of
+      // w0 ends with key key_lo of this page, of w1 with key 64 + key_lo
+      const float z01 = lane_add_swap32(x[0], x[1]);
+      const float z23 = lane_add_swap32(x[2], x[3]);
+      const float z45 = lane_add_swap32(x[4], x[5]);
+      const float z67 = lane_add_swap32(x[6], x[7]);
+      w0 = lane_add_swap16(z01, z23);
+      w1 = lane_add_swap16(z45, z67);
+      w0 = (c0 + key_lo < my_n) ? ksd[key_lo] * w0 : neg_inf;
+      w1 = (c0 + 64 + key_lo < my_n) ? ksd[64 + key_lo] * w1 : neg_inf;
+      if (w0 == 0.0f) w0 = 0.0f;   // one zero: +0.0
+      if (w1 == 0.0f) w1 = 0.0f;
     }
-    // next page: registers -> other LDS buffer, then start the one after
-    if (pi + 1 < npages) {
-      store(pi + 1, buf ^ 1);
-      if (pi + 2 < npages) fetch(pi + 2);
-    }
-    __syncthreads();
+    if (c0 + key_lo < stride) out_row[key_lo] = w0;
+    if (c0 + 64 + key_lo < stride) out_row[64 + key_lo] = w1;
+  };
+
+  static_assert(kStages == 3, "the page loop is unrolled over three stages");
+  if (npages > 0) issue(0, std::integral_constant<int, 0>{});
+  if (npages > 1) issue(1, std::integral_constant<int, 1>{});
+  for (int pi = 0; pi < npages; pi += kStages) {
+    step(pi, std::integral_constant<int, 0>{});
+    if (pi + 1 < npages) step(pi + 1, std::integral_constant<int, 1>{});
+    if (pi + 2 < npages) step(pi + 2, std::integral_constant<int, 2>{});
   }
 }
 
@@ -301,9 +398,12 @@ extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const 
   const long long pages = (score_stride + csa::kPage - 1) / csa::kPage;
   // groups of <= 4 rows never straddle requests: at most ceil(T/4) + B of them
   const long long groups = (num_tokens + 3) / 4 + B;
-  // enough work-groups to fill 256 CUs several times over, few enough that
-  // each amortises loading its query rows over several pages
-  long long ppw = (pages * ((num_tokens + 3) / 4)) / 2048;
+  // one resident round of work-groups (three per CU on 256 CUs): short rows
+  // put every page in flight at once, long rows stream through each
+  // work-group's page ring; a grid just past one round would leave a
+  // straggler round, so pages per work-group round up
+  constexpr long long kSlots = 3 * 256;
+  long long ppw = (pages * ((num_tokens + 3) / 4) + kSlots - 1) / kSlots;
   if (ppw < 1) ppw = 1;
   if (ppw > csa::kMaxPPW) ppw = csa::kMaxPPW;
   const long long gx = (pages + ppw - 1) / ppw;
