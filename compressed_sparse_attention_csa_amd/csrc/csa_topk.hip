@@ -51,25 +51,25 @@ constexpr int kLThreads = 256;
 constexpr int kLWaves = kLThreads / 64;
 constexpr int kSub = kChunk / kLWaves;   // contiguous positions per wave
 constexpr int kLLoads = kSub / 256;      // 16-byte loads per lane
-constexpr int kLBins = 512;          // long-row histogram bins
 constexpr int kLCap = 2048;          // threshold-bin keys compacted into LDS
 constexpr int kRankMax = 256;        // up to this many are ranked directly
-constexpr int kCap = 8192;           // candidate slots per row
-constexpr int kFThreads = 1024;      // final kernel
+constexpr int kCap = 8192;           // candidates the final kernel selects among
+constexpr int kFThreads = 1024;      // sample and final kernels
 constexpr int kFPer = kCap / kFThreads;
-constexpr long long kMaxStride = 1ll << 24;   // long rows: <= 8,192 segments
-constexpr int kMetaWords = 8;
-constexpr int kMetaMax = 0;          // max finite key
-constexpr int kMetaMinInv = 1;       // max of ~(finite key)
-constexpr int kMetaCount = 2;        // candidates appended
+constexpr int kSampleGroups = 4096;  // float4 groups a row's sample reads (4 per thread)
+constexpr long long kMaxStride = 1ll << 24;
+constexpr int kMetaWords = 8;        // [0]: the row's sampled threshold key
 constexpr uint32_t kKeyNegInf = 0x007fffffu;
 constexpr uint32_t kKeyPosInf = 0xff800000u;
 
+// Long-row workspace (no state survives a call; every word is written before
+// it is read): per row a threshold word, one candidate count per wave
+// segment, and one position slot per score (a segment owns the slots of its
+// own positions, so no counter is shared between work-groups).
 struct Workspace {
-  uint32_t* hist;   // [T][kLBins]
   uint32_t* meta;   // [T][kMetaWords]
-  uint2* seg;       // [T][nseg] (first candidate slot, count)
-  uint2* cand;      // [T][kCap] (key, position)
+  uint32_t* seg;    // [T][nseg]
+  uint32_t* cand;   // [T][stride]
   int nseg;         // segments per row: chunks * waves
 };
 
@@ -78,17 +78,16 @@ inline int segs_for(long long stride) {
 }
 
 inline size_t ws_bytes(int T, long long stride) {
-  return static_cast<size_t>(T) * (kLBins + kMetaWords) * sizeof(uint32_t) +
-         static_cast<size_t>(T) * segs_for(stride) * sizeof(uint2) +
-         static_cast<size_t>(T) * kCap * sizeof(uint2);
+  return static_cast<size_t>(T) * kMetaWords * sizeof(uint32_t) +
+         static_cast<size_t>(T) * segs_for(stride) * sizeof(uint32_t) +
+         static_cast<size_t>(T) * stride * sizeof(uint32_t);
 }
 
 inline Workspace ws_layout(void* base, int T, long long stride) {
   Workspace w;
   w.nseg = segs_for(stride);
-  w.hist = static_cast<uint32_t*>(base);
-  w.meta = w.hist + static_cast<size_t>(T) * kLBins;
-  w.seg = reinterpret_cast<uint2*>(w.meta + static_cast<size_t>(T) * kMetaWords);
+  w.meta = static_cast<uint32_t*>(base);
+  w.seg = w.meta + static_cast<size_t>(T) * kMetaWords;
   w.cand = w.seg + static_cast<size_t>(T) * w.nseg;
   return w;
 }
@@ -740,6 +739,56 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
 // ----------------------------------------------------------------------------
 // long rows
 // ----------------------------------------------------------------------------
+// Sampled threshold of a long row: one float4 group every `span` positions
+// (span a multiple of 256 that keeps the groups within kSampleGroups), S
+// samples in all.  The key tau of the r-th best sample, with r a few standard
+// deviations above m * S / n, leaves in expectation about 1.6 m keys >= tau
+// and fewer than m only with a probability of order 1e-4 for random data;
+// the final kernel checks the count and falls back to an exact whole-row
+// select when the sample misled it.
+__global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
+    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
+    int ratio, int num_tokens, int k, Workspace ws) {
+  __shared__ SelShared<kFThreads> sh;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (t >= num_tokens) return;
+  const int n = row_span(positions, t, ratio, stride, nullptr, false);
+  if (n <= kCap) return;
+  const float* row = scores + static_cast<long long>(t) * stride;
+  const long long span =
+      256ll * ((static_cast<long long>(n) + 256ll * kSampleGroups - 1) / (256ll * kSampleGroups));
+  const int G = static_cast<int>((n + span - 1) / span);   // groups, <= kSampleGroups
+  constexpr int KPT = 4 * (kSampleGroups / kFThreads);
+  // thread tid reads groups tid, tid + 1024, ...: its valid groups are a
+  // prefix, so its keys [0, nmine) are the samples it holds (components past
+  // the span take the lowest key, which never moves the r-th best)
+  uint32_t key[KPT];
+  int ng = 0;
+#pragma unroll
+  for (int i = 0; i < KPT / 4; ++i) {
+    const int g = tid + i * kFThreads;
+    const long long p0 = g * span;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (g < G) v = *reinterpret_cast<const float4*>(row + p0);
+    key[4 * i] = g < G ? order_key(v.x) : 0u;
+    key[4 * i + 1] = (g < G && p0 + 1 < n) ? order_key(v.y) : 0u;
+    key[4 * i + 2] = (g < G && p0 + 2 < n) ? order_key(v.z) : 0u;
+    key[4 * i + 3] = (g < G && p0 + 3 < n) ? order_key(v.w) : 0u;
+    ng += g < G ? 1 : 0;
+  }
+  const int nmine = 4 * ng;
+  int S = 0;
+  block_excl_scan<kFThreads / 64>(nmine, sh.wsum, &S);
+  const int m = min(k, n);
+  const float expect = static_cast<float>(m) * static_cast<float>(S) / static_cast<float>(n);
+  const int r = static_cast<int>(ceilf(expect + 3.0f * sqrtf(expect) + 4.0f));
+  uint32_t tau = 0u;   // every key is a candidate
+  if (r < S && find_cut<kFThreads, KPT>(key, nmine, r, sh, [&](int j) { return tid * KPT + j; }))
+    tau = sh.cut[0];
+  if (tid == 0) ws.meta[static_cast<size_t>(t) * kMetaWords] = tau;
+}
+
 // Lane `lane` of wave `wave` loads kLLoads 16-byte groups of the chunk at c0:
 // positions c0 + wave*kSub + 256*i + 4*lane, so each wave owns a contiguous
 // kSub-position run and position order is (i, lane, component).
@@ -762,12 +811,10 @@ __device__ __forceinline__ void load_chunk(const float* row, long long stride, i
   }
 #pragma unroll
   for (int i = 0; i < kLLoads; ++i) {
-    const int c = ck.first + 256 * i;
-    // keys past the span get the NaN code; callers mask them by position
-    ck.key[4 * i] = c < n ? order_key(v[i].x) : 0u;
-    ck.key[4 * i + 1] = c + 1 < n ? order_key(v[i].y) : 0u;
-    ck.key[4 * i + 2] = c + 2 < n ? order_key(v[i].z) : 0u;
-    ck.key[4 * i + 3] = c + 3 < n ? order_key(v[i].w) : 0u;
+    ck.key[4 * i] = order_key(v[i].x);
+    ck.key[4 * i + 1] = order_key(v[i].y);
+    ck.key[4 * i + 2] = order_key(v[i].z);
+    ck.key[4 * i + 3] = order_key(v[i].w);
   }
 }
 
@@ -775,81 +822,11 @@ __device__ __forceinline__ bool in_span(const ChunkKeys& ck, int j, int n) {
   return ck.first + 256 * (j >> 2) + (j & 3) < n;
 }
 
-__global__ void __launch_bounds__(kLThreads) topk_range_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, Workspace ws) {
-  __shared__ uint32_t red[2][kLWaves];
-  const int t = blockIdx.y;
-  if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, nullptr, false);
-  const int c0 = blockIdx.x * kChunk;
-  if (n <= kCap || c0 >= n) return;
-  ChunkKeys ck;
-  load_chunk(scores + static_cast<long long>(t) * stride, stride, n, c0, ck);
-  uint32_t fmin = 0xffffffffu, fmax = 0u;
-#pragma unroll
-  for (int j = 0; j < 4 * kLLoads; ++j) {
-    if (key_finite(ck.key[j])) {   // keys past the span carry the NaN code
-      fmin = min(fmin, ck.key[j]);
-      fmax = max(fmax, ck.key[j]);
-    }
-  }
-  fmin = wave_min_u(fmin);
-  fmax = wave_max_u(fmax);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    red[0][wave] = fmin;
-    red[1][wave] = fmax;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int w = 0; w < kLWaves; ++w) {
-      fmin = min(fmin, red[0][w]);
-      fmax = max(fmax, red[1][w]);
-    }
-    uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
-    if (fmax != 0u) atomicMax(&meta[kMetaMax], fmax);
-    if (fmin != 0xffffffffu) atomicMax(&meta[kMetaMinInv], ~fmin);
-  }
-}
-
-__device__ __forceinline__ Binner row_binner(const uint32_t* meta) {
-  const uint32_t kfmax = meta[kMetaMax];
-  const uint32_t kfmin = ~meta[kMetaMinInv];   // no finite key: 0xffffffff > kfmax
-  return make_binner(kfmin, kfmax, kLBins);
-}
-
-__global__ void __launch_bounds__(kLThreads) topk_hist_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, Workspace ws) {
-  __shared__ uint32_t hist[kLBins + 64];   // + one dummy bin per lane
-  const int t = blockIdx.y;
-  const int tid = threadIdx.x;
-  if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, nullptr, false);
-  const int c0 = blockIdx.x * kChunk;
-  if (n <= kCap || c0 >= n) return;
-  ChunkKeys ck;
-  load_chunk(scores + static_cast<long long>(t) * stride, stride, n, c0, ck);
-  const Binner bn = row_binner(ws.meta + static_cast<size_t>(t) * kMetaWords);
-  for (int i = tid; i < kLBins + 64; i += kLThreads) hist[i] = 0u;
-  __syncthreads();
-  const int dummy = kLBins + (tid & 63);
-#pragma unroll
-  for (int j = 0; j < 4 * kLLoads; ++j)
-    atomicAdd(&hist[in_span(ck, j, n) ? bn(ck.key[j]) : dummy], 1u);
-  __syncthreads();
-  uint32_t* gh = ws.hist + static_cast<size_t>(t) * kLBins;
-  for (int i = tid; i < kLBins; i += kLThreads)
-    if (hist[i]) atomicAdd(&gh[i], hist[i]);
-}
-
+// Keep every key >= tau: each wave writes its kept positions, in position
+// order, into the slots of its own segment and its count into seg[].
 __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
     const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, int k, Workspace ws) {
-  __shared__ int wsum[2 * kLWaves + 1];
-  __shared__ int bsel;
+    int ratio, int num_tokens, Workspace ws) {
   const int t = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -860,37 +837,7 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
   if (n <= kCap || c0 >= n) return;
   ChunkKeys ck;
   load_chunk(scores + static_cast<long long>(t) * stride, stride, n, c0, ck);
-  uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
-  const Binner bn = row_binner(meta);
-
-  // bin of the m-th key, from the row histogram (every work-group of the row
-  // computes the same answer): thread tid sums bins [lo, lo + kPer) from the top
-  const uint32_t* gh = ws.hist + static_cast<size_t>(t) * kLBins;
-  constexpr int kPer = kLBins / kLThreads;
-  const int lo = kLBins - (tid + 1) * kPer;
-  uint32_t h[kPer];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    h[i] = gh[lo + i];
-    s += static_cast<int>(h[i]);
-  }
-  const int m = min(k, n);
-  int run = block_excl_scan<kLWaves>(s, wsum, nullptr);
-  if (run < m && run + s >= m) {
-    for (int i = kPer - 1; i >= 0; --i) {
-      if (run + static_cast<int>(h[i]) >= m) {
-        bsel = lo + i;
-        break;
-      }
-      run += static_cast<int>(h[i]);
-    }
-  }
-  __syncthreads();
-  const int b = bsel;
-
-  // keep keys in or above bin b; the wave's kept keys form one segment in
-  // position order (i, lane, component)
+  const uint32_t tau = ws.meta[static_cast<size_t>(t) * kMetaWords];
   int cnt[kLLoads];
   int off[kLLoads];
   int wave_total = 0;
@@ -899,35 +846,25 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
   for (int i = 0; i < kLLoads; ++i) {
     int c = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool keep = in_span(ck, 4 * i + q, n) && bn(ck.key[4 * i + q]) >= b;
-      c += keep ? 1 : 0;
-    }
+    for (int q = 0; q < 4; ++q) c += (in_span(ck, 4 * i + q, n) && ck.key[4 * i + q] >= tau) ? 1 : 0;
     cnt[i] = c;
     const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
     off[i] = wave_total + __popcll(b0 & below) + 2 * __popcll(b1 & below) +
              4 * __popcll(b2 & below);
     wave_total += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
   }
-  uint32_t slot0 = 0u;
-  if (lane == 0 && wave_total > 0)
-    slot0 = atomicAdd(&meta[kMetaCount], static_cast<uint32_t>(wave_total));
-  slot0 = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(slot0), 0));
-  if (lane == 0)
-    ws.seg[static_cast<size_t>(t) * ws.nseg + blockIdx.x * kLWaves + wave] =
-        make_uint2(slot0, static_cast<uint32_t>(wave_total));
-  uint2* cand = ws.cand + static_cast<size_t>(t) * kCap;
+  const int sidx = blockIdx.x * kLWaves + wave;
+  if (lane == 0) ws.seg[static_cast<size_t>(t) * ws.nseg + sidx] = static_cast<uint32_t>(wave_total);
+  uint32_t* slots = ws.cand + static_cast<size_t>(t) * stride + static_cast<size_t>(c0) + wave * kSub;
 #pragma unroll
   for (int i = 0; i < kLLoads; ++i) {
     if (cnt[i] == 0) continue;
-    uint32_t slot = slot0 + static_cast<uint32_t>(off[i]);
+    int o = off[i];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int j = 4 * i + q;
-      if (in_span(ck, j, n) && bn(ck.key[j]) >= b) {
-        if (slot < static_cast<uint32_t>(kCap))
-          cand[slot] = make_uint2(ck.key[j], static_cast<uint32_t>(ck.first + 256 * i + q));
-        ++slot;
+      if (in_span(ck, 4 * i + q, n) && ck.key[4 * i + q] >= tau) {
+        slots[o] = static_cast<uint32_t>(ck.first + 256 * i + q);
+        ++o;
       }
     }
   }
@@ -947,8 +884,6 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
   const float* row = scores + static_cast<long long>(t) * stride;
   int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
   float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
-  uint32_t* meta = ws.meta + static_cast<size_t>(t) * kMetaWords;
-  uint32_t* gh = ws.hist + static_cast<size_t>(t) * kLBins;
   const int m = min(k, n);
   if (m == n) {
     write_all<kFThreads>(n, k, row, out_i, out_v);
@@ -963,29 +898,30 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       }
       total = n;
     } else {
-      total = static_cast<int>(meta[kMetaCount]);
-      if (total > kCap) {
-        whole_row = true;
+      // candidates: the positions of the keys >= tau, each wave segment's in
+      // position order in the slots of its own positions
+      const int nseg = ((n + kChunk - 1) / kChunk) * kLWaves;
+      const int spt = (nseg + kFThreads - 1) / kFThreads;
+      const uint32_t* seg = ws.seg + static_cast<size_t>(t) * ws.nseg;
+      const uint32_t* cand = ws.cand + static_cast<size_t>(t) * stride;
+      int mine = 0;
+      for (int i = 0; i < spt; ++i) {
+        const int sidx = tid * spt + i;
+        if (sidx < nseg) mine += static_cast<int>(seg[sidx]);
+      }
+      int dst = block_excl_scan<kFThreads / 64>(mine, sh.wsum, &total);
+      if (total < m || total > kCap) {
+        whole_row = true;   // the sample misled: exact select over the row
       } else {
-        // segments in position order: scan their counts, copy each into place
-        const int nseg = ((n + kChunk - 1) / kChunk) * kLWaves;
-        const int spt = (nseg + kFThreads - 1) / kFThreads;
-        const uint2* seg = ws.seg + static_cast<size_t>(t) * ws.nseg;
-        const uint2* cand = ws.cand + static_cast<size_t>(t) * kCap;
-        int mine = 0;
-        for (int i = 0; i < spt; ++i) {
-          const int sidx = tid * spt + i;
-          if (sidx < nseg) mine += static_cast<int>(seg[sidx].y);
-        }
-        int dst = block_excl_scan<kFThreads / 64>(mine, sh.wsum, nullptr);
         for (int i = 0; i < spt; ++i) {
           const int sidx = tid * spt + i;
           if (sidx < nseg) {
-            const uint2 sg = seg[sidx];
-            for (uint32_t q = 0; q < sg.y; ++q) {
-              const uint2 e = cand[sg.x + q];
-              ckey[dst] = e.x;
-              cpos[dst] = e.y;
+            const uint32_t c = seg[sidx];
+            const uint32_t* src = cand + static_cast<size_t>(sidx) * kSub;
+            for (uint32_t q = 0; q < c; ++q) {
+              const uint32_t pos = src[q];
+              cpos[dst] = pos;
+              ckey[dst] = order_key(row[pos]);
               ++dst;
             }
           }
@@ -1009,10 +945,6 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
         select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh);
     }
   }
-  // leave the row's histogram and counters zero for the next call
-  if (n > kCap)
-    for (int i = tid; i < kLBins; i += kFThreads) gh[i] = 0u;
-  if (tid < kMetaWords) meta[tid] = 0u;
 }
 
 }  // namespace
@@ -1053,12 +985,10 @@ extern "C" int csa_topk(const float* scores, int64_t score_stride, const int32_t
     const csa::Workspace ws = csa::ws_layout(workspace, T, stride);
     const dim3 grid(static_cast<unsigned>((stride + csa::kChunk - 1) / csa::kChunk),
                     static_cast<unsigned>(num_tokens));
-    hipLaunchKernelGGL(csa::topk_range_kernel, grid, dim3(csa::kLThreads), 0, st, scores, stride,
-                       positions, ratio, num_tokens, ws);
-    hipLaunchKernelGGL(csa::topk_hist_kernel, grid, dim3(csa::kLThreads), 0, st, scores, stride,
-                       positions, ratio, num_tokens, ws);
+    hipLaunchKernelGGL(csa::topk_sample_kernel, dim3(num_tokens), dim3(csa::kFThreads), 0, st,
+                       scores, stride, positions, ratio, num_tokens, k, ws);
     hipLaunchKernelGGL(csa::topk_filter_kernel, grid, dim3(csa::kLThreads), 0, st, scores,
-                       stride, positions, ratio, num_tokens, k, ws);
+                       stride, positions, ratio, num_tokens, ws);
     hipLaunchKernelGGL(csa::topk_final_kernel, dim3(num_tokens), dim3(csa::kFThreads), 0, st,
                        scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, ws,
                        err);

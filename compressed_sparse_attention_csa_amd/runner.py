@@ -54,8 +54,7 @@ class CsaStep:
         self.lse = torch.empty((T, H), **f32) if with_lse else None
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         tw = _lib.csa_topk_workspace_bytes(T, self.score_stride, self.k)
-        # zero-filled once; the library leaves it zero-filled after every call
-        self.topk_ws = torch.zeros(tw, dtype=torch.uint8, device=dev) if tw else None
+        self.topk_ws = torch.empty(tw, dtype=torch.uint8, device=dev) if tw else None
         aw = 0 if prefill else _lib.csa_sparse_attn_workspace_bytes(T, H, D, self.k, self.window)
         self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=dev) if aw else None
 

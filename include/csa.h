@@ -147,18 +147,19 @@ int csa_index_score(const int8_t* q_idx, const float* q_scale, const float* head
  *              then -1
  *   topk_val   FP32 [T, k] or NULL: the chosen scores, -inf for padding
  *   workspace  device scratch of csa_topk_workspace_bytes(T, score_stride, k)
- *              bytes (may be NULL when that size is 0). It must be zero-filled
- *              before its first use; every call restores the zero state it
- *              relies on (histograms and counters), so one workspace serves any
- *              number of calls on one stream (calls that overlap on different
- *              streams need separate workspaces).
+ *              bytes, 16-byte aligned (may be NULL when that size is 0): per
+ *              row a threshold word, one count per 2,048 positions and one
+ *              4-byte slot per score. No state survives a call, so it needs no
+ *              initialisation (calls that overlap on different streams need
+ *              separate workspaces).
  *
  * Ranking: score descending, ties to the lower position; -0.0 equals +0.0;
  * NaN ranks below every number. Supported: 1 <= k <= 4096, score_stride a
- * multiple of 4, scores 16-byte aligned. Rows whose span exceeds 32,768 use a
- * multi-work-group path (histogram, candidate filter, final select); with more
- * than 8,192 candidates in the threshold bin (massive exact ties) that row
- * falls back to an exact whole-row pass.
+ * multiple of 4 and at most 2^24, scores 16-byte aligned. Rows whose span
+ * exceeds 8,192 in a launch with score_stride > 32,768 take a three-kernel
+ * path (sampled threshold, candidate filter, exact select among the
+ * candidates); when the sample leaves fewer than min(k, n) or more than 8,192
+ * candidates, that row falls back to an exact whole-row select.
  */
 size_t csa_topk_workspace_bytes(int32_t T, int64_t score_stride, int32_t k);
 int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions,
