@@ -56,7 +56,7 @@ constexpr int kRankMax = 256;        // up to this many are ranked directly
 constexpr int kCap = 8192;           // candidates the final kernel selects among
 constexpr int kFThreads = 1024;      // sample and final kernels
 constexpr int kFPer = kCap / kFThreads;
-constexpr int kSampleGroups = 4096;  // float4 groups a row's sample reads (4 per thread)
+constexpr int kSampleGroups = 2048;  // float4 groups a row's sample reads (2 per thread)
 constexpr long long kMaxStride = 1ll << 24;
 constexpr int kMetaWords = 8;        // [0]: the row's sampled threshold key
 constexpr uint32_t kKeyNegInf = 0x007fffffu;
@@ -64,12 +64,12 @@ constexpr uint32_t kKeyPosInf = 0xff800000u;
 
 // Long-row workspace (no state survives a call; every word is written before
 // it is read): per row a threshold word, one candidate count per wave
-// segment, and one position slot per score (a segment owns the slots of its
-// own positions, so no counter is shared between work-groups).
+// segment, and one (key, position) slot per score (a segment owns the slots
+// of its own positions, so no counter is shared between work-groups).
 struct Workspace {
   uint32_t* meta;   // [T][kMetaWords]
   uint32_t* seg;    // [T][nseg]
-  uint32_t* cand;   // [T][stride]
+  uint2* cand;      // [T][stride]
   int nseg;         // segments per row: chunks * waves
 };
 
@@ -78,9 +78,9 @@ inline int segs_for(long long stride) {
 }
 
 inline size_t ws_bytes(int T, long long stride) {
-  return static_cast<size_t>(T) * kMetaWords * sizeof(uint32_t) +
-         static_cast<size_t>(T) * segs_for(stride) * sizeof(uint32_t) +
-         static_cast<size_t>(T) * stride * sizeof(uint32_t);
+  const size_t words = static_cast<size_t>(T) * kMetaWords + static_cast<size_t>(T) * segs_for(stride);
+  return ((words * sizeof(uint32_t) + 15) & ~size_t(15)) +
+         static_cast<size_t>(T) * stride * sizeof(uint2);
 }
 
 inline Workspace ws_layout(void* base, int T, long long stride) {
@@ -88,7 +88,9 @@ inline Workspace ws_layout(void* base, int T, long long stride) {
   w.nseg = segs_for(stride);
   w.meta = static_cast<uint32_t*>(base);
   w.seg = w.meta + static_cast<size_t>(T) * kMetaWords;
-  w.cand = w.seg + static_cast<size_t>(T) * w.nseg;
+  const size_t words = static_cast<size_t>(T) * kMetaWords + static_cast<size_t>(T) * w.nseg;
+  w.cand = reinterpret_cast<uint2*>(static_cast<char*>(base) +
+                                    ((words * sizeof(uint32_t) + 15) & ~size_t(15)));
   return w;
 }
 
@@ -822,8 +824,8 @@ __device__ __forceinline__ bool in_span(const ChunkKeys& ck, int j, int n) {
   return ck.first + 256 * (j >> 2) + (j & 3) < n;
 }
 
-// Keep every key >= tau: each wave writes its kept positions, in position
-// order, into the slots of its own segment and its count into seg[].
+// Keep every key >= tau: each wave writes its kept (key, position) pairs, in
+// position order, into the slots of its own segment and its count into seg[].
 __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
     const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
     int ratio, int num_tokens, Workspace ws) {
@@ -855,7 +857,7 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
   }
   const int sidx = blockIdx.x * kLWaves + wave;
   if (lane == 0) ws.seg[static_cast<size_t>(t) * ws.nseg + sidx] = static_cast<uint32_t>(wave_total);
-  uint32_t* slots = ws.cand + static_cast<size_t>(t) * stride + static_cast<size_t>(c0) + wave * kSub;
+  uint2* slots = ws.cand + static_cast<size_t>(t) * stride + static_cast<size_t>(c0) + wave * kSub;
 #pragma unroll
   for (int i = 0; i < kLLoads; ++i) {
     if (cnt[i] == 0) continue;
@@ -863,7 +865,7 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (in_span(ck, 4 * i + q, n) && ck.key[4 * i + q] >= tau) {
-        slots[o] = static_cast<uint32_t>(ck.first + 256 * i + q);
+        slots[o] = make_uint2(ck.key[4 * i + q], static_cast<uint32_t>(ck.first + 256 * i + q));
         ++o;
       }
     }
@@ -903,7 +905,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       const int nseg = ((n + kChunk - 1) / kChunk) * kLWaves;
       const int spt = (nseg + kFThreads - 1) / kFThreads;
       const uint32_t* seg = ws.seg + static_cast<size_t>(t) * ws.nseg;
-      const uint32_t* cand = ws.cand + static_cast<size_t>(t) * stride;
+      const uint2* cand = ws.cand + static_cast<size_t>(t) * stride;
       int mine = 0;
       for (int i = 0; i < spt; ++i) {
         const int sidx = tid * spt + i;
@@ -917,11 +919,11 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
           const int sidx = tid * spt + i;
           if (sidx < nseg) {
             const uint32_t c = seg[sidx];
-            const uint32_t* src = cand + static_cast<size_t>(sidx) * kSub;
+            const uint2* src = cand + static_cast<size_t>(sidx) * kSub;
             for (uint32_t q = 0; q < c; ++q) {
-              const uint32_t pos = src[q];
-              cpos[dst] = pos;
-              ckey[dst] = order_key(row[pos]);
+              const uint2 e = src[q];
+              ckey[dst] = e.x;
+              cpos[dst] = e.y;
               ++dst;
             }
           }

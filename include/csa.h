@@ -149,7 +149,7 @@ int csa_index_score(const int8_t* q_idx, const float* q_scale, const float* head
  *   workspace  device scratch of csa_topk_workspace_bytes(T, score_stride, k)
  *              bytes, 16-byte aligned (may be NULL when that size is 0): per
  *              row a threshold word, one count per 2,048 positions and one
- *              4-byte slot per score. No state survives a call, so it needs no
+ *              8-byte slot per score. No state survives a call, so it needs no
  *              initialisation (calls that overlap on different streams need
  *              separate workspaces).
  *
