@@ -303,7 +303,7 @@ def main():
     else:
         long_rows = cfg.score_stride > 32768
         names = {"rope": "rope_rows_kernel", "index": "index_score_kernel",
-                 "topk": ("topk_range + topk_hist + topk_filter + topk_final" if long_rows
+                 "topk": ("topk_sample_kernel + topk_filter_kernel + topk_final_kernel" if long_rows
                           else "topk_small_kernel"),
                  "attn": "attn_decode_kernel + attn_merge_kernel"}
         ach = wm["stage_bytes"][dom] / (stage_ms[dom] / 1e3) / 1e9

@@ -32,6 +32,8 @@
 // the B operand of the P*V product (the key order inside the MFMA is permuted
 // identically on both operands).  The rotated query stays in registers as the
 // B operand of S^T.
+#include <type_traits>
+
 #include "csa_common.h"
 
 namespace csa {
@@ -154,7 +156,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   constexpr int GS = RPI * RB + 16;          // LDS stride of one load's rows (+16 B pad)
   constexpr int TS = (kTile / RPI) * GS;     // LDS bytes per tile
   static_assert(kRing == 4, "wait_tiles_behind assumes a ring of 4");
-  __shared__ __attribute__((aligned(16))) uint8_t kv_s[kRing * TS];
+  // one array per ring slot: with a single array indexed by a run-time slot
+  // the compiler cannot tell which slot a direct-to-LDS load writes, and
+  // drains every load in flight before the transposed V reads of each tile
+  __shared__ __attribute__((aligned(16))) uint8_t kv0[TS];
+  __shared__ __attribute__((aligned(16))) uint8_t kv1[TS];
+  __shared__ __attribute__((aligned(16))) uint8_t kv2[TS];
+  __shared__ __attribute__((aligned(16))) uint8_t kv3[TS];
   __shared__ uint32_t row_s[kMaxSplit];   // pool row of each valid entry (bit 31: window pool)
   __shared__ int scan_s[kAttnWaves];
   __shared__ int err_s;
@@ -255,18 +263,33 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   //      dummy bytes (the query) so every wave issues exactly LPW loads per
   //      tile; P = 0 keeps them out of the result.
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
-  auto issue = [&](int tt) {
-    uint8_t* slot = kv_s + (tt % kRing) * TS;
-    uint32_t rr[LPW];
+  auto slot_of = [&](auto sl) -> uint8_t* {
+    constexpr int S = decltype(sl)::value;
+    if constexpr (S == 0) return kv0;
+    else if constexpr (S == 1) return kv1;
+    else if constexpr (S == 2) return kv2;
+    else return kv3;
+  };
+  // tile tt goes to ring slot tt % kRing, passed as a compile-time constant.
+  // fetch() reads the tile's pool rows from LDS, launch() issues its loads;
+  // the prologue fetches the rows of the first kRing tiles before launching
+  // any of them (an LDS read issued after a direct-to-LDS load makes the
+  // compiler wait for that load to land).
+  auto fetch = [&](int tt, uint32_t* rr) {
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int j = tt * kTile + (wave * LPW + u) * RPI + lane / NC;   // compacted entry
       rr[u] = (j < n_valid) ? row_s[j] : kNoRow;
     }
+  };
+  auto launch = [&](auto sl, const uint32_t* rr) {
+    uint8_t* slot = slot_of(sl);
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int ins = wave * LPW + u;
-      const uint32_t r = rr[u];
+      // with one row per load the row is the same for the whole wave: its
+      // address is computed once, on the scalar unit
+      const uint32_t r = (RPI == 1) ? __builtin_amdgcn_readfirstlane(rr[u]) : rr[u];
       const uint16_t* pool = (r & kWinBit) ? a.win_kv : a.cmp_kv;
       const uint8_t* row = reinterpret_cast<const uint8_t*>(
           pool + static_cast<long long>(r & ~kWinBit) * D);
@@ -275,6 +298,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
           src + (lane % NC) * 16, (__attribute__((address_space(3))) void*)(slot + ins * GS), 16,
           0, 0);
     }
+  };
+  auto issue = [&](int tt, auto sl) {
+    uint32_t rr[LPW];
+    fetch(tt, rr);
+    launch(sl, rr);
   };
   auto row_off = [](int r) { return (r / RPI) * GS + (r % RPI) * RB; };
 
@@ -286,7 +314,17 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   for (int i = 0; i < DT; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int ntiles = (n_valid + kTile - 1) / kTile;
-  for (int tt = 0; tt < min(kRing, ntiles); ++tt) issue(tt);
+  {
+    uint32_t r0[LPW], r1[LPW], r2[LPW], r3[LPW];
+    fetch(0, r0);
+    fetch(1, r1);
+    fetch(2, r2);
+    fetch(3, r3);
+    if (ntiles > 0) launch(std::integral_constant<int, 0>{}, r0);
+    if (ntiles > 1) launch(std::integral_constant<int, 1>{}, r1);
+    if (ntiles > 2) launch(std::integral_constant<int, 2>{}, r2);
+    if (ntiles > 3) launch(std::integral_constant<int, 3>{}, r3);
+  }
 
   // ---- query fragments (B operand of S^T): lane (head col, group grp) holds
   //      channels ks*32 + grp*8 .. +8, rotated where they fall in the rope span
@@ -314,13 +352,16 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
     qf[ks] = as_v8bf(raw);
   }
 
-  for (int tt = 0; tt < ntiles; ++tt) {
+  auto tile_step = [&](int tt, auto sl) {
     const int issued = min(ntiles, tt + kRing);
     wait_tiles_behind<LPW>(issued - tt - 1);
     lds_barrier();   // every wave's share of tile tt has landed
-    const uint8_t* tile = kv_s + (tt % kRing) * TS;
+    const uint8_t* tile = slot_of(sl);
 
-    if (wave_active) {
+    {
+      // every wave runs the tile (a wave past the last head multiplies the
+      // zero query it loaded and writes nothing): a branch here would make
+      // the compiler copy the output accumulators at every tile
       // S^T tile: rows = 32 keys (two 16-row M tiles), columns = 16 heads.
       // M-tile mt row i holds key mt*16 + i/4 + 4*(i%4), so the four keys a
       // lane group later needs for one transposed V read are 4 rows apart.
@@ -400,7 +441,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
       }
     }
     lds_barrier();                 // every wave is done with this slot
-    if (tt + kRing < ntiles) issue(tt + kRing);
+    if (tt + kRing < ntiles) issue(tt + kRing, sl);
+  };
+  static_assert(kRing == 4, "the tile loop is unrolled over four ring slots");
+  for (int tt = 0; tt < ntiles; tt += kRing) {
+    tile_step(tt, std::integral_constant<int, 0>{});
+    if (tt + 1 < ntiles) tile_step(tt + 1, std::integral_constant<int, 1>{});
+    if (tt + 2 < ntiles) tile_step(tt + 2, std::integral_constant<int, 2>{});
+    if (tt + 3 < ntiles) tile_step(tt + 3, std::integral_constant<int, 3>{});
   }
 
   if (tid == 0 && err_s) flag_error(a.err, err_s);

@@ -130,14 +130,9 @@ __device__ __forceinline__ float lane_add_swap32(float x, float y) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ float lane_add_swap16(float x, float y) {
-  // per 32-lane half: lanes 0-15: x[l] + x[l+16]; lanes 16-31: y[l-16] + y[l]
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int KK>
-__global__ void __launch_bounds__(kThreads) index_score_kernel(
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) index_score_kernel(
     const int8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ head_w, const int8_t* __restrict__ idx_kv,
     const float* __restrict__ idx_scale, int num_blocks, const int32_t* __restrict__ bt,
@@ -227,29 +222,33 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
   const bool active = wave < nrows;
   const int my_t = row0 + wave;
   const int my_n = nvis_s[wave];
-  const int col = lane & 15;
-  const int grp = lane >> 4;
+  const int col = lane & 31;    // MFMA column: key within a 32-key tile
+  const int half = lane >> 5;   // which 16-byte half of each 32-dim k-step
 
-  // A operand (this wave's query row) and folded head weights, loaded once
-  constexpr int MT = 4;
-  v4i qa[MT][KK];
-  float ww[MT][4];
+  // A operand (this wave's query row: 32-head tiles x 32-dim k-steps, lane
+  // (col, half) holding head mt*32 + col, dims ks*32 + half*16 .. +15) and
+  // the folded head weights w*qs in the MFMA result order (result j of lane
+  // (col, half) is head mt*32 + 8*(j/4) + 4*half + j%4), loaded once
+  constexpr int MT = 2;
+  constexpr int KS = 2 * KK;
+  v4i qa[MT][KS];
+  float ww[MT][16];
   if (active) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int h = mt * 16 + col;
+      const int h = mt * 32 + col;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int off = kk * 64 + grp * 16;
-        qa[mt][kk] = (h < Hi && off < Di)
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = ks * 32 + half * 16;
+        qa[mt][ks] = (h < Hi && off < Di)
                          ? *reinterpret_cast<const v4i*>(
                                q_idx + (static_cast<long long>(my_t) * Hi + h) * Di + off)
                          : v4i{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hh = mt * 16 + grp * 4 + r;
-        ww[mt][r] = (hh < Hi) ? head_w[static_cast<long long>(my_t) * Hi + hh] *
+      for (int j = 0; j < 16; ++j) {
+        const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        ww[mt][j] = (hh < Hi) ? head_w[static_cast<long long>(my_t) * Hi + hh] *
                                     q_scale[static_cast<long long>(my_t) * Hi + hh]
                               : 0.0f;
       }
@@ -300,7 +299,6 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
     }
   };
 
-  const int key_lo = (((grp & 1) << 1) | (grp >> 1)) * 16 + col;   // subtile order 0, 2, 1, 3
   // one page: wait for it, barrier, refill the stage freed by the previous
   // page, score this one
   auto step = [&](int pi, auto stg) {
@@ -323,43 +321,77 @@ __global__ void __launch_bounds__(kThreads) index_score_kernel(
     float* out_row = scores + static_cast<long long>(my_t) * stride + c0;
     float w0 = neg_inf, w1 = neg_inf;
     if (blk_s[pi] >= 0 && c0 < my_n) {
-      float x[8];
+      // eight (32-head, 32-key) tiles p = 2*nt + mt, software-pipelined: the
+      // MFMAs of tile p + 1 are interleaved with the epilogue of tile p.  One
+      // set of B registers: key tile nt + 1 is read from LDS as soon as the
+      // MFMAs of tile 2*nt + 1 (the last to use key tile nt) are issued.
+      float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      v4i bk[KS];
+      v16i acc[2];
+      auto load_b = [&](int nt) {
+        const int kj = nt * 32 + col;
 #pragma unroll
-      for (int sb = 0; sb < 8; ++sb) {
-        const int kj = sb * 16 + col;
-        v4i bk[KK];
+        for (int ks = 0; ks < KS; ++ks)
+          bk[ks] = *reinterpret_cast<const v4i*>(
+              keys + kj * kRowBytes + swz_chunk(kj, ks * 2 + half) * 16);
+      };
+      auto mfma_tile = [&](int p, v16i& a) {
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          bk[kk] = *reinterpret_cast<const v4i*>(
-              keys + kj * kRowBytes + swz_chunk(kj, kk * 4 + grp) * 16);
-        float xs = 0.0f;
+        for (int ks = 0; ks < KS; ++ks)
+          a = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[p & 1][ks], bk[ks],
+                                                    ks == 0 ? v16i{} : a, 0, 0, 0);
+      };
+      load_b(0);
+      mfma_tile(0, acc[0]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          v4i acc = v4i{0, 0, 0, 0};
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mt][kk], bk[kk], acc, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            xs = fmaf(ww[mt][r], static_cast<float>(max(acc[r], 0)), xs);
+      for (int p = 0; p < 8; ++p) {
+        // region p: MFMAs of tile p + 1, epilogue of tile p
+        const bool new_key_tile = ((p + 1) & 1) == 0;   // tile p + 1 needs fresh B registers
+        if (p + 1 < 8) {
+          if (new_key_tile) load_b((p + 1) >> 1);
+          mfma_tile(p + 1, acc[(p + 1) & 1]);
         }
-        x[sb] = xs;
+        float xs = x[p >> 1];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          xs = fmaf(ww[p & 1][j], static_cast<float>(max(acc[p & 1][j], 0)), xs);
+        x[p >> 1] = xs;
+        if (p + 1 < 8) {
+          // each MFMA is followed by a share of the epilogue, so the last
+          // one is done before the next region reads its results; a new key
+          // tile puts its LDS reads and a few epilogue ops first
+          constexpr int kLead = 8;
+          if (new_key_tile) {
+            __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kLead, 0);
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, (48 - kLead) / KS, 0);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < KS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one scheduling region per tile
       }
-      // head sums over the four lane groups, 8 subtiles at once: lane l of
-      // w0 ends with key key_lo of this page, of w1 with key 64 + key_lo
-      const float z01 = lane_add_swap32(x[0], x[1]);
-      const float z23 = lane_add_swap32(x[2], x[3]);
-      const float z45 = lane_add_swap32(x[4], x[5]);
-      const float z67 = lane_add_swap32(x[6], x[7]);
-      w0 = lane_add_swap16(z01, z23);
-      w1 = lane_add_swap16(z45, z67);
-      w0 = (c0 + key_lo < my_n) ? ksd[key_lo] * w0 : neg_inf;
-      w1 = (c0 + 64 + key_lo < my_n) ? ksd[64 + key_lo] * w1 : neg_inf;
+      // head sums: lanes l and l + 32 hold the two 32-head halves of the
+      // same key, so one swap per key pair finishes them; lane l of w0 ends
+      // with key l of this page, of w1 with key 64 + l
+      w0 = lane_add_swap32(x[0], x[1]);
+      w1 = lane_add_swap32(x[2], x[3]);
+      w0 = (c0 + lane < my_n) ? ksd[lane] * w0 : neg_inf;
+      w1 = (c0 + 64 + lane < my_n) ? ksd[64 + lane] * w1 : neg_inf;
       if (w0 == 0.0f) w0 = 0.0f;   // one zero: +0.0
       if (w1 == 0.0f) w1 = 0.0f;
     }
-    if (c0 + key_lo < stride) out_row[key_lo] = w0;
-    if (c0 + 64 + key_lo < stride) out_row[64 + key_lo] = w1;
+    if (c0 + lane < stride) out_row[lane] = w0;
+    if (c0 + 64 + lane < stride) out_row[64 + lane] = w1;
   };
 
   static_assert(kStages == 3, "the page loop is unrolled over three stages");
