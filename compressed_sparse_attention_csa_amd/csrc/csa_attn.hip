@@ -167,6 +167,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   __shared__ int scan_s[kAttnWaves];
   __shared__ int err_s;
   __shared__ float rope_s[2 * kAttnThreads];   // rope row of t: cos, then sin
+  __shared__ v4i p_s[kAttnWaves][64];          // P^T fragments of the current tile
+  __shared__ float f_s[64];                    // per-head output factor
+  __shared__ int ovf_s[kAttnWaves];
 
   // XCD-aware work mapping: consecutive rows land on one XCD.
   const int L = blockIdx.x;
@@ -307,24 +310,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   auto row_off = [](int r) { return (r / RPI) * GS + (r % RPI) * RB; };
 
   const float neg_inf = -__builtin_huge_valf();
-  float m_run = neg_inf;  // running max of this lane's head (base-2 logits)
-  float l_run = 0.0f;     // running sum
-  v4f o_acc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-
   const int ntiles = (n_valid + kTile - 1) / kTile;
-  {
-    uint32_t r0[LPW], r1[LPW], r2[LPW], r3[LPW];
-    fetch(0, r0);
-    fetch(1, r1);
-    fetch(2, r2);
-    fetch(3, r3);
-    if (ntiles > 0) launch(std::integral_constant<int, 0>{}, r0);
-    if (ntiles > 1) launch(std::integral_constant<int, 1>{}, r1);
-    if (ntiles > 2) launch(std::integral_constant<int, 2>{}, r2);
-    if (ntiles > 3) launch(std::integral_constant<int, 3>{}, r3);
-  }
 
   // ---- query fragments (B operand of S^T): lane (head col, group grp) holds
   //      channels ks*32 + grp*8 .. +8, rotated where they fall in the rope span
@@ -352,128 +338,221 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
     qf[ks] = as_v8bf(raw);
   }
 
-  auto tile_step = [&](int tt, auto sl) {
-    const int issued = min(ntiles, tt + kRing);
+  // ---- P*V side: wave w owns channels [w*DW, (w+1)*DW) of every head, so
+  //      each byte of a V tile is read through the transposed path by one
+  //      wave only; the four 16-head P^T fragments come through LDS.
+  constexpr int DW = D / kAttnWaves;   // channels per wave
+  constexpr int DTW = DW / 16;         // 16-channel O^T tiles per wave
+  constexpr int HT = kAttnWaves;       // 16-head tiles (64 heads)
+  const int d0 = wave * DW;
+  v4f o_acc[DTW][HT];
+
+  // Softmax against a fixed reference: m_ref is the first tile's max, and
+  // P = exp2(logit - m_ref) needs no rescaling of O as later tiles arrive
+  // while no logit passes m_ref by more than kOvf (P then stays below
+  // 2^kOvf, far inside BF16 and FP32 range).  A row where one does is run
+  // again with m_ref set to its exact max, which the first pass recorded.
+  constexpr float kOvf = 64.0f;
+  float m_ref = neg_inf;    // this lane's head (base-2 logits)
+  float m_seen = neg_inf;   // exact max over the whole list
+  float l_run = 0.0f;
+  bool ovf = false;
+
+  // The first barrier of a tile makes tile tt visible to every wave and
+  // tells them all that tile tt - 1 is finished, so its slot can take tile
+  // tt + 3; the second one publishes the tile's P.  LDS operand reads run ahead of the MFMAs
+  // that use them, since with one wave per SIMD nothing else hides their
+  // latency.
+  auto tile_step = [&](int tt, int pass, auto sl) {
+    constexpr int S = decltype(sl)::value;
+    const int issued = min(ntiles, tt + kRing - 1);   // tiles issued before this barrier
     wait_tiles_behind<LPW>(issued - tt - 1);
-    lds_barrier();   // every wave's share of tile tt has landed
+    lds_barrier();
     const uint8_t* tile = slot_of(sl);
 
-    {
-      // every wave runs the tile (a wave past the last head multiplies the
-      // zero query it loaded and writes nothing): a branch here would make
-      // the compiler copy the output accumulators at every tile
-      // S^T tile: rows = 32 keys (two 16-row M tiles), columns = 16 heads.
-      // M-tile mt row i holds key mt*16 + i/4 + 4*(i%4), so the four keys a
-      // lane group later needs for one transposed V read are 4 rows apart.
-      v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
-      const int krow = (col >> 2) + 4 * (col & 3);
-      const uint8_t* k0p = tile + row_off(krow) + grp * 16;
-      const uint8_t* k1p = tile + row_off(16 + krow) + grp * 16;
+    // S^T tile: rows = 32 keys (two 16-row M tiles), columns = this wave's
+    // 16 heads.  M-tile mt row i holds key mt*16 + i/4 + 4*(i%4), so the four
+    // keys a lane group later needs for one transposed V read are 4 rows
+    // apart.  Every wave runs the tile (a wave past the last head multiplies
+    // the zero query it loaded and its results are never written).
+    constexpr int PF = 4;   // K steps read ahead
+    const int krow = (col >> 2) + 4 * (col & 3);
+    const uint8_t* k0p = tile + row_off(krow) + grp * 16;
+    const uint8_t* k1p = tile + row_off(16 + krow) + grp * 16;
+    v4i kb0[PF], kb1[PF];
 #pragma unroll
-      for (int kg = 0; kg < KS; kg += 4) {
-#pragma unroll
-        for (int ks = kg; ks < kg + 4 && ks < KS; ++ks) {
-          const v8bf a0 = as_v8bf(*reinterpret_cast<const v4i*>(k0p + ks * 64));
-          const v8bf a1 = as_v8bf(*reinterpret_cast<const v4i*>(k1p + ks * 64));
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // lane (head col, group grp) now holds keys grp + 4r (s0[r]) and
-      // 16 + grp + 4r (s1[r]) of the tile
-      float lg[8];
-      float tmax = neg_inf;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ja = tt * kTile + grp + 4 * r, jb = ja + 16;
-        lg[r] = ja < n_valid ? s0[r] * a.scale_log2 : neg_inf;
-        lg[4 + r] = jb < n_valid ? s1[r] * a.scale_log2 : neg_inf;
-        tmax = fmaxf(tmax, fmaxf(lg[r], lg[4 + r]));
-      }
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-      // the reference max only moves when the tile max passes it by more than
-      // kSlack (probabilities then stay <= 2^kSlack), so the accumulator is
-      // rescaled on few tiles
-      const bool grow = tmax > m_run + kSlack;
-      if (__ballot(grow) != 0ull) {
-        const float m_new = grow ? tmax : m_run;
-        const float alpha = (m_run == neg_inf) ? 0.0f : exp2f(m_run - m_new);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o_acc[dt] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = (m_run == neg_inf) ? 0.0f : m_run;
-      float psum = 0.0f;
-      uint16_t pb[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pj = exp2f(lg[j] - m_use);
-        psum += pj;
-        pb[j] = f32_to_bf16(pj);
-      }
-      psum += shfl_xor_f(psum, 16);
-      psum += shfl_xor_f(psum, 32);
-      l_run += psum;
-      const v8bf pf = as_v8bf(*reinterpret_cast<v4i*>(pb));
-      // V^T operand with transposed LDS reads: in lane group g, source lane
-      // 4e + q points at 8 bytes of key row (g + 4e) [then 16 + g + 4e],
-      // channels n0 + 4q .. +3; lane i of the group receives those rows'
-      // channel n0 + i -- the keys P^T holds in elements e and 4 + e.
-      const int e_src = (lane & 15) >> 2, q_src = lane & 3;
-      const uint8_t* v0p = tile + row_off(grp + 4 * e_src) + q_src * 8;
-      const uint8_t* v1p = tile + row_off(16 + grp + 4 * e_src) + q_src * 8;
-#pragma unroll
-      for (int dg = 0; dg < DT; dg += 8) {
-#pragma unroll
-        for (int dt = dg; dt < dg + 8 && dt < DT; ++dt) {
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(v0p + dt * 32));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(v1p + dt * 32));
-          const v8s va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o_acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, va), pf,
-                                                               o_acc[dt], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < PF && i < KS; ++i) {
+      kb0[i] = *reinterpret_cast<const v4i*>(k0p + i * 64);
+      kb1[i] = *reinterpret_cast<const v4i*>(k1p + i * 64);
     }
-    lds_barrier();                 // every wave is done with this slot
-    if (tt + kRing < ntiles) issue(tt + kRing, sl);
+    // two accumulators per M tile (even and odd K steps) keep the dependent
+    // MFMA chains short
+    v4f sacc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sacc[i][0] = sacc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const v4i x0 = kb0[ks % PF], x1 = kb1[ks % PF];
+      if (ks + PF < KS) {
+        kb0[ks % PF] = *reinterpret_cast<const v4i*>(k0p + (ks + PF) * 64);
+        kb1[ks % PF] = *reinterpret_cast<const v4i*>(k1p + (ks + PF) * 64);
+      }
+      sacc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x0), qf[ks],
+                                                                sacc[0][ks & 1], 0, 0, 0);
+      sacc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x1), qf[ks],
+                                                                sacc[1][ks & 1], 0, 0, 0);
+    }
+    // keep the K reads PF steps ahead of their MFMAs (left alone, the
+    // scheduler moves each read next to its use)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF < KS ? PF : KS), 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    const v4f s0 = sacc[0][0] + sacc[0][1];
+    const v4f s1 = sacc[1][0] + sacc[1][1];
+
+    // V^T operand with transposed LDS reads: in lane group g, source lane
+    // 4e + q points at 8 bytes of key row (g + 4e) [then 16 + g + 4e],
+    // channels n0 + 4q .. +3; lane i of the group receives those rows'
+    // channel n0 + i -- the keys P^T holds in elements e and 4 + e.  The
+    // first VPF channel tiles are read before the softmax, which does not
+    // need them.
+    constexpr int VPF = DTW < 4 ? DTW : 4;
+    const int e_src = (lane & 15) >> 2, q_src = lane & 3;
+    const uint8_t* v0p = tile + row_off(grp + 4 * e_src) + q_src * 8 + d0 * 2;
+    const uint8_t* v1p = tile + row_off(16 + grp + 4 * e_src) + q_src * 8 + d0 * 2;
+    v4s vlo[VPF], vhi[VPF];
+#pragma unroll
+    for (int i = 0; i < VPF; ++i) {
+      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(v0p + i * 32));
+      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(v1p + i * 32));
+    }
+
+    // lane (head col, group grp) holds keys grp + 4r (s0[r]) and
+    // 16 + grp + 4r (s1[r]) of the tile
+    float lg[8];
+    float tmax = neg_inf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ja = tt * kTile + grp + 4 * r, jb = ja + 16;
+      lg[r] = ja < n_valid ? s0[r] * a.scale_log2 : neg_inf;
+      lg[4 + r] = jb < n_valid ? s1[r] * a.scale_log2 : neg_inf;
+      tmax = fmaxf(tmax, fmaxf(lg[r], lg[4 + r]));
+    }
+    tmax = max_xor32(max_xor16(tmax));
+    m_seen = fmaxf(m_seen, tmax);
+    // the first tile always holds a valid key (valid entries are compacted
+    // to the front), so its max is finite
+    if (tt == 0 && pass == 0) m_ref = tmax;
+    ovf = ovf || tmax > m_ref + kOvf;
+    float psum = 0.0f;
+    uint16_t pb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pj = exp2f(lg[j] - m_ref);
+      psum += pj;
+      pb[j] = f32_to_bf16(pj);
+    }
+    psum = sum_xor32(sum_xor16(psum));
+    l_run += psum;
+    p_s[wave][lane] = *reinterpret_cast<v4i*>(pb);
+    lds_barrier();   // every head's P^T fragment of this tile is in LDS
+
+    // O^T += V^T P^T for this wave's channels and all four head tiles: each
+    // transposed V fragment feeds four MFMAs
+    v8bf pf[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) pf[ht] = as_v8bf(p_s[ht][lane]);
+    // the slot of tile tt - 1 takes tile tt + 3 (issued after the P reads: an
+    // LDS read that follows a direct-to-LDS load of the same barrier interval
+    // makes the compiler wait for the load)
+    if (tt + kRing - 1 < ntiles)
+      issue(tt + kRing - 1, std::integral_constant<int, (S + kRing - 1) % kRing>{});
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) {
+      const v4s lo = vlo[dt % VPF], hi = vhi[dt % VPF];
+      if (dt + VPF < DTW) {
+        vlo[dt % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(v0p + (dt + VPF) * 32));
+        vhi[dt % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(v1p + (dt + VPF) * 32));
+      }
+      const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        o_acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[ht], o_acc[dt][ht], 0, 0, 0);
+    }
   };
   static_assert(kRing == 4, "the tile loop is unrolled over four ring slots");
-  for (int tt = 0; tt < ntiles; tt += kRing) {
-    tile_step(tt, std::integral_constant<int, 0>{});
-    if (tt + 1 < ntiles) tile_step(tt + 1, std::integral_constant<int, 1>{});
-    if (tt + 2 < ntiles) tile_step(tt + 2, std::integral_constant<int, 2>{});
-    if (tt + 3 < ntiles) tile_step(tt + 3, std::integral_constant<int, 3>{});
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) o_acc[dt][ht] = v4f{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.0f;
+    ovf = false;
+    {
+      // tiles 0 .. kRing - 2 before the loop; each tile's first barrier then
+      // frees the previous tile's slot for the next one
+      uint32_t r0[LPW], r1[LPW], r2[LPW];
+      fetch(0, r0);
+      fetch(1, r1);
+      fetch(2, r2);
+      if (ntiles > 0) launch(std::integral_constant<int, 0>{}, r0);
+      if (ntiles > 1) launch(std::integral_constant<int, 1>{}, r1);
+      if (ntiles > 2) launch(std::integral_constant<int, 2>{}, r2);
+    }
+    for (int tt = 0; tt < ntiles; tt += kRing) {
+      tile_step(tt, pass, std::integral_constant<int, 0>{});
+      if (tt + 1 < ntiles) tile_step(tt + 1, pass, std::integral_constant<int, 1>{});
+      if (tt + 2 < ntiles) tile_step(tt + 2, pass, std::integral_constant<int, 2>{});
+      if (tt + 3 < ntiles) tile_step(tt + 3, pass, std::integral_constant<int, 3>{});
+    }
+    // a second pass only when a logit outran the first tile's max (no load
+    // is in flight here: the last tile waited for all of them)
+    if (lane == 0) ovf_s[wave] = (__ballot(ovf) != 0ull) ? 1 : 0;
+    __syncthreads();
+    const bool again = (ovf_s[0] | ovf_s[1] | ovf_s[2] | ovf_s[3]) != 0;
+    __syncthreads();
+    if (!again) break;
+    m_ref = m_seen;
   }
 
   if (tid == 0 && err_s) flag_error(a.err, err_s);
   if (b < 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
-  if (!wave_active || h >= a.H) return;
 
-  {
+  // per-head normalisation by the wave that owns the head's softmax
+  if (hv && grp == 0) {
     const float sink2 = a.sink[h] * kLog2e;
-    const float M = fmaxf(m_run, sink2);
-    const float corr = (m_run == neg_inf) ? 0.0f : exp2f(m_run - M);
+    const float M = fmaxf(m_ref, sink2);
+    const float corr = (m_ref == neg_inf) ? 0.0f : exp2f(m_ref - M);
     const float Z = l_run * corr + exp2f(sink2 - M);
-    const float f = corr / Z;
-    uint16_t* orow = a.out + (static_cast<long long>(t) * a.H + h) * D;
+    f_s[h] = corr / Z;
+    if (a.lse) a.lse[static_cast<long long>(t) * a.H + h] = (M + log2f(Z)) * kLn2;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      // o_acc[dt][r] is channel dt*16 + grp*4 + r of head h
+  for (int ht = 0; ht < HT; ++ht) {
+    const int hh = ht * 16 + col;
+    if (hh >= a.H) continue;
+    const float f = f_s[hh];
+    uint16_t* orow = a.out + (static_cast<long long>(t) * a.H + hh) * D + d0;
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) {
+      // o_acc[dt][ht][r] is channel d0 + dt*16 + grp*4 + r of head hh
       const int d = dt * 16 + grp * 4;
       uint2 w;
-      w.x = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][0] * f)) |
-            (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][1] * f)) << 16);
-      w.y = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][2] * f)) |
-            (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][3] * f)) << 16);
+      w.x = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][0] * f)) |
+            (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][1] * f)) << 16);
+      w.y = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][2] * f)) |
+            (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][3] * f)) << 16);
       *reinterpret_cast<uint2*>(orow + d) = w;
     }
-    if (a.lse && grp == 0) a.lse[static_cast<long long>(t) * a.H + h] = (M + log2f(Z)) * kLn2;
   }
 }
 
