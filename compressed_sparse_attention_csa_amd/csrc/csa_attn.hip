@@ -43,6 +43,8 @@ namespace {
 constexpr int kTile = 32;       // key rows per LDS tile
 constexpr int kAttnWaves = 4;   // 16 heads per wave
 constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kRingWaves = 8;   // ring kernel: 4 softmax waves + 4 P*V waves
+constexpr int kRingThreads = 64 * kRingWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -97,8 +99,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Exclusive scan over the 256-thread work-group (scratch: one int per wave).
-__device__ int block_excl_scan(int v, int* wsum, int* total) {
+// Exclusive scan over a work-group of NW waves (scratch: one int per wave).
+template <int NW>
+__device__ int block_excl_scan_n(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int incl = v;
@@ -112,13 +115,16 @@ __device__ int block_excl_scan(int v, int* wsum, int* total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kAttnWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int s = wsum[w];
     if (w < wave) before += s;
     tot += s;
   }
   *total = tot;
   return before + incl - v;
+}
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
+  return block_excl_scan_n<kAttnWaves>(v, wsum, total);
 }
 
 // Work-group barrier for LDS ordering only.  __syncthreads() is a
@@ -134,6 +140,32 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// block_excl_scan_n with LDS-only barriers (vector loads in flight are not
+// waited for).
+template <int NW>
+__device__ int block_excl_scan_lds(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  lds_barrier();   // wsum of the previous scan has been read
+  if (lane == 63) wsum[wave] = incl;
+  lds_barrier();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int s = wsum[w];
+    if (w < wave) before += s;
+    tot += s;
+  }
+  *total = tot;
+  return before + incl - v;
+}
+
 template <int LPW>
 __device__ __forceinline__ void wait_tiles_behind(int behind) {
   // at most `behind` later tiles (LPW loads each) may still be in flight
@@ -146,30 +178,34 @@ __device__ __forceinline__ void wait_tiles_behind(int behind) {
 }
 
 template <int D>
-__global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                 // K steps of S^T
-  constexpr int DT = D / 16;                 // d tiles of O^T
   constexpr int RB = 2 * D;                  // bytes per key row
   constexpr int NC = D / 8;                  // 16-byte chunks per row
   constexpr int RPI = 64 / NC;               // rows one wave-wide load moves
-  constexpr int LPW = kTile / RPI / kAttnWaves;  // loads per wave per tile
+  constexpr int LPT = kTile / RPI;           // loads per tile
+  constexpr int LPW = LPT >= kRingWaves ? LPT / kRingWaves : 1;   // loads per loading wave
+  constexpr int NLW = LPT / LPW;             // waves that load
   constexpr int GS = RPI * RB + 16;          // LDS stride of one load's rows (+16 B pad)
   constexpr int TS = (kTile / RPI) * GS;     // LDS bytes per tile
-  static_assert(kRing == 4, "wait_tiles_behind assumes a ring of 4");
+  constexpr int HT = 4;                      // 16-head tiles (64 heads)
+  constexpr int DW = D / 4;                  // channels per P*V wave
+  constexpr int DTW = DW / 16;               // 16-channel O^T tiles per P*V wave
+  static_assert(kRing == 4, "the step loop is unrolled over four ring slots");
   // one array per ring slot: with a single array indexed by a run-time slot
-  // the compiler cannot tell which slot a direct-to-LDS load writes, and
-  // drains every load in flight before the transposed V reads of each tile
+  // the compiler cannot tell which slot a direct-to-LDS load writes and
+  // drains every load in flight before LDS reads
   __shared__ __attribute__((aligned(16))) uint8_t kv0[TS];
   __shared__ __attribute__((aligned(16))) uint8_t kv1[TS];
   __shared__ __attribute__((aligned(16))) uint8_t kv2[TS];
   __shared__ __attribute__((aligned(16))) uint8_t kv3[TS];
   __shared__ uint32_t row_s[kMaxSplit];   // pool row of each valid entry (bit 31: window pool)
-  __shared__ int scan_s[kAttnWaves];
+  __shared__ int scan_s[kRingWaves];
   __shared__ int err_s;
-  __shared__ float rope_s[2 * kAttnThreads];   // rope row of t: cos, then sin
-  __shared__ v4i p_s[kAttnWaves][64];          // P^T fragments of the current tile
+  __shared__ float rope_s[2 * 256];            // rope row of t: cos, then sin
+  __shared__ v4i p_s[2][HT][64];               // P^T fragments, double-buffered by tile
   __shared__ float f_s[64];                    // per-head output factor
-  __shared__ int ovf_s[kAttnWaves];
+  __shared__ int ovf_s[HT];
 
   // XCD-aware work mapping: consecutive rows land on one XCD.
   const int L = blockIdx.x;
@@ -179,20 +215,21 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int col = lane & 15;  // head within the wave's 16 (B/C column index)
+  const int col = lane & 15;  // head within a 16-head tile (B/C column index)
   const int grp = lane >> 4;  // lane group
-  const int h0 = wave * 16;
-  const bool wave_active = h0 < a.H;
+  // waves 0-3 compute S and the softmax of heads 16w .. 16w+15; waves 4-7
+  // multiply P*V for channels (w-4)*D/4 .. of every head, one tile behind
+  const bool s_wave = wave < HT;
+  const int h0 = (wave & (HT - 1)) * 16;
+  const int h = h0 + col;
+  const bool hv = s_wave && h < a.H;
 
   if (tid == 0) err_s = 0;
 
-  // metadata loads first, then the query and the rope row (vector memory
-  // returns in order: these complete during the row resolution, and nothing
-  // that depends on them is loaded after the tile gathers start)
+  // metadata loads first, then the query, the rope row and the sink (vector
+  // memory returns in order: these complete during the row resolution)
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
-  const int h = h0 + col;
-  const bool hv = wave_active && h < a.H;
   v4i qraw[KS];
   {
     const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
@@ -205,6 +242,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
     rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + tid];
     rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + tid];
   }
+  const float sink2 = hv ? a.sink[h] * kLog2e : 0.0f;
   const int b = owner_from_lanes(qsl_v, a.qsl, a.B, t);
   const int nv = visible_count(p, a.ratio);
   int w_len = 0, w_lo = 0;
@@ -212,9 +250,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
     w_lo = max(0, p - a.window + 1);
     w_len = p - w_lo + 1;
   }
-  const int list_len = (b >= 0) ? (w_len + a.k) : 0;
-  const int n_my = list_len;
-  __syncthreads();
+  const int n_my = (b >= 0) ? (w_len + a.k) : 0;
+  // LDS-only barriers in the prologue: a __syncthreads() would also wait for
+  // the query loads still streaming in from HBM
+  lds_barrier();   // err_s is cleared
 
   // ---- resolve every entry of the key list through the block tables at once;
   //      valid rows are compacted to the front (softmax does not depend on
@@ -223,11 +262,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   int n_valid = 0;
   {
     int ebits = 0;
-    for (int j0 = 0; j0 < n_my; j0 += kAttnThreads) {
-      const int j = j0 + tid;
-      const int i = j;
+    for (int j0 = 0; j0 < n_my; j0 += kRingThreads) {
+      const int i = j0 + tid;
       uint32_t rr = kNoRow;
-      if (j >= n_my) {
+      if (i >= n_my) {
         // past the list: nothing to resolve
       } else if (i < w_len) {
         const long long r = page_row(a.win_bt + static_cast<long long>(b) * a.max_win_blocks,
@@ -246,7 +284,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
         }
       }
       int total = 0;
-      const int slot = n_valid + block_excl_scan(rr != kNoRow ? 1 : 0, scan_s, &total);
+      const int slot = n_valid + block_excl_scan_lds<kRingWaves>(rr != kNoRow ? 1 : 0, scan_s, &total);
       if (rr != kNoRow) row_s[slot] = rr;
       n_valid += total;
     }
@@ -255,17 +293,45 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
 
   if (tid < a.half_rope) {
     rope_s[tid] = rcv;
-    rope_s[kAttnThreads + tid] = rsv;
+    rope_s[256 + tid] = rsv;
   }
-  __syncthreads();  // row_s and rope_s ready
+  lds_barrier();  // row_s and rope_s ready
 
-  // ---- direct-to-LDS gather of one 32-row tile into ring slot tt % kRing.
-  //      Lane l of a wave-wide load moves chunk l % NC of row l / NC; each
-  //      load's rows start 16 bytes past the previous load's, which spreads the
-  //      K and V^T operand reads over the LDS banks.  Masked rows read finite
-  //      dummy bytes (the query) so every wave issues exactly LPW loads per
-  //      tile; P = 0 keeps them out of the result.
+  // ---- query fragments (B operand of S^T) of the S waves: lane (head col,
+  //      group grp) holds channels ks*32 + grp*8 .. +8, rotated where they
+  //      fall in the rope span
+  v8bf qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    v4i raw = qraw[ks];
+    const int r0 = ks * 32 + grp * 8 - a.rope_offset;
+    if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
+      uint16_t e[8];
+      *reinterpret_cast<v4i*>(e) = raw;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const int rr = r0 + 2 * pr;
+        if (rr >= 0 && rr < 2 * a.half_rope) {
+          const float c = rope_s[rr >> 1], sn = rope_s[256 + (rr >> 1)];
+          const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
+          e[2 * pr] = f32_to_bf16(x * c - y * sn);
+          e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
+        }
+      }
+      raw = *reinterpret_cast<v4i*>(e);
+    }
+    qf[ks] = as_v8bf(raw);
+  }
+
+  // ---- direct-to-LDS gather of one 32-row tile into ring slot tt % kRing
+  //      (a compile-time constant).  Lane l of a wave-wide load moves chunk
+  //      l % NC of row l / NC; each load's rows start 16 bytes past the
+  //      previous load's, which spreads the K and V^T operand reads over the
+  //      LDS banks.  Masked rows read finite dummy bytes (the query) so every
+  //      loading wave issues exactly LPW loads per tile; P = 0 keeps them out
+  //      of the result.
   const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
+  const bool loader = wave < NLW;
   auto slot_of = [&](auto sl) -> uint8_t* {
     constexpr int S = decltype(sl)::value;
     if constexpr (S == 0) return kv0;
@@ -273,20 +339,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
     else if constexpr (S == 2) return kv2;
     else return kv3;
   };
-  // tile tt goes to ring slot tt % kRing, passed as a compile-time constant.
-  // fetch() reads the tile's pool rows from LDS, launch() issues its loads;
-  // the prologue fetches the rows of the first kRing tiles before launching
-  // any of them (an LDS read issued after a direct-to-LDS load makes the
-  // compiler wait for that load to land).
-  auto fetch = [&](int tt, uint32_t* rr) {
+  auto issue = [&](int tt, auto sl) {
+    if (!loader) return;
+    uint8_t* slot = slot_of(sl);
+    uint32_t rr[LPW];
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int j = tt * kTile + (wave * LPW + u) * RPI + lane / NC;   // compacted entry
       rr[u] = (j < n_valid) ? row_s[j] : kNoRow;
     }
-  };
-  auto launch = [&](auto sl, const uint32_t* rr) {
-    uint8_t* slot = slot_of(sl);
 #pragma unroll
     for (int u = 0; u < LPW; ++u) {
       const int ins = wave * LPW + u;
@@ -302,50 +363,23 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
           0, 0);
     }
   };
-  auto issue = [&](int tt, auto sl) {
-    uint32_t rr[LPW];
-    fetch(tt, rr);
-    launch(sl, rr);
-  };
   auto row_off = [](int r) { return (r / RPI) * GS + (r % RPI) * RB; };
 
   const float neg_inf = -__builtin_huge_valf();
   const int ntiles = (n_valid + kTile - 1) / kTile;
 
-  // ---- query fragments (B operand of S^T): lane (head col, group grp) holds
-  //      channels ks*32 + grp*8 .. +8, rotated where they fall in the rope span
-  //      (rope values from LDS, so nothing here waits on the gathers).
-  v8bf qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    v4i raw = qraw[ks];
-    const int r0 = ks * 32 + grp * 8 - a.rope_offset;
-    if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
-      uint16_t e[8];
-      *reinterpret_cast<v4i*>(e) = raw;
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const int rr = r0 + 2 * pr;
-        if (rr >= 0 && rr < 2 * a.half_rope) {
-          const float c = rope_s[rr >> 1], sn = rope_s[kAttnThreads + (rr >> 1)];
-          const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
-          e[2 * pr] = f32_to_bf16(x * c - y * sn);
-          e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
-        }
-      }
-      raw = *reinterpret_cast<v4i*>(e);
-    }
-    qf[ks] = as_v8bf(raw);
-  }
-
-  // ---- P*V side: wave w owns channels [w*DW, (w+1)*DW) of every head, so
-  //      each byte of a V tile is read through the transposed path by one
-  //      wave only; the four 16-head P^T fragments come through LDS.
-  constexpr int DW = D / kAttnWaves;   // channels per wave
-  constexpr int DTW = DW / 16;         // 16-channel O^T tiles per wave
-  constexpr int HT = kAttnWaves;       // 16-head tiles (64 heads)
-  const int d0 = wave * DW;
-  v4f o_acc[DTW][HT];
+  // Step k (k = 0 .. ntiles) begins with the step's one barrier: by then
+  // every wave's loads of tile k have landed, the S waves have published
+  // P(k-1), and tile k-2 is finished, so its slot takes tile k+2.  The S
+  // waves then compute S(k) and P(k) while the P*V waves multiply tile k-1:
+  // each SIMD runs one wave of each kind.
+  auto step_sync = [&](int k, auto sl) {
+    constexpr int S = decltype(sl)::value;
+    // only tile k + 1 was issued after tile k
+    wait_tiles_behind<LPW>((k + 1 < ntiles) ? 1 : 0);
+    lds_barrier();
+    if (k + 2 < ntiles) issue(k + 2, std::integral_constant<int, (S + 2) % kRing>{});
+  };
 
   // Softmax against a fixed reference: m_ref is the first tile's max, and
   // P = exp2(logit - m_ref) needs no rescaling of O as later tiles arrive
@@ -356,204 +390,211 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_kernel(AttnArgs a) {
   float m_ref = neg_inf;    // this lane's head (base-2 logits)
   float m_seen = neg_inf;   // exact max over the whole list
   float l_run = 0.0f;
-  bool ovf = false;
 
-  // The first barrier of a tile makes tile tt visible to every wave and
-  // tells them all that tile tt - 1 is finished, so its slot can take tile
-  // tt + 3; the second one publishes the tile's P.  LDS operand reads run ahead of the MFMAs
-  // that use them, since with one wave per SIMD nothing else hides their
-  // latency.
-  auto tile_step = [&](int tt, int pass, auto sl) {
-    constexpr int S = decltype(sl)::value;
-    const int issued = min(ntiles, tt + kRing - 1);   // tiles issued before this barrier
-    wait_tiles_behind<LPW>(issued - tt - 1);
-    lds_barrier();
-    const uint8_t* tile = slot_of(sl);
-
-    // S^T tile: rows = 32 keys (two 16-row M tiles), columns = this wave's
-    // 16 heads.  M-tile mt row i holds key mt*16 + i/4 + 4*(i%4), so the four
-    // keys a lane group later needs for one transposed V read are 4 rows
-    // apart.  Every wave runs the tile (a wave past the last head multiplies
-    // the zero query it loaded and its results are never written).
-    constexpr int PF = 4;   // K steps read ahead
-    const int krow = (col >> 2) + 4 * (col & 3);
-    const uint8_t* k0p = tile + row_off(krow) + grp * 16;
-    const uint8_t* k1p = tile + row_off(16 + krow) + grp * 16;
-    v4i kb0[PF], kb1[PF];
-#pragma unroll
-    for (int i = 0; i < PF && i < KS; ++i) {
-      kb0[i] = *reinterpret_cast<const v4i*>(k0p + i * 64);
-      kb1[i] = *reinterpret_cast<const v4i*>(k1p + i * 64);
-    }
-    // two accumulators per M tile (even and odd K steps) keep the dependent
-    // MFMA chains short
-    v4f sacc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) sacc[i][0] = sacc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const v4i x0 = kb0[ks % PF], x1 = kb1[ks % PF];
-      if (ks + PF < KS) {
-        kb0[ks % PF] = *reinterpret_cast<const v4i*>(k0p + (ks + PF) * 64);
-        kb1[ks % PF] = *reinterpret_cast<const v4i*>(k1p + (ks + PF) * 64);
-      }
-      sacc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x0), qf[ks],
-                                                                sacc[0][ks & 1], 0, 0, 0);
-      sacc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x1), qf[ks],
-                                                                sacc[1][ks & 1], 0, 0, 0);
-    }
-    // keep the K reads PF steps ahead of their MFMAs (left alone, the
-    // scheduler moves each read next to its use)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF < KS ? PF : KS), 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    }
-    const v4f s0 = sacc[0][0] + sacc[0][1];
-    const v4f s1 = sacc[1][0] + sacc[1][1];
-
-    // V^T operand with transposed LDS reads: in lane group g, source lane
-    // 4e + q points at 8 bytes of key row (g + 4e) [then 16 + g + 4e],
-    // channels n0 + 4q .. +3; lane i of the group receives those rows'
-    // channel n0 + i -- the keys P^T holds in elements e and 4 + e.  The
-    // first VPF channel tiles are read before the softmax, which does not
-    // need them.
-    constexpr int VPF = DTW < 4 ? DTW : 4;
-    const int e_src = (lane & 15) >> 2, q_src = lane & 3;
-    const uint8_t* v0p = tile + row_off(grp + 4 * e_src) + q_src * 8 + d0 * 2;
-    const uint8_t* v1p = tile + row_off(16 + grp + 4 * e_src) + q_src * 8 + d0 * 2;
-    v4s vlo[VPF], vhi[VPF];
-#pragma unroll
-    for (int i = 0; i < VPF; ++i) {
-      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(v0p + i * 32));
-      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(v1p + i * 32));
-    }
-
-    // lane (head col, group grp) holds keys grp + 4r (s0[r]) and
-    // 16 + grp + 4r (s1[r]) of the tile
-    float lg[8];
-    float tmax = neg_inf;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ja = tt * kTile + grp + 4 * r, jb = ja + 16;
-      lg[r] = ja < n_valid ? s0[r] * a.scale_log2 : neg_inf;
-      lg[4 + r] = jb < n_valid ? s1[r] * a.scale_log2 : neg_inf;
-      tmax = fmaxf(tmax, fmaxf(lg[r], lg[4 + r]));
-    }
-    tmax = max_xor32(max_xor16(tmax));
-    m_seen = fmaxf(m_seen, tmax);
-    // the first tile always holds a valid key (valid entries are compacted
-    // to the front), so its max is finite
-    if (tt == 0 && pass == 0) m_ref = tmax;
-    ovf = ovf || tmax > m_ref + kOvf;
-    float psum = 0.0f;
-    uint16_t pb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float pj = exp2f(lg[j] - m_ref);
-      psum += pj;
-      pb[j] = f32_to_bf16(pj);
-    }
-    psum = sum_xor32(sum_xor16(psum));
-    l_run += psum;
-    p_s[wave][lane] = *reinterpret_cast<v4i*>(pb);
-    lds_barrier();   // every head's P^T fragment of this tile is in LDS
-
-    // O^T += V^T P^T for this wave's channels and all four head tiles: each
-    // transposed V fragment feeds four MFMAs
-    v8bf pf[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) pf[ht] = as_v8bf(p_s[ht][lane]);
-    // the slot of tile tt - 1 takes tile tt + 3 (issued after the P reads: an
-    // LDS read that follows a direct-to-LDS load of the same barrier interval
-    // makes the compiler wait for the load)
-    if (tt + kRing - 1 < ntiles)
-      issue(tt + kRing - 1, std::integral_constant<int, (S + kRing - 1) % kRing>{});
-#pragma unroll
-    for (int dt = 0; dt < DTW; ++dt) {
-      const v4s lo = vlo[dt % VPF], hi = vhi[dt % VPF];
-      if (dt + VPF < DTW) {
-        vlo[dt % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(v0p + (dt + VPF) * 32));
-        vhi[dt % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(v1p + (dt + VPF) * 32));
-      }
-      const v8bf va = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        o_acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[ht], o_acc[dt][ht], 0, 0, 0);
-    }
+  // both kinds of wave run the same barrier sequence: per pass, one barrier
+  // per step, then the overflow vote and the normalisation hand-off
+  auto prime = [&]() {
+    if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+    if (ntiles > 1) issue(1, std::integral_constant<int, 1>{});
   };
-  static_assert(kRing == 4, "the tile loop is unrolled over four ring slots");
 
-  for (int pass = 0; pass < 2; ++pass) {
+  if (s_wave) {
+    // the softmax waves are the critical path of every step: their
+    // instructions go first when both waves of a SIMD are ready
+    __builtin_amdgcn_s_setprio(2);
+    for (int pass = 0; pass < 2; ++pass) {
+      prime();
+      bool ovf = false;
+      l_run = 0.0f;
+      // S^T tile: rows = 32 keys (two 16-row M tiles), columns = this wave's
+      // 16 heads.  M-tile mt row i holds key mt*16 + i/4 + 4*(i%4), so the
+      // four keys a lane group later needs for one transposed V read are 4
+      // rows apart.  A wave past the last head multiplies its zero query.
+      auto s_step = [&](int k, auto sl) {
+        step_sync(k, sl);
+        if (k >= ntiles) return;
+        const uint8_t* tile = slot_of(sl);
+        constexpr int PF = 4;   // K steps read ahead
+        const int krow = (col >> 2) + 4 * (col & 3);
+        const uint8_t* k0p = tile + row_off(krow) + grp * 16;
+        const uint8_t* k1p = tile + row_off(16 + krow) + grp * 16;
+        v4i kb0[PF], kb1[PF];
 #pragma unroll
-    for (int dt = 0; dt < DTW; ++dt)
+        for (int i = 0; i < PF && i < KS; ++i) {
+          kb0[i] = *reinterpret_cast<const v4i*>(k0p + i * 64);
+          kb1[i] = *reinterpret_cast<const v4i*>(k1p + i * 64);
+        }
+        // two accumulators per M tile (even and odd K steps) keep the
+        // dependent MFMA chains short
+        v4f sacc[2][2];
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) o_acc[dt][ht] = v4f{0.f, 0.f, 0.f, 0.f};
-    l_run = 0.0f;
-    ovf = false;
-    {
-      // tiles 0 .. kRing - 2 before the loop; each tile's first barrier then
-      // frees the previous tile's slot for the next one
-      uint32_t r0[LPW], r1[LPW], r2[LPW];
-      fetch(0, r0);
-      fetch(1, r1);
-      fetch(2, r2);
-      if (ntiles > 0) launch(std::integral_constant<int, 0>{}, r0);
-      if (ntiles > 1) launch(std::integral_constant<int, 1>{}, r1);
-      if (ntiles > 2) launch(std::integral_constant<int, 2>{}, r2);
+        for (int i = 0; i < 2; ++i) sacc[i][0] = sacc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const v4i x0 = kb0[ks % PF], x1 = kb1[ks % PF];
+          if (ks + PF < KS) {
+            kb0[ks % PF] = *reinterpret_cast<const v4i*>(k0p + (ks + PF) * 64);
+            kb1[ks % PF] = *reinterpret_cast<const v4i*>(k1p + (ks + PF) * 64);
+          }
+          sacc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x0), qf[ks],
+                                                                    sacc[0][ks & 1], 0, 0, 0);
+          sacc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x1), qf[ks],
+                                                                    sacc[1][ks & 1], 0, 0, 0);
+        }
+        // keep the K reads PF steps ahead of their MFMAs (left alone, the
+        // scheduler moves each read next to its use)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF < KS ? PF : KS), 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        const v4f s0 = sacc[0][0] + sacc[0][1];
+        const v4f s1 = sacc[1][0] + sacc[1][1];
+        // lane (head col, group grp) holds keys grp + 4r (s0[r]) and
+        // 16 + grp + 4r (s1[r]) of the tile
+        float lg[8];
+        float tmax = neg_inf;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ja = k * kTile + grp + 4 * r, jb = ja + 16;
+          lg[r] = ja < n_valid ? s0[r] * a.scale_log2 : neg_inf;
+          lg[4 + r] = jb < n_valid ? s1[r] * a.scale_log2 : neg_inf;
+          tmax = fmaxf(tmax, fmaxf(lg[r], lg[4 + r]));
+        }
+        tmax = max_xor32(max_xor16(tmax));
+        m_seen = fmaxf(m_seen, tmax);
+        // the first tile always holds a valid key (valid entries are
+        // compacted to the front), so its max is finite
+        if (k == 0 && pass == 0) m_ref = tmax;
+        ovf = ovf || tmax > m_ref + kOvf;
+        // lg - m_ref <= kOvf on every tile that matters (a row where it is
+        // not runs again), so the bare exponential instruction suffices
+        float psum = 0.0f;
+        v4i pw;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(lg[j] - m_ref);
+          const float p1 = __builtin_amdgcn_exp2f(lg[j + 1] - m_ref);
+          psum += p0 + p1;
+          pw[j >> 1] = static_cast<int>(pack_bf16x2(p0, p1));
+        }
+        l_run += sum_xor32(sum_xor16(psum));
+        p_s[k & 1][wave][lane] = pw;
+      };
+      for (int k = 0; k <= ntiles; k += kRing) {
+        s_step(k, std::integral_constant<int, 0>{});
+        if (k + 1 <= ntiles) s_step(k + 1, std::integral_constant<int, 1>{});
+        if (k + 2 <= ntiles) s_step(k + 2, std::integral_constant<int, 2>{});
+        if (k + 3 <= ntiles) s_step(k + 3, std::integral_constant<int, 3>{});
+      }
+      // a second pass only when a logit outran the first tile's max (no load
+      // is in flight here: the last step waited for all of them)
+      if (lane == 0) ovf_s[wave] = (__ballot(ovf) != 0ull) ? 1 : 0;
+      __syncthreads();
+      const bool again = (ovf_s[0] | ovf_s[1] | ovf_s[2] | ovf_s[3]) != 0;
+      __syncthreads();
+      if (again) {
+        m_ref = m_seen;
+        continue;
+      }
+      // per-head normalisation, handed to the P*V waves
+      if (hv && grp == 0) {
+        const float M = fmaxf(m_ref, sink2);
+        const float corr = (m_ref == neg_inf) ? 0.0f : exp2f(m_ref - M);
+        const float Z = l_run * corr + exp2f(sink2 - M);
+        f_s[h] = corr / Z;
+        if (a.lse) a.lse[static_cast<long long>(t) * a.H + h] = (M + log2f(Z)) * kLn2;
+      }
+      __syncthreads();   // f_s is complete
+      break;
     }
-    for (int tt = 0; tt < ntiles; tt += kRing) {
-      tile_step(tt, pass, std::integral_constant<int, 0>{});
-      if (tt + 1 < ntiles) tile_step(tt + 1, pass, std::integral_constant<int, 1>{});
-      if (tt + 2 < ntiles) tile_step(tt + 2, pass, std::integral_constant<int, 2>{});
-      if (tt + 3 < ntiles) tile_step(tt + 3, pass, std::integral_constant<int, 3>{});
+  } else {
+    // O^T += V^T P^T for this wave's channels and all four head tiles: each
+    // transposed V fragment (in lane group g, source lane 4e + q points at 8
+    // bytes of key row g + 4e [then 16 + g + 4e], channels n0 + 4q .. +3;
+    // lane i of the group receives those rows' channel n0 + i -- the keys
+    // P^T holds in elements e and 4 + e) feeds four MFMAs
+    const int d0 = (wave - HT) * DW;
+    v4f o_acc[DTW][HT];
+    for (int pass = 0; pass < 2; ++pass) {
+      prime();
+#pragma unroll
+      for (int dt = 0; dt < DTW; ++dt)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) o_acc[dt][ht] = v4f{0.f, 0.f, 0.f, 0.f};
+      auto pv_step = [&](int k, auto sl) {
+        constexpr int S = decltype(sl)::value;
+        step_sync(k, sl);
+        if (k == 0) return;
+        const uint8_t* tile = slot_of(std::integral_constant<int, (S + kRing - 1) % kRing>{});
+        constexpr int VPF = DTW < 4 ? DTW : 4;
+        const int e_src = (lane & 15) >> 2, q_src = lane & 3;
+        const uint8_t* v0p = tile + row_off(grp + 4 * e_src) + q_src * 8 + d0 * 2;
+        const uint8_t* v1p = tile + row_off(16 + grp + 4 * e_src) + q_src * 8 + d0 * 2;
+        v4s vlo[VPF], vhi[VPF];
+#pragma unroll
+        for (int i = 0; i < VPF; ++i) {
+          vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(v0p + i * 32));
+          vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(v1p + i * 32));
+        }
+        v8bf pf[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) pf[ht] = as_v8bf(p_s[(k - 1) & 1][ht][lane]);
+#pragma unroll
+        for (int dt = 0; dt < DTW; ++dt) {
+          const v4s lo = vlo[dt % VPF], hi = vhi[dt % VPF];
+          if (dt + VPF < DTW) {
+            vlo[dt % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(v0p + (dt + VPF) * 32));
+            vhi[dt % VPF] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(v1p + (dt + VPF) * 32));
+          }
+          const v8bf va =
+              __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+            o_acc[dt][ht] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[ht], o_acc[dt][ht], 0, 0, 0);
+        }
+      };
+      for (int k = 0; k <= ntiles; k += kRing) {
+        pv_step(k, std::integral_constant<int, 0>{});
+        if (k + 1 <= ntiles) pv_step(k + 1, std::integral_constant<int, 1>{});
+        if (k + 2 <= ntiles) pv_step(k + 2, std::integral_constant<int, 2>{});
+        if (k + 3 <= ntiles) pv_step(k + 3, std::integral_constant<int, 3>{});
+      }
+      __syncthreads();   // the S waves' overflow vote
+      const bool again = (ovf_s[0] | ovf_s[1] | ovf_s[2] | ovf_s[3]) != 0;
+      __syncthreads();
+      if (again) continue;
+      __syncthreads();   // f_s is complete
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const int hh = ht * 16 + col;
+        if (hh >= a.H) continue;
+        const float f = f_s[hh];
+        uint16_t* orow = a.out + (static_cast<long long>(t) * a.H + hh) * D + d0;
+#pragma unroll
+        for (int dt = 0; dt < DTW; ++dt) {
+          // o_acc[dt][ht][r] is channel d0 + dt*16 + grp*4 + r of head hh
+          const int d = dt * 16 + grp * 4;
+          uint2 w;
+          w.x = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][0] * f)) |
+                (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][1] * f)) << 16);
+          w.y = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][2] * f)) |
+                (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][3] * f)) << 16);
+          *reinterpret_cast<uint2*>(orow + d) = w;
+        }
+      }
+      break;
     }
-    // a second pass only when a logit outran the first tile's max (no load
-    // is in flight here: the last tile waited for all of them)
-    if (lane == 0) ovf_s[wave] = (__ballot(ovf) != 0ull) ? 1 : 0;
-    __syncthreads();
-    const bool again = (ovf_s[0] | ovf_s[1] | ovf_s[2] | ovf_s[3]) != 0;
-    __syncthreads();
-    if (!again) break;
-    m_ref = m_seen;
   }
 
   if (tid == 0 && err_s) flag_error(a.err, err_s);
   if (b < 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
-
-  // per-head normalisation by the wave that owns the head's softmax
-  if (hv && grp == 0) {
-    const float sink2 = a.sink[h] * kLog2e;
-    const float M = fmaxf(m_ref, sink2);
-    const float corr = (m_ref == neg_inf) ? 0.0f : exp2f(m_ref - M);
-    const float Z = l_run * corr + exp2f(sink2 - M);
-    f_s[h] = corr / Z;
-    if (a.lse) a.lse[static_cast<long long>(t) * a.H + h] = (M + log2f(Z)) * kLn2;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int hh = ht * 16 + col;
-    if (hh >= a.H) continue;
-    const float f = f_s[hh];
-    uint16_t* orow = a.out + (static_cast<long long>(t) * a.H + hh) * D + d0;
-#pragma unroll
-    for (int dt = 0; dt < DTW; ++dt) {
-      // o_acc[dt][ht][r] is channel d0 + dt*16 + grp*4 + r of head hh
-      const int d = dt * 16 + grp * 4;
-      uint2 w;
-      w.x = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][0] * f)) |
-            (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][1] * f)) << 16);
-      w.y = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][2] * f)) |
-            (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][3] * f)) << 16);
-      *reinterpret_cast<uint2*>(orow + d) = w;
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -971,7 +1012,7 @@ int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
   const long long grid = static_cast<long long>(a.items_per_xcd) * 8;
   if (grid > 0x7fffffffll) return CSA_ERR_UNSUPPORTED;
   if (ring)
-    hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kAttnThreads), 0,
+    hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kRingThreads), 0,
                        st, a);
   else
     hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(static_cast<unsigned>(grid)),

@@ -30,6 +30,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats -> packed bf16 pair (lo in bits 0-15) with gfx950's conversion
+// instruction, round to nearest even.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{lo, hi}, v2bf_t));
+}
+
 // Compressed slots visible to a query at absolute position p: c < (p+1)/ratio.
 __device__ __forceinline__ int visible_count(int p, int ratio) {
   return p < 0 ? 0 : (p + 1) / ratio;
