@@ -125,7 +125,8 @@ int csa_materialize_rope_rows(const float* freqs_cos, const float* freqs_sin,
  * score_stride or past 128 * max_blocks -> CSA_EFLAG_POS_RANGE, n is cut;
  * a visible position on a page with an invalid block id ->
  * CSA_EFLAG_BLOCK_RANGE, that position scores -inf.
- * Supported: 1 <= Hi <= 64, Di in {32, 64, 96, 128}, ratio >= 1.
+ * Supported: 1 <= Hi <= 64, 16 <= Di <= 128 with Di a multiple of 16,
+ * ratio >= 1; q_idx and idx_kv 16-byte aligned (else CSA_ERR_UNSUPPORTED).
  */
 int csa_index_score(const int8_t* q_idx, const float* q_scale, const float* head_w,
                     const int8_t* idx_kv, const float* idx_scale, int32_t num_blocks,
@@ -223,10 +224,10 @@ int csa_sparse_attn_decode(const uint16_t* q, const float* rope_cos, const float
 /*
  * csa_sparse_attn_prefill -- the same operation and arguments as
  * csa_sparse_attn_decode, scheduled for many query rows (a prefill walk in
- * 128-token tiles, [MTP] "Deployment configuration"): one work-group per
- * query row, consecutive rows kept on one XCD so their shared window rows and
- * popular compressed rows stay in that XCD's L2. Needs no workspace
- * (csa_sparse_attn_workspace_bytes is still accepted).
+ * 128-token tiles, [MTP] "Deployment configuration"): one 512-thread
+ * work-group per query row, consecutive rows kept on one XCD so their shared
+ * window rows and popular compressed rows stay in that XCD's L2. Needs no
+ * workspace (csa_sparse_attn_workspace_bytes is still accepted).
  */
 int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const float* rope_sin,
                             int32_t rope_dim, int32_t rope_offset, const uint16_t* cmp_kv,

@@ -249,3 +249,24 @@ def test_attention_shapes(H_, D, R, off):
                 dev(x["positions"]), cfg.T, out, lse=lse, workspace=ws, err=err)
             torch.cuda.synchronize()
             assert torch.equal(first, out), "second call on the same workspace differs"
+
+
+@pytest.mark.parametrize("Hi,Di", [(1, 16), (5, 48), (37, 80), (64, 96), (17, 112), (64, 128)])
+def test_index_shapes(Hi, Di):
+    """Indexer widths that leave partial 32-channel MFMA steps and partial
+    32-head tiles, against the oracle's scores."""
+    print(f"[edges] index Hi={Hi} Di={Di}", flush=True)
+    cfg = CsaConfig(name="ishape", description="indexer shape sweep",
+                    rows_per_request=(3, 2), positions=((1000, 1001, 1002), (300, 301)),
+                    H=8, D=64, R=16, Hi=Hi, Di=Di, W=16, ratio=1, k=64, context=1100,
+                    rope_capacity=2048)
+    x = synthetic.make_inputs(cfg, seed=5).t
+    csa = _csa()
+    step = csa.step_for_config(cfg, x)
+    step.index()
+    torch.cuda.synchronize()
+    o, oe = oracle.index_scores(x["q_idx"], x["q_scale"], x["head_w"], x["idx_kv"], x["idx_scale"],
+                                x["cmp_block_table"], x["query_start_loc"], x["positions"],
+                                cfg.T, cfg.ratio, step.score_stride)
+    assert int(step.err.item()) == oe == 0
+    H.check_scores(step.scores.cpu().numpy().astype(np.float64), o, f"index Hi{Hi} Di{Di}")
