@@ -152,7 +152,7 @@ __device__ int block_excl_scan_lds(int v, int* wsum, int* total) {
     const int y = __shfl_up(incl, off, 64);
     if (lane >= off) incl += y;
   }
-  lds_barrier();   // wsum of the previous scan has been read
+  lds_barrier();   // wsum of an earlier scan has been read
   if (lane == 63) wsum[wave] = incl;
   lds_barrier();
   int before = 0, tot = 0;
@@ -644,9 +644,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   const bool hv = h < a.H;
   if (tid == 0) err_s = 0;
   // metadata loads first, then the query and rope loads, then the first use
-  // of the metadata (vector memory returns in order)
+  // of the metadata (vector memory returns in order).  The selected index of
+  // this thread's entry is fetched with them on the guess that the row's
+  // window is full (position >= window - 1, every row but a request's first
+  // few tokens), which takes a dependent round trip off the resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
+  const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
+  const int i_spec = split * kSpan + tid - a.window;
+  const int c_spec = (i_spec >= 0 && i_spec < a.k) ? topk_row[i_spec] : -1;
   // the query and the rope row: in flight during the row resolution, and
   // complete before the gather is issued (a load issued after the gather
   // would wait for it)
@@ -673,12 +679,13 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   const int list_len = (b >= 0) ? (w_len + a.k) : 0;
   const int i_begin = split * kSpan;
   const int n_my = max(0, min(list_len, i_begin + kSpan) - i_begin);
-  __syncthreads();
+  // LDS-only barriers in the prologue: a __syncthreads() would also wait for
+  // the query loads still streaming in from HBM
+  lds_barrier();   // err_s is cleared
 
   // ---- resolve this span through the block tables; compact valid rows
   int n_valid = 0;
   {
-    const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
     int ebits = 0;
     uint32_t rr = kNoRow;
     const int j = tid;
@@ -689,7 +696,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
                                      a.max_win_blocks, a.num_win_blocks, w_lo + i);
         if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
       } else {
-        const int c = topk_row[i - w_len];
+        const int c = (w_len == a.window) ? c_spec : topk_row[i - w_len];
         if (c >= 0) {
           if (c >= nv) {
             ebits |= CSA_EFLAG_TOPK_RANGE;
@@ -703,7 +710,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
     }
     if (ebits && hg == 0) atomicOr(&err_s, ebits);
     int total = 0;
-    const int slot = block_excl_scan(rr != kNoRow ? 1 : 0, scan_s, &total);
+    const int slot = block_excl_scan_lds<kAttnWaves>(rr != kNoRow ? 1 : 0, scan_s, &total);
     if (rr != kNoRow) row_s[slot] = rr;
     n_valid = total;
   }

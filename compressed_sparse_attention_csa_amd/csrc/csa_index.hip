@@ -189,10 +189,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     return;
   }
 
+  // the positions of the group's rows and the block ids of the run's pages
+  // are fetched together (a block id is used only if its page turns out to
+  // be visible to some row)
+  int pos_v = 0, blk_v = -1;
+  if (tid < nrows) pos_v = positions[row0 + tid];
+  if (tid < npages) {
+    const int page = page0 + tid;
+    blk_v = (page < max_blocks) ? bt[static_cast<long long>(b) * max_blocks + page] : -1;
+  }
   if (tid < kRowsPerWG) {
     int n = 0;
     if (tid < nrows) {
-      n = visible_count(positions[row0 + tid], ratio);
+      n = visible_count(pos_v, ratio);
       const long long cap = static_cast<long long>(max_blocks) * kPage;
       if (static_cast<long long>(n) > stride || static_cast<long long>(n) > cap) {
         if (blockIdx.x == 0) flag_error(err, CSA_EFLAG_POS_RANGE);
@@ -210,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const int page = page0 + tid;
     int blk = -1;
     if (page * kPage < nmax) {
-      blk = (page < max_blocks) ? bt[static_cast<long long>(b) * max_blocks + page] : -1;
+      blk = blk_v;
       if (blk < 0 || blk >= num_blocks) {
         flag_error(err, CSA_EFLAG_BLOCK_RANGE);
         blk = -1;
@@ -228,12 +237,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   // A operand (this wave's query row: 32-head tiles x 32-dim k-steps, lane
   // (col, half) holding head mt*32 + col, dims ks*32 + half*16 .. +15) and
   // the folded head weights w*qs in the MFMA result order (result j of lane
-  // (col, half) is head mt*32 + 8*(j/4) + 4*half + j%4), loaded once
+  // (col, half) is head mt*32 + 8*(j/4) + 4*half + j%4), loaded once, after
+  // the first pages' loads are issued
   constexpr int MT = 2;
   constexpr int KS = 2 * KK;
   v4i qa[MT][KS];
   float ww[MT][16];
-  if (active) {
+  auto load_query = [&]() {
+    if (!active) return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int h = mt * 32 + col;
@@ -253,7 +264,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
                               : 0.0f;
       }
     }
-  }
+  };
   __syncthreads();  // blk_s ready (no direct-to-LDS load is in flight yet)
 
   // ---- page pi -> LDS stage pi % kStages with direct-to-LDS loads.  LDS
@@ -397,6 +408,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   static_assert(kStages == 3, "the page loop is unrolled over three stages");
   if (npages > 0) issue(0, std::integral_constant<int, 0>{});
   if (npages > 1) issue(1, std::integral_constant<int, 1>{});
+  // the query loads go after the first pages' loads, so their latencies
+  // overlap (the first page's wait then also covers them: vector memory
+  // completes in issue order)
+  load_query();
   for (int pi = 0; pi < npages; pi += kStages) {
     step(pi, std::integral_constant<int, 0>{});
     if (pi + 1 < npages) step(pi + 1, std::integral_constant<int, 1>{});
