@@ -162,8 +162,53 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   if (npages <= 0) return;
   const float neg_inf = -__builtin_huge_valf();
 
-  int row0 = 0, nrows = 0;
-  const int b = locate_group(qsl, B, num_tokens, blockIdx.y, &row0, &nrows, scratch);
+  // The request and rows of work-group y, with the positions of those rows and
+  // the block ids of this run's pages.  First guess that the B requests own
+  // equal runs of rows from row 0 (qsl[b] = b * num_tokens / B, the usual
+  // decode batch): the guessed rows' positions and block ids are then fetched
+  // in the same round trip as query_start_loc, and the guess is checked
+  // against every entry of it.  Otherwise the groups are located by a scan
+  // over query_start_loc and the rows' metadata fetched after it.
+  int row0 = 0, nrows = 0, b = -1;
+  int pos_v = 0, blk_v = -1;
+  bool located = false;
+  if (B > 0 && B < kThreads && num_tokens % B == 0) {
+    const int R = num_tokens / B;
+    const int gpr = (R + kRowsPerWG - 1) / kRowsPerWG;   // groups per request
+    const int bg = static_cast<int>(blockIdx.y) / gpr;
+    const int r0 = bg * R + (static_cast<int>(blockIdx.y) % gpr) * kRowsPerWG;
+    const int nr = bg < B ? min(kRowsPerWG, (bg + 1) * R - r0) : 0;
+    const int qv = tid <= B ? min(max(qsl[tid], 0), num_tokens) : 0;
+    if (tid < nr) pos_v = positions[r0 + tid];
+    if (bg < B && tid < npages) {
+      const int page = page0 + tid;
+      blk_v = (page < max_blocks) ? bt[static_cast<long long>(bg) * max_blocks + page] : -1;
+    }
+    const bool ok = __all(tid > B || qv == tid * R);
+    if (lane == 0) scratch[wave] = ok ? 1 : 0;
+    lds_barrier();
+    bool all_ok = true;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) all_ok = all_ok && scratch[w] != 0;
+    if (all_ok) {
+      if (bg >= B) return;   // every row is owned, and these groups are past them
+      located = true;
+      b = bg;
+      row0 = r0;
+      nrows = nr;
+    }
+  }
+  if (!located) {
+    b = locate_group(qsl, B, num_tokens, blockIdx.y, &row0, &nrows, scratch);
+    if (b >= 0) {
+      pos_v = tid < nrows ? positions[row0 + tid] : 0;
+      blk_v = -1;
+      if (tid < npages) {
+        const int page = page0 + tid;
+        blk_v = (page < max_blocks) ? bt[static_cast<long long>(b) * max_blocks + page] : -1;
+      }
+    }
+  }
   if (b < 0) {
     // rows that no request owns: the first groups past the owned ones cover them
     const int owned_end = (B > 0) ? min(max(qsl[B], 0), num_tokens) : 0;
@@ -189,15 +234,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     return;
   }
 
-  // the positions of the group's rows and the block ids of the run's pages
-  // are fetched together (a block id is used only if its page turns out to
-  // be visible to some row)
-  int pos_v = 0, blk_v = -1;
-  if (tid < nrows) pos_v = positions[row0 + tid];
-  if (tid < npages) {
-    const int page = page0 + tid;
-    blk_v = (page < max_blocks) ? bt[static_cast<long long>(b) * max_blocks + page] : -1;
-  }
+  // (a block id is used only if its page turns out to be visible to some row)
   if (tid < kRowsPerWG) {
     int n = 0;
     if (tid < nrows) {
