@@ -127,19 +127,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
   return block_excl_scan_n<kAttnWaves>(v, wsum, total);
 }
 
-// Work-group barrier for LDS ordering only.  __syncthreads() is a
-// work-group release/acquire: with direct-to-LDS loads in flight it waits for
-// ALL of them (vmcnt(0)), which would drain the tile ring at every barrier.
-// Here each wave first waits for its own LDS operations (lgkmcnt(0)); the
-// caller waits explicitly (vmcnt) for exactly the tiles the next phase reads.
-// The signal fences keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // block_excl_scan_n with LDS-only barriers (vector loads in flight are not
 // waited for).
 template <int NW>

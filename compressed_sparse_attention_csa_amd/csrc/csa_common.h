@@ -122,4 +122,17 @@ __device__ __forceinline__ float sum_xor32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Work-group barrier that orders LDS only.  A __syncthreads() is a
+// work-group release/acquire and waits for every vector-memory operation in
+// flight (vmcnt(0)), direct-to-LDS loads and prefetches included; here each
+// wave waits for its own LDS operations only (lgkmcnt(0)), and the caller
+// waits explicitly (vmcnt) for exactly the loads the next phase reads.  The
+// signal fences keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 }  // namespace csa

@@ -116,15 +116,6 @@ __device__ __forceinline__ void wait_vm_rt(int n) {
   }
 }
 
-// Work-group barrier that orders LDS only (see the attention kernels: a
-// __syncthreads() would wait for every direct-to-LDS load in flight).
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt((63 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 __device__ __forceinline__ float lane_add_swap32(float x, float y) {
   // lanes 0-31: x[l] + x[l+32]; lanes 32-63: y[l-32] + y[l]
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
