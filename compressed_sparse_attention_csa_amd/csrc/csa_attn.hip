@@ -214,9 +214,17 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   if (tid == 0) err_s = 0;
 
   // metadata loads first, then the query, the rope row and the sink (vector
-  // memory returns in order: these complete during the row resolution)
+  // memory returns in order: these complete during the row resolution).  The
+  // selected indices of this thread's first two list entries are fetched
+  // with them on the guess that the row's window is full (every row but a
+  // request's first window - 1 tokens), which takes a dependent round trip
+  // off the resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
+  const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
+  const int i_spec0 = tid - a.window, i_spec1 = kRingThreads + tid - a.window;
+  const int c_spec0 = (i_spec0 >= 0 && i_spec0 < a.k) ? topk_row[i_spec0] : -1;
+  const int c_spec1 = (i_spec1 >= 0 && i_spec1 < a.k) ? topk_row[i_spec1] : -1;
   v4i qraw[KS];
   {
     const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
@@ -245,11 +253,11 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   // ---- resolve every entry of the key list through the block tables at once;
   //      valid rows are compacted to the front (softmax does not depend on
   //      their order), so a tile's mask is just j < n_valid
-  const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
   int n_valid = 0;
   {
     int ebits = 0;
-    for (int j0 = 0; j0 < n_my; j0 += kRingThreads) {
+    const bool spec_ok = w_len == a.window;
+    for (int j0 = 0, r = 0; j0 < n_my; j0 += kRingThreads, ++r) {
       const int i = j0 + tid;
       uint32_t rr = kNoRow;
       if (i >= n_my) {
@@ -259,7 +267,7 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
                                      a.max_win_blocks, a.num_win_blocks, w_lo + i);
         if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
       } else {
-        const int c = topk_row[i - w_len];
+        const int c = (spec_ok && r < 2) ? (r == 0 ? c_spec0 : c_spec1) : topk_row[i - w_len];
         if (c >= 0) {
           if (c >= nv) {
             ebits |= CSA_EFLAG_TOPK_RANGE;
