@@ -7,18 +7,20 @@
 // scale.  Score = sum_h w[t,h] * relu(qs[t,h] * ks[c] * <q8[t,h], k8[c]>).
 //
 // Mapping.  Work-groups are (request, up to 4 of its rows) x (a run of
-// 128-key pages); wave w owns one query row and computes its heads as 16-row
-// MFMA tiles (M = heads, N = keys, K = Di), so a key page staged once in LDS
-// feeds every row of the group.  Pages stream through a 3-stage LDS ring
-// filled by direct-to-LDS loads (two pages in flight behind the one being
-// scored, three work-groups per CU); the barriers between pages order LDS only, so the loads stay in
-// flight across them.  LDS rows are 128 bytes with XOR-swizzled 16-byte
-// chunks (conflict-free operand reads), the swizzle applied by choosing each
-// lane's source chunk.  INT32 accumulators stay in registers: the epilogue
-// applies ReLU and the folded weight w*qs per head, the head sums of eight
-// 16-key subtiles are finished together with two rounds of cross-lane swaps
-// (gfx950 permlane32/permlane16), and each lane scales its two keys by ks and
-// stores them.  Pages past every row's visible span only receive -inf.
+// 128-key pages); wave w owns one query row and computes its 64 heads as
+// 32x32x32 INT8 MFMA tiles (M = 32 heads, N = 32 keys, K = Di in 32-byte
+// steps), so a key page staged once in LDS feeds every row of the group.
+// Pages stream through a 3-stage LDS ring filled by direct-to-LDS loads (two
+// pages in flight behind the one being scored, three work-groups per CU);
+// the barriers between pages order LDS only, so the loads stay in flight
+// across them.  LDS rows are 128 bytes with XOR-swizzled 16-byte chunks
+// (conflict-free operand reads), the swizzle applied by choosing each lane's
+// source chunk.  INT32 accumulators stay in registers and start from a bias
+// that makes ReLU one clamped float add (see the page loop); the folded
+// weight w*qs of each head follows in one FMA, a cross-lane swap (gfx950
+// permlane32) finishes the head sum of each key, and each lane scales its
+// two keys by ks and stores them.  Pages past every row's visible span only
+// receive -inf.
 #include <type_traits>
 
 #include "csa_common.h"
@@ -287,8 +289,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        // times 2^21: the epilogue's ReLU leaves dot * 2^-21 (see mfma_tile)
         ww[mt][j] = (hh < Hi) ? head_w[static_cast<long long>(my_t) * Hi + hh] *
-                                    q_scale[static_cast<long long>(my_t) * Hi + hh]
+                                    q_scale[static_cast<long long>(my_t) * Hi + hh] * 2097152.0f
                               : 0.0f;
       }
     }
@@ -360,13 +363,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     float* out_row = scores + static_cast<long long>(my_t) * stride + c0;
     float w0 = neg_inf, w1 = neg_inf;
     if (blk_s[pi] >= 0 && c0 < my_n) {
-      // eight (32-head, 32-key) tiles p = 2*nt + mt, software-pipelined: the
-      // MFMAs of tile p + 1 are interleaved with the epilogue of tile p.  One
-      // set of B registers: key tile nt + 1 is read from LDS as soon as the
-      // MFMAs of tile 2*nt + 1 (the last to use key tile nt) are issued.
+      // eight (32-head, 32-key) tiles p = 2*nt + mt, each scored as soon as
+      // its MFMAs are issued: the epilogue waits for them, and the SIMD's
+      // other waves fill that wait.  One set of B registers per key tile.
       float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       v4i bk[KS];
-      v16i acc[2];
+      v16i acc;
       auto load_b = [&](int nt) {
         const int kj = nt * 32 + col;
 #pragma unroll
@@ -374,50 +376,30 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
           bk[ks] = *reinterpret_cast<const v4i*>(
               keys + kj * kRowBytes + swz_chunk(kj, ks * 2 + half) * 16);
       };
-      auto mfma_tile = [&](int p, v16i& a) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          a = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[p & 1][ks], bk[ks],
-                                                    ks == 0 ? v16i{} : a, 0, 0, 0);
-      };
-      load_b(0);
-      mfma_tile(0, acc[0]);
-      __builtin_amdgcn_sched_barrier(0);
+      // The accumulators start at 0x40800000, the bits of 4.0f.  A dot
+      // product of Di <= 128 INT8 pairs lies in [-2^21, 2^21], so the INT32
+      // result read as a float is 4 + dot * 2^-21 when dot >= 0 (the
+      // mantissa step of [4, 8) is 2^-21) and below 4 otherwise.  One
+      // clamped add of -4 (v_add_f32 ... clamp) then gives relu(dot) * 2^-21
+      // exactly, in [0, 1], and the weight, pre-scaled by 2^21, multiplies it
+      // back: the same product as w * relu(dot), with no separate max and
+      // int-to-float conversion (two VALU ops per head and key, not three).
+      constexpr int kBias = 0x40800000;
+      constexpr v16i kBiasV = {kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
+                               kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias};
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        // region p: MFMAs of tile p + 1, epilogue of tile p
-        const bool new_key_tile = ((p + 1) & 1) == 0;   // tile p + 1 needs fresh B registers
-        if (p + 1 < 8) {
-          if (new_key_tile) load_b((p + 1) >> 1);
-          mfma_tile(p + 1, acc[(p + 1) & 1]);
-        }
+        if ((p & 1) == 0) load_b(p >> 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[p & 1][ks], bk[ks],
+                                                      ks == 0 ? kBiasV : acc, 0, 0, 0);
         float xs = x[p >> 1];
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          xs = fmaf(ww[p & 1][j], static_cast<float>(max(acc[p & 1][j], 0)), xs);
+          xs = fmaf(ww[p & 1][j],
+                    __builtin_amdgcn_fmed3f(__int_as_float(acc[j]) - 4.0f, 0.0f, 1.0f), xs);
         x[p >> 1] = xs;
-        if (p + 1 < 8) {
-          // each MFMA is followed by a share of the epilogue, so the last
-          // one is done before the next region reads its results; a new key
-          // tile puts its LDS reads and a few epilogue ops first
-          constexpr int kLead = 8;
-          if (new_key_tile) {
-            __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, kLead, 0);
-#pragma unroll
-            for (int i = 0; i < KS; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, (48 - kLead) / KS, 0);
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < KS; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, 48 / KS, 0);
-            }
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);   // one scheduling region per tile
       }
       // head sums: lanes l and l + 32 hold the two 32-head halves of the
       // same key, so one swap per key pair finishes them; lane l of w0 ends
