@@ -21,6 +21,7 @@
 // permlane32) finishes the head sum of each key, and each lane scales its
 // two keys by ks and stores them.  Pages past every row's visible span only
 // receive -inf.
+#include <algorithm>
 #include <type_traits>
 
 #include "csa_common.h"
@@ -459,8 +460,12 @@ extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const 
   // put every page in flight at once, long rows stream through each
   // work-group's page ring; a grid just past one round would leave a
   // straggler round, so pages per work-group round up
+  // (the group count is estimated from below: every request owns at least
+  // one group, and four rows fill one; decode batches of 2-row requests
+  // have B groups, not num_tokens / 4)
   constexpr long long kSlots = 3 * 256;
-  long long ppw = (pages * ((num_tokens + 3) / 4) + kSlots - 1) / kSlots;
+  const long long groups_est = std::max<long long>((num_tokens + 3) / 4, std::min(B, num_tokens));
+  long long ppw = (pages * groups_est + kSlots - 1) / kSlots;
   if (ppw < 1) ppw = 1;
   if (ppw > csa::kMaxPPW) ppw = csa::kMaxPPW;
   const long long gx = (pages + ppw - 1) / ppw;
