@@ -10,22 +10,19 @@
 //
 // Two schedules share the same tile code.
 //
-// Ring kernel (prefill, large decode batches): a work-group (8 waves) owns
-// one query row and walks its whole key list; four softmax waves own 16
-// heads each, four P*V waves a quarter of the channels each.
+// Ring kernel (prefill, large decode batches): a work-group (4 waves) owns
+// one query row and walks its whole key list; wave w owns heads 16w..16w+15.
 // The key list is virtual -- entry i < W_len is window position w_lo + i,
 // later entries are topk_idx[t][i - W_len] -- and the work-group resolves it
 // through the block tables in one parallel pass into LDS, compacting the
 // valid rows to the front.  Rows then stream into a four-tile LDS ring (32
 // rows per tile) with gfx950's direct global->LDS loads -- one wave-wide
 // 16-byte-per-lane load moves a whole 1 KiB row, no registers involved --
-// keeping two tiles in flight while the softmax waves work on one tile and
-// the P*V waves on the one before it.
+// keeping three tiles in flight behind the one being multiplied.
 //
 // Decode kernel (small batches): a work-group owns one (row, 16-head group,
-// span of 64 or 128 entries); each wave gathers and multiplies its own 32-row
-// tile, so a span costs one memory latency and every key byte is read from
-// LDS once.
+// 128-entry span); each wave gathers and multiplies its own 32-row tile, so a
+// span costs one memory latency and every key byte is read from LDS once.
 // Partials of the spans are merged with the sink by a third kernel.
 //
 // Tile code.  Rows sit at a 16-byte-padded stride so the K operand reads
@@ -44,6 +41,8 @@ namespace csa {
 namespace {
 
 constexpr int kTile = 32;       // key rows per LDS tile
+constexpr int kAttnWaves = 4;   // 16 heads per wave
+constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kRingWaves = 8;   // ring kernel: 4 softmax waves + 4 P*V waves
 constexpr int kRingThreads = 64 * kRingWaves;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -123,6 +122,9 @@ __device__ int block_excl_scan_n(int v, int* wsum, int* total) {
   }
   *total = tot;
   return before + incl - v;
+}
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
+  return block_excl_scan_n<kAttnWaves>(v, wsum, total);
 }
 
 // block_excl_scan_n with LDS-only barriers (vector loads in flight are not
@@ -591,24 +593,18 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode schedule: a work-group owns one (row, 16-head group, span of the key
-// list).  Each of its NW waves gathers its own 32 rows into a private
+// Decode schedule: a work-group owns one (row, 16-head group, 128-entry span of
+// the key list).  Each of its four waves gathers its own 32 rows into a private
 // LDS slot with direct-to-LDS loads -- all at once, so a work-group pays one
 // memory latency -- and runs one 32-key tile (S^T, softmax, P*V) for the
 // group's 16 heads; no key byte is read from LDS by more than one wave.  The
-// per-wave softmax states are then combined in LDS.  With one span the
+// four per-wave softmax states are then combined in LDS.  With one span the
 // work-group writes the output rows directly; with several it writes an FP32
 // partial (16 heads x D, relative to its own max) for the merge kernel.
-// NW waves per work-group (2 or 4): a span is NW 32-row tiles.  The schedule
-// takes four waves when a launch of them already fills the CUs, and two
-// otherwise (twice the work-groups, each with half the gather).
-constexpr int kDecodeCUs = 256;   // MI355X compute units: one decode work-group each
+constexpr int kSpan = kAttnWaves * kTile;   // list entries per decode work-group
 
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, 1) attn_decode_kernel(AttnArgs a) {
-  constexpr int kAttnWaves = NW;
-  constexpr int kAttnThreads = 64 * NW;
-  constexpr int kSpan = NW * kTile;   // list entries per work-group
+template <int D>
+__global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   constexpr int RB = 2 * D;
@@ -621,7 +617,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t slot_s[kAttnWaves * SS];
   __shared__ uint32_t row_s[kSpan];
   __shared__ float ml_s[kAttnWaves][2][16];
-  __shared__ float rope_s[2 * 256];   // rope row of t: cos, then sin
+  __shared__ float rope_s[2 * kAttnThreads];   // rope row of t: cos, then sin
   __shared__ int scan_s[kAttnWaves];
   __shared__ int err_s;
 
@@ -662,13 +658,10 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_decode_kernel(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks)
       qraw[ks] = hv ? *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8) : v4i{0, 0, 0, 0};
   }
-  constexpr int RPT = (256 + kAttnThreads - 1) / kAttnThreads;   // rope entries per thread
-  float rcv[RPT], rsv[RPT];
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int i = u * kAttnThreads + tid;
-    rcv[u] = i < a.half_rope ? a.rope_cos[static_cast<long long>(t) * a.half_rope + i] : 0.0f;
-    rsv[u] = i < a.half_rope ? a.rope_sin[static_cast<long long>(t) * a.half_rope + i] : 0.0f;
+  float rcv = 0.0f, rsv = 0.0f;
+  if (tid < a.half_rope) {
+    rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + tid];
+    rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + tid];
   }
 
   const int b = owner_from_lanes(qsl_v, a.qsl, a.B, t);
@@ -716,13 +709,9 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_decode_kernel(AttnArgs a) {
     if (rr != kNoRow) row_s[slot] = rr;
     n_valid = total;
   }
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int i = u * kAttnThreads + tid;
-    if (i < a.half_rope) {
-      rope_s[i] = rcv[u];
-      rope_s[256 + i] = rsv[u];
-    }
+  if (tid < a.half_rope) {
+    rope_s[tid] = rcv;
+    rope_s[kAttnThreads + tid] = rsv;
   }
   __syncthreads();
 
@@ -768,7 +757,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_decode_kernel(AttnArgs a) {
       for (int pr = 0; pr < 4; ++pr) {
         const int rr = r0 + 2 * pr;
         if (rr >= 0 && rr < 2 * a.half_rope) {
-          const float c = rope_s[rr >> 1], sn = rope_s[256 + (rr >> 1)];
+          const float c = rope_s[rr >> 1], sn = rope_s[kAttnThreads + (rr >> 1)];
           const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
           e[2 * pr] = f32_to_bf16(x * c - y * sn);
           e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
@@ -854,7 +843,7 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_decode_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // ---- combine the waves: each parks (m, l, O) in LDS (its own slot)
+  // ---- combine the four waves: each parks (m, l, O) in LDS (its own slot)
   {
     float* ow = reinterpret_cast<float*>(myslot);
 #pragma unroll
@@ -871,59 +860,51 @@ __global__ void __launch_bounds__(64 * NW, 1) attn_decode_kernel(AttnArgs a) {
   {
     // thread (head hh, lane c4) combines channels c4*4 + 64m: consecutive
     // lanes touch consecutive 16-byte LDS words and output bytes
+    const int hh = tid >> 4;
     const int c4 = (tid & 15) * 4;
-    // one head per 16 threads; with two waves each thread takes two heads
-    // (a run-time loop: unrolled, the two copies schedule worse)
-    auto combine_head = [&](int hh) {
-      const int head = hg * 16 + hh;
-      if (head < a.H) {
-        float mw[kAttnWaves], e[kAttnWaves];
-        float M = neg_inf;
-  #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
-          mw[w] = ml_s[w][0][hh];
-          M = fmaxf(M, mw[w]);
-        }
-        float Lsum = 0.0f;
-  #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
-          e[w] = (mw[w] == neg_inf) ? 0.0f : exp2f(mw[w] - M);
-          Lsum += ml_s[w][1][hh] * e[w];
-        }
-        float scale = 1.0f;
+    const int head = hg * 16 + hh;
+    if (head < a.H) {
+      float mw[kAttnWaves], e[kAttnWaves];
+      float M = neg_inf;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        mw[w] = ml_s[w][0][hh];
+        M = fmaxf(M, mw[w]);
+      }
+      float Lsum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        e[w] = (mw[w] == neg_inf) ? 0.0f : exp2f(mw[w] - M);
+        Lsum += ml_s[w][1][hh] * e[w];
+      }
+      float scale = 1.0f;
+      if (a.splits == 1) {
+        const float sink2 = a.sink[head] * kLog2e;
+        const float Mt = fmaxf(M, sink2);
+        const float corr = (M == neg_inf) ? 0.0f : exp2f(M - Mt);
+        const float Z = Lsum * corr + exp2f(sink2 - Mt);
+        scale = corr / Z;
+        if (a.lse && c4 == 0) a.lse[static_cast<long long>(t) * a.H + head] = (Mt + log2f(Z)) * kLn2;
+      } else if (c4 == 0) {
+        a.part_ml[static_cast<long long>(ts) * a.H + head] = make_float2(M, Lsum);
+      }
+#pragma unroll
+      for (int c = c4; c < D; c += 64) {
+        v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w)
+          acc += *reinterpret_cast<const v4f*>(
+                     reinterpret_cast<const float*>(slot_s + w * SS) + hh * OSTR + c) * e[w];
         if (a.splits == 1) {
-          const float sink2 = a.sink[head] * kLog2e;
-          const float Mt = fmaxf(M, sink2);
-          const float corr = (M == neg_inf) ? 0.0f : exp2f(M - Mt);
-          const float Z = Lsum * corr + exp2f(sink2 - Mt);
-          scale = corr / Z;
-          if (a.lse && c4 == 0) a.lse[static_cast<long long>(t) * a.H + head] = (Mt + log2f(Z)) * kLn2;
-        } else if (c4 == 0) {
-          a.part_ml[static_cast<long long>(ts) * a.H + head] = make_float2(M, Lsum);
-        }
-  #pragma unroll
-        for (int c = c4; c < D; c += 64) {
-          v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int w = 0; w < kAttnWaves; ++w)
-            acc += *reinterpret_cast<const v4f*>(
-                       reinterpret_cast<const float*>(slot_s + w * SS) + hh * OSTR + c) * e[w];
-          if (a.splits == 1) {
-            acc *= scale;
-            uint2 pk;
-            pk.x = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-            pk.y = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-            *reinterpret_cast<uint2*>(a.out + (static_cast<long long>(t) * a.H + head) * D + c) = pk;
-          } else {
-            *reinterpret_cast<v4f*>(a.part_o + (static_cast<long long>(ts) * a.H + head) * D + c) = acc;
-          }
+          acc *= scale;
+          uint2 pk;
+          pk.x = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+          pk.y = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+          *reinterpret_cast<uint2*>(a.out + (static_cast<long long>(t) * a.H + head) * D + c) = pk;
+        } else {
+          *reinterpret_cast<v4f*>(a.part_o + (static_cast<long long>(ts) * a.H + head) * D + c) = acc;
         }
       }
-    };
-    if constexpr (kAttnThreads / 16 >= 16) {
-      combine_head(tid >> 4);
-    } else {
-      for (int hh = tid >> 4; hh < 16; hh += kAttnThreads / 16) combine_head(hh);
     }
   }
 }
@@ -1005,22 +986,17 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
 
 // Schedule shared by the launcher and the workspace helper.  Prefill and
 // large decode batches walk each row's whole key list in one work-group (the
-// ring kernel, no partials); small decode batches split the list into spans
-// of NW * 32 entries per 16-head group (the decode kernel) and merge: four
-// waves per span when that many work-groups already fill the CUs, else two.
+// ring kernel, no partials); small decode batches split the list into
+// kSpan-entry spans per 16-head group (the decode kernel) and merge.
 struct SplitPlan {
   bool ring;
   int splits;
-  int waves;
 };
 
-SplitPlan plan_splits(int T, int H, int k, int window, bool prefill) {
+SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   const int lmax = max(1, window + k);
-  if (prefill || T >= 256) return SplitPlan{true, 1, 0};
-  const long long hg = (H + 15) / 16;
-  const int s4 = (lmax + 4 * kTile - 1) / (4 * kTile);
-  if (static_cast<long long>(T) * s4 * hg > kDecodeCUs) return SplitPlan{false, s4, 4};
-  return SplitPlan{false, (lmax + 2 * kTile - 1) / (2 * kTile), 2};
+  if (prefill || T >= 256) return SplitPlan{true, 1};
+  return SplitPlan{false, (lmax + kSpan - 1) / kSpan};
 }
 
 // Decode workspace: the FP32 partials [T][splits][H][D] and their (max, sum)
@@ -1030,7 +1006,7 @@ inline size_t attn_ws_bytes(int T, int splits, int H, int D) {
 }
 
 template <int D>
-int launch_attn(const AttnArgs& in, bool ring, int waves, hipStream_t st) {
+int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
   AttnArgs a = in;
   const long long items = static_cast<long long>(a.num_tokens) * a.splits *
                           (ring ? 1 : (a.H + 15) / 16);
@@ -1040,12 +1016,9 @@ int launch_attn(const AttnArgs& in, bool ring, int waves, hipStream_t st) {
   if (ring)
     hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kRingThreads), 0,
                        st, a);
-  else if (waves == 4)
-    hipLaunchKernelGGL((attn_decode_kernel<D, 4>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, st, a);
   else
-    hipLaunchKernelGGL((attn_decode_kernel<D, 2>), dim3(static_cast<unsigned>(grid)), dim3(128),
-                       0, st, a);
+    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(static_cast<unsigned>(grid)),
+                       dim3(kAttnThreads), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   if (a.splits > 1) {
     const long long mgrid = static_cast<long long>(a.num_tokens) * a.H;
@@ -1086,7 +1059,7 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   if (static_cast<long long>(num_cmp_blocks) * kPage >= (1ll << 31) ||
       static_cast<long long>(num_win_blocks) * kPage >= (1ll << 31))
     return CSA_ERR_UNSUPPORTED;
-  const SplitPlan plan = plan_splits(num_tokens, H, k, window, prefill);
+  const SplitPlan plan = plan_splits(num_tokens, k, window, prefill);
   AttnArgs a{};
   a.q = q;
   a.rope_cos = rope_cos;
@@ -1127,10 +1100,10 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (D) {
-    case 64: return launch_attn<64>(a, plan.ring, plan.waves, st);
-    case 128: return launch_attn<128>(a, plan.ring, plan.waves, st);
-    case 256: return launch_attn<256>(a, plan.ring, plan.waves, st);
-    default: return launch_attn<512>(a, plan.ring, plan.waves, st);
+    case 64: return launch_attn<64>(a, plan.ring, st);
+    case 128: return launch_attn<128>(a, plan.ring, st);
+    case 256: return launch_attn<256>(a, plan.ring, st);
+    default: return launch_attn<512>(a, plan.ring, st);
   }
 }
 
@@ -1141,7 +1114,7 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
 extern "C" size_t csa_sparse_attn_workspace_bytes(int32_t T, int32_t H, int32_t D, int32_t k,
                                                   int32_t window) {
   if (T <= 0 || H <= 0 || D <= 0 || k < 0 || window < 0) return 0;
-  const csa::SplitPlan plan = csa::plan_splits(T, H, k, window, false);
+  const csa::SplitPlan plan = csa::plan_splits(T, k, window, false);
   if (plan.splits <= 1) return 0;
   return csa::attn_ws_bytes(T, plan.splits, H, D);
 }
