@@ -90,14 +90,6 @@ constexpr uint32_t kNoRow = 0xffffffffu;
 constexpr int kRing = 4;          // key tiles resident in LDS (in flight or in use)
 constexpr float kSlack = 8.0f;    // log2 headroom before the running max is moved
 
-// s_waitcnt immediate that waits until at most n vector-memory ops are
-// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
-// left at "no wait").
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Exclusive scan over a work-group of NW waves (scratch: one int per wave).
 template <int NW>
@@ -122,9 +114,6 @@ __device__ int block_excl_scan_n(int v, int* wsum, int* total) {
   }
   *total = tot;
   return before + incl - v;
-}
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
-  return block_excl_scan_n<kAttnWaves>(v, wsum, total);
 }
 
 // block_excl_scan_n with LDS-only barriers (vector loads in flight are not
