@@ -270,3 +270,26 @@ def test_index_shapes(Hi, Di):
                                 cfg.T, cfg.ratio, step.score_stride)
     assert int(step.err.item()) == oe == 0
     H.check_scores(step.scores.cpu().numpy().astype(np.float64), o, f"index Hi{Hi} Di{Di}")
+
+
+@pytest.mark.parametrize("rows", [(6, 6), (1, 1, 1, 1), (3, 1), (2, 2, 2), (5,), (4, 0, 4)])
+def test_index_group_layouts(rows):
+    """Row groups of the indexer: requests of equal length (whose groups the
+    kernel derives without scanning query_start_loc, including requests of
+    more than four rows), and divisible or empty-request batches where that
+    guess is wrong and the scan decides."""
+    print(f"[edges] index rows={rows}", flush=True)
+    positions = tuple(tuple(300 + 97 * b + 5 * i for i in range(n)) for b, n in enumerate(rows))
+    cfg = CsaConfig(name="igroups", description="indexer row-group layouts",
+                    rows_per_request=rows, positions=positions, H=8, D=64, R=16, Hi=8, Di=64,
+                    W=16, ratio=1, k=64, context=1100, rope_capacity=2048)
+    x = synthetic.make_inputs(cfg, seed=9).t
+    csa = _csa()
+    step = csa.step_for_config(cfg, x)
+    step.index()
+    torch.cuda.synchronize()
+    o, oe = oracle.index_scores(x["q_idx"], x["q_scale"], x["head_w"], x["idx_kv"], x["idx_scale"],
+                                x["cmp_block_table"], x["query_start_loc"], x["positions"],
+                                cfg.T, cfg.ratio, step.score_stride)
+    assert int(step.err.item()) == oe == 0
+    H.check_scores(step.scores.cpu().numpy().astype(np.float64), o, f"index rows {rows}")
