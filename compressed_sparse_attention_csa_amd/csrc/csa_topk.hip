@@ -485,13 +485,17 @@ __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, co
                     (key[j] > ck || (key[j] == ck && static_cast<uint32_t>(pos(j)) <= cp));
     pick |= in ? (1u << j) : 0u;
   }
+  // the chosen scores are loaded before any is stored, so a thread's picks
+  // share one memory latency
+  float val[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) val[j] = (out_v && ((pick >> j) & 1u)) ? row[pos(j)] : 0.0f;
   int o = block_excl_scan<THREADS / 64>(__popc(pick), sh.wsum, nullptr);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if ((pick >> j) & 1u) {
-      const int c = pos(j);
-      out_i[o] = c;
-      if (out_v) out_v[o] = row[c];
+      out_i[o] = pos(j);
+      if (out_v) out_v[o] = val[j];
       ++o;
     }
   }
