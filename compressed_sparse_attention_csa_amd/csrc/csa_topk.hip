@@ -58,6 +58,7 @@ constexpr int kFThreads = 1024;      // sample and final kernels
 constexpr int kFPer = kCap / kFThreads;
 constexpr int kSampleGroups = 2048;  // float4 groups a row's sample reads (2 per thread)
 constexpr long long kMaxStride = 1ll << 24;
+constexpr int kMaxSeg = static_cast<int>(kMaxStride / kChunk) * kLWaves;   // segments per row
 constexpr int kMetaWords = 8;        // [0]: the row's sampled threshold key
 constexpr uint32_t kKeyNegInf = 0x007fffffu;
 constexpr uint32_t kKeyPosInf = 0xff800000u;
@@ -883,6 +884,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
   __shared__ SelShared<kFThreads> sh;
   __shared__ uint32_t ckey[kCap];
   __shared__ uint32_t cpos[kCap];
+  __shared__ uint32_t segstart[kMaxSeg + 1];   // first candidate slot of each segment, then total
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
@@ -919,16 +921,39 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       if (total < m || total > kCap) {
         whole_row = true;   // the sample misled: exact select over the row
       } else {
+        // segment s is copied by tps threads (kFThreads / nseg rounded down
+        // to a power of two, at least 1), each taking every tps-th entry;
+        // loads go out in batches of kBatch before any is stored
         for (int i = 0; i < spt; ++i) {
           const int sidx = tid * spt + i;
           if (sidx < nseg) {
-            const uint32_t c = seg[sidx];
-            const uint2* src = cand + static_cast<size_t>(sidx) * kSub;
-            for (uint32_t q = 0; q < c; ++q) {
-              const uint2 e = src[q];
-              ckey[dst] = e.x;
-              cpos[dst] = e.y;
-              ++dst;
+            segstart[sidx] = static_cast<uint32_t>(dst);
+            dst += static_cast<int>(seg[sidx]);
+          }
+        }
+        if (tid == 0) segstart[nseg] = static_cast<uint32_t>(total);
+        __syncthreads();
+        int tps = 1;
+        while (tps * 2 * nseg <= kFThreads) tps *= 2;
+        constexpr int kBatch = 8;
+        for (int sidx = tid / tps; sidx < nseg; sidx += kFThreads / tps) {
+          const int d0 = static_cast<int>(segstart[sidx]);
+          const int c = static_cast<int>(segstart[sidx + 1]) - d0;
+          const uint2* src = cand + static_cast<size_t>(sidx) * kSub;
+          for (int q0 = tid % tps; q0 < c; q0 += kBatch * tps) {
+            uint2 e[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+              const int q = q0 + u * tps;
+              e[u] = q < c ? src[q] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+              const int q = q0 + u * tps;
+              if (q < c) {
+                ckey[d0 + q] = e[u].x;
+                cpos[d0 + q] = e[u].y;
+              }
             }
           }
         }
