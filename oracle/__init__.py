@@ -12,5 +12,5 @@ from .csa_oracle import (  # noqa: F401
     PAGE, EFLAG_POS_RANGE, EFLAG_BLOCK_RANGE, EFLAG_TOPK_RANGE, EFLAG_META,
     bf16_to_f64, visible_count, window_positions, owner_request,
     rotate_adjacent_pairs, materialize_rope_rows, index_scores, topk,
-    kv_rows_for_query, sparse_attn,
+    kv_rows_for_query, deterministic_selection, sparse_attn,
 )

@@ -263,19 +263,39 @@ def topk(scores, positions, ratio, num_tokens, k):
 # a5 + a6/a7: shared-KV sparse attention with sink
 # ----------------------------------------------------------------------------
 
+def deterministic_selection(p, ratio, k):
+    """The compressed rows of a layer without an indexer (the ratio-128 HCA
+    layers): every causally visible compressed row, positions 0 .. n_vis - 1.
+    [HP] Stage-2 call for ratio=128 passes no sparse indices (attention over
+    the whole causally visible compressed KV plus the window); [MTP] sections
+    "Layer schedule" and "Attention paths" give the HCA layers a
+    deterministic top-k and no indexer.  k bounds the count:
+    a row with more visible rows keeps the first k and reports TOPK_RANGE.
+    Returns (positions, err)."""
+    n = visible_count(p, ratio)
+    m = min(n, int(k))
+    return np.arange(m, dtype=np.int64), (EFLAG_TOPK_RANGE if n > m else 0)
+
+
 def kv_rows_for_query(t, b, p, topk_row, ratio, window, cmp_block_table, num_cmp_blocks,
-                      win_block_table, num_win_blocks):
+                      win_block_table, num_win_blocks, k=None):
     """The key/value rows of one query, window first then selected compressed
     rows, as (pool, flat_row) pairs -- [HP] 9.1: kv_full = [window KV,
     compressed KV], topk_idxs = [window_idxs, compressed_idxs]; the two caches
-    are separate, so nothing is deduplicated.  Returns (win_rows, cmp_rows, err)."""
+    are separate, so nothing is deduplicated.  topk_row None takes the
+    deterministic selection (every visible compressed row, bounded by k).
+    Returns (win_rows, cmp_rows, err)."""
     err = 0
     wpos = np.asarray(list(window_positions(p, window)), dtype=np.int64)
     wrows, wok = _physical_rows(win_block_table[b], num_win_blocks, wpos)
     if not wok.all():
         err |= EFLAG_BLOCK_RANGE
     n = visible_count(p, ratio)
-    sel = np.asarray([int(c) for c in topk_row if int(c) >= 0], dtype=np.int64)
+    if topk_row is None:
+        sel, e = deterministic_selection(p, ratio, k)
+        err |= e
+    else:
+        sel = np.asarray([int(c) for c in topk_row if int(c) >= 0], dtype=np.int64)
     if np.any(sel >= n):
         err |= EFLAG_TOPK_RANGE
     sel = sel[sel < n]
@@ -287,7 +307,7 @@ def kv_rows_for_query(t, b, p, topk_row, ratio, window, cmp_block_table, num_cmp
 
 def sparse_attn(q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table,
                 topk_idx, ratio, win_kv, win_block_table, window, attn_sink,
-                softmax_scale, query_start_loc, positions, num_tokens):
+                softmax_scale, query_start_loc, positions, num_tokens, k=None):
     """Shared-KV multi-head attention over the window rows and the selected
     compressed rows, with one sink logit per head.
 
@@ -302,6 +322,11 @@ def sparse_attn(q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table,
         Z      = exp(sink_h - M) + sum_j exp(l_j - M)
         out    = sum_j exp(l_j - M) / Z * K_j
         lse    = M + log Z
+
+    topk_idx None (with the bound k) selects every causally visible
+    compressed row (deterministic_selection: the HCA layers); a selection
+    with no columns leaves the window alone (the SWA-only layers of [MTP]
+    "Layer schedule": sliding window only, no compressor, no indexer).
 
     Contract checks: an active row that no request owns flags META and is
     treated as having no keys; window pages with invalid block ids, and
@@ -330,8 +355,9 @@ def sparse_attn(q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table,
             lse[t] = sink
             continue
         p = int(positions[t])
-        wrows, crows, e = kv_rows_for_query(t, b, p, topk_idx[t], ratio, window,
-                                            cmp_block_table, ncb, win_block_table, nwb)
+        wrows, crows, e = kv_rows_for_query(t, b, p, None if topk_idx is None else topk_idx[t],
+                                            ratio, window, cmp_block_table, ncb,
+                                            win_block_table, nwb, k)
         err |= e
         kv = np.concatenate([bf16_to_f64(win_flat[wrows]), bf16_to_f64(cmp_flat[crows])], axis=0)
         qt = bf16_to_f64(q[t])                                          # [H, D]

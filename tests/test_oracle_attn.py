@@ -8,7 +8,9 @@ under permuting the selection and shuffling block tables; k covering every
 visible compressed row equalling dense causal attention over those rows plus
 the window; the relative-position property of the query rotation; the window
 extent of gitcode hyper-parallel issue #2 section 7.1; and the union without
-dedup of section 9.1.
+dedup of section 9.1.  The layers without an indexer are checked the same
+way: the HCA selection (every visible compressed row) against the dense
+route and an explicit selection, its bound, and the SWA-only window.
 """
 import json
 import math
@@ -299,3 +301,62 @@ def test_contract_flags_and_empty_set():
     a["query_start_loc"] = np.array([0, 1], np.int32)
     out, lse, err = oracle.sparse_attn(**a)
     assert err == oracle.EFLAG_META and np.all(out[1] == 0)
+
+
+# ---- layers without an indexer: HCA (every visible compressed row) and
+#      SWA-only (the window alone)
+
+def test_hca_selection_is_dense_causal_attention():
+    """No selection array: every causally visible compressed row plus the
+    window, checked by the independent dense route (scipy softmax) and
+    against the same rows passed as an explicit selection."""
+    rng = np.random.default_rng(41)
+    ctx, ratio, W = 1100, 128, 16     # ratio 128: 7 .. 8 visible compressed rows
+    a, cd, wd = _build(rng, rows=(2, 3), B=2, ctx=(ctx, 900), ratio=ratio, W=W, k=16)
+    a["topk_idx"] = None
+    out, lse, err = oracle.sparse_attn(**a, k=16)
+    assert err == 0
+    explicit = np.full((a["num_tokens"], 16), -1, np.int32)
+    for t in range(a["num_tokens"]):
+        nv = oracle.visible_count(a["positions"][t], ratio)
+        assert 1 <= nv <= 16
+        explicit[t, :nv] = np.arange(nv)
+    b = dict(a, topk_idx=explicit)
+    out2, lse2, err2 = oracle.sparse_attn(**b)
+    assert err2 == 0 and np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    ro, rl = _dense_reference(b, cd, wd)
+    assert np.allclose(out, ro, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, rl, rtol=1e-12)
+
+
+def test_hca_selection_bound():
+    """A row with more visible compressed rows than the bound keeps the first
+    k of them and reports TOPK_RANGE."""
+    assert oracle.deterministic_selection(1279, 128, 16)[1] == 0
+    sel, e = oracle.deterministic_selection(1279, 128, 16)
+    assert np.array_equal(sel, np.arange(10)) and e == 0
+    sel, e = oracle.deterministic_selection(1279, 128, 4)
+    assert np.array_equal(sel, np.arange(4)) and e == oracle.EFLAG_TOPK_RANGE
+    sel, e = oracle.deterministic_selection(126, 128, 4)
+    assert sel.size == 0 and e == 0
+    rng = np.random.default_rng(43)
+    a, cd, wd = _build(rng, rows=(1,), ctx=(1100,), ratio=128, W=8, k=4)
+    a["topk_idx"] = None
+    out, lse, err = oracle.sparse_attn(**a, k=4)
+    assert err == oracle.EFLAG_TOPK_RANGE
+    b = dict(a, topk_idx=np.arange(4, dtype=np.int32)[None, :])
+    out2, lse2, _ = oracle.sparse_attn(**b)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_swa_only_is_window_softmax_attention():
+    """A selection with no columns attends over the window alone: the
+    independent dense route over the window rows."""
+    rng = np.random.default_rng(47)
+    a, cd, wd = _build(rng, rows=(3,), ctx=(400,), ratio=4, W=32, k=4)
+    a["topk_idx"] = np.zeros((a["num_tokens"], 0), np.int32)
+    out, lse, err = oracle.sparse_attn(**a)
+    assert err == 0
+    ro, rl = _dense_reference(a, cd, wd)
+    assert np.allclose(out, ro, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, rl, rtol=1e-12)
