@@ -86,6 +86,7 @@ def work_model(cfg, x, topk_idx: np.ndarray):
     index keys of every visible position once per request, every unique
     gathered KV row once per request, Q, O, lse and small metadata)."""
     T, H, D, R, Hi, Di, k = cfg.T, cfg.H, cfg.D, cfg.R, cfg.Hi, cfg.Di, cfg.k
+    mode = getattr(cfg, "mode", "csa")
     qsl = np.asarray(x["query_start_loc"])
     pos = np.asarray(x["positions"])
     nv = np.array([visible(p, cfg.ratio) for p in pos])
@@ -96,25 +97,34 @@ def work_model(cfg, x, topk_idx: np.ndarray):
         rows = range(qsl[b], qsl[b + 1])
         if not len(rows):
             continue
-        idx_keys += int(max(nv[t] for t in rows))
+        if mode == "csa":
+            idx_keys += int(max(nv[t] for t in rows))
         win, sel = set(), set()
         for t in rows:
             p = int(pos[t])
             w = list(range(max(0, p - cfg.W + 1), p + 1))
-            s = [int(c) for c in topk_idx[t] if c >= 0]
+            if mode == "csa":
+                s = [int(c) for c in topk_idx[t] if c >= 0]
+            elif mode == "hca":   # every visible compressed row, bounded by k
+                s = list(range(min(int(nv[t]), k)))
+            else:                 # swa: the window alone
+                s = []
             win.update(w)
             sel.update(s)
             pairs += len(w) + len(s)
         kv_rows += len(win) + len(sel)
-    q_side = T * Hi * (Di + 8)
+    q_side = T * Hi * (Di + 8) if mode == "csa" else 0
+    sel_bytes = 4 * T * k if mode == "csa" else 0   # the selection array the attention reads
     st = {
         "rope": 8 * T * R + 4 * T,   # read + write cos and sin rows (R/2 FP32 each), positions
         "index": idx_keys * (Di + 4) + q_side + 4 * T * cfg.score_stride,
         "topk": 4 * int(nv.clip(max=cfg.score_stride).sum()) + 8 * T * k,
-        "attn": kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + 4 * T * k + 4 * T * R,
+        "attn": kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + sel_bytes + 4 * T * R,
     }
+    if mode != "csa":
+        st = {"rope": st["rope"], "attn": st["attn"]}
     step = (idx_keys * (Di + 4) + kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + q_side
-            + 8 * T * k + 4 * T * R)
+            + 2 * sel_bytes + 4 * T * R)
     flops = {"attn": pairs * H * D * 4,
              "index": int(sum(nv[t] for t in range(T))) * Hi * Di * 2}
     return dict(stage_bytes=st, step_bytes=step, flops=flops, kv_rows=kv_rows,
@@ -158,6 +168,7 @@ def cpu_baseline(cfg, x, budget_s: float):
         blas_threads = 1
     cores = min(blas_threads, len(os.sched_getaffinity(0)))
     T = cfg.T
+    mode = getattr(cfg, "mode", "csa")
     # sample: whole rows of the workload; all of them when they fit the budget
     rows_per_call = T if T <= 16 else 16
     done_rows = 0
@@ -180,17 +191,21 @@ def cpu_baseline(cfg, x, budget_s: float):
         oracle.materialize_rope_rows(sub["freqs_cos"], sub["freqs_sin"], sub["position_ids"], n,
                                      rc, rs)
         b_ = time.perf_counter()
-        s, _ = oracle.index_scores(sub["q_idx"], sub["q_scale"], sub["head_w"], sub["idx_kv"],
-                                   sub["idx_scale"], sub["cmp_block_table"],
-                                   sub["query_start_loc"], sub["positions"], n, cfg.ratio,
-                                   cfg.score_stride)
-        c_ = time.perf_counter()
-        idx, _, _ = oracle.topk(s, sub["positions"], cfg.ratio, n, cfg.k)
+        if mode == "csa":
+            s, _ = oracle.index_scores(sub["q_idx"], sub["q_scale"], sub["head_w"], sub["idx_kv"],
+                                       sub["idx_scale"], sub["cmp_block_table"],
+                                       sub["query_start_loc"], sub["positions"], n, cfg.ratio,
+                                       cfg.score_stride)
+            c_ = time.perf_counter()
+            idx, _, _ = oracle.topk(s, sub["positions"], cfg.ratio, n, cfg.k)
+        else:   # hca: every visible compressed row; swa: no compressed row
+            c_ = time.perf_counter()
+            idx = None if mode == "hca" else np.zeros((n, 0), np.int32)
         d_ = time.perf_counter()
         oracle.sparse_attn(sub["q"], rc, rs, cfg.rope_offset, sub["cmp_kv"],
                            sub["cmp_block_table"], idx, cfg.ratio, sub["win_kv"],
                            sub["win_block_table"], cfg.W, sub["attn_sink"], cfg.softmax_scale,
-                           sub["query_start_loc"], sub["positions"], n)
+                           sub["query_start_loc"], sub["positions"], n, k=cfg.k)
         e_ = time.perf_counter()
         stage["rope"] += b_ - a
         stage["index"] += c_ - b_
@@ -202,8 +217,10 @@ def cpu_baseline(cfg, x, budget_s: float):
     el = time.perf_counter() - t0
     return {"value": done_rows / el, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done_rows} query rows of this workload ({rows_per_call} per oracle call, "
-                      f"all four stages, float64 NumPy) in {el:.1f} s",
-            "stage_seconds": {k: round(v, 3) for k, v in stage.items()}}
+                      f"{'all four stages' if mode == 'csa' else 'rope rows and attention'}, "
+                      f"float64 NumPy) in {el:.1f} s",
+            "stage_seconds": {k: round(v, 3) for k, v in stage.items()
+                              if mode == "csa" or k in ("rope", "attn")}}
 
 
 # ---------------------------------------------------------------------------
@@ -236,7 +253,7 @@ def main():
         copies = int(min(48, max(1, -(-(512 << 20) // max(per_copy_touch, 1)))))
     steps = [first] + [csa.step_for_config(cfg, x, shared=shared) for _ in range(copies - 1)]
 
-    stages = ("rope", "index", "topk", "attn")
+    stages = first.stages
     for i in range(args.warmup):
         steps[i % copies].run()
     torch.cuda.synchronize()
@@ -320,7 +337,10 @@ def main():
         "config": {"workload": cfg.name, "rows": cfg.T, "requests": cfg.B, "heads": cfg.H,
                    "head_dim": cfg.D, "ratio": cfg.ratio, "top_k": cfg.k, "window": cfg.W,
                    "compressed_rows_per_request": cfg.n_cmp_per_request,
-                   "indexer": f"{cfg.Hi}x{cfg.Di}", "input_copies": copies,
+                   "indexer": f"{cfg.Hi}x{cfg.Di}" if first.mode == "csa" else "none",
+                   "selection": {"csa": "indexer top-k", "hca": "every visible compressed row",
+                                 "swa": "window only"}[first.mode],
+                   "input_copies": copies,
                    "cache": "warm" if copies == 1 else "cold (rotating copies > 512 MiB)"},
         "step_hbm": {"algorithmic_bytes": wm["step_bytes"], "achieved_gbs": round(step_gbs, 1),
                      "frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4)},

@@ -154,16 +154,23 @@ def csa_sparse_attn_workspace_bytes(T: int, H: int, D: int, k: int, window: int)
 
 def _attn(fn_name, q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table, topk_idx, ratio,
           win_kv, win_block_table, window, attn_sink, softmax_scale, query_start_loc, positions,
-          num_tokens, out, lse=None, workspace=None, err=None, stream=None):
+          num_tokens, out, lse=None, workspace=None, err=None, stream=None, k=None):
+    """topk_idx None selects every visible compressed row, with k (required
+    then) bounding their count; k = 0 attends over the window alone, and the
+    compressed pool and table may then be None."""
     _need(q, _BF16, 3, "q")
     _need(out, _BF16, 3, "out")
     T, H, D = q.shape
-    k = topk_idx.shape[1]
+    if topk_idx is not None:
+        k = topk_idx.shape[1]
+    elif k is None:
+        raise CsaError("k is required when topk_idx is None")
     rope_dim = 2 * rope_cos.shape[1]
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(load(), fn_name)(
         _ptr(q), _ptr(rope_cos), _ptr(rope_sin), rope_dim, int(rope_offset), _ptr(cmp_kv),
-        cmp_kv.shape[0], _ptr(cmp_block_table), cmp_block_table.shape[1], _ptr(topk_idx), k,
+        0 if cmp_kv is None else cmp_kv.shape[0], _ptr(cmp_block_table),
+        0 if cmp_block_table is None else cmp_block_table.shape[1], _ptr(topk_idx), int(k),
         int(ratio), _ptr(win_kv), win_kv.shape[0], _ptr(win_block_table),
         win_block_table.shape[1], int(window), _ptr(attn_sink), float(softmax_scale),
         _ptr(query_start_loc), _ptr(positions), query_start_loc.shape[0] - 1, T,

@@ -84,7 +84,8 @@ struct AttnArgs {
 
 __device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
-constexpr int kMaxSplit = 4224;  // longest key list: window + k
+constexpr int kMaxSplit = 4224;  // longest key list of the ring schedule: window + k
+constexpr int kMaxDenseK = 1 << 20;   // bound on k without a selection array
 constexpr uint32_t kWinBit = 0x80000000u;
 constexpr uint32_t kNoRow = 0xffffffffu;
 constexpr int kRing = 4;          // key tiles resident in LDS (in flight or in use)
@@ -210,10 +211,11 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   // off the resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
-  const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
+  // (no selection array: the compressed set is every visible row, 0 .. n_vis-1)
+  const int32_t* topk_row = a.topk ? a.topk + static_cast<long long>(t) * a.k : nullptr;
   const int i_spec0 = tid - a.window, i_spec1 = kRingThreads + tid - a.window;
-  const int c_spec0 = (i_spec0 >= 0 && i_spec0 < a.k) ? topk_row[i_spec0] : -1;
-  const int c_spec1 = (i_spec1 >= 0 && i_spec1 < a.k) ? topk_row[i_spec1] : -1;
+  const int c_spec0 = (topk_row && i_spec0 >= 0 && i_spec0 < a.k) ? topk_row[i_spec0] : -1;
+  const int c_spec1 = (topk_row && i_spec1 >= 0 && i_spec1 < a.k) ? topk_row[i_spec1] : -1;
   v4i qraw[KS];
   {
     const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
@@ -246,6 +248,7 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   {
     int ebits = 0;
     const bool spec_ok = w_len == a.window;
+    if (!topk_row && a.k > 0 && b >= 0 && nv > a.k && tid == 0) ebits |= CSA_EFLAG_TOPK_RANGE;
     for (int j0 = 0, r = 0; j0 < n_my; j0 += kRingThreads, ++r) {
       const int i = j0 + tid;
       uint32_t rr = kNoRow;
@@ -256,10 +259,11 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
                                      a.max_win_blocks, a.num_win_blocks, w_lo + i);
         if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
       } else {
-        const int c = (spec_ok && r < 2) ? (r == 0 ? c_spec0 : c_spec1) : topk_row[i - w_len];
+        const int c = !topk_row ? i - w_len
+                      : (spec_ok && r < 2) ? (r == 0 ? c_spec0 : c_spec1) : topk_row[i - w_len];
         if (c >= 0) {
           if (c >= nv) {
-            ebits |= CSA_EFLAG_TOPK_RANGE;
+            if (topk_row) ebits |= CSA_EFLAG_TOPK_RANGE;   // past n_vis: not selected
           } else {
             const long long r = page_row(a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks,
                                          a.max_cmp_blocks, a.num_cmp_blocks, c);
@@ -634,9 +638,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   // few tokens), which takes a dependent round trip off the resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
-  const int32_t* topk_row = a.topk + static_cast<long long>(t) * a.k;
+  // (no selection array: the compressed set is every visible row, 0 .. n_vis-1)
+  const int32_t* topk_row = a.topk ? a.topk + static_cast<long long>(t) * a.k : nullptr;
   const int i_spec = split * kSpan + tid - a.window;
-  const int c_spec = (i_spec >= 0 && i_spec < a.k) ? topk_row[i_spec] : -1;
+  const int c_spec = (topk_row && i_spec >= 0 && i_spec < a.k) ? topk_row[i_spec] : -1;
   // the query and the rope row: in flight during the row resolution, and
   // complete before the gather is issued (a load issued after the gather
   // would wait for it)
@@ -671,6 +676,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   int n_valid = 0;
   {
     int ebits = 0;
+    if (!topk_row && a.k > 0 && b >= 0 && nv > a.k && split == 0 && tid == 0)
+      ebits |= CSA_EFLAG_TOPK_RANGE;   // bound below n_vis (k = 0: the window alone)
     uint32_t rr = kNoRow;
     const int j = tid;
     if (j < n_my) {
@@ -680,10 +687,10 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
                                      a.max_win_blocks, a.num_win_blocks, w_lo + i);
         if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
       } else {
-        const int c = (w_len == a.window) ? c_spec : topk_row[i - w_len];
+        const int c = !topk_row ? i - w_len : (w_len == a.window) ? c_spec : topk_row[i - w_len];
         if (c >= 0) {
           if (c >= nv) {
-            ebits |= CSA_EFLAG_TOPK_RANGE;
+            if (topk_row) ebits |= CSA_EFLAG_TOPK_RANGE;   // past n_vis: not selected
           } else {
             const long long r = page_row(a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks,
                                          a.max_cmp_blocks, a.num_cmp_blocks, c);
@@ -900,8 +907,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
 
 // Combine the span partials of each (row, head) with the sink: one wave per
 // (row, head).  Lane l owns channels [8l, 8l + 8) of every partial (D = 512;
-// D / 64 channels in general).  The (max, sum) pairs and the first eight
-// partials are loaded together, so a merge costs one memory latency.
+// D / 64 channels in general).  Lanes stride over the spans for the running
+// max and the denominator (any number of spans); each chunk of eight
+// partials is loaded together with its spans' (max, sum) pairs, and the
+// first chunk goes out with the pairs of the max pass, so a row of at most
+// 64 spans costs one memory latency before its sums.
 constexpr int kMergeChunk = 8;
 
 template <int D>
@@ -923,11 +933,14 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
   float chunk[kMergeChunk][CPL];
+  float2 cml[kMergeChunk];
   auto load_chunk = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
       const int sp = s0 + u;
-      const float* po = part_o + ((tbase + (sp < splits ? sp : 0)) * H + h) * D + lane * CPL;
+      const long long sl = tbase + (sp < splits ? sp : 0);
+      cml[u] = sp < splits ? part_ml[sl * H + h] : make_float2(neg_inf, 0.0f);
+      const float* po = part_o + (sl * H + h) * D + lane * CPL;
       if constexpr (CPL >= 4) {
 #pragma unroll
         for (int v = 0; v < V4; ++v) {
@@ -947,11 +960,15 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
   // running max and denominator over the spans, with the sink
   const float sink2 = sink[h] * kLog2e;
   float M = ml.x;
+  for (int s = lane + 64; s < splits; s += 64) M = fmaxf(M, part_ml[(tbase + s) * H + h].x);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   M = fmaxf(M, sink2);
-  const float w_l = (ml.x == neg_inf) ? 0.0f : exp2f(ml.x - M);
-  float z = ml.y * w_l;
+  float z = ml.x == neg_inf ? 0.0f : ml.y * exp2f(ml.x - M);
+  for (int s = lane + 64; s < splits; s += 64) {
+    const float2 m2 = part_ml[(tbase + s) * H + h];
+    z += m2.x == neg_inf ? 0.0f : m2.y * exp2f(m2.x - M);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
   z += exp2f(sink2 - M);
@@ -959,8 +976,8 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
     if (s0 > 0) load_chunk(s0);
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
-      const float w = __shfl(w_l, (s0 + u) & 63, 64);
       if (s0 + u < splits) {
+        const float w = cml[u].x == neg_inf ? 0.0f : exp2f(cml[u].x - M);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) acc[i] += chunk[u][i] * w;
       }
@@ -1030,10 +1047,13 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   if (T < 0 || B < 0 || num_cmp_blocks < 0 || num_win_blocks < 0 || max_cmp_blocks < 0 ||
       max_win_blocks < 0 || window < 0 || k < 0)
     return CSA_ERR_SHAPE;
-  if (num_tokens < 0 || num_tokens > T || ratio < 1 || k > 4096) return CSA_ERR_RANGE;
+  // a selection array holds at most 4096 entries per row (csa_topk's bound);
+  // without one, k bounds the visible compressed rows of a row
+  if (num_tokens < 0 || num_tokens > T || ratio < 1 || (topk_idx && k > 4096) ||
+      k > kMaxDenseK)
+    return CSA_ERR_RANGE;
   if (num_tokens == 0) return CSA_OK;
   if (!q || !attn_sink || !query_start_loc || !positions || !out) return CSA_ERR_NULL;
-  if (k > 0 && !topk_idx) return CSA_ERR_NULL;
   if (rope_dim > 0 && (!rope_cos || !rope_sin)) return CSA_ERR_NULL;
   if (H < 1 || H > 64) return CSA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128 && D != 256 && D != 512) return CSA_ERR_UNSUPPORTED;
@@ -1043,12 +1063,13 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
        reinterpret_cast<uintptr_t>(cmp_kv) | reinterpret_cast<uintptr_t>(win_kv)) & 15)
     return CSA_ERR_UNSUPPORTED;
-  // the key list lives in LDS; pool rows are packed in 31 bits
-  if (window + k > kMaxSplit) return CSA_ERR_UNSUPPORTED;
+  // pool rows are packed in 31 bits
   if (static_cast<long long>(num_cmp_blocks) * kPage >= (1ll << 31) ||
       static_cast<long long>(num_win_blocks) * kPage >= (1ll << 31))
     return CSA_ERR_UNSUPPORTED;
   const SplitPlan plan = plan_splits(num_tokens, k, window, prefill);
+  // the ring schedule holds a row's whole key list in LDS
+  if (plan.ring && window + k > kMaxSplit) return CSA_ERR_UNSUPPORTED;
   AttnArgs a{};
   a.q = q;
   a.rope_cos = rope_cos;

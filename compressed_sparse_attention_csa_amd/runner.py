@@ -2,7 +2,8 @@
 
 ``CsaStep`` uploads host arrays (NumPy) once, allocates every output and
 workspace up front, and then runs the path as four library calls on one
-stream: RoPE rows -> indexer scores -> top-k -> sparse attention.  It only
+stream: RoPE rows -> indexer scores -> top-k -> sparse attention (RoPE rows ->
+attention for the layers without an indexer).  It only
 moves memory and passes pointers; all arithmetic runs in libcsa.so.
 """
 from __future__ import annotations
@@ -27,7 +28,14 @@ class CsaStep:
     def __init__(self, arrays: Dict[str, np.ndarray], *, ratio: int, k: int, window: int,
                  rope_offset: int, softmax_scale: float, num_tokens: Optional[int] = None,
                  prefill: bool = False, device: str = "cuda", with_values: bool = True,
-                 with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None):
+                 with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None,
+                 mode: str = "csa"):
+        # mode "csa": indexer scores and top-k select the compressed rows;
+        # "hca": no indexer, every visible compressed row (k bounds them);
+        # "swa": the window alone (k = 0)
+        if mode not in ("csa", "hca", "swa"):
+            raise ValueError(f"unknown mode {mode!r}")
+        self.mode = mode
         self.ratio, self.k, self.window = int(ratio), int(k), int(window)
         self.rope_offset, self.softmax_scale = int(rope_offset), float(softmax_scale)
         self.prefill = prefill
@@ -79,20 +87,25 @@ class CsaStep:
     def attn(self, stream=None, topk_idx: Optional[torch.Tensor] = None):
         t = self.t
         fn = _lib.csa_sparse_attn_prefill if self.prefill else _lib.csa_sparse_attn_decode
+        if topk_idx is None and self.mode == "csa":
+            topk_idx = self.topk_idx
         fn(t["q"], self.rope_cos, self.rope_sin, self.rope_offset, t["cmp_kv"],
-           t["cmp_block_table"], self.topk_idx if topk_idx is None else topk_idx, self.ratio,
-           t["win_kv"], t["win_block_table"], self.window, t["attn_sink"], self.softmax_scale,
-           t["query_start_loc"], t["positions"], self.num_tokens, self.out, lse=self.lse,
-           workspace=self.attn_ws, err=self.err, stream=stream)
+           t["cmp_block_table"], topk_idx, self.ratio, t["win_kv"], t["win_block_table"],
+           self.window, t["attn_sink"], self.softmax_scale, t["query_start_loc"],
+           t["positions"], self.num_tokens, self.out, lse=self.lse, workspace=self.attn_ws,
+           err=self.err, stream=stream, k=self.k)
+
+    @property
+    def stages(self):
+        return ("rope", "index", "topk", "attn") if self.mode == "csa" else ("rope", "attn")
 
     def run(self, stream=None):
-        self.rope(stream)
-        self.index(stream)
-        self.topk(stream)
-        self.attn(stream)
+        for s in self.stages:
+            getattr(self, s)(stream)
 
 
 def step_for_config(cfg, arrays: Dict[str, np.ndarray], **kw) -> CsaStep:
     """CsaStep with the scalar parameters of a workload config."""
     return CsaStep(arrays, ratio=cfg.ratio, k=cfg.k, window=cfg.W, rope_offset=cfg.rope_offset,
-                   softmax_scale=cfg.softmax_scale, prefill=(cfg.T > 256), **kw)
+                   softmax_scale=cfg.softmax_scale, prefill=(cfg.T > 256),
+                   mode=getattr(cfg, "mode", "csa"), **kw)

@@ -180,7 +180,15 @@ int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions
  *   cmp_kv       BF16 [num_cmp_blocks, 128, D]  compressed KV (K = V)
  *   cmp_block_table INT32 [B, max_cmp_blocks]
  *   topk_idx     INT32 [T, k]: request-local compressed positions; negative
- *                entries are padding
+ *                entries are padding.  NULL selects, for each row, every
+ *                causally visible compressed row, positions 0 .. n_vis - 1
+ *                (the indexer-less ratio-128 HCA layers: [MTP] "Layer
+ *                schedule" and "Attention paths"; the [HP] Stage-2 call for
+ *                ratio=128 passes no sparse indices); k then bounds n_vis,
+ *                and a row with n_vis > k keeps positions 0 .. k - 1 and sets
+ *                CSA_EFLAG_TOPK_RANGE.  k = 0 leaves the window alone (the
+ *                SWA-only layers; no flag); topk_idx and the compressed pool
+ *                may then be NULL
  *   win_kv       BF16 [num_win_blocks, 128, D]  raw-token (window) KV
  *   win_block_table INT32 [B, max_win_blocks], indexed by raw position
  *   attn_sink    FP32 [H]
@@ -202,8 +210,10 @@ int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions
  * CSA_EFLAG_TOPK_RANGE, left out; a window or selected row whose page is past
  * the table or names an invalid block -> CSA_EFLAG_BLOCK_RANGE, left out.
  * Supported: 1 <= H <= 64, D in {64, 128, 256, 512}, rope_dim and rope_offset
- * even, rope_offset + rope_dim <= D, window >= 0, 0 <= k <= 4096,
- * window + k <= 4224, pools of fewer than 2^31 rows.
+ * even, rope_offset + rope_dim <= D, window >= 0, 0 <= k <= 4096 with a
+ * selection array and k <= 2^20 without one, pools of fewer than 2^31 rows;
+ * the prefill schedule (and decode batches of 256 rows or more) needs
+ * window + k <= 4224, the decode schedule takes any key-list length.
  * Arithmetic: the rotated query and the probabilities are rounded to BF16 as
  * MFMA operands; logits, softmax and accumulation are FP32.
  */

@@ -270,11 +270,12 @@ def deterministic_selection(p, ratio, k):
     the whole causally visible compressed KV plus the window); [MTP] sections
     "Layer schedule" and "Attention paths" give the HCA layers a
     deterministic top-k and no indexer.  k bounds the count:
-    a row with more visible rows keeps the first k and reports TOPK_RANGE.
-    Returns (positions, err)."""
+    a row with more visible rows keeps the first k and reports TOPK_RANGE;
+    k = 0 selects nothing and reports nothing (the SWA-only layers: the
+    window alone).  Returns (positions, err)."""
     n = visible_count(p, ratio)
     m = min(n, int(k))
-    return np.arange(m, dtype=np.int64), (EFLAG_TOPK_RANGE if n > m else 0)
+    return np.arange(m, dtype=np.int64), (EFLAG_TOPK_RANGE if int(k) > 0 and n > m else 0)
 
 
 def kv_rows_for_query(t, b, p, topk_row, ratio, window, cmp_block_table, num_cmp_blocks,

@@ -38,6 +38,10 @@ class CsaConfig:
     theta: float = 10000.0
     outlier_frac: float = 0.0   # fraction of compressed positions whose key scale is x4
     shared_pool: bool = False   # all requests page into one pool (C5)
+    # "csa": indexer + top-k select the compressed rows; "hca": no indexer,
+    # every causally visible compressed row (k bounds them); "swa": the
+    # window alone (k = 0)
+    mode: str = "csa"
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -126,8 +130,23 @@ C5 = _decode(
     n_req=2, s=4, context=1 << 20, ratio=1, k=2048, outlier_frac=0.05,
     shared_pool=True)
 
-CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5)}
-SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
+# Layers without an indexer (the layer schedule of the pages' MTP-point
+# model): HCA at ratio 128 attends over every visible compressed row plus the
+# window, SWA over the window alone.
+C6 = _decode(
+    "c6_hca_ratio128_decode",
+    "HCA ratio-128 decode: 8 rows (4 requests x S=2), 1,048,576 tokens -> 8,192 "
+    "compressed rows per request, all of them attended with the 128-token window",
+    n_req=4, s=2, context=1 << 20, ratio=128, k=8192, mode="hca")
+
+C7 = _decode(
+    "c7_swa_decode",
+    "SWA-only decode: 8 rows (4 requests x S=2), 32,768 tokens, the 128-token "
+    "window alone",
+    n_req=4, s=2, context=32768, ratio=128, k=0, mode="swa")
+
+CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7)}
+SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7}
 
 
 def get(name: str) -> CsaConfig:

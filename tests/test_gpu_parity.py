@@ -4,11 +4,13 @@ Every workload config runs the whole step (RoPE rows, indexer scores, top-k,
 sparse attention) on the GPU; the oracle runs on the same seeded inputs (all
 rows, or a fixed sample of the 8,192-row prefill).  Attention is also checked
 on the oracle's own selection, so a selection that differs only at ties never
-hides an attention error.
+hides an attention error.  The layers without an indexer (HCA: every visible
+compressed row; SWA-only: the window) run their RoPE rows and attention.
 """
 import numpy as np
 import pytest
 
+import oracle
 import synthetic
 from tests import harness as H
 
@@ -115,3 +117,63 @@ def test_determinism_c2():
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+@pytest.mark.parametrize("name", ["c6", "c7"])
+def test_indexerless_layer_parity(name):
+    """The layers without an indexer at their full sizes: HCA ratio-128 decode
+    (every visible compressed row of a 1,048,576-token context plus the
+    window, no selection array) and SWA-only decode (the window alone),
+    against the oracle's deterministic selection."""
+    csa = _lib()
+    cfg = synthetic.get(name)
+    print(f"[parity] {cfg.name}", flush=True)
+    x = synthetic.make_inputs(cfg, seed=11).t
+    step = csa.step_for_config(cfg, x)
+    step.out.view(torch.int16).fill_(0x7FDE)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    half = cfg.R // 2
+    rc = np.zeros((cfg.T, half), np.float32)
+    rs = np.zeros_like(rc)
+    oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["position_ids"], cfg.T, rc, rs)
+    assert np.array_equal(step.rope_cos.cpu().numpy().view(np.uint32), rc.view(np.uint32))
+    sel = None if cfg.mode == "hca" else np.zeros((cfg.T, 0), np.int32)
+    oo, ol, oe = oracle.sparse_attn(x["q"], rc, rs, cfg.rope_offset, x["cmp_kv"],
+                                    x["cmp_block_table"], sel, cfg.ratio, x["win_kv"],
+                                    x["win_block_table"], cfg.W, x["attn_sink"],
+                                    cfg.softmax_scale, x["query_start_loc"], x["positions"],
+                                    cfg.T, k=cfg.k)
+    assert oe == 0
+    H.check_attn(H.bf16_to_f64(step.out), oo, step.lse.cpu().numpy(), ol, cfg.name)
+
+
+def test_hca_prefill_and_bound():
+    """HCA through the prefill (ring) schedule, and a bound k below the
+    visible count: the first k compressed rows and TOPK_RANGE, as the
+    oracle."""
+    from synthetic.configs import CsaConfig
+    csa = _lib()
+    cfg = CsaConfig(name="hca_small", description="HCA prefill rows and a short bound",
+                    rows_per_request=(300, 2), positions=(tuple(range(4000, 4300)), (9000, 9001)),
+                    H=16, D=128, R=32, Hi=4, Di=32, W=64, ratio=128, k=80, context=9100,
+                    rope_capacity=16384, mode="hca")
+    x = synthetic.make_inputs(cfg, seed=13).t
+    for fn, k, expect in (("prefill", 80, 0), ("decode", 80, 0), ("decode", 40, oracle.EFLAG_TOPK_RANGE)):
+        step = csa.CsaStep(x, ratio=cfg.ratio, k=k, window=cfg.W, rope_offset=cfg.rope_offset,
+                           softmax_scale=cfg.softmax_scale, prefill=(fn == "prefill"), mode="hca")
+        step.run()
+        torch.cuda.synchronize()
+        half = cfg.R // 2
+        rc = np.zeros((cfg.T, half), np.float32)
+        rs = np.zeros_like(rc)
+        oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["position_ids"], cfg.T,
+                                     rc, rs)
+        oo, ol, oe = oracle.sparse_attn(x["q"], rc, rs, cfg.rope_offset, x["cmp_kv"],
+                                        x["cmp_block_table"], None, cfg.ratio, x["win_kv"],
+                                        x["win_block_table"], cfg.W, x["attn_sink"],
+                                        cfg.softmax_scale, x["query_start_loc"], x["positions"],
+                                        cfg.T, k=k)
+        assert oe == expect and int(step.err.item()) == expect, (fn, k)
+        H.check_attn(H.bf16_to_f64(step.out), oo, step.lse.cpu().numpy(), ol, f"hca {fn} k{k}")

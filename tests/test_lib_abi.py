@@ -105,3 +105,20 @@ def test_attention_host_checks(lib):
     base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
             FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, None, 0, None, None]
     assert lib.csa_sparse_attn_decode(*base) == -5
+
+
+def test_attention_selection_bounds(lib):
+    """A selection array holds at most 4096 entries per row; without one
+    (every visible compressed row) k bounds the visible count up to 2^20, and
+    only the prefill (ring) schedule caps window + k at 4224."""
+    base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
+            FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, None, 0, None, None]
+    bad = list(base); bad[10] = 4097                  # selection array past 4096 entries
+    assert lib.csa_sparse_attn_decode(*bad) == -3
+    no_sel = list(base); no_sel[9] = None; no_sel[10] = 8192
+    assert lib.csa_sparse_attn_decode(*no_sel) == -5   # long list: workspace needed
+    assert lib.csa_sparse_attn_prefill(*no_sel) == -4  # ring schedule: list past 4224
+    bad = list(no_sel); bad[10] = (1 << 20) + 1
+    assert lib.csa_sparse_attn_decode(*bad) == -3
+    need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 8192, 128)
+    assert need >= 8 * ((8192 + 128 + 127) // 128) * 64 * 512 * 4

@@ -339,6 +339,8 @@ def test_hca_selection_bound():
     assert np.array_equal(sel, np.arange(4)) and e == oracle.EFLAG_TOPK_RANGE
     sel, e = oracle.deterministic_selection(126, 128, 4)
     assert sel.size == 0 and e == 0
+    sel, e = oracle.deterministic_selection(1279, 128, 0)   # k = 0: the window alone
+    assert sel.size == 0 and e == 0
     rng = np.random.default_rng(43)
     a, cd, wd = _build(rng, rows=(1,), ctx=(1100,), ratio=128, W=8, k=4)
     a["topk_idx"] = None
