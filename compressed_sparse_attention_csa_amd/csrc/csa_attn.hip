@@ -32,6 +32,7 @@
 // the B operand of the P*V product (the key order inside the MFMA is permuted
 // identically on both operands).  The rotated query stays in registers as the
 // B operand of S^T.
+#include <algorithm>
 #include <type_traits>
 
 #include "csa_common.h"
@@ -78,6 +79,7 @@ struct AttnArgs {
   float* part_o;     // [T][splits][H][D]
   float2* part_ml;   // [T][splits][H]
   int splits;
+  int ring_span;     // ring schedule with splits > 1: list entries per span
   int items_per_xcd;
   int32_t* err;
 };
@@ -86,6 +88,7 @@ __device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf,
 
 constexpr int kMaxSplit = 4224;  // longest key list of the ring schedule: window + k
 constexpr int kMaxDenseK = 1 << 20;   // bound on k without a selection array
+constexpr int kDecodeCUs = 256;       // MI355X compute units: the split-ring target
 constexpr uint32_t kWinBit = 0x80000000u;
 constexpr uint32_t kNoRow = 0xffffffffu;
 constexpr int kRing = 4;          // key tiles resident in LDS (in flight or in use)
@@ -185,9 +188,15 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   __shared__ int ovf_s[HT];
 
   // XCD-aware work mapping: consecutive rows land on one XCD.
+  // An item is one row, or with splits > 1 one span of ring_span entries of
+  // a row's key list (a long decode list): the span's FP32 partial goes to
+  // the merge kernel.
   const int L = blockIdx.x;
-  const int t = (L & 7) * a.items_per_xcd + (L >> 3);
+  const int item = (L & 7) * a.items_per_xcd + (L >> 3);
+  const int t = item / a.splits;
+  const int split = item - t * a.splits;
   if (t >= a.num_tokens) return;
+  const int i0 = split * a.ring_span;   // first list entry of this item
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -213,7 +222,7 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   const int p = a.positions[t];
   // (no selection array: the compressed set is every visible row, 0 .. n_vis-1)
   const int32_t* topk_row = a.topk ? a.topk + static_cast<long long>(t) * a.k : nullptr;
-  const int i_spec0 = tid - a.window, i_spec1 = kRingThreads + tid - a.window;
+  const int i_spec0 = i0 + tid - a.window, i_spec1 = i0 + kRingThreads + tid - a.window;
   const int c_spec0 = (topk_row && i_spec0 >= 0 && i_spec0 < a.k) ? topk_row[i_spec0] : -1;
   const int c_spec1 = (topk_row && i_spec1 >= 0 && i_spec1 < a.k) ? topk_row[i_spec1] : -1;
   v4i qraw[KS];
@@ -236,7 +245,8 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     w_lo = max(0, p - a.window + 1);
     w_len = p - w_lo + 1;
   }
-  const int n_my = (b >= 0) ? (w_len + a.k) : 0;
+  const int list_len = (b >= 0) ? (w_len + a.k) : 0;
+  const int n_my = a.splits == 1 ? list_len : max(0, min(list_len, i0 + a.ring_span) - i0);
   // LDS-only barriers in the prologue: a __syncthreads() would also wait for
   // the query loads still streaming in from HBM
   lds_barrier();   // err_s is cleared
@@ -248,11 +258,12 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   {
     int ebits = 0;
     const bool spec_ok = w_len == a.window;
-    if (!topk_row && a.k > 0 && b >= 0 && nv > a.k && tid == 0) ebits |= CSA_EFLAG_TOPK_RANGE;
+    if (!topk_row && a.k > 0 && b >= 0 && nv > a.k && split == 0 && tid == 0)
+      ebits |= CSA_EFLAG_TOPK_RANGE;
     for (int j0 = 0, r = 0; j0 < n_my; j0 += kRingThreads, ++r) {
-      const int i = j0 + tid;
+      const int i = i0 + j0 + tid;   // list entry
       uint32_t rr = kNoRow;
-      if (i >= n_my) {
+      if (j0 + tid >= n_my) {
         // past the list: nothing to resolve
       } else if (i < w_len) {
         const long long r = page_row(a.win_bt + static_cast<long long>(b) * a.max_win_blocks,
@@ -486,13 +497,18 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
         m_ref = m_seen;
         continue;
       }
-      // per-head normalisation, handed to the P*V waves
+      // per-head normalisation, handed to the P*V waves; a span of a split
+      // list publishes its (max, sum) for the merge instead
       if (hv && grp == 0) {
-        const float M = fmaxf(m_ref, sink2);
-        const float corr = (m_ref == neg_inf) ? 0.0f : exp2f(m_ref - M);
-        const float Z = l_run * corr + exp2f(sink2 - M);
-        f_s[h] = corr / Z;
-        if (a.lse) a.lse[static_cast<long long>(t) * a.H + h] = (M + log2f(Z)) * kLn2;
+        if (a.splits > 1) {
+          a.part_ml[static_cast<long long>(item) * a.H + h] = make_float2(m_ref, l_run);
+        } else {
+          const float M = fmaxf(m_ref, sink2);
+          const float corr = (m_ref == neg_inf) ? 0.0f : exp2f(m_ref - M);
+          const float Z = l_run * corr + exp2f(sink2 - M);
+          f_s[h] = corr / Z;
+          if (a.lse) a.lse[static_cast<long long>(t) * a.H + h] = (M + log2f(Z)) * kLn2;
+        }
       }
       __syncthreads();   // f_s is complete
       break;
@@ -559,6 +575,19 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
       __syncthreads();
       if (again) continue;
       __syncthreads();   // f_s is complete
+      if (a.splits > 1) {
+        // the span's partial: O relative to its own softmax reference
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          const int hh = ht * 16 + col;
+          if (hh >= a.H) continue;
+          float* prow = a.part_o + (static_cast<long long>(item) * a.H + hh) * D + d0;
+#pragma unroll
+          for (int dt = 0; dt < DTW; ++dt)
+            *reinterpret_cast<v4f*>(prow + dt * 16 + grp * 4) = o_acc[dt][ht];
+        }
+        break;
+      }
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         const int hh = ht * 16 + col;
@@ -582,7 +611,7 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   }
 
   if (tid == 0 && err_s) flag_error(a.err, err_s);
-  if (b < 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
+  if (b < 0 && split == 0 && tid == 0) flag_error(a.err, CSA_EFLAG_META);
 }
 
 // ---------------------------------------------------------------------------
@@ -997,12 +1026,25 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
 struct SplitPlan {
   bool ring;
   int splits;
+  int ring_span;
 };
+
+// Decode lists at least this long walk spans through the ring kernel (all
+// 64 heads per work-group, tiles pipelined through the LDS ring) instead of
+// one 16-head work-group per 128 entries, whose setup latency repeats for
+// every span and every head group.
+constexpr int kRingSplitMin = 1024;
 
 SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   const int lmax = max(1, window + k);
-  if (prefill || T >= 256) return SplitPlan{true, 1};
-  return SplitPlan{false, (lmax + kSpan - 1) / kSpan};
+  if (prefill || T >= 256) return SplitPlan{true, 1, lmax};
+  if (lmax < kRingSplitMin) return SplitPlan{false, (lmax + kSpan - 1) / kSpan, 0};
+  // spans sized so that the row x span items fill the CUs about once
+  long long span = (static_cast<long long>(lmax) * T + kDecodeCUs - 1) / kDecodeCUs;
+  span = std::max<long long>(span, 4 * kTile);
+  span = std::min<long long>((span + kTile - 1) / kTile * kTile, kMaxSplit - kMaxSplit % kTile);
+  const int sp = static_cast<int>(span);
+  return SplitPlan{true, (lmax + sp - 1) / sp, sp};
 }
 
 // Decode workspace: the FP32 partials [T][splits][H][D] and their (max, sum)
@@ -1069,7 +1111,7 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
     return CSA_ERR_UNSUPPORTED;
   const SplitPlan plan = plan_splits(num_tokens, k, window, prefill);
   // the ring schedule holds a row's whole key list in LDS
-  if (plan.ring && window + k > kMaxSplit) return CSA_ERR_UNSUPPORTED;
+  if (plan.ring && plan.splits == 1 && window + k > kMaxSplit) return CSA_ERR_UNSUPPORTED;
   AttnArgs a{};
   a.q = q;
   a.rope_cos = rope_cos;
@@ -1098,6 +1140,7 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   a.out = out;
   a.lse = lse;
   a.splits = plan.splits;
+  a.ring_span = plan.ring_span;
   a.err = err;
   if (plan.splits > 1) {
     const size_t need = attn_ws_bytes(num_tokens, plan.splits, H, D);
