@@ -936,14 +936,15 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
 
 // Combine the span partials of each (row, head) with the sink: one wave per
 // (row, head).  Lane l owns channels [8l, 8l + 8) of every partial (D = 512;
-// D / 64 channels in general).  Lanes stride over the spans for the running
-// max and the denominator (any number of spans); each chunk of eight
-// partials is loaded together with its spans' (max, sum) pairs, and the
-// first chunk goes out with the pairs of the max pass, so a row of at most
-// 64 spans costs one memory latency before its sums.
+// D / 64 channels in general).  With at most 64 spans (MANY false) lane s
+// holds span s's (max, sum) and the weights travel by lane shuffles; with
+// more, lanes stride over the spans for the max and the denominator and each
+// chunk of eight partials loads its spans' pairs too.  The first chunk goes
+// out with the pairs of the max pass, so a row of at most 64 spans costs one
+// memory latency before its sums.
 constexpr int kMergeChunk = 8;
 
-template <int D>
+template <int D, bool MANY>
 __global__ void __launch_bounds__(64) attn_merge_kernel(
     const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const float* __restrict__ sink, int splits, int H, int num_tokens,
@@ -968,7 +969,7 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
     for (int u = 0; u < kMergeChunk; ++u) {
       const int sp = s0 + u;
       const long long sl = tbase + (sp < splits ? sp : 0);
-      cml[u] = sp < splits ? part_ml[sl * H + h] : make_float2(neg_inf, 0.0f);
+      if constexpr (MANY) cml[u] = sp < splits ? part_ml[sl * H + h] : make_float2(neg_inf, 0.0f);
       const float* po = part_o + (sl * H + h) * D + lane * CPL;
       if constexpr (CPL >= 4) {
 #pragma unroll
@@ -989,14 +990,18 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
   // running max and denominator over the spans, with the sink
   const float sink2 = sink[h] * kLog2e;
   float M = ml.x;
-  for (int s = lane + 64; s < splits; s += 64) M = fmaxf(M, part_ml[(tbase + s) * H + h].x);
+  if constexpr (MANY)
+    for (int s = lane + 64; s < splits; s += 64) M = fmaxf(M, part_ml[(tbase + s) * H + h].x);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   M = fmaxf(M, sink2);
-  float z = ml.x == neg_inf ? 0.0f : ml.y * exp2f(ml.x - M);
-  for (int s = lane + 64; s < splits; s += 64) {
-    const float2 m2 = part_ml[(tbase + s) * H + h];
-    z += m2.x == neg_inf ? 0.0f : m2.y * exp2f(m2.x - M);
+  const float w_l = ml.x == neg_inf ? 0.0f : exp2f(ml.x - M);   // lane's span weight
+  float z = ml.y * w_l;
+  if constexpr (MANY) {
+    for (int s = lane + 64; s < splits; s += 64) {
+      const float2 m2 = part_ml[(tbase + s) * H + h];
+      z += m2.x == neg_inf ? 0.0f : m2.y * exp2f(m2.x - M);
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
@@ -1005,8 +1010,10 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
     if (s0 > 0) load_chunk(s0);
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
+      float w;
+      if constexpr (MANY) w = cml[u].x == neg_inf ? 0.0f : exp2f(cml[u].x - M);
+      else w = __shfl(w_l, (s0 + u) & 63, 64);
       if (s0 + u < splits) {
-        const float w = cml[u].x == neg_inf ? 0.0f : exp2f(cml[u].x - M);
 #pragma unroll
         for (int i = 0; i < CPL; ++i) acc[i] += chunk[u][i] * w;
       }
@@ -1070,8 +1077,14 @@ int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
   if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   if (a.splits > 1) {
     const long long mgrid = static_cast<long long>(a.num_tokens) * a.H;
-    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3(static_cast<unsigned>(mgrid)), dim3(64), 0, st,
-                       a.part_o, a.part_ml, a.sink, a.splits, a.H, a.num_tokens, a.out, a.lse);
+    if (a.splits <= 64)
+      hipLaunchKernelGGL((attn_merge_kernel<D, false>), dim3(static_cast<unsigned>(mgrid)),
+                         dim3(64), 0, st, a.part_o, a.part_ml, a.sink, a.splits, a.H,
+                         a.num_tokens, a.out, a.lse);
+    else
+      hipLaunchKernelGGL((attn_merge_kernel<D, true>), dim3(static_cast<unsigned>(mgrid)),
+                         dim3(64), 0, st, a.part_o, a.part_ml, a.sink, a.splits, a.H,
+                         a.num_tokens, a.out, a.lse);
     if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   }
   return CSA_OK;

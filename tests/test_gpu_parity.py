@@ -177,3 +177,30 @@ def test_hca_prefill_and_bound():
                                         cfg.T, k=k)
         assert oe == expect and int(step.err.item()) == expect, (fn, k)
         H.check_attn(H.bf16_to_f64(step.out), oo, step.lse.cpu().numpy(), ol, f"hca {fn} k{k}")
+
+
+def test_hca_many_spans():
+    """Two rows over a 1,048,576-token HCA context: 8,320 keys per row in 65
+    spans, past the 64 a merge wave holds one per lane."""
+    from synthetic.configs import CsaConfig
+    csa = _lib()
+    ctx = 1 << 20
+    cfg = CsaConfig(name="hca_many", description="HCA rows with more than 64 spans",
+                    rows_per_request=(2,), positions=((ctx - 2, ctx - 1),), H=16, D=128, R=32,
+                    Hi=4, Di=32, W=128, ratio=128, k=8192, context=ctx, mode="hca")
+    x = synthetic.make_inputs(cfg, seed=17).t
+    step = csa.step_for_config(cfg, x)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    half = cfg.R // 2
+    rc = np.zeros((cfg.T, half), np.float32)
+    rs = np.zeros_like(rc)
+    oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["position_ids"], cfg.T, rc, rs)
+    oo, ol, oe = oracle.sparse_attn(x["q"], rc, rs, cfg.rope_offset, x["cmp_kv"],
+                                    x["cmp_block_table"], None, cfg.ratio, x["win_kv"],
+                                    x["win_block_table"], cfg.W, x["attn_sink"],
+                                    cfg.softmax_scale, x["query_start_loc"], x["positions"],
+                                    cfg.T, k=cfg.k)
+    assert oe == 0
+    H.check_attn(H.bf16_to_f64(step.out), oo, step.lse.cpu().numpy(), ol, cfg.name)
