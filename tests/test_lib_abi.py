@@ -120,5 +120,7 @@ def test_attention_selection_bounds(lib):
     assert lib.csa_sparse_attn_prefill(*no_sel) == -4  # ring schedule: list past 4224
     bad = list(no_sel); bad[10] = (1 << 20) + 1
     assert lib.csa_sparse_attn_decode(*bad) == -3
+    # whole span partials (O and its (max, sum) per head), at least two spans
     need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 8192, 128)
-    assert need >= 8 * ((8192 + 128 + 127) // 128) * 64 * 512 * 4
+    per_span = 8 * 64 * (512 + 2) * 4
+    assert need % per_span == 0 and need // per_span >= 2
