@@ -212,12 +212,14 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
 
   if (tid == 0) err_s = 0;
 
-  // metadata loads first, then the query, the rope row and the sink (vector
-  // memory returns in order: these complete during the row resolution).  The
-  // selected indices of this thread's first two list entries are fetched
-  // with them on the guess that the row's window is full (every row but a
-  // request's first window - 1 tokens), which takes a dependent round trip
-  // off the resolution.
+  // metadata loads first, then the rope row and the sink.  The selected
+  // indices of this thread's first two list entries are fetched with them on
+  // the guess that the row's window is full (every row but a request's first
+  // window - 1 tokens), which takes a dependent round trip off the
+  // resolution.  The query (64 KiB per row, usually cold) is loaded only
+  // after the resolution and the first two tile gathers: vector memory
+  // counts complete in order, so loaded here it would hold up every wait of
+  // the resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
   // (no selection array: the compressed set is every visible row, 0 .. n_vis-1)
@@ -225,13 +227,6 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   const int i_spec0 = i0 + tid - a.window, i_spec1 = i0 + kRingThreads + tid - a.window;
   const int c_spec0 = (topk_row && i_spec0 >= 0 && i_spec0 < a.k) ? topk_row[i_spec0] : -1;
   const int c_spec1 = (topk_row && i_spec1 >= 0 && i_spec1 < a.k) ? topk_row[i_spec1] : -1;
-  v4i qraw[KS];
-  {
-    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qraw[ks] = hv ? *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8) : v4i{0, 0, 0, 0};
-  }
   float rcv = 0.0f, rsv = 0.0f;
   if (tid < a.half_rope) {
     rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + tid];
@@ -295,32 +290,6 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     rope_s[256 + tid] = rsv;
   }
   lds_barrier();  // row_s and rope_s ready
-
-  // ---- query fragments (B operand of S^T) of the S waves: lane (head col,
-  //      group grp) holds channels ks*32 + grp*8 .. +8, rotated where they
-  //      fall in the rope span
-  v8bf qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    v4i raw = qraw[ks];
-    const int r0 = ks * 32 + grp * 8 - a.rope_offset;
-    if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
-      uint16_t e[8];
-      *reinterpret_cast<v4i*>(e) = raw;
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) {
-        const int rr = r0 + 2 * pr;
-        if (rr >= 0 && rr < 2 * a.half_rope) {
-          const float c = rope_s[rr >> 1], sn = rope_s[256 + (rr >> 1)];
-          const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
-          e[2 * pr] = f32_to_bf16(x * c - y * sn);
-          e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
-        }
-      }
-      raw = *reinterpret_cast<v4i*>(e);
-    }
-    qf[ks] = as_v8bf(raw);
-  }
 
   // ---- direct-to-LDS gather of one 32-row tile into ring slot tt % kRing
   //      (a compile-time constant).  Lane l of a wave-wide load moves chunk
@@ -397,12 +366,46 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     if (ntiles > 1) issue(1, std::integral_constant<int, 1>{});
   };
 
+  // first two tiles of the first pass, then the query behind them
+  prime();
+  v4i qraw[KS];
+  {
+    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[ks] = hv ? *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8) : v4i{0, 0, 0, 0};
+  }
+
+  // ---- query fragments (B operand of S^T) of the S waves: lane (head col,
+  //      group grp) holds channels ks*32 + grp*8 .. +8, rotated where they
+  //      fall in the rope span
+  v8bf qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    v4i raw = qraw[ks];
+    const int r0 = ks * 32 + grp * 8 - a.rope_offset;
+    if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const int rr = r0 + 2 * pr;
+        if (rr >= 0 && rr < 2 * a.half_rope) {
+          const float c = rope_s[rr >> 1], sn = rope_s[256 + (rr >> 1)];
+          const uint32_t e = static_cast<uint32_t>(raw[pr]);
+          const float x = bf16_to_f32(e & 0xffffu), y = bf16_to_f32(e >> 16);
+          raw[pr] = static_cast<int>(pack_bf16x2(x * c - y * sn, x * sn + y * c));
+        }
+      }
+    }
+    qf[ks] = as_v8bf(raw);
+  }
+
+
   if (s_wave) {
     // the softmax waves are the critical path of every step: their
     // instructions go first when both waves of a SIMD are ready
     __builtin_amdgcn_s_setprio(2);
     for (int pass = 0; pass < 2; ++pass) {
-      prime();
+      if (pass > 0) prime();
       bool ovf = false;
       l_run = 0.0f;
       // S^T tile: rows = 32 keys (two 16-row M tiles), columns = this wave's
@@ -522,7 +525,7 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     const int d0 = (wave - HT) * DW;
     v4f o_acc[DTW][HT];
     for (int pass = 0; pass < 2; ++pass) {
-      prime();
+      if (pass > 0) prime();
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt)
 #pragma unroll
@@ -599,10 +602,8 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
           // o_acc[dt][ht][r] is channel d0 + dt*16 + grp*4 + r of head hh
           const int d = dt * 16 + grp * 4;
           uint2 w;
-          w.x = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][0] * f)) |
-                (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][1] * f)) << 16);
-          w.y = static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][2] * f)) |
-                (static_cast<uint32_t>(f32_to_bf16(o_acc[dt][ht][3] * f)) << 16);
+          w.x = pack_bf16x2(o_acc[dt][ht][0] * f, o_acc[dt][ht][1] * f);
+          w.y = pack_bf16x2(o_acc[dt][ht][2] * f, o_acc[dt][ht][3] * f);
           *reinterpret_cast<uint2*>(orow + d) = w;
         }
       }
@@ -776,19 +777,16 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
     v4i raw = qraw[ks];
     const int r0 = ks * 32 + grp * 8 - a.rope_offset;
     if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
-      uint16_t e[8];
-      *reinterpret_cast<v4i*>(e) = raw;
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) {
         const int rr = r0 + 2 * pr;
         if (rr >= 0 && rr < 2 * a.half_rope) {
           const float c = rope_s[rr >> 1], sn = rope_s[kAttnThreads + (rr >> 1)];
-          const float x = bf16_to_f32(e[2 * pr]), y = bf16_to_f32(e[2 * pr + 1]);
-          e[2 * pr] = f32_to_bf16(x * c - y * sn);
-          e[2 * pr + 1] = f32_to_bf16(x * sn + y * c);
+          const uint32_t e = static_cast<uint32_t>(raw[pr]);
+          const float x = bf16_to_f32(e & 0xffffu), y = bf16_to_f32(e >> 16);
+          raw[pr] = static_cast<int>(pack_bf16x2(x * c - y * sn, x * sn + y * c));
         }
       }
-      raw = *reinterpret_cast<v4i*>(e);
     }
     qf[ks] = as_v8bf(raw);
   }
@@ -839,17 +837,17 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
     m_w = tmax;   // finite: the wave has at least one valid row
     float psum = 0.0f;
-    uint16_t pb[8];
+    v4i pw;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float pj = exp2f(lg[jj] - m_w);
-      psum += pj;
-      pb[jj] = f32_to_bf16(pj);
+    for (int jj = 0; jj < 8; jj += 2) {
+      const float p0 = exp2f(lg[jj] - m_w), p1 = exp2f(lg[jj + 1] - m_w);
+      psum += p0 + p1;
+      pw[jj >> 1] = static_cast<int>(pack_bf16x2(p0, p1));
     }
     psum += shfl_xor_f(psum, 16);
     psum += shfl_xor_f(psum, 32);
     l_w = psum;
-    const v8bf pf = as_v8bf(*reinterpret_cast<v4i*>(pb));
+    const v8bf pf = as_v8bf(pw);
     const int e_src = (lane & 15) >> 2, q_src = lane & 3;
     const uint8_t* v0p = tile + row_off(grp + 4 * e_src) + q_src * 8;
     const uint8_t* v1p = tile + row_off(16 + grp + 4 * e_src) + q_src * 8;
@@ -923,8 +921,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
         if (a.splits == 1) {
           acc *= scale;
           uint2 pk;
-          pk.x = static_cast<uint32_t>(f32_to_bf16(acc[0])) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-          pk.y = static_cast<uint32_t>(f32_to_bf16(acc[2])) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+          pk.x = pack_bf16x2(acc[0], acc[1]);
+          pk.y = pack_bf16x2(acc[2], acc[3]);
           *reinterpret_cast<uint2*>(a.out + (static_cast<long long>(t) * a.H + head) * D + c) = pk;
         } else {
           *reinterpret_cast<v4f*>(a.part_o + (static_cast<long long>(ts) * a.H + head) * D + c) = acc;
@@ -1021,8 +1019,14 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
   }
   const float f = 1.0f / z;
   uint16_t* orow = out + (static_cast<long long>(t) * H + h) * D + lane * CPL;
+  if constexpr (CPL % 2 == 0) {
+    uint32_t* o32 = reinterpret_cast<uint32_t*>(orow);
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) orow[i] = f32_to_bf16(acc[i] * f);
+    for (int i = 0; i < CPL; i += 2) o32[i >> 1] = pack_bf16x2(acc[i] * f, acc[i + 1] * f);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) orow[i] = f32_to_bf16(acc[i] * f);
+  }
   if (lse && lane == 0) lse[static_cast<long long>(t) * H + h] = (M + log2f(z)) * kLn2;
 }
 

@@ -22,20 +22,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
 // Two floats -> packed bf16 pair (lo in bits 0-15) with gfx950's conversion
 // instruction, round to nearest even.
 typedef float v2f_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{lo, hi}, v2bf_t));
+}
+
+// float -> bf16 bits with the same instruction, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Compressed slots visible to a query at absolute position p: c < (p+1)/ratio.
