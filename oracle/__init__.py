@@ -13,4 +13,5 @@ from .csa_oracle import (  # noqa: F401
     bf16_to_f64, visible_count, window_positions, owner_request,
     rotate_adjacent_pairs, materialize_rope_rows, index_scores, topk,
     kv_rows_for_query, deterministic_selection, sparse_attn,
+    candidate_blocks, candidate_positions, index_scores_in_candidates, topk_in_candidates,
 )

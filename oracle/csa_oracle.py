@@ -250,13 +250,156 @@ def topk(scores, positions, ratio, num_tokens, k):
         if m == 0:
             continue
         s = scores[t, :n]
-        nan = np.isnan(s)
-        primary = np.where(nan, np.inf, -s)          # ascending sort = descending score
-        order = np.lexsort((np.arange(n), nan, primary))
-        chosen = np.sort(order[:m])
+        chosen = _best_ascending(s, m)
         idx[t, :m] = chosen
         val[t, :m] = s[chosen]
     return idx, val, err
+
+
+def _best_ascending(s, m):
+    """Indices of the m best entries of s -- score descending, the lower
+    index first among equal scores, NaN below everything -- in ascending
+    index order."""
+    s = np.asarray(s, dtype=np.float64)
+    nan = np.isnan(s)
+    primary = np.where(nan, np.inf, -s)          # ascending sort = descending score
+    order = np.lexsort((np.arange(len(s)), nan, primary))
+    return np.sort(order[:m])
+
+
+# ----------------------------------------------------------------------------
+# Hierarchical selection: the full layer's candidate blocks, then a reindex
+# layer's selection inside them
+# ----------------------------------------------------------------------------
+
+def candidate_blocks(scores, positions, ratio, num_tokens, block, kb):
+    """The full layer's candidate mask ([V41] "Decode composition": the
+    hierarchical indexer first picks 2,048 blocks of eight compressed
+    positions; later reindex layers select only inside that mask, which stays
+    in request-local compressed-position space).
+
+    Reading (the pages name the block selection but not the block score):
+    block j of row t covers positions j*block .. j*block + block - 1, and its
+    score is the largest score among its visible positions (c < n_vis, the
+    span cut to the score row width as in ``topk``).  A block with no visible
+    position is not eligible.  The min(kb, eligible) best blocks -- block score
+    descending, lower block id first, NaN below everything -- are returned in
+    ascending block order, padded with -1.
+
+    Returns (blocks int32 [num_tokens, kb], err)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    nt = int(num_tokens)
+    out = np.full((nt, int(kb)), -1, dtype=np.int32)
+    err = 0
+    width = scores.shape[1]
+    for t in range(nt):
+        n = visible_count(positions[t], ratio)
+        if n > width:
+            err |= EFLAG_POS_RANGE
+            n = width
+        nb = -(-n // block)
+        bs = np.empty(nb, dtype=np.float64)
+        for j in range(nb):
+            part = scores[t, j * block:min(n, (j + 1) * block)]
+            finite = part[~np.isnan(part)]
+            bs[j] = finite.max() if finite.size else np.nan
+        m = min(int(kb), nb)
+        if m:
+            out[t, :m] = _best_ascending(bs, m)
+    return out, err
+
+
+def candidate_positions(cand_row, block, n_vis):
+    """Positions of one row's candidate slots: slot i is position
+    cand_row[i // block] * block + i % block.  Returns (pos int64 [kb*block],
+    eligible bool) -- a slot is eligible when its block entry is not -1 and
+    its position is visible (c < n_vis)."""
+    cand_row = np.asarray(cand_row, dtype=np.int64)
+    slots = np.arange(len(cand_row) * block)
+    blk = cand_row[slots // block]
+    pos = blk * block + slots % block
+    eligible = (blk >= 0) & (pos < n_vis)
+    return np.where(blk >= 0, pos, -1), eligible
+
+
+def index_scores_in_candidates(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table,
+                               query_start_loc, positions, num_tokens, ratio,
+                               cand_blocks, block):
+    """A reindex layer's scores: the ``index_scores`` formula with the layer's
+    own index query, evaluated only at the positions of row t's candidate
+    blocks ([V41] "Decode composition": reindex layers compute a new index
+    query and read the supplied candidate mask).
+
+    Slot i of row t is position cand_blocks[t, i // block] * block + i % block.
+    A slot that is not eligible (block -1, or position not visible) scores
+    -inf.  A candidate block past the visible span is a selection the row may
+    not see: TOPK_RANGE.  Page / block-id problems flag as in
+    ``index_scores``; a row no request owns flags META and scores -inf.
+
+    Returns (scores float64 [num_tokens, kb*block], err)."""
+    qsl = np.asarray(query_start_loc)
+    cand_blocks = np.asarray(cand_blocks)
+    num_blocks = idx_kv.shape[0]
+    Di = idx_kv.shape[2]
+    keys_flat = idx_kv.reshape(num_blocks * PAGE, Di)
+    scales_flat = np.asarray(idx_scale, dtype=np.float64).reshape(-1)
+    nslot = cand_blocks.shape[1] * block
+    scores = np.full((int(num_tokens), nslot), -np.inf, dtype=np.float64)
+    err = 0
+    for t in range(int(num_tokens)):
+        b = owner_request(t, qsl)
+        if b < 0:
+            err |= EFLAG_META
+            continue
+        n = visible_count(positions[t], ratio)
+        row = cand_blocks[t]
+        if np.any(row[row >= 0].astype(np.int64) * block >= n):
+            err |= EFLAG_TOPK_RANGE
+        pos, eligible = candidate_positions(row, block, n)
+        sl = np.nonzero(eligible)[0]
+        if sl.size == 0:
+            continue
+        rows, ok = _physical_rows(block_table[b], num_blocks, pos[sl])
+        if not ok.all():
+            err |= EFLAG_BLOCK_RANGE
+        q = np.asarray(q_idx[t], dtype=np.float64)
+        qs = np.asarray(q_scale[t], dtype=np.float64)
+        w = np.asarray(head_w[t], dtype=np.float64)
+        k8 = keys_flat[rows].astype(np.float64)
+        ks = scales_flat[rows]
+        dots = q @ k8.T
+        s = (w[:, None] * np.maximum(qs[:, None] * ks[None, :] * dots, 0.0)).sum(axis=0)
+        s[~ok] = -np.inf
+        scores[t, sl] = s
+    return scores, err
+
+
+def topk_in_candidates(cand_scores, cand_blocks, block, positions, ratio, num_tokens, k):
+    """A reindex layer's final selection: per active row, the k best eligible
+    candidate slots, reported as compressed positions ([V41] "Decode
+    composition": the final 512 positions come only from inside the candidate
+    mask).  Same order and output contract as ``topk``: score descending, the
+    lower position first, NaN below everything; m = min(k, eligible slots);
+    the chosen positions ascending, then -1 (value -inf).
+
+    Returns (idx int32 [num_tokens, k], val float64 [num_tokens, k], err)."""
+    cand_scores = np.asarray(cand_scores, dtype=np.float64)
+    cand_blocks = np.asarray(cand_blocks)
+    nt = int(num_tokens)
+    idx = np.full((nt, int(k)), -1, dtype=np.int32)
+    val = np.full((nt, int(k)), -np.inf, dtype=np.float64)
+    for t in range(nt):
+        n = visible_count(positions[t], ratio)
+        pos, eligible = candidate_positions(cand_blocks[t], block, n)
+        sl = np.nonzero(eligible)[0]
+        m = min(int(k), sl.size)
+        if m == 0:
+            continue
+        by_pos = sl[np.argsort(pos[sl], kind="stable")]
+        chosen = by_pos[_best_ascending(cand_scores[t, by_pos], m)]
+        idx[t, :m] = pos[chosen]
+        val[t, :m] = cand_scores[t, chosen]
+    return idx, val, 0
 
 
 # ----------------------------------------------------------------------------
