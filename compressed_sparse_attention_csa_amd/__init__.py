@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     CsaError, EXPORTS, LIB_PATH, load,
     csa_status_string, csa_materialize_rope_rows, csa_index_score, csa_topk,
     csa_topk_workspace_bytes, csa_sparse_attn_decode, csa_sparse_attn_prefill,
-    csa_sparse_attn_workspace_bytes,
+    csa_sparse_attn_workspace_bytes, csa_candidate_blocks, csa_candidate_blocks_workspace_bytes,
+    csa_index_score_candidates, csa_topk_candidates, csa_topk_candidates_workspace_bytes,
 )
 from .runner import CsaStep, step_for_config  # noqa: F401

@@ -42,6 +42,15 @@ _SIGS = {
                                               _I32, _P, _I32, _P, _I32, _I32, _P, _F32, _P, _P,
                                               _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P,
                                               _P]),
+    "csa_candidate_blocks_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32]),
+    "csa_candidate_blocks": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _P, _P,
+                                            _SZ, _P, _P]),
+    "csa_index_score_candidates": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _P,
+                                                  _I32, _I32, _I32, _I32, _I32, _I32, _P, _I32,
+                                                  _I32, _P, _I64, _P, _P, _P]),
+    "csa_topk_candidates_workspace_bytes": (_SZ, [_I32, _I64, _I32]),
+    "csa_topk_candidates": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _I32, _I32, _P,
+                                           _P, _P, _SZ, _P, _P]),
 }
 _SIGS["csa_sparse_attn_prefill"] = _SIGS["csa_sparse_attn_decode"]
 
@@ -146,6 +155,59 @@ def csa_topk(scores, positions, ratio, num_tokens, k, topk_idx, topk_val=None, w
                          int(num_tokens), int(k), _ptr(topk_idx), _ptr(topk_val),
                          _ptr(workspace), wsb, _ptr(err), _stream(stream))
     _check(st, "csa_topk")
+
+
+def csa_candidate_blocks_workspace_bytes(T: int, score_stride: int, block: int, kb: int) -> int:
+    return int(load().csa_candidate_blocks_workspace_bytes(T, score_stride, block, kb))
+
+
+def csa_candidate_blocks(scores, positions, ratio, num_tokens, block, cand_blocks, workspace,
+                         err=None, stream=None) -> None:
+    _need(scores, (torch.float32,), 2, "scores")
+    _need(cand_blocks, (torch.int32,), 2, "cand_blocks")
+    T = scores.shape[0]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().csa_candidate_blocks(_ptr(scores), scores.shape[1], _ptr(positions), int(ratio),
+                                     T, int(num_tokens), int(block), cand_blocks.shape[1],
+                                     _ptr(cand_blocks), _ptr(workspace), wsb, _ptr(err),
+                                     _stream(stream))
+    _check(st, "csa_candidate_blocks")
+
+
+def csa_index_score_candidates(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table,
+                               query_start_loc, positions, num_tokens, ratio, cand_blocks,
+                               block, cand_scores, cand_count, err=None, stream=None) -> None:
+    _need(q_idx, (torch.int8,), 3, "q_idx")
+    _need(idx_kv, (torch.int8,), 3, "idx_kv")
+    _need(cand_blocks, (torch.int32,), 2, "cand_blocks")
+    _need(cand_scores, (torch.float32,), 2, "cand_scores")
+    _need(cand_count, (torch.int32,), 1, "cand_count")
+    T, Hi, Di = q_idx.shape
+    st = load().csa_index_score_candidates(
+        _ptr(q_idx), _ptr(q_scale), _ptr(head_w), _ptr(idx_kv), _ptr(idx_scale),
+        idx_kv.shape[0], _ptr(block_table), block_table.shape[1], _ptr(query_start_loc),
+        _ptr(positions), query_start_loc.shape[0] - 1, T, int(num_tokens), Hi, Di, int(ratio),
+        _ptr(cand_blocks), cand_blocks.shape[1], int(block), _ptr(cand_scores),
+        cand_scores.shape[1], _ptr(cand_count), _ptr(err), _stream(stream))
+    _check(st, "csa_index_score_candidates")
+
+
+def csa_topk_candidates_workspace_bytes(T: int, cand_stride: int, k: int) -> int:
+    return int(load().csa_topk_candidates_workspace_bytes(T, cand_stride, k))
+
+
+def csa_topk_candidates(cand_scores, cand_count, cand_blocks, block, num_tokens, k, topk_idx,
+                        topk_val=None, workspace=None, err=None, stream=None) -> None:
+    _need(cand_scores, (torch.float32,), 2, "cand_scores")
+    _need(cand_blocks, (torch.int32,), 2, "cand_blocks")
+    _need(topk_idx, (torch.int32,), 2, "topk_idx")
+    T = cand_scores.shape[0]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().csa_topk_candidates(_ptr(cand_scores), cand_scores.shape[1], _ptr(cand_count),
+                                    _ptr(cand_blocks), cand_blocks.shape[1], int(block), T,
+                                    int(num_tokens), int(k), _ptr(topk_idx), _ptr(topk_val),
+                                    _ptr(workspace), wsb, _ptr(err), _stream(stream))
+    _check(st, "csa_topk_candidates")
 
 
 def csa_sparse_attn_workspace_bytes(T: int, H: int, D: int, k: int, window: int) -> int:

@@ -426,6 +426,179 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   }
 }
 
+// ---------------------------------------------------------------------------
+// Reindex scoring: the same score, evaluated only at the slots of each row's
+// candidate mask (pypto-lib "DeepSeek V4.1 Flash", section "Decode
+// composition": reindex layers score with their own index query inside the
+// full layer's candidate blocks).  Slot s of row t is position
+// cand[t][s / block] * block + s % block.  A work-group scores 256 slots of
+// one row, 64 per wave, as the 32x32x32 INT8 MFMA tiles and biased-
+// accumulator epilogue of index_score_kernel in the same order, so a slot's
+// score is bit-identical to the full scorer's at that position.  Keys are
+// gathered straight into operand registers (each lane 16 bytes of one key).
+constexpr int kCandSlots = 256;   // slots per work-group
+
+template <int KS>
+__global__ void __launch_bounds__(kThreads) index_cand_kernel(
+    const int8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
+    const float* __restrict__ head_w, const int8_t* __restrict__ idx_kv,
+    const float* __restrict__ idx_scale, int num_blocks, const int32_t* __restrict__ bt,
+    int max_blocks, const int32_t* __restrict__ qsl, const int32_t* __restrict__ positions,
+    int B, int num_tokens, int Hi, int Di, int ratio, const int32_t* __restrict__ cand, int kb,
+    int block, float* __restrict__ out, long long ostride, int32_t* __restrict__ count,
+    int32_t* err) {
+  __shared__ long long base_s[kCandSlots];   // pool row of an entry's first slot, or -1
+  __shared__ int elig_s[kCandSlots];         // eligible leading slots of the entry
+  __shared__ int err_s;
+  const int t = blockIdx.y;
+  if (t >= num_tokens) return;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int nslot = kb * block;
+  const int s0 = blockIdx.x * kCandSlots;
+  const int e0 = s0 / block;                 // first mask entry of this work-group
+  const int ne = kCandSlots / block;         // entries it covers
+  if (tid == 0) err_s = 0;
+
+  // metadata, this work-group's mask entries (and the entry before them),
+  // then the query: nothing here depends on another load
+  const int qsl_v = qsl_lane_load(qsl, B);
+  const int p = positions[t];
+  const int32_t* crow = cand + static_cast<long long>(t) * kb;
+  const int my_e = e0 + tid;
+  const int cb = (tid < ne && my_e < kb) ? crow[my_e] : -1;
+  const int prev_cb = (s0 > 0) ? crow[e0 - 1] : -1;
+  v4i qa[2][KS];
+  float ww[2][16];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int h = mt * 32 + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = ks * 32 + half * 16;
+      qa[mt][ks] = (h < Hi && off < Di)
+                       ? *reinterpret_cast<const v4i*>(
+                             q_idx + (static_cast<long long>(t) * Hi + h) * Di + off)
+                       : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+      ww[mt][j] = (hh < Hi) ? head_w[static_cast<long long>(t) * Hi + hh] *
+                                  q_scale[static_cast<long long>(t) * Hi + hh] * 2097152.0f
+                            : 0.0f;
+    }
+  }
+  const int b = owner_from_lanes(qsl_v, qsl, B, t);
+  const int nv = (b >= 0) ? visible_count(p, ratio) : 0;
+
+  // ---- each mask entry: visibility, then its page through the block table
+  int ebits = 0;
+  if (tid < ne) {
+    long long base = -1;
+    int elig = 0;
+    if (cb >= 0 && my_e < kb) {
+      const long long c = static_cast<long long>(cb) * block;
+      if (c >= nv) {
+        if (b >= 0) ebits |= CSA_EFLAG_TOPK_RANGE;   // a candidate the row may not see
+      } else {
+        const long long r = page_row(bt + static_cast<long long>(b) * max_blocks, max_blocks,
+                                     num_blocks, static_cast<int>(c));
+        if (r >= 0) {
+          base = r;
+          elig = static_cast<int>(min(static_cast<long long>(block), nv - c));
+        } else {
+          ebits |= CSA_EFLAG_BLOCK_RANGE;
+        }
+      }
+    }
+    base_s[tid] = base;
+    elig_s[tid] = elig;
+  }
+  if (ebits) atomicOr(&err_s, ebits);
+  __syncthreads();
+
+  // ---- the row's eligible slots form a prefix when the mask ascends with
+  //      trailing -1 (as csa_candidate_blocks writes it); the work-group that
+  //      holds its end (with the slot before its range eligible) records it
+  if (tid == 0) {
+    const bool prev_full =
+        s0 == 0 || (b >= 0 && prev_cb >= 0 &&
+                    (static_cast<long long>(prev_cb) + 1) * block <= static_cast<long long>(nv));
+    if (prev_full && b >= 0) {
+      int c = -1;
+      for (int e = 0; e < ne; ++e) {
+        if (e0 + e >= kb || elig_s[e] < block) {
+          c = min(nslot, s0 + e * block + (e0 + e < kb ? elig_s[e] : 0));
+          break;
+        }
+      }
+      if (c >= 0 || s0 + kCandSlots >= nslot) count[t] = c >= 0 ? c : nslot;
+    } else if (b < 0 && s0 == 0) {
+      count[t] = 0;
+    }
+    if (err_s) flag_error(err, err_s);
+    if (b < 0 && s0 == 0) flag_error(err, CSA_EFLAG_META);
+  }
+
+  // ---- this wave's 64 slots: key of B-operand column kj, and (for the
+  //      epilogue) the slot of lane l
+  const int neg_bits = 0xff800000;
+  const float neg_inf = __int_as_float(neg_bits);
+  auto slot_row = [&](int sl, bool& ok) -> long long {
+    const int e = sl / block - e0;
+    const int o = sl - (e0 + e) * block;
+    ok = sl < nslot && e < ne && o < elig_s[e];
+    return ok ? base_s[e] + o : 0;
+  };
+  v4i bk[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    bool ok;
+    const long long r = slot_row(s0 + wave * 64 + nt * 32 + col, ok);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = ks * 32 + half * 16;
+      bk[nt][ks] = (ok && off < Di)
+                       ? *reinterpret_cast<const v4i*>(idx_kv + r * Di + off)
+                       : v4i{0, 0, 0, 0};
+    }
+  }
+  bool my_ok;
+  const int my_slot = s0 + wave * 64 + lane;
+  const long long my_row = slot_row(my_slot, my_ok);
+  const float my_ks = my_ok ? idx_scale[my_row] : 0.0f;
+
+  constexpr int kBias = 0x40800000;
+  constexpr v16i kBiasV = {kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
+                           kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias};
+  float x[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    const int nt = pt >> 1, mt = pt & 1;
+    v16i acc;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[mt][ks], bk[nt][ks],
+                                                  ks == 0 ? kBiasV : acc, 0, 0, 0);
+    float xs = x[nt];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      xs = fmaf(ww[mt][j], __builtin_amdgcn_fmed3f(__int_as_float(acc[j]) - 4.0f, 0.0f, 1.0f),
+                xs);
+    x[nt] = xs;
+  }
+  // lanes l and l + 32 hold the two 32-head halves of a key: after the swap
+  // lane l holds the head sum of slot l of this wave
+  float w = lane_add_swap32(x[0], x[1]);
+  w = my_ok ? my_ks * w : neg_inf;
+  if (w == 0.0f) w = 0.0f;   // one zero: +0.0
+  if (my_slot < nslot) out[static_cast<long long>(t) * ostride + my_slot] = w;
+}
+
 }  // namespace
 
 }  // namespace csa
@@ -478,6 +651,47 @@ extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const 
                        q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table, max_blocks,
                        query_start_loc, positions, B, num_tokens, Hi, Di, ratio, scores,
                        static_cast<long long>(score_stride), static_cast<int>(ppw), err);
+  }
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+extern "C" int csa_index_score_candidates(
+    const int8_t* q_idx, const float* q_scale, const float* head_w, const int8_t* idx_kv,
+    const float* idx_scale, int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+    const int32_t* query_start_loc, const int32_t* positions, int32_t B, int32_t T,
+    int32_t num_tokens, int32_t Hi, int32_t Di, int32_t ratio, const int32_t* cand_blocks,
+    int32_t kb, int32_t block, float* cand_scores, int64_t cand_stride, int32_t* cand_count,
+    int32_t* err, void* stream) {
+  if (T < 0 || B < 0 || num_blocks < 0 || max_blocks < 0 || cand_stride < 0) return CSA_ERR_SHAPE;
+  if (num_tokens < 0 || num_tokens > T || ratio < 1 || kb < 1 || block < 1 || block > 128 ||
+      (csa::kPage % block) != 0 || cand_stride < static_cast<int64_t>(kb) * block ||
+      static_cast<long long>(kb) * block > (1ll << 30))
+    return CSA_ERR_RANGE;
+  if (num_tokens == 0) return CSA_OK;
+  if (!q_idx || !q_scale || !head_w || !query_start_loc || !positions || !cand_blocks ||
+      !cand_scores || !cand_count)
+    return CSA_ERR_NULL;
+  if (num_blocks > 0 && max_blocks > 0 && B > 0 && (!idx_kv || !idx_scale || !block_table))
+    return CSA_ERR_NULL;
+  if (Hi < 1 || Hi > 64 || Di < 16 || Di > 128 || (Di % 16) != 0) return CSA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q_idx) | reinterpret_cast<uintptr_t>(idx_kv)) & 15)
+    return CSA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(num_blocks) * csa::kPage * Di >= (1ll << 40)) return CSA_ERR_SHAPE;
+  const long long nslot = static_cast<long long>(kb) * block;
+  const long long gx = (nslot + csa::kCandSlots - 1) / csa::kCandSlots;
+  if (num_tokens > 65535) return CSA_ERR_UNSUPPORTED;
+  const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(num_tokens));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (Di <= 64) {
+    hipLaunchKernelGGL(csa::index_cand_kernel<2>, grid, dim3(csa::kThreads), 0, st, q_idx,
+                       q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table, max_blocks,
+                       query_start_loc, positions, B, num_tokens, Hi, Di, ratio, cand_blocks, kb,
+                       block, cand_scores, static_cast<long long>(cand_stride), cand_count, err);
+  } else {
+    hipLaunchKernelGGL(csa::index_cand_kernel<4>, grid, dim3(csa::kThreads), 0, st, q_idx,
+                       q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table, max_blocks,
+                       query_start_loc, positions, B, num_tokens, Hi, Di, ratio, cand_blocks, kb,
+                       block, cand_scores, static_cast<long long>(cand_stride), cand_count, err);
   }
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }

@@ -463,21 +463,48 @@ __device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared
   return true;
 }
 
-__device__ __forceinline__ int row_span(const int32_t* positions, int t, int ratio,
-                                        long long stride, int32_t* err, bool report) {
-  long long nv = visible_count(positions[t], ratio);
-  if (nv > stride) {
-    if (report) flag_error(err, CSA_EFLAG_POS_RANGE);
-    nv = stride;
+// Which entries of a score row take part, and how a chosen entry is reported.
+// The span of row t is its visible count (p + 1) / ratio, grouped into
+// ceil(count / group) entries (group 8: the blocks of a candidate mask), or
+// counts[t] when counts is given.  A chosen entry i is reported as i, or with
+// remap as remap[t][i / rgroup] * rgroup + i % rgroup (the position of
+// candidate slot i).
+struct RowSpec {
+  const int32_t* positions;
+  int ratio;
+  int group;
+  const int32_t* counts;
+  const int32_t* remap;
+  int rgroup;
+  int rstride;
+
+  __device__ __forceinline__ int span(int t, long long stride, int32_t* err, bool report) const {
+    long long nv;
+    if (counts) {
+      nv = max(0, counts[t]);
+    } else {
+      nv = visible_count(positions[t], ratio);
+      if (group > 1) nv = (nv + group - 1) / group;
+    }
+    if (nv > stride) {
+      if (report) flag_error(err, CSA_EFLAG_POS_RANGE);
+      nv = stride;
+    }
+    return static_cast<int>(nv);
   }
-  return static_cast<int>(nv);
-}
+  __device__ __forceinline__ int out(int t, int i) const {
+    if (!remap) return i;
+    const int q = i / rgroup;
+    return remap[static_cast<long long>(t) * rstride + q] * rgroup + (i - q * rgroup);
+  }
+};
 
 // Writes, in position order, every key better than or equal to the cut
 // (exactly m of them), then the -1 / -inf padding.
 template <int THREADS, int KPT, typename PosFn>
 __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, const float* row,
-                         int32_t* out_i, float* out_v, SelShared<THREADS>& sh, PosFn pos) {
+                         int32_t* out_i, float* out_v, SelShared<THREADS>& sh, PosFn pos,
+                         const RowSpec& rs, int t) {
   const uint32_t ck = sh.cut[0], cp = sh.cut[1];
   uint32_t pick = 0u;
 #pragma unroll
@@ -495,7 +522,7 @@ __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, co
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if ((pick >> j) & 1u) {
-      out_i[o] = pos(j);
+      out_i[o] = rs.out(t, pos(j));
       if (out_v) out_v[o] = val[j];
       ++o;
     }
@@ -509,10 +536,11 @@ __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, co
 
 // Every visible position is chosen: 0 .. n-1 ascending, then padding.
 template <int THREADS>
-__device__ void write_all(int n, int k, const float* row, int32_t* out_i, float* out_v) {
+__device__ void write_all(int n, int k, const float* row, int32_t* out_i, float* out_v,
+                          const RowSpec& rs, int t) {
   const float neg_inf = -__builtin_huge_valf();
   for (int i = threadIdx.x; i < k; i += THREADS) {
-    out_i[i] = i < n ? i : -1;
+    out_i[i] = i < n ? rs.out(t, i) : -1;
     if (out_v) out_v[i] = i < n ? row[i] : neg_inf;
   }
 }
@@ -522,7 +550,8 @@ __device__ void write_all(int n, int k, const float* row, int32_t* out_i, float*
 // positions: the path for rows whose threshold bin held too many keys.
 template <int THREADS>
 __device__ void select_whole_row(const float* row, int n, int m, int k, int32_t* out_i,
-                                 float* out_v, SelShared<THREADS>& sh) {
+                                 float* out_v, SelShared<THREADS>& sh, const RowSpec& rs,
+                                 int t) {
   const int tid = threadIdx.x;
   int* sel = reinterpret_cast<int*>(sh.list);
   int* sel_count = &sh.sel_count;
@@ -632,7 +661,7 @@ __device__ void select_whole_row(const float* row, int n, int m, int k, int32_t*
   const float neg_inf = -__builtin_huge_valf();
   for (int i = tid; i < k; i += THREADS) {
     const int c = i < m ? sel[i] : -1;
-    out_i[i] = c;
+    out_i[i] = c >= 0 ? rs.out(t, c) : -1;
     if (out_v) out_v[i] = c >= 0 ? row[c] : neg_inf;
   }
 }
@@ -642,8 +671,8 @@ __device__ void select_whole_row(const float* row, int n, int m, int k, int32_t*
 // ----------------------------------------------------------------------------
 template <int THREADS, int KPT>
 __global__ void __launch_bounds__(THREADS) topk_small_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, int k, int32_t* __restrict__ topk_idx,
+    const float* __restrict__ scores, long long stride, RowSpec rs,
+    int num_tokens, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_val, int32_t* err) {
   constexpr int kSmallCand = THREADS >= 1024 ? 4096 : 8 * THREADS;
   __shared__ SelShared<THREADS> sh;
@@ -666,12 +695,12 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
     if (4 * i < per && base + 4 * i < span)
       v[i] = *reinterpret_cast<const float4*>(row + base + 4 * i);
   }
-  const int n = row_span(positions, t, ratio, stride, err, tid == 0);
+  const int n = rs.span(t, stride, err, tid == 0);
   int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
   float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
   const int m = min(k, n);
   if (m == n) {
-    write_all<THREADS>(n, k, row, out_i, out_v);
+    write_all<THREADS>(n, k, row, out_i, out_v, rs, t);
     return;
   }
   uint32_t key[KPT];
@@ -729,7 +758,7 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
         const int cn = max(0, min(cper, total - cbase));
         auto cpos = [&](int j) { return static_cast<int>(cand_p[cbase + j]); };
         if (find_cut<THREADS, CPT>(ck, cn, m, sh, cpos)) {
-          emit_cut<THREADS, CPT>(ck, cn, m, k, row, out_i, out_v, sh, cpos);
+          emit_cut<THREADS, CPT>(ck, cn, m, k, row, out_i, out_v, sh, cpos, rs, t);
           done = true;
         }
       }
@@ -738,9 +767,9 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
   }
   if (done) return;
   if (find_cut<THREADS, KPT>(key, nmine, m, sh, pos))
-    emit_cut<THREADS, KPT>(key, nmine, m, k, row, out_i, out_v, sh, pos);
+    emit_cut<THREADS, KPT>(key, nmine, m, k, row, out_i, out_v, sh, pos, rs, t);
   else
-    select_whole_row<THREADS>(row, n, m, k, out_i, out_v, sh);
+    select_whole_row<THREADS>(row, n, m, k, out_i, out_v, sh, rs, t);
 }
 
 // ----------------------------------------------------------------------------
@@ -754,13 +783,13 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
 // the final kernel checks the count and falls back to an exact whole-row
 // select when the sample misled it.
 __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, int k, Workspace ws) {
+    const float* __restrict__ scores, long long stride, RowSpec rs,
+    int num_tokens, int k, Workspace ws) {
   __shared__ SelShared<kFThreads> sh;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, nullptr, false);
+  const int n = rs.span(t, stride, nullptr, false);
   if (n <= kCap) return;
   const float* row = scores + static_cast<long long>(t) * stride;
   const long long span =
@@ -832,14 +861,14 @@ __device__ __forceinline__ bool in_span(const ChunkKeys& ck, int j, int n) {
 // Keep every key >= tau: each wave writes its kept (key, position) pairs, in
 // position order, into the slots of its own segment and its count into seg[].
 __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, Workspace ws) {
+    const float* __restrict__ scores, long long stride, RowSpec rs,
+    int num_tokens, Workspace ws) {
   const int t = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, nullptr, false);
+  const int n = rs.span(t, stride, nullptr, false);
   const int c0 = blockIdx.x * kChunk;
   if (n <= kCap || c0 >= n) return;
   ChunkKeys ck;
@@ -878,8 +907,8 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
 }
 
 __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
-    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
-    int ratio, int num_tokens, int k, int32_t* __restrict__ topk_idx,
+    const float* __restrict__ scores, long long stride, RowSpec rs,
+    int num_tokens, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_val, Workspace ws, int32_t* err) {
   __shared__ SelShared<kFThreads> sh;
   __shared__ uint32_t ckey[kCap];
@@ -888,13 +917,13 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
-  const int n = row_span(positions, t, ratio, stride, err, tid == 0);
+  const int n = rs.span(t, stride, err, tid == 0);
   const float* row = scores + static_cast<long long>(t) * stride;
   int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
   float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
   const int m = min(k, n);
   if (m == n) {
-    write_all<kFThreads>(n, k, row, out_i, out_v);
+    write_all<kFThreads>(n, k, row, out_i, out_v, rs, t);
   } else {
     int total = 0;
     bool whole_row = false;
@@ -961,7 +990,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
     }
     __syncthreads();
     if (whole_row) {
-      select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh);
+      select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh, rs, t);
     } else {
       const int per = (total + kFThreads - 1) / kFThreads;   // <= kFPer
       const int base = tid * per;
@@ -971,11 +1000,89 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       const int nmine = max(0, min(per, total - base));
       auto pos = [&](int j) { return static_cast<int>(cpos[base + j]); };
       if (find_cut<kFThreads, kFPer>(key, nmine, m, sh, pos))
-        emit_cut<kFThreads, kFPer>(key, nmine, m, k, row, out_i, out_v, sh, pos);
+        emit_cut<kFThreads, kFPer>(key, nmine, m, k, row, out_i, out_v, sh, pos, rs, t);
       else
-        select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh);
+        select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh, rs, t);
     }
   }
+}
+
+// Block score of a candidate mask: the best visible score of each group of
+// `block` consecutive positions (NaN only when every visible score of the
+// block is NaN).  Writes the row's block count for the selection.
+__global__ void __launch_bounds__(256) block_max_kernel(
+    const float* __restrict__ scores, long long stride, const int32_t* __restrict__ positions,
+    int ratio, int block, int num_tokens, float* __restrict__ bs, long long bstride,
+    int32_t* __restrict__ counts, int32_t* err) {
+  const int t = blockIdx.y;
+  if (t >= num_tokens) return;
+  long long nv = visible_count(positions[t], ratio);
+  if (nv > stride) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) flag_error(err, CSA_EFLAG_POS_RANGE);
+    nv = stride;
+  }
+  const long long nb = (nv + block - 1) / block;
+  if (blockIdx.x == 0 && threadIdx.x == 0) counts[t] = static_cast<int32_t>(nb);
+  const long long j = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  if (j >= nb) return;
+  const long long c0 = j * block;
+  const int cnt = static_cast<int>(min(static_cast<long long>(block), nv - c0));
+  const float* row = scores + static_cast<long long>(t) * stride + c0;
+  float m = __builtin_nanf("");
+  if (cnt == block && (block & 3) == 0) {
+    for (int i = 0; i < block; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + i);
+      m = fmaxf(fmaxf(m, v.x), fmaxf(v.y, fmaxf(v.z, v.w)));
+    }
+  } else {
+    for (int i = 0; i < cnt; ++i) m = fmaxf(m, row[i]);
+  }
+  bs[static_cast<long long>(t) * bstride + j] = m;
+}
+
+size_t topk_ws_bytes(int T, long long stride) {
+  return (T <= 0 || stride <= kSmallMax) ? 0 : ws_bytes(T, stride);
+}
+
+// Launches the selection of the k best entries of each row of `scores`
+// (row length `stride`, a multiple of 4, 16-byte aligned).
+int launch_topk(const float* scores, long long stride, const RowSpec& rs, int T, int num_tokens,
+                int k, int32_t* topk_idx, float* topk_val, void* workspace,
+                size_t workspace_bytes, int32_t* err, hipStream_t st) {
+  if (reinterpret_cast<uintptr_t>(scores) & 15 || (stride & 3)) return CSA_ERR_UNSUPPORTED;
+  if (stride <= 4096) {
+    hipLaunchKernelGGL((topk_small_kernel<256, 16>), dim3(num_tokens), dim3(256), 0, st,
+                       scores, stride, rs, num_tokens, k, topk_idx, topk_val, err);
+  } else if (stride <= 16384) {
+    hipLaunchKernelGGL((topk_small_kernel<1024, 16>), dim3(num_tokens), dim3(1024), 0, st,
+                       scores, stride, rs, num_tokens, k, topk_idx, topk_val, err);
+  } else if (stride <= kSmallMax) {
+    hipLaunchKernelGGL((topk_small_kernel<1024, 32>), dim3(num_tokens), dim3(1024), 0, st,
+                       scores, stride, rs, num_tokens, k, topk_idx, topk_val, err);
+  } else {
+    if (stride > kMaxStride || num_tokens > 65535) return CSA_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < ws_bytes(T, stride)) return CSA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
+    const Workspace ws = ws_layout(workspace, T, stride);
+    const dim3 grid(static_cast<unsigned>((stride + kChunk - 1) / kChunk),
+                    static_cast<unsigned>(num_tokens));
+    hipLaunchKernelGGL(topk_sample_kernel, dim3(num_tokens), dim3(kFThreads), 0, st, scores,
+                       stride, rs, num_tokens, k, ws);
+    hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kLThreads), 0, st, scores, stride, rs,
+                       num_tokens, ws);
+    hipLaunchKernelGGL(topk_final_kernel, dim3(num_tokens), dim3(kFThreads), 0, st, scores,
+                       stride, rs, num_tokens, k, topk_idx, topk_val, ws, err);
+  }
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+// Candidate-mask workspace: block scores [T][bstride], block counts [T]
+// (16-byte aligned), then the selection's own workspace.
+long long block_stride(long long stride, int block) {
+  return ((stride + block - 1) / block + 3) / 4 * 4;
+}
+size_t cand_ws_head(int T, long long bstride) {
+  return (static_cast<size_t>(T) * bstride * 4 + static_cast<size_t>(T) * 4 + 15) / 16 * 16;
 }
 
 }  // namespace
@@ -984,8 +1091,8 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
 
 extern "C" size_t csa_topk_workspace_bytes(int32_t T, int64_t score_stride, int32_t k) {
   (void)k;
-  if (T <= 0 || score_stride <= csa::kSmallMax) return 0;
-  return csa::ws_bytes(T, score_stride);
+  if (score_stride < 0) return 0;
+  return csa::topk_ws_bytes(T, score_stride);
 }
 
 extern "C" int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions,
@@ -997,32 +1104,69 @@ extern "C" int csa_topk(const float* scores, int64_t score_stride, const int32_t
     return CSA_ERR_RANGE;
   if (num_tokens == 0) return CSA_OK;
   if (!scores || !positions || !topk_idx) return CSA_ERR_NULL;
+  const csa::RowSpec rs{positions, ratio, 1, nullptr, nullptr, 1, 0};
+  return csa::launch_topk(scores, score_stride, rs, T, num_tokens, k, topk_idx, topk_val,
+                          workspace, workspace_bytes, err, static_cast<hipStream_t>(stream));
+}
+
+extern "C" size_t csa_candidate_blocks_workspace_bytes(int32_t T, int64_t score_stride,
+                                                       int32_t block, int32_t kb) {
+  (void)kb;
+  if (T <= 0 || score_stride < 0 || block < 1) return 0;
+  const long long bstride = csa::block_stride(score_stride, block);
+  return csa::cand_ws_head(T, bstride) + csa::topk_ws_bytes(T, bstride);
+}
+
+extern "C" int csa_candidate_blocks(const float* scores, int64_t score_stride,
+                                    const int32_t* positions, int32_t ratio, int32_t T,
+                                    int32_t num_tokens, int32_t block, int32_t kb,
+                                    int32_t* cand_blocks, void* workspace, size_t workspace_bytes,
+                                    int32_t* err, void* stream) {
+  if (T < 0 || score_stride < 0) return CSA_ERR_SHAPE;
+  if (num_tokens < 0 || num_tokens > T || ratio < 1 || block < 1 || block > 128 ||
+      (csa::kPage % block) != 0 || kb < 1 || kb > csa::kMaxK)
+    return CSA_ERR_RANGE;
+  if (num_tokens == 0) return CSA_OK;
+  if (!scores || !positions || !cand_blocks) return CSA_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(scores) & 15 || (score_stride & 3)) return CSA_ERR_UNSUPPORTED;
+  const long long bstride = csa::block_stride(score_stride, block);
+  const size_t head = csa::cand_ws_head(T, bstride);
+  if (!workspace || workspace_bytes < head + csa::topk_ws_bytes(T, bstride))
+    return CSA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
+  float* bs = static_cast<float*>(workspace);
+  int32_t* counts = reinterpret_cast<int32_t*>(bs + static_cast<size_t>(T) * bstride);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const long long stride = score_stride;
-  if (stride <= 4096) {
-    hipLaunchKernelGGL((csa::topk_small_kernel<256, 16>), dim3(num_tokens), dim3(256), 0, st,
-                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, err);
-  } else if (stride <= 16384) {
-    hipLaunchKernelGGL((csa::topk_small_kernel<1024, 16>), dim3(num_tokens), dim3(1024), 0, st,
-                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, err);
-  } else if (stride <= csa::kSmallMax) {
-    hipLaunchKernelGGL((csa::topk_small_kernel<1024, 32>), dim3(num_tokens), dim3(1024), 0, st,
-                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, err);
-  } else {
-    if (stride > csa::kMaxStride || num_tokens > 65535) return CSA_ERR_UNSUPPORTED;
-    if (!workspace || workspace_bytes < csa::ws_bytes(T, stride)) return CSA_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
-    const csa::Workspace ws = csa::ws_layout(workspace, T, stride);
-    const dim3 grid(static_cast<unsigned>((stride + csa::kChunk - 1) / csa::kChunk),
-                    static_cast<unsigned>(num_tokens));
-    hipLaunchKernelGGL(csa::topk_sample_kernel, dim3(num_tokens), dim3(csa::kFThreads), 0, st,
-                       scores, stride, positions, ratio, num_tokens, k, ws);
-    hipLaunchKernelGGL(csa::topk_filter_kernel, grid, dim3(csa::kLThreads), 0, st, scores,
-                       stride, positions, ratio, num_tokens, ws);
-    hipLaunchKernelGGL(csa::topk_final_kernel, dim3(num_tokens), dim3(csa::kFThreads), 0, st,
-                       scores, stride, positions, ratio, num_tokens, k, topk_idx, topk_val, ws,
-                       err);
-  }
-  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+  const long long nb_max = (score_stride + block - 1) / block;
+  const dim3 grid(static_cast<unsigned>(std::max<long long>(1, (nb_max + 255) / 256)),
+                  static_cast<unsigned>(num_tokens));
+  hipLaunchKernelGGL(csa::block_max_kernel, grid, dim3(256), 0, st, scores,
+                     static_cast<long long>(score_stride), positions, ratio, block, num_tokens,
+                     bs, bstride, counts, err);
+  const csa::RowSpec rs{nullptr, 1, 1, counts, nullptr, 1, 0};
+  return csa::launch_topk(bs, bstride, rs, T, num_tokens, kb, cand_blocks, nullptr,
+                          static_cast<uint8_t*>(workspace) + head, workspace_bytes - head, err,
+                          st);
+}
+
+extern "C" size_t csa_topk_candidates_workspace_bytes(int32_t T, int64_t cand_stride, int32_t k) {
+  (void)k;
+  if (cand_stride < 0) return 0;
+  return csa::topk_ws_bytes(T, cand_stride);
+}
+
+extern "C" int csa_topk_candidates(const float* cand_scores, int64_t cand_stride,
+                                   const int32_t* cand_count, const int32_t* cand_blocks,
+                                   int32_t kb, int32_t block, int32_t T, int32_t num_tokens,
+                                   int32_t k, int32_t* topk_idx, float* topk_val, void* workspace,
+                                   size_t workspace_bytes, int32_t* err, void* stream) {
+  if (T < 0 || cand_stride < 0) return CSA_ERR_SHAPE;
+  if (num_tokens < 0 || num_tokens > T || block < 1 || kb < 1 || k < 1 || k > csa::kMaxK ||
+      cand_stride < static_cast<int64_t>(kb) * block)
+    return CSA_ERR_RANGE;
+  if (num_tokens == 0) return CSA_OK;
+  if (!cand_scores || !cand_count || !cand_blocks || !topk_idx) return CSA_ERR_NULL;
+  const csa::RowSpec rs{nullptr, 1, 1, cand_count, cand_blocks, block, kb};
+  return csa::launch_topk(cand_scores, cand_stride, rs, T, num_tokens, k, topk_idx, topk_val,
+                          workspace, workspace_bytes, err, static_cast<hipStream_t>(stream));
 }

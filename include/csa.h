@@ -7,6 +7,8 @@
  *   2. csa_index_score            -- INT8 lightning-indexer scores over the
  *                                    causally visible compressed positions
  *   3. csa_topk                   -- the k best positions, ascending, -1 padded
+ *      (hierarchical layers: csa_candidate_blocks publishes a block mask;
+ *      csa_index_score_candidates + csa_topk_candidates select inside it)
  *   4. csa_sparse_attn_decode /   -- shared-KV attention over the 128-token
  *      csa_sparse_attn_prefill       window and the selected compressed rows,
  *                                    with one sink logit per head
@@ -250,6 +252,83 @@ int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const floa
                             int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
                             uint16_t* out, float* lse, void* workspace,
                             size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * Hierarchical selection ([V41] "Decode composition"): a full layer publishes
+ * a candidate mask of blocks of `block` consecutive compressed positions
+ * (2,048 blocks of eight in V4.1); a later reindex layer scores only the
+ * mask's positions with its own index query and selects its final k
+ * positions there.  A reuse layer takes another layer's selection as it is:
+ * it calls the attention entry points with that topk_idx and needs nothing
+ * below.  Masks stay in request-local compressed-position space.
+ *
+ * csa_candidate_blocks -- the full layer's mask.  Block j of row t covers
+ * positions j*block .. j*block + block - 1; its score is the largest score
+ * among its visible positions (c < (p + 1) / ratio, cut to score_stride with
+ * CSA_EFLAG_POS_RANGE), NaN when all of them are NaN.  Blocks with no visible
+ * position are not eligible.
+ *
+ *   scores       FP32 [T, score_stride] (csa_index_score's output)
+ *   cand_blocks  INT32 [T, kb]: the min(kb, eligible) best blocks (block score
+ *                descending, the lower block first, NaN below every number)
+ *                ascending, then -1
+ *   workspace    csa_candidate_blocks_workspace_bytes(T, score_stride, block,
+ *                kb) bytes, 16-byte aligned: the block scores, one count per
+ *                row, then the selection's scratch; nothing survives a call
+ *
+ * Supported: block divides 128, 1 <= kb <= 4096, score_stride a multiple of
+ * 4, scores 16-byte aligned.
+ */
+size_t csa_candidate_blocks_workspace_bytes(int32_t T, int64_t score_stride, int32_t block,
+                                            int32_t kb);
+int csa_candidate_blocks(const float* scores, int64_t score_stride, const int32_t* positions,
+                         int32_t ratio, int32_t T, int32_t num_tokens, int32_t block, int32_t kb,
+                         int32_t* cand_blocks, void* workspace, size_t workspace_bytes,
+                         int32_t* err, void* stream);
+
+/*
+ * csa_index_score_candidates -- a reindex layer's scores.  Slot s of row t is
+ * position cand_blocks[t][s / block] * block + s % block; it scores exactly as
+ * csa_index_score does at that position (the same arithmetic, bit for bit).
+ * Query, key, block-table and metadata arguments are csa_index_score's.
+ *
+ *   cand_blocks  INT32 [T, kb]: ascending block ids, then -1 (as
+ *                csa_candidate_blocks writes them)
+ *   cand_scores  FP32 [T, cand_stride], cand_stride >= kb * block: slots
+ *                0 .. kb*block - 1 written; a slot that is not eligible (block
+ *                -1, position not visible, or its page invalid) is -inf
+ *   cand_count   INT32 [T]: the number of leading eligible slots (with an
+ *                ascending mask the eligible slots are exactly that prefix)
+ *
+ * Errors: a block past the row's visible span sets CSA_EFLAG_TOPK_RANGE, an
+ * invalid page CSA_EFLAG_BLOCK_RANGE, a row no request owns CSA_EFLAG_META
+ * (count 0); those slots are left out.  With a mask that does not ascend,
+ * cand_count covers only its eligible prefix.
+ */
+int csa_index_score_candidates(const int8_t* q_idx, const float* q_scale, const float* head_w,
+                               const int8_t* idx_kv, const float* idx_scale, int32_t num_blocks,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* query_start_loc, const int32_t* positions,
+                               int32_t B, int32_t T, int32_t num_tokens, int32_t Hi, int32_t Di,
+                               int32_t ratio, const int32_t* cand_blocks, int32_t kb,
+                               int32_t block, float* cand_scores, int64_t cand_stride,
+                               int32_t* cand_count, int32_t* err, void* stream);
+
+/*
+ * csa_topk_candidates -- a reindex layer's final selection: per active row,
+ * the k best of its first cand_count[t] slots, reported as compressed
+ * positions (slot s -> cand_blocks[t][s / block] * block + s % block), in
+ * csa_topk's output contract (ascending, -1 / -inf padding, the same
+ * ranking; with an ascending mask slot order is position order, so ties go to
+ * the lower position).  workspace: csa_topk_candidates_workspace_bytes(T,
+ * cand_stride, k) bytes (0 for cand_stride <= 32,768).  Supported as csa_topk,
+ * with cand_stride >= kb * block.
+ */
+size_t csa_topk_candidates_workspace_bytes(int32_t T, int64_t cand_stride, int32_t k);
+int csa_topk_candidates(const float* cand_scores, int64_t cand_stride, const int32_t* cand_count,
+                        const int32_t* cand_blocks, int32_t kb, int32_t block, int32_t T,
+                        int32_t num_tokens, int32_t k, int32_t* topk_idx, float* topk_val,
+                        void* workspace, size_t workspace_bytes, int32_t* err, void* stream);
 
 #ifdef __cplusplus
 }
