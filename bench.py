@@ -93,17 +93,27 @@ def work_model(cfg, x, topk_idx: np.ndarray):
     idx_keys = 0
     kv_rows = 0
     pairs = 0
+    scored = 0   # index scores written (score rows, or the mask's slots)
+    kb, blk = getattr(cfg, "cand_kb", 0), getattr(cfg, "cand_block", 8)
     for b in range(len(qsl) - 1):
         rows = range(qsl[b], qsl[b + 1])
         if not len(rows):
             continue
-        if mode == "csa":
+        if mode in ("csa", "hier_full"):
             idx_keys += int(max(nv[t] for t in rows))
+        elif mode == "reindex":   # every key of the request's candidate slots, once
+            cand = np.asarray(x["cand_blocks"])
+            keys = set()
+            for t in rows:
+                for c in cand[t]:
+                    if c >= 0:
+                        keys.update(range(int(c) * blk, min(int(nv[t]), (int(c) + 1) * blk)))
+            idx_keys += len(keys)
         win, sel = set(), set()
         for t in rows:
             p = int(pos[t])
             w = list(range(max(0, p - cfg.W + 1), p + 1))
-            if mode == "csa":
+            if mode in ("csa", "reindex", "hier_full"):
                 s = [int(c) for c in topk_idx[t] if c >= 0]
             elif mode == "hca":   # every visible compressed row, bounded by k
                 s = list(range(min(int(nv[t]), k)))
@@ -113,18 +123,31 @@ def work_model(cfg, x, topk_idx: np.ndarray):
             sel.update(s)
             pairs += len(w) + len(s)
         kv_rows += len(win) + len(sel)
-    q_side = T * Hi * (Di + 8) if mode == "csa" else 0
-    sel_bytes = 4 * T * k if mode == "csa" else 0   # the selection array the attention reads
+    indexed = mode in ("csa", "reindex", "hier_full")
+    q_side = T * Hi * (Di + 8) if indexed else 0
+    sel_bytes = 4 * T * k if indexed else 0   # the selection array the attention reads
+    mask_bytes = 4 * T * kb if mode in ("reindex", "hier_full") else 0
+    if mode == "reindex":
+        scored = T * kb * blk
+        ranked = 0
+        for t in range(T):
+            c = np.asarray(x["cand_blocks"])[t]
+            ranked += sum(min(blk, max(0, int(nv[t]) - int(b) * blk)) for b in c if b >= 0)
+    else:
+        scored = T * cfg.score_stride
+        ranked = int(nv.clip(max=cfg.score_stride).sum())
     st = {
         "rope": 8 * T * R + 4 * T,   # read + write cos and sin rows (R/2 FP32 each), positions
-        "index": idx_keys * (Di + 4) + q_side + 4 * T * cfg.score_stride,
-        "topk": 4 * int(nv.clip(max=cfg.score_stride).sum()) + 8 * T * k,
+        "index": idx_keys * (Di + 4) + q_side + 4 * scored + mask_bytes * (mode == "reindex"),
+        "topk": 4 * ranked + 8 * T * k + mask_bytes * (mode == "reindex"),
         "attn": kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + sel_bytes + 4 * T * R,
     }
-    if mode != "csa":
+    if mode == "hier_full":   # block maxima over every visible score, then the mask
+        st["cand"] = 4 * int(nv.clip(max=cfg.score_stride).sum()) + mask_bytes
+    if not indexed:
         st = {"rope": st["rope"], "attn": st["attn"]}
     step = (idx_keys * (Di + 4) + kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + q_side
-            + 2 * sel_bytes + 4 * T * R)
+            + 2 * sel_bytes + 4 * T * R + mask_bytes)
     flops = {"attn": pairs * H * D * 4,
              "index": int(sum(nv[t] for t in range(T))) * Hi * Di * 2}
     return dict(stage_bytes=st, step_bytes=step, flops=flops, kv_rows=kv_rows,
@@ -174,6 +197,8 @@ def cpu_baseline(cfg, x, budget_s: float):
     done_rows = 0
     t0 = time.perf_counter()
     stage = dict(rope=0.0, index=0.0, topk=0.0, attn=0.0)
+    if mode == "hier_full":
+        stage["cand"] = 0.0
     rng = np.random.default_rng(0)
     while True:
         rows = np.arange(T) if rows_per_call == T else np.sort(rng.choice(T, rows_per_call, False))
@@ -182,22 +207,37 @@ def cpu_baseline(cfg, x, budget_s: float):
         cnt = np.bincount(owner, minlength=len(qsl) - 1)
         sub = dict(x)
         sub["query_start_loc"] = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
-        for key in ("q_idx", "q_scale", "head_w", "positions", "position_ids", "q"):
-            sub[key] = np.ascontiguousarray(np.asarray(x[key])[rows])
+        for key in ("q_idx", "q_scale", "head_w", "positions", "position_ids", "q", "cand_blocks"):
+            if key in x:
+                sub[key] = np.ascontiguousarray(np.asarray(x[key])[rows])
         n = len(rows)
         a = time.perf_counter()
+        cand_before = stage.get("cand", 0.0)
         rc = np.zeros((n, cfg.R // 2), np.float32)
         rs = np.zeros_like(rc)
         oracle.materialize_rope_rows(sub["freqs_cos"], sub["freqs_sin"], sub["position_ids"], n,
                                      rc, rs)
         b_ = time.perf_counter()
-        if mode == "csa":
+        if mode in ("csa", "hier_full"):
             s, _ = oracle.index_scores(sub["q_idx"], sub["q_scale"], sub["head_w"], sub["idx_kv"],
                                        sub["idx_scale"], sub["cmp_block_table"],
                                        sub["query_start_loc"], sub["positions"], n, cfg.ratio,
                                        cfg.score_stride)
             c_ = time.perf_counter()
             idx, _, _ = oracle.topk(s, sub["positions"], cfg.ratio, n, cfg.k)
+            if mode == "hier_full":
+                m_ = time.perf_counter()
+                oracle.candidate_blocks(s, sub["positions"], cfg.ratio, n, cfg.cand_block,
+                                        cfg.cand_kb)
+                stage["cand"] += time.perf_counter() - m_
+        elif mode == "reindex":
+            s, _ = oracle.index_scores_in_candidates(
+                sub["q_idx"], sub["q_scale"], sub["head_w"], sub["idx_kv"], sub["idx_scale"],
+                sub["cmp_block_table"], sub["query_start_loc"], sub["positions"], n, cfg.ratio,
+                sub["cand_blocks"], cfg.cand_block)
+            c_ = time.perf_counter()
+            idx, _, _ = oracle.topk_in_candidates(s, sub["cand_blocks"], cfg.cand_block,
+                                                  sub["positions"], cfg.ratio, n, cfg.k)
         else:   # hca: every visible compressed row; swa: no compressed row
             c_ = time.perf_counter()
             idx = None if mode == "hca" else np.zeros((n, 0), np.int32)
@@ -209,7 +249,7 @@ def cpu_baseline(cfg, x, budget_s: float):
         e_ = time.perf_counter()
         stage["rope"] += b_ - a
         stage["index"] += c_ - b_
-        stage["topk"] += d_ - c_
+        stage["topk"] += d_ - c_ - (stage.get("cand", 0.0) - cand_before)
         stage["attn"] += e_ - d_
         done_rows += n
         if time.perf_counter() - t0 >= budget_s:
@@ -217,10 +257,11 @@ def cpu_baseline(cfg, x, budget_s: float):
     el = time.perf_counter() - t0
     return {"value": done_rows / el, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done_rows} query rows of this workload ({rows_per_call} per oracle call, "
-                      f"{'all four stages' if mode == 'csa' else 'rope rows and attention'}, "
+                      f"{'every stage' if mode in ('csa', 'reindex', 'hier_full') else 'rope rows and attention'}, "
                       f"float64 NumPy) in {el:.1f} s",
             "stage_seconds": {k: round(v, 3) for k, v in stage.items()
-                              if mode == "csa" or k in ("rope", "attn")}}
+                              if mode in ("csa", "reindex", "hier_full")
+                              or k in ("rope", "attn")}}
 
 
 # ---------------------------------------------------------------------------
@@ -243,7 +284,9 @@ def main():
     shared_names = ("freqs_cos", "freqs_sin")
     first = csa.step_for_config(cfg, x)
     shared = {n: first.t[n] for n in shared_names}
-    per_copy_touch = (cfg.B * cfg.n_cmp_per_request * (cfg.Di + 4) +
+    idx_touch = (cfg.T * cfg.cand_kb * cfg.cand_block if cfg.mode == "reindex"
+                 else cfg.B * cfg.n_cmp_per_request)
+    per_copy_touch = (idx_touch * (cfg.Di + 4) +
                       cfg.T * (cfg.k + cfg.W) * 2 * cfg.D + 4 * cfg.T * cfg.H * cfg.D)
     if args.warm:
         copies = 1
@@ -319,10 +362,16 @@ def main():
                 "algorithmic_per_launch": wm["flops"]["attn"], "avg_launch_ms": stage_ms[dom]}
     else:
         long_rows = cfg.score_stride > 32768
-        names = {"rope": "rope_rows_kernel", "index": "index_score_kernel",
+        if first.mode == "reindex":
+            long_rows = first.score_stride > 32768
+        split_ring = (not first.prefill and cfg.W + cfg.k >= 1024)
+        names = {"rope": "rope_rows_kernel",
+                 "index": "index_cand_kernel" if first.mode == "reindex" else "index_score_kernel",
                  "topk": ("topk_sample_kernel + topk_filter_kernel + topk_final_kernel" if long_rows
                           else "topk_small_kernel"),
-                 "attn": "attn_decode_kernel + attn_merge_kernel"}
+                 "cand": "block_max_kernel + top-k of the block scores",
+                 "attn": ("attn_kernel + attn_merge_kernel" if split_ring
+                          else "attn_decode_kernel + attn_merge_kernel")}
         ach = wm["stage_bytes"][dom] / (stage_ms[dom] / 1e3) / 1e9
         roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
@@ -337,9 +386,14 @@ def main():
         "config": {"workload": cfg.name, "rows": cfg.T, "requests": cfg.B, "heads": cfg.H,
                    "head_dim": cfg.D, "ratio": cfg.ratio, "top_k": cfg.k, "window": cfg.W,
                    "compressed_rows_per_request": cfg.n_cmp_per_request,
-                   "indexer": f"{cfg.Hi}x{cfg.Di}" if first.mode == "csa" else "none",
+                   "indexer": (f"{cfg.Hi}x{cfg.Di}" if first.mode in ("csa", "reindex", "hier_full")
+                               else "none"),
                    "selection": {"csa": "indexer top-k", "hca": "every visible compressed row",
-                                 "swa": "window only"}[first.mode],
+                                 "swa": "window only",
+                                 "reindex": f"indexer top-k inside {cfg.cand_kb} candidate blocks "
+                                            f"of {cfg.cand_block}",
+                                 "hier_full": f"indexer top-k, publishing {cfg.cand_kb} candidate "
+                                              f"blocks of {cfg.cand_block}"}[first.mode],
                    "input_copies": copies,
                    "cache": "warm" if copies == 1 else "cold (rotating copies > 512 MiB)"},
         "step_hbm": {"algorithmic_bytes": wm["step_bytes"], "achieved_gbs": round(step_gbs, 1),

@@ -29,12 +29,17 @@ class CsaStep:
                  rope_offset: int, softmax_scale: float, num_tokens: Optional[int] = None,
                  prefill: bool = False, device: str = "cuda", with_values: bool = True,
                  with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None,
-                 mode: str = "csa"):
+                 mode: str = "csa", cand_kb: int = 0, cand_block: int = 8):
         # mode "csa": indexer scores and top-k select the compressed rows;
         # "hca": no indexer, every visible compressed row (k bounds them);
-        # "swa": the window alone (k = 0)
-        if mode not in ("csa", "hca", "swa"):
+        # "swa": the window alone (k = 0); "reindex": scores and top-k only
+        # inside the supplied candidate mask arrays["cand_blocks"];
+        # "hier_full": the csa step, then the candidate mask of cand_kb blocks
+        # of cand_block positions it publishes
+        if mode not in ("csa", "hca", "swa", "reindex", "hier_full"):
             raise ValueError(f"unknown mode {mode!r}")
+        if mode in ("reindex", "hier_full") and cand_kb < 1:
+            raise ValueError(f"mode {mode!r} needs cand_kb >= 1")
         self.mode = mode
         self.ratio, self.k, self.window = int(ratio), int(k), int(window)
         self.rope_offset, self.softmax_scale = int(rope_offset), float(softmax_scale)
@@ -55,6 +60,17 @@ class CsaStep:
         f32 = dict(dtype=torch.float32, device=dev)
         self.rope_cos = torch.empty((T, half), **f32)
         self.rope_sin = torch.empty((T, half), **f32)
+        self.cand_kb, self.cand_block = int(cand_kb), int(cand_block)
+        if mode == "reindex":
+            # the scores of the mask's slots replace the full score rows
+            self.score_stride = (self.cand_kb * self.cand_block + 3) // 4 * 4
+            self.cand_blocks = self.t["cand_blocks"]
+            self.cand_count = torch.empty((T,), dtype=torch.int32, device=dev)
+        elif mode == "hier_full":
+            self.cand_blocks = torch.empty((T, self.cand_kb), dtype=torch.int32, device=dev)
+            cw = _lib.csa_candidate_blocks_workspace_bytes(T, self.score_stride, self.cand_block,
+                                                           self.cand_kb)
+            self.cand_ws = torch.empty(cw, dtype=torch.uint8, device=dev)
         self.scores = torch.empty((T, self.score_stride), **f32)
         self.topk_idx = torch.empty((T, self.k), dtype=torch.int32, device=dev)
         self.topk_val = torch.empty((T, self.k), **f32) if with_values else None
@@ -74,12 +90,25 @@ class CsaStep:
 
     def index(self, stream=None):
         t = self.t
+        if self.mode == "reindex":
+            _lib.csa_index_score_candidates(
+                t["q_idx"], t["q_scale"], t["head_w"], t["idx_kv"], t["idx_scale"],
+                t["cmp_block_table"], t["query_start_loc"], t["positions"], self.num_tokens,
+                self.ratio, self.cand_blocks, self.cand_block, self.scores, self.cand_count,
+                err=self.err, stream=stream)
+            return
         _lib.csa_index_score(t["q_idx"], t["q_scale"], t["head_w"], t["idx_kv"], t["idx_scale"],
                              t["cmp_block_table"], t["query_start_loc"], t["positions"],
                              self.num_tokens, self.ratio, self.scores, err=self.err,
                              stream=stream)
 
     def topk(self, stream=None):
+        if self.mode == "reindex":
+            _lib.csa_topk_candidates(self.scores, self.cand_count, self.cand_blocks,
+                                     self.cand_block, self.num_tokens, self.k, self.topk_idx,
+                                     self.topk_val, workspace=self.topk_ws, err=self.err,
+                                     stream=stream)
+            return
         _lib.csa_topk(self.scores, self.t["positions"], self.ratio, self.num_tokens, self.k,
                       self.topk_idx, self.topk_val, workspace=self.topk_ws, err=self.err,
                       stream=stream)
@@ -87,7 +116,7 @@ class CsaStep:
     def attn(self, stream=None, topk_idx: Optional[torch.Tensor] = None):
         t = self.t
         fn = _lib.csa_sparse_attn_prefill if self.prefill else _lib.csa_sparse_attn_decode
-        if topk_idx is None and self.mode == "csa":
+        if topk_idx is None and self.mode in ("csa", "reindex", "hier_full"):
             topk_idx = self.topk_idx
         fn(t["q"], self.rope_cos, self.rope_sin, self.rope_offset, t["cmp_kv"],
            t["cmp_block_table"], topk_idx, self.ratio, t["win_kv"], t["win_block_table"],
@@ -97,7 +126,17 @@ class CsaStep:
 
     @property
     def stages(self):
-        return ("rope", "index", "topk", "attn") if self.mode == "csa" else ("rope", "attn")
+        if self.mode == "hier_full":
+            return ("rope", "index", "topk", "cand", "attn")
+        if self.mode in ("csa", "reindex"):
+            return ("rope", "index", "topk", "attn")
+        return ("rope", "attn")
+
+    def cand(self, stream=None):
+        """The candidate mask the full layer publishes (mode hier_full)."""
+        _lib.csa_candidate_blocks(self.scores, self.t["positions"], self.ratio,
+                                  self.num_tokens, self.cand_block, self.cand_blocks,
+                                  self.cand_ws, err=self.err, stream=stream)
 
     def run(self, stream=None):
         for s in self.stages:
@@ -108,4 +147,5 @@ def step_for_config(cfg, arrays: Dict[str, np.ndarray], **kw) -> CsaStep:
     """CsaStep with the scalar parameters of a workload config."""
     return CsaStep(arrays, ratio=cfg.ratio, k=cfg.k, window=cfg.W, rope_offset=cfg.rope_offset,
                    softmax_scale=cfg.softmax_scale, prefill=(cfg.T > 256),
-                   mode=getattr(cfg, "mode", "csa"), **kw)
+                   mode=getattr(cfg, "mode", "csa"), cand_kb=getattr(cfg, "cand_kb", 0),
+                   cand_block=getattr(cfg, "cand_block", 8), **kw)

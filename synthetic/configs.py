@@ -40,8 +40,13 @@ class CsaConfig:
     shared_pool: bool = False   # all requests page into one pool (C5)
     # "csa": indexer + top-k select the compressed rows; "hca": no indexer,
     # every causally visible compressed row (k bounds them); "swa": the
-    # window alone (k = 0)
+    # window alone (k = 0); "reindex": a layer that scores only the positions
+    # of a supplied candidate mask (cand_kb blocks of cand_block positions)
+    # and selects its k there; "hier_full": the csa step that also publishes
+    # such a mask for the reindex layers
     mode: str = "csa"
+    cand_kb: int = 0
+    cand_block: int = 8
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -145,8 +150,25 @@ C7 = _decode(
     "window alone",
     n_req=4, s=2, context=32768, ratio=128, k=0, mode="swa")
 
-CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7)}
-SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7}
+# The hierarchical indexer of the ratio-1 layers (pypto-lib "DeepSeek V4.1
+# Flash", section "Decode composition"): the full layer keeps 2,048 blocks of
+# eight compressed positions, a reindex layer picks its final 512 inside them.
+C8 = _decode(
+    "c8_reindex_ratio1_decode",
+    "ratio-1 reindex decode: 8 rows (4 x 2), 131,072 compressed rows per request, "
+    "a supplied mask of 2,048 blocks of 8 per row, indexer 64x128 scored inside "
+    "it, top-k 512, window 128",
+    n_req=4, s=2, context=131072, ratio=1, k=512, mode="reindex", cand_kb=2048)
+
+C9 = _decode(
+    "c9_full_hier_ratio1_decode",
+    "ratio-1 full decode that also publishes the candidate mask: C3's step (top-k "
+    "2048) plus 2,048 blocks of 8 per row",
+    n_req=4, s=2, context=131072, ratio=1, k=2048, mode="hier_full", cand_kb=2048)
+
+CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8, C9)}
+SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7, "c8": C8,
+         "c9": C9}
 
 
 def get(name: str) -> CsaConfig:

@@ -39,6 +39,7 @@ from .configs import PAGE, CsaConfig
 _TENSOR_IDS = {
     "q": 1, "cmp_kv": 2, "win_kv": 3, "q_idx_f": 4, "head_w": 5, "idx_kv": 6,
     "idx_scale": 7, "outlier": 8, "attn_sink": 9, "cmp_perm": 10, "win_perm": 11,
+    "cand_blocks": 12,
 }
 
 _CHUNK_ELEMS = 1 << 24  # fixed chunk so the draws never depend on the caller
@@ -172,4 +173,19 @@ def make_inputs(cfg: CsaConfig, seed: int = 0, with_tables: bool = True) -> CsaI
             i += 1
     t["win_block_table"] = wbt
     t["win_kv"] = _bf16_normal(seed, "win_kv", (nbw, PAGE, D))
+
+    # ---- a reindex layer's candidate mask (the full layer's output, supplied
+    #      as an input): per row, cand_kb distinct blocks of cand_block
+    #      positions drawn uniformly from the blocks its position reaches,
+    #      ascending, padded with -1
+    if cfg.mode == "reindex":
+        kb, blk = cfg.cand_kb, cfg.cand_block
+        g = _rng(seed, "cand_blocks")
+        cand = np.full((T, kb), -1, dtype=np.int32)
+        for r in range(T):
+            reach = -(-max(0, (int(pos[r]) + 1) // cfg.ratio) // blk)
+            m = min(kb, reach)
+            if m:
+                cand[r, :m] = np.sort(g.choice(reach, size=m, replace=False))
+        t["cand_blocks"] = cand
     return CsaInputs(cfg, t)

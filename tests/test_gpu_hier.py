@@ -256,3 +256,69 @@ def test_hierarchical_chain_c2():
     o = H.oracle_step(x, cfg, topk_override=g_idx)
     H.check_attn(H.bf16_to_f64(step.out), o["out"], step.lse.cpu().numpy().astype(np.float64),
                  o["lse"], "reindex attention")
+
+
+def _oracle_attn_on(x, cfg, sel):
+    T = cfg.T
+    half = cfg.R // 2
+    rc = np.zeros((T, half), np.float32)
+    rs = np.zeros((T, half), np.float32)
+    oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["position_ids"], T, rc, rs)
+    out, lse, _ = oracle.sparse_attn(x["q"], rc, rs, cfg.rope_offset, x["cmp_kv"],
+                                     x["cmp_block_table"], sel, cfg.ratio, x["win_kv"],
+                                     x["win_block_table"], cfg.W, x["attn_sink"],
+                                     cfg.softmax_scale, x["query_start_loc"], x["positions"], T,
+                                     k=cfg.k)
+    return out, lse
+
+
+def test_reindex_layer_step_parity():
+    """C8, the reindex layer's whole step (RoPE rows, scores inside the
+    supplied mask, top-512 there, attention) through CsaStep."""
+    csa = _csa()
+    cfg = synthetic.get("c8")
+    x = synthetic.make_inputs(cfg, seed=0).t
+    print("[hier] c8 step", flush=True)
+    step = csa.step_for_config(cfg, x)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    T, kb, blk = cfg.T, cfg.cand_kb, cfg.cand_block
+    cand = x["cand_blocks"]
+    g_sc = step.scores.cpu().numpy().astype(np.float64)[:, :kb * blk]
+    o_sc, oe = oracle.index_scores_in_candidates(x["q_idx"], x["q_scale"], x["head_w"],
+                                                 x["idx_kv"], x["idx_scale"],
+                                                 x["cmp_block_table"], x["query_start_loc"],
+                                                 x["positions"], T, cfg.ratio, cand, blk)
+    assert oe == 0
+    H.check_scores(g_sc, o_sc, "c8 scores")
+    g_idx = step.topk_idx.cpu().numpy()
+    g_ref, _, _ = oracle.topk_in_candidates(g_sc, cand, blk, x["positions"], cfg.ratio, T, cfg.k)
+    np.testing.assert_array_equal(g_idx, g_ref)
+    o_idx, _, _ = oracle.topk_in_candidates(o_sc, cand, blk, x["positions"], cfg.ratio, T, cfg.k)
+    o_by_pos = np.full((T, cfg.score_stride), -np.inf)
+    for t in range(T):
+        nv = oracle.visible_count(int(x["positions"][t]), cfg.ratio)
+        pos, elig = oracle.candidate_positions(cand[t], blk, nv)
+        o_by_pos[t, pos[elig]] = o_sc[t, elig]
+    H.check_topk(g_idx, o_idx, o_by_pos, x["positions"], cfg.ratio, "c8 top-k")
+    out, lse = _oracle_attn_on(x, cfg, g_idx)
+    H.check_attn(H.bf16_to_f64(step.out), out, step.lse.cpu().numpy().astype(np.float64), lse,
+                 "c8 attention")
+
+
+def test_full_layer_publishes_mask():
+    """C9: the full layer's step also writes the candidate mask; it is exactly
+    the oracle's selection over the GPU's own scores."""
+    csa = _csa()
+    cfg = synthetic.get("c9")
+    x = synthetic.make_inputs(cfg, seed=0, with_tables=True).t
+    print("[hier] c9 step", flush=True)
+    step = csa.step_for_config(cfg, x)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    g_full = step.scores.cpu().numpy().astype(np.float64)
+    ref, _ = oracle.candidate_blocks(g_full, x["positions"], cfg.ratio, cfg.T, cfg.cand_block,
+                                     cfg.cand_kb)
+    np.testing.assert_array_equal(step.cand_blocks.cpu().numpy(), ref)
