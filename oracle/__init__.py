@@ -14,4 +14,5 @@ from .csa_oracle import (  # noqa: F401
     rotate_adjacent_pairs, materialize_rope_rows, index_scores, topk,
     kv_rows_for_query, deterministic_selection, sparse_attn,
     candidate_blocks, candidate_positions, index_scores_in_candidates, topk_in_candidates,
+    decode_e2m1, decode_e8m0, mx_rows, index_scores_mxfp4,
 )

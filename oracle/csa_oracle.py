@@ -220,6 +220,87 @@ def index_scores(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table,
 
 
 # ----------------------------------------------------------------------------
+# a2 with the low-bit index plane: MXFP4 keys and queries
+# ----------------------------------------------------------------------------
+
+def decode_e2m1(codes):
+    """Values of packed E2M1 (FP4) codes.  Each byte holds two elements, the
+    one with the lower index in bits 0-3.  A 4-bit code is sign | 2-bit
+    exponent | 1-bit mantissa: exponent 0 is subnormal (mantissa * 0.5),
+    otherwise 2^(e-1) * (1 + mantissa / 2) -- the magnitudes 0, 0.5, 1, 1.5,
+    2, 3, 4, 6 ([V41] cache ABI: packed MXFP4 E2M1 index keys).  Returns
+    float64 with the last axis doubled."""
+    b = np.asarray(codes, dtype=np.uint8)
+    nib = np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[:-1] + (2 * b.shape[-1],))
+    sign = np.where(nib & 8, -1.0, 1.0)
+    e = (nib >> 1) & 3
+    m = (nib & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e.astype(np.int64) - 1))
+    return sign * mag
+
+
+def decode_e8m0(scale_bytes):
+    """Value of an E8M0 block scale: 2^(byte - 127) (the pages settle this
+    convention: a scale byte reads as 2^(byte - 127), the same as torch's
+    float8_e8m0fnu; byte 255 is NaN)."""
+    b = np.asarray(scale_bytes, dtype=np.int64)
+    return np.where(b == 255, np.nan, np.ldexp(1.0, b - 127))
+
+
+def mx_rows(codes, scale_bytes, group=32):
+    """Dequantised rows of an MX plane: E2M1 values times the E8M0 scale of
+    their group of `group` consecutive elements."""
+    v = decode_e2m1(codes)
+    sc = decode_e8m0(scale_bytes)
+    return v * np.repeat(sc, group, axis=-1)
+
+
+def index_scores_mxfp4(q_fp4, q_sc, head_w, idx_fp4, idx_sc, block_table, query_start_loc,
+                       positions, num_tokens, ratio, score_stride, key_chunk: int = 1 << 15):
+    """The indexer score with the FP4 index plane ([ATOM] "Current execution
+    scope": the FP4 index arithmetic is E2M1 with one E8M0 scale per 32
+    dims; [V41] cache ABI: index keys packed MXFP4 E2M1 with group-of-32
+    E8M0 scales).  Reading: the query side uses the same MX format, and the
+    score keeps the formula of ``index_scores`` with each head's dot taken
+    over the dequantised rows (the block scales replace the per-row scales):
+
+        score[t, c] = sum_h w[t,h] * relu( <mx(q[t,h]), mx(k[c])> )
+
+    Visibility, contract checks and flags are those of ``index_scores``.
+    Returns (scores float64 [num_tokens, score_stride], err)."""
+    qsl = np.asarray(query_start_loc)
+    num_blocks = idx_fp4.shape[0]
+    Db = idx_fp4.shape[2]
+    keys_flat = np.asarray(idx_fp4).reshape(num_blocks * PAGE, Db)
+    sc_flat = np.asarray(idx_sc).reshape(num_blocks * PAGE, -1)
+    scores = np.full((int(num_tokens), int(score_stride)), -np.inf, dtype=np.float64)
+    err = 0
+    max_blocks = block_table.shape[1]
+    for t in range(int(num_tokens)):
+        b = owner_request(t, qsl)
+        if b < 0:
+            err |= EFLAG_META
+            continue
+        n = visible_count(positions[t], ratio)
+        if n > score_stride or n > PAGE * max_blocks:
+            err |= EFLAG_POS_RANGE
+            n = min(n, int(score_stride), PAGE * max_blocks)
+        q = mx_rows(q_fp4[t], q_sc[t])                     # [Hi, Di]
+        w = np.asarray(head_w[t], dtype=np.float64)
+        for c0 in range(0, n, key_chunk):
+            cs = np.arange(c0, min(n, c0 + key_chunk))
+            rows, ok = _physical_rows(block_table[b], num_blocks, cs)
+            if not ok.all():
+                err |= EFLAG_BLOCK_RANGE
+            k = mx_rows(keys_flat[rows], sc_flat[rows])     # [n_c, Di]
+            dots = q @ k.T                                  # [Hi, n_c]
+            s = (w[:, None] * np.maximum(dots, 0.0)).sum(axis=0)
+            s[~ok] = -np.inf
+            scores[t, cs] = s
+    return scores, err
+
+
+# ----------------------------------------------------------------------------
 # a3: top-k
 # ----------------------------------------------------------------------------
 
