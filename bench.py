@@ -124,7 +124,9 @@ def work_model(cfg, x, topk_idx: np.ndarray):
             pairs += len(w) + len(s)
         kv_rows += len(win) + len(sel)
     indexed = mode in ("csa", "reindex", "hier_full")
-    q_side = T * Hi * (Di + 8) if indexed else 0
+    kbytes = cfg.index_key_bytes           # one index key: payload + scales
+    qbytes = kbytes + 4                     # one query head: payload + scales + weight
+    q_side = T * Hi * qbytes if indexed else 0
     sel_bytes = 4 * T * k if indexed else 0   # the selection array the attention reads
     mask_bytes = 4 * T * kb if mode in ("reindex", "hier_full") else 0
     if mode == "reindex":
@@ -138,7 +140,7 @@ def work_model(cfg, x, topk_idx: np.ndarray):
         ranked = int(nv.clip(max=cfg.score_stride).sum())
     st = {
         "rope": 8 * T * R + 4 * T,   # read + write cos and sin rows (R/2 FP32 each), positions
-        "index": idx_keys * (Di + 4) + q_side + 4 * scored + mask_bytes * (mode == "reindex"),
+        "index": idx_keys * kbytes + q_side + 4 * scored + mask_bytes * (mode == "reindex"),
         "topk": 4 * ranked + 8 * T * k + mask_bytes * (mode == "reindex"),
         "attn": kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + sel_bytes + 4 * T * R,
     }
@@ -146,7 +148,7 @@ def work_model(cfg, x, topk_idx: np.ndarray):
         st["cand"] = 4 * int(nv.clip(max=cfg.score_stride).sum()) + mask_bytes
     if not indexed:
         st = {"rope": st["rope"], "attn": st["attn"]}
-    step = (idx_keys * (Di + 4) + kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + q_side
+    step = (idx_keys * kbytes + kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + q_side
             + 2 * sel_bytes + 4 * T * R + mask_bytes)
     flops = {"attn": pairs * H * D * 4,
              "index": int(sum(nv[t] for t in range(T))) * Hi * Di * 2}
@@ -218,7 +220,14 @@ def cpu_baseline(cfg, x, budget_s: float):
         oracle.materialize_rope_rows(sub["freqs_cos"], sub["freqs_sin"], sub["position_ids"], n,
                                      rc, rs)
         b_ = time.perf_counter()
-        if mode in ("csa", "hier_full"):
+        if mode in ("csa", "hier_full") and cfg.index_format == "mxfp4":
+            s, _ = oracle.index_scores_mxfp4(sub["q_idx"], sub["q_scale"], sub["head_w"],
+                                             sub["idx_kv"], sub["idx_scale"],
+                                             sub["cmp_block_table"], sub["query_start_loc"],
+                                             sub["positions"], n, cfg.ratio, cfg.score_stride)
+            c_ = time.perf_counter()
+            idx, _, _ = oracle.topk(s, sub["positions"], cfg.ratio, n, cfg.k)
+        elif mode in ("csa", "hier_full"):
             s, _ = oracle.index_scores(sub["q_idx"], sub["q_scale"], sub["head_w"], sub["idx_kv"],
                                        sub["idx_scale"], sub["cmp_block_table"],
                                        sub["query_start_loc"], sub["positions"], n, cfg.ratio,
@@ -286,7 +295,7 @@ def main():
     shared = {n: first.t[n] for n in shared_names}
     idx_touch = (cfg.T * cfg.cand_kb * cfg.cand_block if cfg.mode == "reindex"
                  else cfg.B * cfg.n_cmp_per_request)
-    per_copy_touch = (idx_touch * (cfg.Di + 4) +
+    per_copy_touch = (idx_touch * cfg.index_key_bytes +
                       cfg.T * (cfg.k + cfg.W) * 2 * cfg.D + 4 * cfg.T * cfg.H * cfg.D)
     if args.warm:
         copies = 1
@@ -382,12 +391,15 @@ def main():
         "metric": "CSA decode rows/s per layer + achieved HBM GB/s (% of MI355X peak)",
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8+bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4+bf16" if cfg.index_format == "mxfp4" else "int8+bf16",
+        "data": "synthetic",
         "config": {"workload": cfg.name, "rows": cfg.T, "requests": cfg.B, "heads": cfg.H,
                    "head_dim": cfg.D, "ratio": cfg.ratio, "top_k": cfg.k, "window": cfg.W,
                    "compressed_rows_per_request": cfg.n_cmp_per_request,
-                   "indexer": (f"{cfg.Hi}x{cfg.Di}" if first.mode in ("csa", "reindex", "hier_full")
-                               else "none"),
+                   "indexer": ((f"{cfg.Hi}x{cfg.Di}" +
+                                (" mxfp4" if cfg.index_format == "mxfp4" else " int8"))
+                               if first.mode in ("csa", "reindex", "hier_full") else "none"),
                    "selection": {"csa": "indexer top-k", "hca": "every visible compressed row",
                                  "swa": "window only",
                                  "reindex": f"indexer top-k inside {cfg.cand_kb} candidate blocks "

@@ -42,6 +42,8 @@ _SIGS = {
                                               _I32, _P, _I32, _P, _I32, _I32, _P, _F32, _P, _P,
                                               _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P,
                                               _P]),
+    "csa_index_score_mxfp4": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I32,
+                                             _I32, _I32, _I32, _I32, _I32, _P, _I64, _P, _P]),
     "csa_candidate_blocks_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I32]),
     "csa_candidate_blocks": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                             _SZ, _P, _P]),
@@ -139,6 +141,20 @@ def csa_index_score(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table, quer
         _ptr(positions), query_start_loc.shape[0] - 1, T, int(num_tokens), Hi, Di, int(ratio),
         _ptr(scores), scores.shape[1], _ptr(err), _stream(stream))
     _check(st, "csa_index_score")
+
+
+def csa_index_score_mxfp4(q_fp4, q_sc, head_w, idx_fp4, idx_sc, block_table, query_start_loc,
+                          positions, num_tokens, ratio, scores, err=None, stream=None) -> None:
+    _need(q_fp4, (torch.uint8,), 3, "q_fp4")
+    _need(idx_fp4, (torch.uint8,), 3, "idx_fp4")
+    _need(scores, (torch.float32,), 2, "scores")
+    T, Hi, Db = q_fp4.shape
+    st = load().csa_index_score_mxfp4(
+        _ptr(q_fp4), _ptr(q_sc), _ptr(head_w), _ptr(idx_fp4), _ptr(idx_sc), idx_fp4.shape[0],
+        _ptr(block_table), block_table.shape[1], _ptr(query_start_loc), _ptr(positions),
+        query_start_loc.shape[0] - 1, T, int(num_tokens), Hi, 2 * Db, int(ratio), _ptr(scores),
+        scores.shape[1], _ptr(err), _stream(stream))
+    _check(st, "csa_index_score_mxfp4")
 
 
 def csa_topk_workspace_bytes(T: int, score_stride: int, k: int) -> int:

@@ -121,7 +121,14 @@ __device__ __forceinline__ float lane_add_swap32(float x, float y) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int KK>
+// FP4: the MXFP4 index plane -- query and key rows are packed E2M1 (Di/2
+// bytes) and the FP32 scale slots hold four E8M0 bytes, one per 32 dims; the
+// dots run on the scaled FP4 MFMA with those bytes as its block scales.
+__device__ __forceinline__ v8i lo_v8i(v4i x) {
+  return __builtin_shufflevector(x, v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int KK, bool FP4>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) index_score_kernel(
     const int8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ head_w, const int8_t* __restrict__ idx_kv,
@@ -267,9 +274,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   // (col, half) is head mt*32 + 8*(j/4) + 4*half + j%4), loaded once, after
   // the first pages' loads are issued
   constexpr int MT = 2;
-  constexpr int KS = 2 * KK;
+  // k-steps of 32 bytes: 32 INT8 dims, or 64 FP4 dims (32x32x64 MFMA)
+  constexpr int KS = FP4 ? KK : 2 * KK;
+  const int RB = FP4 ? Di / 2 : Di;   // bytes per query / key row
   v4i qa[MT][KS];
   float ww[MT][16];
+  int sa[MT][KS];   // FP4: the E8M0 byte of lane (col, half)'s 32 dims
   auto load_query = [&]() {
     if (!active) return;
 #pragma unroll
@@ -278,17 +288,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int off = ks * 32 + half * 16;
-        qa[mt][ks] = (h < Hi && off < Di)
+        qa[mt][ks] = (h < Hi && off < RB)
                          ? *reinterpret_cast<const v4i*>(
-                               q_idx + (static_cast<long long>(my_t) * Hi + h) * Di + off)
+                               q_idx + (static_cast<long long>(my_t) * Hi + h) * RB + off)
                          : v4i{0, 0, 0, 0};
+      }
+      if constexpr (FP4) {
+        const uint32_t qsw =
+            h < Hi ? __float_as_uint(q_scale[static_cast<long long>(my_t) * Hi + h]) : 0u;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sa[mt][ks] = (qsw >> (8 * (ks * 2 + half))) & 0xff;
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-        // times 2^21: the epilogue's ReLU leaves dot * 2^-21 (see mfma_tile)
-        ww[mt][j] = (hh < Hi) ? head_w[static_cast<long long>(my_t) * Hi + hh] *
-                                    q_scale[static_cast<long long>(my_t) * Hi + hh] * 2097152.0f
+        // INT8: times 2^21, as the epilogue's ReLU leaves dot * 2^-21 (see
+        // the page loop); FP4: the scales are inside the MFMA
+        ww[mt][j] = (hh < Hi) ? (FP4 ? head_w[static_cast<long long>(my_t) * Hi + hh]
+                                     : head_w[static_cast<long long>(my_t) * Hi + hh] *
+                                           q_scale[static_cast<long long>(my_t) * Hi + hh] *
+                                           2097152.0f)
                               : 0.0f;
       }
     }
@@ -317,15 +336,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     int8_t* keys = keys_of(stg);
     float* ksd = ks_of(stg);
     const int blk = blk_s[pi];
-    const int8_t* pbase = idx_kv + static_cast<long long>(blk < 0 ? 0 : blk) * kPage * Di;
+    const int8_t* pbase = idx_kv + static_cast<long long>(blk < 0 ? 0 : blk) * kPage * RB;
 #pragma unroll
     for (int u = 0; u < kLoadsPerWave; ++u) {
       const int ins = wave * kLoadsPerWave + u;
       const int q = ins * 64 + lane;
       const int key = q >> 3;
       int c = (q & 7) ^ ((key >> 1) & 7);
-      if (c * 16 >= Di) c = 0;   // padding slot: any bytes of the same key
-      const int8_t* src = blk >= 0 ? pbase + key * Di + c * 16 : q_idx;
+      if (c * 16 >= RB) c = 0;   // padding slot: any bytes of the same key
+      const int8_t* src = blk >= 0 ? pbase + key * RB + c * 16 : q_idx;
       __builtin_amdgcn_global_load_lds(
           src, (__attribute__((address_space(3))) void*)(keys + ins * 1024), 16, 0, 0);
     }
@@ -365,6 +384,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       // other waves fill that wait.  One set of B registers per key tile.
       float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       v4i bk[KS];
+      int sb[KS];
       v16i acc;
       auto load_b = [&](int nt) {
         const int kj = nt * 32 + col;
@@ -372,6 +392,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         for (int ks = 0; ks < KS; ++ks)
           bk[ks] = *reinterpret_cast<const v4i*>(
               keys + kj * kRowBytes + swz_chunk(kj, ks * 2 + half) * 16);
+        if constexpr (FP4) {
+          const uint32_t kw = __float_as_uint(ksd[kj]);
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) sb[ks] = (kw >> (8 * (ks * 2 + half))) & 0xff;
+        }
       };
       // The accumulators start at 0x40800000, the bits of 4.0f.  A dot
       // product of Di <= 128 INT8 pairs lies in [-2^21, 2^21], so the INT32
@@ -387,15 +412,29 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         if ((p & 1) == 0) load_b(p >> 1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[p & 1][ks], bk[ks],
-                                                      ks == 0 ? kBiasV : acc, 0, 0, 0);
         float xs = x[p >> 1];
+        if constexpr (FP4) {
+          // FP32 dots of the dequantised rows (E2M1 values, E8M0 scales of
+          // each 32 dims applied by the MFMA); ReLU and the head weight
+          const v16f zero16 = {};
+          v16f accf;
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          xs = fmaf(ww[p & 1][j],
-                    __builtin_amdgcn_fmed3f(__int_as_float(acc[j]) - 4.0f, 0.0f, 1.0f), xs);
+          for (int ks = 0; ks < KS; ++ks)
+            accf = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                lo_v8i(qa[p & 1][ks]), lo_v8i(bk[ks]), ks == 0 ? zero16 : accf, 4, 4, 0,
+                sa[p & 1][ks], 0, sb[ks]);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) xs = fmaf(ww[p & 1][j], fmaxf(accf[j], 0.0f), xs);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[p & 1][ks], bk[ks],
+                                                        ks == 0 ? kBiasV : acc, 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            xs = fmaf(ww[p & 1][j],
+                      __builtin_amdgcn_fmed3f(__int_as_float(acc[j]) - 4.0f, 0.0f, 1.0f), xs);
+        }
         x[p >> 1] = xs;
       }
       // head sums: lanes l and l + 32 hold the two 32-head halves of the
@@ -403,8 +442,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       // with key l of this page, of w1 with key 64 + l
       w0 = lane_add_swap32(x[0], x[1]);
       w1 = lane_add_swap32(x[2], x[3]);
-      w0 = (c0 + lane < my_n) ? ksd[lane] * w0 : neg_inf;
-      w1 = (c0 + 64 + lane < my_n) ? ksd[64 + lane] * w1 : neg_inf;
+      w0 = (c0 + lane < my_n) ? (FP4 ? w0 : ksd[lane] * w0) : neg_inf;
+      w1 = (c0 + 64 + lane < my_n) ? (FP4 ? w1 : ksd[64 + lane] * w1) : neg_inf;
       if (w0 == 0.0f) w0 = 0.0f;   // one zero: +0.0
       if (w1 == 0.0f) w1 = 0.0f;
     }
@@ -642,12 +681,12 @@ extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const 
   dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(groups));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (Di <= 64) {
-    hipLaunchKernelGGL(csa::index_score_kernel<1>, grid, dim3(csa::kThreads), 0, st, q_idx,
+    hipLaunchKernelGGL((csa::index_score_kernel<1, false>), grid, dim3(csa::kThreads), 0, st, q_idx,
                        q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table, max_blocks,
                        query_start_loc, positions, B, num_tokens, Hi, Di, ratio, scores,
                        static_cast<long long>(score_stride), static_cast<int>(ppw), err);
   } else {
-    hipLaunchKernelGGL(csa::index_score_kernel<2>, grid, dim3(csa::kThreads), 0, st, q_idx,
+    hipLaunchKernelGGL((csa::index_score_kernel<2, false>), grid, dim3(csa::kThreads), 0, st, q_idx,
                        q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table, max_blocks,
                        query_start_loc, positions, B, num_tokens, Hi, Di, ratio, scores,
                        static_cast<long long>(score_stride), static_cast<int>(ppw), err);
@@ -693,5 +732,46 @@ extern "C" int csa_index_score_candidates(
                        query_start_loc, positions, B, num_tokens, Hi, Di, ratio, cand_blocks, kb,
                        block, cand_scores, static_cast<long long>(cand_stride), cand_count, err);
   }
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+extern "C" int csa_index_score_mxfp4(const uint8_t* q_fp4, const uint8_t* q_sc,
+                                     const float* head_w, const uint8_t* idx_fp4,
+                                     const uint8_t* idx_sc, int32_t num_blocks,
+                                     const int32_t* block_table, int32_t max_blocks,
+                                     const int32_t* query_start_loc, const int32_t* positions,
+                                     int32_t B, int32_t T, int32_t num_tokens, int32_t Hi,
+                                     int32_t Di, int32_t ratio, float* scores,
+                                     int64_t score_stride, int32_t* err, void* stream) {
+  if (T < 0 || B < 0 || num_blocks < 0 || max_blocks < 0 || score_stride < 0) return CSA_ERR_SHAPE;
+  if (num_tokens < 0 || num_tokens > T || ratio < 1) return CSA_ERR_RANGE;
+  if (num_tokens == 0 || score_stride == 0) return CSA_OK;
+  if (!q_fp4 || !q_sc || !head_w || !query_start_loc || !positions || !scores)
+    return CSA_ERR_NULL;
+  if (num_blocks > 0 && max_blocks > 0 && B > 0 && (!idx_fp4 || !idx_sc || !block_table))
+    return CSA_ERR_NULL;
+  if (Hi < 1 || Hi > 64 || Di != 128) return CSA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(q_fp4) | reinterpret_cast<uintptr_t>(idx_fp4) |
+       reinterpret_cast<uintptr_t>(q_sc) | reinterpret_cast<uintptr_t>(idx_sc)) & 15)
+    return CSA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(num_blocks) * csa::kPage * Di >= (1ll << 40)) return CSA_ERR_SHAPE;
+  const long long pages = (score_stride + csa::kPage - 1) / csa::kPage;
+  const long long groups = (num_tokens + 3) / 4 + B;
+  constexpr long long kSlots = 3 * 256;
+  const long long groups_est = std::max<long long>((num_tokens + 3) / 4, std::min(B, num_tokens));
+  long long ppw = (pages * groups_est + kSlots - 1) / kSlots;
+  if (ppw < 1) ppw = 1;
+  if (ppw > csa::kMaxPPW) ppw = csa::kMaxPPW;
+  const long long gx = (pages + ppw - 1) / ppw;
+  if (gx > 0x7fffffffll || groups > 65535) return CSA_ERR_UNSUPPORTED;
+  dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(groups));
+  // the E8M0 bytes of a row (Di / 32 = 4) travel in the FP32 scale slots
+  hipLaunchKernelGGL((csa::index_score_kernel<2, true>), grid, dim3(csa::kThreads), 0,
+                     static_cast<hipStream_t>(stream), reinterpret_cast<const int8_t*>(q_fp4),
+                     reinterpret_cast<const float*>(q_sc), head_w,
+                     reinterpret_cast<const int8_t*>(idx_fp4),
+                     reinterpret_cast<const float*>(idx_sc), num_blocks, block_table, max_blocks,
+                     query_start_loc, positions, B, num_tokens, Hi, Di, ratio, scores,
+                     static_cast<long long>(score_stride), static_cast<int>(ppw), err);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }

@@ -29,7 +29,8 @@ class CsaStep:
                  rope_offset: int, softmax_scale: float, num_tokens: Optional[int] = None,
                  prefill: bool = False, device: str = "cuda", with_values: bool = True,
                  with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None,
-                 mode: str = "csa", cand_kb: int = 0, cand_block: int = 8):
+                 mode: str = "csa", cand_kb: int = 0, cand_block: int = 8,
+                 index_format: str = "int8"):
         # mode "csa": indexer scores and top-k select the compressed rows;
         # "hca": no indexer, every visible compressed row (k bounds them);
         # "swa": the window alone (k = 0); "reindex": scores and top-k only
@@ -41,6 +42,11 @@ class CsaStep:
         if mode in ("reindex", "hier_full") and cand_kb < 1:
             raise ValueError(f"mode {mode!r} needs cand_kb >= 1")
         self.mode = mode
+        if index_format not in ("int8", "mxfp4"):
+            raise ValueError(f"unknown index format {index_format!r}")
+        if index_format == "mxfp4" and mode == "reindex":
+            raise ValueError("the reindex scorer takes the INT8 index plane")
+        self.index_format = index_format
         self.ratio, self.k, self.window = int(ratio), int(k), int(window)
         self.rope_offset, self.softmax_scale = int(rope_offset), float(softmax_scale)
         self.prefill = prefill
@@ -97,6 +103,12 @@ class CsaStep:
                 self.ratio, self.cand_blocks, self.cand_block, self.scores, self.cand_count,
                 err=self.err, stream=stream)
             return
+        if self.index_format == "mxfp4":
+            _lib.csa_index_score_mxfp4(t["q_idx"], t["q_scale"], t["head_w"], t["idx_kv"],
+                                       t["idx_scale"], t["cmp_block_table"],
+                                       t["query_start_loc"], t["positions"], self.num_tokens,
+                                       self.ratio, self.scores, err=self.err, stream=stream)
+            return
         _lib.csa_index_score(t["q_idx"], t["q_scale"], t["head_w"], t["idx_kv"], t["idx_scale"],
                              t["cmp_block_table"], t["query_start_loc"], t["positions"],
                              self.num_tokens, self.ratio, self.scores, err=self.err,
@@ -148,4 +160,5 @@ def step_for_config(cfg, arrays: Dict[str, np.ndarray], **kw) -> CsaStep:
     return CsaStep(arrays, ratio=cfg.ratio, k=cfg.k, window=cfg.W, rope_offset=cfg.rope_offset,
                    softmax_scale=cfg.softmax_scale, prefill=(cfg.T > 256),
                    mode=getattr(cfg, "mode", "csa"), cand_kb=getattr(cfg, "cand_kb", 0),
-                   cand_block=getattr(cfg, "cand_block", 8), **kw)
+                   cand_block=getattr(cfg, "cand_block", 8),
+                   index_format=getattr(cfg, "index_format", "int8"), **kw)

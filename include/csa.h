@@ -254,6 +254,34 @@ int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const floa
                             size_t workspace_bytes, int32_t* err, void* stream);
 
 /*
+ * csa_index_score_mxfp4 -- csa_index_score with the FP4 index plane
+ * ([V41] cache ABI: index keys packed MXFP4 E2M1 with group-of-32 E8M0
+ * scales; [ATOM] "Current execution scope": the FP4 index arithmetic is E2M1
+ * with one E8M0 scale per 32 dims).  The query side uses the same format, and
+ * the score is
+ *     score[t,c] = sum_h w[t,h] * relu( <mx(q[t,h]), mx(k[c])> )
+ * where mx() multiplies each E2M1 value by 2^(s - 127), s the E8M0 byte of its
+ * group of 32 dims.  Visibility, metadata, flags and the output layout are
+ * csa_index_score's.
+ *
+ *   q_fp4    UINT8 [T, Hi, Di/2]: packed E2M1, the lower-indexed element of a
+ *            pair in bits 0-3
+ *   q_sc     UINT8 [T, Hi, Di/32]: E8M0 scales of the query rows
+ *   head_w   FP32 [T, Hi]
+ *   idx_fp4  UINT8 [num_blocks, 128, Di/2]; idx_sc UINT8 [num_blocks, 128,
+ *            Di/32]: the key pool, paged like csa_index_score's
+ *
+ * Supported: Di = 128, Hi <= 64; q_fp4, q_sc, idx_fp4, idx_sc 16-byte
+ * aligned.  The dots run on gfx950's block-scaled FP4 MFMA in FP32.
+ */
+int csa_index_score_mxfp4(const uint8_t* q_fp4, const uint8_t* q_sc, const float* head_w,
+                          const uint8_t* idx_fp4, const uint8_t* idx_sc, int32_t num_blocks,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* query_start_loc, const int32_t* positions, int32_t B,
+                          int32_t T, int32_t num_tokens, int32_t Hi, int32_t Di, int32_t ratio,
+                          float* scores, int64_t score_stride, int32_t* err, void* stream);
+
+/*
  * Hierarchical selection ([V41] "Decode composition"): a full layer publishes
  * a candidate mask of blocks of `block` consecutive compressed positions
  * (2,048 blocks of eight in V4.1); a later reindex layer scores only the

@@ -47,6 +47,14 @@ class CsaConfig:
     mode: str = "csa"
     cand_kb: int = 0
     cand_block: int = 8
+    # index plane: "int8" (INT8 keys and query, FP32 per-row scales) or
+    # "mxfp4" (packed E2M1 keys and query, one E8M0 scale per 32 dims)
+    index_format: str = "int8"
+
+    @property
+    def index_key_bytes(self) -> int:
+        """Bytes of one index key (payload + scales)."""
+        return self.Di // 2 + self.Di // 32 if self.index_format == "mxfp4" else self.Di + 4
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -166,9 +174,24 @@ C9 = _decode(
     "2048) plus 2,048 blocks of 8 per row",
     n_req=4, s=2, context=131072, ratio=1, k=2048, mode="hier_full", cand_kb=2048)
 
-CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8, C9)}
+# The FP4 index plane of the production cache ABI (pypto-lib "DeepSeek V4.1
+# Flash": index keys packed MXFP4 E2M1 with group-of-32 E8M0 scales) on the
+# max-context and the ratio-2 decode shapes.
+C10 = _decode(
+    "c10_maxctx_mxfp4_decode",
+    "max-context ratio-1 decode with the MXFP4 index plane: C5's shapes, index keys "
+    "and queries packed E2M1 with one E8M0 scale per 32 dims (68 bytes per key)",
+    n_req=2, s=4, context=1 << 20, ratio=1, k=2048, shared_pool=True, index_format="mxfp4")
+
+C11 = _decode(
+    "c11_ratio2_mxfp4_decode",
+    "V4.1 ratio-2 decode with the MXFP4 index plane: C2's shapes",
+    n_req=4, s=2, context=32768, ratio=2, k=512, index_format="mxfp4")
+
+CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8, C9, C10,
+                                                     C11)}
 SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7, "c8": C8,
-         "c9": C9}
+         "c9": C9, "c10": C10, "c11": C11}
 
 
 def get(name: str) -> CsaConfig:

@@ -39,7 +39,7 @@ from .configs import PAGE, CsaConfig
 _TENSOR_IDS = {
     "q": 1, "cmp_kv": 2, "win_kv": 3, "q_idx_f": 4, "head_w": 5, "idx_kv": 6,
     "idx_scale": 7, "outlier": 8, "attn_sink": 9, "cmp_perm": 10, "win_perm": 11,
-    "cand_blocks": 12,
+    "cand_blocks": 12, "q_fp4": 13, "q_e8m0": 14, "idx_fp4": 15, "idx_e8m0": 16,
 }
 
 _CHUNK_ELEMS = 1 << 24  # fixed chunk so the draws never depend on the caller
@@ -152,6 +152,17 @@ def make_inputs(cfg: CsaConfig, seed: int = 0, with_tables: bool = True) -> CsaI
         hit = _rng(seed, "outlier").random((nbc, PAGE)) < cfg.outlier_frac
         sc = np.where(hit, sc * np.float32(4.0), sc).astype(np.float32)
     t["idx_scale"] = sc
+    if cfg.index_format == "mxfp4":
+        # the FP4 plane replaces the INT8 one (same names): packed E2M1 codes,
+        # every nibble uniform over the 16 codes, and E8M0 group scales
+        # 2^-6 .. 2^1 (bytes 121 .. 128)
+        t["q_idx"] = _rng(seed, "q_fp4").integers(0, 256, size=(T, Hi, Di // 2), dtype=np.uint8)
+        t["q_scale"] = _rng(seed, "q_e8m0").integers(121, 129, size=(T, Hi, Di // 32),
+                                                     dtype=np.uint8)
+        t["idx_kv"] = _rng(seed, "idx_fp4").integers(0, 256, size=(nbc, PAGE, Di // 2),
+                                                     dtype=np.uint8)
+        t["idx_scale"] = _rng(seed, "idx_e8m0").integers(121, 129, size=(nbc, PAGE, Di // 32),
+                                                         dtype=np.uint8)
 
     # ---- window pool: only the pages some window touches are backed
     wpages = cfg.win_pages_per_request

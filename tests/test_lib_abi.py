@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "csa.h")
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(csa_[a-z0-9_]+)\s*\(", txt)))
 
 
 @pytest.fixture(scope="module")
