@@ -152,6 +152,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
+  // direct-to-LDS loads per wave per page (FP4 rows take 64 LDS bytes, INT8
+  // rows 128), and vector-memory operations per page with the scale load
+  constexpr int LPWv = FP4 ? kLoadsPerWave / 2 : kLoadsPerWave;
+  constexpr int VMPv = LPWv + 1;
   const long long stride_pages = (stride + kPage - 1) / kPage;
   const int page0 = blockIdx.x * pages_per_wg;
   const int npages = static_cast<int>(min(static_cast<long long>(pages_per_wg),
@@ -317,9 +321,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   // ---- page pi -> LDS stage pi % kStages with direct-to-LDS loads.  LDS
   //      slot q of a page holds 16-byte chunk (q & 7) ^ ((key >> 1) & 7) of key
   //      q >> 3 (the XOR swizzle that makes the operand reads conflict-free),
-  //      so each lane picks its source chunk.  Every wave issues exactly
-  //      kLoadsPerWave + 1 loads per page (pages with nothing to stage read a
-  //      dummy 16 bytes), which keeps the vmcnt bookkeeping uniform.
+  //      so each lane picks its source chunk.  FP4 rows are 64 bytes: slot q
+  //      holds chunk (q & 3) ^ ((key >> 2) & 3) of key q >> 2, so sixteen
+  //      lanes reading one chunk of sixteen keys touch sixteen different
+  //      16-byte bank groups.  Every wave issues exactly LPWv + 1 loads per
+  //      page (pages with nothing to stage read a dummy 16 bytes), which keeps
+  //      the vmcnt bookkeeping uniform.
   auto keys_of = [&](auto stg) -> int8_t* {
     constexpr int S = decltype(stg)::value;
     if constexpr (S == 0) return keys0;
@@ -338,12 +345,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const int blk = blk_s[pi];
     const int8_t* pbase = idx_kv + static_cast<long long>(blk < 0 ? 0 : blk) * kPage * RB;
 #pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) {
-      const int ins = wave * kLoadsPerWave + u;
+    for (int u = 0; u < LPWv; ++u) {
+      const int ins = wave * LPWv + u;
       const int q = ins * 64 + lane;
-      const int key = q >> 3;
-      int c = (q & 7) ^ ((key >> 1) & 7);
-      if (c * 16 >= RB) c = 0;   // padding slot: any bytes of the same key
+      int key, c;
+      if constexpr (FP4) {   // 64-byte rows: four chunks per key
+        key = q >> 2;
+        c = (q & 3) ^ ((key >> 2) & 3);
+      } else {
+        key = q >> 3;
+        c = (q & 7) ^ ((key >> 1) & 7);
+        if (c * 16 >= RB) c = 0;   // padding slot: any bytes of the same key
+      }
       const int8_t* src = blk >= 0 ? pbase + key * RB + c * 16 : q_idx;
       __builtin_amdgcn_global_load_lds(
           src, (__attribute__((address_space(3))) void*)(keys + ins * 1024), 16, 0, 0);
@@ -367,7 +380,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     // (its lane for key 0 is always inside the row), so only it is counted:
     // counting too few ops just waits a little longer.
     const int newer = min(kStages - 2, npages - 1 - pi);
-    wait_vm_rt(__builtin_amdgcn_readfirstlane(kVmPerPage * newer +
+    wait_vm_rt(__builtin_amdgcn_readfirstlane(VMPv * newer +
                                               (active ? min(kStages - 1, pi) : 0)));
     lds_barrier();
     if (pi + kStages - 1 < npages)
@@ -390,8 +403,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
         const int kj = nt * 32 + col;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          bk[ks] = *reinterpret_cast<const v4i*>(
-              keys + kj * kRowBytes + swz_chunk(kj, ks * 2 + half) * 16);
+          bk[ks] = FP4 ? *reinterpret_cast<const v4i*>(
+                             keys + kj * 64 + (((ks * 2 + half) ^ ((kj >> 2) & 3)) * 16))
+                       : *reinterpret_cast<const v4i*>(
+                             keys + kj * kRowBytes + swz_chunk(kj, ks * 2 + half) * 16);
         if constexpr (FP4) {
           const uint32_t kw = __float_as_uint(ksd[kj]);
 #pragma unroll
