@@ -146,6 +146,31 @@ __device__ int block_excl_scan_lds(int v, int* wsum, int* total) {
   return before + incl - v;
 }
 
+// ds_read_b128 of K step `step` (64 bytes apart) as an inline instruction with
+// an immediate offset; `step` is a compile-time constant after unrolling, so
+// the switch folds away.
+__device__ __forceinline__ void lds_read128_step(v4i& d, uint32_t addr, int step) {
+  switch (step) {
+    case 0: asm volatile("ds_read_b128 %0, %1 offset:0" : "=v"(d) : "v"(addr)); break;
+    case 1: asm volatile("ds_read_b128 %0, %1 offset:64" : "=v"(d) : "v"(addr)); break;
+    case 2: asm volatile("ds_read_b128 %0, %1 offset:128" : "=v"(d) : "v"(addr)); break;
+    case 3: asm volatile("ds_read_b128 %0, %1 offset:192" : "=v"(d) : "v"(addr)); break;
+    case 4: asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(d) : "v"(addr)); break;
+    case 5: asm volatile("ds_read_b128 %0, %1 offset:320" : "=v"(d) : "v"(addr)); break;
+    case 6: asm volatile("ds_read_b128 %0, %1 offset:384" : "=v"(d) : "v"(addr)); break;
+    case 7: asm volatile("ds_read_b128 %0, %1 offset:448" : "=v"(d) : "v"(addr)); break;
+    case 8: asm volatile("ds_read_b128 %0, %1 offset:512" : "=v"(d) : "v"(addr)); break;
+    case 9: asm volatile("ds_read_b128 %0, %1 offset:576" : "=v"(d) : "v"(addr)); break;
+    case 10: asm volatile("ds_read_b128 %0, %1 offset:640" : "=v"(d) : "v"(addr)); break;
+    case 11: asm volatile("ds_read_b128 %0, %1 offset:704" : "=v"(d) : "v"(addr)); break;
+    case 12: asm volatile("ds_read_b128 %0, %1 offset:768" : "=v"(d) : "v"(addr)); break;
+    case 13: asm volatile("ds_read_b128 %0, %1 offset:832" : "=v"(d) : "v"(addr)); break;
+    case 14: asm volatile("ds_read_b128 %0, %1 offset:896" : "=v"(d) : "v"(addr)); break;
+    case 15: asm volatile("ds_read_b128 %0, %1 offset:960" : "=v"(d) : "v"(addr)); break;
+    default: asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(addr + 64 * step)); break;
+  }
+}
+
 template <int LPW>
 __device__ __forceinline__ void wait_tiles_behind(int behind) {
   // at most `behind` later tiles (LPW loads each) may still be in flight
@@ -416,15 +441,26 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
         step_sync(k, sl);
         if (k >= ntiles) return;
         const uint8_t* tile = slot_of(sl);
-        constexpr int PF = 4;   // K steps read ahead
+        // K reads PF steps ahead of their MFMAs.  They are issued as inline
+        // ds_read_b128 with explicit partial lgkmcnt waits: the compiler
+        // counts the direct-to-LDS gathers in flight as pending LDS work and
+        // would wait for every outstanding read (lgkmcnt(0)) before each use.
+        // The wait takes the read registers as operands, which orders every
+        // MFMA after the wait for its operands; PF + 1 register slots keep a
+        // new read off the registers the previous MFMA pair read.
+        constexpr int PF = KS < 4 ? KS : 4;
+        constexpr int NB = PF + 1;
         const int krow = (col >> 2) + 4 * (col & 3);
-        const uint8_t* k0p = tile + row_off(krow) + grp * 16;
-        const uint8_t* k1p = tile + row_off(16 + krow) + grp * 16;
-        v4i kb0[PF], kb1[PF];
+        const uint32_t a0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) const uint8_t*)(tile + row_off(krow) + grp * 16)));
+        const uint32_t a1 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) const uint8_t*)(tile + row_off(16 + krow) +
+                                                                grp * 16)));
+        v4i kb0[NB], kb1[NB];
 #pragma unroll
-        for (int i = 0; i < PF && i < KS; ++i) {
-          kb0[i] = *reinterpret_cast<const v4i*>(k0p + i * 64);
-          kb1[i] = *reinterpret_cast<const v4i*>(k1p + i * 64);
+        for (int i = 0; i < PF; ++i) {
+          lds_read128_step(kb0[i], a0, i);
+          lds_read128_step(kb1[i], a1, i);
         }
         // two accumulators per M tile (even and odd K steps) keep the
         // dependent MFMA chains short
@@ -433,23 +469,23 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
         for (int i = 0; i < 2; ++i) sacc[i][0] = sacc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const v4i x0 = kb0[ks % PF], x1 = kb1[ks % PF];
-          if (ks + PF < KS) {
-            kb0[ks % PF] = *reinterpret_cast<const v4i*>(k0p + (ks + PF) * 64);
-            kb1[ks % PF] = *reinterpret_cast<const v4i*>(k1p + (ks + PF) * 64);
+          const int s = ks % NB;
+          // reads issued after this step's two: those of the next PF - 1 steps
+          const int later = 2 * ((KS - 1 - ks) < (PF - 1) ? (KS - 1 - ks) : (PF - 1));
+          switch (later) {
+            case 6: asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(kb0[s]), "+v"(kb1[s])); break;
+            case 4: asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(kb0[s]), "+v"(kb1[s])); break;
+            case 2: asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(kb0[s]), "+v"(kb1[s])); break;
+            default: asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kb0[s]), "+v"(kb1[s])); break;
           }
-          sacc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x0), qf[ks],
+          sacc[0][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(kb0[s]), qf[ks],
                                                                     sacc[0][ks & 1], 0, 0, 0);
-          sacc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(x1), qf[ks],
+          sacc[1][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(kb1[s]), qf[ks],
                                                                     sacc[1][ks & 1], 0, 0, 0);
-        }
-        // keep the K reads PF steps ahead of their MFMAs (left alone, the
-        // scheduler moves each read next to its use)
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (PF < KS ? PF : KS), 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if (ks + PF < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          if (ks + PF < KS) {
+            lds_read128_step(kb0[(ks + PF) % NB], a0, ks + PF);
+            lds_read128_step(kb1[(ks + PF) % NB], a1, ks + PF);
+          }
         }
         const v4f s0 = sacc[0][0] + sacc[0][1];
         const v4f s1 = sacc[1][0] + sacc[1][1];
