@@ -307,12 +307,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       for (int j = 0; j < 16; ++j) {
         const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
         // INT8: times 2^21, as the epilogue's ReLU leaves dot * 2^-21 (see
-        // the page loop); FP4: the scales are inside the MFMA
-        ww[mt][j] = (hh < Hi) ? (FP4 ? head_w[static_cast<long long>(my_t) * Hi + hh]
-                                     : head_w[static_cast<long long>(my_t) * Hi + hh] *
-                                           q_scale[static_cast<long long>(my_t) * Hi + hh] *
-                                           2097152.0f)
-                              : 0.0f;
+        // the page loop); FP4: the scales are inside the MFMA.  The loads
+        // read a valid head for every lane (a head past Hi is dropped by the
+        // select), so they issue together instead of one guarded round trip
+        // each.
+        const long long hc = static_cast<long long>(my_t) * Hi + (hh < Hi ? hh : 0);
+        const float wv = FP4 ? head_w[hc] : head_w[hc] * q_scale[hc] * 2097152.0f;
+        ww[mt][j] = (hh < Hi) ? wv : 0.0f;
       }
     }
   };
@@ -541,9 +542,10 @@ __global__ void __launch_bounds__(kThreads) index_cand_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-      ww[mt][j] = (hh < Hi) ? head_w[static_cast<long long>(t) * Hi + hh] *
-                                  q_scale[static_cast<long long>(t) * Hi + hh] * 2097152.0f
-                            : 0.0f;
+      // unguarded loads of a valid head, then the select (one round trip)
+      const long long hc = static_cast<long long>(t) * Hi + (hh < Hi ? hh : 0);
+      const float wv = head_w[hc] * q_scale[hc] * 2097152.0f;
+      ww[mt][j] = (hh < Hi) ? wv : 0.0f;
     }
   }
   const int b = owner_from_lanes(qsl_v, qsl, B, t);
