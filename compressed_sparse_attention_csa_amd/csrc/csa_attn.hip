@@ -283,12 +283,19 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     for (int j0 = 0, r = 0; j0 < n_my; j0 += kRingThreads, ++r) {
       const int i = i0 + j0 + tid;   // list entry
       uint32_t rr = kNoRow;
+      // each entry names a table and a position; one page lookup serves
+      // both kinds (lookups in two divergent branches cost two round trips)
+      const int32_t* bt_row = nullptr;
+      int lk_pos = 0, lk_max = 0, lk_num = 0;
+      uint32_t lk_bit = 0u;
       if (j0 + tid >= n_my) {
         // past the list: nothing to resolve
       } else if (i < w_len) {
-        const long long r = page_row(a.win_bt + static_cast<long long>(b) * a.max_win_blocks,
-                                     a.max_win_blocks, a.num_win_blocks, w_lo + i);
-        if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
+        bt_row = a.win_bt + static_cast<long long>(b) * a.max_win_blocks;
+        lk_pos = w_lo + i;
+        lk_max = a.max_win_blocks;
+        lk_num = a.num_win_blocks;
+        lk_bit = kWinBit;
       } else {
         const int c = !topk_row ? i - w_len
                       : (spec_ok && r < 2) ? (r == 0 ? c_spec0 : c_spec1) : topk_row[i - w_len];
@@ -296,11 +303,20 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
           if (c >= nv) {
             if (topk_row) ebits |= CSA_EFLAG_TOPK_RANGE;   // past n_vis: not selected
           } else {
-            const long long r = page_row(a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks,
-                                         a.max_cmp_blocks, a.num_cmp_blocks, c);
-            if (r >= 0) rr = static_cast<uint32_t>(r); else ebits |= CSA_EFLAG_BLOCK_RANGE;
+            bt_row = a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks;
+            lk_pos = c;
+            lk_max = a.max_cmp_blocks;
+            lk_num = a.num_cmp_blocks;
           }
         }
+      }
+      const int lk_page = lk_pos / kPage;
+      const int blk = (bt_row && lk_page < lk_max) ? bt_row[lk_page] : -1;
+      if (bt_row) {
+        if (blk >= 0 && blk < lk_num)
+          rr = static_cast<uint32_t>(static_cast<long long>(blk) * kPage + (lk_pos % kPage)) | lk_bit;
+        else
+          ebits |= CSA_EFLAG_BLOCK_RANGE;
       }
       int total = 0;
       const int slot = n_valid + block_excl_scan_lds<kRingWaves>(rr != kNoRow ? 1 : 0, scan_s, &total);
@@ -697,32 +713,17 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   const int h = hg * 16 + col;
   const bool hv = h < a.H;
   if (tid == 0) err_s = 0;
-  // metadata loads first, then the query and rope loads, then the first use
-  // of the metadata (vector memory returns in order).  The selected index of
-  // this thread's entry is fetched with them on the guess that the row's
-  // window is full (position >= window - 1, every row but a request's first
-  // few tokens), which takes a dependent round trip off the resolution.
+  // metadata loads first, then the first use of the metadata.  The selected
+  // index of this thread's entry is fetched with them on the guess that the
+  // row's window is full (position >= window - 1, every row but a request's
+  // first few tokens), which takes a dependent round trip off the
+  // resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
   // (no selection array: the compressed set is every visible row, 0 .. n_vis-1)
   const int32_t* topk_row = a.topk ? a.topk + static_cast<long long>(t) * a.k : nullptr;
   const int i_spec = split * kSpan + tid - a.window;
   const int c_spec = (topk_row && i_spec >= 0 && i_spec < a.k) ? topk_row[i_spec] : -1;
-  // the query and the rope row: in flight during the row resolution, and
-  // complete before the gather is issued (a load issued after the gather
-  // would wait for it)
-  v4i qraw[KS];
-  {
-    const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qraw[ks] = hv ? *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8) : v4i{0, 0, 0, 0};
-  }
-  float rcv = 0.0f, rsv = 0.0f;
-  if (tid < a.half_rope) {
-    rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + tid];
-    rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + tid];
-  }
 
   const int b = owner_from_lanes(qsl_v, a.qsl, a.B, t);
   const int nv = visible_count(p, a.ratio);
@@ -738,32 +739,63 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   // the query loads still streaming in from HBM
   lds_barrier();   // err_s is cleared
 
+  v4i qraw[KS];
+  float rcv = 0.0f, rsv = 0.0f;
   // ---- resolve this span through the block tables; compact valid rows
   int n_valid = 0;
   {
     int ebits = 0;
     if (!topk_row && a.k > 0 && b >= 0 && nv > a.k && split == 0 && tid == 0)
       ebits |= CSA_EFLAG_TOPK_RANGE;   // bound below n_vis (k = 0: the window alone)
+    // each entry names a table and a position; one page lookup serves both
+    // kinds (two lookups in divergent branches would cost two round trips)
     uint32_t rr = kNoRow;
     const int j = tid;
+    const int32_t* bt_row = nullptr;
+    int lk_pos = 0, lk_max = 0, lk_num = 0;
+    uint32_t lk_bit = 0u;
     if (j < n_my) {
       const int i = i_begin + j;
       if (i < w_len) {
-        const long long r = page_row(a.win_bt + static_cast<long long>(b) * a.max_win_blocks,
-                                     a.max_win_blocks, a.num_win_blocks, w_lo + i);
-        if (r >= 0) rr = static_cast<uint32_t>(r) | kWinBit; else ebits |= CSA_EFLAG_BLOCK_RANGE;
+        bt_row = a.win_bt + static_cast<long long>(b) * a.max_win_blocks;
+        lk_pos = w_lo + i;
+        lk_max = a.max_win_blocks;
+        lk_num = a.num_win_blocks;
+        lk_bit = kWinBit;
       } else {
         const int c = !topk_row ? i - w_len : (w_len == a.window) ? c_spec : topk_row[i - w_len];
         if (c >= 0) {
           if (c >= nv) {
             if (topk_row) ebits |= CSA_EFLAG_TOPK_RANGE;   // past n_vis: not selected
           } else {
-            const long long r = page_row(a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks,
-                                         a.max_cmp_blocks, a.num_cmp_blocks, c);
-            if (r >= 0) rr = static_cast<uint32_t>(r); else ebits |= CSA_EFLAG_BLOCK_RANGE;
+            bt_row = a.cmp_bt + static_cast<long long>(b) * a.max_cmp_blocks;
+            lk_pos = c;
+            lk_max = a.max_cmp_blocks;
+            lk_num = a.num_cmp_blocks;
           }
         }
       }
+    }
+    const int lk_page = lk_pos / kPage;
+    const int blk = (bt_row && lk_page < lk_max) ? bt_row[lk_page] : -1;
+    // the query and the rope row, behind the page lookup: unguarded loads of
+    // a valid head (a head past H gets zeros below), so the lookup's wait
+    // does not include them; complete before the gather is issued
+    {
+      const uint16_t* qrow = a.q + (static_cast<long long>(t) * a.H + (hv ? h : 0)) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8);
+    }
+    if (a.half_rope > 0) {   // uniform: no table without a rope span
+      const int rt = tid < a.half_rope ? tid : 0;
+      rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + rt];
+      rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + rt];
+    }
+    if (bt_row) {
+      if (blk >= 0 && blk < lk_num)
+        rr = static_cast<uint32_t>(static_cast<long long>(blk) * kPage + (lk_pos % kPage)) | lk_bit;
+      else
+        ebits |= CSA_EFLAG_BLOCK_RANGE;
     }
     if (ebits && hg == 0) atomicOr(&err_s, ebits);
     int total = 0;
@@ -810,7 +842,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   v8bf qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    v4i raw = qraw[ks];
+    v4i raw = hv ? qraw[ks] : v4i{0, 0, 0, 0};
     const int r0 = ks * 32 + grp * 8 - a.rope_offset;
     if (hv && r0 + 8 > 0 && r0 < 2 * a.half_rope) {
 #pragma unroll
