@@ -1024,7 +1024,11 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
   const int lane = threadIdx.x;
   const float neg_inf = -__builtin_huge_valf();
   const long long tbase = static_cast<long long>(t) * splits;
-  const float2 ml = lane < splits ? part_ml[(tbase + lane) * H + h] : make_float2(neg_inf, 0.0f);
+  // loads read a valid span in every lane (a clamped index) and the select
+  // follows, so they issue together rather than one guarded round trip each
+  float2 ml = part_ml[(tbase + (lane < splits ? lane : 0)) * H + h];
+  if (lane >= splits) ml = make_float2(neg_inf, 0.0f);
+  const float sinkv = sink[h];
   float acc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
@@ -1035,12 +1039,16 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
     for (int u = 0; u < kMergeChunk; ++u) {
       const int sp = s0 + u;
       const long long sl = tbase + (sp < splits ? sp : 0);
-      if constexpr (MANY) cml[u] = sp < splits ? part_ml[sl * H + h] : make_float2(neg_inf, 0.0f);
+      if constexpr (MANY) {
+        cml[u] = part_ml[sl * H + h];
+        if (sp >= splits) cml[u] = make_float2(neg_inf, 0.0f);
+      }
+      // a span past the list reads span 0; its weight is never applied
       const float* po = part_o + (sl * H + h) * D + lane * CPL;
       if constexpr (CPL >= 4) {
 #pragma unroll
         for (int v = 0; v < V4; ++v) {
-          const v4f x = sp < splits ? *reinterpret_cast<const v4f*>(po + 4 * v) : v4f{0.f, 0.f, 0.f, 0.f};
+          const v4f x = *reinterpret_cast<const v4f*>(po + 4 * v);
           chunk[u][4 * v] = x[0];
           chunk[u][4 * v + 1] = x[1];
           chunk[u][4 * v + 2] = x[2];
@@ -1048,19 +1056,17 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) chunk[u][i] = sp < splits ? po[i] : 0.0f;
+        for (int i = 0; i < CPL; ++i) chunk[u][i] = po[i];
       }
     }
   };
   load_chunk(0);
   // running max and denominator over the spans, with the sink
-  const float sink2 = sink[h] * kLog2e;
+  const float sink2 = sinkv * kLog2e;
   float M = ml.x;
   if constexpr (MANY)
     for (int s = lane + 64; s < splits; s += 64) M = fmaxf(M, part_ml[(tbase + s) * H + h].x);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  M = fmaxf(M, sink2);
+  M = fmaxf(wave_max(M), sink2);
   const float w_l = ml.x == neg_inf ? 0.0f : exp2f(ml.x - M);   // lane's span weight
   float z = ml.y * w_l;
   if constexpr (MANY) {
@@ -1069,16 +1075,14 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
       z += m2.x == neg_inf ? 0.0f : m2.y * exp2f(m2.x - M);
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
-  z += exp2f(sink2 - M);
+  z = wave_sum(z) + exp2f(sink2 - M);
   for (int s0 = 0; s0 < splits; s0 += kMergeChunk) {
     if (s0 > 0) load_chunk(s0);
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
       float w;
       if constexpr (MANY) w = cml[u].x == neg_inf ? 0.0f : exp2f(cml[u].x - M);
-      else w = __shfl(w_l, (s0 + u) & 63, 64);
+      else w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), (s0 + u) & 63));
       if (s0 + u < splits) {
 #pragma unroll
         for (int i = 0; i < CPL; ++i) acc[i] += chunk[u][i] * w;

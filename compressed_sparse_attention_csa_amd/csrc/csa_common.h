@@ -121,6 +121,28 @@ __device__ __forceinline__ float sum_xor32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Whole-wave max and sum on the VALU: DPP quad swaps and row mirrors combine
+// the 16 lanes of a row, then the two lane swaps above.  Every lane ends with
+// the same value (each step adds or compares symmetric pairs).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xb1>(v));    // quad_perm 1,0,3,2: lane ^ 1
+  v = fmaxf(v, dpp_f<0x4e>(v));    // quad_perm 2,3,0,1: lane ^ 2
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror: the other quad of 8
+  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror: the other half of 16
+  return max_xor32(max_xor16(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xb1>(v);
+  v += dpp_f<0x4e>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return sum_xor32(sum_xor16(v));
+}
+
 // Work-group barrier that orders LDS only.  A __syncthreads() is a
 // work-group release/acquire and waits for every vector-memory operation in
 // flight (vmcnt(0)), direct-to-LDS loads and prefetches included; here each
