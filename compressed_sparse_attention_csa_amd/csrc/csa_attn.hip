@@ -1061,6 +1061,11 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
     }
   };
   load_chunk(0);
+  // the first chunk's loads are issued before the span statistics are
+  // reduced: these empty instructions consume one value of each span, so
+  // all of them share one memory latency with the statistics' loads
+#pragma unroll
+  for (int u = 0; u < kMergeChunk; ++u) asm volatile("" ::"v"(chunk[u][0]));
   // running max and denominator over the spans, with the sink
   const float sink2 = sinkv * kLog2e;
   float M = ml.x;
