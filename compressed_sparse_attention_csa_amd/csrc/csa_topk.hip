@@ -469,6 +469,8 @@ __device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared
 // counts[t] when counts is given.  A chosen entry i is reported as i, or with
 // remap as remap[t][i / rgroup] * rgroup + i % rgroup (the position of
 // candidate slot i).
+// (The fields are handed on as scalars: a helper that took the struct by
+// address would make the compiler keep it in scratch memory.)
 struct RowSpec {
   const int32_t* positions;
   int ratio;
@@ -477,22 +479,31 @@ struct RowSpec {
   const int32_t* remap;
   int rgroup;
   int rstride;
+};
 
-  __device__ __forceinline__ int span(int t, long long stride, int32_t* err, bool report) const {
-    long long nv;
-    if (counts) {
-      nv = max(0, counts[t]);
-    } else {
-      nv = visible_count(positions[t], ratio);
-      if (group > 1) nv = (nv + group - 1) / group;
-    }
-    if (nv > stride) {
-      if (report) flag_error(err, CSA_EFLAG_POS_RANGE);
-      nv = stride;
-    }
-    return static_cast<int>(nv);
+__device__ __forceinline__ int row_span(const RowSpec rs, int t, long long stride, int32_t* err,
+                                        bool report) {
+  long long nv;
+  if (rs.counts) {
+    nv = max(0, rs.counts[t]);
+  } else {
+    nv = visible_count(rs.positions[t], rs.ratio);
+    if (rs.group > 1) nv = (nv + rs.group - 1) / rs.group;
   }
-  __device__ __forceinline__ int out(int t, int i) const {
+  if (nv > stride) {
+    if (report) flag_error(err, CSA_EFLAG_POS_RANGE);
+    nv = stride;
+  }
+  return static_cast<int>(nv);
+}
+
+// How a chosen entry i of row t is reported (see RowSpec).
+struct Remap {
+  const int32_t* remap;
+  int rgroup;
+  int rstride;
+  int t;
+  __device__ __forceinline__ int operator()(int i) const {
     if (!remap) return i;
     const int q = i / rgroup;
     return remap[static_cast<long long>(t) * rstride + q] * rgroup + (i - q * rgroup);
@@ -504,7 +515,7 @@ struct RowSpec {
 template <int THREADS, int KPT, typename PosFn>
 __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, const float* row,
                          int32_t* out_i, float* out_v, SelShared<THREADS>& sh, PosFn pos,
-                         const RowSpec& rs, int t) {
+                         Remap rm) {
   const uint32_t ck = sh.cut[0], cp = sh.cut[1];
   uint32_t pick = 0u;
 #pragma unroll
@@ -522,7 +533,7 @@ __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, co
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if ((pick >> j) & 1u) {
-      out_i[o] = rs.out(t, pos(j));
+      out_i[o] = rm(pos(j));
       if (out_v) out_v[o] = val[j];
       ++o;
     }
@@ -537,10 +548,10 @@ __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, co
 // Every visible position is chosen: 0 .. n-1 ascending, then padding.
 template <int THREADS>
 __device__ void write_all(int n, int k, const float* row, int32_t* out_i, float* out_v,
-                          const RowSpec& rs, int t) {
+                          Remap rm) {
   const float neg_inf = -__builtin_huge_valf();
   for (int i = threadIdx.x; i < k; i += THREADS) {
-    out_i[i] = i < n ? rs.out(t, i) : -1;
+    out_i[i] = i < n ? rm(i) : -1;
     if (out_v) out_v[i] = i < n ? row[i] : neg_inf;
   }
 }
@@ -550,8 +561,7 @@ __device__ void write_all(int n, int k, const float* row, int32_t* out_i, float*
 // positions: the path for rows whose threshold bin held too many keys.
 template <int THREADS>
 __device__ void select_whole_row(const float* row, int n, int m, int k, int32_t* out_i,
-                                 float* out_v, SelShared<THREADS>& sh, const RowSpec& rs,
-                                 int t) {
+                                 float* out_v, SelShared<THREADS>& sh, Remap rm) {
   const int tid = threadIdx.x;
   int* sel = reinterpret_cast<int*>(sh.list);
   int* sel_count = &sh.sel_count;
@@ -661,7 +671,7 @@ __device__ void select_whole_row(const float* row, int n, int m, int k, int32_t*
   const float neg_inf = -__builtin_huge_valf();
   for (int i = tid; i < k; i += THREADS) {
     const int c = i < m ? sel[i] : -1;
-    out_i[i] = c >= 0 ? rs.out(t, c) : -1;
+    out_i[i] = c >= 0 ? rm(c) : -1;
     if (out_v) out_v[i] = c >= 0 ? row[c] : neg_inf;
   }
 }
@@ -695,12 +705,12 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
     if (4 * i < per && base + 4 * i < span)
       v[i] = *reinterpret_cast<const float4*>(row + base + 4 * i);
   }
-  const int n = rs.span(t, stride, err, tid == 0);
+  const int n = row_span(rs, t, stride, err, tid == 0);
   int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
   float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
   const int m = min(k, n);
   if (m == n) {
-    write_all<THREADS>(n, k, row, out_i, out_v, rs, t);
+    write_all<THREADS>(n, k, row, out_i, out_v, Remap{rs.remap, rs.rgroup, rs.rstride, t});
     return;
   }
   uint32_t key[KPT];
@@ -758,7 +768,7 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
         const int cn = max(0, min(cper, total - cbase));
         auto cpos = [&](int j) { return static_cast<int>(cand_p[cbase + j]); };
         if (find_cut<THREADS, CPT>(ck, cn, m, sh, cpos)) {
-          emit_cut<THREADS, CPT>(ck, cn, m, k, row, out_i, out_v, sh, cpos, rs, t);
+          emit_cut<THREADS, CPT>(ck, cn, m, k, row, out_i, out_v, sh, cpos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
           done = true;
         }
       }
@@ -767,9 +777,9 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
   }
   if (done) return;
   if (find_cut<THREADS, KPT>(key, nmine, m, sh, pos))
-    emit_cut<THREADS, KPT>(key, nmine, m, k, row, out_i, out_v, sh, pos, rs, t);
+    emit_cut<THREADS, KPT>(key, nmine, m, k, row, out_i, out_v, sh, pos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
   else
-    select_whole_row<THREADS>(row, n, m, k, out_i, out_v, sh, rs, t);
+    select_whole_row<THREADS>(row, n, m, k, out_i, out_v, sh, Remap{rs.remap, rs.rgroup, rs.rstride, t});
 }
 
 // ----------------------------------------------------------------------------
@@ -789,7 +799,7 @@ __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
-  const int n = rs.span(t, stride, nullptr, false);
+  const int n = row_span(rs, t, stride, nullptr, false);
   if (n <= kCap) return;
   const float* row = scores + static_cast<long long>(t) * stride;
   const long long span =
@@ -868,7 +878,7 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   if (t >= num_tokens) return;
-  const int n = rs.span(t, stride, nullptr, false);
+  const int n = row_span(rs, t, stride, nullptr, false);
   const int c0 = blockIdx.x * kChunk;
   if (n <= kCap || c0 >= n) return;
   ChunkKeys ck;
@@ -917,13 +927,13 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
-  const int n = rs.span(t, stride, err, tid == 0);
+  const int n = row_span(rs, t, stride, err, tid == 0);
   const float* row = scores + static_cast<long long>(t) * stride;
   int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
   float* out_v = topk_val ? topk_val + static_cast<long long>(t) * k : nullptr;
   const int m = min(k, n);
   if (m == n) {
-    write_all<kFThreads>(n, k, row, out_i, out_v, rs, t);
+    write_all<kFThreads>(n, k, row, out_i, out_v, Remap{rs.remap, rs.rgroup, rs.rstride, t});
   } else {
     int total = 0;
     bool whole_row = false;
@@ -990,7 +1000,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
     }
     __syncthreads();
     if (whole_row) {
-      select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh, rs, t);
+      select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh, Remap{rs.remap, rs.rgroup, rs.rstride, t});
     } else {
       const int per = (total + kFThreads - 1) / kFThreads;   // <= kFPer
       const int base = tid * per;
@@ -1000,9 +1010,9 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       const int nmine = max(0, min(per, total - base));
       auto pos = [&](int j) { return static_cast<int>(cpos[base + j]); };
       if (find_cut<kFThreads, kFPer>(key, nmine, m, sh, pos))
-        emit_cut<kFThreads, kFPer>(key, nmine, m, k, row, out_i, out_v, sh, pos, rs, t);
+        emit_cut<kFThreads, kFPer>(key, nmine, m, k, row, out_i, out_v, sh, pos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
       else
-        select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh, rs, t);
+        select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh, Remap{rs.remap, rs.rgroup, rs.rstride, t});
     }
   }
 }
