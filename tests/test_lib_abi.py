@@ -124,3 +124,72 @@ def test_attention_selection_bounds(lib):
     need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 8192, 128)
     per_span = 8 * 64 * (512 + 2) * 4
     assert need % per_span == 0 and need // per_span >= 2
+
+
+def test_hierarchical_host_checks(lib):
+    # every call below is refused on the host (or has no work): nothing launches
+    cb = lib.csa_candidate_blocks
+    ws = lib.csa_candidate_blocks_workspace_bytes(8, 1 << 17, 8, 2048)
+    assert ws > 8 * (1 << 17) // 8 * 4                       # at least the block scores
+    base = [FAKE, 1 << 17, FAKE, 1, 8, 8, 8, 2048, FAKE, None, 0, None, None]
+    bad = list(base); bad[6] = 3                              # block does not divide 128
+    assert cb(*bad) == -3
+    bad = list(base); bad[7] = 0                              # kb < 1
+    assert cb(*bad) == -3
+    bad = list(base); bad[7] = 5000                           # kb past the top-k limit
+    assert cb(*bad) == -3
+    bad = list(base); bad[0] = None                           # scores NULL
+    assert cb(*bad) == -1
+    bad = list(base); bad[0] = ctypes.c_void_p(0x1004)        # scores not 16-byte aligned
+    assert cb(*bad) == -4
+    assert cb(*base) == -5                                    # no workspace
+    bad = list(base); bad[5] = 0                              # no active rows
+    assert cb(*bad) == 0
+
+    sc = lib.csa_index_score_candidates
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, FAKE, FAKE, 1, 2, 2, 64, 128, 1, FAKE,
+            16, 8, FAKE, 128, FAKE, None, None]
+    bad = list(base); bad[20] = 100                           # cand_stride < kb * block
+    assert sc(*bad) == -3
+    bad = list(base); bad[18] = 3                             # block does not divide 128
+    assert sc(*bad) == -3
+    bad = list(base); bad[13] = 65                            # Hi > 64
+    assert sc(*bad) == -4
+    bad = list(base); bad[21] = None                          # cand_count NULL
+    assert sc(*bad) == -1
+    bad = list(base); bad[12] = 0
+    assert sc(*bad) == 0
+
+    tc = lib.csa_topk_candidates
+    base = [FAKE, 128, FAKE, FAKE, 16, 8, 2, 2, 32, FAKE, None, None, 0, None, None]
+    bad = list(base); bad[1] = 100                            # cand_stride < kb * block
+    assert tc(*bad) == -3
+    bad = list(base); bad[8] = 0                              # k < 1
+    assert tc(*bad) == -3
+    bad = list(base); bad[2] = None                           # cand_count NULL
+    assert tc(*bad) == -1
+    bad = list(base); bad[0] = ctypes.c_void_p(0x1004)        # scores not 16-byte aligned
+    assert tc(*bad) == -4
+    bad = list(base); bad[1] = 40000; bad[4] = 5000           # long rows need a workspace
+    assert tc(*bad) == -5
+    bad = list(base); bad[7] = 0
+    assert tc(*bad) == 0
+    assert lib.csa_topk_candidates_workspace_bytes(8, 16384, 512) == 0
+
+
+def test_mxfp4_host_checks(lib):
+    f = lib.csa_index_score_mxfp4
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, FAKE, FAKE, 1, 2, 2, 64, 128, 1, FAKE,
+            256, None, None]
+    bad = list(base); bad[14] = 64                            # the FP4 plane takes Di = 128
+    assert f(*bad) == -4
+    bad = list(base); bad[13] = 65                            # Hi > 64
+    assert f(*bad) == -4
+    bad = list(base); bad[1] = ctypes.c_void_p(0x1004)        # scales not 16-byte aligned
+    assert f(*bad) == -4
+    bad = list(base); bad[0] = None                           # query NULL
+    assert f(*bad) == -1
+    bad = list(base); bad[15] = 0                             # ratio < 1
+    assert f(*bad) == -3
+    bad = list(base); bad[12] = 0
+    assert f(*bad) == 0
