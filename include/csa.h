@@ -6,6 +6,7 @@
  *   1. csa_materialize_rope_rows  -- gather FP32 half-width RoPE rows
  *   2. csa_index_score            -- INT8 lightning-indexer scores over the
  *                                    causally visible compressed positions
+ *      (csa_index_score_mxfp4: the same scores from the MXFP4 index plane)
  *   3. csa_topk                   -- the k best positions, ascending, -1 padded
  *      (hierarchical layers: csa_candidate_blocks publishes a block mask;
  *      csa_index_score_candidates + csa_topk_candidates select inside it)
