@@ -3,8 +3,10 @@
 
 A step is the whole hot path on one batch: RoPE rows -> INT8 indexer scores ->
 top-k -> shared-KV sparse attention (four library calls on one stream).  The
-default workload is the V4.1 ratio-2 decode layer (8 rows = 4 requests x S=2,
-64 heads x 512, 16,384 compressed rows per request, top-k 512, window 128).
+default workload is the largest single-GPU decode configuration, the
+max-context ratio-1 decode layer (8 rows = 2 requests x 4, 64 heads x 512,
+1,048,576 compressed rows per request in 128-token pages, top-k 2048, window
+128, about 5% heavy-tailed index-key outliers); --config picks another.
 
 Timing: W untimed warmup steps, then exactly K steps bracketed by
 torch.cuda.synchronize(); inputs are resident in HBM.  A step is one replay of
@@ -47,7 +49,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c2", help="c1..c5 (default c2: ratio-2 decode)")
+    ap.add_argument("--config", default="c5",
+                    help="c1..c11 (default c5: max-context ratio-1 decode)")
     ap.add_argument("--copies", type=int, default=0, help="input copies (0 = auto, cold L2/MALL)")
     ap.add_argument("--warm", action="store_true", help="one input copy (cache-warm timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,6 +187,16 @@ def measured_traffic(stage: str, workload: str):
 # CPU baseline: the oracle as it stands, on host cores
 # ---------------------------------------------------------------------------
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, x, budget_s: float):
     import oracle  # the cpu_baseline leg is the one place bench.py uses the oracle
     try:
@@ -265,6 +278,7 @@ def cpu_baseline(cfg, x, budget_s: float):
             break
     el = time.perf_counter() - t0
     return {"value": done_rows / el, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{done_rows} query rows of this workload ({rows_per_call} per oracle call, "
                       f"{'every stage' if mode in ('csa', 'reindex', 'hier_full') else 'rope rows and attention'}, "
                       f"float64 NumPy) in {el:.1f} s",

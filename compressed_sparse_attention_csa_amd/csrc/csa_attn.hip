@@ -1123,9 +1123,13 @@ struct SplitPlan {
 // every span and every head group.
 constexpr int kRingSplitMin = 1024;
 
+// Decode batches of at least this many active rows fill the CUs with one
+// work-group per row.
+constexpr int kRingRowsMin = 256;
+
 SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   const int lmax = max(1, window + k);
-  if (prefill || T >= 256) return SplitPlan{true, 1, lmax};
+  if (prefill || T >= kRingRowsMin) return SplitPlan{true, 1, lmax};
   if (lmax < kRingSplitMin) return SplitPlan{false, (lmax + kSpan - 1) / kSpan, 0};
   // spans sized so that the row x span items fill the CUs about once
   long long span = (static_cast<long long>(lmax) * T + kDecodeCUs - 1) / kDecodeCUs;
@@ -1139,6 +1143,19 @@ SplitPlan plan_splits(int T, int k, int window, bool prefill) {
 // pairs [T][splits][H].
 inline size_t attn_ws_bytes(int T, int splits, int H, int D) {
   return static_cast<size_t>(T) * splits * H * (D + 2) * sizeof(float);
+}
+
+// Largest decode workspace over the active counts 1 .. T: counts from
+// kRingRowsMin on run whole lists without partials, so at most
+// kRingRowsMin - 1 plans are compared.
+size_t attn_ws_bytes_max(int T, int H, int D, int k, int window) {
+  size_t need = 0;
+  const int n_hi = std::min(T, kRingRowsMin - 1);
+  for (int n = 1; n <= n_hi; ++n) {
+    const SplitPlan plan = plan_splits(n, k, window, false);
+    if (plan.splits > 1) need = std::max(need, attn_ws_bytes(n, plan.splits, H, D));
+  }
+  return need;
 }
 
 template <int D>
@@ -1258,12 +1275,13 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
 
 }  // namespace csa
 
+// The launcher plans on the active count, which a padded batch ([V41]
+// "Compressor state ownership": T may include trailing storage padding)
+// keeps below T; the size returned covers the plan of every count 1 .. T.
 extern "C" size_t csa_sparse_attn_workspace_bytes(int32_t T, int32_t H, int32_t D, int32_t k,
                                                   int32_t window) {
   if (T <= 0 || H <= 0 || D <= 0 || k < 0 || window < 0) return 0;
-  const csa::SplitPlan plan = csa::plan_splits(T, k, window, false);
-  if (plan.splits <= 1) return 0;
-  return csa::attn_ws_bytes(T, plan.splits, H, D);
+  return csa::attn_ws_bytes_max(T, H, D, k, window);
 }
 
 extern "C" int csa_sparse_attn_decode(

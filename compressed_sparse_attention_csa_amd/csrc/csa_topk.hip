@@ -21,22 +21,22 @@
 // already ascending -- no sort.
 //
 // Rows with span <= 32,768: one work-group per row, keys straight from the
-// score row.  Longer rows (up to the 1,048,576-position context): four
+// score row.  Longer rows (up to the 1,048,576-position context): three
 // kernels over the row, which the indexer has just left in L2 / MALL:
-//   range:  work-groups over 8,192-score chunks fold the row's finite min and
-//           max into two counters;
-//   hist:   they add a 4,096-bin value histogram into the row's global one;
-//   filter: each work-group finds the bin of the m-th key from that histogram
-//           and keeps every key in or above it (typically m plus a handful),
-//           each wave writing one position-ordered segment;
+//   sample: one work-group per row reads 8,192 scores spread over the row and
+//           takes as threshold tau the key of a sampled rank a few standard
+//           deviations above m * samples / span, which leaves about
+//           m * (1 + 3 / sqrt(m)) keys >= tau;
+//   filter: work-groups over 8,192-score chunks keep every key >= tau, each
+//           wave writing its (key, position) pairs in position order into the
+//           workspace slots of its own positions, with its count;
 //   final:  one work-group per row gathers the segments in position order
-//           into LDS, runs the selection core on them and clears the row's
-//           histogram and counters.
-// No work-group waits on another inside a kernel, so no device-scope fences.
-// Rows of a long launch with span <= 8,192 skip the first three kernels; the
-// final kernel selects on the row itself.  If more than 8,192 keys tie into
-// the threshold bin, the final kernel falls back to an exact radix select
-// over the whole row.
+//           into LDS and runs the selection core on them.  When the sample
+//           misled it (fewer than m keys >= tau, or more candidates than LDS
+//           holds), it selects exactly over the whole row instead.
+// No work-group waits on another inside a kernel and no counter is shared
+// between work-groups, so the kernels need no device-scope fences or atomics
+// in global memory, and the workspace keeps nothing between calls.
 #include "csa_common.h"
 
 namespace csa {

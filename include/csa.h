@@ -201,6 +201,10 @@ int csa_topk(const float* scores, int64_t score_stride, const int32_t* positions
  *                16-byte aligned (NULL when that size is 0); scratch for the
  *                split partials, always written before it is read (calls
  *                that overlap on different streams need separate workspaces).
+ *                The schedule is chosen from num_tokens; the helper's size,
+ *                taken with the storage extent T, covers every num_tokens in
+ *                [0, T], so a padded batch sized by T never gets
+ *                CSA_ERR_WORKSPACE.
  *
  * Row t of request b at position p attends, with every head, over the window
  * rows at raw positions [max(0, p - window + 1), p] followed by the selected

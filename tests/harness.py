@@ -111,6 +111,29 @@ def check_attn(g_out, o_out, g_lse=None, o_lse=None, what=""):
         assert not (dl > tl).any(), f"{what}: lse off, worst {np.max(dl / tl):.3g}x"
 
 
+def check_budgets(g, o, what=""):
+    """The pages' per-row precision budget for attention outputs (pypto-lib
+    "DeepSeek V4.1 Flash", "Compressor state ownership": every token's output
+    row meets RMS(err) <= 1e-6 + 0.01 RMS(ref) and max|err| <= 1e-5 +
+    0.05 RMS(ref); non-finite values fail).  A second check beside the
+    elementwise tolerance."""
+    g = np.asarray(g, np.float64).reshape(g.shape[0], -1)
+    o = np.asarray(o, np.float64).reshape(o.shape[0], -1)
+    assert np.isfinite(g).all(), f"{what}: non-finite outputs"
+    rms_ref = np.sqrt(np.mean(o * o, axis=1))
+    err = g - o
+    rms_err = np.sqrt(np.mean(err * err, axis=1))
+    peak = np.max(np.abs(err), axis=1)
+    bad_rms = rms_err > 1e-6 + 0.01 * rms_ref
+    bad_peak = peak > 1e-5 + 0.05 * rms_ref
+    assert not bad_rms.any(), (f"{what}: rows {np.flatnonzero(bad_rms)[:8]} over the RMS "
+                               f"budget; worst {np.max(rms_err / (1e-6 + 0.01 * rms_ref)):.3g}x")
+    assert not bad_peak.any(), (f"{what}: rows {np.flatnonzero(bad_peak)[:8]} over the peak "
+                                f"budget; worst {np.max(peak / (1e-5 + 0.05 * rms_ref)):.3g}x")
+    return dict(rms=float(np.max(rms_err / (1e-6 + 0.01 * rms_ref))),
+                peak=float(np.max(peak / (1e-5 + 0.05 * rms_ref))))
+
+
 def rel_stats(g, o):
     """Diagnostics of the pages' precision budgets (per-row RMS / peak)."""
     g = g.reshape(g.shape[0], -1)

@@ -322,3 +322,45 @@ def test_full_layer_publishes_mask():
     ref, _ = oracle.candidate_blocks(g_full, x["positions"], cfg.ratio, cfg.T, cfg.cand_block,
                                      cfg.cand_kb)
     np.testing.assert_array_equal(step.cand_blocks.cpu().numpy(), ref)
+
+
+def test_full_layer_mask_against_oracle_scores():
+    """C9's published mask against the oracle's mask over the oracle's own
+    float64 scores: the same blocks, except where block scores tie within
+    1e-5 of the kb-th best block score (the top-k rule of the task, applied
+    to the block scores)."""
+    csa = _csa()
+    cfg = synthetic.get("c9")
+    x = synthetic.make_inputs(cfg, seed=2, with_tables=True).t
+    print("[hier] c9 mask vs oracle scores", flush=True)
+    step = csa.step_for_config(cfg, x)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    T, blk, kb = cfg.T, cfg.cand_block, cfg.cand_kb
+    o_sc, oe = oracle.index_scores(x["q_idx"], x["q_scale"], x["head_w"], x["idx_kv"],
+                                   x["idx_scale"], x["cmp_block_table"], x["query_start_loc"],
+                                   x["positions"], T, cfg.ratio, cfg.score_stride)
+    assert oe == 0
+    o_mask, _ = oracle.candidate_blocks(o_sc, x["positions"], cfg.ratio, T, blk, kb)
+    g_mask = step.cand_blocks.cpu().numpy()
+    differing = 0
+    for t in range(T):
+        nv = oracle.visible_count(int(x["positions"][t]), cfg.ratio)
+        nb = -(-nv // blk)
+        row = np.full(nb * blk, -np.inf)
+        row[:nv] = o_sc[t, :nv]
+        bs = row.reshape(nb, blk).max(axis=1)          # a block is as good as its best slot
+        o, g = o_mask[t], g_mask[t]
+        m = int((o >= 0).sum())
+        assert np.all(g[m:] == -1), f"row {t}: tail not -1"
+        gs = g[:m]
+        assert np.all(np.diff(gs) > 0) and np.all((gs >= 0) & (gs < nb)), f"row {t}: invalid mask"
+        if np.array_equal(g, o):
+            continue
+        differing += 1
+        sk = np.min(bs[o[:m]])
+        diff = np.setxor1d(gs, o[:m])
+        assert np.all(np.abs(bs[diff] - sk) <= 1e-5 * abs(sk)), (
+            f"row {t}: mask differs beyond ties ({len(diff)} blocks)")
+    print(f"[hier] c9 mask rows differing only at ties: {differing}/{T}", flush=True)

@@ -75,14 +75,17 @@ def test_config_parity(name):
     # top-k
     same = H.check_topk(g["topk_idx"][r], o["topk_idx"], o["scores"], o_positions(x, rows),
                         cfg.ratio, cfg.name)
-    # attention on the oracle's selection
+    # attention on the oracle's selection: the task's elementwise bar, then
+    # the pages' per-row RMS / peak budget
     H.check_attn(ga["out"], o["out"], ga["lse"], o["lse"], cfg.name + " attn")
+    bud = H.check_budgets(ga["out"], o["out"], cfg.name + " attn budget")
     # end to end where the selections agree
     if same.any():
         H.check_attn(g["out"][r][same], o["out"][same], g["lse"][r][same], o["lse"][same],
                      cfg.name + " step")
+        H.check_budgets(g["out"][r][same], o["out"][same], cfg.name + " step budget")
     print(f"[parity] {cfg.name}: rows with identical selection {same.sum()}/{len(rows)}; "
-          f"budget diagnostics {H.rel_stats(ga['out'], o['out'])}", flush=True)
+          f"worst budget use rms {bud['rms']:.3f}, peak {bud['peak']:.3f}", flush=True)
 
 
 def o_positions(x, rows):
@@ -97,9 +100,13 @@ def test_c5_max_context_parity():
     same = H.check_topk(g["topk_idx"], o["topk_idx"], o["scores"], x["positions"], cfg.ratio,
                         cfg.name)
     H.check_attn(ga["out"], o["out"], ga["lse"], o["lse"], cfg.name + " attn")
+    bud = H.check_budgets(ga["out"], o["out"], cfg.name + " attn budget")
     if same.any():
         H.check_attn(g["out"][same], o["out"][same], g["lse"][same], o["lse"][same],
                      cfg.name + " step")
+        H.check_budgets(g["out"][same], o["out"][same], cfg.name + " step budget")
+    print(f"[parity] {cfg.name}: worst budget use rms {bud['rms']:.3f}, "
+          f"peak {bud['peak']:.3f}", flush=True)
     _CACHE.pop("c5", None)
 
 

@@ -193,3 +193,23 @@ def test_mxfp4_host_checks(lib):
     assert f(*bad) == -3
     bad = list(base); bad[12] = 0
     assert f(*bad) == 0
+
+
+def test_attention_workspace_covers_padded_batches(lib):
+    """The schedule follows num_tokens while the helper takes the storage
+    extent T (a padded batch): its size must cover every active count up to
+    T.  T = 300 with 10 active rows splits the key lists (partials), although
+    300 active rows would not."""
+    f = lib.csa_sparse_attn_workspace_bytes
+    for k, w in ((512, 128), (2048, 128), (8192, 128), (4096, 0)):
+        sizes = [f(n, 64, 512, k, w) for n in range(1, 301)]
+        assert f(300, 64, 512, k, w) == max(sizes)
+        assert f(300, 64, 512, k, w) >= f(10, 64, 512, k, w) > 0
+    # the launcher's own need for 10 active rows is what the helper reports:
+    # one byte less is refused on the host, before any launch
+    need10 = f(10, 64, 512, 512, 128)
+    args = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
+            FAKE, 0.04, FAKE, FAKE, 1, 300, 10, 64, 512, FAKE, None, FAKE, need10 - 1, None,
+            None]
+    assert lib.csa_sparse_attn_decode(*args) == -5
+    assert f(300, 64, 512, 512, 128) >= need10
