@@ -37,6 +37,14 @@ constexpr int kMaxPPW = 64;      // pages per work-group
 constexpr int kStages = 3;       // key pages resident in LDS (in flight or in use)
 constexpr int kLoadsPerWave = kPage * kRowBytes / (64 * 16) / (kThreads / 64);  // per page
 constexpr int kVmPerPage = kLoadsPerWave + 1;   // + one load of 32 key scales
+#ifndef CSA_IDX_WPE
+#define CSA_IDX_WPE 3
+#endif
+#ifndef CSA_IDX_DB
+#define CSA_IDX_DB 0
+#endif
+constexpr int kIdxWaves = CSA_IDX_WPE;       // waves per SIMD (work-groups per CU)
+constexpr bool kIdxDB = CSA_IDX_DB != 0;     // key operands double-buffered by key tile
 
 __device__ __forceinline__ int swz_chunk(int key, int chunk) {
   return chunk ^ ((key >> 1) & 7);
@@ -115,6 +123,25 @@ __device__ __forceinline__ void wait_vm_rt(int n) {
   }
 }
 
+// LDS address of a __shared__ object, and LDS reads the compiler does not
+// track (the caller waits with an explicit lgkmcnt that names the result).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+__device__ __forceinline__ void lds_read_b128(v4i& d, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1" : "=v"(d) : "v"(addr));
+}
+__device__ __forceinline__ void lds_read_b32(uint32_t& d, uint32_t addr) {
+  asm volatile("ds_read_b32 %0, %1" : "=v"(d) : "v"(addr));
+}
+// ds_read_b128 at addr + OFF, OFF an immediate (16-bit instruction offset)
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128_at(v4i& d, uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset range");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF));
+}
+
 __device__ __forceinline__ float lane_add_swap32(float x, float y) {
   // lanes 0-31: x[l] + x[l+32]; lanes 32-63: y[l-32] + y[l]
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
@@ -129,7 +156,7 @@ __device__ __forceinline__ v8i lo_v8i(v4i x) {
 }
 
 template <int KK, bool FP4>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3))) index_score_kernel(
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kIdxWaves, kIdxWaves))) index_score_kernel(
     const int8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ head_w, const int8_t* __restrict__ idx_kv,
     const float* __restrict__ idx_scale, int num_blocks, const int32_t* __restrict__ bt,
@@ -150,7 +177,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   __shared__ int scratch[kThreads / 64 + 2];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
   const int lane = tid & 63;
   // direct-to-LDS loads per wave per page (FP4 rows take 64 LDS bytes, INT8
   // rows 128), and vector-memory operations per page with the scale load
@@ -340,34 +367,47 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     else if constexpr (S == 1) return ks1;
     else return ks2;
   };
+  // byte offset inside a page of this lane's source chunk for the wave's
+  // load u: the same for every page (hoisted out of the page loop), so a
+  // page's loads take one uniform base and no per-lane address arithmetic.
+  // FP4: 64-byte rows, four chunks per key; INT8: 128-byte LDS rows, and a
+  // padding slot past Di takes any bytes of the same key.
+  auto lane_off = [&](int u) -> uint32_t {
+    const int q = (wave * LPWv + u) * 64 + lane;
+    const int key = FP4 ? (q >> 2) : (q >> 3);
+    int c = FP4 ? ((q & 3) ^ ((key >> 2) & 3)) : ((q & 7) ^ ((key >> 1) & 7));
+    c = (c * 16 >= RB) ? 0 : c;
+    return static_cast<uint32_t>(key * RB + c * 16);
+  };
   auto issue = [&](int pi, auto stg) {
     int8_t* keys = keys_of(stg);
     float* ksd = ks_of(stg);
-    const int blk = blk_s[pi];
-    const int8_t* pbase = idx_kv + static_cast<long long>(blk < 0 ? 0 : blk) * kPage * RB;
+    const int blk = __builtin_amdgcn_readfirstlane(blk_s[pi]);
+    if (blk >= 0) {
+      const int8_t* pbase = idx_kv + static_cast<long long>(blk) * kPage * RB;
+      const float* sbase = idx_scale + static_cast<long long>(blk) * kPage;
 #pragma unroll
-    for (int u = 0; u < LPWv; ++u) {
-      const int ins = wave * LPWv + u;
-      const int q = ins * 64 + lane;
-      int key, c;
-      if constexpr (FP4) {   // 64-byte rows: four chunks per key
-        key = q >> 2;
-        c = (q & 3) ^ ((key >> 2) & 3);
-      } else {
-        key = q >> 3;
-        c = (q & 7) ^ ((key >> 1) & 7);
-        if (c * 16 >= RB) c = 0;   // padding slot: any bytes of the same key
-      }
-      const int8_t* src = blk >= 0 ? pbase + key * RB + c * 16 : q_idx;
-      __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(keys + ins * 1024), 16, 0, 0);
-    }
-    if (lane < 8) {   // key scales: wave w brings keys 32w .. 32w+31
-      const float* ssrc = blk >= 0
-                              ? idx_scale + static_cast<long long>(blk) * kPage + wave * 32 + lane * 4
-                              : reinterpret_cast<const float*>(q_idx);
-      __builtin_amdgcn_global_load_lds(
-          ssrc, (__attribute__((address_space(3))) void*)(ksd + wave * 32), 16, 0, 0);
+      for (int u = 0; u < LPWv; ++u)
+        __builtin_amdgcn_global_load_lds(
+            pbase + static_cast<int>(lane_off(u)),
+            (__attribute__((address_space(3))) void*)(keys + (wave * LPWv + u) * 1024), 16, 0,
+            0);
+      // key scales: wave w brings keys 32w .. 32w+31, 16 bytes per lane
+      // (each active lane writes 16 LDS bytes, so only lanes 0-7 run it)
+      if (lane < 8)
+        __builtin_amdgcn_global_load_lds(
+            sbase + (lane & 7) * 4 + wave * 32,
+            (__attribute__((address_space(3))) void*)(ksd + wave * 32), 16, 0, 0);
+    } else {
+      // nothing to stage: the same number of loads, of 16 valid bytes
+#pragma unroll
+      for (int u = 0; u < LPWv; ++u)
+        __builtin_amdgcn_global_load_lds(
+            q_idx, (__attribute__((address_space(3))) void*)(keys + (wave * LPWv + u) * 1024),
+            16, 0, 0);
+      if (lane < 8)
+        __builtin_amdgcn_global_load_lds(
+            q_idx, (__attribute__((address_space(3))) void*)(ksd + wave * 32), 16, 0, 0);
     }
   };
 
@@ -384,6 +424,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     wait_vm_rt(__builtin_amdgcn_readfirstlane(VMPv * newer +
                                               (active ? min(kStages - 1, pi) : 0)));
     lds_barrier();
+    const int blk_here = blk_s[pi];   // read before the refill's loads go out
     if (pi + kStages - 1 < npages)
       issue(pi + kStages - 1, std::integral_constant<int, (S + kStages - 1) % kStages>{});
     if (!active) return;
@@ -392,27 +433,51 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const int c0 = (page0 + pi) * kPage;
     float* out_row = scores + static_cast<long long>(my_t) * stride + c0;
     float w0 = neg_inf, w1 = neg_inf;
-    if (blk_s[pi] >= 0 && c0 < my_n) {
+    if (blk_here >= 0 && c0 < my_n) {
+      // Key operands come from LDS through inline ds_read instructions with
+      // explicit lgkmcnt waits.  The compiler cannot tell a read of this
+      // page's stage from the direct-to-LDS loads of the later pages still in
+      // flight, and guards a plain LDS read with vmcnt(0), which would make
+      // every page wait for the page just requested; this page's own loads
+      // are already waited for (the vmcnt wait and barrier above).
+      // Each wait names the registers it covers, which orders their uses
+      // after it.
+      const uint32_t kbase = lds_addr(keys);
+      const uint32_t sbase = lds_addr(ksd);
+      uint32_t ksw0 = 0u, ksw1 = 0u;   // INT8: the FP32 scales of keys lane, 64 + lane
+      if constexpr (!FP4) {
+        lds_read_b32(ksw0, sbase + 4 * lane);
+        lds_read_b32(ksw1, sbase + 4 * (64 + lane));
+      }
       // eight (32-head, 32-key) tiles p = 2*nt + mt, each scored as soon as
       // its MFMAs are issued: the epilogue waits for them, and the SIMD's
-      // other waves fill that wait.  One set of B registers per key tile.
+      // other waves fill that wait.  Key operands are double-buffered by key
+      // tile: the reads for tile nt + 1 go out before tile nt's MFMAs, into
+      // the set whose MFMAs (tile nt - 1) the epilogue has already waited for.
       float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      v4i bk[KS];
-      int sb[KS];
-      v16i acc;
-      auto load_b = [&](int nt) {
-        const int kj = nt * 32 + col;
+      v4i bk[kIdxDB ? 2 : 1][KS];
+      uint32_t kw[kIdxDB ? 2 : 1] = {};   // FP4: the key's E8M0 bytes (its scale slot)
+      // Key kj = nt * 32 + col: its swizzle does not depend on nt (32 keys
+      // move the XOR pattern by whole periods), so one address per k-step
+      // serves every key tile, with the tile's row offset as an immediate
+      constexpr int RBL = FP4 ? 64 : kRowBytes;   // LDS bytes per key row
+      uint32_t kaddr[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          bk[ks] = FP4 ? *reinterpret_cast<const v4i*>(
-                             keys + kj * 64 + (((ks * 2 + half) ^ ((kj >> 2) & 3)) * 16))
-                       : *reinterpret_cast<const v4i*>(
-                             keys + kj * kRowBytes + swz_chunk(kj, ks * 2 + half) * 16);
-        if constexpr (FP4) {
-          const uint32_t kw = __float_as_uint(ksd[kj]);
+      for (int ks = 0; ks < KS; ++ks)
+        kaddr[ks] = kbase + static_cast<uint32_t>(
+                                FP4 ? col * 64 + (((ks * 2 + half) ^ ((col >> 2) & 3)) * 16)
+                                    : col * kRowBytes + swz_chunk(col, ks * 2 + half) * 16);
+      auto read_b = [&](int nt, int buf) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) sb[ks] = (kw >> (8 * (ks * 2 + half))) & 0xff;
+        for (int ks = 0; ks < KS; ++ks) {
+          switch (nt) {
+            case 0: lds_read_b128_at<0>(bk[buf][ks], kaddr[ks]); break;
+            case 1: lds_read_b128_at<32 * RBL>(bk[buf][ks], kaddr[ks]); break;
+            case 2: lds_read_b128_at<64 * RBL>(bk[buf][ks], kaddr[ks]); break;
+            default: lds_read_b128_at<96 * RBL>(bk[buf][ks], kaddr[ks]); break;
+          }
         }
+        if constexpr (FP4) lds_read_b32(kw[buf], sbase + 4 * (nt * 32 + col));
       };
       // The accumulators start at 0x40800000, the bits of 4.0f.  A dot
       // product of Di <= 128 INT8 pairs lies in [-2^21, 2^21], so the INT32
@@ -425,46 +490,94 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
       constexpr int kBias = 0x40800000;
       constexpr v16i kBiasV = {kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias,
                                kBias, kBias, kBias, kBias, kBias, kBias, kBias, kBias};
+      if constexpr (kIdxDB) read_b(0, 0);
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        if ((p & 1) == 0) load_b(p >> 1);
-        float xs = x[p >> 1];
-        if constexpr (FP4) {
-          // FP32 dots of the dequantised rows (E2M1 values, E8M0 scales of
-          // each 32 dims applied by the MFMA); ReLU and the head weight
-          const v16f zero16 = {};
-          v16f accf;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            accf = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                lo_v8i(qa[p & 1][ks]), lo_v8i(bk[ks]), ks == 0 ? zero16 : accf, 4, 4, 0,
-                sa[p & 1][ks], 0, sb[ks]);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) xs = fmaf(ww[p & 1][j], fmaxf(accf[j], 0.0f), xs);
-        } else {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[p & 1][ks], bk[ks],
-                                                        ks == 0 ? kBiasV : acc, 0, 0, 0);
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            xs = fmaf(ww[p & 1][j],
-                      __builtin_amdgcn_fmed3f(__int_as_float(acc[j]) - 4.0f, 0.0f, 1.0f), xs);
+      for (int nt = 0; nt < 4; ++nt) {
+        const int cur = kIdxDB ? (nt & 1) : 0;
+        if constexpr (!kIdxDB) {
+          // one set: tile nt's reads go out once tile nt - 1's MFMAs are
+          // done (its epilogue has consumed their results)
+          read_b(nt, 0);
+          if constexpr (FP4)
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bk[0][0]), "+v"(bk[0][1]),
+                         "+v"(bk[0][2]), "+v"(bk[0][3]), "+v"(kw[0]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bk[0][0]), "+v"(bk[0][1]),
+                         "+v"(bk[0][2]), "+v"(bk[0][3]), "+v"(ksw0), "+v"(ksw1));
+        } else if (nt + 1 < 4) {
+          read_b(nt + 1, cur ^ 1);
         }
-        x[p >> 1] = xs;
+        // LDS operations complete in order: once at most the next tile's
+        // reads are outstanding, this tile's (and the scales') have landed
+        if constexpr (!kIdxDB) {
+        } else if constexpr (FP4) {
+          if (nt + 1 < 4)
+            asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(bk[cur][0]), "+v"(bk[cur][1]),
+                         "+v"(bk[cur][2]), "+v"(bk[cur][3]), "+v"(kw[cur]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bk[cur][0]), "+v"(bk[cur][1]),
+                         "+v"(bk[cur][2]), "+v"(bk[cur][3]), "+v"(kw[cur]));
+        } else {
+          if (nt == 0)
+            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(bk[0][0]), "+v"(bk[0][1]),
+                         "+v"(bk[0][2]), "+v"(bk[0][3]), "+v"(ksw0), "+v"(ksw1));
+          else if (nt + 1 < 4)
+            asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(bk[cur][0]), "+v"(bk[cur][1]),
+                         "+v"(bk[cur][2]), "+v"(bk[cur][3]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bk[cur][0]), "+v"(bk[cur][1]),
+                         "+v"(bk[cur][2]), "+v"(bk[cur][3]));
+        }
+        int sb[KS];
+        if constexpr (FP4) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) sb[ks] = (kw[cur] >> (8 * (ks * 2 + half))) & 0xff;
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          float xs = x[nt];
+          if constexpr (FP4) {
+            // FP32 dots of the dequantised rows (E2M1 values, E8M0 scales of
+            // each 32 dims applied by the MFMA); ReLU and the head weight
+            const v16f zero16 = {};
+            v16f accf;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              accf = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  lo_v8i(qa[mt][ks]), lo_v8i(bk[cur][ks]), ks == 0 ? zero16 : accf, 4, 4, 0,
+                  sa[mt][ks], 0, sb[ks]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) xs = fmaf(ww[mt][j], fmaxf(accf[j], 0.0f), xs);
+          } else {
+            v16i acc;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[mt][ks], bk[cur][ks],
+                                                          ks == 0 ? kBiasV : acc, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              xs = fmaf(ww[mt][j],
+                        __builtin_amdgcn_fmed3f(__int_as_float(acc[j]) - 4.0f, 0.0f, 1.0f), xs);
+          }
+          x[nt] = xs;
+        }
       }
       // head sums: lanes l and l + 32 hold the two 32-head halves of the
       // same key, so one swap per key pair finishes them; lane l of w0 ends
       // with key l of this page, of w1 with key 64 + l
       w0 = lane_add_swap32(x[0], x[1]);
       w1 = lane_add_swap32(x[2], x[3]);
-      w0 = (c0 + lane < my_n) ? (FP4 ? w0 : ksd[lane] * w0) : neg_inf;
-      w1 = (c0 + 64 + lane < my_n) ? (FP4 ? w1 : ksd[64 + lane] * w1) : neg_inf;
-      if (w0 == 0.0f) w0 = 0.0f;   // one zero: +0.0
-      if (w1 == 0.0f) w1 = 0.0f;
+      // adding +0.0 turns a -0.0 score into +0.0 (one zero) and leaves every
+      // other value unchanged; it folds into the scale multiply as an FMA
+      const int vis = my_n - c0;   // visible keys of this page (> 0 here)
+      w0 = (lane < vis) ? (FP4 ? w0 + 0.0f : fmaf(__uint_as_float(ksw0), w0, 0.0f)) : neg_inf;
+      w1 = (64 + lane < vis) ? (FP4 ? w1 + 0.0f : fmaf(__uint_as_float(ksw1), w1, 0.0f))
+                             : neg_inf;
     }
-    if (c0 + lane < stride) out_row[lane] = w0;
-    if (c0 + 64 + lane < stride) out_row[64 + lane] = w1;
+    // the score row ends at stride (a page may reach past it)
+    const int lim = static_cast<int>(min(static_cast<long long>(kPage), stride - c0));
+    if (lane < lim) out_row[lane] = w0;
+    if (64 + lane < lim) out_row[64 + lane] = w1;
   };
 
   static_assert(kStages == 3, "the page loop is unrolled over three stages");
@@ -688,7 +801,7 @@ extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const 
   // (the group count is estimated from below: every request owns at least
   // one group, and four rows fill one; decode batches of 2-row requests
   // have B groups, not num_tokens / 4)
-  constexpr long long kSlots = 3 * 256;
+  constexpr long long kSlots = csa::kIdxWaves * 256;
   const long long groups_est = std::max<long long>((num_tokens + 3) / 4, std::min(B, num_tokens));
   long long ppw = (pages * groups_est + kSlots - 1) / kSlots;
   if (ppw < 1) ppw = 1;
@@ -774,7 +887,7 @@ extern "C" int csa_index_score_mxfp4(const uint8_t* q_fp4, const uint8_t* q_sc,
   if (static_cast<long long>(num_blocks) * csa::kPage * Di >= (1ll << 40)) return CSA_ERR_SHAPE;
   const long long pages = (score_stride + csa::kPage - 1) / csa::kPage;
   const long long groups = (num_tokens + 3) / 4 + B;
-  constexpr long long kSlots = 3 * 256;
+  constexpr long long kSlots = csa::kIdxWaves * 256;
   const long long groups_est = std::max<long long>((num_tokens + 3) / 4, std::min(B, num_tokens));
   long long ppw = (pages * groups_est + kSlots - 1) / kSlots;
   if (ppw < 1) ppw = 1;
