@@ -55,6 +55,10 @@ _SIGS = {
                                            _P, _P, _SZ, _P, _P]),
 }
 _SIGS["csa_sparse_attn_prefill"] = _SIGS["csa_sparse_attn_decode"]
+_SIGS["csa_sparse_attn_noalloc_max_bytes"] = (_SZ, [])
+# the decode arguments without (workspace, workspace_bytes)
+_SIGS["csa_sparse_attn_decode_noalloc"] = (
+    ctypes.c_int, _SIGS["csa_sparse_attn_decode"][1][:28] + _SIGS["csa_sparse_attn_decode"][1][30:])
 
 EXPORTS = tuple(_SIGS)
 
@@ -232,7 +236,8 @@ def csa_sparse_attn_workspace_bytes(T: int, H: int, D: int, k: int, window: int)
 
 def _attn(fn_name, q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table, topk_idx, ratio,
           win_kv, win_block_table, window, attn_sink, softmax_scale, query_start_loc, positions,
-          num_tokens, out, lse=None, workspace=None, err=None, stream=None, k=None):
+          num_tokens, out, lse=None, workspace=None, err=None, stream=None, k=None,
+          noalloc=False):
     """topk_idx None selects every visible compressed row, with k (required
     then) bounding their count; k = 0 attends over the window alone, and the
     compressed pool and table may then be None."""
@@ -245,20 +250,35 @@ def _attn(fn_name, q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table, 
         raise CsaError("k is required when topk_idx is None")
     rope_dim = 2 * rope_cos.shape[1]
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = getattr(load(), fn_name)(
+    args = [
         _ptr(q), _ptr(rope_cos), _ptr(rope_sin), rope_dim, int(rope_offset), _ptr(cmp_kv),
         0 if cmp_kv is None else cmp_kv.shape[0], _ptr(cmp_block_table),
         0 if cmp_block_table is None else cmp_block_table.shape[1], _ptr(topk_idx), int(k),
         int(ratio), _ptr(win_kv), win_kv.shape[0], _ptr(win_block_table),
         win_block_table.shape[1], int(window), _ptr(attn_sink), float(softmax_scale),
         _ptr(query_start_loc), _ptr(positions), query_start_loc.shape[0] - 1, T,
-        int(num_tokens), H, D, _ptr(out), _ptr(lse), _ptr(workspace), wsb, _ptr(err),
-        _stream(stream))
+        int(num_tokens), H, D, _ptr(out), _ptr(lse)]
+    args += [_ptr(err), _stream(stream)] if noalloc else [_ptr(workspace), wsb, _ptr(err),
+                                                          _stream(stream)]
+    st = getattr(load(), fn_name)(*args)
     _check(st, fn_name)
 
 
 def csa_sparse_attn_decode(*args, **kw) -> None:
     _attn("csa_sparse_attn_decode", *args, **kw)
+
+
+def csa_sparse_attn_noalloc_max_bytes() -> int:
+    return int(load().csa_sparse_attn_noalloc_max_bytes())
+
+
+def csa_sparse_attn_decode_noalloc(*args, **kw) -> None:
+    """csa_sparse_attn_decode with the library's static scratch instead of a
+    workspace (no workspace argument)."""
+    if kw.get("workspace") is not None:
+        raise CsaError("csa_sparse_attn_decode_noalloc takes no workspace")
+    kw.pop("workspace", None)
+    _attn("csa_sparse_attn_decode_noalloc", *args, noalloc=True, **kw)
 
 
 def csa_sparse_attn_prefill(*args, **kw) -> None:

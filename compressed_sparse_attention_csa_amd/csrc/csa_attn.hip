@@ -33,9 +33,22 @@
 // identically on both operands).  The rotated query stays in registers as the
 // B operand of S^T.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "csa_common.h"
+
+// Allocation-free decode: the span partials live in a file-scope device array
+// instead of a caller workspace, for callers that cannot allocate (code under
+// HIP graph capture, tight serving loops).  Each GPU the library runs on holds
+// its own copy of the array until the process ends; its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever handed to kernels -- the array's name in host
+// code is a host-side stand-in, not a device address.  The partials are
+// always written before they are read, so nothing needs clearing, and every
+// call on one GPU shares the array: calls that overlap on one GPU race.
+static constexpr size_t kScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace csa {
 
@@ -1188,6 +1201,24 @@ int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
   return CSA_OK;
 }
 
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array (looked up on first use).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
 int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const float* rope_sin,
                int32_t rope_dim, int32_t rope_offset, const uint16_t* cmp_kv,
                int32_t num_cmp_blocks, const int32_t* cmp_block_table, int32_t max_cmp_blocks,
@@ -1196,7 +1227,8 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
                int32_t window, const float* attn_sink, float softmax_scale,
                const int32_t* query_start_loc, const int32_t* positions, int32_t B, int32_t T,
                int32_t num_tokens, int32_t H, int32_t D, uint16_t* out, float* lse,
-               void* workspace, size_t workspace_bytes, int32_t* err, void* stream) {
+               void* workspace, size_t workspace_bytes, int32_t* err, void* stream,
+               bool static_scratch = false) {
   if (T < 0 || B < 0 || num_cmp_blocks < 0 || num_win_blocks < 0 || max_cmp_blocks < 0 ||
       max_win_blocks < 0 || window < 0 || k < 0)
     return CSA_ERR_SHAPE;
@@ -1255,6 +1287,12 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   a.err = err;
   if (plan.splits > 1) {
     const size_t need = attn_ws_bytes(num_tokens, plan.splits, H, D);
+    if (static_scratch) {   // the library's own array instead of a workspace
+      if (need > kScratchBytes) return CSA_ERR_SCRATCH;
+      const int st = scratch_for_current_device(&workspace);
+      if (st != CSA_OK) return st;
+      workspace_bytes = kScratchBytes;
+    }
     if (!workspace || workspace_bytes < need) return CSA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
     char* w = static_cast<char*>(workspace);
@@ -1318,6 +1356,24 @@ extern "C" int csa_sparse_attn_prefill(
                          H, D, out, lse, workspace, workspace_bytes, err, stream);
 }
 
+extern "C" size_t csa_sparse_attn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+extern "C" int csa_sparse_attn_decode_noalloc(
+    const uint16_t* q, const float* rope_cos, const float* rope_sin, int32_t rope_dim,
+    int32_t rope_offset, const uint16_t* cmp_kv, int32_t num_cmp_blocks,
+    const int32_t* cmp_block_table, int32_t max_cmp_blocks, const int32_t* topk_idx, int32_t k,
+    int32_t ratio, const uint16_t* win_kv, int32_t num_win_blocks,
+    const int32_t* win_block_table, int32_t max_win_blocks, int32_t window,
+    const float* attn_sink, float softmax_scale, const int32_t* query_start_loc,
+    const int32_t* positions, int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
+    uint16_t* out, float* lse, int32_t* err, void* stream) {
+  return csa::attn_entry(false, q, rope_cos, rope_sin, rope_dim, rope_offset, cmp_kv,
+                         num_cmp_blocks, cmp_block_table, max_cmp_blocks, topk_idx, k, ratio,
+                         win_kv, num_win_blocks, win_block_table, max_win_blocks, window,
+                         attn_sink, softmax_scale, query_start_loc, positions, B, T, num_tokens,
+                         H, D, out, lse, nullptr, 0, err, stream, /*static_scratch=*/true);
+}
+
 extern "C" const char* csa_status_string(int status) {
   switch (status) {
     case CSA_OK: return "CSA_OK";
@@ -1327,6 +1383,8 @@ extern "C" const char* csa_status_string(int status) {
     case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: shape or alignment without a kernel";
     case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
     case CSA_ERR_LAUNCH: return "CSA_ERR_LAUNCH: the HIP runtime refused a launch";
+    case CSA_ERR_SCRATCH:
+      return "CSA_ERR_SCRATCH: the call needs more than the library's static scratch holds";
     default: return "unknown csa_status";
   }
 }

@@ -75,7 +75,8 @@ typedef enum {
   CSA_ERR_RANGE = -3,       /* num_tokens outside [0, T], k > width, ratio < 1   */
   CSA_ERR_UNSUPPORTED = -4, /* a shape this build has no kernel for              */
   CSA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the helper's size  */
-  CSA_ERR_LAUNCH = -6       /* the HIP runtime refused a launch                  */
+  CSA_ERR_LAUNCH = -6,      /* the HIP runtime refused a launch                  */
+  CSA_ERR_SCRATCH = -7      /* needs more than the static scratch of a *_noalloc */
 } csa_status;
 
 /* device error word bits, OR-ed into *err */
@@ -257,6 +258,39 @@ int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const floa
                             int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
                             uint16_t* out, float* lse, void* workspace,
                             size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * csa_sparse_attn_decode_noalloc -- csa_sparse_attn_decode for callers that
+ * cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * operation, arguments (without the workspace), kernels and results; the
+ * split partials go to a static device array of the library,
+ * csa_sparse_attn_noalloc_max_bytes() bytes (32 MiB) per GPU, held by each
+ * GPU the library runs on until the process ends.  Its device address is
+ * looked up on the first call on a device (the stream must belong to the
+ * current device).  The call allocates nothing and frees nothing.
+ *
+ * Limit: a call whose schedule needs more partial bytes than the array holds
+ * (csa_sparse_attn_workspace_bytes(num_tokens, H, D, k, window) for a batch
+ * of num_tokens rows) returns CSA_ERR_SCRATCH and launches nothing.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (partials are written before they are read, so nothing needs
+ * clearing): calls that overlap on one GPU (different streams, or a graph
+ * replayed concurrently) race and must be serialized by the caller.
+ */
+size_t csa_sparse_attn_noalloc_max_bytes(void);
+int csa_sparse_attn_decode_noalloc(const uint16_t* q, const float* rope_cos,
+                                   const float* rope_sin, int32_t rope_dim, int32_t rope_offset,
+                                   const uint16_t* cmp_kv, int32_t num_cmp_blocks,
+                                   const int32_t* cmp_block_table, int32_t max_cmp_blocks,
+                                   const int32_t* topk_idx, int32_t k, int32_t ratio,
+                                   const uint16_t* win_kv, int32_t num_win_blocks,
+                                   const int32_t* win_block_table, int32_t max_win_blocks,
+                                   int32_t window, const float* attn_sink, float softmax_scale,
+                                   const int32_t* query_start_loc, const int32_t* positions,
+                                   int32_t B, int32_t T, int32_t num_tokens, int32_t H,
+                                   int32_t D, uint16_t* out, float* lse, int32_t* err,
+                                   void* stream);
 
 /*
  * csa_index_score_mxfp4 -- csa_index_score with the FP4 index plane

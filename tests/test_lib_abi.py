@@ -43,7 +43,7 @@ def test_binding_covers_header():
 
 
 def test_status_strings(lib):
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert lib.csa_status_string(s).decode().startswith("CSA_")
 
 
@@ -213,3 +213,27 @@ def test_attention_workspace_covers_padded_batches(lib):
             None]
     assert lib.csa_sparse_attn_decode(*args) == -5
     assert f(300, 64, 512, 512, 128) >= need10
+
+
+def test_noalloc_decode_host_checks(lib):
+    """The allocation-free decode refuses, before any launch, a call whose
+    partials would not fit its static scratch, and otherwise applies the
+    decode call's own host checks."""
+    cap = lib.csa_sparse_attn_noalloc_max_bytes()
+    assert cap == 32 << 20
+    f = lib.csa_sparse_attn_decode_noalloc
+    # 200 active rows of 4096 + 128 keys: two spans of whole-head partials
+    need = lib.csa_sparse_attn_workspace_bytes(200, 64, 512, 4096, 128)
+    assert need > cap
+    big = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 4096, 1, FAKE, 2, FAKE, 2, 128,
+           FAKE, 0.04, FAKE, FAKE, 1, 200, 200, 64, 512, FAKE, None, None, None]
+    assert f(*big) == -7
+    assert lib.csa_status_string(-7).decode().startswith("CSA_ERR_SCRATCH")
+    base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
+            FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, None, None]
+    bad = list(base); bad[25] = 320               # D without a kernel
+    assert f(*bad) == -4
+    bad = list(base); bad[0] = None               # q NULL
+    assert f(*bad) == -1
+    bad = list(base); bad[23] = 0                 # no active rows: nothing to do
+    assert f(*bad) == 0
