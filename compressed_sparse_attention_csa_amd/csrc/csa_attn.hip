@@ -23,7 +23,8 @@
 // Decode kernel (small batches): a work-group owns one (row, 16-head group,
 // 128-entry span); each wave gathers and multiplies its own 32-row tile, so a
 // span costs one memory latency and every key byte is read from LDS once.
-// Partials of the spans are merged with the sink by a third kernel.
+// BF16 partials of the spans, normalised by their own sums, are merged with the
+// sink by a third kernel.
 //
 // Tile code.  Rows sit at a 16-byte-padded stride so the K operand reads
 // (A of S^T = K Q^T) and the transposed V reads (A of O^T = V^T P^T) spread
@@ -89,8 +90,8 @@ struct AttnArgs {
   int H;
   uint16_t* out;
   float* lse;
-  float* part_o;     // [T][splits][H][D]
-  float2* part_ml;   // [T][splits][H]
+  uint16_t* part_o;  // BF16 [T][splits][H][D]: span partials normalised by their sum
+  float2* part_ml;   // [T][splits][H]: (max, sum) of each span, base-2 logits
   int splits;
   int ring_span;     // ring schedule with splits > 1: list entries per span
   int items_per_xcd;
@@ -569,7 +570,9 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
       // list publishes its (max, sum) for the merge instead
       if (hv && grp == 0) {
         if (a.splits > 1) {
+          // the span's (max, sum); its partial is O / sum
           a.part_ml[static_cast<long long>(item) * a.H + h] = make_float2(m_ref, l_run);
+          f_s[h] = l_run > 0.0f ? 1.0f / l_run : 0.0f;
         } else {
           const float M = fmaxf(m_ref, sink2);
           const float corr = (m_ref == neg_inf) ? 0.0f : exp2f(m_ref - M);
@@ -643,25 +646,16 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
       __syncthreads();
       if (again) continue;
       __syncthreads();   // f_s is complete
-      if (a.splits > 1) {
-        // the span's partial: O relative to its own softmax reference
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          const int hh = ht * 16 + col;
-          if (hh >= a.H) continue;
-          float* prow = a.part_o + (static_cast<long long>(item) * a.H + hh) * D + d0;
-#pragma unroll
-          for (int dt = 0; dt < DTW; ++dt)
-            *reinterpret_cast<v4f*>(prow + dt * 16 + grp * 4) = o_acc[dt][ht];
-        }
-        break;
-      }
+      // the output rows, or with splits > 1 the span's BF16 partial (f is
+      // then 1 / its sum)
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         const int hh = ht * 16 + col;
         if (hh >= a.H) continue;
         const float f = f_s[hh];
-        uint16_t* orow = a.out + (static_cast<long long>(t) * a.H + hh) * D + d0;
+        uint16_t* orow = (a.splits > 1 ? a.part_o + static_cast<long long>(item) * a.H * D
+                                       : a.out + static_cast<long long>(t) * a.H * D) +
+                         static_cast<long long>(hh) * D + d0;
 #pragma unroll
         for (int dt = 0; dt < DTW; ++dt) {
           // o_acc[dt][ht][r] is channel d0 + dt*16 + grp*4 + r of head hh
@@ -687,8 +681,9 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
 // memory latency -- and runs one 32-key tile (S^T, softmax, P*V) for the
 // group's 16 heads; no key byte is read from LDS by more than one wave.  The
 // four per-wave softmax states are then combined in LDS.  With one span the
-// work-group writes the output rows directly; with several it writes an FP32
-// partial (16 heads x D, relative to its own max) for the merge kernel.
+// work-group writes the output rows directly; with several it writes a BF16
+// partial (16 heads x D, normalised by its own sum) with the FP32 (max, sum)
+// for the merge kernel.
 constexpr int kSpan = kAttnWaves * kTile;   // list entries per decode work-group
 
 template <int D>
@@ -981,7 +976,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
         e[w] = (mw[w] == neg_inf) ? 0.0f : exp2f(mw[w] - M);
         Lsum += ml_s[w][1][hh] * e[w];
       }
-      float scale = 1.0f;
+      float scale;
       if (a.splits == 1) {
         const float sink2 = a.sink[head] * kLog2e;
         const float Mt = fmaxf(M, sink2);
@@ -989,9 +984,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
         const float Z = Lsum * corr + exp2f(sink2 - Mt);
         scale = corr / Z;
         if (a.lse && c4 == 0) a.lse[static_cast<long long>(t) * a.H + head] = (Mt + log2f(Z)) * kLn2;
-      } else if (c4 == 0) {
-        a.part_ml[static_cast<long long>(ts) * a.H + head] = make_float2(M, Lsum);
+      } else {
+        // the span's partial, normalised by its own sum (an empty span: 0)
+        scale = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+        if (c4 == 0) a.part_ml[static_cast<long long>(ts) * a.H + head] = make_float2(M, Lsum);
       }
+      uint16_t* dst = (a.splits == 1)
+                          ? a.out + (static_cast<long long>(t) * a.H + head) * D
+                          : a.part_o + (static_cast<long long>(ts) * a.H + head) * D;
 #pragma unroll
       for (int c = c4; c < D; c += 64) {
         v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -999,38 +999,36 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
         for (int w = 0; w < kAttnWaves; ++w)
           acc += *reinterpret_cast<const v4f*>(
                      reinterpret_cast<const float*>(slot_s + w * SS) + hh * OSTR + c) * e[w];
-        if (a.splits == 1) {
-          acc *= scale;
-          uint2 pk;
-          pk.x = pack_bf16x2(acc[0], acc[1]);
-          pk.y = pack_bf16x2(acc[2], acc[3]);
-          *reinterpret_cast<uint2*>(a.out + (static_cast<long long>(t) * a.H + head) * D + c) = pk;
-        } else {
-          *reinterpret_cast<v4f*>(a.part_o + (static_cast<long long>(ts) * a.H + head) * D + c) = acc;
-        }
+        acc *= scale;
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[0], acc[1]);
+        pk.y = pack_bf16x2(acc[2], acc[3]);
+        *reinterpret_cast<uint2*>(dst + c) = pk;
       }
     }
   }
 }
 
 // Combine the span partials of each (row, head) with the sink: one wave per
-// (row, head).  Lane l owns channels [8l, 8l + 8) of every partial (D = 512;
-// D / 64 channels in general).  With at most 64 spans (MANY false) lane s
-// holds span s's (max, sum) and the weights travel by lane shuffles; with
-// more, lanes stride over the spans for the max and the denominator and each
-// chunk of eight partials loads its spans' pairs too.  The first chunk goes
-// out with the pairs of the max pass, so a row of at most 64 spans costs one
-// memory latency before its sums.
+// (row, head).  Span s contributes its normalised partial O_s with weight
+// l_s * 2^(m_s - M) (M the max over the spans' maxima and the sink), so
+//   out = sum_s w_s O_s / (sum_s w_s + 2^(sink - M)),  lse = (M + log2 Z) ln 2.
+// Lane l owns channels [8l, 8l + 8) of every partial (D = 512; D / 64
+// channels in general).  With at most 64 spans (MANY false) lane s holds span
+// s's (max, sum) and the weights travel by lane reads; with more, lanes
+// stride over the spans for the max and the denominator and each chunk of
+// eight partials loads its spans' pairs too.  The first chunk goes out with
+// the pairs of the max pass, so a row of at most 64 spans costs one memory
+// latency before its sums.
 constexpr int kMergeChunk = 8;
 
 template <int D, bool MANY>
 __global__ void __launch_bounds__(64) attn_merge_kernel(
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml,
+    const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
     const float* __restrict__ sink, int splits, int H, int num_tokens,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int CPL = D / 64;            // channels per lane
-  constexpr int V4 = CPL >= 4 ? CPL / 4 : 1;
-  static_assert(CPL % 4 == 0 || CPL == 1 || CPL == 2, "channels per lane");
+  static_assert(CPL == 1 || CPL == 2 || CPL == 4 || CPL == 8, "channels per lane");
   const int t = blockIdx.x / H;
   const int h = blockIdx.x % H;
   if (t >= num_tokens) return;
@@ -1057,19 +1055,25 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
         if (sp >= splits) cml[u] = make_float2(neg_inf, 0.0f);
       }
       // a span past the list reads span 0; its weight is never applied
-      const float* po = part_o + (sl * H + h) * D + lane * CPL;
-      if constexpr (CPL >= 4) {
-#pragma unroll
-        for (int v = 0; v < V4; ++v) {
-          const v4f x = *reinterpret_cast<const v4f*>(po + 4 * v);
-          chunk[u][4 * v] = x[0];
-          chunk[u][4 * v + 1] = x[1];
-          chunk[u][4 * v + 2] = x[2];
-          chunk[u][4 * v + 3] = x[3];
-        }
+      const uint16_t* po = part_o + (sl * H + h) * D + lane * CPL;
+      if constexpr (CPL == 1) {
+        chunk[u][0] = bf16_to_f32(*po);
       } else {
+        uint32_t w[CPL / 2];
+        if constexpr (CPL == 8) {
+          const uint4 x = *reinterpret_cast<const uint4*>(po);
+          w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+        } else if constexpr (CPL == 4) {
+          const uint2 x = *reinterpret_cast<const uint2*>(po);
+          w[0] = x.x; w[1] = x.y;
+        } else {
+          w[0] = *reinterpret_cast<const uint32_t*>(po);
+        }
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) chunk[u][i] = po[i];
+        for (int i = 0; i < CPL / 2; ++i) {
+          chunk[u][2 * i] = __uint_as_float(w[i] << 16);
+          chunk[u][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
       }
     }
   };
@@ -1085,8 +1089,8 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
   if constexpr (MANY)
     for (int s = lane + 64; s < splits; s += 64) M = fmaxf(M, part_ml[(tbase + s) * H + h].x);
   M = fmaxf(wave_max(M), sink2);
-  const float w_l = ml.x == neg_inf ? 0.0f : exp2f(ml.x - M);   // lane's span weight
-  float z = ml.y * w_l;
+  const float w_l = ml.x == neg_inf ? 0.0f : ml.y * exp2f(ml.x - M);   // lane's span weight
+  float z = w_l;
   if constexpr (MANY) {
     for (int s = lane + 64; s < splits; s += 64) {
       const float2 m2 = part_ml[(tbase + s) * H + h];
@@ -1099,7 +1103,7 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
       float w;
-      if constexpr (MANY) w = cml[u].x == neg_inf ? 0.0f : exp2f(cml[u].x - M);
+      if constexpr (MANY) w = cml[u].x == neg_inf ? 0.0f : cml[u].y * exp2f(cml[u].x - M);
       else w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), (s0 + u) & 63));
       if (s0 + u < splits) {
 #pragma unroll
@@ -1152,10 +1156,10 @@ SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   return SplitPlan{true, (lmax + sp - 1) / sp, sp};
 }
 
-// Decode workspace: the FP32 partials [T][splits][H][D] and their (max, sum)
-// pairs [T][splits][H].
+// Decode workspace: the BF16 normalised partials [T][splits][H][D], then
+// their FP32 (max, sum) pairs [T][splits][H].
 inline size_t attn_ws_bytes(int T, int splits, int H, int D) {
-  return static_cast<size_t>(T) * splits * H * (D + 2) * sizeof(float);
+  return static_cast<size_t>(T) * splits * H * (static_cast<size_t>(D) * 2 + 8);
 }
 
 // Largest decode workspace over the active counts 1 .. T: counts from
@@ -1296,9 +1300,9 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
     if (!workspace || workspace_bytes < need) return CSA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
     char* w = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<float*>(w);
+    a.part_o = reinterpret_cast<uint16_t*>(w);
     a.part_ml = reinterpret_cast<float2*>(w + static_cast<size_t>(num_tokens) * plan.splits * H *
-                                                  D * sizeof(float));
+                                                  D * sizeof(uint16_t));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (D) {

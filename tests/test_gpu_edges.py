@@ -78,6 +78,31 @@ def test_topk_ties_nan_zero_inf(stride):
     _compare_topk(sc, pos, 1, 512, f"ties stride {stride}")
 
 
+@pytest.mark.parametrize("case", ["ascending", "clustered", "outliers", "few_groups"])
+def test_topk_long_row_group_bound(case):
+    """Long rows take a threshold from the maxima of 32-score groups: rows
+    whose best keys pack into few groups (ascending, clustered), heavy-tailed
+    rows, and a row with more keys to choose than groups, exactly as the
+    oracle."""
+    print(f"[edges] topk long row {case}", flush=True)
+    rng = np.random.default_rng(31)
+    T, stride, k = 4, 1 << 18, 2048
+    sc = rng.standard_normal((T, stride)).astype(np.float32)
+    pos = np.full(T, stride - 1)
+    if case == "ascending":
+        sc[0] = np.arange(stride, dtype=np.float32)
+        sc[1] = np.sort(sc[1])
+    elif case == "clustered":
+        sc[:, 1000:1000 + 3 * k] += 6.0        # the best keys in one run of groups
+        sc[2, ::64] += 9.0                      # one high key in every other group
+    elif case == "outliers":
+        out = rng.random((T, stride)) < 0.05
+        sc[out] *= 4.0
+    else:
+        pos[:] = [40000, 50000, 65535, 32768]   # fewer groups than k at 40000 and 50000
+    _compare_topk(sc, pos, 1, k, f"long row {case}")
+
+
 def test_topk_workspace_needs_no_clearing():
     """The long-row workspace carries no state between calls: garbage in it
     (here 0xff bytes, then the leftovers of a previous call) changes nothing."""

@@ -187,14 +187,16 @@ def test_hca_prefill_and_bound():
 
 
 def test_hca_many_spans():
-    """Two rows over a 1,048,576-token HCA context: 8,320 keys per row in 65
-    spans, past the 64 a merge wave holds one per lane."""
+    """Two rows over a 5,000,000-token HCA context: 39,062 visible compressed
+    rows plus the window per row, split into more spans than the 64 a merge
+    wave holds one per lane."""
     from synthetic.configs import CsaConfig
     csa = _lib()
-    ctx = 1 << 20
+    ctx = 5_000_000
     cfg = CsaConfig(name="hca_many", description="HCA rows with more than 64 spans",
                     rows_per_request=(2,), positions=((ctx - 2, ctx - 1),), H=16, D=128, R=32,
-                    Hi=4, Di=32, W=128, ratio=128, k=8192, context=ctx, mode="hca")
+                    Hi=4, Di=32, W=128, ratio=128, k=40000, context=ctx,
+                    rope_neg_rows=(0, 1), rope_capacity=4096, mode="hca")   # identity rope rows
     x = synthetic.make_inputs(cfg, seed=17).t
     step = csa.step_for_config(cfg, x)
     step.run()

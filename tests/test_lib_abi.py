@@ -99,10 +99,11 @@ def test_attention_host_checks(lib):
         assert f(*bad) == -1
         bad = list(base); bad[23] = 0                 # no active rows
         assert f(*bad) == 0
-    # decode with several splits needs the workspace the helper reports
-    need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 512, 128)
+    # decode lists split into several spans need the workspace the helper
+    # reports
+    need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 2048, 128)
     assert need > 0
-    base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
+    base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 2048, 2, FAKE, 2, FAKE, 2, 128,
             FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, None, 0, None, None]
     assert lib.csa_sparse_attn_decode(*base) == -5
 
@@ -120,9 +121,9 @@ def test_attention_selection_bounds(lib):
     assert lib.csa_sparse_attn_prefill(*no_sel) == -4  # ring schedule: list past 4224
     bad = list(no_sel); bad[10] = (1 << 20) + 1
     assert lib.csa_sparse_attn_decode(*bad) == -3
-    # whole span partials (O and its (max, sum) per head), at least two spans
+    # whole span partials (BF16 O and FP32 (max, sum) per head), at least two
     need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 8192, 128)
-    per_span = 8 * 64 * (512 + 2) * 4
+    per_span = 8 * 64 * (512 * 2 + 8)
     assert need % per_span == 0 and need // per_span >= 2
 
 
@@ -201,18 +202,18 @@ def test_attention_workspace_covers_padded_batches(lib):
     T.  T = 300 with 10 active rows splits the key lists (partials), although
     300 active rows would not."""
     f = lib.csa_sparse_attn_workspace_bytes
-    for k, w in ((512, 128), (2048, 128), (8192, 128), (4096, 0)):
+    for k, w in ((1024, 128), (2048, 128), (8192, 128), (4096, 0)):
         sizes = [f(n, 64, 512, k, w) for n in range(1, 301)]
         assert f(300, 64, 512, k, w) == max(sizes)
         assert f(300, 64, 512, k, w) >= f(10, 64, 512, k, w) > 0
     # the launcher's own need for 10 active rows is what the helper reports:
     # one byte less is refused on the host, before any launch
-    need10 = f(10, 64, 512, 512, 128)
-    args = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,
+    need10 = f(10, 64, 512, 2048, 128)
+    args = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 2048, 2, FAKE, 2, FAKE, 2, 128,
             FAKE, 0.04, FAKE, FAKE, 1, 300, 10, 64, 512, FAKE, None, FAKE, need10 - 1, None,
             None]
     assert lib.csa_sparse_attn_decode(*args) == -5
-    assert f(300, 64, 512, 512, 128) >= need10
+    assert f(300, 64, 512, 2048, 128) >= need10
 
 
 def test_noalloc_decode_host_checks(lib):
@@ -222,11 +223,11 @@ def test_noalloc_decode_host_checks(lib):
     cap = lib.csa_sparse_attn_noalloc_max_bytes()
     assert cap == 32 << 20
     f = lib.csa_sparse_attn_decode_noalloc
-    # 200 active rows of 4096 + 128 keys: two spans of whole-head partials
-    need = lib.csa_sparse_attn_workspace_bytes(200, 64, 512, 4096, 128)
+    # 255 active rows of 895 + 128 keys: eight 128-entry spans per row
+    need = lib.csa_sparse_attn_workspace_bytes(255, 64, 512, 895, 128)
     assert need > cap
-    big = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 4096, 1, FAKE, 2, FAKE, 2, 128,
-           FAKE, 0.04, FAKE, FAKE, 1, 200, 200, 64, 512, FAKE, None, None, None]
+    big = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 895, 1, FAKE, 2, FAKE, 2, 128,
+           FAKE, 0.04, FAKE, FAKE, 1, 255, 255, 64, 512, FAKE, None, None, None]
     assert f(*big) == -7
     assert lib.csa_status_string(-7).decode().startswith("CSA_ERR_SCRATCH")
     base = [FAKE, FAKE, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE, 2, 128,

@@ -4,9 +4,9 @@ csa_sparse_attn_decode_noalloc runs the same kernels as
 csa_sparse_attn_decode, with the split partials in the library's static
 device array instead of a caller workspace, so its outputs must equal the
 workspace call's bit for bit.  Two calls in a row on one GPU: a ratio-1 decode
-batch whose long key lists take the split ring (the larger partials), then a
-smaller ratio-2 batch of three active rows on the short-list schedule, which
-must not see anything the first call left in the array.
+batch of eight rows whose key lists are split into spans (the larger
+partials), then three active rows of another draw, which must not see
+anything the first call left in the array.
 """
 import numpy as np
 import pytest
@@ -34,7 +34,7 @@ def _attn_args(step, num_tokens):
 def _compare(csa, name, num_tokens):
     cfg = synthetic.get(name)
     print(f"[noalloc] {cfg.name}: num_tokens={num_tokens}", flush=True)
-    x = synthetic.make_inputs(cfg, seed=8).t
+    x = synthetic.make_inputs(cfg, seed=8 + num_tokens).t
     step = csa.step_for_config(cfg, x, num_tokens=num_tokens)
     step.rope()
     step.index()
@@ -68,6 +68,6 @@ def _compare(csa, name, num_tokens):
 
 def test_noalloc_matches_workspace_call_twice():
     csa = _csa()
-    big = _compare(csa, "c3", 8)     # split ring: long lists
-    small = _compare(csa, "c2", 3)   # short lists, fewer rows
+    big = _compare(csa, "c3", 8)     # four spans per row, merged
+    small = _compare(csa, "c3", 3)   # the same lists, fewer rows
     assert small < big
