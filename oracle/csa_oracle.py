@@ -255,6 +255,22 @@ def mx_rows(codes, scale_bytes, group=32):
     return v * np.repeat(sc, group, axis=-1)
 
 
+def decode_e4m3(codes):
+    """Values of FP8 E4M3 codes in the OCP "E4M3FN" form: sign | 4-bit
+    exponent (bias 7) | 3-bit mantissa; exponent 0 is subnormal
+    (mantissa / 8 * 2^-6), otherwise (1 + mantissa / 8) * 2^(e - 7); there is
+    no infinity, and S.1111.111 is NaN, so the largest magnitude is 448 ([V41]
+    cache ABI: the window KV payload is MXFP8 E4M3 and the compressed KV
+    scales are E4M3).  Returns float64 of the same shape."""
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    mag = np.where((e == 15) & ((b & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
 def index_scores_mxfp4(q_fp4, q_sc, head_w, idx_fp4, idx_sc, block_table, query_start_loc,
                        positions, num_tokens, ratio, score_stride, key_chunk: int = 1 << 15):
     """The indexer score with the FP4 index plane ([ATOM] "Current execution
@@ -502,6 +518,58 @@ def deterministic_selection(p, ratio, k):
     return np.arange(m, dtype=np.int64), (EFLAG_TOPK_RANGE if int(k) > 0 and n > m else 0)
 
 
+class KvPlane:
+    """A paged KV cache, read row by row: ``num_blocks`` pages of 128 rows and
+    ``rows(flat)`` -> float64 [len(flat), D], the values of flat pool rows
+    (page * 128 + slot).  Attention reads keys/values only through this, so
+    the BF16 cache and the low-bit caches of [V41]'s cache ABI share the
+    attention arithmetic; the low-bit planes are dequantised on read (the
+    pages' references quantise on cache publication and dequantise on cache
+    reads)."""
+
+    def __init__(self, num_blocks, d, rows):
+        self.num_blocks = int(num_blocks)
+        self.d = int(d)
+        self._rows = rows
+
+    def rows(self, flat):
+        return self._rows(np.asarray(flat, dtype=np.int64))
+
+
+def bf16_plane(kv):
+    """BF16 KV cache [blocks, 128, D] (uint16 bit patterns)."""
+    kv = np.asarray(kv)
+    nb, _, d = kv.shape
+    flat = kv.reshape(nb * PAGE, d)
+    return KvPlane(nb, d, lambda r: bf16_to_f64(flat[r]))
+
+
+def mxfp8_plane(payload, scales):
+    """The window KV plane of [V41]'s cache ABI: payload [blocks, 128, D] MXFP8
+    E4M3 codes, scales [blocks, 128, D / 32] E8M0 bytes; channel c of a row is
+    e4m3(payload[c]) * 2^(scales[c // 32] - 127)."""
+    payload = np.asarray(payload, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    nb, _, d = payload.shape
+    pf = payload.reshape(nb * PAGE, d)
+    sf = scales.reshape(nb * PAGE, d // 32)
+    return KvPlane(nb, d, lambda r: decode_e4m3(pf[r]) * np.repeat(decode_e8m0(sf[r]), 32, axis=-1))
+
+
+def mxfp4_e4m3_plane(payload, scales):
+    """The compressed KV plane of [V41]'s cache ABI: payload [blocks, 128, D / 2]
+    of packed E2M1 codes (element 2i in bits 0-3 of byte i), scales
+    [blocks, 128, D / 16] E4M3 codes; channel c of a row is
+    e2m1(c) * e4m3(scales[c // 16])."""
+    payload = np.asarray(payload, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    nb, _, half = payload.shape
+    pf = payload.reshape(nb * PAGE, half)
+    sf = scales.reshape(nb * PAGE, (2 * half) // 16)
+    return KvPlane(nb, 2 * half,
+                   lambda r: decode_e2m1(pf[r]) * np.repeat(decode_e4m3(sf[r]), 16, axis=-1))
+
+
 def kv_rows_for_query(t, b, p, topk_row, ratio, window, cmp_block_table, num_cmp_blocks,
                       win_block_table, num_win_blocks, k=None):
     """The key/value rows of one query, window first then selected compressed
@@ -559,15 +627,18 @@ def sparse_attn(q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table,
     pages (BLOCK_RANGE), are flagged and left out; negative selected entries
     are padding.
 
+    cmp_kv and win_kv are BF16 caches [blocks, 128, D] (uint16 bit patterns)
+    or KvPlane row sources (the low-bit planes, dequantised on read).
+
     Returns (out float64 [num_tokens, H, D], lse float64 [num_tokens, H], err)."""
     nt = int(num_tokens)
     T, H, D = q.shape
     half = rope_cos.shape[1]
     qsl = np.asarray(query_start_loc)
-    ncb = cmp_kv.shape[0]
-    nwb = win_kv.shape[0]
-    cmp_flat = cmp_kv.reshape(ncb * PAGE, D)
-    win_flat = win_kv.reshape(nwb * PAGE, D)
+    cmp_src = cmp_kv if isinstance(cmp_kv, KvPlane) else bf16_plane(cmp_kv)
+    win_src = win_kv if isinstance(win_kv, KvPlane) else bf16_plane(win_kv)
+    ncb = cmp_src.num_blocks
+    nwb = win_src.num_blocks
     sink = np.asarray(attn_sink, dtype=np.float64)
     out = np.zeros((nt, H, D), dtype=np.float64)
     lse = np.zeros((nt, H), dtype=np.float64)
@@ -584,7 +655,8 @@ def sparse_attn(q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table,
                                             ratio, window, cmp_block_table, ncb,
                                             win_block_table, nwb, k)
         err |= e
-        kv = np.concatenate([bf16_to_f64(win_flat[wrows]), bf16_to_f64(cmp_flat[crows])], axis=0)
+        kv = np.concatenate([win_src.rows(wrows).reshape(-1, D),
+                             cmp_src.rows(crows).reshape(-1, D)], axis=0)
         qt = bf16_to_f64(q[t])                                          # [H, D]
         qt[:, rope_offset:rope_offset + 2 * half] = rotate_adjacent_pairs(
             qt[:, rope_offset:rope_offset + 2 * half], rope_cos[t], rope_sin[t])
