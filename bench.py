@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c5",
-                    help="c1..c11 (default c5: max-context ratio-1 decode)")
+                    help="c1..c13 (default c5: max-context ratio-1 decode)")
     ap.add_argument("--copies", type=int, default=0, help="input copies (0 = auto, cold L2/MALL)")
     ap.add_argument("--warm", action="store_true", help="one input copy (cache-warm timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -95,6 +95,8 @@ def work_model(cfg, x, topk_idx: np.ndarray):
     nv = np.array([visible(p, cfg.ratio) for p in pos])
     idx_keys = 0
     kv_rows = 0
+    kv_bytes = 0   # KV bytes of those rows (window and compressed rows differ in the MX planes)
+    win_rb, cmp_rb = cfg.kv_row_bytes
     pairs = 0
     scored = 0   # index scores written (score rows, or the mask's slots)
     kb, blk = getattr(cfg, "cand_kb", 0), getattr(cfg, "cand_block", 8)
@@ -126,6 +128,7 @@ def work_model(cfg, x, topk_idx: np.ndarray):
             sel.update(s)
             pairs += len(w) + len(s)
         kv_rows += len(win) + len(sel)
+        kv_bytes += len(win) * win_rb + len(sel) * cmp_rb
     indexed = mode in ("csa", "reindex", "hier_full")
     kbytes = cfg.index_key_bytes           # one index key: payload + scales
     qbytes = kbytes + 4                     # one query head: payload + scales + weight
@@ -145,18 +148,18 @@ def work_model(cfg, x, topk_idx: np.ndarray):
         "rope": 8 * T * R + 4 * T,   # read + write cos and sin rows (R/2 FP32 each), positions
         "index": idx_keys * kbytes + q_side + 4 * scored + mask_bytes * (mode == "reindex"),
         "topk": 4 * ranked + 8 * T * k + mask_bytes * (mode == "reindex"),
-        "attn": kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + sel_bytes + 4 * T * R,
+        "attn": kv_bytes + 4 * T * H * D + 4 * T * H + sel_bytes + 4 * T * R,
     }
     if mode == "hier_full":   # block maxima over every visible score, then the mask
         st["cand"] = 4 * int(nv.clip(max=cfg.score_stride).sum()) + mask_bytes
     if not indexed:
         st = {"rope": st["rope"], "attn": st["attn"]}
-    step = (idx_keys * kbytes + kv_rows * 2 * D + 4 * T * H * D + 4 * T * H + q_side
+    step = (idx_keys * kbytes + kv_bytes + 4 * T * H * D + 4 * T * H + q_side
             + 2 * sel_bytes + 4 * T * R + mask_bytes)
     flops = {"attn": pairs * H * D * 4,
              "index": int(sum(nv[t] for t in range(T))) * Hi * Di * 2}
     return dict(stage_bytes=st, step_bytes=step, flops=flops, kv_rows=kv_rows,
-                idx_keys=idx_keys, pairs=pairs)
+                kv_bytes=kv_bytes, idx_keys=idx_keys, pairs=pairs)
 
 
 def source_hash(name: str) -> str:
@@ -264,8 +267,13 @@ def cpu_baseline(cfg, x, budget_s: float):
             c_ = time.perf_counter()
             idx = None if mode == "hca" else np.zeros((n, 0), np.int32)
         d_ = time.perf_counter()
-        oracle.sparse_attn(sub["q"], rc, rs, cfg.rope_offset, sub["cmp_kv"],
-                           sub["cmp_block_table"], idx, cfg.ratio, sub["win_kv"],
+        if cfg.kv_format == "mx":   # the oracle dequantises the low-bit planes on read
+            cmp_kv = oracle.mxfp4_e4m3_plane(sub["cmp_fp4"], sub["cmp_scale"])
+            win_kv = oracle.mxfp8_plane(sub["win_fp8"], sub["win_scale"])
+        else:
+            cmp_kv, win_kv = sub["cmp_kv"], sub["win_kv"]
+        oracle.sparse_attn(sub["q"], rc, rs, cfg.rope_offset, cmp_kv,
+                           sub["cmp_block_table"], idx, cfg.ratio, win_kv,
                            sub["win_block_table"], cfg.W, sub["attn_sink"], cfg.softmax_scale,
                            sub["query_start_loc"], sub["positions"], n, k=cfg.k)
         e_ = time.perf_counter()
@@ -310,7 +318,8 @@ def main():
     idx_touch = (cfg.T * cfg.cand_kb * cfg.cand_block if cfg.mode == "reindex"
                  else cfg.B * cfg.n_cmp_per_request)
     per_copy_touch = (idx_touch * cfg.index_key_bytes +
-                      cfg.T * (cfg.k + cfg.W) * 2 * cfg.D + 4 * cfg.T * cfg.H * cfg.D)
+                      cfg.T * (cfg.k * cfg.kv_row_bytes[1] + cfg.W * cfg.kv_row_bytes[0]) +
+                      4 * cfg.T * cfg.H * cfg.D)
     if args.warm:
         copies = 1
     elif args.copies > 0:
@@ -387,14 +396,16 @@ def main():
         long_rows = cfg.score_stride > 32768
         if first.mode == "reindex":
             long_rows = first.score_stride > 32768
-        split_ring = (not first.prefill and cfg.W + cfg.k >= 1024)
+        split_ring = (not first.prefill and cfg.W + cfg.k >= 1024 and cfg.kv_format == "bf16")
         names = {"rope": "rope_rows_kernel",
                  "index": "index_cand_kernel" if first.mode == "reindex" else "index_score_kernel",
                  "topk": ("topk_sample_kernel + topk_filter_kernel + topk_final_kernel" if long_rows
                           else "topk_small_kernel"),
                  "cand": "block_max_kernel + top-k of the block scores",
                  "attn": ("attn_kernel + attn_merge_kernel" if split_ring
-                          else "attn_decode_kernel + attn_merge_kernel")}
+                          else ("attn_decode_kernel (low-bit KV) + attn_merge_kernel"
+                                if cfg.kv_format == "mx"
+                                else "attn_decode_kernel + attn_merge_kernel"))}
         ach = wm["stage_bytes"][dom] / (stage_ms[dom] / 1e3) / 1e9
         roof = {"kernel": names[dom], "bound": "hbm", "achieved": round(ach, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
@@ -411,6 +422,8 @@ def main():
         "config": {"workload": cfg.name, "rows": cfg.T, "requests": cfg.B, "heads": cfg.H,
                    "head_dim": cfg.D, "ratio": cfg.ratio, "top_k": cfg.k, "window": cfg.W,
                    "compressed_rows_per_request": cfg.n_cmp_per_request,
+                   "kv_cache": ("window MXFP8 E4M3 + E8M0/32, compressed MXFP4 E2M1 + E4M3/16"
+                                if cfg.kv_format == "mx" else "bf16"),
                    "indexer": ((f"{cfg.Hi}x{cfg.Di}" +
                                 (" mxfp4" if cfg.index_format == "mxfp4" else " int8"))
                                if first.mode in ("csa", "reindex", "hier_full") else "none"),

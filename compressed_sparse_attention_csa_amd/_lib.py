@@ -55,6 +55,11 @@ _SIGS = {
                                            _P, _P, _SZ, _P, _P]),
 }
 _SIGS["csa_sparse_attn_prefill"] = _SIGS["csa_sparse_attn_decode"]
+_SIGS["csa_sparse_attn_mx_workspace_bytes"] = _SIGS["csa_sparse_attn_workspace_bytes"]
+# the decode arguments with a scale plane after each payload plane
+_SIGS["csa_sparse_attn_decode_mx"] = (
+    ctypes.c_int, _SIGS["csa_sparse_attn_decode"][1][:6] + [_P]
+    + _SIGS["csa_sparse_attn_decode"][1][6:13] + [_P] + _SIGS["csa_sparse_attn_decode"][1][13:])
 _SIGS["csa_sparse_attn_noalloc_max_bytes"] = (_SZ, [])
 # the decode arguments without (workspace, workspace_bytes)
 _SIGS["csa_sparse_attn_decode_noalloc"] = (
@@ -283,3 +288,49 @@ def csa_sparse_attn_decode_noalloc(*args, **kw) -> None:
 
 def csa_sparse_attn_prefill(*args, **kw) -> None:
     _attn("csa_sparse_attn_prefill", *args, **kw)
+
+
+def csa_sparse_attn_mx_workspace_bytes(T: int, H: int, D: int, k: int, window: int) -> int:
+    return int(load().csa_sparse_attn_mx_workspace_bytes(T, H, D, k, window))
+
+
+def csa_sparse_attn_decode_mx(q, rope_cos, rope_sin, rope_offset, cmp_fp4, cmp_scale,
+                              cmp_block_table, topk_idx, ratio, win_fp8, win_scale,
+                              win_block_table, window, attn_sink, softmax_scale, query_start_loc,
+                              positions, num_tokens, out, lse=None, workspace=None, err=None,
+                              stream=None, k=None) -> None:
+    """Decode attention over the low-bit KV planes: cmp_fp4 uint8 [blocks, 128,
+    D/2] with cmp_scale uint8 [blocks, 128, D/16] (E4M3), win_fp8 uint8
+    [blocks, 128, D] with win_scale uint8 [blocks, 128, D/32] (E8M0).  The
+    other arguments are csa_sparse_attn_decode's."""
+    _need(q, _BF16, 3, "q")
+    _need(out, _BF16, 3, "out")
+    _need(win_fp8, (torch.uint8,), 3, "win_fp8")
+    _need(win_scale, (torch.uint8,), 3, "win_scale")
+    T, H, D = q.shape
+    if win_fp8.shape[2] != D or tuple(win_scale.shape) != (win_fp8.shape[0], PAGE, D // 32):
+        raise CsaError(f"window planes {tuple(win_fp8.shape)} / {tuple(win_scale.shape)} do not "
+                       f"match D = {D}")
+    if cmp_fp4 is not None:
+        _need(cmp_fp4, (torch.uint8,), 3, "cmp_fp4")
+        _need(cmp_scale, (torch.uint8,), 3, "cmp_scale")
+        if (cmp_fp4.shape[2] != D // 2
+                or tuple(cmp_scale.shape) != (cmp_fp4.shape[0], PAGE, D // 16)):
+            raise CsaError(f"compressed planes {tuple(cmp_fp4.shape)} / "
+                           f"{tuple(cmp_scale.shape)} do not match D = {D}")
+    if topk_idx is not None:
+        k = topk_idx.shape[1]
+    elif k is None:
+        raise CsaError("k is required when topk_idx is None")
+    rope_dim = 2 * rope_cos.shape[1]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().csa_sparse_attn_decode_mx(
+        _ptr(q), _ptr(rope_cos), _ptr(rope_sin), rope_dim, int(rope_offset), _ptr(cmp_fp4),
+        _ptr(cmp_scale), 0 if cmp_fp4 is None else cmp_fp4.shape[0], _ptr(cmp_block_table),
+        0 if cmp_block_table is None else cmp_block_table.shape[1], _ptr(topk_idx), int(k),
+        int(ratio), _ptr(win_fp8), _ptr(win_scale), win_fp8.shape[0], _ptr(win_block_table),
+        win_block_table.shape[1], int(window), _ptr(attn_sink), float(softmax_scale),
+        _ptr(query_start_loc), _ptr(positions), query_start_loc.shape[0] - 1, T,
+        int(num_tokens), H, D, _ptr(out), _ptr(lse), _ptr(workspace), wsb, _ptr(err),
+        _stream(stream))
+    _check(st, "csa_sparse_attn_decode_mx")

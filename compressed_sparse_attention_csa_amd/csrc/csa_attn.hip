@@ -23,7 +23,7 @@
 // Decode kernel (small batches): a work-group owns one (row, 16-head group,
 // 128-entry span); each wave gathers and multiplies its own 32-row tile, so a
 // span costs one memory latency and every key byte is read from LDS once.
-// BF16 partials of the spans, normalised by their own sums, are merged with the
+// FP32 partials of the spans, normalised by their own sums, are merged with the
 // sink by a third kernel.
 //
 // Tile code.  Rows sit at a 16-byte-padded stride so the K operand reads
@@ -81,6 +81,13 @@ struct AttnArgs {
   const int32_t* win_bt;
   int max_win_blocks;
   int window;
+  // low-bit planes (decode kernel with MX = true): window rows as MXFP8 E4M3
+  // codes [.][D] with one E8M0 byte per 32 channels, compressed rows as packed
+  // E2M1 codes [.][D/2] with one E4M3 byte per 16 channels
+  const uint8_t* win_fp8;
+  const uint8_t* win_sc;
+  const uint8_t* cmp_fp4;
+  const uint8_t* cmp_sc;
   const float* sink;
   float scale_log2;  // softmax_scale * log2(e)
   const int32_t* qsl;
@@ -90,7 +97,7 @@ struct AttnArgs {
   int H;
   uint16_t* out;
   float* lse;
-  uint16_t* part_o;  // BF16 [T][splits][H][D]: span partials normalised by their sum
+  float* part_o;     // FP32 [T][splits][H][D]: span partials normalised by their sum
   float2* part_ml;   // [T][splits][H]: (max, sum) of each span, base-2 logits
   int splits;
   int ring_span;     // ring schedule with splits > 1: list entries per span
@@ -646,24 +653,29 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
       __syncthreads();
       if (again) continue;
       __syncthreads();   // f_s is complete
-      // the output rows, or with splits > 1 the span's BF16 partial (f is
-      // then 1 / its sum)
+      // the BF16 output rows, or with splits > 1 the span's FP32 partial (f
+      // is then 1 / its sum)
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         const int hh = ht * 16 + col;
         if (hh >= a.H) continue;
         const float f = f_s[hh];
-        uint16_t* orow = (a.splits > 1 ? a.part_o + static_cast<long long>(item) * a.H * D
-                                       : a.out + static_cast<long long>(t) * a.H * D) +
-                         static_cast<long long>(hh) * D + d0;
+        const long long roff = static_cast<long long>(hh) * D + d0;
+        if (a.splits > 1) {
+          float* prow = a.part_o + static_cast<long long>(item) * a.H * D + roff;
 #pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) {
-          // o_acc[dt][ht][r] is channel d0 + dt*16 + grp*4 + r of head hh
-          const int d = dt * 16 + grp * 4;
-          uint2 w;
-          w.x = pack_bf16x2(o_acc[dt][ht][0] * f, o_acc[dt][ht][1] * f);
-          w.y = pack_bf16x2(o_acc[dt][ht][2] * f, o_acc[dt][ht][3] * f);
-          *reinterpret_cast<uint2*>(orow + d) = w;
+          for (int dt = 0; dt < DTW; ++dt)
+            *reinterpret_cast<v4f*>(prow + dt * 16 + grp * 4) = o_acc[dt][ht] * f;
+        } else {
+          uint16_t* orow = a.out + static_cast<long long>(t) * a.H * D + roff;
+#pragma unroll
+          for (int dt = 0; dt < DTW; ++dt) {
+            // o_acc[dt][ht][r] is channel d0 + dt*16 + grp*4 + r of head hh
+            uint2 w;
+            w.x = pack_bf16x2(o_acc[dt][ht][0] * f, o_acc[dt][ht][1] * f);
+            w.y = pack_bf16x2(o_acc[dt][ht][2] * f, o_acc[dt][ht][3] * f);
+            *reinterpret_cast<uint2*>(orow + dt * 16 + grp * 4) = w;
+          }
         }
       }
       break;
@@ -686,7 +698,18 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
 // for the merge kernel.
 constexpr int kSpan = kAttnWaves * kTile;   // list entries per decode work-group
 
-template <int D>
+// Two E2M1 codes (byte BS of w, the lower-indexed one in bits 0-3) times an
+// FP32 scale, as a BF16 pair.  The products are BF16 values (at most 6
+// significant bits for an E4M3 scale), so their upper halves are exact.
+template <int BS>
+__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t w, float sc) {
+  const v2f_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BS);
+  const float lo = e[0] * sc, hi = e[1] * sc;
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                               0x07060302u);
+}
+
+template <int D, bool MX>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a) {
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
@@ -822,8 +845,43 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   //      from LDS first, so the direct-to-LDS loads issue back to back.
   uint8_t* myslot = slot_s + wave * SS;
   const int j0 = wave * kTile;
-  if (j0 < n_valid) {
-    constexpr int NI = kTile / RPI;
+  constexpr int NI = kTile / RPI;
+  // low-bit rows go through registers: lane (row ins * RPI + lane / NC,
+  // chunk lane % NC) holds the codes of channels 8 * chunk .. + 7 and their
+  // group's scale byte until the conversion below
+  [[maybe_unused]] uint2 mx_pay[MX ? NI : 1];
+  [[maybe_unused]] uint32_t mx_sc[MX ? NI : 1];
+  [[maybe_unused]] uint32_t mx_row[MX ? NI : 1];
+  if constexpr (MX) {
+    if (j0 < n_valid) {
+      const int chunk = lane % NC;
+      const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
+#pragma unroll
+      for (int ins = 0; ins < NI; ++ins) {
+        const int j = j0 + ins * RPI + lane / NC;
+        mx_row[ins] = (j < n_valid) ? row_s[j] : kNoRow;
+      }
+      // one 8-byte payload load and one scale-byte load per row, from
+      // addresses picked without branches (a branch per row would serialise
+      // the loads): an E2M1 chunk is the half (chunk & 1) of an aligned
+      // 8-byte word shared with its neighbour; a masked row reads the
+      // query's first bytes (always present) and is zeroed after conversion
+#pragma unroll
+      for (int ins = 0; ins < NI; ++ins) {
+        const uint32_t r = mx_row[ins];
+        const long long row = static_cast<long long>(r & ~kWinBit);
+        const bool win = (r & kWinBit) != 0u;
+        const uint8_t* pay = win ? a.win_fp8 + row * D + chunk * 8
+                                 : a.cmp_fp4 + row * (D / 2) + (chunk >> 1) * 8;
+        const uint8_t* scp = win ? a.win_sc + row * (D / 32) + (chunk >> 2)
+                                 : a.cmp_sc + row * (D / 16) + (chunk >> 1);
+        pay = (r == kNoRow) ? dummy : pay;
+        scp = (r == kNoRow) ? dummy : scp;
+        mx_pay[ins] = *reinterpret_cast<const uint2*>(pay);
+        mx_sc[ins] = *scp;
+      }
+    }
+  } else if (j0 < n_valid) {
     uint32_t rr[NI];
 #pragma unroll
     for (int ins = 0; ins < NI; ++ins) {
@@ -872,7 +930,36 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   v4f o_acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's rows have landed in its slot
+  if constexpr (MX) {
+    // dequantise into the BF16 tile (exact: an E4M3 code times a power of two,
+    // or an E2M1 code times an E4M3 code, has at most 6 significant bits)
+    if (j0 < n_valid) {
+#pragma unroll
+      for (int ins = 0; ins < NI; ++ins) {
+        const uint32_t r = mx_row[ins];
+        uint4 v;
+        if (r & kWinBit) {
+          // the E8M0 byte as the exponent field of the FP32 scale operand:
+          // the conversion multiplies by 2^(byte - 127) (byte 255: NaN)
+          const float sc = __builtin_bit_cast(float, mx_sc[ins] << 23);
+          const uint32_t wx = mx_pay[ins].x, wy = mx_pay[ins].y;
+          v = uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, sc, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, sc, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, sc, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, sc, true))};
+        } else {
+          const float sc = __builtin_amdgcn_cvt_f32_fp8(mx_sc[ins], 0);
+          const uint32_t wx = (lane % NC) & 1 ? mx_pay[ins].y : mx_pay[ins].x;
+          v = uint4{fp4_pair_bf16<0>(wx, sc), fp4_pair_bf16<1>(wx, sc),
+                    fp4_pair_bf16<2>(wx, sc), fp4_pair_bf16<3>(wx, sc)};
+        }
+        if (r == kNoRow) v = uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4*>(myslot + ins * GS + lane * 16) = v;
+      }
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's rows have landed in its slot
+  }
 
   if (j0 < n_valid) {
     const uint8_t* tile = myslot;
@@ -989,9 +1076,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
         scale = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
         if (c4 == 0) a.part_ml[static_cast<long long>(ts) * a.H + head] = make_float2(M, Lsum);
       }
-      uint16_t* dst = (a.splits == 1)
-                          ? a.out + (static_cast<long long>(t) * a.H + head) * D
-                          : a.part_o + (static_cast<long long>(ts) * a.H + head) * D;
+      uint16_t* dst = a.out + (static_cast<long long>(t) * a.H + head) * D;
+      float* pdst = a.part_o + (static_cast<long long>(ts) * a.H + head) * D;
 #pragma unroll
       for (int c = c4; c < D; c += 64) {
         v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
@@ -1000,10 +1086,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
           acc += *reinterpret_cast<const v4f*>(
                      reinterpret_cast<const float*>(slot_s + w * SS) + hh * OSTR + c) * e[w];
         acc *= scale;
-        uint2 pk;
-        pk.x = pack_bf16x2(acc[0], acc[1]);
-        pk.y = pack_bf16x2(acc[2], acc[3]);
-        *reinterpret_cast<uint2*>(dst + c) = pk;
+        if (a.splits == 1) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[0], acc[1]);
+          pk.y = pack_bf16x2(acc[2], acc[3]);
+          *reinterpret_cast<uint2*>(dst + c) = pk;
+        } else {
+          *reinterpret_cast<v4f*>(pdst + c) = acc;
+        }
       }
     }
   }
@@ -1024,7 +1114,7 @@ constexpr int kMergeChunk = 8;
 
 template <int D, bool MANY>
 __global__ void __launch_bounds__(64) attn_merge_kernel(
-    const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml,
     const float* __restrict__ sink, int splits, int H, int num_tokens,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int CPL = D / 64;            // channels per lane
@@ -1055,25 +1145,17 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
         if (sp >= splits) cml[u] = make_float2(neg_inf, 0.0f);
       }
       // a span past the list reads span 0; its weight is never applied
-      const uint16_t* po = part_o + (sl * H + h) * D + lane * CPL;
-      if constexpr (CPL == 1) {
-        chunk[u][0] = bf16_to_f32(*po);
-      } else {
-        uint32_t w[CPL / 2];
-        if constexpr (CPL == 8) {
-          const uint4 x = *reinterpret_cast<const uint4*>(po);
-          w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-        } else if constexpr (CPL == 4) {
-          const uint2 x = *reinterpret_cast<const uint2*>(po);
-          w[0] = x.x; w[1] = x.y;
-        } else {
-          w[0] = *reinterpret_cast<const uint32_t*>(po);
-        }
+      const float* po = part_o + (sl * H + h) * D + lane * CPL;
+      if constexpr (CPL >= 4) {
 #pragma unroll
-        for (int i = 0; i < CPL / 2; ++i) {
-          chunk[u][2 * i] = __uint_as_float(w[i] << 16);
-          chunk[u][2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        for (int i = 0; i < CPL; i += 4) {
+          const v4f x = *reinterpret_cast<const v4f*>(po + i);
+          chunk[u][i] = x[0]; chunk[u][i + 1] = x[1]; chunk[u][i + 2] = x[2];
+          chunk[u][i + 3] = x[3];
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) chunk[u][i] = po[i];
       }
     }
   };
@@ -1156,10 +1238,17 @@ SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   return SplitPlan{true, (lmax + sp - 1) / sp, sp};
 }
 
-// Decode workspace: the BF16 normalised partials [T][splits][H][D], then
+// Low-bit planes: every decode batch runs the decode kernel, kSpan entries
+// per span.
+inline SplitPlan mx_plan(int k, int window) {
+  const int lmax = max(1, window + k);
+  return SplitPlan{false, (lmax + kSpan - 1) / kSpan, 0};
+}
+
+// Decode workspace: the FP32 normalised partials [T][splits][H][D], then
 // their FP32 (max, sum) pairs [T][splits][H].
 inline size_t attn_ws_bytes(int T, int splits, int H, int D) {
-  return static_cast<size_t>(T) * splits * H * (static_cast<size_t>(D) * 2 + 8);
+  return static_cast<size_t>(T) * splits * H * (static_cast<size_t>(D) * 4 + 8);
 }
 
 // Largest decode workspace over the active counts 1 .. T: counts from
@@ -1176,7 +1265,7 @@ size_t attn_ws_bytes_max(int T, int H, int D, int k, int window) {
 }
 
 template <int D>
-int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
+int launch_attn(const AttnArgs& in, bool ring, bool mx, hipStream_t st) {
   AttnArgs a = in;
   const long long items = static_cast<long long>(a.num_tokens) * a.splits *
                           (ring ? 1 : (a.H + 15) / 16);
@@ -1186,8 +1275,11 @@ int launch_attn(const AttnArgs& in, bool ring, hipStream_t st) {
   if (ring)
     hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kRingThreads), 0,
                        st, a);
+  else if (mx)
+    hipLaunchKernelGGL((attn_decode_kernel<D, true>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kAttnThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_decode_kernel<D>, dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((attn_decode_kernel<D, false>), dim3(static_cast<unsigned>(grid)),
                        dim3(kAttnThreads), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   if (a.splits > 1) {
@@ -1223,16 +1315,19 @@ int scratch_for_current_device(void** out) {
   return CSA_OK;
 }
 
+// cmp_kv / win_kv: BF16 pools, or with mx the low-bit payload planes (packed
+// E2M1 compressed rows, E4M3 window rows) whose scale planes are cmp_sc / win_sc.
 int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const float* rope_sin,
-               int32_t rope_dim, int32_t rope_offset, const uint16_t* cmp_kv,
+               int32_t rope_dim, int32_t rope_offset, const void* cmp_kv,
                int32_t num_cmp_blocks, const int32_t* cmp_block_table, int32_t max_cmp_blocks,
-               const int32_t* topk_idx, int32_t k, int32_t ratio, const uint16_t* win_kv,
+               const int32_t* topk_idx, int32_t k, int32_t ratio, const void* win_kv,
                int32_t num_win_blocks, const int32_t* win_block_table, int32_t max_win_blocks,
                int32_t window, const float* attn_sink, float softmax_scale,
                const int32_t* query_start_loc, const int32_t* positions, int32_t B, int32_t T,
                int32_t num_tokens, int32_t H, int32_t D, uint16_t* out, float* lse,
                void* workspace, size_t workspace_bytes, int32_t* err, void* stream,
-               bool static_scratch = false) {
+               bool static_scratch = false, bool mx = false, const uint8_t* cmp_sc = nullptr,
+               const uint8_t* win_sc = nullptr) {
   if (T < 0 || B < 0 || num_cmp_blocks < 0 || num_win_blocks < 0 || max_cmp_blocks < 0 ||
       max_win_blocks < 0 || window < 0 || k < 0)
     return CSA_ERR_SHAPE;
@@ -1252,11 +1347,14 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
        reinterpret_cast<uintptr_t>(cmp_kv) | reinterpret_cast<uintptr_t>(win_kv)) & 15)
     return CSA_ERR_UNSUPPORTED;
+  // a low-bit payload plane comes with its scale plane
+  if (mx && ((cmp_kv && !cmp_sc) || (win_kv && !win_sc))) return CSA_ERR_NULL;
   // pool rows are packed in 31 bits
   if (static_cast<long long>(num_cmp_blocks) * kPage >= (1ll << 31) ||
       static_cast<long long>(num_win_blocks) * kPage >= (1ll << 31))
     return CSA_ERR_UNSUPPORTED;
-  const SplitPlan plan = plan_splits(num_tokens, k, window, prefill);
+  // the low-bit planes are read by the decode kernel alone (spans of kSpan)
+  const SplitPlan plan = mx ? mx_plan(k, window) : plan_splits(num_tokens, k, window, prefill);
   // the ring schedule holds a row's whole key list in LDS
   if (plan.ring && plan.splits == 1 && window + k > kMaxSplit) return CSA_ERR_UNSUPPORTED;
   AttnArgs a{};
@@ -1265,14 +1363,21 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   a.rope_sin = rope_sin;
   a.half_rope = rope_dim / 2;
   a.rope_offset = rope_offset;
-  a.cmp_kv = cmp_kv;
+  if (mx) {
+    a.cmp_fp4 = static_cast<const uint8_t*>(cmp_kv);
+    a.cmp_sc = cmp_sc;
+    a.win_fp8 = static_cast<const uint8_t*>(win_kv);
+    a.win_sc = win_sc;
+  } else {
+    a.cmp_kv = static_cast<const uint16_t*>(cmp_kv);
+    a.win_kv = static_cast<const uint16_t*>(win_kv);
+  }
   a.num_cmp_blocks = cmp_kv ? num_cmp_blocks : 0;
   a.cmp_bt = cmp_block_table;
   a.max_cmp_blocks = cmp_block_table ? max_cmp_blocks : 0;
   a.topk = topk_idx;
   a.k = k;
   a.ratio = ratio;
-  a.win_kv = win_kv;
   a.num_win_blocks = win_kv ? num_win_blocks : 0;
   a.win_bt = win_block_table;
   a.max_win_blocks = win_block_table ? max_win_blocks : 0;
@@ -1300,16 +1405,16 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
     if (!workspace || workspace_bytes < need) return CSA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
     char* w = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<uint16_t*>(w);
+    a.part_o = reinterpret_cast<float*>(w);
     a.part_ml = reinterpret_cast<float2*>(w + static_cast<size_t>(num_tokens) * plan.splits * H *
-                                                  D * sizeof(uint16_t));
+                                                  D * sizeof(float));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (D) {
-    case 64: return launch_attn<64>(a, plan.ring, st);
-    case 128: return launch_attn<128>(a, plan.ring, st);
-    case 256: return launch_attn<256>(a, plan.ring, st);
-    default: return launch_attn<512>(a, plan.ring, st);
+    case 64: return launch_attn<64>(a, plan.ring, mx, st);
+    case 128: return launch_attn<128>(a, plan.ring, mx, st);
+    case 256: return launch_attn<256>(a, plan.ring, mx, st);
+    default: return launch_attn<512>(a, plan.ring, mx, st);
   }
 }
 
@@ -1358,6 +1463,33 @@ extern "C" int csa_sparse_attn_prefill(
                          win_kv, num_win_blocks, win_block_table, max_win_blocks, window,
                          attn_sink, softmax_scale, query_start_loc, positions, B, T, num_tokens,
                          H, D, out, lse, workspace, workspace_bytes, err, stream);
+}
+
+// The low-bit plan does not depend on the active count, so the size for T
+// covers every count up to T.
+extern "C" size_t csa_sparse_attn_mx_workspace_bytes(int32_t T, int32_t H, int32_t D, int32_t k,
+                                                     int32_t window) {
+  if (T <= 0 || H <= 0 || D <= 0 || k < 0 || window < 0) return 0;
+  const csa::SplitPlan plan = csa::mx_plan(k, window);
+  return plan.splits > 1 ? csa::attn_ws_bytes(T, plan.splits, H, D) : 0;
+}
+
+extern "C" int csa_sparse_attn_decode_mx(
+    const uint16_t* q, const float* rope_cos, const float* rope_sin, int32_t rope_dim,
+    int32_t rope_offset, const uint8_t* cmp_fp4, const uint8_t* cmp_scale,
+    int32_t num_cmp_blocks, const int32_t* cmp_block_table, int32_t max_cmp_blocks,
+    const int32_t* topk_idx, int32_t k, int32_t ratio, const uint8_t* win_fp8,
+    const uint8_t* win_scale, int32_t num_win_blocks, const int32_t* win_block_table,
+    int32_t max_win_blocks, int32_t window, const float* attn_sink, float softmax_scale,
+    const int32_t* query_start_loc, const int32_t* positions, int32_t B, int32_t T,
+    int32_t num_tokens, int32_t H, int32_t D, uint16_t* out, float* lse, void* workspace,
+    size_t workspace_bytes, int32_t* err, void* stream) {
+  return csa::attn_entry(false, q, rope_cos, rope_sin, rope_dim, rope_offset, cmp_fp4,
+                         num_cmp_blocks, cmp_block_table, max_cmp_blocks, topk_idx, k, ratio,
+                         win_fp8, num_win_blocks, win_block_table, max_win_blocks, window,
+                         attn_sink, softmax_scale, query_start_loc, positions, B, T, num_tokens,
+                         H, D, out, lse, workspace, workspace_bytes, err, stream,
+                         /*static_scratch=*/false, /*mx=*/true, cmp_scale, win_scale);
 }
 
 extern "C" size_t csa_sparse_attn_noalloc_max_bytes(void) { return kScratchBytes; }

@@ -30,7 +30,7 @@ class CsaStep:
                  prefill: bool = False, device: str = "cuda", with_values: bool = True,
                  with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None,
                  mode: str = "csa", cand_kb: int = 0, cand_block: int = 8,
-                 index_format: str = "int8"):
+                 index_format: str = "int8", kv_format: str = "bf16"):
         # mode "csa": indexer scores and top-k select the compressed rows;
         # "hca": no indexer, every visible compressed row (k bounds them);
         # "swa": the window alone (k = 0); "reindex": scores and top-k only
@@ -47,6 +47,13 @@ class CsaStep:
         if index_format == "mxfp4" and mode == "reindex":
             raise ValueError("the reindex scorer takes the INT8 index plane")
         self.index_format = index_format
+        # "bf16": arrays cmp_kv / win_kv; "mx": the low-bit planes cmp_fp4 +
+        # cmp_scale and win_fp8 + win_scale (decode only)
+        if kv_format not in ("bf16", "mx"):
+            raise ValueError(f"unknown KV format {kv_format!r}")
+        if kv_format == "mx" and prefill:
+            raise ValueError("the low-bit KV planes have a decode entry point only")
+        self.kv_format = kv_format
         self.ratio, self.k, self.window = int(ratio), int(k), int(window)
         self.rope_offset, self.softmax_scale = int(rope_offset), float(softmax_scale)
         self.prefill = prefill
@@ -85,7 +92,11 @@ class CsaStep:
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         tw = _lib.csa_topk_workspace_bytes(T, self.score_stride, self.k)
         self.topk_ws = torch.empty(tw, dtype=torch.uint8, device=dev) if tw else None
-        aw = 0 if prefill else _lib.csa_sparse_attn_workspace_bytes(T, H, D, self.k, self.window)
+        if kv_format == "mx":
+            aw = _lib.csa_sparse_attn_mx_workspace_bytes(T, H, D, self.k, self.window)
+        else:
+            aw = 0 if prefill else _lib.csa_sparse_attn_workspace_bytes(T, H, D, self.k,
+                                                                        self.window)
         self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=dev) if aw else None
 
     # ---- the four stages -------------------------------------------------
@@ -130,6 +141,15 @@ class CsaStep:
         fn = _lib.csa_sparse_attn_prefill if self.prefill else _lib.csa_sparse_attn_decode
         if topk_idx is None and self.mode in ("csa", "reindex", "hier_full"):
             topk_idx = self.topk_idx
+        if self.kv_format == "mx":
+            _lib.csa_sparse_attn_decode_mx(
+                t["q"], self.rope_cos, self.rope_sin, self.rope_offset, t["cmp_fp4"],
+                t["cmp_scale"], t["cmp_block_table"], topk_idx, self.ratio, t["win_fp8"],
+                t["win_scale"], t["win_block_table"], self.window, t["attn_sink"],
+                self.softmax_scale, t["query_start_loc"], t["positions"], self.num_tokens,
+                self.out, lse=self.lse, workspace=self.attn_ws, err=self.err, stream=stream,
+                k=self.k)
+            return
         fn(t["q"], self.rope_cos, self.rope_sin, self.rope_offset, t["cmp_kv"],
            t["cmp_block_table"], topk_idx, self.ratio, t["win_kv"], t["win_block_table"],
            self.window, t["attn_sink"], self.softmax_scale, t["query_start_loc"],
@@ -161,4 +181,5 @@ def step_for_config(cfg, arrays: Dict[str, np.ndarray], **kw) -> CsaStep:
                    softmax_scale=cfg.softmax_scale, prefill=(cfg.T > 256),
                    mode=getattr(cfg, "mode", "csa"), cand_kb=getattr(cfg, "cand_kb", 0),
                    cand_block=getattr(cfg, "cand_block", 8),
-                   index_format=getattr(cfg, "index_format", "int8"), **kw)
+                   index_format=getattr(cfg, "index_format", "int8"),
+                   kv_format=getattr(cfg, "kv_format", "bf16"), **kw)

@@ -13,6 +13,8 @@
  *   4. csa_sparse_attn_decode /   -- shared-KV attention over the 128-token
  *      csa_sparse_attn_prefill       window and the selected compressed rows,
  *                                    with one sink logit per head
+ *      (csa_sparse_attn_decode_mx: the same over the MXFP8 window and MXFP4
+ *      compressed KV planes)
  *
  * Pages the contracts follow (cited by title and section):
  *   [V41]  pypto-lib "DeepSeek V4.1 Flash": "Serving-owned full RoPE tables",
@@ -258,6 +260,52 @@ int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const floa
                             int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
                             uint16_t* out, float* lse, void* workspace,
                             size_t workspace_bytes, int32_t* err, void* stream);
+
+/*
+ * csa_sparse_attn_decode_mx -- csa_sparse_attn_decode reading the low-bit KV
+ * planes of the production cache ABI ([V41], the paragraph on the production
+ * cache ABI before "Compressor state ownership": window KV as MXFP8 E4M3 with
+ * E8M0 group-of-32 scales, compressed KV as packed MXFP4 E2M1 with E4M3
+ * group-of-16 scales; the references quantise on cache publication and
+ * dequantise on cache reads).  Every argument but the four planes is that of
+ * csa_sparse_attn_decode, with the same meaning, checks and flags.
+ *
+ *   cmp_fp4   UINT8 [num_cmp_blocks, 128, D / 2]: packed E2M1 codes, channel
+ *             2i in bits 0-3 of byte i, channel 2i + 1 in bits 4-7
+ *   cmp_scale UINT8 [num_cmp_blocks, 128, D / 16]: E4M3 (OCP E4M3FN) codes;
+ *             channel c of a row is e2m1(c) * e4m3(cmp_scale[c / 16])
+ *   win_fp8   UINT8 [num_win_blocks, 128, D]: E4M3 codes
+ *   win_scale UINT8 [num_win_blocks, 128, D / 32]: E8M0 bytes; channel c of a
+ *             row is e4m3(c) * 2^(win_scale[c / 32] - 127) (byte 255 is NaN)
+ *   workspace csa_sparse_attn_mx_workspace_bytes(T, H, D, k, window) bytes,
+ *             16-byte aligned (NULL when that size is 0); its schedule does
+ *             not depend on num_tokens, so the size for T covers any count.
+ *
+ * Each row is dequantised exactly (an E4M3 code times a power of two, or an
+ * E2M1 code times an E4M3 code, is a BF16 value; only products outside BF16's
+ * normal range, from extreme E8M0 bytes, are rounded) into the BF16 tile the
+ * attention multiplies, so the result is csa_sparse_attn_decode's on the
+ * dequantised rows.  NaN codes propagate as NaN.  A payload plane given without its scale plane returns
+ * CSA_ERR_NULL; a NULL pair is an empty pool (its rows flag BLOCK_RANGE).
+ * Plane pointers are 16-byte aligned.  Every batch size runs the decode
+ * schedule (128-entry spans per 16-head group, merged); there is no prefill
+ * form.
+ */
+size_t csa_sparse_attn_mx_workspace_bytes(int32_t T, int32_t H, int32_t D, int32_t k,
+                                          int32_t window);
+int csa_sparse_attn_decode_mx(const uint16_t* q, const float* rope_cos, const float* rope_sin,
+                              int32_t rope_dim, int32_t rope_offset, const uint8_t* cmp_fp4,
+                              const uint8_t* cmp_scale, int32_t num_cmp_blocks,
+                              const int32_t* cmp_block_table, int32_t max_cmp_blocks,
+                              const int32_t* topk_idx, int32_t k, int32_t ratio,
+                              const uint8_t* win_fp8, const uint8_t* win_scale,
+                              int32_t num_win_blocks, const int32_t* win_block_table,
+                              int32_t max_win_blocks, int32_t window, const float* attn_sink,
+                              float softmax_scale, const int32_t* query_start_loc,
+                              const int32_t* positions, int32_t B, int32_t T,
+                              int32_t num_tokens, int32_t H, int32_t D, uint16_t* out,
+                              float* lse, void* workspace, size_t workspace_bytes,
+                              int32_t* err, void* stream);
 
 /*
  * csa_sparse_attn_decode_noalloc -- csa_sparse_attn_decode for callers that

@@ -50,6 +50,17 @@ class CsaConfig:
     # index plane: "int8" (INT8 keys and query, FP32 per-row scales) or
     # "mxfp4" (packed E2M1 keys and query, one E8M0 scale per 32 dims)
     index_format: str = "int8"
+    # KV planes: "bf16" (one BF16 cache per pool) or "mx" (the low-bit cache
+    # ABI: window rows MXFP8 E4M3 with one E8M0 byte per 32 channels,
+    # compressed rows packed MXFP4 E2M1 with one E4M3 byte per 16 channels)
+    kv_format: str = "bf16"
+
+    @property
+    def kv_row_bytes(self):
+        """(window, compressed) bytes of one KV row, payload + scales."""
+        if self.kv_format == "mx":
+            return self.D + self.D // 32, self.D // 2 + self.D // 16
+        return 2 * self.D, 2 * self.D
 
     @property
     def index_key_bytes(self) -> int:
@@ -188,10 +199,28 @@ C11 = _decode(
     "V4.1 ratio-2 decode with the MXFP4 index plane: C2's shapes",
     n_req=4, s=2, context=32768, ratio=2, k=512, index_format="mxfp4")
 
+# The low-bit KV planes of the production cache ABI (pypto-lib "DeepSeek V4.1
+# Flash", the paragraph on the production cache ABI: MXFP8 window KV, MXFP4
+# compressed KV with E4M3 group-of-16 scales) on the ratio-1 decode shapes;
+# the max-context one also takes the MXFP4 index plane, so every cache it
+# reads is in its production format.
+C12 = _decode(
+    "c12_ratio1_mxkv_decode",
+    "ratio-1 decode over the low-bit KV planes: C3's shapes, window rows MXFP8 E4M3 "
+    "(528 bytes), compressed rows MXFP4 E2M1 with E4M3 group-16 scales (288 bytes)",
+    n_req=4, s=2, context=131072, ratio=1, k=2048, rope_neg_rows=(0,), kv_format="mx")
+
+C13 = _decode(
+    "c13_maxctx_lowbit_decode",
+    "max-context ratio-1 decode with every cache low-bit: C5's shapes, MXFP4 index "
+    "keys, MXFP8 window KV and MXFP4 compressed KV",
+    n_req=2, s=4, context=1 << 20, ratio=1, k=2048, shared_pool=True, index_format="mxfp4",
+    kv_format="mx")
+
 CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8, C9, C10,
-                                                     C11)}
+                                                     C11, C12, C13)}
 SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7, "c8": C8,
-         "c9": C9, "c10": C10, "c11": C11}
+         "c9": C9, "c10": C10, "c11": C11, "c12": C12, "c13": C13}
 
 
 def get(name: str) -> CsaConfig:

@@ -22,6 +22,14 @@ for the larger ones:
   only holds the pages that some window touches; every other table entry is -1.
 * RoPE tables: FP32 half-width [capacity, R/2], angle = pos * theta^(-2i/R)
   evaluated in float64 (no YaRN).  Tables are caller inputs of the path.
+* low-bit KV planes (``kv_format`` "mx"), codes drawn directly, no quantiser:
+  window E4M3 codes with uniform sign and mantissa and exponent field 4..10
+  (magnitudes 2^-3 .. 2^3 times 1 + m/8, never NaN) beside E8M0 bytes
+  122..125 (2^-5 .. 2^-2); compressed packed E2M1 bytes uniform over all 256
+  (every nibble uniform over the 16 codes) beside positive E4M3 scales with
+  exponent field 3..6 (2^-4 .. 2^-1 times 1 + m/8).  The dequantised values
+  have an RMS near 0.6 (window) and 1.0 (compressed), the scale of the BF16
+  rows.  These planes replace the BF16 pools.
 
 No arithmetic of the method (scores, selection, attention, rotation) lives here.
 """
@@ -40,6 +48,8 @@ _TENSOR_IDS = {
     "q": 1, "cmp_kv": 2, "win_kv": 3, "q_idx_f": 4, "head_w": 5, "idx_kv": 6,
     "idx_scale": 7, "outlier": 8, "attn_sink": 9, "cmp_perm": 10, "win_perm": 11,
     "cand_blocks": 12, "q_fp4": 13, "q_e8m0": 14, "idx_fp4": 15, "idx_e8m0": 16,
+    "win_fp8_bits": 17, "win_fp8_exp": 18, "win_e8m0": 19, "cmp_fp4": 20, "cmp_sc_m": 21,
+    "cmp_sc_e": 22,
 }
 
 _CHUNK_ELEMS = 1 << 24  # fixed chunk so the draws never depend on the caller
@@ -75,6 +85,26 @@ def _bf16_normal(seed: int, name: str, shape) -> np.ndarray:
         e = min(n, s + _CHUNK_ELEMS)
         g = _rng(seed, name, ci)
         out[s:e] = f32_to_bf16_bits(g.standard_normal(e - s, dtype=np.float32))
+
+    nchunks = -(-n // _CHUNK_ELEMS)
+    if nchunks <= 1:
+        if n:
+            fill(0)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
+def _u8_uniform(seed: int, name: str, shape, lo: int, hi: int) -> np.ndarray:
+    """uint8 integers uniform on [lo, hi], drawn in fixed chunks."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+
+    def fill(ci: int) -> None:
+        s = ci * _CHUNK_ELEMS
+        e = min(n, s + _CHUNK_ELEMS)
+        out[s:e] = _rng(seed, name, ci).integers(lo, hi + 1, size=e - s, dtype=np.uint8)
 
     nchunks = -(-n // _CHUNK_ELEMS)
     if nchunks <= 1:
@@ -144,7 +174,12 @@ def make_inputs(cfg: CsaConfig, seed: int = 0, with_tables: bool = True) -> CsaI
     nbc = B * pages
     perm = _rng(seed, "cmp_perm").permutation(nbc).astype(np.int32)
     t["cmp_block_table"] = perm.reshape(B, pages)
-    t["cmp_kv"] = _bf16_normal(seed, "cmp_kv", (nbc, PAGE, D))
+    if cfg.kv_format == "mx":
+        t["cmp_fp4"] = _u8_uniform(seed, "cmp_fp4", (nbc, PAGE, D // 2), 0, 255)
+        t["cmp_scale"] = ((_u8_uniform(seed, "cmp_sc_e", (nbc, PAGE, D // 16), 3, 6) << 3)
+                          | _u8_uniform(seed, "cmp_sc_m", (nbc, PAGE, D // 16), 0, 7))
+    else:
+        t["cmp_kv"] = _bf16_normal(seed, "cmp_kv", (nbc, PAGE, D))
     t["idx_kv"] = _rng(seed, "idx_kv").integers(-127, 128, size=(nbc, PAGE, Di),
                                                  dtype=np.int8)
     sc = _rng(seed, "idx_scale").uniform(0.005, 0.02, size=(nbc, PAGE)).astype(np.float32)
@@ -183,7 +218,12 @@ def make_inputs(cfg: CsaConfig, seed: int = 0, with_tables: bool = True) -> CsaI
             wbt[b, pg] = wperm[i]
             i += 1
     t["win_block_table"] = wbt
-    t["win_kv"] = _bf16_normal(seed, "win_kv", (nbw, PAGE, D))
+    if cfg.kv_format == "mx":
+        bits = _u8_uniform(seed, "win_fp8_bits", (nbw, PAGE, D), 0, 255)
+        t["win_fp8"] = (bits & 0x87) | (_u8_uniform(seed, "win_fp8_exp", (nbw, PAGE, D), 4, 10) << 3)
+        t["win_scale"] = _u8_uniform(seed, "win_e8m0", (nbw, PAGE, D // 32), 122, 125)
+    else:
+        t["win_kv"] = _bf16_normal(seed, "win_kv", (nbw, PAGE, D))
 
     # ---- a reindex layer's candidate mask (the full layer's output, supplied
     #      as an input): per row, cand_kb distinct blocks of cand_block

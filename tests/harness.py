@@ -33,19 +33,30 @@ def sub_batch(x: dict, rows) -> dict:
     return y
 
 
+def kv_sources(x: dict, cfg):
+    """The oracle's (compressed, window) KV arguments for a config's format."""
+    if getattr(cfg, "kv_format", "bf16") == "mx":
+        return (oracle.mxfp4_e4m3_plane(x["cmp_fp4"], x["cmp_scale"]),
+                oracle.mxfp8_plane(x["win_fp8"], x["win_scale"]))
+    return x["cmp_kv"], x["win_kv"]
+
+
 def oracle_step(x: dict, cfg, topk_override=None) -> dict:
     T = x["q"].shape[0]
     half = cfg.R // 2
     rc = np.full((T, half), np.nan, np.float32)
     rs = np.full((T, half), np.nan, np.float32)
     e0 = oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["position_ids"], T, rc, rs)
-    s, e1 = oracle.index_scores(x["q_idx"], x["q_scale"], x["head_w"], x["idx_kv"],
-                                x["idx_scale"], x["cmp_block_table"], x["query_start_loc"],
-                                x["positions"], T, cfg.ratio, cfg.score_stride)
+    score_fn = (oracle.index_scores_mxfp4 if getattr(cfg, "index_format", "int8") == "mxfp4"
+                else oracle.index_scores)
+    s, e1 = score_fn(x["q_idx"], x["q_scale"], x["head_w"], x["idx_kv"], x["idx_scale"],
+                     x["cmp_block_table"], x["query_start_loc"], x["positions"], T, cfg.ratio,
+                     cfg.score_stride)
     idx, val, e2 = oracle.topk(s, x["positions"], cfg.ratio, T, cfg.k)
     sel = idx if topk_override is None else topk_override
-    out, lse, e3 = oracle.sparse_attn(x["q"], rc, rs, cfg.rope_offset, x["cmp_kv"],
-                                      x["cmp_block_table"], sel, cfg.ratio, x["win_kv"],
+    cmp_kv, win_kv = kv_sources(x, cfg)
+    out, lse, e3 = oracle.sparse_attn(x["q"], rc, rs, cfg.rope_offset, cmp_kv,
+                                      x["cmp_block_table"], sel, cfg.ratio, win_kv,
                                       x["win_block_table"], cfg.W, x["attn_sink"],
                                       cfg.softmax_scale, x["query_start_loc"], x["positions"], T)
     return dict(rope_cos=rc, rope_sin=rs, scores=s, topk_idx=idx, topk_val=val, out=out,

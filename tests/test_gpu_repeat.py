@@ -34,7 +34,7 @@ PER_ROW = ("q", "q_idx", "q_scale", "head_w", "positions", "position_ids")
 
 def test_padded_decode_batch_uses_helper_sized_workspaces():
     csa = _csa()
-    cfg = synthetic.get("c3")   # 2048 + 128 entries per row: four spans, merged
+    cfg = synthetic.get("c3")   # 2048 + 128 entries per row: 17 spans, merged
     x = synthetic.make_inputs(cfg, seed=21).t
     T_store, nt = 300, cfg.T
     xp = dict(x)

@@ -121,9 +121,9 @@ def test_attention_selection_bounds(lib):
     assert lib.csa_sparse_attn_prefill(*no_sel) == -4  # ring schedule: list past 4224
     bad = list(no_sel); bad[10] = (1 << 20) + 1
     assert lib.csa_sparse_attn_decode(*bad) == -3
-    # whole span partials (BF16 O and FP32 (max, sum) per head), at least two
+    # whole span partials (FP32 O and (max, sum) per head), at least two
     need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 8192, 128)
-    per_span = 8 * 64 * (512 * 2 + 8)
+    per_span = 8 * 64 * (512 * 4 + 8)
     assert need % per_span == 0 and need // per_span >= 2
 
 
@@ -237,4 +237,35 @@ def test_noalloc_decode_host_checks(lib):
     bad = list(base); bad[0] = None               # q NULL
     assert f(*bad) == -1
     bad = list(base); bad[23] = 0                 # no active rows: nothing to do
+    assert f(*bad) == 0
+
+
+def test_mx_decode_host_checks(lib):
+    """The low-bit KV decode: a payload plane without its scale plane is
+    refused, its workspace follows one plan for every active count, and the
+    decode call's own host checks apply."""
+    f = lib.csa_sparse_attn_decode_mx
+    ws = lib.csa_sparse_attn_mx_workspace_bytes
+    # (2048 + 128) keys in 128-entry spans: 17 partials per row and head
+    per = 64 * (512 * 4 + 8)
+    assert ws(8, 64, 512, 2048, 128) == 8 * 17 * per
+    assert ws(300, 64, 512, 2048, 128) == 300 * 17 * per   # no ring schedule for many rows
+    assert ws(8, 64, 512, 0, 100) == 0                     # one span: no partials
+    assert ws(0, 64, 512, 2048, 128) == 0
+    need = ws(8, 64, 512, 2048, 128)
+    #       q     cos   sin  rd  off  fp4   sc4   ncb bt   mcb topk  k    r  fp8   sc8
+    base = [FAKE, FAKE, FAKE, 64, 448, FAKE, FAKE, 4, FAKE, 2, FAKE, 2048, 1, FAKE, FAKE,
+            2, FAKE, 2, 128, FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, FAKE, need,
+            None, None]
+    bad = list(base); bad[6] = None                # compressed codes without scales
+    assert f(*bad) == -1
+    bad = list(base); bad[14] = None               # window codes without scales
+    assert f(*bad) == -1
+    bad = list(base); bad[27] = 320                # D without a kernel
+    assert f(*bad) == -4
+    bad = list(base); bad[31] = need - 1           # workspace one byte short
+    assert f(*bad) == -5
+    bad = list(base); bad[11] = 4097               # selection array past 4096 entries
+    assert f(*bad) == -3
+    bad = list(base); bad[25] = 0                  # no active rows: nothing to do
     assert f(*bad) == 0

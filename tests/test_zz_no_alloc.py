@@ -68,6 +68,6 @@ def _compare(csa, name, num_tokens):
 
 def test_noalloc_matches_workspace_call_twice():
     csa = _csa()
-    big = _compare(csa, "c3", 8)     # four spans per row, merged
+    big = _compare(csa, "c3", 8)     # 17 spans of 128 entries per row, merged
     small = _compare(csa, "c3", 3)   # the same lists, fewer rows
     assert small < big
