@@ -23,7 +23,8 @@
 // Decode kernel (small batches): a work-group owns one (row, 16-head group,
 // 128-entry span); each wave gathers and multiplies its own 32-row tile, so a
 // span costs one memory latency and every key byte is read from LDS once.
-// FP32 partials of the spans, normalised by their own sums, are merged with the
+// FP16 partials of the spans, normalised by their own sums and scaled by a power
+// of two per channel quarter, are merged with the
 // sink by a third kernel.
 //
 // Tile code.  Rows sit at a 16-byte-padded stride so the K operand reads
@@ -97,8 +98,10 @@ struct AttnArgs {
   int H;
   uint16_t* out;
   float* lse;
-  float* part_o;     // FP32 [T][splits][H][D]: span partials normalised by their sum
+  uint16_t* part_o;  // FP16 [T][splits][H][D]: span partials normalised by their sum,
+                     // times a power of two per channel quarter
   float2* part_ml;   // [T][splits][H]: (max, sum) of each span, base-2 logits
+  float* part_mult;  // [T][splits][H][4]: the inverse of each quarter's power of two
   int splits;
   int ring_span;     // ring schedule with splits > 1: list entries per span
   int items_per_xcd;
@@ -106,6 +109,33 @@ struct AttnArgs {
 };
 
 __device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
+
+// Span partials travel as FP16 with a power-of-two factor per (span, head,
+// channel quarter): the factor puts the quarter's largest magnitude mx in
+// [0.5, 1), so every stored value keeps 11 bits relative to that maximum and
+// none overflows.  Returns (factor, its inverse); a zero, subnormal,
+// infinite or NaN maximum keeps the values as they are.
+__device__ __forceinline__ float2 fp16_block_scale(float mx) {
+  const uint32_t e = (__float_as_uint(mx) >> 23) & 0xffu;
+  if (e == 0u || e == 255u) return make_float2(1.0f, 1.0f);
+  const uint32_t ec = e < 252u ? e : 252u;
+  return make_float2(__uint_as_float((253u - ec) << 23), __uint_as_float((ec + 1u) << 23));
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 a = static_cast<_Float16>(lo), b = static_cast<_Float16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// Max over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+  return v;
+}
 
 constexpr int kMaxSplit = 4224;  // longest key list of the ring schedule: window + k
 constexpr int kMaxDenseK = 1 << 20;   // bound on k without a selection array
@@ -653,20 +683,34 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
       __syncthreads();
       if (again) continue;
       __syncthreads();   // f_s is complete
-      // the BF16 output rows, or with splits > 1 the span's FP32 partial (f
-      // is then 1 / its sum)
+      // the BF16 output rows, or with splits > 1 the span's FP16 partial (f
+      // is then 1 / its sum) scaled for this wave's channel quarter
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         const int hh = ht * 16 + col;
-        if (hh >= a.H) continue;
-        const float f = f_s[hh];
+        const float f = f_s[hh < a.H ? hh : 0];
         const long long roff = static_cast<long long>(hh) * D + d0;
         if (a.splits > 1) {
-          float* prow = a.part_o + static_cast<long long>(item) * a.H * D + roff;
+          float mx = 0.0f;
 #pragma unroll
           for (int dt = 0; dt < DTW; ++dt)
-            *reinterpret_cast<v4f*>(prow + dt * 16 + grp * 4) = o_acc[dt][ht] * f;
-        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(o_acc[dt][ht][r] * f));
+          mx = max_xor32(max_xor16(mx));   // the four lane groups of head hh
+          if (hh >= a.H) continue;
+          const float2 sc = fp16_block_scale(mx);
+          const float fs = f * sc.x;
+          uint16_t* prow = a.part_o + static_cast<long long>(item) * a.H * D + roff;
+#pragma unroll
+          for (int dt = 0; dt < DTW; ++dt) {
+            uint2 w;
+            w.x = pack_f16x2(o_acc[dt][ht][0] * fs, o_acc[dt][ht][1] * fs);
+            w.y = pack_f16x2(o_acc[dt][ht][2] * fs, o_acc[dt][ht][3] * fs);
+            *reinterpret_cast<uint2*>(prow + dt * 16 + grp * 4) = w;
+          }
+          if (grp == 0)
+            a.part_mult[(static_cast<long long>(item) * a.H + hh) * 4 + (wave - HT)] = sc.y;
+        } else if (hh < a.H) {
           uint16_t* orow = a.out + static_cast<long long>(t) * a.H * D + roff;
 #pragma unroll
           for (int dt = 0; dt < DTW; ++dt) {
@@ -849,7 +893,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   // low-bit rows go through registers: lane (row ins * RPI + lane / NC,
   // chunk lane % NC) holds the codes of channels 8 * chunk .. + 7 and their
   // group's scale byte until the conversion below
-  [[maybe_unused]] uint2 mx_pay[MX ? NI : 1];
+  // (a native vector type: arrays of HIP's uint2 struct stay in scratch memory)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  [[maybe_unused]] u32x2 mx_pay[MX ? NI : 1];
   [[maybe_unused]] uint32_t mx_sc[MX ? NI : 1];
   [[maybe_unused]] uint32_t mx_row[MX ? NI : 1];
   if constexpr (MX) {
@@ -877,7 +923,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
                                  : a.cmp_sc + row * (D / 16) + (chunk >> 1);
         pay = (r == kNoRow) ? dummy : pay;
         scp = (r == kNoRow) ? dummy : scp;
-        mx_pay[ins] = *reinterpret_cast<const uint2*>(pay);
+        mx_pay[ins] = *reinterpret_cast<const u32x2*>(pay);
         mx_sc[ins] = *scp;
       }
     }
@@ -942,14 +988,14 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
           // the E8M0 byte as the exponent field of the FP32 scale operand:
           // the conversion multiplies by 2^(byte - 127) (byte 255: NaN)
           const float sc = __builtin_bit_cast(float, mx_sc[ins] << 23);
-          const uint32_t wx = mx_pay[ins].x, wy = mx_pay[ins].y;
+          const uint32_t wx = mx_pay[ins][0], wy = mx_pay[ins][1];
           v = uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, sc, false)),
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, sc, true)),
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, sc, false)),
                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, sc, true))};
         } else {
           const float sc = __builtin_amdgcn_cvt_f32_fp8(mx_sc[ins], 0);
-          const uint32_t wx = (lane % NC) & 1 ? mx_pay[ins].y : mx_pay[ins].x;
+          const uint32_t wx = (lane % NC) & 1 ? mx_pay[ins][1] : mx_pay[ins][0];
           v = uint4{fp4_pair_bf16<0>(wx, sc), fp4_pair_bf16<1>(wx, sc),
                     fp4_pair_bf16<2>(wx, sc), fp4_pair_bf16<3>(wx, sc)};
         }
@@ -1076,24 +1122,43 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
         scale = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
         if (c4 == 0) a.part_ml[static_cast<long long>(ts) * a.H + head] = make_float2(M, Lsum);
       }
-      uint16_t* dst = a.out + (static_cast<long long>(t) * a.H + head) * D;
-      float* pdst = a.part_o + (static_cast<long long>(ts) * a.H + head) * D;
+      // channels c4 + 64 m, m < D / 64, of head `head`, combined over the waves
+      v4f accs[D / 64];
+      float mx = 0.0f;
 #pragma unroll
-      for (int c = c4; c < D; c += 64) {
+      for (int m = 0; m < D / 64; ++m) {
         v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w)
-          acc += *reinterpret_cast<const v4f*>(
-                     reinterpret_cast<const float*>(slot_s + w * SS) + hh * OSTR + c) * e[w];
-        acc *= scale;
-        if (a.splits == 1) {
+          acc += *reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(slot_s + w * SS) +
+                                               hh * OSTR + c4 + 64 * m) * e[w];
+        accs[m] = acc * scale;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(accs[m][r]));
+      }
+      if (a.splits == 1) {
+        uint16_t* dst = a.out + (static_cast<long long>(t) * a.H + head) * D;
+#pragma unroll
+        for (int m = 0; m < D / 64; ++m) {
           uint2 pk;
-          pk.x = pack_bf16x2(acc[0], acc[1]);
-          pk.y = pack_bf16x2(acc[2], acc[3]);
-          *reinterpret_cast<uint2*>(dst + c) = pk;
-        } else {
-          *reinterpret_cast<v4f*>(pdst + c) = acc;
+          pk.x = pack_bf16x2(accs[m][0], accs[m][1]);
+          pk.y = pack_bf16x2(accs[m][2], accs[m][3]);
+          *reinterpret_cast<uint2*>(dst + c4 + 64 * m) = pk;
         }
+      } else {
+        // one factor for the head's four quarters: the max over its 16 lanes
+        const float2 sc = fp16_block_scale(row16_max(mx));
+        uint16_t* pdst = a.part_o + (static_cast<long long>(ts) * a.H + head) * D;
+#pragma unroll
+        for (int m = 0; m < D / 64; ++m) {
+          uint2 pk;
+          pk.x = pack_f16x2(accs[m][0] * sc.x, accs[m][1] * sc.x);
+          pk.y = pack_f16x2(accs[m][2] * sc.x, accs[m][3] * sc.x);
+          *reinterpret_cast<uint2*>(pdst + c4 + 64 * m) = pk;
+        }
+        if (c4 == 0)
+          *reinterpret_cast<float4*>(a.part_mult + (static_cast<long long>(ts) * a.H + head) * 4) =
+              make_float4(sc.y, sc.y, sc.y, sc.y);
       }
     }
   }
@@ -1103,6 +1168,8 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
 // (row, head).  Span s contributes its normalised partial O_s with weight
 // l_s * 2^(m_s - M) (M the max over the spans' maxima and the sink), so
 //   out = sum_s w_s O_s / (sum_s w_s + 2^(sink - M)),  lse = (M + log2 Z) ln 2.
+// O_s arrives as FP16 times a power of two per channel quarter, whose inverse
+// joins the weight of the lane's quarter.
 // Lane l owns channels [8l, 8l + 8) of every partial (D = 512; D / 64
 // channels in general).  With at most 64 spans (MANY false) lane s holds span
 // s's (max, sum) and the weights travel by lane reads; with more, lanes
@@ -1114,8 +1181,9 @@ constexpr int kMergeChunk = 8;
 
 template <int D, bool MANY>
 __global__ void __launch_bounds__(64) attn_merge_kernel(
-    const float* __restrict__ part_o, const float2* __restrict__ part_ml,
-    const float* __restrict__ sink, int splits, int H, int num_tokens,
+    const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
+    const float* __restrict__ part_mult, const float* __restrict__ sink, int splits, int H,
+    int num_tokens,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int CPL = D / 64;            // channels per lane
   static_assert(CPL == 1 || CPL == 2 || CPL == 4 || CPL == 8, "channels per lane");
@@ -1134,7 +1202,9 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
   float chunk[kMergeChunk][CPL];
+  float cmult[kMergeChunk];
   float2 cml[kMergeChunk];
+  const int quarter = lane >> 4;   // channels lane * CPL .. lie in quarter lane / 16
   auto load_chunk = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kMergeChunk; ++u) {
@@ -1145,18 +1215,24 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
         if (sp >= splits) cml[u] = make_float2(neg_inf, 0.0f);
       }
       // a span past the list reads span 0; its weight is never applied
-      const float* po = part_o + (sl * H + h) * D + lane * CPL;
-      if constexpr (CPL >= 4) {
-#pragma unroll
-        for (int i = 0; i < CPL; i += 4) {
-          const v4f x = *reinterpret_cast<const v4f*>(po + i);
-          chunk[u][i] = x[0]; chunk[u][i + 1] = x[1]; chunk[u][i + 2] = x[2];
-          chunk[u][i + 3] = x[3];
-        }
+      cmult[u] = part_mult[(sl * H + h) * 4 + quarter];
+      const uint16_t* po = part_o + (sl * H + h) * D + lane * CPL;
+      uint32_t w[(CPL + 1) / 2];
+      if constexpr (CPL == 8) {
+        const uint4 x = *reinterpret_cast<const uint4*>(po);
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+      } else if constexpr (CPL == 4) {
+        const uint2 x = *reinterpret_cast<const uint2*>(po);
+        w[0] = x.x; w[1] = x.y;
+      } else if constexpr (CPL == 2) {
+        w[0] = *reinterpret_cast<const uint32_t*>(po);
       } else {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) chunk[u][i] = po[i];
+        w[0] = *po;
       }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        chunk[u][i] = static_cast<float>(
+            __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i >> 1] >> (16 * (i & 1)))));
     }
   };
   load_chunk(0);
@@ -1188,6 +1264,7 @@ __global__ void __launch_bounds__(64) attn_merge_kernel(
       if constexpr (MANY) w = cml[u].x == neg_inf ? 0.0f : cml[u].y * exp2f(cml[u].x - M);
       else w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), (s0 + u) & 63));
       if (s0 + u < splits) {
+        w *= cmult[u];
 #pragma unroll
         for (int i = 0; i < CPL; ++i) acc[i] += chunk[u][i] * w;
       }
@@ -1245,10 +1322,15 @@ inline SplitPlan mx_plan(int k, int window) {
   return SplitPlan{false, (lmax + kSpan - 1) / kSpan, 0};
 }
 
-// Decode workspace: the FP32 normalised partials [T][splits][H][D], then
-// their FP32 (max, sum) pairs [T][splits][H].
+// Decode workspace: the FP16 scaled partials [T][splits][H][D], their FP32
+// (max, sum) pairs [T][splits][H], then (16-byte aligned) the quarter factors
+// [T][splits][H][4].
+inline size_t attn_ws_mult_offset(int T, int splits, int H, int D) {
+  const size_t n = static_cast<size_t>(T) * splits * H;
+  return (n * (static_cast<size_t>(D) * 2 + 8) + 15) / 16 * 16;
+}
 inline size_t attn_ws_bytes(int T, int splits, int H, int D) {
-  return static_cast<size_t>(T) * splits * H * (static_cast<size_t>(D) * 4 + 8);
+  return attn_ws_mult_offset(T, splits, H, D) + static_cast<size_t>(T) * splits * H * 16;
 }
 
 // Largest decode workspace over the active counts 1 .. T: counts from
@@ -1286,11 +1368,11 @@ int launch_attn(const AttnArgs& in, bool ring, bool mx, hipStream_t st) {
     const long long mgrid = static_cast<long long>(a.num_tokens) * a.H;
     if (a.splits <= 64)
       hipLaunchKernelGGL((attn_merge_kernel<D, false>), dim3(static_cast<unsigned>(mgrid)),
-                         dim3(64), 0, st, a.part_o, a.part_ml, a.sink, a.splits, a.H,
+                         dim3(64), 0, st, a.part_o, a.part_ml, a.part_mult, a.sink, a.splits, a.H,
                          a.num_tokens, a.out, a.lse);
     else
       hipLaunchKernelGGL((attn_merge_kernel<D, true>), dim3(static_cast<unsigned>(mgrid)),
-                         dim3(64), 0, st, a.part_o, a.part_ml, a.sink, a.splits, a.H,
+                         dim3(64), 0, st, a.part_o, a.part_ml, a.part_mult, a.sink, a.splits, a.H,
                          a.num_tokens, a.out, a.lse);
     if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   }
@@ -1405,9 +1487,10 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
     if (!workspace || workspace_bytes < need) return CSA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
     char* w = static_cast<char*>(workspace);
-    a.part_o = reinterpret_cast<float*>(w);
-    a.part_ml = reinterpret_cast<float2*>(w + static_cast<size_t>(num_tokens) * plan.splits * H *
-                                                  D * sizeof(float));
+    const size_t n_part = static_cast<size_t>(num_tokens) * plan.splits * H;
+    a.part_o = reinterpret_cast<uint16_t*>(w);
+    a.part_ml = reinterpret_cast<float2*>(w + n_part * D * sizeof(uint16_t));
+    a.part_mult = reinterpret_cast<float*>(w + attn_ws_mult_offset(num_tokens, plan.splits, H, D));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (D) {

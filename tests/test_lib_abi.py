@@ -121,9 +121,9 @@ def test_attention_selection_bounds(lib):
     assert lib.csa_sparse_attn_prefill(*no_sel) == -4  # ring schedule: list past 4224
     bad = list(no_sel); bad[10] = (1 << 20) + 1
     assert lib.csa_sparse_attn_decode(*bad) == -3
-    # whole span partials (FP32 O and (max, sum) per head), at least two
+    # whole span partials (FP16 O, (max, sum) and 4 quarter factors per head), at least two
     need = lib.csa_sparse_attn_workspace_bytes(8, 64, 512, 8192, 128)
-    per_span = 8 * 64 * (512 * 4 + 8)
+    per_span = 8 * 64 * (512 * 2 + 24)
     assert need % per_span == 0 and need // per_span >= 2
 
 
@@ -247,7 +247,7 @@ def test_mx_decode_host_checks(lib):
     f = lib.csa_sparse_attn_decode_mx
     ws = lib.csa_sparse_attn_mx_workspace_bytes
     # (2048 + 128) keys in 128-entry spans: 17 partials per row and head
-    per = 64 * (512 * 4 + 8)
+    per = 64 * (512 * 2 + 24)
     assert ws(8, 64, 512, 2048, 128) == 8 * 17 * per
     assert ws(300, 64, 512, 2048, 128) == 300 * 17 * per   # no ring schedule for many rows
     assert ws(8, 64, 512, 0, 100) == 0                     # one span: no partials
