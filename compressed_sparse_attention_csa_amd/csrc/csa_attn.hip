@@ -108,6 +108,13 @@ struct AttnArgs {
   int32_t* err;
 };
 
+constexpr int kMaxSplit = 4224;  // longest key list of the ring schedule: window + k
+constexpr int kMaxDenseK = 1 << 20;   // bound on k without a selection array
+constexpr int kDecodeCUs = 256;       // MI355X compute units: the split-ring target
+constexpr uint32_t kWinBit = 0x80000000u;
+constexpr uint32_t kNoRow = 0xffffffffu;
+constexpr int kRing = 4;          // key tiles resident in LDS (in flight or in use)
+
 __device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
 // Span partials travel as FP16 with a power-of-two factor per (span, head,
@@ -137,13 +144,80 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-constexpr int kMaxSplit = 4224;  // longest key list of the ring schedule: window + k
-constexpr int kMaxDenseK = 1 << 20;   // bound on k without a selection array
-constexpr int kDecodeCUs = 256;       // MI355X compute units: the split-ring target
-constexpr uint32_t kWinBit = 0x80000000u;
-constexpr uint32_t kNoRow = 0xffffffffu;
-constexpr int kRing = 4;          // key tiles resident in LDS (in flight or in use)
-constexpr float kSlack = 8.0f;    // log2 headroom before the running max is moved
+// Two E2M1 codes (byte BS of w, the lower-indexed one in bits 0-3) times an
+// FP32 scale, as a BF16 pair.  The products are BF16 values (at most 6
+// significant bits for an E4M3 scale), so their upper halves are exact.
+template <int BS>
+__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t w, float sc) {
+  const v2f_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BS);
+  const float lo = e[0] * sc, hi = e[1] * sc;
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                               0x07060302u);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr uint32_t kMxWin = 0x100u;    // scale word flags: a window row,
+constexpr uint32_t kMxMasked = 0x200u; // an entry past the valid rows
+
+// The low-bit planes as values (read once from the kernel arguments: a
+// choice between two argument fields made per lane would otherwise become a
+// per-lane load from the argument block, and its wait would hold up every
+// load issued before it).
+struct MxPlanes {
+  const uint8_t* win_fp8;
+  const uint8_t* win_sc;
+  const uint8_t* cmp_fp4;
+  const uint8_t* cmp_sc;
+  const uint8_t* dummy;   // the query's first bytes, read for masked entries
+};
+
+// One lane's share of a low-bit row r (a compacted entry: pool row, bit 31
+// for the window pool, kNoRow when masked): the codes of channels 8 * chunk
+// .. + 7 and their group's scale byte, with the flags above.  One 8-byte
+// payload load and one scale-byte load, from addresses picked without
+// branches: an E2M1 chunk is the half (chunk & 1) of an aligned 8-byte word
+// shared with its neighbour; a masked entry reads the dummy bytes and is
+// zeroed by the conversion.  UNIFORM: r is the same in every lane (one row
+// per load instruction), so the row's bases are formed on the scalar unit and
+// only the lane's chunk offset is per lane.
+template <int D, bool UNIFORM>
+__device__ __forceinline__ void mx_load(const MxPlanes& p, uint32_t r, int chunk, u32x2& pay,
+                                        uint32_t& sc) {
+  if constexpr (UNIFORM) r = __builtin_amdgcn_readfirstlane(r);
+  const bool win = (r & kWinBit) != 0u;
+  const bool masked = r == kNoRow;
+  const long long row = static_cast<long long>(r & ~kWinBit);
+  // (pointer selects, not integer arithmetic, so the loads stay global ones)
+  const uint8_t* pbase = masked ? p.dummy : (win ? p.win_fp8 + row * D : p.cmp_fp4 + row * (D / 2));
+  const uint8_t* sbase = masked ? p.dummy : (win ? p.win_sc + row * (D / 32) : p.cmp_sc + row * (D / 16));
+  const uint32_t poff = masked ? 0u : (win ? chunk * 8u : (chunk >> 1) * 8u);
+  const uint32_t soff = masked ? 0u : (win ? (chunk >> 2) : (chunk >> 1));
+  pay = *reinterpret_cast<const u32x2*>(pbase + poff);
+  sc = static_cast<uint32_t>(sbase[soff]) | (win ? kMxWin : 0u) | (masked ? kMxMasked : 0u);
+}
+
+// The eight channels as BF16, exactly (an E4M3 code times a power of two, or
+// an E2M1 code times an E4M3 code, has at most 6 significant bits).
+__device__ __forceinline__ uint4 mx_bf16x8(u32x2 pay, uint32_t sc, bool odd_chunk) {
+  uint4 v;
+  if (sc & kMxWin) {
+    // the E8M0 byte as the exponent field of the FP32 scale operand: the
+    // conversion multiplies by 2^(byte - 127) (byte 255: NaN)
+    const float f = __builtin_bit_cast(float, (sc & 0xffu) << 23);
+    v = uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pay[0], f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pay[0], f, true)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pay[1], f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pay[1], f, true))};
+  } else {
+    const float f = __builtin_amdgcn_cvt_f32_fp8(sc & 0xffu, 0);
+    const uint32_t w = odd_chunk ? pay[1] : pay[0];
+    v = uint4{fp4_pair_bf16<0>(w, f), fp4_pair_bf16<1>(w, f), fp4_pair_bf16<2>(w, f),
+              fp4_pair_bf16<3>(w, f)};
+  }
+  if (sc & kMxMasked) v = uint4{0u, 0u, 0u, 0u};
+  return v;
+}
+
 
 
 // Exclusive scan over a work-group of NW waves (scratch: one int per wave).
@@ -233,7 +307,7 @@ __device__ __forceinline__ void wait_tiles_behind(int behind) {
   }
 }
 
-template <int D>
+template <int D, bool MX>
 __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   constexpr int KS = D / 32;                 // K steps of S^T
   constexpr int RB = 2 * D;                  // bytes per key row
@@ -423,6 +497,34 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
           0, 0);
     }
   };
+  // Low-bit rows (MX): a loading wave's share of tile tt goes to register
+  // set tt & 1 (codes and scale words) and is dequantised into the tile's
+  // ring slot one step before the tile is used, the same lanes writing the
+  // same 16 bytes a direct-to-LDS load would.
+  [[maybe_unused]] const MxPlanes mp{a.win_fp8, a.win_sc, a.cmp_fp4, a.cmp_sc, dummy};
+  [[maybe_unused]] u32x2 mxp[2][MX ? LPW : 1];
+  [[maybe_unused]] uint32_t mxs[2][MX ? LPW : 1];
+  auto mx_issue = [&](int tt, auto set) {
+    constexpr int Q = decltype(set)::value;
+    if (!loader) return;
+    uint32_t rr[LPW];
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) {
+      const int j = tt * kTile + (wave * LPW + u) * RPI + lane / NC;
+      rr[u] = (j < n_valid) ? row_s[j] : kNoRow;
+    }
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) mx_load<D, RPI == 1>(mp, rr[u], lane % NC, mxp[Q][u], mxs[Q][u]);
+  };
+  auto mx_land = [&](auto set, auto sl) {
+    constexpr int Q = decltype(set)::value;
+    if (!loader) return;
+    uint8_t* slot = slot_of(sl);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u)
+      *reinterpret_cast<uint4*>(slot + (wave * LPW + u) * GS + lane * 16) =
+          mx_bf16x8(mxp[Q][u], mxs[Q][u], ((lane % NC) & 1) != 0);
+  };
   auto row_off = [](int r) { return (r / RPI) * GS + (r % RPI) * RB; };
 
   const float neg_inf = -__builtin_huge_valf();
@@ -435,10 +537,14 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   // each SIMD runs one wave of each kind.
   auto step_sync = [&](int k, auto sl) {
     constexpr int S = decltype(sl)::value;
-    // only tile k + 1 was issued after tile k
-    wait_tiles_behind<LPW>((k + 1 < ntiles) ? 1 : 0);
-    lds_barrier();
-    if (k + 2 < ntiles) issue(k + 2, std::integral_constant<int, (S + 2) % kRing>{});
+    if constexpr (MX) {
+      lds_barrier();   // every wave has written its rows of tile k (mx_end)
+    } else {
+      // only tile k + 1 was issued after tile k
+      wait_tiles_behind<LPW>((k + 1 < ntiles) ? 1 : 0);
+      lds_barrier();
+      if (k + 2 < ntiles) issue(k + 2, std::integral_constant<int, (S + 2) % kRing>{});
+    }
   };
 
   // Softmax against a fixed reference: m_ref is the first tile's max, and
@@ -454,8 +560,33 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   // both kinds of wave run the same barrier sequence: per pass, one barrier
   // per step, then the overflow vote and the normalisation hand-off
   auto prime = [&]() {
-    if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
-    if (ntiles > 1) issue(1, std::integral_constant<int, 1>{});
+    if constexpr (MX) {
+      if (ntiles > 0) mx_issue(0, std::integral_constant<int, 0>{});
+      if (ntiles > 1) mx_issue(1, std::integral_constant<int, 1>{});
+    } else {
+      if (ntiles > 0) issue(0, std::integral_constant<int, 0>{});
+      if (ntiles > 1) issue(1, std::integral_constant<int, 1>{});
+    }
+  };
+  // MX, after step k's work: tile k + 1 lands in its slot (free since tile
+  // k - 3 finished), and tile k + 3 goes out to the register set that frees.
+  // Landing after the step's work gives every load two steps' work to arrive.
+  auto mx_end = [&](int k, auto sl) {
+    if constexpr (MX) {
+      constexpr int S = decltype(sl)::value;
+      constexpr int Q = (S + 1) & 1;
+      if (k + 1 < ntiles)
+        mx_land(std::integral_constant<int, Q>{}, std::integral_constant<int, (S + 1) % kRing>{});
+      if (k + 3 < ntiles) mx_issue(k + 3, std::integral_constant<int, Q>{});
+    }
+  };
+  // MX: tile 0 lands and tile 2 goes out before the first step
+  auto prime_land = [&]() {
+    if constexpr (MX) {
+      if (ntiles > 0)
+        mx_land(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+      if (ntiles > 2) mx_issue(2, std::integral_constant<int, 0>{});
+    }
   };
 
   // first two tiles of the first pass, then the query behind them
@@ -467,6 +598,7 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < KS; ++ks)
       qraw[ks] = hv ? *reinterpret_cast<const v4i*>(qrow + ks * 32 + grp * 8) : v4i{0, 0, 0, 0};
   }
+  prime_land();
 
   // ---- query fragments (B operand of S^T) of the S waves: lane (head col,
   //      group grp) holds channels ks*32 + grp*8 .. +8, rotated where they
@@ -497,7 +629,10 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     // instructions go first when both waves of a SIMD are ready
     __builtin_amdgcn_s_setprio(2);
     for (int pass = 0; pass < 2; ++pass) {
-      if (pass > 0) prime();
+      if (pass > 0) {
+        prime();
+        prime_land();
+      }
       bool ovf = false;
       l_run = 0.0f;
       // S^T tile: rows = 32 keys (two 16-row M tiles), columns = this wave's
@@ -589,9 +724,19 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
       };
       for (int k = 0; k <= ntiles; k += kRing) {
         s_step(k, std::integral_constant<int, 0>{});
-        if (k + 1 <= ntiles) s_step(k + 1, std::integral_constant<int, 1>{});
-        if (k + 2 <= ntiles) s_step(k + 2, std::integral_constant<int, 2>{});
-        if (k + 3 <= ntiles) s_step(k + 3, std::integral_constant<int, 3>{});
+        mx_end(k, std::integral_constant<int, 0>{});
+        if (k + 1 <= ntiles) {
+          s_step(k + 1, std::integral_constant<int, 1>{});
+          mx_end(k + 1, std::integral_constant<int, 1>{});
+        }
+        if (k + 2 <= ntiles) {
+          s_step(k + 2, std::integral_constant<int, 2>{});
+          mx_end(k + 2, std::integral_constant<int, 2>{});
+        }
+        if (k + 3 <= ntiles) {
+          s_step(k + 3, std::integral_constant<int, 3>{});
+          mx_end(k + 3, std::integral_constant<int, 3>{});
+        }
       }
       // a second pass only when a logit outran the first tile's max (no load
       // is in flight here: the last step waited for all of them)
@@ -630,7 +775,10 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     const int d0 = (wave - HT) * DW;
     v4f o_acc[DTW][HT];
     for (int pass = 0; pass < 2; ++pass) {
-      if (pass > 0) prime();
+      if (pass > 0) {
+        prime();
+        prime_land();
+      }
 #pragma unroll
       for (int dt = 0; dt < DTW; ++dt)
 #pragma unroll
@@ -674,9 +822,19 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
       };
       for (int k = 0; k <= ntiles; k += kRing) {
         pv_step(k, std::integral_constant<int, 0>{});
-        if (k + 1 <= ntiles) pv_step(k + 1, std::integral_constant<int, 1>{});
-        if (k + 2 <= ntiles) pv_step(k + 2, std::integral_constant<int, 2>{});
-        if (k + 3 <= ntiles) pv_step(k + 3, std::integral_constant<int, 3>{});
+        mx_end(k, std::integral_constant<int, 0>{});
+        if (k + 1 <= ntiles) {
+          pv_step(k + 1, std::integral_constant<int, 1>{});
+          mx_end(k + 1, std::integral_constant<int, 1>{});
+        }
+        if (k + 2 <= ntiles) {
+          pv_step(k + 2, std::integral_constant<int, 2>{});
+          mx_end(k + 2, std::integral_constant<int, 2>{});
+        }
+        if (k + 3 <= ntiles) {
+          pv_step(k + 3, std::integral_constant<int, 3>{});
+          mx_end(k + 3, std::integral_constant<int, 3>{});
+        }
       }
       __syncthreads();   // the S waves' overflow vote
       const bool again = (ovf_s[0] | ovf_s[1] | ovf_s[2] | ovf_s[3]) != 0;
@@ -741,17 +899,6 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
 // partial (16 heads x D, normalised by its own sum) with the FP32 (max, sum)
 // for the merge kernel.
 constexpr int kSpan = kAttnWaves * kTile;   // list entries per decode work-group
-
-// Two E2M1 codes (byte BS of w, the lower-indexed one in bits 0-3) times an
-// FP32 scale, as a BF16 pair.  The products are BF16 values (at most 6
-// significant bits for an E4M3 scale), so their upper halves are exact.
-template <int BS>
-__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t w, float sc) {
-  const v2f_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BS);
-  const float lo = e[0] * sc, hi = e[1] * sc;
-  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
-                               0x07060302u);
-}
 
 template <int D, bool MX>
 __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a) {
@@ -891,41 +1038,22 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   const int j0 = wave * kTile;
   constexpr int NI = kTile / RPI;
   // low-bit rows go through registers: lane (row ins * RPI + lane / NC,
-  // chunk lane % NC) holds the codes of channels 8 * chunk .. + 7 and their
-  // group's scale byte until the conversion below
-  // (a native vector type: arrays of HIP's uint2 struct stay in scratch memory)
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  // chunk lane % NC) holds its codes and scale word until the conversion below
   [[maybe_unused]] u32x2 mx_pay[MX ? NI : 1];
   [[maybe_unused]] uint32_t mx_sc[MX ? NI : 1];
-  [[maybe_unused]] uint32_t mx_row[MX ? NI : 1];
   if constexpr (MX) {
     if (j0 < n_valid) {
-      const int chunk = lane % NC;
-      const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q);
+      uint32_t rr[NI];
 #pragma unroll
       for (int ins = 0; ins < NI; ++ins) {
         const int j = j0 + ins * RPI + lane / NC;
-        mx_row[ins] = (j < n_valid) ? row_s[j] : kNoRow;
+        rr[ins] = (j < n_valid) ? row_s[j] : kNoRow;
       }
-      // one 8-byte payload load and one scale-byte load per row, from
-      // addresses picked without branches (a branch per row would serialise
-      // the loads): an E2M1 chunk is the half (chunk & 1) of an aligned
-      // 8-byte word shared with its neighbour; a masked row reads the
-      // query's first bytes (always present) and is zeroed after conversion
+      const MxPlanes mp{a.win_fp8, a.win_sc, a.cmp_fp4, a.cmp_sc,
+                        reinterpret_cast<const uint8_t*>(a.q)};
 #pragma unroll
-      for (int ins = 0; ins < NI; ++ins) {
-        const uint32_t r = mx_row[ins];
-        const long long row = static_cast<long long>(r & ~kWinBit);
-        const bool win = (r & kWinBit) != 0u;
-        const uint8_t* pay = win ? a.win_fp8 + row * D + chunk * 8
-                                 : a.cmp_fp4 + row * (D / 2) + (chunk >> 1) * 8;
-        const uint8_t* scp = win ? a.win_sc + row * (D / 32) + (chunk >> 2)
-                                 : a.cmp_sc + row * (D / 16) + (chunk >> 1);
-        pay = (r == kNoRow) ? dummy : pay;
-        scp = (r == kNoRow) ? dummy : scp;
-        mx_pay[ins] = *reinterpret_cast<const u32x2*>(pay);
-        mx_sc[ins] = *scp;
-      }
+      for (int ins = 0; ins < NI; ++ins)
+        mx_load<D, RPI == 1>(mp, rr[ins], lane % NC, mx_pay[ins], mx_sc[ins]);
     }
   } else if (j0 < n_valid) {
     uint32_t rr[NI];
@@ -977,31 +1105,11 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
 #pragma unroll
   for (int i = 0; i < DT; ++i) o_acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   if constexpr (MX) {
-    // dequantise into the BF16 tile (exact: an E4M3 code times a power of two,
-    // or an E2M1 code times an E4M3 code, has at most 6 significant bits)
     if (j0 < n_valid) {
 #pragma unroll
-      for (int ins = 0; ins < NI; ++ins) {
-        const uint32_t r = mx_row[ins];
-        uint4 v;
-        if (r & kWinBit) {
-          // the E8M0 byte as the exponent field of the FP32 scale operand:
-          // the conversion multiplies by 2^(byte - 127) (byte 255: NaN)
-          const float sc = __builtin_bit_cast(float, mx_sc[ins] << 23);
-          const uint32_t wx = mx_pay[ins][0], wy = mx_pay[ins][1];
-          v = uint4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, sc, false)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wx, sc, true)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, sc, false)),
-                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wy, sc, true))};
-        } else {
-          const float sc = __builtin_amdgcn_cvt_f32_fp8(mx_sc[ins], 0);
-          const uint32_t wx = (lane % NC) & 1 ? mx_pay[ins][1] : mx_pay[ins][0];
-          v = uint4{fp4_pair_bf16<0>(wx, sc), fp4_pair_bf16<1>(wx, sc),
-                    fp4_pair_bf16<2>(wx, sc), fp4_pair_bf16<3>(wx, sc)};
-        }
-        if (r == kNoRow) v = uint4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<uint4*>(myslot + ins * GS + lane * 16) = v;
-      }
+      for (int ins = 0; ins < NI; ++ins)
+        *reinterpret_cast<uint4*>(myslot + ins * GS + lane * 16) =
+            mx_bf16x8(mx_pay[ins], mx_sc[ins], ((lane % NC) & 1) != 0);
     }
   } else {
     __builtin_amdgcn_s_waitcnt(0);   // this wave's rows have landed in its slot
@@ -1315,13 +1423,6 @@ SplitPlan plan_splits(int T, int k, int window, bool prefill) {
   return SplitPlan{true, (lmax + sp - 1) / sp, sp};
 }
 
-// Low-bit planes: every decode batch runs the decode kernel, kSpan entries
-// per span.
-inline SplitPlan mx_plan(int k, int window) {
-  const int lmax = max(1, window + k);
-  return SplitPlan{false, (lmax + kSpan - 1) / kSpan, 0};
-}
-
 // Decode workspace: the FP16 scaled partials [T][splits][H][D], their FP32
 // (max, sum) pairs [T][splits][H], then (16-byte aligned) the quarter factors
 // [T][splits][H][4].
@@ -1354,9 +1455,12 @@ int launch_attn(const AttnArgs& in, bool ring, bool mx, hipStream_t st) {
   a.items_per_xcd = static_cast<int>((items + 7) / 8);
   const long long grid = static_cast<long long>(a.items_per_xcd) * 8;
   if (grid > 0x7fffffffll) return CSA_ERR_UNSUPPORTED;
-  if (ring)
-    hipLaunchKernelGGL(attn_kernel<D>, dim3(static_cast<unsigned>(grid)), dim3(kRingThreads), 0,
-                       st, a);
+  if (ring && mx)
+    hipLaunchKernelGGL((attn_kernel<D, true>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kRingThreads), 0, st, a);
+  else if (ring)
+    hipLaunchKernelGGL((attn_kernel<D, false>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kRingThreads), 0, st, a);
   else if (mx)
     hipLaunchKernelGGL((attn_decode_kernel<D, true>), dim3(static_cast<unsigned>(grid)),
                        dim3(kAttnThreads), 0, st, a);
@@ -1435,8 +1539,7 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   if (static_cast<long long>(num_cmp_blocks) * kPage >= (1ll << 31) ||
       static_cast<long long>(num_win_blocks) * kPage >= (1ll << 31))
     return CSA_ERR_UNSUPPORTED;
-  // the low-bit planes are read by the decode kernel alone (spans of kSpan)
-  const SplitPlan plan = mx ? mx_plan(k, window) : plan_splits(num_tokens, k, window, prefill);
+  const SplitPlan plan = plan_splits(num_tokens, k, window, prefill);
   // the ring schedule holds a row's whole key list in LDS
   if (plan.ring && plan.splits == 1 && window + k > kMaxSplit) return CSA_ERR_UNSUPPORTED;
   AttnArgs a{};
@@ -1548,13 +1651,10 @@ extern "C" int csa_sparse_attn_prefill(
                          H, D, out, lse, workspace, workspace_bytes, err, stream);
 }
 
-// The low-bit plan does not depend on the active count, so the size for T
-// covers every count up to T.
+// The low-bit planes run the schedules of csa_sparse_attn_decode.
 extern "C" size_t csa_sparse_attn_mx_workspace_bytes(int32_t T, int32_t H, int32_t D, int32_t k,
                                                      int32_t window) {
-  if (T <= 0 || H <= 0 || D <= 0 || k < 0 || window < 0) return 0;
-  const csa::SplitPlan plan = csa::mx_plan(k, window);
-  return plan.splits > 1 ? csa::attn_ws_bytes(T, plan.splits, H, D) : 0;
+  return csa_sparse_attn_workspace_bytes(T, H, D, k, window);
 }
 
 extern "C" int csa_sparse_attn_decode_mx(

@@ -277,9 +277,10 @@ int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const floa
  *   win_fp8   UINT8 [num_win_blocks, 128, D]: E4M3 codes
  *   win_scale UINT8 [num_win_blocks, 128, D / 32]: E8M0 bytes; channel c of a
  *             row is e4m3(c) * 2^(win_scale[c / 32] - 127) (byte 255 is NaN)
- *   workspace csa_sparse_attn_mx_workspace_bytes(T, H, D, k, window) bytes,
- *             16-byte aligned (NULL when that size is 0); its schedule does
- *             not depend on num_tokens, so the size for T covers any count.
+ *   workspace csa_sparse_attn_mx_workspace_bytes(T, H, D, k, window) bytes
+ *             (the same size as csa_sparse_attn_workspace_bytes), 16-byte
+ *             aligned, NULL when that size is 0; it covers every num_tokens
+ *             up to T.
  *
  * Each row is dequantised exactly (an E4M3 code times a power of two, or an
  * E2M1 code times an E4M3 code, is a BF16 value; only products outside BF16's
@@ -287,9 +288,10 @@ int csa_sparse_attn_prefill(const uint16_t* q, const float* rope_cos, const floa
  * attention multiplies, so the result is csa_sparse_attn_decode's on the
  * dequantised rows.  NaN codes propagate as NaN.  A payload plane given without its scale plane returns
  * CSA_ERR_NULL; a NULL pair is an empty pool (its rows flag BLOCK_RANGE).
- * Plane pointers are 16-byte aligned.  Every batch size runs the decode
- * schedule (128-entry spans per 16-head group, merged); there is no prefill
- * form.
+ * Plane pointers are 16-byte aligned.  The schedules are those of
+ * csa_sparse_attn_decode (its kernels with the rows dequantised on their way
+ * into LDS), so the result has the same bits as csa_sparse_attn_decode on
+ * BF16 pools holding the dequantised rows.  There is no prefill form.
  */
 size_t csa_sparse_attn_mx_workspace_bytes(int32_t T, int32_t H, int32_t D, int32_t k,
                                           int32_t window);

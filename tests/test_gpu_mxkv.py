@@ -114,9 +114,8 @@ def _bf16_bits(values):
 
 def _same_as_bf16_decode(csa, cfg, x, sel, rc, rs, what):
     """The low-bit call against the BF16 decode entry point on the pools the
-    oracle's planes dequantise: key lists below 1024 entries run the same
-    decode kernel from either entry point, so the bits must agree."""
-    assert cfg.W + cfg.k < 1024
+    oracle's planes dequantise: both entry points run the same schedule and
+    kernels once a tile is in LDS, so the bits must agree."""
     out, lse, err = _run_mx(csa, cfg, x, sel, rc, rs)
     assert err == 0
     cmp_src, win_src = H.kv_sources(x, cfg)
@@ -141,24 +140,27 @@ def _same_as_bf16_decode(csa, cfg, x, sel, rc, rs, what):
     assert torch.equal(lse, lse_b), what
 
 
-@pytest.mark.parametrize("H_,D,R", [(8, 64, 16), (64, 512, 64)])
-def test_mx_equals_bf16_decode_on_dequantised_planes(H_, D, R):
-    print(f"[mxkv] vs bf16 H={H_} D={D}", flush=True)
+@pytest.mark.parametrize("H_,D,R,k", [(8, 64, 16, 500), (64, 512, 64, 500), (8, 64, 16, 1000),
+                                      (64, 512, 64, 1000)])
+def test_mx_equals_bf16_decode_on_dequantised_planes(H_, D, R, k):
+    """k = 500: the decode kernel (128-entry spans per 16-head group);
+    k = 1000: lists past 1024 entries, the ring kernel over spans."""
+    print(f"[mxkv] vs bf16 H={H_} D={D} k={k}", flush=True)
     csa = _csa()
-    cfg = _shape_cfg(H_, D, R, k=500)
+    cfg = _shape_cfg(H_, D, R, k=k)
     x = synthetic.make_inputs(cfg, seed=8).t
     _same_as_bf16_decode(csa, cfg, x, _selection(cfg, 4), *_rope(cfg, 6), f"D{D}")
 
 
-@pytest.mark.parametrize("D", [64, 512])
-def test_mx_extreme_scales_and_every_code(D):
+@pytest.mark.parametrize("D,k", [(64, 500), (512, 500), (512, 1000)])
+def test_mx_extreme_scales_and_every_code(D, k):
     """Every non-NaN E4M3 window code beside E8M0 bytes over 10 .. 150 (the
     products stay normal BF16 numbers), every E2M1 nibble beside every
     non-NaN E4M3 group scale of either sign (subnormals and zero included):
     the same bits as the BF16 decode on the oracle's dequantised pools."""
-    print(f"[mxkv] extreme scales D={D}", flush=True)
+    print(f"[mxkv] extreme scales D={D} k={k}", flush=True)
     csa = _csa()
-    cfg = _shape_cfg(8 if D == 64 else 64, D, 16 if D == 64 else 64, k=500)
+    cfg = _shape_cfg(8 if D == 64 else 64, D, 16 if D == 64 else 64, k=k)
     x = dict(synthetic.make_inputs(cfg, seed=9).t)
     rng = np.random.default_rng(10)
     codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
@@ -166,7 +168,8 @@ def test_mx_extreme_scales_and_every_code(D):
     x["win_scale"] = rng.integers(10, 151, size=x["win_scale"].shape, dtype=np.uint8)
     x["cmp_fp4"] = rng.integers(0, 256, size=x["cmp_fp4"].shape, dtype=np.uint8)
     x["cmp_scale"] = rng.choice(codes, size=x["cmp_scale"].shape).astype(np.uint8)
-    _same_as_bf16_decode(csa, cfg, x, _selection(cfg, 12), *_rope(cfg, 13), f"extreme D{D}")
+    _same_as_bf16_decode(csa, cfg, x, _selection(cfg, 12), *_rope(cfg, 13),
+                         f"extreme D{D} k{k}")
 
 
 def test_mx_nan_codes_propagate():

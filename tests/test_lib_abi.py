@@ -246,10 +246,10 @@ def test_mx_decode_host_checks(lib):
     decode call's own host checks apply."""
     f = lib.csa_sparse_attn_decode_mx
     ws = lib.csa_sparse_attn_mx_workspace_bytes
-    # (2048 + 128) keys in 128-entry spans: 17 partials per row and head
-    per = 64 * (512 * 2 + 24)
-    assert ws(8, 64, 512, 2048, 128) == 8 * 17 * per
-    assert ws(300, 64, 512, 2048, 128) == 300 * 17 * per   # no ring schedule for many rows
+    # the schedules, and so the sizes, of the BF16 decode
+    for T in (1, 8, 255, 300):
+        for k, w in ((2048, 128), (512, 128), (0, 100)):
+            assert ws(T, 64, 512, k, w) == lib.csa_sparse_attn_workspace_bytes(T, 64, 512, k, w)
     assert ws(8, 64, 512, 0, 100) == 0                     # one span: no partials
     assert ws(0, 64, 512, 2048, 128) == 0
     need = ws(8, 64, 512, 2048, 128)
