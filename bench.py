@@ -40,7 +40,7 @@ INT8_PEAK_TOPS = 5000.0        # dense INT8 MFMA
 
 KERNEL_SOURCES = {
     "rope": "csa_rope.hip", "index": "csa_index.hip", "topk": "csa_topk.hip",
-    "attn": "csa_attn.hip",
+    "attn": "csa_attn.hip", "cand": "csa_topk.hip",
 }
 
 
@@ -438,6 +438,7 @@ def main():
         "step_hbm": {"algorithmic_bytes": wm["step_bytes"], "achieved_gbs": round(step_gbs, 1),
                      "frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4)},
         "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
+        "stage_bytes_algorithmic": wm["stage_bytes"],
         "roofline": roof,
         "device_errors": errs[0],
     }

@@ -442,8 +442,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
       // are already waited for (the vmcnt wait and barrier above).
       // Each wait names the registers it covers, which orders their uses
       // after it.
-      const uint32_t kbase = lds_addr(keys);
-      const uint32_t sbase = lds_addr(ksd);
+      uint32_t kbase = lds_addr(keys);
+      uint32_t sbase = lds_addr(ksd);
+      // The stage's LDS bases pass through an empty asm, so the per-lane
+      // addresses below are formed here, for each page, instead of being
+      // hoisted out of the page loop as one live set per stage: those sets
+      // spilled, and each reload's vmcnt(0) waited for the next pages' loads.
+      asm volatile("" : "+s"(kbase), "+s"(sbase));
       uint32_t ksw0 = 0u, ksw1 = 0u;   // INT8: the FP32 scales of keys lane, 64 + lane
       if constexpr (!FP4) {
         lds_read_b32(ksw0, sbase + 4 * lane);
