@@ -219,6 +219,56 @@ def index_scores(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table,
     return scores, err
 
 
+def index_scores_fp8(q_fp8, q_scale, head_w, idx_fp8, idx_scale, block_table,
+                     query_start_loc, positions, num_tokens, ratio, score_stride,
+                     key_chunk: int = 1 << 16):
+    """The indexer score with the FP8 index plane ([ATOM] "Current execution
+    scope": FP8 is the default index cache dtype; its layout is not given).
+    Reading: the INT8 plane's layout with E4M3 codes in place of INT8 ones --
+    key rows [blocks, 128, Di] of OCP E4M3FN codes with one FP32 scale per
+    row, the query [T, Hi, Di] of E4M3 codes with one FP32 scale per (row,
+    head) -- and the score formula of ``index_scores`` over the decoded values:
+
+        score[t, c] = sum_h w[t,h] * relu( qs[t,h] * ks[c] * <e4m3(q[t,h]), e4m3(k[c])> )
+
+    Every product of two E4M3 values, and every sum of Di <= 128 of them, is
+    exact in float64.  Visibility, contract checks and flags are those of
+    ``index_scores``.  Returns (scores float64 [num_tokens, score_stride], err)."""
+    qsl = np.asarray(query_start_loc)
+    num_blocks = idx_fp8.shape[0]
+    Di = idx_fp8.shape[2]
+    keys_flat = np.asarray(idx_fp8, dtype=np.uint8).reshape(num_blocks * PAGE, Di)
+    scales_flat = np.asarray(idx_scale, dtype=np.float64).reshape(-1)
+    scores = np.full((int(num_tokens), int(score_stride)), -np.inf, dtype=np.float64)
+    err = 0
+    max_blocks = block_table.shape[1]
+    for t in range(int(num_tokens)):
+        b = owner_request(t, qsl)
+        if b < 0:
+            err |= EFLAG_META
+            continue
+        n = visible_count(positions[t], ratio)
+        if n > score_stride or n > PAGE * max_blocks:
+            err |= EFLAG_POS_RANGE
+            n = min(n, int(score_stride), PAGE * max_blocks)
+        q = decode_e4m3(q_fp8[t])                             # [Hi, Di]
+        qs = np.asarray(q_scale[t], dtype=np.float64)         # [Hi]
+        w = np.asarray(head_w[t], dtype=np.float64)           # [Hi]
+        for c0 in range(0, n, key_chunk):
+            cs = np.arange(c0, min(n, c0 + key_chunk))
+            rows, ok = _physical_rows(block_table[b], num_blocks, cs)
+            if not ok.all():
+                err |= EFLAG_BLOCK_RANGE
+            k = decode_e4m3(keys_flat[rows])                  # [n_c, Di]
+            ks = scales_flat[rows]                            # [n_c]
+            dots = q @ k.T                                    # [Hi, n_c], exact
+            per_head = qs[:, None] * ks[None, :] * dots
+            s = (w[:, None] * np.maximum(per_head, 0.0)).sum(axis=0)
+            s[~ok] = -np.inf
+            scores[t, cs] = s
+    return scores, err
+
+
 # ----------------------------------------------------------------------------
 # a2 with the low-bit index plane: MXFP4 keys and queries
 # ----------------------------------------------------------------------------
