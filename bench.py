@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c5",
-                    help="c1..c13 (default c5: max-context ratio-1 decode)")
+                    help="c1..c15 (default c5: max-context ratio-1 decode)")
     ap.add_argument("--copies", type=int, default=0, help="input copies (0 = auto, cold L2/MALL)")
     ap.add_argument("--warm", action="store_true", help="one input copy (cache-warm timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -236,7 +236,14 @@ def cpu_baseline(cfg, x, budget_s: float):
         oracle.materialize_rope_rows(sub["freqs_cos"], sub["freqs_sin"], sub["position_ids"], n,
                                      rc, rs)
         b_ = time.perf_counter()
-        if mode in ("csa", "hier_full") and cfg.index_format == "mxfp4":
+        if mode in ("csa", "hier_full") and cfg.index_format == "fp8":
+            s, _ = oracle.index_scores_fp8(sub["q_idx"], sub["q_scale"], sub["head_w"],
+                                           sub["idx_kv"], sub["idx_scale"],
+                                           sub["cmp_block_table"], sub["query_start_loc"],
+                                           sub["positions"], n, cfg.ratio, cfg.score_stride)
+            c_ = time.perf_counter()
+            idx, _, _ = oracle.topk(s, sub["positions"], cfg.ratio, n, cfg.k)
+        elif mode in ("csa", "hier_full") and cfg.index_format == "mxfp4":
             s, _ = oracle.index_scores_mxfp4(sub["q_idx"], sub["q_scale"], sub["head_w"],
                                              sub["idx_kv"], sub["idx_scale"],
                                              sub["cmp_block_table"], sub["query_start_loc"],
@@ -417,7 +424,7 @@ def main():
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp4+bf16" if cfg.index_format == "mxfp4" else "int8+bf16",
+        "dtype": {"mxfp4": "mxfp4+bf16", "fp8": "fp8+bf16"}.get(cfg.index_format, "int8+bf16"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "rows": cfg.T, "requests": cfg.B, "heads": cfg.H,
                    "head_dim": cfg.D, "ratio": cfg.ratio, "top_k": cfg.k, "window": cfg.W,
@@ -425,7 +432,7 @@ def main():
                    "kv_cache": ("window MXFP8 E4M3 + E8M0/32, compressed MXFP4 E2M1 + E4M3/16"
                                 if cfg.kv_format == "mx" else "bf16"),
                    "indexer": ((f"{cfg.Hi}x{cfg.Di}" +
-                                (" mxfp4" if cfg.index_format == "mxfp4" else " int8"))
+                                " " + cfg.index_format)
                                if first.mode in ("csa", "reindex", "hier_full") else "none"),
                    "selection": {"csa": "indexer top-k", "hca": "every visible compressed row",
                                  "swa": "window only",

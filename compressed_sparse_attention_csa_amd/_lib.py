@@ -55,6 +55,7 @@ _SIGS = {
                                            _P, _P, _SZ, _P, _P]),
 }
 _SIGS["csa_sparse_attn_prefill"] = _SIGS["csa_sparse_attn_decode"]
+_SIGS["csa_index_score_fp8"] = _SIGS["csa_index_score"]
 _SIGS["csa_sparse_attn_mx_workspace_bytes"] = _SIGS["csa_sparse_attn_workspace_bytes"]
 # the decode arguments with a scale plane after each payload plane
 _SIGS["csa_sparse_attn_decode_mx"] = (
@@ -164,6 +165,21 @@ def csa_index_score_mxfp4(q_fp4, q_sc, head_w, idx_fp4, idx_sc, block_table, que
         query_start_loc.shape[0] - 1, T, int(num_tokens), Hi, 2 * Db, int(ratio), _ptr(scores),
         scores.shape[1], _ptr(err), _stream(stream))
     _check(st, "csa_index_score_mxfp4")
+
+
+def csa_index_score_fp8(q_fp8, q_scale, head_w, idx_fp8, idx_scale, block_table,
+                        query_start_loc, positions, num_tokens, ratio, scores, err=None,
+                        stream=None) -> None:
+    _need(q_fp8, (torch.uint8,), 3, "q_fp8")
+    _need(idx_fp8, (torch.uint8,), 3, "idx_fp8")
+    _need(scores, (torch.float32,), 2, "scores")
+    T, Hi, Di = q_fp8.shape
+    st = load().csa_index_score_fp8(
+        _ptr(q_fp8), _ptr(q_scale), _ptr(head_w), _ptr(idx_fp8), _ptr(idx_scale),
+        idx_fp8.shape[0], _ptr(block_table), block_table.shape[1], _ptr(query_start_loc),
+        _ptr(positions), query_start_loc.shape[0] - 1, T, int(num_tokens), Hi, Di, int(ratio),
+        _ptr(scores), scores.shape[1], _ptr(err), _stream(stream))
+    _check(st, "csa_index_score_fp8")
 
 
 def csa_topk_workspace_bytes(T: int, score_stride: int, k: int) -> int:

@@ -155,7 +155,12 @@ __device__ __forceinline__ v8i lo_v8i(v4i x) {
   return __builtin_shufflevector(x, v4i{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int KK, bool FP4>
+// FP8: the FP8 index plane -- E4M3 codes in the INT8 plane's layout (Di
+// bytes per row, FP32 per-row key and per-(row, head) query scales); the
+// dots run on the block-scaled FP8 MFMA with unit block scales, each 64-dim
+// operand being two of the INT8 path's 32-dim fragments (a dot does not
+// depend on the order of its terms, and both operands pair the same dims).
+template <int KK, bool FP4, bool FP8 = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kIdxWaves, kIdxWaves))) index_score_kernel(
     const int8_t* __restrict__ q_idx, const float* __restrict__ q_scale,
     const float* __restrict__ head_w, const int8_t* __restrict__ idx_kv,
@@ -339,7 +344,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
         // select), so they issue together instead of one guarded round trip
         // each.
         const long long hc = static_cast<long long>(my_t) * Hi + (hh < Hi ? hh : 0);
-        const float wv = FP4 ? head_w[hc] : head_w[hc] * q_scale[hc] * 2097152.0f;
+        const float wv = FP4 ? head_w[hc]
+                             : head_w[hc] * q_scale[hc] * (FP8 ? 1.0f : 2097152.0f);
         ww[mt][j] = (hh < Hi) ? wv : 0.0f;
       }
     }
@@ -551,6 +557,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
               accf = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   lo_v8i(qa[mt][ks]), lo_v8i(bk[cur][ks]), ks == 0 ? zero16 : accf, 4, 4, 0,
                   sa[mt][ks], 0, sb[ks]);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) xs = fmaf(ww[mt][j], fmaxf(accf[j], 0.0f), xs);
+          } else if constexpr (FP8) {
+            // FP32 dots of the E4M3 rows (block scales 2^0), ReLU, head weight
+            const v16f zero16 = {};
+            v16f accf;
+#pragma unroll
+            for (int s2 = 0; s2 < KS / 2; ++s2) {
+              const v8i a8 = __builtin_shufflevector(qa[mt][2 * s2], qa[mt][2 * s2 + 1], 0, 1, 2,
+                                                     3, 4, 5, 6, 7);
+              const v8i b8 = __builtin_shufflevector(bk[cur][2 * s2], bk[cur][2 * s2 + 1], 0, 1,
+                                                     2, 3, 4, 5, 6, 7);
+              accf = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  a8, b8, s2 == 0 ? zero16 : accf, 0, 0, 0, 127, 0, 127);
+            }
 #pragma unroll
             for (int j = 0; j < 16; ++j) xs = fmaf(ww[mt][j], fmaxf(accf[j], 0.0f), xs);
           } else {
@@ -777,7 +798,9 @@ __global__ void __launch_bounds__(kThreads) index_cand_kernel(
 
 }  // namespace csa
 
-extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const float* head_w,
+namespace {
+template <bool FP8>
+int index_entry(const int8_t* q_idx, const float* q_scale, const float* head_w,
                                const int8_t* idx_kv, const float* idx_scale, int32_t num_blocks,
                                const int32_t* block_table, int32_t max_blocks,
                                const int32_t* query_start_loc, const int32_t* positions,
@@ -816,17 +839,45 @@ extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const 
   dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(groups));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (Di <= 64) {
-    hipLaunchKernelGGL((csa::index_score_kernel<1, false>), grid, dim3(csa::kThreads), 0, st, q_idx,
+    hipLaunchKernelGGL((csa::index_score_kernel<1, false, FP8>), grid, dim3(csa::kThreads), 0, st, q_idx,
                        q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table, max_blocks,
                        query_start_loc, positions, B, num_tokens, Hi, Di, ratio, scores,
                        static_cast<long long>(score_stride), static_cast<int>(ppw), err);
   } else {
-    hipLaunchKernelGGL((csa::index_score_kernel<2, false>), grid, dim3(csa::kThreads), 0, st, q_idx,
+    hipLaunchKernelGGL((csa::index_score_kernel<2, false, FP8>), grid, dim3(csa::kThreads), 0, st, q_idx,
                        q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table, max_blocks,
                        query_start_loc, positions, B, num_tokens, Hi, Di, ratio, scores,
                        static_cast<long long>(score_stride), static_cast<int>(ppw), err);
   }
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int csa_index_score(const int8_t* q_idx, const float* q_scale, const float* head_w,
+                               const int8_t* idx_kv, const float* idx_scale, int32_t num_blocks,
+                               const int32_t* block_table, int32_t max_blocks,
+                               const int32_t* query_start_loc, const int32_t* positions,
+                               int32_t B, int32_t T, int32_t num_tokens, int32_t Hi, int32_t Di,
+                               int32_t ratio, float* scores, int64_t score_stride, int32_t* err,
+                               void* stream) {
+  return index_entry<false>(q_idx, q_scale, head_w, idx_kv, idx_scale, num_blocks, block_table,
+                            max_blocks, query_start_loc, positions, B, T, num_tokens, Hi, Di,
+                            ratio, scores, score_stride, err, stream);
+}
+
+extern "C" int csa_index_score_fp8(const uint8_t* q_fp8, const float* q_scale,
+                                   const float* head_w, const uint8_t* idx_fp8,
+                                   const float* idx_scale, int32_t num_blocks,
+                                   const int32_t* block_table, int32_t max_blocks,
+                                   const int32_t* query_start_loc, const int32_t* positions,
+                                   int32_t B, int32_t T, int32_t num_tokens, int32_t Hi,
+                                   int32_t Di, int32_t ratio, float* scores,
+                                   int64_t score_stride, int32_t* err, void* stream) {
+  return index_entry<true>(reinterpret_cast<const int8_t*>(q_fp8), q_scale, head_w,
+                           reinterpret_cast<const int8_t*>(idx_fp8), idx_scale, num_blocks,
+                           block_table, max_blocks, query_start_loc, positions, B, T, num_tokens,
+                           Hi, Di, ratio, scores, score_stride, err, stream);
 }
 
 extern "C" int csa_index_score_candidates(

@@ -42,9 +42,9 @@ class CsaStep:
         if mode in ("reindex", "hier_full") and cand_kb < 1:
             raise ValueError(f"mode {mode!r} needs cand_kb >= 1")
         self.mode = mode
-        if index_format not in ("int8", "mxfp4"):
+        if index_format not in ("int8", "mxfp4", "fp8"):
             raise ValueError(f"unknown index format {index_format!r}")
-        if index_format == "mxfp4" and mode == "reindex":
+        if index_format != "int8" and mode == "reindex":
             raise ValueError("the reindex scorer takes the INT8 index plane")
         self.index_format = index_format
         # "bf16": arrays cmp_kv / win_kv; "mx": the low-bit planes cmp_fp4 +
@@ -119,6 +119,12 @@ class CsaStep:
                                        t["idx_scale"], t["cmp_block_table"],
                                        t["query_start_loc"], t["positions"], self.num_tokens,
                                        self.ratio, self.scores, err=self.err, stream=stream)
+            return
+        if self.index_format == "fp8":
+            _lib.csa_index_score_fp8(t["q_idx"], t["q_scale"], t["head_w"], t["idx_kv"],
+                                     t["idx_scale"], t["cmp_block_table"], t["query_start_loc"],
+                                     t["positions"], self.num_tokens, self.ratio, self.scores,
+                                     err=self.err, stream=stream)
             return
         _lib.csa_index_score(t["q_idx"], t["q_scale"], t["head_w"], t["idx_kv"], t["idx_scale"],
                              t["cmp_block_table"], t["query_start_loc"], t["positions"],

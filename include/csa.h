@@ -6,7 +6,8 @@
  *   1. csa_materialize_rope_rows  -- gather FP32 half-width RoPE rows
  *   2. csa_index_score            -- INT8 lightning-indexer scores over the
  *                                    causally visible compressed positions
- *      (csa_index_score_mxfp4: the same scores from the MXFP4 index plane)
+ *      (csa_index_score_mxfp4 / csa_index_score_fp8: the same scores from
+ *      the MXFP4 or FP8 index plane)
  *   3. csa_topk                   -- the k best positions, ascending, -1 padded
  *      (hierarchical layers: csa_candidate_blocks publishes a block mask;
  *      csa_index_score_candidates + csa_topk_candidates select inside it)
@@ -369,6 +370,30 @@ int csa_index_score_mxfp4(const uint8_t* q_fp4, const uint8_t* q_sc, const float
                           const int32_t* query_start_loc, const int32_t* positions, int32_t B,
                           int32_t T, int32_t num_tokens, int32_t Hi, int32_t Di, int32_t ratio,
                           float* scores, int64_t score_stride, int32_t* err, void* stream);
+
+/*
+ * csa_index_score_fp8 -- csa_index_score with the FP8 index plane ([ATOM]
+ * "Current execution scope": FP8 is the default index cache dtype; the pages
+ * give no layout, so it is read as the INT8 plane's with OCP E4M3FN codes in
+ * place of INT8 ones).  The score is
+ *     score[t,c] = sum_h w[t,h] * relu( qs[t,h] * ks[c] * <e4m3(q[t,h]), e4m3(k[c])> )
+ * with every argument, layout, check and flag as in csa_index_score, except:
+ *
+ *   q_fp8    UINT8 [T, Hi, Di]: E4M3 codes of the query rows
+ *   idx_fp8  UINT8 [num_blocks, 128, Di]: E4M3 codes of the key rows
+ *
+ * The codes must not be NaN (0x7F, 0xFF).  The dots run on gfx950's
+ * block-scaled FP8 MFMA with unit block scales; products of two E4M3 values
+ * are exact in FP32, so only the accumulation order differs from an exact
+ * dot.  Supported: as csa_index_score (16 <= Di <= 128, Di a multiple of 16,
+ * Hi <= 64).
+ */
+int csa_index_score_fp8(const uint8_t* q_fp8, const float* q_scale, const float* head_w,
+                        const uint8_t* idx_fp8, const float* idx_scale, int32_t num_blocks,
+                        const int32_t* block_table, int32_t max_blocks,
+                        const int32_t* query_start_loc, const int32_t* positions, int32_t B,
+                        int32_t T, int32_t num_tokens, int32_t Hi, int32_t Di, int32_t ratio,
+                        float* scores, int64_t score_stride, int32_t* err, void* stream);
 
 /*
  * Hierarchical selection ([V41] "Decode composition"): a full layer publishes

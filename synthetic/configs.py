@@ -47,8 +47,9 @@ class CsaConfig:
     mode: str = "csa"
     cand_kb: int = 0
     cand_block: int = 8
-    # index plane: "int8" (INT8 keys and query, FP32 per-row scales) or
-    # "mxfp4" (packed E2M1 keys and query, one E8M0 scale per 32 dims)
+    # index plane: "int8" (INT8 keys and query, FP32 per-row scales), "fp8"
+    # (E4M3 codes in the same layout) or "mxfp4" (packed E2M1 keys and query,
+    # one E8M0 scale per 32 dims)
     index_format: str = "int8"
     # KV planes: "bf16" (one BF16 cache per pool) or "mx" (the low-bit cache
     # ABI: window rows MXFP8 E4M3 with one E8M0 byte per 32 channels,
@@ -217,10 +218,24 @@ C13 = _decode(
     n_req=2, s=4, context=1 << 20, ratio=1, k=2048, shared_pool=True, index_format="mxfp4",
     kv_format="mx")
 
+# The FP8 index plane, ROCm ATOM's default index cache dtype ("DeepSeek-V4.1
+# native paged runtime", "Current execution scope"), on the max-context and
+# the ratio-2 decode shapes.
+C14 = _decode(
+    "c14_maxctx_fp8index_decode",
+    "max-context ratio-1 decode with the FP8 index plane: C5's shapes, index keys and "
+    "queries as E4M3 codes with FP32 per-row / per-head scales (132 bytes per key)",
+    n_req=2, s=4, context=1 << 20, ratio=1, k=2048, shared_pool=True, index_format="fp8")
+
+C15 = _decode(
+    "c15_ratio2_fp8index_decode",
+    "V4.1 ratio-2 decode with the FP8 index plane: C2's shapes",
+    n_req=4, s=2, context=32768, ratio=2, k=512, index_format="fp8")
+
 CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8, C9, C10,
-                                                     C11, C12, C13)}
+                                                     C11, C12, C13, C14, C15)}
 SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7, "c8": C8,
-         "c9": C9, "c10": C10, "c11": C11, "c12": C12, "c13": C13}
+         "c9": C9, "c10": C10, "c11": C11, "c12": C12, "c13": C13, "c14": C14, "c15": C15}
 
 
 def get(name: str) -> CsaConfig:

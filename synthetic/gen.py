@@ -13,6 +13,9 @@ for the larger ones:
 * indexer keys: integers uniform on [-127, 127]; per-row FP32 key scales
   U(0.005, 0.02); with ``outlier_frac`` > 0 each compressed position is an
   outlier with that probability and its key scale is multiplied by 4.
+* FP8 index plane (``index_format`` "fp8"): key and query E4M3 codes drawn
+  like the window plane's below (exponent field 4..10, never NaN), the INT8
+  plane's FP32 key scales, query scales U(0.01, 0.05).
 * indexer query: float32 N(0,1) quantised per (row, head) to INT8 with the
   per-token amax rule of pypto-lib "DeepSeek V4-Flash, MTP point", section
   "What is quantized" (amax floored at 1e-4, mapped to 127).  This is input
@@ -49,7 +52,8 @@ _TENSOR_IDS = {
     "idx_scale": 7, "outlier": 8, "attn_sink": 9, "cmp_perm": 10, "win_perm": 11,
     "cand_blocks": 12, "q_fp4": 13, "q_e8m0": 14, "idx_fp4": 15, "idx_e8m0": 16,
     "win_fp8_bits": 17, "win_fp8_exp": 18, "win_e8m0": 19, "cmp_fp4": 20, "cmp_sc_m": 21,
-    "cmp_sc_e": 22,
+    "cmp_sc_e": 22, "idx_fp8_bits": 23, "idx_fp8_exp": 24, "q_fp8_bits": 25, "q_fp8_exp": 26,
+    "q_fp8_scale": 27,
 }
 
 _CHUNK_ELEMS = 1 << 24  # fixed chunk so the draws never depend on the caller
@@ -187,6 +191,16 @@ def make_inputs(cfg: CsaConfig, seed: int = 0, with_tables: bool = True) -> CsaI
         hit = _rng(seed, "outlier").random((nbc, PAGE)) < cfg.outlier_frac
         sc = np.where(hit, sc * np.float32(4.0), sc).astype(np.float32)
     t["idx_scale"] = sc
+    if cfg.index_format == "fp8":
+        # the FP8 plane replaces the INT8 one (same names, same FP32 scales):
+        # E4M3 codes with uniform sign and mantissa and exponent field 4..10,
+        # never NaN; query scales U(0.01, 0.05)
+        def e4m3_codes(bits_name, exp_name, shape):
+            bits = _u8_uniform(seed, bits_name, shape, 0, 255)
+            return (bits & 0x87) | (_u8_uniform(seed, exp_name, shape, 4, 10) << 3)
+        t["q_idx"] = e4m3_codes("q_fp8_bits", "q_fp8_exp", (T, Hi, Di))
+        t["q_scale"] = _rng(seed, "q_fp8_scale").uniform(0.01, 0.05, size=(T, Hi)).astype(np.float32)
+        t["idx_kv"] = e4m3_codes("idx_fp8_bits", "idx_fp8_exp", (nbc, PAGE, Di))
     if cfg.index_format == "mxfp4":
         # the FP4 plane replaces the INT8 one (same names): packed E2M1 codes,
         # every nibble uniform over the 16 codes, and E8M0 group scales

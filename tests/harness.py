@@ -47,8 +47,8 @@ def oracle_step(x: dict, cfg, topk_override=None) -> dict:
     rc = np.full((T, half), np.nan, np.float32)
     rs = np.full((T, half), np.nan, np.float32)
     e0 = oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["position_ids"], T, rc, rs)
-    score_fn = (oracle.index_scores_mxfp4 if getattr(cfg, "index_format", "int8") == "mxfp4"
-                else oracle.index_scores)
+    score_fn = {"mxfp4": oracle.index_scores_mxfp4, "fp8": oracle.index_scores_fp8}.get(
+        getattr(cfg, "index_format", "int8"), oracle.index_scores)
     s, e1 = score_fn(x["q_idx"], x["q_scale"], x["head_w"], x["idx_kv"], x["idx_scale"],
                      x["cmp_block_table"], x["query_start_loc"], x["positions"], T, cfg.ratio,
                      cfg.score_stride)
@@ -68,7 +68,29 @@ def bf16_to_f64(t) -> np.ndarray:
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def check_scores(g: np.ndarray, o: np.ndarray, what=""):
+def fp8_dot_tolerance(q_fp8, q_scale, head_w, idx_fp8, idx_scale, block_table,
+                      query_start_loc, positions, num_tokens, ratio, score_stride):
+    """Extra absolute score tolerance of the FP8 index plane (the INT8 plane's
+    dots are exact).  gfx950's block-scaled FP8 MFMA sums each group of eight
+    products in fixed point aligned to the group's largest product, keeping 13
+    bits below that product's leading bit and truncating the rest (measured
+    with single-MFMA probes: one 448 * 1 product beside seven products of
+    2^-5 .. 2^-4 keeps them to multiples of 2^-5; seven of 2^-6 or less
+    vanish).  A group's error is then below 8 * 2^-13 of its largest product,
+    so a head's dot is off by at most 2^-10 * sum_i |q_i k_i|, plus
+    Di * 2^-24 of it for the FP32 accumulation across groups.  Summed over
+    the heads with |w qs ks|, that is the factor times the score of the
+    absolute values, which the oracle computes on codes with their sign bits
+    cleared."""
+    Di = np.asarray(idx_fp8).shape[2]
+    b, _ = oracle.index_scores_fp8(np.asarray(q_fp8) & 0x7F, np.abs(q_scale), np.abs(head_w),
+                                   np.asarray(idx_fp8) & 0x7F, np.abs(idx_scale), block_table,
+                                   query_start_loc, positions, num_tokens, ratio, score_stride)
+    return np.where(np.isfinite(b), b * (2.0 ** -10 + Di * 2.0 ** -24), 0.0)
+
+
+def check_scores(g: np.ndarray, o: np.ndarray, what="", extra_tol=None):
+    """extra_tol: an absolute tolerance added per score (the FP8 plane's)."""
     assert g.shape == o.shape, (g.shape, o.shape)
     ninf_o = np.isneginf(o)
     assert np.array_equal(np.isneginf(g), ninf_o), f"{what}: -inf pattern differs"
@@ -80,14 +102,18 @@ def check_scores(g: np.ndarray, o: np.ndarray, what=""):
         scale = np.max(np.abs(o[t, f]))
         d = np.abs(g[t, f] - o[t, f])
         tol = 1e-5 * np.abs(o[t, f]) + 2e-6 * scale
+        if extra_tol is not None:
+            tol = tol + extra_tol[t, f]
         bad = d > tol
         assert not bad.any(), (f"{what} row {t}: {bad.sum()} scores off; worst "
                                f"{np.max(d / np.maximum(tol, 1e-30)):.3g}x tolerance")
 
 
 def check_topk(g_idx: np.ndarray, o_idx: np.ndarray, o_scores: np.ndarray, positions, ratio,
-               what=""):
-    """Exact, or differing only at oracle ties within 1e-5 relative of the k-th score."""
+               what="", extra_tol=None):
+    """Exact, or differing only at oracle ties within 1e-5 relative of the k-th
+    score (plus, with extra_tol, twice the larger score tolerance of the two
+    entries a swap exchanges)."""
     T, k = o_idx.shape
     assert g_idx.shape == o_idx.shape
     rows_equal = np.zeros(T, bool)
@@ -105,7 +131,10 @@ def check_topk(g_idx: np.ndarray, o_idx: np.ndarray, o_scores: np.ndarray, posit
             continue
         sk = np.min(o_scores[t, o[:m]])  # the oracle's m-th best score
         diff = np.setxor1d(gs, o[:m])
-        assert np.all(np.abs(o_scores[t, diff] - sk) <= 1e-5 * abs(sk)), (
+        tie = 1e-5 * abs(sk)
+        if extra_tol is not None:
+            tie = tie + 2.0 * np.max(extra_tol[t, np.concatenate([diff, o[:m]])])
+        assert np.all(np.abs(o_scores[t, diff] - sk) <= tie), (
             f"{what} row {t}: selection differs beyond ties ({len(diff)} entries)")
     return rows_equal
 

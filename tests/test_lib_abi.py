@@ -58,8 +58,9 @@ def test_rope_rows_host_checks(lib):
     assert f(None, None, 8, 4, None, 4, 0, None, None, None, None) == 0    # no work, no launch
 
 
-def test_index_score_host_checks(lib):
-    f = lib.csa_index_score
+@pytest.mark.parametrize("name", ["csa_index_score", "csa_index_score_fp8"])
+def test_index_score_host_checks(lib, name):
+    f = getattr(lib, name)
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, FAKE, FAKE, 1, 2, 2, 64, 128, 1, FAKE,
             256, None, None]
     bad = list(args); bad[15] = 0                     # ratio < 1
