@@ -11,7 +11,7 @@ forms, textbook special cases and brute force on tiny inputs.
 from .csa_oracle import (  # noqa: F401
     PAGE, EFLAG_POS_RANGE, EFLAG_BLOCK_RANGE, EFLAG_TOPK_RANGE, EFLAG_META,
     bf16_to_f64, visible_count, window_positions, owner_request,
-    rotate_adjacent_pairs, materialize_rope_rows, index_scores, topk,
+    rotate_adjacent_pairs, materialize_rope_rows, inverse_rope, index_scores, topk,
     kv_rows_for_query, deterministic_selection, sparse_attn,
     candidate_blocks, candidate_positions, index_scores_in_candidates, topk_in_candidates,
     decode_e2m1, decode_e8m0, mx_rows, index_scores_mxfp4,

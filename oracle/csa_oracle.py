@@ -119,6 +119,27 @@ def rotate_adjacent_pairs(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np
 # a1: RoPE rows
 # ----------------------------------------------------------------------------
 
+def inverse_rope(out, rope_cos, rope_sin, rope_offset, num_tokens):
+    """Inverse RoPE of the attention output ([ATOM] "DeepSeek-V4.1 native paged
+    runtime", introduction and "Current execution scope": the V4 attention is
+    followed by an inverse RoPE kernel; the pages do not define it).  Reading:
+    shared K = V rows carry their rope span rotated by their own positions, so
+    the output's rope span is a mix of rotated values; the inverse rotates
+    that span of every head of active row t back by row t's angles -- the
+    conjugate of its rope row, multiplication by e^{-i theta} in the pair
+    convention of ``rotate_adjacent_pairs``.  Channels outside
+    [rope_offset, rope_offset + 2 * half) are unchanged; rows >= num_tokens
+    are returned as given.  Returns float64 [T, H, D]."""
+    o = np.array(out, dtype=np.float64, copy=True)
+    c = np.asarray(rope_cos, dtype=np.float64)
+    s = np.asarray(rope_sin, dtype=np.float64)
+    half = c.shape[1]
+    for t in range(int(num_tokens)):
+        span = o[t, :, rope_offset:rope_offset + 2 * half]
+        o[t, :, rope_offset:rope_offset + 2 * half] = rotate_adjacent_pairs(span, c[t], -s[t])
+    return o
+
+
 def materialize_rope_rows(freqs_cos, freqs_sin, position_ids, num_tokens,
                           rope_cos, rope_sin) -> int:
     """[V41] "Serving-owned full RoPE tables": for each active row t < num_tokens
