@@ -56,6 +56,8 @@ _SIGS = {
 }
 _SIGS["csa_sparse_attn_prefill"] = _SIGS["csa_sparse_attn_decode"]
 _SIGS["csa_index_score_fp8"] = _SIGS["csa_index_score"]
+_SIGS["csa_inverse_rope"] = (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                            _P])
 _SIGS["csa_sparse_attn_mx_workspace_bytes"] = _SIGS["csa_sparse_attn_workspace_bytes"]
 # the decode arguments with a scale plane after each payload plane
 _SIGS["csa_sparse_attn_decode_mx"] = (
@@ -137,6 +139,20 @@ def csa_materialize_rope_rows(freqs_cos, freqs_sin, position_ids, num_tokens, ro
         _ptr(position_ids), position_ids.shape[0], int(num_tokens), _ptr(rope_cos),
         _ptr(rope_sin), _ptr(err), _stream(stream))
     _check(st, "csa_materialize_rope_rows")
+
+
+def csa_inverse_rope(inp, out, rope_cos, rope_sin, rope_offset, num_tokens, stream=None) -> None:
+    """out (BF16 [T, H, D], may be inp) = inp with the rope span of each
+    active row rotated by the conjugate of its rope row."""
+    _need(inp, _BF16, 3, "in")
+    _need(out, _BF16, 3, "out")
+    T, H, D = inp.shape
+    if tuple(out.shape) != (T, H, D):
+        raise CsaError(f"out {tuple(out.shape)} does not match in {tuple(inp.shape)}")
+    st = load().csa_inverse_rope(_ptr(inp), _ptr(out), _ptr(rope_cos), _ptr(rope_sin),
+                                 2 * rope_cos.shape[1], int(rope_offset), T, int(num_tokens), H,
+                                 D, _stream(stream))
+    _check(st, "csa_inverse_rope")
 
 
 def csa_index_score(q_idx, q_scale, head_w, idx_kv, idx_scale, block_table, query_start_loc,

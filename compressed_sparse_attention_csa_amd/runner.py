@@ -170,6 +170,17 @@ class CsaStep:
             return ("rope", "index", "topk", "attn")
         return ("rope", "attn")
 
+    def inv_rope(self, stream=None, out=None):
+        """The output's rope span rotated back by each row's angles (into
+        `out`, by default a buffer of the step's own, leaving self.out as the
+        attention result)."""
+        if out is None:
+            if getattr(self, "out_inv", None) is None:
+                self.out_inv = torch.empty_like(self.out)
+            out = self.out_inv
+        _lib.csa_inverse_rope(self.out, out, self.rope_cos, self.rope_sin, self.rope_offset,
+                              self.num_tokens, stream=stream)
+
     def cand(self, stream=None):
         """The candidate mask the full layer publishes (mode hier_full)."""
         _lib.csa_candidate_blocks(self.scores, self.t["positions"], self.ratio,

@@ -16,6 +16,8 @@
  *                                    with one sink logit per head
  *      (csa_sparse_attn_decode_mx: the same over the MXFP8 window and MXFP4
  *      compressed KV planes)
+ *   5. csa_inverse_rope           -- the output's rope span rotated back by the
+ *                                    query row's angles
  *
  * Pages the contracts follow (cited by title and section):
  *   [V41]  pypto-lib "DeepSeek V4.1 Flash": "Serving-owned full RoPE tables",
@@ -108,6 +110,30 @@ int csa_materialize_rope_rows(const float* freqs_cos, const float* freqs_sin,
                               const int32_t* position_ids, int32_t T, int32_t num_tokens,
                               float* rope_cos, float* rope_sin, int32_t* err, void* stream);
 
+/*
+ * csa_inverse_rope -- inverse RoPE of the attention output ([ATOM]
+ * "DeepSeek-V4.1 native paged runtime", introduction and "Current execution
+ * scope": the V4 attention is followed by an inverse RoPE kernel, which the
+ * pages name but do not define).  Reading: K = V rows carry their rope span
+ * rotated by their own positions, so the output's rope span mixes rotated
+ * values; this call rotates that span back by the query row's angles.  For
+ * every head of active row t and pair i of channels
+ * (rope_offset + 2i, rope_offset + 2i + 1):
+ *     (x, y) -> (x c + y s, y c - x s),  c = rope_cos[t][i], s = rope_sin[t][i]
+ * (multiplication by the conjugate of the rope row), in FP32, rounded to
+ * nearest even BF16; the other channels are copied.
+ *
+ *   in, out            BF16 [T, H, D]; out may equal in (in place)
+ *   rope_cos/sin       FP32 [T, rope_dim / 2]: the rows the query was rotated
+ *                      with (csa_materialize_rope_rows)
+ *
+ * Rows t >= num_tokens of out are not written.  Supported: D a multiple of 4,
+ * rope_dim and rope_offset even, rope_offset + rope_dim <= D, in and out
+ * 8-byte aligned.
+ */
+int csa_inverse_rope(const uint16_t* in, uint16_t* out, const float* rope_cos,
+                     const float* rope_sin, int32_t rope_dim, int32_t rope_offset, int32_t T,
+                     int32_t num_tokens, int32_t H, int32_t D, void* stream);
 /*
  * csa_index_score -- lightning-indexer scores ([HP] 10.2 / 10.3; [MTP] INT8
  * index keys with an FP32 per-row scale; per-row bounds as in [ATOM]).

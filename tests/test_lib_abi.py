@@ -270,3 +270,22 @@ def test_mx_decode_host_checks(lib):
     assert f(*bad) == -3
     bad = list(base); bad[25] = 0                  # no active rows: nothing to do
     assert f(*bad) == 0
+
+
+def test_inverse_rope_host_checks(lib):
+    f = lib.csa_inverse_rope
+    base = [FAKE, FAKE, FAKE, FAKE, 64, 448, 8, 8, 64, 512, None]
+    bad = list(base); bad[5] = 449                 # odd rope offset
+    assert f(*bad) == -4
+    bad = list(base); bad[5] = 456                 # rope span past D
+    assert f(*bad) == -4
+    bad = list(base); bad[9] = 510                 # D not a multiple of 4
+    assert f(*bad) == -4
+    bad = list(base); bad[7] = 9                   # num_tokens > T
+    assert f(*bad) == -3
+    bad = list(base); bad[2] = None                # rope rows NULL
+    assert f(*bad) == -1
+    bad = list(base); bad[1] = ctypes.c_void_p(0x1004)   # out not 8-byte aligned
+    assert f(*bad) == -4
+    bad = list(base); bad[7] = 0                   # nothing to do
+    assert f(*bad) == 0
