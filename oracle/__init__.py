@@ -16,4 +16,5 @@ from .csa_oracle import (  # noqa: F401
     candidate_blocks, candidate_positions, index_scores_in_candidates, topk_in_candidates,
     decode_e2m1, decode_e8m0, mx_rows, index_scores_mxfp4,
     decode_e4m3, KvPlane, bf16_plane, mxfp8_plane, mxfp4_e4m3_plane, index_scores_fp8,
+    f64_to_bf16, compress_pairs,
 )

@@ -68,6 +68,16 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def f64_to_bf16(x) -> np.ndarray:
+    """BF16 bit patterns of float64 values, rounded to nearest even in one
+    step from the float64 value (8 significant bits kept).  Finite values in
+    BF16's normal range only."""
+    b = np.asarray(x, dtype=np.float64).view(np.uint64)
+    lsb = (b >> np.uint64(45)) & np.uint64(1)
+    r = (b + np.uint64(0x0FFFFFFFFFFF) + lsb) & ~np.uint64((1 << 45) - 1)
+    return (r.view(np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def visible_count(pos: int, ratio: int) -> int:
     """Compressed slots a query at absolute position ``pos`` may see.
 
@@ -288,6 +298,104 @@ def index_scores_fp8(q_fp8, q_scale, head_w, idx_fp8, idx_scale, block_table,
             s[~ok] = -np.inf
             scores[t, cs] = s
     return scores, err
+
+
+# ----------------------------------------------------------------------------
+# the step before the path: ratio-2 compressor publication
+# ----------------------------------------------------------------------------
+
+def compress_pairs(kv_proj, gate, query_start_loc, positions, num_tokens, state_block_table,
+                   state_cache, rms_gamma, rms_eps, rope_cos, rope_sin, rope_offset, cmp_kv,
+                   cmp_block_table):
+    """Ratio-2 compressor publication with its FP32 state ring ([V41]
+    "Compressor state ownership" and the paragraph on the production cache
+    ABI: the state ring [num_state_blocks, CAP, 2D] holds each token's KV
+    projection then its gate score; a valid token at position p lives in slot
+    block * CAP + p % CAP with block = state_block_table[b]; an odd position
+    closes a pair; the first token of a chunk reads its predecessor from the
+    ring, later ones take the preceding input row; every ring read comes
+    before every ring write; only the last min(chunk, CAP) rows of a chunk are
+    written; negative positions neither publish nor write; block -1 disables
+    the request's compressor; one compressed row covers two tokens).
+
+    Readings (the pages name the pooling softmax, the BF16 rounding before
+    RMSNorm and group-start RoPE rows without formulas): for a pair (p - 1, p)
+    with projections kv_j and gate scores g_j,
+        pooled[c] = sum_j e^{g_j[c]} kv_j[c] / sum_j e^{g_j[c]}     (per channel)
+        x = bf16(pooled);  y = x / sqrt(mean(x^2) + eps) * gamma
+        y[off:off+R] rotated by the rope row of the pair's start p - 1
+    (rope_cos / rope_sin row t holds that row for token t), and bf16(y) is
+    published at compressed position p // 2 of the request's BF16 pool.
+
+    Flags: a state block or publication page outside its pool -> BLOCK_RANGE
+    (the access is skipped); a row no request owns -> META.
+    Returns (cmp_kv after, state_cache after, err); the inputs are not changed."""
+    qsl = np.asarray(query_start_loc)
+    pos = np.asarray(positions)
+    kv = np.asarray(kv_proj, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    state_in = np.asarray(state_cache, dtype=np.float32)
+    state = state_in.copy()
+    cmp_out = np.array(cmp_kv, copy=True)
+    nsb, cap, two_d = state_in.shape
+    D = two_d // 2
+    nb = cmp_out.shape[0]
+    gamma = np.asarray(rms_gamma, dtype=np.float64)
+    c = np.asarray(rope_cos, dtype=np.float64)
+    sn = np.asarray(rope_sin, dtype=np.float64)
+    half = c.shape[1]
+    err = 0
+    nt = int(num_tokens)
+    writes = []   # (slot index tuple, row) applied after every read
+    for t in range(nt):
+        if owner_request(t, qsl) < 0:
+            err |= EFLAG_META
+    for b in range(len(qsl) - 1):
+        lo, hi = min(int(qsl[b]), nt), min(int(qsl[b + 1]), nt)
+        if hi <= lo:
+            continue
+        blk = int(state_block_table[b])
+        if blk < 0:
+            continue                                   # compressor disabled
+        blk_ok = blk < nsb
+        if not blk_ok:
+            err |= EFLAG_BLOCK_RANGE
+        for t in range(lo, hi):
+            p = int(pos[t])
+            if p < 0 or p % 2 == 0:
+                continue
+            if t > lo:
+                prev_kv, prev_g = kv[t - 1], g[t - 1]
+            elif blk_ok:
+                row = state_in[blk, (p - 1) % cap].astype(np.float64)
+                prev_kv, prev_g = row[:D], row[D:]
+            else:
+                continue
+            gg = np.stack([prev_g, g[t]])
+            w = np.exp(gg - gg.max(axis=0))
+            w = w / w.sum(axis=0)
+            pooled = w[0] * prev_kv + w[1] * kv[t]
+            x = bf16_to_f64(f64_to_bf16(pooled))
+            y = x / np.sqrt(np.mean(x * x) + float(rms_eps)) * gamma
+            if half:
+                y[rope_offset:rope_offset + 2 * half] = rotate_adjacent_pairs(
+                    y[rope_offset:rope_offset + 2 * half], c[t], sn[t])
+            rows, ok = _physical_rows(cmp_block_table[b], nb, np.array([p // 2]))
+            if not ok[0]:
+                err |= EFLAG_BLOCK_RANGE
+                continue
+            r = int(rows[0])
+            cmp_out[r // PAGE, r % PAGE] = f64_to_bf16(y)
+        if not blk_ok:
+            continue
+        for t in range(max(lo, hi - cap), hi):
+            p = int(pos[t])
+            if p < 0:
+                continue
+            writes.append(((blk, p % cap), np.concatenate([kv[t], g[t]]).astype(np.float32)))
+    for (bi, si), row in writes:
+        state[bi, si] = row
+    return cmp_out, state, err
 
 
 # ----------------------------------------------------------------------------
