@@ -56,6 +56,9 @@ _SIGS = {
 }
 _SIGS["csa_sparse_attn_prefill"] = _SIGS["csa_sparse_attn_decode"]
 _SIGS["csa_index_score_fp8"] = _SIGS["csa_index_score"]
+_SIGS["csa_compress_pairs"] = (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P,
+                                              _I32, _I32, _P, _F32, _P, _P, _I32, _I32, _P, _I32,
+                                              _P, _I32, _P, _P])
 _SIGS["csa_inverse_rope"] = (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                             _P])
 _SIGS["csa_sparse_attn_mx_workspace_bytes"] = _SIGS["csa_sparse_attn_workspace_bytes"]
@@ -139,6 +142,28 @@ def csa_materialize_rope_rows(freqs_cos, freqs_sin, position_ids, num_tokens, ro
         _ptr(position_ids), position_ids.shape[0], int(num_tokens), _ptr(rope_cos),
         _ptr(rope_sin), _ptr(err), _stream(stream))
     _check(st, "csa_materialize_rope_rows")
+
+
+def csa_compress_pairs(kv_proj, gate, query_start_loc, positions, num_tokens, state_block_table,
+                       state_cache, rms_gamma, rms_eps, rope_cos, rope_sin, rope_offset, cmp_kv,
+                       cmp_block_table, err=None, stream=None) -> None:
+    """Ratio-2 compressor publication into cmp_kv (BF16 [blocks, 128, D]) and
+    the FP32 state ring state_cache [blocks, capacity, 2 D] (both in place)."""
+    _need(kv_proj, (torch.float32,), 2, "kv_proj")
+    _need(gate, (torch.float32,), 2, "gate")
+    _need(state_cache, (torch.float32,), 3, "state_cache")
+    _need(cmp_kv, _BF16, 3, "cmp_kv")
+    T, D = kv_proj.shape
+    if tuple(gate.shape) != (T, D) or state_cache.shape[2] != 2 * D or cmp_kv.shape[2] != D:
+        raise CsaError("kv_proj, gate, state_cache and cmp_kv disagree on D")
+    st = load().csa_compress_pairs(
+        _ptr(kv_proj), _ptr(gate), D, _ptr(query_start_loc), _ptr(positions),
+        query_start_loc.shape[0] - 1, T, int(num_tokens), _ptr(state_block_table),
+        _ptr(state_cache), state_cache.shape[0], state_cache.shape[1], _ptr(rms_gamma),
+        float(rms_eps), _ptr(rope_cos), _ptr(rope_sin), 2 * rope_cos.shape[1], int(rope_offset),
+        _ptr(cmp_kv), cmp_kv.shape[0], _ptr(cmp_block_table), cmp_block_table.shape[1],
+        _ptr(err), _stream(stream))
+    _check(st, "csa_compress_pairs")
 
 
 def csa_inverse_rope(inp, out, rope_cos, rope_sin, rope_offset, num_tokens, stream=None) -> None:

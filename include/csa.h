@@ -18,6 +18,8 @@
  *      compressed KV planes)
  *   5. csa_inverse_rope           -- the output's rope span rotated back by the
  *                                    query row's angles
+ * and the step before the path: csa_compress_pairs publishes ratio-2
+ * compressed rows from the projections and its FP32 state ring.
  *
  * Pages the contracts follow (cited by title and section):
  *   [V41]  pypto-lib "DeepSeek V4.1 Flash": "Serving-owned full RoPE tables",
@@ -420,6 +422,55 @@ int csa_index_score_fp8(const uint8_t* q_fp8, const float* q_scale, const float*
                         const int32_t* query_start_loc, const int32_t* positions, int32_t B,
                         int32_t T, int32_t num_tokens, int32_t Hi, int32_t Di, int32_t ratio,
                         float* scores, int64_t score_stride, int32_t* err, void* stream);
+
+/*
+ * csa_compress_pairs -- the ratio-2 compressor's publication and its FP32
+ * state ring, the step before the path ([V41] "Compressor state ownership";
+ * the cache ABI paragraph: a ring row is the token's KV projection followed by
+ * its gate score).  For request b (rows query_start_loc[b] .. [b+1] of the
+ * active prefix, consecutive positions) with state block
+ * blk = state_block_table[b]:
+ *   - a token at odd position p closes the pair (p - 1, p) and publishes
+ *     compressed position p / 2 of request b; its predecessor is the
+ *     preceding input row, or for the chunk's first row the ring row
+ *     blk * state_capacity + (p - 1) % state_capacity;
+ *   - publication: per channel, the softmax of the pair's gate scores weights
+ *     its KV projections; the result is rounded to BF16, normalised
+ *     (x * rsqrt(mean(x^2) + rms_eps) * rms_gamma), its rope span
+ *     [rope_offset, rope_offset + rope_dim) rotated in adjacent pairs by the
+ *     rope row given for the token (the pair's start position: the pages'
+ *     group-start RoPE rows), and stored rounded to nearest even BF16 in the
+ *     compressed pool through cmp_block_table (128-row pages);
+ *   - after every ring read of the call, the last min(chunk, state_capacity)
+ *     rows of each chunk are stored at slot blk * state_capacity + p %
+ *     state_capacity ([kv_proj row | gate row], FP32).
+ * The pooling, rounding, normalisation and rope steps are named but not
+ * defined on the pages; the above is the plain reading.
+ *
+ *   kv_proj, gate      FP32 [T, D]
+ *   state_block_table  INT32 [B]: -1 disables the request (no access at all)
+ *   state_cache        FP32 [num_state_blocks, state_capacity, 2 * D], in/out
+ *   rms_gamma          FP32 [D]; rms_eps >= 0
+ *   rope_cos/sin       FP32 [T, rope_dim / 2]
+ *   cmp_kv             BF16 [num_cmp_blocks, 128, D], written at published rows
+ *   cmp_block_table    INT32 [B, max_cmp_blocks]
+ *
+ * Negative positions neither publish nor write.  A state block >= the pool
+ * size or a publication page past the table or naming an invalid block sets
+ * CSA_EFLAG_BLOCK_RANGE and that access is skipped; an active row no request
+ * owns sets CSA_EFLAG_META.  Supported: D even and <= 2048, rope_dim and
+ * rope_offset even, rope_offset + rope_dim <= D, state_capacity >= 1, the FP32
+ * arrays and cmp_kv 8-byte aligned.  Two kernel launches on `stream`.
+ */
+int csa_compress_pairs(const float* kv_proj, const float* gate, int32_t D,
+                       const int32_t* query_start_loc, const int32_t* positions, int32_t B,
+                       int32_t T, int32_t num_tokens, const int32_t* state_block_table,
+                       float* state_cache, int32_t num_state_blocks, int32_t state_capacity,
+                       const float* rms_gamma, float rms_eps, const float* rope_cos,
+                       const float* rope_sin, int32_t rope_dim, int32_t rope_offset,
+                       uint16_t* cmp_kv, int32_t num_cmp_blocks,
+                       const int32_t* cmp_block_table, int32_t max_cmp_blocks, int32_t* err,
+                       void* stream);
 
 /*
  * Hierarchical selection ([V41] "Decode composition"): a full layer publishes

@@ -289,3 +289,29 @@ def test_inverse_rope_host_checks(lib):
     assert f(*bad) == -4
     bad = list(base); bad[7] = 0                   # nothing to do
     assert f(*bad) == 0
+
+
+def test_compress_pairs_host_checks(lib):
+    f = lib.csa_compress_pairs
+    #       kv    gate  D    qsl   pos   B  T  nt  sbt   state nsb cap gamma eps
+    base = [FAKE, FAKE, 512, FAKE, FAKE, 2, 8, 8, FAKE, FAKE, 4, 4, FAKE, 1e-6,
+            #  cos   sin   R   off  cmp   ncb bt    mcb err   stream
+            FAKE, FAKE, 64, 448, FAKE, 8, FAKE, 4, None, None]
+    bad = list(base); bad[11] = 0                  # ring capacity 0
+    assert f(*bad) == -3
+    bad = list(base); bad[2] = 511                 # odd D
+    assert f(*bad) == -4
+    bad = list(base); bad[2] = 4096                # D past what a work-group holds
+    assert f(*bad) == -4
+    bad = list(base); bad[17] = 450                # rope span past D
+    assert f(*bad) == -4
+    bad = list(base); bad[13] = -1.0               # negative eps
+    assert f(*bad) == -4
+    bad = list(base); bad[8] = None                # state block table NULL
+    assert f(*bad) == -1
+    bad = list(base); bad[0] = ctypes.c_void_p(0x1004)   # kv_proj not 8-byte aligned
+    assert f(*bad) == -4
+    bad = list(base); bad[7] = 9                   # num_tokens > T
+    assert f(*bad) == -3
+    bad = list(base); bad[7] = 0                   # nothing to do
+    assert f(*bad) == 0
