@@ -40,7 +40,7 @@ INT8_PEAK_TOPS = 5000.0        # dense INT8 MFMA
 
 KERNEL_SOURCES = {
     "rope": "csa_rope.hip", "index": "csa_index.hip", "topk": "csa_topk.hip",
-    "attn": "csa_attn.hip", "cand": "csa_topk.hip",
+    "attn": "csa_attn.hip", "cand": "csa_topk.hip", "compress_pairs": "csa_compress.hip",
 }
 
 
@@ -84,12 +84,39 @@ def visible(p, ratio):
     return max(0, (int(p) + 1) // ratio)
 
 
+def compress_bytes(cfg, x):
+    """The compressor's bytes: every token's FP32 KV projection and gate row
+    once, each published BF16 row, the ring rows it reads (a chunk's odd first
+    row) and writes (the chunk's last min(chunk, CAP) rows), the RMSNorm
+    weights and each publishing row's rope row."""
+    D, R, cap = cfg.D, cfg.R, cfg.state_capacity
+    qsl = np.asarray(x["query_start_loc"])
+    pos = np.asarray(x["positions"])
+    pub = ring_rd = ring_wr = 0
+    for b in range(len(qsl) - 1):
+        lo, hi = int(qsl[b]), int(qsl[b + 1])
+        if hi <= lo:
+            continue
+        pub += int(sum(1 for t in range(lo, hi) if pos[t] >= 0 and pos[t] % 2 == 1))
+        ring_rd += int(pos[lo] >= 0 and pos[lo] % 2 == 1)
+        ring_wr += int(sum(1 for t in range(max(lo, hi - cap), hi) if pos[t] >= 0))
+    T = len(pos)
+    return (8 * T * D + 2 * D * pub + 8 * D * (ring_rd + ring_wr) + 4 * D + 4 * R * pub
+            + 4 * T)
+
+
 def work_model(cfg, x, topk_idx: np.ndarray):
     """Bytes each stage must move once, and the step total (decode formula:
     index keys of every visible position once per request, every unique
-    gathered KV row once per request, Q, O, lse and small metadata)."""
+    gathered KV row once per request, Q, O, lse and small metadata; with the
+    compressor, its bytes on top)."""
     T, H, D, R, Hi, Di, k = cfg.T, cfg.H, cfg.D, cfg.R, cfg.Hi, cfg.Di, cfg.k
     mode = getattr(cfg, "mode", "csa")
+    if mode == "compress":   # the publication alone: rope rows of the pair starts, then it
+        cb = compress_bytes(cfg, x)
+        st = {"rope": 8 * T * R + 4 * T, "compress_pairs": cb}
+        return dict(stage_bytes=st, step_bytes=cb, flops={}, kv_rows=0, kv_bytes=0,
+                    idx_keys=0, pairs=0)
     qsl = np.asarray(x["query_start_loc"])
     pos = np.asarray(x["positions"])
     nv = np.array([visible(p, cfg.ratio) for p in pos])
@@ -156,6 +183,10 @@ def work_model(cfg, x, topk_idx: np.ndarray):
         st = {"rope": st["rope"], "attn": st["attn"]}
     step = (idx_keys * kbytes + kv_bytes + 4 * T * H * D + 4 * T * H + q_side
             + 2 * sel_bytes + 4 * T * R + mask_bytes)
+    if getattr(cfg, "compress", False):
+        st["rope"] += 8 * T * R + 4 * T      # the pair starts' rope rows, same launch
+        st["compress_pairs"] = compress_bytes(cfg, x)
+        step += st["compress_pairs"]
     flops = {"attn": pairs * H * D * 4,
              "index": int(sum(nv[t] for t in range(T))) * Hi * Di * 2}
     return dict(stage_bytes=st, step_bytes=step, flops=flops, kv_rows=kv_rows,
@@ -210,13 +241,42 @@ def cpu_baseline(cfg, x, budget_s: float):
     cores = min(blas_threads, len(os.sched_getaffinity(0)))
     T = cfg.T
     mode = getattr(cfg, "mode", "csa")
+    compress = getattr(cfg, "compress", False)
+
+    def oracle_compress(sub, n, cmp_kv):
+        rc = np.zeros((n, cfg.R // 2), np.float32)
+        rs = np.zeros_like(rc)
+        oracle.materialize_rope_rows(sub["freqs_cos"], sub["freqs_sin"], sub["cmp_position_ids"],
+                                     n, rc, rs)
+        return oracle.compress_pairs(sub["kv_proj"], sub["gate"], sub["query_start_loc"],
+                                     sub["positions"], n, sub["state_block_table"],
+                                     sub["state_cache"], sub["rms_gamma"], cfg.rms_eps, rc, rs,
+                                     cfg.rope_offset, cmp_kv, sub["cmp_block_table"])[0]
+
+    if mode == "compress":
+        # sample: the whole chunk, repeated until the budget is spent
+        done, t0 = 0, time.perf_counter()
+        while True:
+            oracle_compress(x, T, x["cmp_kv"])
+            done += T
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        el = time.perf_counter() - t0
+        return {"value": done / el, "unit": "rows/s", "cores": int(cores), "kind": "oracle",
+                "cpu_model": cpu_model(),
+                "sample": f"{done // T} x the whole {T}-token chunk (rope rows of the pair "
+                          f"starts and the compressor, float64 NumPy) in {el:.1f} s"}
     # sample: whole rows of the workload; all of them when they fit the budget
     rows_per_call = T if T <= 16 else 16
+    if compress and rows_per_call != T:
+        raise ValueError("the compressor's baseline samples whole chunks")
     done_rows = 0
     t0 = time.perf_counter()
     stage = dict(rope=0.0, index=0.0, topk=0.0, attn=0.0)
     if mode == "hier_full":
         stage["cand"] = 0.0
+    if compress:
+        stage["compress_pairs"] = 0.0
     rng = np.random.default_rng(0)
     while True:
         rows = np.arange(T) if rows_per_call == T else np.sort(rng.choice(T, rows_per_call, False))
@@ -229,6 +289,10 @@ def cpu_baseline(cfg, x, budget_s: float):
             if key in x:
                 sub[key] = np.ascontiguousarray(np.asarray(x[key])[rows])
         n = len(rows)
+        if compress:   # the publication first (whole chunks: rows_per_call == T)
+            z = time.perf_counter()
+            sub["cmp_kv"] = oracle_compress(sub, n, x["cmp_kv"])
+            stage["compress_pairs"] += time.perf_counter() - z
         a = time.perf_counter()
         cand_before = stage.get("cand", 0.0)
         rc = np.zeros((n, cfg.R // 2), np.float32)
@@ -299,7 +363,7 @@ def cpu_baseline(cfg, x, budget_s: float):
                       f"float64 NumPy) in {el:.1f} s",
             "stage_seconds": {k: round(v, 3) for k, v in stage.items()
                               if mode in ("csa", "reindex", "hier_full")
-                              or k in ("rope", "attn")}}
+                              or k in ("rope", "attn", "compress_pairs")}}
 
 
 # ---------------------------------------------------------------------------
@@ -327,6 +391,8 @@ def main():
     per_copy_touch = (idx_touch * cfg.index_key_bytes +
                       cfg.T * (cfg.k * cfg.kv_row_bytes[1] + cfg.W * cfg.kv_row_bytes[0]) +
                       4 * cfg.T * cfg.H * cfg.D)
+    if cfg.mode == "compress":
+        per_copy_touch = 9 * cfg.T * cfg.D
     if args.warm:
         copies = 1
     elif args.copies > 0:
@@ -383,7 +449,7 @@ def main():
         torch.cuda.synchronize()
         stage_ms[s] = e0.elapsed_time(e1) / (n_rep * reps)
     errs = [int(s.err.item()) for s in steps]
-    topk_host = first.topk_idx.cpu().numpy()
+    topk_host = first.topk_idx.cpu().numpy() if cfg.mode != "compress" else None
 
     wm = work_model(cfg, x, topk_host)
     rows = cfg.T
@@ -409,6 +475,7 @@ def main():
                  "topk": ("topk_sample_kernel + topk_filter_kernel + topk_final_kernel" if long_rows
                           else "topk_small_kernel"),
                  "cand": "block_max_kernel + top-k of the block scores",
+                 "compress_pairs": "compress_pairs_kernel",
                  "attn": ("attn_kernel + attn_merge_kernel" if split_ring
                           else ("attn_decode_kernel (low-bit KV) + attn_merge_kernel"
                                 if cfg.kv_format == "mx"
@@ -424,7 +491,8 @@ def main():
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": {"mxfp4": "mxfp4+bf16", "fp8": "fp8+bf16"}.get(cfg.index_format, "int8+bf16"),
+        "dtype": ("fp32+bf16" if cfg.mode == "compress" else
+                  {"mxfp4": "mxfp4+bf16", "fp8": "fp8+bf16"}.get(cfg.index_format, "int8+bf16")),
         "data": "synthetic",
         "config": {"workload": cfg.name, "rows": cfg.T, "requests": cfg.B, "heads": cfg.H,
                    "head_dim": cfg.D, "ratio": cfg.ratio, "top_k": cfg.k, "window": cfg.W,
@@ -434,7 +502,10 @@ def main():
                    "indexer": ((f"{cfg.Hi}x{cfg.Di}" +
                                 " " + cfg.index_format)
                                if first.mode in ("csa", "reindex", "hier_full") else "none"),
+                   "compressor": ("ratio-2 publication, FP32 state ring of "
+                                  f"{cfg.state_capacity}" if cfg.compress else "none"),
                    "selection": {"csa": "indexer top-k", "hca": "every visible compressed row",
+                                 "compress": "none (the compressor alone)",
                                  "swa": "window only",
                                  "reindex": f"indexer top-k inside {cfg.cand_kb} candidate blocks "
                                             f"of {cfg.cand_block}",

@@ -11,15 +11,16 @@
 //   x = bf16(pooled), y = x * rsqrt(mean(x^2) + eps) * gamma, the rope span
 //   of y rotated by the pair's start row, bf16(y) published at p / 2.
 //
-// Two launches on the stream: the publication kernel reads the ring, the
-// state kernel then writes it, so every read precedes every write.
+// One launch: only a request's first row reads the ring, and its wave writes
+// the request's ring rows after that read.  Requests must not share a state
+// block.
 #include "csa_common.h"
 
 namespace csa {
 
 namespace {
 
-constexpr int kCmpThreads = 256;
+constexpr int kCmpLanes = 64;   // one wave per token
 
 struct CompressArgs {
   const float* kv;      // [T][D]
@@ -46,118 +47,133 @@ struct CompressArgs {
   int32_t* err;
 };
 
-// One work-group per token; the tokens at odd positions publish.  Thread i
-// owns channel pairs (2i + 2 * kCmpThreads * m, + 1), so a rope pair is
-// always one thread's.
-__global__ void __launch_bounds__(kCmpThreads) compress_publish_kernel(CompressArgs a) {
-  __shared__ float red_s[kCmpThreads / 64];
+// One wave per token; the tokens at odd positions publish.  Lane l owns the
+// channel pairs (2l + 128 m, + 1), m < NCH, so a rope pair is always one
+// lane's.  The row loads (this row, the input row before it, the RMSNorm
+// weights and the rope row) are issued before the request lookup; a chunk's
+// first row replaces the predecessor by its ring slot.  Only that first row
+// reads the ring, and its wave writes every ring row of the request after
+// the read (each lane rewrites the channels it read), so every read precedes
+// every write within one launch.
+template <int NCH>
+__global__ void __launch_bounds__(kCmpLanes) compress_pairs_kernel(CompressArgs a) {
   const int t = blockIdx.x;
   if (t >= a.num_tokens) return;
-  const int tid = threadIdx.x;
-  const int b = owner_request_wave(a.qsl, a.B, t);
+  const int lane = threadIdx.x;
+  const int D = a.D;
+  const int qv = qsl_lane_load(a.qsl, a.B);
+  const int p = a.pos[t];
+  const bool odd = p >= 0 && (p & 1) == 1;
+  float2 k0[NCH], g0[NCH], k1[NCH], g1[NCH], gm[NCH], rot[NCH];
+  uint32_t in_rope = 0;           // bit m: chunk m's pair lies in the rope span
+  if (odd) {
+    const float* ck = a.kv + static_cast<long long>(t) * D;
+    const float* cg = a.gate + static_cast<long long>(t) * D;
+    const long long prev = static_cast<long long>(t > 0 ? t - 1 : 0) * D;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = 2 * lane + 2 * kCmpLanes * m;
+      k0[m] = g0[m] = k1[m] = g1[m] = gm[m] = make_float2(0.0f, 0.0f);
+      rot[m] = make_float2(0.0f, 0.0f);
+      if (c < D) {
+        k1[m] = *reinterpret_cast<const float2*>(ck + c);
+        g1[m] = *reinterpret_cast<const float2*>(cg + c);
+        k0[m] = *reinterpret_cast<const float2*>(a.kv + prev + c);
+        g0[m] = *reinterpret_cast<const float2*>(a.gate + prev + c);
+        gm[m] = *reinterpret_cast<const float2*>(a.gamma + c);
+        const int rr = c - a.rope_offset;
+        if (rr >= 0 && rr < 2 * a.half) {
+          const long long ri = static_cast<long long>(t) * a.half + (rr >> 1);
+          rot[m] = make_float2(a.rcos[ri], a.rsin[ri]);
+          in_rope |= 1u << m;
+        }
+      }
+    }
+  }
+  const int b = owner_from_lanes(qv, a.qsl, a.B, t);
   if (b < 0) {
-    if (tid == 0) flag_error(a.err, CSA_EFLAG_META);
+    if (lane == 0) flag_error(a.err, CSA_EFLAG_META);
     return;
   }
-  const int p = a.pos[t];
   const int blk = a.sbt[b];
   if (blk < 0) return;            // compressor disabled for the request
   // a state block outside the pool skips only the ring accesses
   const bool ring_ok = blk < a.nsb;
-  if (!ring_ok && tid == 0) flag_error(a.err, CSA_EFLAG_BLOCK_RANGE);
-  if (p < 0 || (p & 1) == 0) return;   // no publication; an even position opens a pair
+  if (!ring_ok && lane == 0) flag_error(a.err, CSA_EFLAG_BLOCK_RANGE);
   const int lo = min(max(a.qsl[b], 0), a.num_tokens);
-  // predecessor: the preceding input row inside the chunk, else the ring
-  const float* pk;
-  const float* pg;
-  if (t > lo) {
-    pk = a.kv + static_cast<long long>(t - 1) * a.D;
-    pg = a.gate + static_cast<long long>(t - 1) * a.D;
-  } else {
-    if (!ring_ok) return;
-    pk = a.state + (static_cast<long long>(blk) * a.cap + (p - 1) % a.cap) * 2 * a.D;
-    pg = pk + a.D;
+  const int hi = min(max(a.qsl[b + 1], 0), a.num_tokens);
+  // an odd position closes a pair; its predecessor is the preceding input
+  // row inside the chunk, else the ring
+  bool publish = odd && (t > lo || ring_ok);
+  long long crow = -1;
+  if (publish) {
+    crow = page_row(a.cbt + static_cast<long long>(b) * a.max_cb, a.max_cb, a.ncb, p >> 1);
+    if (crow < 0) {
+      if (lane == 0) flag_error(a.err, CSA_EFLAG_BLOCK_RANGE);
+      publish = false;
+    }
   }
-  const float* ck = a.kv + static_cast<long long>(t) * a.D;
-  const float* cg = a.gate + static_cast<long long>(t) * a.D;
-  // the publication row (checked before anything is computed)
-  const int cp = p >> 1;
-  const long long crow = page_row(a.cbt + static_cast<long long>(b) * a.max_cb, a.max_cb, a.ncb, cp);
-  if (crow < 0) {
-    if (tid == 0) flag_error(a.err, CSA_EFLAG_BLOCK_RANGE);
-    return;
-  }
-  constexpr int kMaxPairs = 4;    // D <= 2 * kCmpThreads * kMaxPairs
-  float x[kMaxPairs][2];
-  float ss = 0.0f;
+  if (publish) {
+    if (t == lo) {
+      const float* pk = a.state + (static_cast<long long>(blk) * a.cap + (p - 1) % a.cap) * 2 * D;
 #pragma unroll
-  for (int m = 0; m < kMaxPairs; ++m) {
-    const int c = 2 * tid + 2 * kCmpThreads * m;
-    x[m][0] = x[m][1] = 0.0f;
-    if (c < a.D) {
-      const float2 k0 = *reinterpret_cast<const float2*>(pk + c);
-      const float2 g0 = *reinterpret_cast<const float2*>(pg + c);
-      const float2 k1 = *reinterpret_cast<const float2*>(ck + c);
-      const float2 g1 = *reinterpret_cast<const float2*>(cg + c);
-      const float kk0[2] = {k0.x, k0.y}, gg0[2] = {g0.x, g0.y};
-      const float kk1[2] = {k1.x, k1.y}, gg1[2] = {g1.x, g1.y};
+      for (int m = 0; m < NCH; ++m) {
+        const int c = 2 * lane + 2 * kCmpLanes * m;
+        if (c < D) {
+          k0[m] = *reinterpret_cast<const float2*>(pk + c);
+          g0[m] = *reinterpret_cast<const float2*>(pk + D + c);
+        }
+      }
+    }
+    float x[NCH][2];
+    float ss = 0.0f;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const float kk0[2] = {k0[m].x, k0[m].y}, gg0[2] = {g0[m].x, g0[m].y};
+      const float kk1[2] = {k1[m].x, k1[m].y}, gg1[2] = {g1[m].x, g1[m].y};
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float mg = fmaxf(gg0[e], gg1[e]);
         const float w0 = expf(gg0[e] - mg), w1 = expf(gg1[e] - mg);
         const float pooled = (w0 * kk0[e] + w1 * kk1[e]) / (w0 + w1);
         x[m][e] = bf16_to_f32(f32_to_bf16(pooled));   // BF16 before the norm
-        ss += x[m][e] * x[m][e];
+        ss += x[m][e] * x[m][e];                      // lanes past D hold zeros
       }
     }
-  }
-  // sum of squares over the row
+    const float r = rsqrtf(wave_sum(ss) / static_cast<float>(D) + a.eps);
+    uint16_t* dst = a.cmp + crow * D;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  if ((tid & 63) == 0) red_s[tid >> 6] = ss;
-  __syncthreads();
-  float tot = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kCmpThreads / 64; ++w) tot += red_s[w];
-  const float r = rsqrtf(tot / static_cast<float>(a.D) + a.eps);
-  uint16_t* dst = a.cmp + crow * a.D;
-#pragma unroll
-  for (int m = 0; m < kMaxPairs; ++m) {
-    const int c = 2 * tid + 2 * kCmpThreads * m;
-    if (c >= a.D) continue;
-    const float2 gm = *reinterpret_cast<const float2*>(a.gamma + c);
-    float y0 = x[m][0] * r * gm.x, y1 = x[m][1] * r * gm.y;
-    const int rr = c - a.rope_offset;
-    if (rr >= 0 && rr < 2 * a.half) {
-      const float co = a.rcos[static_cast<long long>(t) * a.half + (rr >> 1)];
-      const float si = a.rsin[static_cast<long long>(t) * a.half + (rr >> 1)];
-      const float z0 = y0 * co - y1 * si, z1 = y0 * si + y1 * co;
-      y0 = z0;
-      y1 = z1;
+    for (int m = 0; m < NCH; ++m) {
+      const int c = 2 * lane + 2 * kCmpLanes * m;
+      if (c >= D) continue;
+      float y0 = x[m][0] * r * gm[m].x, y1 = x[m][1] * r * gm[m].y;
+      if (in_rope & (1u << m)) {
+        const float co = rot[m].x, si = rot[m].y;
+        const float z0 = y0 * co - y1 * si, z1 = y0 * si + y1 * co;
+        y0 = z0;
+        y1 = z1;
+      }
+      *reinterpret_cast<uint32_t*>(dst + c) = pack_bf16x2(y0, y1);
     }
-    *reinterpret_cast<uint32_t*>(dst + c) = pack_bf16x2(y0, y1);
   }
-}
-
-// One work-group per token: the last min(chunk, CAP) rows of each request's
-// chunk go to their ring slots.
-__global__ void __launch_bounds__(kCmpThreads) compress_state_kernel(CompressArgs a) {
-  const int t = blockIdx.x;
-  if (t >= a.num_tokens) return;
-  const int b = owner_request_wave(a.qsl, a.B, t);
-  if (b < 0) return;
-  const int p = a.pos[t];
-  const int blk = a.sbt[b];
-  if (p < 0 || blk < 0 || blk >= a.nsb) return;
-  const int lo = min(max(a.qsl[b], 0), a.num_tokens);
-  const int hi = min(max(a.qsl[b + 1], 0), a.num_tokens);
-  if (t < max(lo, hi - a.cap)) return;
-  float* row = a.state + (static_cast<long long>(blk) * a.cap + p % a.cap) * 2 * a.D;
-  const float* k = a.kv + static_cast<long long>(t) * a.D;
-  const float* g = a.gate + static_cast<long long>(t) * a.D;
-  for (int c = threadIdx.x; c < a.D; c += kCmpThreads) {
-    row[c] = k[c];
-    row[a.D + c] = g[c];
+  if (t != lo || !ring_ok) return;
+  // the request's ring rows: the last min(chunk, CAP) of its chunk, in row
+  // order (a later row with the same slot wins, channel by channel in the
+  // same lane)
+  for (int tt = max(lo, hi - a.cap); tt < hi; ++tt) {
+    const int q = a.pos[tt];
+    if (q < 0) continue;
+    float* row = a.state + (static_cast<long long>(blk) * a.cap + q % a.cap) * 2 * D;
+    const float* k = a.kv + static_cast<long long>(tt) * D;
+    const float* g = a.gate + static_cast<long long>(tt) * D;
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+      const int c = 2 * lane + 2 * kCmpLanes * m;
+      if (c < D) {
+        *reinterpret_cast<float2*>(row + c) = *reinterpret_cast<const float2*>(k + c);
+        *reinterpret_cast<float2*>(row + D + c) = *reinterpret_cast<const float2*>(g + c);
+      }
+    }
   }
 }
 
@@ -179,7 +195,7 @@ extern "C" int csa_compress_pairs(const float* kv_proj, const float* gate, int32
       max_cmp_blocks < 0 || rope_dim < 0 || rope_offset < 0)
     return CSA_ERR_SHAPE;
   if (num_tokens < 0 || num_tokens > T || state_capacity < 1) return CSA_ERR_RANGE;
-  if ((D & 1) || D > 2 * 256 * 4 || (rope_dim & 1) || (rope_offset & 1) ||
+  if ((D & 1) || D > 2048 || (rope_dim & 1) || (rope_offset & 1) ||
       rope_offset + rope_dim > D || !(rms_eps >= 0.0f))
     return CSA_ERR_UNSUPPORTED;
   if (num_tokens == 0 || D == 0) return CSA_OK;
@@ -217,10 +233,16 @@ extern "C" int csa_compress_pairs(const float* kv_proj, const float* gate, int32
   a.max_cb = max_cmp_blocks;
   a.err = err;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(csa::compress_publish_kernel, dim3(static_cast<unsigned>(num_tokens)),
-                     dim3(csa::kCmpThreads), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
-  hipLaunchKernelGGL(csa::compress_state_kernel, dim3(static_cast<unsigned>(num_tokens)),
-                     dim3(csa::kCmpThreads), 0, st, a);
+  const dim3 grid(static_cast<unsigned>(num_tokens)), block(csa::kCmpLanes);
+  if (D <= 128)
+    hipLaunchKernelGGL(csa::compress_pairs_kernel<1>, grid, block, 0, st, a);
+  else if (D <= 256)
+    hipLaunchKernelGGL(csa::compress_pairs_kernel<2>, grid, block, 0, st, a);
+  else if (D <= 512)
+    hipLaunchKernelGGL(csa::compress_pairs_kernel<4>, grid, block, 0, st, a);
+  else if (D <= 1024)
+    hipLaunchKernelGGL(csa::compress_pairs_kernel<8>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(csa::compress_pairs_kernel<16>, grid, block, 0, st, a);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }

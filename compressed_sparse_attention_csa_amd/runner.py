@@ -3,7 +3,8 @@
 ``CsaStep`` uploads host arrays (NumPy) once, allocates every output and
 workspace up front, and then runs the path as four library calls on one
 stream: RoPE rows -> indexer scores -> top-k -> sparse attention (RoPE rows ->
-attention for the layers without an indexer).  It only
+attention for the layers without an indexer), with the ratio-2 compressor's
+publication after the RoPE rows when the step carries it.  It only
 moves memory and passes pointers; all arithmetic runs in libcsa.so.
 """
 from __future__ import annotations
@@ -30,14 +31,17 @@ class CsaStep:
                  prefill: bool = False, device: str = "cuda", with_values: bool = True,
                  with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None,
                  mode: str = "csa", cand_kb: int = 0, cand_block: int = 8,
-                 index_format: str = "int8", kv_format: str = "bf16"):
+                 index_format: str = "int8", kv_format: str = "bf16", compress: bool = False,
+                 rms_eps: float = 1e-6):
         # mode "csa": indexer scores and top-k select the compressed rows;
         # "hca": no indexer, every visible compressed row (k bounds them);
         # "swa": the window alone (k = 0); "reindex": scores and top-k only
         # inside the supplied candidate mask arrays["cand_blocks"];
         # "hier_full": the csa step, then the candidate mask of cand_kb blocks
-        # of cand_block positions it publishes
-        if mode not in ("csa", "hca", "swa", "reindex", "hier_full"):
+        # of cand_block positions it publishes; "compress": the ratio-2
+        # compressor's publication alone.  compress=True runs that
+        # publication first in any mode (its rope rows share the rope launch).
+        if mode not in ("csa", "hca", "swa", "reindex", "hier_full", "compress"):
             raise ValueError(f"unknown mode {mode!r}")
         if mode in ("reindex", "hier_full") and cand_kb < 1:
             raise ValueError(f"mode {mode!r} needs cand_kb >= 1")
@@ -64,15 +68,37 @@ class CsaStep:
                 self.t[name] = shared[name]   # e.g. read-only RoPE tables reused by copies
             else:
                 self.t[name] = _to_dev(a, dev)
-        q = self.t["q"]
-        T, H, D = q.shape
-        self.T, self.H, self.D = T, H, D
-        self.num_tokens = T if num_tokens is None else int(num_tokens)
-        half = self.t["freqs_cos"].shape[1]
-        self.score_stride = self.t["cmp_block_table"].shape[1] * PAGE
+        self.compress = bool(compress) or mode == "compress"
+        if self.compress and (kv_format != "bf16" or ratio != 2):
+            raise ValueError("the compressor publishes BF16 rows at ratio 2")
+        self.rms_eps = float(rms_eps)
         f32 = dict(dtype=torch.float32, device=dev)
-        self.rope_cos = torch.empty((T, half), **f32)
-        self.rope_sin = torch.empty((T, half), **f32)
+        half = self.t["freqs_cos"].shape[1]
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        if mode == "compress":
+            T, D = self.t["kv_proj"].shape
+            self.T, self.H, self.D = T, 0, D
+        else:
+            T, H, D = self.t["q"].shape
+            self.T, self.H, self.D = T, H, D
+        self.num_tokens = T if num_tokens is None else int(num_tokens)
+        # RoPE rows: the queries' rows, then (with the compressor) the rows of
+        # each token's pair start, materialised by one launch when no row is
+        # padding
+        pos_ids = [] if mode == "compress" else [self.t["position_ids"]]
+        if self.compress:
+            pos_ids.append(self.t["cmp_position_ids"])
+        self.rope_pos = pos_ids[0] if len(pos_ids) == 1 else torch.cat(pos_ids)
+        self.rope_all_cos = torch.empty((len(pos_ids) * T, half), **f32)
+        self.rope_all_sin = torch.empty((len(pos_ids) * T, half), **f32)
+        if mode != "compress":
+            self.rope_cos, self.rope_sin = self.rope_all_cos[:T], self.rope_all_sin[:T]
+        if self.compress:
+            self.cmp_rope_cos, self.cmp_rope_sin = self.rope_all_cos[-T:], self.rope_all_sin[-T:]
+        if mode == "compress":
+            return
+        q = self.t["q"]
+        self.score_stride = self.t["cmp_block_table"].shape[1] * PAGE
         self.cand_kb, self.cand_block = int(cand_kb), int(cand_block)
         if mode == "reindex":
             # the scores of the mask's slots replace the full score rows
@@ -89,7 +115,6 @@ class CsaStep:
         self.topk_val = torch.empty((T, self.k), **f32) if with_values else None
         self.out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((T, H), **f32) if with_lse else None
-        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         tw = _lib.csa_topk_workspace_bytes(T, self.score_stride, self.k)
         self.topk_ws = torch.empty(tw, dtype=torch.uint8, device=dev) if tw else None
         if kv_format == "mx":
@@ -101,9 +126,28 @@ class CsaStep:
 
     # ---- the four stages -------------------------------------------------
     def rope(self, stream=None):
-        _lib.csa_materialize_rope_rows(self.t["freqs_cos"], self.t["freqs_sin"],
-                                       self.t["position_ids"], self.num_tokens, self.rope_cos,
-                                       self.rope_sin, err=self.err, stream=stream)
+        T, n = self.T, self.rope_pos.shape[0]
+        if self.num_tokens == T:
+            _lib.csa_materialize_rope_rows(self.t["freqs_cos"], self.t["freqs_sin"],
+                                           self.rope_pos, n, self.rope_all_cos,
+                                           self.rope_all_sin, err=self.err, stream=stream)
+            return
+        for i in range(0, n, T):   # each part keeps its padding rows untouched
+            _lib.csa_materialize_rope_rows(self.t["freqs_cos"], self.t["freqs_sin"],
+                                           self.rope_pos[i:i + T], self.num_tokens,
+                                           self.rope_all_cos[i:i + T],
+                                           self.rope_all_sin[i:i + T], err=self.err,
+                                           stream=stream)
+
+    def compress_pairs(self, stream=None):
+        """The ratio-2 compressor: every pair an odd row closes is published
+        into cmp_kv, the state ring keeps the chunk's last rows."""
+        t = self.t
+        _lib.csa_compress_pairs(t["kv_proj"], t["gate"], t["query_start_loc"], t["positions"],
+                                self.num_tokens, t["state_block_table"], t["state_cache"],
+                                t["rms_gamma"], self.rms_eps, self.cmp_rope_cos,
+                                self.cmp_rope_sin, self.rope_offset, t["cmp_kv"],
+                                t["cmp_block_table"], err=self.err, stream=stream)
 
     def index(self, stream=None):
         t = self.t
@@ -164,11 +208,14 @@ class CsaStep:
 
     @property
     def stages(self):
+        if self.mode == "compress":
+            return ("rope", "compress_pairs")
+        pre = ("rope", "compress_pairs") if self.compress else ("rope",)
         if self.mode == "hier_full":
-            return ("rope", "index", "topk", "cand", "attn")
+            return pre + ("index", "topk", "cand", "attn")
         if self.mode in ("csa", "reindex"):
-            return ("rope", "index", "topk", "attn")
-        return ("rope", "attn")
+            return pre + ("index", "topk", "attn")
+        return pre + ("attn",)
 
     def inv_rope(self, stream=None, out=None):
         """The output's rope span rotated back by each row's angles (into
@@ -199,4 +246,6 @@ def step_for_config(cfg, arrays: Dict[str, np.ndarray], **kw) -> CsaStep:
                    mode=getattr(cfg, "mode", "csa"), cand_kb=getattr(cfg, "cand_kb", 0),
                    cand_block=getattr(cfg, "cand_block", 8),
                    index_format=getattr(cfg, "index_format", "int8"),
-                   kv_format=getattr(cfg, "kv_format", "bf16"), **kw)
+                   kv_format=getattr(cfg, "kv_format", "bf16"),
+                   compress=getattr(cfg, "compress", False),
+                   rms_eps=getattr(cfg, "rms_eps", 1e-6), **kw)

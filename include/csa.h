@@ -460,7 +460,10 @@ int csa_index_score_fp8(const uint8_t* q_fp8, const float* q_scale, const float*
  * CSA_EFLAG_BLOCK_RANGE and that access is skipped; an active row no request
  * owns sets CSA_EFLAG_META.  Supported: D even and <= 2048, rope_dim and
  * rope_offset even, rope_offset + rope_dim <= D, state_capacity >= 1, the FP32
- * arrays and cmp_kv 8-byte aligned.  Two kernel launches on `stream`.
+ * arrays and cmp_kv 8-byte aligned.  Requests must not share a state block
+ * (their ring accesses would race).  One kernel launch on `stream`: the work-
+ * group of a request's first row does its only ring read and then writes the
+ * request's ring rows, in row order (a later row with the same slot wins).
  */
 int csa_compress_pairs(const float* kv_proj, const float* gate, int32_t D,
                        const int32_t* query_start_loc, const int32_t* positions, int32_t B,

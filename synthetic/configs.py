@@ -43,7 +43,8 @@ class CsaConfig:
     # window alone (k = 0); "reindex": a layer that scores only the positions
     # of a supplied candidate mask (cand_kb blocks of cand_block positions)
     # and selects its k there; "hier_full": the csa step that also publishes
-    # such a mask for the reindex layers
+    # such a mask for the reindex layers; "compress": the compressor's
+    # publication alone (no query side)
     mode: str = "csa"
     cand_kb: int = 0
     cand_block: int = 8
@@ -55,6 +56,13 @@ class CsaConfig:
     # ABI: window rows MXFP8 E4M3 with one E8M0 byte per 32 channels,
     # compressed rows packed MXFP4 E2M1 with one E4M3 byte per 16 channels)
     kv_format: str = "bf16"
+    # the ratio-2 compressor's publication ahead of the step (pypto-lib
+    # "DeepSeek V4.1 Flash", "Compressor state ownership": an FP32 state ring
+    # of state_capacity slots per request, pairs closed by odd positions);
+    # mode "compress" runs that publication alone
+    compress: bool = False
+    state_capacity: int = 4
+    rms_eps: float = 1e-6
 
     @property
     def kv_row_bytes(self):
@@ -232,10 +240,30 @@ C15 = _decode(
     "V4.1 ratio-2 decode with the FP8 index plane: C2's shapes",
     n_req=4, s=2, context=32768, ratio=2, k=512, index_format="fp8")
 
+# The ratio-2 compressor (pypto-lib "DeepSeek V4.1 Flash", "Compressor state
+# ownership"): each decode step first publishes the pair its odd row closes,
+# then scores, selects and attends; a prefill chunk publishes every pair it
+# closes (the compressor alone, at the 8,192-token prefill shape).
+C16 = _decode(
+    "c16_ratio2_decode_compress",
+    "V4.1 ratio-2 decode with the compressor ahead of it: C2's shapes, each request's "
+    "rows (32766, 32767) close one pair, published at compressed position 16383 from "
+    "FP32 KV projections and gate scores, FP32 state ring of 4 slots",
+    n_req=4, s=2, context=32768, ratio=2, k=512, compress=True)
+
+C17 = CsaConfig(
+    name="c17_ratio2_prefill_compress",
+    description="ratio-2 compressor over an 8,192-token prefill chunk: 1 request, "
+                "positions 0..8191, FP32 KV projections and gate scores of width 512, "
+                "4,096 pairs published into 32 pages, the last 4 rows to the ring",
+    rows_per_request=(8192,), positions=(tuple(range(8192)),), context=8192, ratio=2,
+    k=0, mode="compress", compress=True)
+
 CONFIGS: Dict[str, CsaConfig] = {c.name: c for c in (C1, C2, C3, C4, C5, C6, C7, C8, C9, C10,
-                                                     C11, C12, C13, C14, C15)}
+                                                     C11, C12, C13, C14, C15, C16, C17)}
 SHORT = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5, "c6": C6, "c7": C7, "c8": C8,
-         "c9": C9, "c10": C10, "c11": C11, "c12": C12, "c13": C13, "c14": C14, "c15": C15}
+         "c9": C9, "c10": C10, "c11": C11, "c12": C12, "c13": C13, "c14": C14, "c15": C15,
+         "c16": C16, "c17": C17}
 
 
 def get(name: str) -> CsaConfig:

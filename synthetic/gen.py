@@ -33,6 +33,12 @@ for the larger ones:
   exponent field 3..6 (2^-4 .. 2^-1 times 1 + m/8).  The dequantised values
   have an RMS near 0.6 (window) and 1.0 (compressed), the scale of the BF16
   rows.  These planes replace the BF16 pools.
+* compressor inputs (``compress``): FP32 KV projections and gate scores
+  N(0,1) per token, an FP32 state ring N(0,1) (the tokens before the chunk),
+  state blocks a seeded permutation of one per request, RMSNorm weights
+  U(0.5, 1.5), and the rope positions the caller gives the compressor: each
+  token's pair start (its position rounded down to even), -1 for negative
+  positions.
 
 No arithmetic of the method (scores, selection, attention, rotation) lives here.
 """
@@ -53,7 +59,8 @@ _TENSOR_IDS = {
     "cand_blocks": 12, "q_fp4": 13, "q_e8m0": 14, "idx_fp4": 15, "idx_e8m0": 16,
     "win_fp8_bits": 17, "win_fp8_exp": 18, "win_e8m0": 19, "cmp_fp4": 20, "cmp_sc_m": 21,
     "cmp_sc_e": 22, "idx_fp8_bits": 23, "idx_fp8_exp": 24, "q_fp8_bits": 25, "q_fp8_exp": 26,
-    "q_fp8_scale": 27,
+    "q_fp8_scale": 27, "kv_proj": 28, "gate": 29, "state_cache": 30, "state_perm": 31,
+    "rms_gamma": 32,
 }
 
 _CHUNK_ELEMS = 1 << 24  # fixed chunk so the draws never depend on the caller
@@ -147,6 +154,20 @@ class CsaInputs:
         return self.t[k]
 
 
+def _f32_normal(seed: int, name: str, shape) -> np.ndarray:
+    return _rng(seed, name).standard_normal(shape, dtype=np.float32)
+
+
+def _compressor_inputs(t: Dict[str, np.ndarray], cfg: CsaConfig, seed: int, pos: np.ndarray):
+    T, B, D = cfg.T, cfg.B, cfg.D
+    t["kv_proj"] = _f32_normal(seed, "kv_proj", (T, D))
+    t["gate"] = _f32_normal(seed, "gate", (T, D))
+    t["state_cache"] = _f32_normal(seed, "state_cache", (B, cfg.state_capacity, 2 * D))
+    t["state_block_table"] = _rng(seed, "state_perm").permutation(B).astype(np.int32)
+    t["rms_gamma"] = _rng(seed, "rms_gamma").uniform(0.5, 1.5, D).astype(np.float32)
+    t["cmp_position_ids"] = np.where(pos >= 0, pos - pos % 2, -1).astype(np.int32)
+
+
 def make_inputs(cfg: CsaConfig, seed: int = 0, with_tables: bool = True) -> CsaInputs:
     T, B, H, D, R = cfg.T, cfg.B, cfg.H, cfg.D, cfg.R
     Hi, Di = cfg.Hi, cfg.Di
@@ -165,6 +186,14 @@ def make_inputs(cfg: CsaConfig, seed: int = 0, with_tables: bool = True) -> CsaI
 
     if with_tables:
         t["freqs_cos"], t["freqs_sin"] = rope_tables(cfg.rope_capacity, R, cfg.theta)
+    if cfg.compress:
+        _compressor_inputs(t, cfg, seed, pos)
+    if cfg.mode == "compress":   # the publication alone: the compressed pool and its table
+        pages = cfg.cmp_pages_per_request
+        perm = _rng(seed, "cmp_perm").permutation(B * pages).astype(np.int32)
+        t["cmp_block_table"] = perm.reshape(B, pages)
+        t["cmp_kv"] = _bf16_normal(seed, "cmp_kv", (B * pages, PAGE, D))
+        return CsaInputs(cfg, t)
 
     # ---- query side
     t["q"] = _bf16_normal(seed, "q", (T, H, D))

@@ -41,9 +41,32 @@ def kv_sources(x: dict, cfg):
     return x["cmp_kv"], x["win_kv"]
 
 
+def oracle_compress(x: dict, cfg, cmp_kv=None):
+    """The oracle's compressor publication for a config carrying one: its
+    rope rows (the pair starts), then compress_pairs.  Returns (cmp_kv,
+    state_cache, err)."""
+    T = x["kv_proj"].shape[0]
+    half = cfg.R // 2
+    rc = np.full((T, half), np.nan, np.float32)
+    rs = np.full((T, half), np.nan, np.float32)
+    e0 = oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["cmp_position_ids"], T,
+                                      rc, rs)
+    c, st, e1 = oracle.compress_pairs(x["kv_proj"], x["gate"], x["query_start_loc"],
+                                      x["positions"], T, x["state_block_table"],
+                                      x["state_cache"], x["rms_gamma"], cfg.rms_eps, rc, rs,
+                                      cfg.rope_offset,
+                                      x["cmp_kv"] if cmp_kv is None else cmp_kv,
+                                      x["cmp_block_table"])
+    return c, st, e0 | e1
+
+
 def oracle_step(x: dict, cfg, topk_override=None) -> dict:
     T = x["q"].shape[0]
     half = cfg.R // 2
+    ec, cst = 0, None
+    if getattr(cfg, "compress", False):   # the publication comes first
+        cmp_pub, cst, ec = oracle_compress(x, cfg)
+        x = dict(x, cmp_kv=cmp_pub)
     rc = np.full((T, half), np.nan, np.float32)
     rs = np.full((T, half), np.nan, np.float32)
     e0 = oracle.materialize_rope_rows(x["freqs_cos"], x["freqs_sin"], x["position_ids"], T, rc, rs)
@@ -60,7 +83,7 @@ def oracle_step(x: dict, cfg, topk_override=None) -> dict:
                                       x["win_block_table"], cfg.W, x["attn_sink"],
                                       cfg.softmax_scale, x["query_start_loc"], x["positions"], T)
     return dict(rope_cos=rc, rope_sin=rs, scores=s, topk_idx=idx, topk_val=val, out=out,
-                lse=lse, err=e0 | e1 | e2 | e3)
+                lse=lse, err=e0 | e1 | e2 | e3 | ec, cmp_kv=x["cmp_kv"], state_cache=cst)
 
 
 def bf16_to_f64(t) -> np.ndarray:

@@ -4,7 +4,9 @@ Published rows against the oracle, with a tolerance from the arithmetic: the
 FP32 pooling differs from the exact value by a few FP32 ulps, so its BF16
 rounding can land one BF16 ulp (at most 2^-7 relative) away from the
 oracle's; the norm factor moves by far less; each side's output rounding adds
-at most half an ulp (2^-8 relative).  Off the rope span that bounds
+at most half an ulp (2^-8 relative).  Where the pooled value cancels, the
+FP32 rounding is relative to the pair's inputs instead: an absolute
+2^-18 RMS(row) covers inputs up to 16 times the row's RMS.  Off the rope span that bounds
 |g - o| by 2^-6 |o| up to second-order terms (the test allows 1.05 times
 that).  A rope pair mixes two channels: the rotation carries the 2^-7
 errors of both inputs into each output, at most sqrt(2) 2^-7 (|o_c| + |o_p|),
@@ -17,6 +19,8 @@ import numpy as np
 import pytest
 
 import oracle
+import synthetic
+from tests import harness as H
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -81,6 +85,23 @@ def _run(a):
             int(err.item()))
 
 
+def _check_rows(g_bits, o_bits, off, half, what):
+    """Published BF16 rows against the oracle's, to the tolerance above."""
+    g = oracle.bf16_to_f64(g_bits)
+    o = oracle.bf16_to_f64(o_bits)
+    tol = 1.05 * 2.0 ** -6 * np.abs(o)
+    span = slice(off, off + 2 * half)
+    mag = np.abs(o[..., span])
+    partner = mag.reshape(mag.shape[:-1] + (-1, 2))[..., ::-1].reshape(mag.shape)
+    tol[..., span] = 2.0 ** -5 * (mag + partner)
+    # the FP32 pooling's rounding is relative to the pair's inputs, not to a
+    # pooled value that cancels: a few FP32 ulps of inputs up to 16x the row
+    # RMS, carried through the norm factor
+    tol += 2.0 ** -18 * np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
+    assert np.all(np.abs(g - o) <= tol + 1e-30), (
+        f"{what}: worst {np.max(np.abs(g - o) - tol):.3g} over, rows {o.shape[0]}")
+
+
 def _compare(a, what):
     g_cmp, g_st, g_err = _run(a)
     o_cmp, o_st, o_err = oracle.compress_pairs(**a)
@@ -91,16 +112,8 @@ def _compare(a, what):
     assert not np.any(np.all(g_cmp == SENT, axis=-1) & ~untouched), f"{what}: missing rows"
     if untouched.all():
         return 0
-    g = oracle.bf16_to_f64(g_cmp[~untouched])
-    o = oracle.bf16_to_f64(o_cmp[~untouched])
-    off = a["rope_offset"]
-    tol = 1.05 * 2.0 ** -6 * np.abs(o)
-    span = slice(off, off + 2 * a["rope_cos"].shape[1])
-    mag = np.abs(o[:, span])
-    partner = mag.reshape(mag.shape[0], -1, 2)[:, :, ::-1].reshape(mag.shape)
-    tol[:, span] = 2.0 ** -5 * (mag + partner)
-    assert np.all(np.abs(g - o) <= tol + 1e-30), (
-        f"{what}: worst {np.max(np.abs(g - o) - tol):.3g} over, rows {int((~untouched).sum())}")
+    _check_rows(g_cmp[~untouched], o_cmp[~untouched], a["rope_offset"], a["rope_cos"].shape[1],
+                what)
     return int((~untouched).sum())
 
 
@@ -113,6 +126,16 @@ def test_mixed_chunks_against_the_oracle():
     print("[compress] mixed chunks", flush=True)
     n = _compare(a, "mixed")
     assert n == 1 + 1 + 3 + 3   # 11; 13; 21, 23, 25; 101, 103, 105
+
+
+@pytest.mark.parametrize("D,R", [(96, 32), (256, 0), (1000, 64), (2048, 64)])
+def test_head_widths(D, R):
+    """Every channel-chunk count the kernel instantiates, partial chunks
+    (lanes past D) and a layer without a rope span."""
+    rng = np.random.default_rng(D + R)
+    a = _case(rng, chunks=[3, 4, 1], starts=[5, 20, 9], D=D, R=R)
+    print(f"[compress] D={D} R={R}", flush=True)
+    assert _compare(a, f"D={D}") == 2 + 2 + 1
 
 
 def test_contract_flags_and_negative_positions():
@@ -167,3 +190,85 @@ def test_chunking_invariance_bitwise():
     assert t0 == n
     assert np.array_equal(cmp, g_whole)
     assert np.array_equal(state.view(np.uint32), st_whole.view(np.uint32))
+
+
+def _step(cfg_name):
+    import compressed_sparse_attention_csa_amd as csa
+    cfg = synthetic.get(cfg_name)
+    x = synthetic.make_inputs(cfg, seed=0).t
+    step = csa.step_for_config(cfg, x)
+    return cfg, x, step
+
+
+def _published_rows(cfg, x, cmp_bits):
+    """(request, compressed position, pool row) of every pair the chunk closes."""
+    qsl, pos, bt = x["query_start_loc"], x["positions"], x["cmp_block_table"]
+    out = []
+    for b in range(cfg.B):
+        for t in range(qsl[b], qsl[b + 1]):
+            p = int(pos[t])
+            if p >= 0 and p % 2 == 1:
+                c = p // 2
+                out.append(cmp_bits[bt[b, c // PAGE], c % PAGE])
+    return np.stack(out)
+
+
+def test_c16_decode_step_with_the_compressor():
+    """C2's decode step with the publication first: the published rows, the
+    ring, the step's scores / top-k / attention, and attention over a
+    selection that holds the freshly published row."""
+    cfg, x, step = _step("c16")
+    print("[compress] c16 step", flush=True)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    o = H.oracle_step(x, cfg)
+    assert o["err"] == 0
+    g_cmp = step.t["cmp_kv"].view(torch.int16).cpu().numpy().view(np.uint16)
+    g_rows = _published_rows(cfg, x, g_cmp)
+    assert g_rows.shape[0] == cfg.B
+    _check_rows(g_rows, _published_rows(cfg, x, o["cmp_kv"]), cfg.rope_offset, cfg.R // 2,
+                "c16 published rows")
+    # every other row of the pool is untouched
+    mask = np.ones(g_cmp.shape[:2], bool)
+    for b in range(cfg.B):
+        mask[x["cmp_block_table"][b, 16383 // PAGE], 16383 % PAGE] = False
+    assert np.array_equal(g_cmp[mask], x["cmp_kv"][mask])
+    g_st = step.t["state_cache"].cpu().numpy()
+    assert np.array_equal(g_st.view(np.uint32), o["state_cache"].view(np.uint32))
+    H.check_scores(step.scores.cpu().numpy().astype(np.float64), o["scores"], "c16 scores")
+    same = H.check_topk(step.topk_idx.cpu().numpy(), o["topk_idx"], o["scores"], x["positions"],
+                        cfg.ratio, "c16 top-k")
+    H.check_attn(H.bf16_to_f64(step.out)[same], o["out"][same],
+                 step.lse.cpu().numpy()[same], o["lse"][same], "c16 attention")
+    # the freshly published row inside the selection of the rows that see it
+    # (the odd rows: position 32767 sees compressed positions 0..16383): the
+    # oracle's selection with one entry replaced by 16383, re-sorted
+    sel = o["topk_idx"].copy()
+    for t in range(cfg.T):
+        if x["positions"][t] % 2 == 0:
+            continue
+        row = [c for c in sel[t] if c != 16383][:cfg.k - 1] + [16383]
+        sel[t] = np.sort(np.asarray(row, np.int32))
+    step.attn(topk_idx=torch.from_numpy(sel).cuda())
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    o2 = H.oracle_step(x, cfg, topk_override=sel)
+    H.check_attn(H.bf16_to_f64(step.out), o2["out"], step.lse.cpu().numpy(), o2["lse"],
+                 "c16 attention over the published row")
+
+
+def test_c17_prefill_chunk_publication():
+    """The 8,192-token prefill chunk: all 4,096 published rows and the ring."""
+    cfg, x, step = _step("c17")
+    print("[compress] c17 chunk", flush=True)
+    step.run()
+    torch.cuda.synchronize()
+    assert int(step.err.item()) == 0
+    o_cmp, o_st, oe = H.oracle_compress(x, cfg)
+    assert oe == 0
+    g_cmp = step.t["cmp_kv"].view(torch.int16).cpu().numpy().view(np.uint16)
+    _check_rows(g_cmp.reshape(-1, cfg.D), o_cmp.reshape(-1, cfg.D), cfg.rope_offset, cfg.R // 2,
+                "c17 published rows")
+    g_st = step.t["state_cache"].cpu().numpy()
+    assert np.array_equal(g_st.view(np.uint32), o_st.view(np.uint32))
