@@ -423,12 +423,15 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     constexpr int S = decltype(stg)::value;
     // page pi has landed once only the newer pages and the score stores
     // issued since may still be in flight (vector memory completes in issue
-    // order).  Only the first of a page's two stores is sure to be issued
-    // (its lane for key 0 is always inside the row), so only it is counted:
-    // counting too few ops just waits a little longer.
+    // order): an active wave issues both of a page's two stores on every
+    // page but the last of the score row (only there can the row end cut
+    // the second to no lanes), which is the last page of its work-group's
+    // run, so no wait comes after it.  Counting every store matters: a
+    // count one short per page makes each page wait for the stores of the
+    // page two back to reach memory.
     const int newer = min(kStages - 2, npages - 1 - pi);
     wait_vm_rt(__builtin_amdgcn_readfirstlane(VMPv * newer +
-                                              (active ? min(kStages - 1, pi) : 0)));
+                                              (active ? 2 * min(kStages - 1, pi) : 0)));
     lds_barrier();
     const int blk_here = blk_s[pi];   // read before the refill's loads go out
     if (pi + kStages - 1 < npages)

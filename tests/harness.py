@@ -83,7 +83,7 @@ def oracle_step(x: dict, cfg, topk_override=None) -> dict:
                                       x["win_block_table"], cfg.W, x["attn_sink"],
                                       cfg.softmax_scale, x["query_start_loc"], x["positions"], T)
     return dict(rope_cos=rc, rope_sin=rs, scores=s, topk_idx=idx, topk_val=val, out=out,
-                lse=lse, err=e0 | e1 | e2 | e3 | ec, cmp_kv=x["cmp_kv"], state_cache=cst)
+                lse=lse, err=e0 | e1 | e2 | e3 | ec, cmp_kv=x.get("cmp_kv"), state_cache=cst)
 
 
 def bf16_to_f64(t) -> np.ndarray:
