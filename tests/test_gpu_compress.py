@@ -138,6 +138,16 @@ def test_head_widths(D, R):
     assert _compare(a, f"D={D}") == 2 + 2 + 1
 
 
+def test_repeated_slots_keep_the_later_row():
+    """Non-consecutive positions whose slots repeat among a chunk's last CAP
+    rows: the later row wins each slot (the oracle writes in row order)."""
+    rng = np.random.default_rng(64)
+    a = _case(rng, chunks=[6], starts=[0])
+    a["positions"] = np.array([3, 8, 13, 17, 21, 24], np.int32)   # last 4: slots 1, 1, 1, 0
+    print("[compress] repeated slots", flush=True)
+    _compare(a, "repeated slots")
+
+
 def test_contract_flags_and_negative_positions():
     rng = np.random.default_rng(61)
     # request 0: positions 7, -1, 9 (9 pools with the negative row's input);
