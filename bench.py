@@ -486,6 +486,18 @@ def main():
                 "traffic": measured_traffic(dom, cfg.name),
                 "algorithmic_per_launch": wm["stage_bytes"][dom], "avg_launch_ms": stage_ms[dom]}
 
+    # the indexer's dot products against the matrix-core peak of its dtype
+    # (the INT8 and FP8 planes 5 POPS dense, MXFP4 10): at C5 the kernel is
+    # bound by its MFMAs and VALU epilogue together, so this figure sits
+    # beside the HBM one
+    compute_roof = None
+    if first.mode in ("csa", "hier_full") and wm["flops"].get("index"):
+        pk = 10000.0 if cfg.index_format == "mxfp4" else INT8_PEAK_TOPS
+        ach_c = wm["flops"]["index"] / (stage_ms["index"] / 1e3) / 1e12
+        compute_roof = {"kernel": "index_score_kernel", "bound": "mfma",
+                        "achieved": round(ach_c, 1), "peak": pk, "unit": "TOP/s",
+                        "frac": round(ach_c / pk, 4), "dtype": cfg.index_format,
+                        "algorithmic_ops_per_launch": wm["flops"]["index"]}
     rec = {
         "metric": "CSA decode rows/s per layer + achieved HBM GB/s (% of MI355X peak)",
         "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
@@ -518,6 +530,7 @@ def main():
         "stage_ms": {s: round(v, 5) for s, v in stage_ms.items()},
         "stage_bytes_algorithmic": wm["stage_bytes"],
         "roofline": roof,
+        "roofline_compute": compute_roof,
         "device_errors": errs[0],
     }
     if not args.no_cpu_baseline:
