@@ -105,11 +105,12 @@ def compress_bytes(cfg, x):
             + 4 * T)
 
 
-def work_model(cfg, x, topk_idx: np.ndarray):
+def work_model(cfg, x, topk_idx: np.ndarray, fused_rope: bool = False):
     """Bytes each stage must move once, and the step total (decode formula:
     index keys of every visible position once per request, every unique
     gathered KV row once per request, Q, O, lse and small metadata; with the
-    compressor, its bytes on top)."""
+    compressor, its bytes on top).  fused_rope: the attention launch gathers
+    the rope rows from the tables and writes them (no rope stage)."""
     T, H, D, R, Hi, Di, k = cfg.T, cfg.H, cfg.D, cfg.R, cfg.Hi, cfg.Di, cfg.k
     mode = getattr(cfg, "mode", "csa")
     if mode == "compress":   # the publication alone: rope rows of the pair starts, then it
@@ -183,6 +184,9 @@ def work_model(cfg, x, topk_idx: np.ndarray):
         st = {"rope": st["rope"], "attn": st["attn"]}
     step = (idx_keys * kbytes + kv_bytes + 4 * T * H * D + 4 * T * H + q_side
             + 2 * sel_bytes + 4 * T * R + mask_bytes)
+    if fused_rope:   # table rows read in place of rope rows; the rows written, position ids
+        st["attn"] += 4 * T * R + 4 * T
+        del st["rope"]
     if getattr(cfg, "compress", False):
         st["rope"] += 8 * T * R + 4 * T      # the pair starts' rope rows, same launch
         st["compress_pairs"] = compress_bytes(cfg, x)
@@ -463,7 +467,7 @@ def main():
     errs = [int(s.err.item()) for s in steps]
     topk_host = first.topk_idx.cpu().numpy() if cfg.mode != "compress" else None
 
-    wm = work_model(cfg, x, topk_host)
+    wm = work_model(cfg, x, topk_host, fused_rope=("rope" not in stages))
     rows = cfg.T
     value = rows / (ms_per_step / 1e3)
     step_gbs = wm["step_bytes"] / (ms_per_step / 1e3) / 1e9

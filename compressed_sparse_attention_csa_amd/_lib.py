@@ -66,6 +66,11 @@ _SIGS["csa_sparse_attn_mx_workspace_bytes"] = _SIGS["csa_sparse_attn_workspace_b
 _SIGS["csa_sparse_attn_decode_mx"] = (
     ctypes.c_int, _SIGS["csa_sparse_attn_decode"][1][:6] + [_P]
     + _SIGS["csa_sparse_attn_decode"][1][6:13] + [_P] + _SIGS["csa_sparse_attn_decode"][1][13:])
+# the decode arguments with (freqs_cos, freqs_sin, table_capacity) in place
+# of the rope rows, and the rope rows it writes after lse
+_SIGS["csa_sparse_attn_decode_rope"] = (
+    ctypes.c_int, [_P, _P, _P, _I32, _P] + _SIGS["csa_sparse_attn_decode"][1][3:28] + [_P, _P]
+    + _SIGS["csa_sparse_attn_decode"][1][28:])
 _SIGS["csa_sparse_attn_noalloc_max_bytes"] = (_SZ, [])
 # the decode arguments without (workspace, workspace_bytes)
 _SIGS["csa_sparse_attn_decode_noalloc"] = (
@@ -328,6 +333,46 @@ def _attn(fn_name, q, rope_cos, rope_sin, rope_offset, cmp_kv, cmp_block_table, 
 
 def csa_sparse_attn_decode(*args, **kw) -> None:
     _attn("csa_sparse_attn_decode", *args, **kw)
+
+
+def csa_sparse_attn_decode_rope(q, freqs_cos, freqs_sin, position_ids, rope_offset, cmp_kv,
+                                cmp_block_table, topk_idx, ratio, win_kv, win_block_table, window,
+                                attn_sink, softmax_scale, query_start_loc, positions, num_tokens,
+                                out, lse=None, rope_cos=None, rope_sin=None, workspace=None,
+                                err=None, stream=None, k=None) -> None:
+    """csa_sparse_attn_decode that gathers each row's rope row (table row
+    position_ids[t] of freqs_cos / freqs_sin, FP32 [capacity, rope_dim / 2])
+    itself and, when rope_cos / rope_sin (FP32 [T, rope_dim / 2]) are given,
+    writes them as csa_materialize_rope_rows would."""
+    _need(q, _BF16, 3, "q")
+    _need(out, _BF16, 3, "out")
+    _need(freqs_cos, (torch.float32,), 2, "freqs_cos")
+    _need(freqs_sin, (torch.float32,), 2, "freqs_sin")
+    T, H, D = q.shape
+    half = freqs_cos.shape[1]
+    if tuple(freqs_sin.shape) != tuple(freqs_cos.shape):
+        raise CsaError("freqs_cos and freqs_sin differ in shape")
+    for name, r in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        if r is not None:
+            _need(r, (torch.float32,), 2, name)
+            if tuple(r.shape) != (T, half):
+                raise CsaError(f"{name}: expected {(T, half)}, got {tuple(r.shape)}")
+    if topk_idx is not None:
+        k = topk_idx.shape[1]
+    elif k is None:
+        raise CsaError("k is required when topk_idx is None")
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().csa_sparse_attn_decode_rope(
+        _ptr(q), _ptr(freqs_cos), _ptr(freqs_sin), freqs_cos.shape[0], _ptr(position_ids),
+        2 * half,
+        int(rope_offset), _ptr(cmp_kv), 0 if cmp_kv is None else cmp_kv.shape[0],
+        _ptr(cmp_block_table), 0 if cmp_block_table is None else cmp_block_table.shape[1],
+        _ptr(topk_idx), int(k), int(ratio), _ptr(win_kv), win_kv.shape[0], _ptr(win_block_table),
+        win_block_table.shape[1], int(window), _ptr(attn_sink), float(softmax_scale),
+        _ptr(query_start_loc), _ptr(positions), query_start_loc.shape[0] - 1, T,
+        int(num_tokens), H, D, _ptr(out), _ptr(lse), _ptr(rope_cos), _ptr(rope_sin),
+        _ptr(workspace), wsb, _ptr(err), _stream(stream))
+    _check(st, "csa_sparse_attn_decode_rope")
 
 
 def csa_sparse_attn_noalloc_max_bytes() -> int:

@@ -70,6 +70,17 @@ struct AttnArgs {
   const float* rope_sin;
   int half_rope;
   int rope_offset;
+  // full RoPE tables [tab_cap][half_rope] instead of rope rows (rope_cos is
+  // then NULL): row t takes table row rope_pos[t], the identity rotation
+  // when that is negative; with rope_out_cos the work-group of head group 0
+  // and span 0 also stores the row there (rows past the tables are flagged
+  // and left untouched)
+  const int32_t* rope_pos;
+  const float* tab_cos;
+  const float* tab_sin;
+  int tab_cap;
+  float* rope_out_cos;
+  float* rope_out_sin;
   const uint16_t* cmp_kv;
   int num_cmp_blocks;
   const int32_t* cmp_bt;
@@ -107,6 +118,38 @@ struct AttnArgs {
   int items_per_xcd;
   int32_t* err;
 };
+
+// Element j of the rope row at position p, gathered from the full tables
+// (pypto-lib "DeepSeek V4.1 Flash", section "Serving-owned full RoPE
+// tables"): a negative position takes the identity rotation, and so (for
+// this kernel's own use) does a position past the tables, which
+// publish_rope_row flags.
+__device__ __forceinline__ void rope_from_tables(const float* __restrict__ tc,
+                                                 const float* __restrict__ ts, int cap, int half,
+                                                 int p, int j, float& c, float& s) {
+  c = 1.0f;
+  s = 0.0f;
+  if (p >= 0 && p < cap) {
+    c = tc[static_cast<long long>(p) * half + j];
+    s = ts[static_cast<long long>(p) * half + j];
+  }
+}
+
+// The rope row of token t as the materialisation step writes it: thread j <
+// half stores element j; a row past the tables stays untouched and raises
+// POS_RANGE (in the work-group's LDS error word).
+__device__ __forceinline__ void publish_rope_row(float* __restrict__ oc, float* __restrict__ os,
+                                                 int cap, int half, int t, int p, int j, float c,
+                                                 float s, int* err_lds) {
+  if (p >= cap) {
+    if (j == 0 && half > 0) atomicOr(err_lds, CSA_EFLAG_POS_RANGE);
+    return;
+  }
+  if (j < half) {
+    oc[static_cast<long long>(t) * half + j] = c;
+    os[static_cast<long long>(t) * half + j] = s;
+  }
+}
 
 constexpr int kMaxSplit = 4224;  // longest key list of the ring schedule: window + k
 constexpr int kMaxDenseK = 1 << 20;   // bound on k without a selection array
@@ -372,19 +415,24 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
   // the resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
+  const int rp = a.tab_cos ? a.rope_pos[t] : -1;   // the rope row's position
   // (no selection array: the compressed set is every visible row, 0 .. n_vis-1)
   const int32_t* topk_row = a.topk ? a.topk + static_cast<long long>(t) * a.k : nullptr;
   const int i_spec0 = i0 + tid - a.window, i_spec1 = i0 + kRingThreads + tid - a.window;
   const int c_spec0 = (topk_row && i_spec0 >= 0 && i_spec0 < a.k) ? topk_row[i_spec0] : -1;
   const int c_spec1 = (topk_row && i_spec1 >= 0 && i_spec1 < a.k) ? topk_row[i_spec1] : -1;
   float rcv = 0.0f, rsv = 0.0f;
-  if (tid < a.half_rope) {
+  if (tid < a.half_rope && !a.tab_cos) {
     rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + tid];
     rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + tid];
   }
   const float sink2 = hv ? a.sink[h] * kLog2e : 0.0f;
   const int b = owner_from_lanes(qsl_v, a.qsl, a.B, t);
   const int nv = visible_count(p, a.ratio);
+  // from the full tables: row rp, fetched once rp is in, ahead of the
+  // resolution's lookups (whose waits then cover it)
+  if (tid < a.half_rope && a.tab_cos)
+    rope_from_tables(a.tab_cos, a.tab_sin, a.tab_cap, a.half_rope, rp, tid, rcv, rsv);
   int w_len = 0, w_lo = 0;
   if (b >= 0 && p >= 0 && a.window > 0) {
     w_lo = max(0, p - a.window + 1);
@@ -455,6 +503,9 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
     rope_s[tid] = rcv;
     rope_s[256 + tid] = rsv;
   }
+  if (a.rope_out_cos && split == 0)
+    publish_rope_row(a.rope_out_cos, a.rope_out_sin, a.tab_cap, a.half_rope, t, rp, tid, rcv,
+                     rsv, &err_s);
   lds_barrier();  // row_s and rope_s ready
 
   // ---- direct-to-LDS gather of one 32-row tile into ring slot tt % kRing
@@ -942,6 +993,7 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
   // resolution.
   const int qsl_v = qsl_lane_load(a.qsl, a.B);
   const int p = a.positions[t];
+  const int rp = a.tab_cos ? a.rope_pos[t] : -1;   // the rope row's position
   // (no selection array: the compressed set is every visible row, 0 .. n_vis-1)
   const int32_t* topk_row = a.topk ? a.topk + static_cast<long long>(t) * a.k : nullptr;
   const int i_spec = split * kSpan + tid - a.window;
@@ -1010,8 +1062,12 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
     }
     if (a.half_rope > 0) {   // uniform: no table without a rope span
       const int rt = tid < a.half_rope ? tid : 0;
-      rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + rt];
-      rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + rt];
+      if (a.tab_cos) {
+        rope_from_tables(a.tab_cos, a.tab_sin, a.tab_cap, a.half_rope, rp, rt, rcv, rsv);
+      } else {
+        rcv = a.rope_cos[static_cast<long long>(t) * a.half_rope + rt];
+        rsv = a.rope_sin[static_cast<long long>(t) * a.half_rope + rt];
+      }
     }
     if (bt_row) {
       if (blk >= 0 && blk < lk_num)
@@ -1029,6 +1085,9 @@ __global__ void __launch_bounds__(kAttnThreads, 1) attn_decode_kernel(AttnArgs a
     rope_s[tid] = rcv;
     rope_s[kAttnThreads + tid] = rsv;
   }
+  if (a.rope_out_cos && split == 0 && hg == 0)
+    publish_rope_row(a.rope_out_cos, a.rope_out_sin, a.tab_cap, a.half_rope, t, rp, tid, rcv,
+                     rsv, &err_s);
   __syncthreads();
 
   // ---- this wave's 32 rows straight into its LDS slot (masked rows read the
@@ -1513,7 +1572,10 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
                int32_t num_tokens, int32_t H, int32_t D, uint16_t* out, float* lse,
                void* workspace, size_t workspace_bytes, int32_t* err, void* stream,
                bool static_scratch = false, bool mx = false, const uint8_t* cmp_sc = nullptr,
-               const uint8_t* win_sc = nullptr) {
+               const uint8_t* win_sc = nullptr, const int32_t* rope_pos = nullptr,
+               const float* tab_cos = nullptr,
+               const float* tab_sin = nullptr, int32_t tab_cap = 0,
+               float* rope_out_cos = nullptr, float* rope_out_sin = nullptr) {
   if (T < 0 || B < 0 || num_cmp_blocks < 0 || num_win_blocks < 0 || max_cmp_blocks < 0 ||
       max_win_blocks < 0 || window < 0 || k < 0)
     return CSA_ERR_SHAPE;
@@ -1524,7 +1586,13 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
     return CSA_ERR_RANGE;
   if (num_tokens == 0) return CSA_OK;
   if (!q || !attn_sink || !query_start_loc || !positions || !out) return CSA_ERR_NULL;
-  if (rope_dim > 0 && (!rope_cos || !rope_sin)) return CSA_ERR_NULL;
+  if (tab_cos || tab_sin) {   // rope rows gathered from the full tables
+    if (tab_cap < 0) return CSA_ERR_SHAPE;
+    if (rope_dim > 0 && (!tab_cos || !tab_sin || !rope_pos)) return CSA_ERR_NULL;
+    if (!rope_out_cos != !rope_out_sin) return CSA_ERR_NULL;
+  } else if (rope_dim > 0 && (!rope_cos || !rope_sin)) {
+    return CSA_ERR_NULL;
+  }
   if (H < 1 || H > 64) return CSA_ERR_UNSUPPORTED;
   if (D != 64 && D != 128 && D != 256 && D != 512) return CSA_ERR_UNSUPPORTED;
   if (rope_dim < 0 || (rope_dim & 1) || rope_offset < 0 || (rope_offset & 1) ||
@@ -1548,6 +1616,16 @@ int attn_entry(bool prefill, const uint16_t* q, const float* rope_cos, const flo
   a.rope_sin = rope_sin;
   a.half_rope = rope_dim / 2;
   a.rope_offset = rope_offset;
+  if (tab_cos && rope_dim > 0) {
+    a.rope_cos = nullptr;
+    a.rope_sin = nullptr;
+    a.rope_pos = rope_pos;
+    a.tab_cos = tab_cos;
+    a.tab_sin = tab_sin;
+    a.tab_cap = tab_cap;
+    a.rope_out_cos = rope_out_cos;
+    a.rope_out_sin = rope_out_sin;
+  }
   if (mx) {
     a.cmp_fp4 = static_cast<const uint8_t*>(cmp_kv);
     a.cmp_sc = cmp_sc;
@@ -1632,6 +1710,29 @@ extern "C" int csa_sparse_attn_decode(
                          win_kv, num_win_blocks, win_block_table, max_win_blocks, window,
                          attn_sink, softmax_scale, query_start_loc, positions, B, T, num_tokens,
                          H, D, out, lse, workspace, workspace_bytes, err, stream);
+}
+
+extern "C" int csa_sparse_attn_decode_rope(
+    const uint16_t* q, const float* freqs_cos, const float* freqs_sin, int32_t table_capacity,
+    const int32_t* position_ids, int32_t rope_dim, int32_t rope_offset, const uint16_t* cmp_kv,
+    int32_t num_cmp_blocks,
+    const int32_t* cmp_block_table, int32_t max_cmp_blocks, const int32_t* topk_idx, int32_t k,
+    int32_t ratio, const uint16_t* win_kv, int32_t num_win_blocks,
+    const int32_t* win_block_table, int32_t max_win_blocks, int32_t window,
+    const float* attn_sink, float softmax_scale, const int32_t* query_start_loc,
+    const int32_t* positions, int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
+    uint16_t* out, float* lse, float* rope_cos, float* rope_sin, void* workspace,
+    size_t workspace_bytes, int32_t* err, void* stream) {
+  if (table_capacity < 0) return CSA_ERR_SHAPE;
+  if (rope_dim > 0 && (!freqs_cos || !freqs_sin || !position_ids)) return CSA_ERR_NULL;
+  if (rope_dim == 0) freqs_cos = freqs_sin = nullptr;   // no rope span: nothing to gather
+  return csa::attn_entry(false, q, nullptr, nullptr, rope_dim, rope_offset, cmp_kv,
+                         num_cmp_blocks, cmp_block_table, max_cmp_blocks, topk_idx, k, ratio,
+                         win_kv, num_win_blocks, win_block_table, max_win_blocks, window,
+                         attn_sink, softmax_scale, query_start_loc, positions, B, T, num_tokens,
+                         H, D, out, lse, workspace, workspace_bytes, err, stream,
+                         /*static_scratch=*/false, /*mx=*/false, nullptr, nullptr,
+                         position_ids, freqs_cos, freqs_sin, table_capacity, rope_cos, rope_sin);
 }
 
 extern "C" int csa_sparse_attn_prefill(

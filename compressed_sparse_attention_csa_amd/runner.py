@@ -4,8 +4,10 @@
 workspace up front, and then runs the path as four library calls on one
 stream: RoPE rows -> indexer scores -> top-k -> sparse attention (RoPE rows ->
 attention for the layers without an indexer), with the ratio-2 compressor's
-publication after the RoPE rows when the step carries it.  It only
-moves memory and passes pointers; all arithmetic runs in libcsa.so.
+publication after the RoPE rows when the step carries it.  BF16 decode steps
+without the compressor gather the RoPE rows inside the attention launch
+instead (three launches).  It only moves memory and passes pointers; all
+arithmetic runs in libcsa.so.
 """
 from __future__ import annotations
 
@@ -32,7 +34,7 @@ class CsaStep:
                  with_lse: bool = True, shared: Optional[Dict[str, torch.Tensor]] = None,
                  mode: str = "csa", cand_kb: int = 0, cand_block: int = 8,
                  index_format: str = "int8", kv_format: str = "bf16", compress: bool = False,
-                 rms_eps: float = 1e-6):
+                 rms_eps: float = 1e-6, fuse_rope: bool = True):
         # mode "csa": indexer scores and top-k select the compressed rows;
         # "hca": no indexer, every visible compressed row (k bounds them);
         # "swa": the window alone (k = 0); "reindex": scores and top-k only
@@ -72,6 +74,11 @@ class CsaStep:
         if self.compress and (kv_format != "bf16" or ratio != 2):
             raise ValueError("the compressor publishes BF16 rows at ratio 2")
         self.rms_eps = float(rms_eps)
+        # BF16 decode steps without the compressor gather their rope rows in
+        # the attention launch (csa_sparse_attn_decode_rope), which also
+        # writes them out: one launch fewer per step
+        self.fuse_rope = (bool(fuse_rope) and not prefill and kv_format == "bf16"
+                          and not self.compress)
         f32 = dict(dtype=torch.float32, device=dev)
         half = self.t["freqs_cos"].shape[1]
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -200,6 +207,15 @@ class CsaStep:
                 self.out, lse=self.lse, workspace=self.attn_ws, err=self.err, stream=stream,
                 k=self.k)
             return
+        if self.fuse_rope:
+            _lib.csa_sparse_attn_decode_rope(
+                t["q"], t["freqs_cos"], t["freqs_sin"], t["position_ids"], self.rope_offset,
+                t["cmp_kv"], t["cmp_block_table"], topk_idx, self.ratio, t["win_kv"],
+                t["win_block_table"], self.window, t["attn_sink"], self.softmax_scale,
+                t["query_start_loc"], t["positions"], self.num_tokens, self.out, lse=self.lse,
+                rope_cos=self.rope_cos, rope_sin=self.rope_sin, workspace=self.attn_ws,
+                err=self.err, stream=stream, k=self.k)
+            return
         fn(t["q"], self.rope_cos, self.rope_sin, self.rope_offset, t["cmp_kv"],
            t["cmp_block_table"], topk_idx, self.ratio, t["win_kv"], t["win_block_table"],
            self.window, t["attn_sink"], self.softmax_scale, t["query_start_loc"],
@@ -210,7 +226,8 @@ class CsaStep:
     def stages(self):
         if self.mode == "compress":
             return ("rope", "compress_pairs")
-        pre = ("rope", "compress_pairs") if self.compress else ("rope",)
+        pre = (("rope", "compress_pairs") if self.compress
+               else () if self.fuse_rope else ("rope",))
         if self.mode == "hier_full":
             return pre + ("index", "topk", "cand", "attn")
         if self.mode in ("csa", "reindex"):

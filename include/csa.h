@@ -271,6 +271,47 @@ int csa_sparse_attn_decode(const uint16_t* q, const float* rope_cos, const float
                            size_t workspace_bytes, int32_t* err, void* stream);
 
 /*
+ * csa_sparse_attn_decode_rope -- csa_sparse_attn_decode with the RoPE-row
+ * materialisation ([V41] "Serving-owned full RoPE tables") folded into the
+ * same launch: the query of row t is rotated by row position_ids[t] of the
+ * full tables, and that row is also written out, so a decode step needs no
+ * separate csa_materialize_rope_rows launch.
+ *
+ *   freqs_cos, freqs_sin  FP32 [table_capacity, rope_dim / 2], read only
+ *   position_ids          INT32 [T]: each row's RoPE position (as for
+ *                         csa_materialize_rope_rows; positions still gives
+ *                         the cache position); the three may be NULL when
+ *                         rope_dim = 0
+ *   rope_cos, rope_sin    FP32 [T, rope_dim / 2], written for t < num_tokens
+ *                         exactly as csa_materialize_rope_rows writes them
+ *                         (identity for a negative position, table row p bit
+ *                         for bit, untouched and CSA_EFLAG_POS_RANGE when
+ *                         p >= table_capacity); both NULL: not written
+ *
+ * Every other argument, the result and its arithmetic are those of
+ * csa_sparse_attn_decode (same workspace size): out and lse are bit for bit
+ * what csa_materialize_rope_rows followed by csa_sparse_attn_decode give for
+ * rows whose position lies inside the tables.  A row past the tables attends
+ * with the identity rotation.  CSA_ERR_SHAPE for table_capacity < 0;
+ * CSA_ERR_NULL for a missing table or position_ids with rope_dim > 0, or
+ * only one of rope_cos and rope_sin.
+ */
+int csa_sparse_attn_decode_rope(const uint16_t* q, const float* freqs_cos, const float* freqs_sin,
+                                int32_t table_capacity, const int32_t* position_ids,
+                                int32_t rope_dim, int32_t rope_offset,
+                                const uint16_t* cmp_kv, int32_t num_cmp_blocks,
+                                const int32_t* cmp_block_table, int32_t max_cmp_blocks,
+                                const int32_t* topk_idx, int32_t k, int32_t ratio,
+                                const uint16_t* win_kv, int32_t num_win_blocks,
+                                const int32_t* win_block_table, int32_t max_win_blocks,
+                                int32_t window, const float* attn_sink, float softmax_scale,
+                                const int32_t* query_start_loc, const int32_t* positions,
+                                int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
+                                uint16_t* out, float* lse, float* rope_cos, float* rope_sin,
+                                void* workspace, size_t workspace_bytes, int32_t* err,
+                                void* stream);
+
+/*
  * csa_sparse_attn_prefill -- the same operation and arguments as
  * csa_sparse_attn_decode, scheduled for many query rows (a prefill walk in
  * 128-token tiles, [MTP] "Deployment configuration"): one 512-thread

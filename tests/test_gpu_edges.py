@@ -181,7 +181,8 @@ def test_zero_tokens_writes_nothing():
     assert np.all(step.out.view(torch.int16).cpu().numpy() == 0x7FDE)
 
 
-def test_device_error_flags_match_oracle():
+@pytest.mark.parametrize("fuse_rope", [True, False])
+def test_device_error_flags_match_oracle(fuse_rope):
     csa = _csa()
     cfg = _ragged_cfg()
     x = dict(synthetic.make_inputs(cfg, seed=6).t)
@@ -189,7 +190,8 @@ def test_device_error_flags_match_oracle():
     x["cmp_block_table"][0, 1] = 10_000          # visible page of request 0 -> invalid block
     x["position_ids"] = x["position_ids"].copy()
     x["position_ids"][2] = cfg.rope_capacity + 3  # past the RoPE table
-    step = csa.step_for_config(cfg, x)
+    step = csa.step_for_config(cfg, x, fuse_rope=fuse_rope)
+    assert step.fuse_rope == fuse_rope
     _fill_sentinels(step)
     step.run()
     torch.cuda.synchronize()
@@ -206,6 +208,8 @@ def test_device_error_flags_match_oracle():
     step.t["query_start_loc"].copy_(torch.as_tensor(qsl_bad))
     step.err.zero_()
     # RoPE rows of the oracle: row 2 is untouched there too; use identity for it
+    # (the fused call gathers the rows again, flags row 2 again and rotates it
+    # by the identity)
     rc = torch.as_tensor(np.nan_to_num(o["rope_cos"], nan=1.0), device="cuda")
     rs = torch.as_tensor(np.nan_to_num(o["rope_sin"], nan=0.0), device="cuda")
     step.rope_cos.copy_(rc)
@@ -217,7 +221,7 @@ def test_device_error_flags_match_oracle():
                                     cfg.ratio, x["win_kv"], x["win_block_table"], cfg.W,
                                     x["attn_sink"], cfg.softmax_scale, qsl_bad, x["positions"],
                                     cfg.T)
-    assert int(step.err.item()) == oe
+    assert int(step.err.item()) == oe | (oracle.EFLAG_POS_RANGE if fuse_rope else 0)
     assert oe & oracle.EFLAG_TOPK_RANGE and oe & oracle.EFLAG_META
     H.check_attn(H.bf16_to_f64(step.out), oo, step.lse.cpu().numpy(), ol, "flags attn")
 

@@ -109,6 +109,33 @@ def test_attention_host_checks(lib):
     assert lib.csa_sparse_attn_decode(*base) == -5
 
 
+def test_attention_rope_tables_host_checks(lib):
+    """The decode call that gathers its rope rows from the full tables:
+    table and rope-row arguments are checked on the host, then the decode
+    call's own checks apply."""
+    f = lib.csa_sparse_attn_decode_rope
+    base = [FAKE, FAKE, FAKE, 1024, FAKE, 64, 448, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE, 2, FAKE,
+            2, 128, FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, FAKE, FAKE, None, 0,
+            None, None]
+    bad = list(base); bad[3] = -1                 # table capacity < 0
+    assert f(*bad) == -2
+    bad = list(base); bad[1] = None               # no cos table
+    assert f(*bad) == -1
+    bad = list(base); bad[4] = None               # no position ids
+    assert f(*bad) == -1
+    bad = list(base); bad[31] = None              # rope_cos without rope_sin
+    assert f(*bad) == -1
+    bad = list(base); bad[27] = 320               # D without a kernel
+    assert f(*bad) == -4
+    bad = list(base); bad[25] = 0                 # no active rows
+    assert f(*bad) == 0
+    bad = list(base); bad[12] = 2048              # split key lists need the workspace
+    assert f(*bad) == -5
+    bad = list(base); bad[5] = 0; bad[1] = bad[2] = bad[4] = None   # no rope span: no tables
+    bad[12] = 2048
+    assert f(*bad) == -5
+
+
 def test_attention_selection_bounds(lib):
     """A selection array holds at most 4096 entries per row; without one
     (every visible compressed row) k bounds the visible count up to 2^20, and
