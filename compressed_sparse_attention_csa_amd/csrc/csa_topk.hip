@@ -301,7 +301,6 @@ __device__ void block_select(const uint32_t (&key)[KPT], int nmine, int m, SelSh
   constexpr int NW = THREADS / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
   uint32_t live = nmine >= 32 ? 0xffffffffu : ((1u << nmine) - 1u);
   chosen = 0u;
   tie = 0u;
@@ -398,7 +397,6 @@ __device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared
   constexpr int NW = THREADS / 64;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
   uint32_t fmin = 0xffffffffu, fmax = 0u;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
