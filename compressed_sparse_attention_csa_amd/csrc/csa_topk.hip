@@ -63,10 +63,12 @@ constexpr int kMetaWords = 8;        // [0]: the row's sampled threshold key
 constexpr uint32_t kKeyNegInf = 0x007fffffu;
 constexpr uint32_t kKeyPosInf = 0xff800000u;
 
-// Long-row workspace (no state survives a call; every word is written before
-// it is read): per row a threshold word, one candidate count per wave
-// segment, and one (key, position) slot per score (a segment owns the slots
-// of its own positions, so no counter is shared between work-groups).
+// Long-row workspace (no state survives a call: a word is used only after
+// this call wrote it; the final kernel may fetch a segment's slots ahead of
+// its count and then drops those past it): per row a threshold word, one
+// candidate count per wave segment, and one (score bits, position) slot per
+// score (a segment owns the slots of its own positions, so no counter is
+// shared between work-groups).
 struct Workspace {
   uint32_t* meta;   // [T][kMetaWords]
   uint32_t* seg;    // [T][nseg]
@@ -509,9 +511,9 @@ struct Remap {
 };
 
 // Writes, in position order, every key better than or equal to the cut
-// (exactly m of them), then the -1 / -inf padding.
-template <int THREADS, int KPT, typename PosFn>
-__device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, const float* row,
+// (exactly m of them), then the -1 / -inf padding; val(j) is key j's score.
+template <int THREADS, int KPT, typename PosFn, typename ValFn>
+__device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, ValFn val_of,
                          int32_t* out_i, float* out_v, SelShared<THREADS>& sh, PosFn pos,
                          Remap rm) {
   const uint32_t ck = sh.cut[0], cp = sh.cut[1];
@@ -522,11 +524,11 @@ __device__ void emit_cut(const uint32_t (&key)[KPT], int nmine, int m, int k, co
                     (key[j] > ck || (key[j] == ck && static_cast<uint32_t>(pos(j)) <= cp));
     pick |= in ? (1u << j) : 0u;
   }
-  // the chosen scores are loaded before any is stored, so a thread's picks
-  // share one memory latency
+  // the chosen scores are fetched before any is stored, so a thread's picks
+  // share one latency
   float val[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) val[j] = (out_v && ((pick >> j) & 1u)) ? row[pos(j)] : 0.0f;
+  for (int j = 0; j < KPT; ++j) val[j] = (out_v && ((pick >> j) & 1u)) ? val_of(j) : 0.0f;
   int o = block_excl_scan<THREADS / 64>(__popc(pick), sh.wsum, nullptr);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
@@ -766,7 +768,8 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
         const int cn = max(0, min(cper, total - cbase));
         auto cpos = [&](int j) { return static_cast<int>(cand_p[cbase + j]); };
         if (find_cut<THREADS, CPT>(ck, cn, m, sh, cpos)) {
-          emit_cut<THREADS, CPT>(ck, cn, m, k, row, out_i, out_v, sh, cpos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
+          emit_cut<THREADS, CPT>(ck, cn, m, k, [&](int j) { return row[cpos(j)]; }, out_i, out_v,
+                                 sh, cpos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
           done = true;
         }
       }
@@ -775,7 +778,8 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
   }
   if (done) return;
   if (find_cut<THREADS, KPT>(key, nmine, m, sh, pos))
-    emit_cut<THREADS, KPT>(key, nmine, m, k, row, out_i, out_v, sh, pos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
+    emit_cut<THREADS, KPT>(key, nmine, m, k, [&](int j) { return row[pos(j)]; }, out_i, out_v, sh,
+                           pos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
   else
     select_whole_row<THREADS>(row, n, m, k, out_i, out_v, sh, Remap{rs.remap, rs.rgroup, rs.rstride, t});
 }
@@ -838,7 +842,8 @@ __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
 // kSub-position run and position order is (i, lane, component).
 struct ChunkKeys {
   uint32_t key[4 * kLLoads];
-  int first;   // position of key[0]
+  uint32_t raw[4 * kLLoads];   // the scores' bits
+  int first;                   // position of key[0]
 };
 
 __device__ __forceinline__ void load_chunk(const float* row, long long stride, int n, int c0,
@@ -855,19 +860,22 @@ __device__ __forceinline__ void load_chunk(const float* row, long long stride, i
   }
 #pragma unroll
   for (int i = 0; i < kLLoads; ++i) {
-    ck.key[4 * i] = order_key(v[i].x);
-    ck.key[4 * i + 1] = order_key(v[i].y);
-    ck.key[4 * i + 2] = order_key(v[i].z);
-    ck.key[4 * i + 3] = order_key(v[i].w);
+    ck.raw[4 * i] = __float_as_uint(v[i].x);
+    ck.raw[4 * i + 1] = __float_as_uint(v[i].y);
+    ck.raw[4 * i + 2] = __float_as_uint(v[i].z);
+    ck.raw[4 * i + 3] = __float_as_uint(v[i].w);
   }
+#pragma unroll
+  for (int j = 0; j < 4 * kLLoads; ++j) ck.key[j] = order_key(__uint_as_float(ck.raw[j]));
 }
 
 __device__ __forceinline__ bool in_span(const ChunkKeys& ck, int j, int n) {
   return ck.first + 256 * (j >> 2) + (j & 3) < n;
 }
 
-// Keep every key >= tau: each wave writes its kept (key, position) pairs, in
-// position order, into the slots of its own segment and its count into seg[].
+// Keep every key >= tau: each wave writes its kept (score bits, position)
+// pairs, in position order, into the slots of its own segment and its count
+// into seg[].
 __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
     const float* __restrict__ scores, long long stride, RowSpec rs,
     int num_tokens, Workspace ws) {
@@ -907,7 +915,7 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (in_span(ck, 4 * i + q, n) && ck.key[4 * i + q] >= tau) {
-        slots[o] = make_uint2(ck.key[4 * i + q], static_cast<uint32_t>(ck.first + 256 * i + q));
+        slots[o] = make_uint2(ck.raw[4 * i + q], static_cast<uint32_t>(ck.first + 256 * i + q));
         ++o;
       }
     }
@@ -919,7 +927,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
     int num_tokens, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_val, Workspace ws, int32_t* err) {
   __shared__ SelShared<kFThreads> sh;
-  __shared__ uint32_t ckey[kCap];
+  __shared__ uint32_t craw[kCap];   // candidate score bits
   __shared__ uint32_t cpos[kCap];
   __shared__ uint32_t segstart[kMaxSeg + 1];   // first candidate slot of each segment, then total
   const int t = blockIdx.x;
@@ -938,7 +946,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
     if (n <= kCap) {
       // short row: the row itself is the candidate list
       for (int i = tid; i < n; i += kFThreads) {
-        ckey[i] = order_key(row[i]);
+        craw[i] = __float_as_uint(row[i]);
         cpos[i] = static_cast<uint32_t>(i);
       }
       total = n;
@@ -949,6 +957,21 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       const int spt = (nseg + kFThreads - 1) / kFThreads;
       const uint32_t* seg = ws.seg + static_cast<size_t>(t) * ws.nseg;
       const uint2* cand = ws.cand + static_cast<size_t>(t) * stride;
+      // segment s is copied by tps threads (kFThreads / nseg rounded down
+      // to a power of two, at least 1), each taking every tps-th entry in
+      // batches of kBatch loads before any is stored.  The first batch of
+      // each thread's first segment is fetched with the counts, ahead of
+      // them (slots past a count are dropped), which saves a round trip
+      int tps = 1;
+      while (tps * 2 * nseg <= kFThreads) tps *= 2;
+      constexpr int kBatch = 8;
+      const int s0 = tid / tps;
+      uint2 pre[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const long long slot = static_cast<long long>(s0) * kSub + tid % tps + u * tps;
+        pre[u] = (s0 < nseg && slot < stride) ? cand[slot] : make_uint2(0u, 0u);
+      }
       int mine = 0;
       for (int i = 0; i < spt; ++i) {
         const int sidx = tid * spt + i;
@@ -958,9 +981,6 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       if (total < m || total > kCap) {
         whole_row = true;   // the sample misled: exact select over the row
       } else {
-        // segment s is copied by tps threads (kFThreads / nseg rounded down
-        // to a power of two, at least 1), each taking every tps-th entry;
-        // loads go out in batches of kBatch before any is stored
         for (int i = 0; i < spt; ++i) {
           const int sidx = tid * spt + i;
           if (sidx < nseg) {
@@ -970,14 +990,23 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
         }
         if (tid == 0) segstart[nseg] = static_cast<uint32_t>(total);
         __syncthreads();
-        int tps = 1;
-        while (tps * 2 * nseg <= kFThreads) tps *= 2;
-        constexpr int kBatch = 8;
-        for (int sidx = tid / tps; sidx < nseg; sidx += kFThreads / tps) {
+        for (int sidx = s0; sidx < nseg; sidx += kFThreads / tps) {
           const int d0 = static_cast<int>(segstart[sidx]);
           const int c = static_cast<int>(segstart[sidx + 1]) - d0;
           const uint2* src = cand + static_cast<size_t>(sidx) * kSub;
-          for (int q0 = tid % tps; q0 < c; q0 += kBatch * tps) {
+          int q0 = tid % tps;
+          if (sidx == s0) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+              const int q = q0 + u * tps;
+              if (q < c) {
+                craw[d0 + q] = pre[u].x;
+                cpos[d0 + q] = pre[u].y;
+              }
+            }
+            q0 += kBatch * tps;
+          }
+          for (; q0 < c; q0 += kBatch * tps) {
             uint2 e[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
@@ -988,7 +1017,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
             for (int u = 0; u < kBatch; ++u) {
               const int q = q0 + u * tps;
               if (q < c) {
-                ckey[d0 + q] = e[u].x;
+                craw[d0 + q] = e[u].x;
                 cpos[d0 + q] = e[u].y;
               }
             }
@@ -1004,11 +1033,15 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       const int base = tid * per;
       uint32_t key[kFPer];
 #pragma unroll
-      for (int j = 0; j < kFPer; ++j) key[j] = (j < per && base + j < total) ? ckey[base + j] : 0u;
+      for (int j = 0; j < kFPer; ++j)
+        key[j] = (j < per && base + j < total) ? order_key(__uint_as_float(craw[base + j])) : 0u;
       const int nmine = max(0, min(per, total - base));
       auto pos = [&](int j) { return static_cast<int>(cpos[base + j]); };
+      // the chosen scores come from the candidates' own bits, not the row
+      auto val = [&](int j) { return __uint_as_float(craw[base + j]); };
       if (find_cut<kFThreads, kFPer>(key, nmine, m, sh, pos))
-        emit_cut<kFThreads, kFPer>(key, nmine, m, k, row, out_i, out_v, sh, pos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
+        emit_cut<kFThreads, kFPer>(key, nmine, m, k, val, out_i, out_v, sh, pos,
+                                   Remap{rs.remap, rs.rgroup, rs.rstride, t});
       else
         select_whole_row<kFThreads>(row, n, m, k, out_i, out_v, sh, Remap{rs.remap, rs.rgroup, rs.rstride, t});
     }
