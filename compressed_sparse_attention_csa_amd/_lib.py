@@ -71,6 +71,10 @@ _SIGS["csa_sparse_attn_decode_mx"] = (
 _SIGS["csa_sparse_attn_decode_rope"] = (
     ctypes.c_int, [_P, _P, _P, _I32, _P] + _SIGS["csa_sparse_attn_decode"][1][3:28] + [_P, _P]
     + _SIGS["csa_sparse_attn_decode"][1][28:])
+# the low-bit decode arguments with the same replacement
+_SIGS["csa_sparse_attn_decode_mx_rope"] = (
+    ctypes.c_int, [_P, _P, _P, _I32, _P] + _SIGS["csa_sparse_attn_decode_mx"][1][3:30] + [_P, _P]
+    + _SIGS["csa_sparse_attn_decode_mx"][1][30:])
 _SIGS["csa_sparse_attn_noalloc_max_bytes"] = (_SZ, [])
 # the decode arguments without (workspace, workspace_bytes)
 _SIGS["csa_sparse_attn_decode_noalloc"] = (
@@ -335,6 +339,21 @@ def csa_sparse_attn_decode(*args, **kw) -> None:
     _attn("csa_sparse_attn_decode", *args, **kw)
 
 
+def _rope_tables_check(freqs_cos, freqs_sin, rope_cos, rope_sin, T):
+    """Full RoPE tables FP32 [capacity, half]; rope rows FP32 [T, half] or None."""
+    _need(freqs_cos, (torch.float32,), 2, "freqs_cos")
+    _need(freqs_sin, (torch.float32,), 2, "freqs_sin")
+    half = freqs_cos.shape[1]
+    if tuple(freqs_sin.shape) != tuple(freqs_cos.shape):
+        raise CsaError("freqs_cos and freqs_sin differ in shape")
+    for name, r in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+        if r is not None:
+            _need(r, (torch.float32,), 2, name)
+            if tuple(r.shape) != (T, half):
+                raise CsaError(f"{name}: expected {(T, half)}, got {tuple(r.shape)}")
+    return half
+
+
 def csa_sparse_attn_decode_rope(q, freqs_cos, freqs_sin, position_ids, rope_offset, cmp_kv,
                                 cmp_block_table, topk_idx, ratio, win_kv, win_block_table, window,
                                 attn_sink, softmax_scale, query_start_loc, positions, num_tokens,
@@ -346,17 +365,8 @@ def csa_sparse_attn_decode_rope(q, freqs_cos, freqs_sin, position_ids, rope_offs
     writes them as csa_materialize_rope_rows would."""
     _need(q, _BF16, 3, "q")
     _need(out, _BF16, 3, "out")
-    _need(freqs_cos, (torch.float32,), 2, "freqs_cos")
-    _need(freqs_sin, (torch.float32,), 2, "freqs_sin")
     T, H, D = q.shape
-    half = freqs_cos.shape[1]
-    if tuple(freqs_sin.shape) != tuple(freqs_cos.shape):
-        raise CsaError("freqs_cos and freqs_sin differ in shape")
-    for name, r in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
-        if r is not None:
-            _need(r, (torch.float32,), 2, name)
-            if tuple(r.shape) != (T, half):
-                raise CsaError(f"{name}: expected {(T, half)}, got {tuple(r.shape)}")
+    half = _rope_tables_check(freqs_cos, freqs_sin, rope_cos, rope_sin, T)
     if topk_idx is not None:
         k = topk_idx.shape[1]
     elif k is None:
@@ -396,15 +406,7 @@ def csa_sparse_attn_mx_workspace_bytes(T: int, H: int, D: int, k: int, window: i
     return int(load().csa_sparse_attn_mx_workspace_bytes(T, H, D, k, window))
 
 
-def csa_sparse_attn_decode_mx(q, rope_cos, rope_sin, rope_offset, cmp_fp4, cmp_scale,
-                              cmp_block_table, topk_idx, ratio, win_fp8, win_scale,
-                              win_block_table, window, attn_sink, softmax_scale, query_start_loc,
-                              positions, num_tokens, out, lse=None, workspace=None, err=None,
-                              stream=None, k=None) -> None:
-    """Decode attention over the low-bit KV planes: cmp_fp4 uint8 [blocks, 128,
-    D/2] with cmp_scale uint8 [blocks, 128, D/16] (E4M3), win_fp8 uint8
-    [blocks, 128, D] with win_scale uint8 [blocks, 128, D/32] (E8M0).  The
-    other arguments are csa_sparse_attn_decode's."""
+def _mx_planes(q, out, cmp_fp4, cmp_scale, win_fp8, win_scale):
     _need(q, _BF16, 3, "q")
     _need(out, _BF16, 3, "out")
     _need(win_fp8, (torch.uint8,), 3, "win_fp8")
@@ -420,19 +422,63 @@ def csa_sparse_attn_decode_mx(q, rope_cos, rope_sin, rope_offset, cmp_fp4, cmp_s
                 or tuple(cmp_scale.shape) != (cmp_fp4.shape[0], PAGE, D // 16)):
             raise CsaError(f"compressed planes {tuple(cmp_fp4.shape)} / "
                            f"{tuple(cmp_scale.shape)} do not match D = {D}")
+    return T, H, D
+
+
+def _mx_tail(cmp_fp4, cmp_scale, cmp_block_table, topk_idx, k, ratio, win_fp8, win_scale,
+             win_block_table, window, attn_sink, softmax_scale, query_start_loc, positions, T,
+             num_tokens, H, D):
+    """The arguments from cmp_fp4 to D, shared by both low-bit decode calls."""
     if topk_idx is not None:
         k = topk_idx.shape[1]
     elif k is None:
         raise CsaError("k is required when topk_idx is None")
-    rope_dim = 2 * rope_cos.shape[1]
+    return [_ptr(cmp_fp4), _ptr(cmp_scale), 0 if cmp_fp4 is None else cmp_fp4.shape[0],
+            _ptr(cmp_block_table), 0 if cmp_block_table is None else cmp_block_table.shape[1],
+            _ptr(topk_idx), int(k), int(ratio), _ptr(win_fp8), _ptr(win_scale), win_fp8.shape[0],
+            _ptr(win_block_table), win_block_table.shape[1], int(window), _ptr(attn_sink),
+            float(softmax_scale), _ptr(query_start_loc), _ptr(positions),
+            query_start_loc.shape[0] - 1, T, int(num_tokens), H, D]
+
+
+def csa_sparse_attn_decode_mx(q, rope_cos, rope_sin, rope_offset, cmp_fp4, cmp_scale,
+                              cmp_block_table, topk_idx, ratio, win_fp8, win_scale,
+                              win_block_table, window, attn_sink, softmax_scale, query_start_loc,
+                              positions, num_tokens, out, lse=None, workspace=None, err=None,
+                              stream=None, k=None) -> None:
+    """Decode attention over the low-bit KV planes: cmp_fp4 uint8 [blocks, 128,
+    D/2] with cmp_scale uint8 [blocks, 128, D/16] (E4M3), win_fp8 uint8
+    [blocks, 128, D] with win_scale uint8 [blocks, 128, D/32] (E8M0).  The
+    other arguments are csa_sparse_attn_decode's."""
+    T, H, D = _mx_planes(q, out, cmp_fp4, cmp_scale, win_fp8, win_scale)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().csa_sparse_attn_decode_mx(
-        _ptr(q), _ptr(rope_cos), _ptr(rope_sin), rope_dim, int(rope_offset), _ptr(cmp_fp4),
-        _ptr(cmp_scale), 0 if cmp_fp4 is None else cmp_fp4.shape[0], _ptr(cmp_block_table),
-        0 if cmp_block_table is None else cmp_block_table.shape[1], _ptr(topk_idx), int(k),
-        int(ratio), _ptr(win_fp8), _ptr(win_scale), win_fp8.shape[0], _ptr(win_block_table),
-        win_block_table.shape[1], int(window), _ptr(attn_sink), float(softmax_scale),
-        _ptr(query_start_loc), _ptr(positions), query_start_loc.shape[0] - 1, T,
-        int(num_tokens), H, D, _ptr(out), _ptr(lse), _ptr(workspace), wsb, _ptr(err),
-        _stream(stream))
+        _ptr(q), _ptr(rope_cos), _ptr(rope_sin), 2 * rope_cos.shape[1], int(rope_offset),
+        *_mx_tail(cmp_fp4, cmp_scale, cmp_block_table, topk_idx, k, ratio, win_fp8, win_scale,
+                  win_block_table, window, attn_sink, softmax_scale, query_start_loc, positions,
+                  T, num_tokens, H, D),
+        _ptr(out), _ptr(lse), _ptr(workspace), wsb, _ptr(err), _stream(stream))
     _check(st, "csa_sparse_attn_decode_mx")
+
+
+def csa_sparse_attn_decode_mx_rope(q, freqs_cos, freqs_sin, position_ids, rope_offset, cmp_fp4,
+                                   cmp_scale, cmp_block_table, topk_idx, ratio, win_fp8,
+                                   win_scale, win_block_table, window, attn_sink, softmax_scale,
+                                   query_start_loc, positions, num_tokens, out, lse=None,
+                                   rope_cos=None, rope_sin=None, workspace=None, err=None,
+                                   stream=None, k=None) -> None:
+    """csa_sparse_attn_decode_mx gathering each row's rope row from the full
+    tables (as csa_sparse_attn_decode_rope), writing them to rope_cos /
+    rope_sin when given."""
+    T, H, D = _mx_planes(q, out, cmp_fp4, cmp_scale, win_fp8, win_scale)
+    half = _rope_tables_check(freqs_cos, freqs_sin, rope_cos, rope_sin, T)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().csa_sparse_attn_decode_mx_rope(
+        _ptr(q), _ptr(freqs_cos), _ptr(freqs_sin), freqs_cos.shape[0], _ptr(position_ids),
+        2 * half, int(rope_offset),
+        *_mx_tail(cmp_fp4, cmp_scale, cmp_block_table, topk_idx, k, ratio, win_fp8, win_scale,
+                  win_block_table, window, attn_sink, softmax_scale, query_start_loc, positions,
+                  T, num_tokens, H, D),
+        _ptr(out), _ptr(lse), _ptr(rope_cos), _ptr(rope_sin), _ptr(workspace), wsb, _ptr(err),
+        _stream(stream))
+    _check(st, "csa_sparse_attn_decode_mx_rope")

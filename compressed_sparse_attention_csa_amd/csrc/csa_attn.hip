@@ -1776,6 +1776,29 @@ extern "C" int csa_sparse_attn_decode_mx(
                          /*static_scratch=*/false, /*mx=*/true, cmp_scale, win_scale);
 }
 
+extern "C" int csa_sparse_attn_decode_mx_rope(
+    const uint16_t* q, const float* freqs_cos, const float* freqs_sin, int32_t table_capacity,
+    const int32_t* position_ids, int32_t rope_dim, int32_t rope_offset, const uint8_t* cmp_fp4,
+    const uint8_t* cmp_scale, int32_t num_cmp_blocks, const int32_t* cmp_block_table,
+    int32_t max_cmp_blocks, const int32_t* topk_idx, int32_t k, int32_t ratio,
+    const uint8_t* win_fp8, const uint8_t* win_scale, int32_t num_win_blocks,
+    const int32_t* win_block_table, int32_t max_win_blocks, int32_t window,
+    const float* attn_sink, float softmax_scale, const int32_t* query_start_loc,
+    const int32_t* positions, int32_t B, int32_t T, int32_t num_tokens, int32_t H, int32_t D,
+    uint16_t* out, float* lse, float* rope_cos, float* rope_sin, void* workspace,
+    size_t workspace_bytes, int32_t* err, void* stream) {
+  if (table_capacity < 0) return CSA_ERR_SHAPE;
+  if (rope_dim > 0 && (!freqs_cos || !freqs_sin || !position_ids)) return CSA_ERR_NULL;
+  if (rope_dim == 0) freqs_cos = freqs_sin = nullptr;   // no rope span: nothing to gather
+  return csa::attn_entry(false, q, nullptr, nullptr, rope_dim, rope_offset, cmp_fp4,
+                         num_cmp_blocks, cmp_block_table, max_cmp_blocks, topk_idx, k, ratio,
+                         win_fp8, num_win_blocks, win_block_table, max_win_blocks, window,
+                         attn_sink, softmax_scale, query_start_loc, positions, B, T, num_tokens,
+                         H, D, out, lse, workspace, workspace_bytes, err, stream,
+                         /*static_scratch=*/false, /*mx=*/true, cmp_scale, win_scale,
+                         position_ids, freqs_cos, freqs_sin, table_capacity, rope_cos, rope_sin);
+}
+
 extern "C" size_t csa_sparse_attn_noalloc_max_bytes(void) { return kScratchBytes; }
 
 extern "C" int csa_sparse_attn_decode_noalloc(

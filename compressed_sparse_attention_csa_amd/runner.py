@@ -4,7 +4,7 @@
 workspace up front, and then runs the path as four library calls on one
 stream: RoPE rows -> indexer scores -> top-k -> sparse attention (RoPE rows ->
 attention for the layers without an indexer), with the ratio-2 compressor's
-publication after the RoPE rows when the step carries it.  BF16 decode steps
+publication after the RoPE rows when the step carries it.  Decode steps
 without the compressor gather the RoPE rows inside the attention launch
 instead (three launches).  It only moves memory and passes pointers; all
 arithmetic runs in libcsa.so.
@@ -74,11 +74,10 @@ class CsaStep:
         if self.compress and (kv_format != "bf16" or ratio != 2):
             raise ValueError("the compressor publishes BF16 rows at ratio 2")
         self.rms_eps = float(rms_eps)
-        # BF16 decode steps without the compressor gather their rope rows in
-        # the attention launch (csa_sparse_attn_decode_rope), which also
-        # writes them out: one launch fewer per step
-        self.fuse_rope = (bool(fuse_rope) and not prefill and kv_format == "bf16"
-                          and not self.compress)
+        # decode steps without the compressor gather their rope rows in the
+        # attention launch (csa_sparse_attn_decode_rope / _mx_rope), which
+        # also writes them out: one launch fewer per step
+        self.fuse_rope = bool(fuse_rope) and not prefill and not self.compress
         f32 = dict(dtype=torch.float32, device=dev)
         half = self.t["freqs_cos"].shape[1]
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -198,6 +197,15 @@ class CsaStep:
         fn = _lib.csa_sparse_attn_prefill if self.prefill else _lib.csa_sparse_attn_decode
         if topk_idx is None and self.mode in ("csa", "reindex", "hier_full"):
             topk_idx = self.topk_idx
+        if self.kv_format == "mx" and self.fuse_rope:
+            _lib.csa_sparse_attn_decode_mx_rope(
+                t["q"], t["freqs_cos"], t["freqs_sin"], t["position_ids"], self.rope_offset,
+                t["cmp_fp4"], t["cmp_scale"], t["cmp_block_table"], topk_idx, self.ratio,
+                t["win_fp8"], t["win_scale"], t["win_block_table"], self.window, t["attn_sink"],
+                self.softmax_scale, t["query_start_loc"], t["positions"], self.num_tokens,
+                self.out, lse=self.lse, rope_cos=self.rope_cos, rope_sin=self.rope_sin,
+                workspace=self.attn_ws, err=self.err, stream=stream, k=self.k)
+            return
         if self.kv_format == "mx":
             _lib.csa_sparse_attn_decode_mx(
                 t["q"], self.rope_cos, self.rope_sin, self.rope_offset, t["cmp_fp4"],

@@ -380,6 +380,31 @@ int csa_sparse_attn_decode_mx(const uint16_t* q, const float* rope_cos, const fl
                               int32_t* err, void* stream);
 
 /*
+ * csa_sparse_attn_decode_mx_rope -- csa_sparse_attn_decode_mx with the RoPE
+ * rows gathered from the full tables in the same launch, exactly as
+ * csa_sparse_attn_decode_rope does for the BF16 pools: freqs_cos / freqs_sin
+ * / table_capacity / position_ids replace the rope rows, and rope_cos /
+ * rope_sin (both or neither) receive them.  Every other argument, check and
+ * flag is csa_sparse_attn_decode_mx's.
+ */
+int csa_sparse_attn_decode_mx_rope(const uint16_t* q, const float* freqs_cos,
+                                   const float* freqs_sin, int32_t table_capacity,
+                                   const int32_t* position_ids, int32_t rope_dim,
+                                   int32_t rope_offset, const uint8_t* cmp_fp4,
+                                   const uint8_t* cmp_scale, int32_t num_cmp_blocks,
+                                   const int32_t* cmp_block_table, int32_t max_cmp_blocks,
+                                   const int32_t* topk_idx, int32_t k, int32_t ratio,
+                                   const uint8_t* win_fp8, const uint8_t* win_scale,
+                                   int32_t num_win_blocks, const int32_t* win_block_table,
+                                   int32_t max_win_blocks, int32_t window,
+                                   const float* attn_sink, float softmax_scale,
+                                   const int32_t* query_start_loc, const int32_t* positions,
+                                   int32_t B, int32_t T, int32_t num_tokens, int32_t H,
+                                   int32_t D, uint16_t* out, float* lse, float* rope_cos,
+                                   float* rope_sin, void* workspace, size_t workspace_bytes,
+                                   int32_t* err, void* stream);
+
+/*
  * csa_sparse_attn_decode_noalloc -- csa_sparse_attn_decode for callers that
  * cannot allocate device memory or pass a workspace: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same

@@ -1,11 +1,13 @@
 """The decode attention that gathers its rope rows from the full tables
-(csa_sparse_attn_decode_rope, pypto-lib "DeepSeek V4.1 Flash", section
+(csa_sparse_attn_decode_rope and, over the low-bit KV planes,
+csa_sparse_attn_decode_mx_rope: pypto-lib "DeepSeek V4.1 Flash", section
 "Serving-owned full RoPE tables" folded into the attention launch), through
 the C ABI: the rope rows it writes equal the oracle's materialisation bit for
 bit, and its output and lse equal, bit for bit, those of the separate
-launches (csa_materialize_rope_rows, then csa_sparse_attn_decode) on the same
-inputs -- on the short-list and split-ring schedules, HCA and SWA layers, a
-padded batch, rows whose RoPE position is -1, and rows past the tables."""
+launches (csa_materialize_rope_rows, then the attention call) on the same
+inputs -- on the short-list and split-ring schedules, HCA and SWA layers,
+the low-bit planes, a padded batch, rows whose RoPE position is -1, and rows
+past the tables."""
 import numpy as np
 import pytest
 
@@ -56,7 +58,7 @@ def _pair(cfg, x, nt=None):
     return sep, fused
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5", "c6", "c7", "c8"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5", "c6", "c7", "c8", "c12", "c13", "c14"])
 def test_fused_rope_equals_separate_launches(name):
     print(f"[rope-fused] {name}", flush=True)
     cfg = synthetic.get(name)

@@ -136,6 +136,28 @@ def test_attention_rope_tables_host_checks(lib):
     assert f(*bad) == -5
 
 
+def test_attention_mx_rope_tables_host_checks(lib):
+    """The low-bit decode call with table-gathered rope rows: the table
+    arguments are checked first, then the low-bit call's own checks."""
+    f = lib.csa_sparse_attn_decode_mx_rope
+    base = [FAKE, FAKE, FAKE, 1024, FAKE, 64, 448, FAKE, FAKE, 4, FAKE, 2, FAKE, 512, 2, FAKE,
+            FAKE, 2, FAKE, 2, 128, FAKE, 0.04, FAKE, FAKE, 1, 8, 8, 64, 512, FAKE, None, FAKE,
+            FAKE, None, 0, None, None]
+    assert len(base) == 38
+    bad = list(base); bad[3] = -1                 # table capacity < 0
+    assert f(*bad) == -2
+    bad = list(base); bad[2] = None               # no sin table
+    assert f(*bad) == -1
+    bad = list(base); bad[4] = None               # no position ids
+    assert f(*bad) == -1
+    bad = list(base); bad[32] = None              # rope_sin without rope_cos
+    assert f(*bad) == -1
+    bad = list(base); bad[8] = None               # a compressed plane without its scales
+    assert f(*bad) == -1
+    bad = list(base); bad[27] = 0                 # no active rows
+    assert f(*bad) == 0
+
+
 def test_attention_selection_bounds(lib):
     """A selection array holds at most 4096 entries per row; without one
     (every visible compressed row) k bounds the visible count up to 2^20, and
