@@ -110,12 +110,14 @@ def work_model(cfg, x, topk_idx: np.ndarray, fused_rope: bool = False):
     index keys of every visible position once per request, every unique
     gathered KV row once per request, Q, O, lse and small metadata; with the
     compressor, its bytes on top).  fused_rope: the attention launch gathers
-    the rope rows from the tables and writes them (no rope stage)."""
+    the query rope rows from the tables and writes them, and the compressor
+    reads its table rows itself (no rope stage)."""
     T, H, D, R, Hi, Di, k = cfg.T, cfg.H, cfg.D, cfg.R, cfg.Hi, cfg.Di, cfg.k
     mode = getattr(cfg, "mode", "csa")
     if mode == "compress":   # the publication alone: rope rows of the pair starts, then it
         cb = compress_bytes(cfg, x)
-        st = {"rope": 8 * T * R + 4 * T, "compress_pairs": cb}
+        st = {"compress_pairs": cb} if fused_rope else {"rope": 8 * T * R + 4 * T,
+                                                        "compress_pairs": cb}
         return dict(stage_bytes=st, step_bytes=cb, flops={}, kv_rows=0, kv_bytes=0,
                     idx_keys=0, pairs=0)
     qsl = np.asarray(x["query_start_loc"])
@@ -188,7 +190,8 @@ def work_model(cfg, x, topk_idx: np.ndarray, fused_rope: bool = False):
         st["attn"] += 4 * T * R + 4 * T
         del st["rope"]
     if getattr(cfg, "compress", False):
-        st["rope"] += 8 * T * R + 4 * T      # the pair starts' rope rows, same launch
+        if "rope" in st:
+            st["rope"] += 8 * T * R + 4 * T      # the pair starts' rope rows, same launch
         st["compress_pairs"] = compress_bytes(cfg, x)
         step += st["compress_pairs"]
     flops = {"attn": pairs * H * D * 4,

@@ -15,6 +15,6 @@ from ._lib import (  # noqa: F401
     csa_index_score_mxfp4, csa_sparse_attn_decode_noalloc, csa_sparse_attn_noalloc_max_bytes,
     csa_sparse_attn_decode_mx, csa_sparse_attn_mx_workspace_bytes, csa_index_score_fp8,
     csa_inverse_rope, csa_compress_pairs, csa_sparse_attn_decode_rope,
-    csa_sparse_attn_decode_mx_rope,
+    csa_sparse_attn_decode_mx_rope, csa_compress_pairs_rope,
 )
 from .runner import CsaStep, step_for_config  # noqa: F401

@@ -59,6 +59,11 @@ _SIGS["csa_index_score_fp8"] = _SIGS["csa_index_score"]
 _SIGS["csa_compress_pairs"] = (ctypes.c_int, [_P, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P,
                                               _I32, _I32, _P, _F32, _P, _P, _I32, _I32, _P, _I32,
                                               _P, _I32, _P, _P])
+# the compressor's arguments with (freqs_cos, freqs_sin, table_capacity,
+# rope_position_ids) in place of the rope rows
+_SIGS["csa_compress_pairs_rope"] = (
+    ctypes.c_int, _SIGS["csa_compress_pairs"][1][:14] + [_P, _P, _I32, _P]
+    + _SIGS["csa_compress_pairs"][1][16:])
 _SIGS["csa_inverse_rope"] = (ctypes.c_int, [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                             _P])
 _SIGS["csa_sparse_attn_mx_workspace_bytes"] = _SIGS["csa_sparse_attn_workspace_bytes"]
@@ -173,6 +178,30 @@ def csa_compress_pairs(kv_proj, gate, query_start_loc, positions, num_tokens, st
         _ptr(cmp_kv), cmp_kv.shape[0], _ptr(cmp_block_table), cmp_block_table.shape[1],
         _ptr(err), _stream(stream))
     _check(st, "csa_compress_pairs")
+
+
+def csa_compress_pairs_rope(kv_proj, gate, query_start_loc, positions, num_tokens,
+                            state_block_table, state_cache, rms_gamma, rms_eps, freqs_cos,
+                            freqs_sin, rope_position_ids, rope_offset, cmp_kv, cmp_block_table,
+                            err=None, stream=None) -> None:
+    """csa_compress_pairs with each token's rope row taken from the full tables
+    (FP32 [capacity, rope_dim / 2]) at rope_position_ids[t]."""
+    _need(kv_proj, (torch.float32,), 2, "kv_proj")
+    _need(gate, (torch.float32,), 2, "gate")
+    _need(state_cache, (torch.float32,), 3, "state_cache")
+    _need(cmp_kv, _BF16, 3, "cmp_kv")
+    T, D = kv_proj.shape
+    if tuple(gate.shape) != (T, D) or state_cache.shape[2] != 2 * D or cmp_kv.shape[2] != D:
+        raise CsaError("kv_proj, gate, state_cache and cmp_kv disagree on D")
+    half = _rope_tables_check(freqs_cos, freqs_sin, None, None, T)
+    st = load().csa_compress_pairs_rope(
+        _ptr(kv_proj), _ptr(gate), D, _ptr(query_start_loc), _ptr(positions),
+        query_start_loc.shape[0] - 1, T, int(num_tokens), _ptr(state_block_table),
+        _ptr(state_cache), state_cache.shape[0], state_cache.shape[1], _ptr(rms_gamma),
+        float(rms_eps), _ptr(freqs_cos), _ptr(freqs_sin), freqs_cos.shape[0],
+        _ptr(rope_position_ids), 2 * half, int(rope_offset), _ptr(cmp_kv), cmp_kv.shape[0],
+        _ptr(cmp_block_table), cmp_block_table.shape[1], _ptr(err), _stream(stream))
+    _check(st, "csa_compress_pairs_rope")
 
 
 def csa_inverse_rope(inp, out, rope_cos, rope_sin, rope_offset, num_tokens, stream=None) -> None:

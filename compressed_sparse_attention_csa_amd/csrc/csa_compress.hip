@@ -38,6 +38,13 @@ struct CompressArgs {
   float eps;
   const float* rcos;    // [T][half]: the rope row of each token's pair start
   const float* rsin;
+  // or the full tables [tab_cap][half] (rcos NULL): row rope_pos[t], the
+  // identity rotation for a negative position, and for one past the tables
+  // (flagged)
+  const int32_t* rope_pos;
+  const float* tab_cos;
+  const float* tab_sin;
+  int tab_cap;
   int half;
   int rope_offset;
   uint16_t* cmp;        // [ncb][128][D] BF16
@@ -64,6 +71,13 @@ __global__ void __launch_bounds__(kCmpLanes) compress_pairs_kernel(CompressArgs 
   const int qv = qsl_lane_load(a.qsl, a.B);
   const int p = a.pos[t];
   const bool odd = p >= 0 && (p & 1) == 1;
+  // the rope row of the pair start: row t of the rope rows, or row rp of the
+  // full tables (negative: identity; past the tables: flagged as the
+  // materialisation flags it, identity here)
+  const int rp = a.tab_cos ? a.rope_pos[t] : -1;
+  if (a.tab_cos && a.half > 0 && rp >= a.tab_cap && lane == 0)
+    flag_error(a.err, CSA_EFLAG_POS_RANGE);
+  const bool tab_row = a.tab_cos && rp >= 0 && rp < a.tab_cap;
   float2 k0[NCH], g0[NCH], k1[NCH], g1[NCH], gm[NCH], rot[NCH];
   uint32_t in_rope = 0;           // bit m: chunk m's pair lies in the rope span
   if (odd) {
@@ -83,8 +97,15 @@ __global__ void __launch_bounds__(kCmpLanes) compress_pairs_kernel(CompressArgs 
         gm[m] = *reinterpret_cast<const float2*>(a.gamma + c);
         const int rr = c - a.rope_offset;
         if (rr >= 0 && rr < 2 * a.half) {
-          const long long ri = static_cast<long long>(t) * a.half + (rr >> 1);
-          rot[m] = make_float2(a.rcos[ri], a.rsin[ri]);
+          if (!a.tab_cos) {
+            const long long ri = static_cast<long long>(t) * a.half + (rr >> 1);
+            rot[m] = make_float2(a.rcos[ri], a.rsin[ri]);
+          } else if (tab_row) {
+            const long long ri = static_cast<long long>(rp) * a.half + (rr >> 1);
+            rot[m] = make_float2(a.tab_cos[ri], a.tab_sin[ri]);
+          } else {
+            rot[m] = make_float2(1.0f, 0.0f);
+          }
           in_rope |= 1u << m;
         }
       }
@@ -177,6 +198,81 @@ __global__ void __launch_bounds__(kCmpLanes) compress_pairs_kernel(CompressArgs 
   }
 }
 
+int compress_entry(const float* kv_proj, const float* gate, int32_t D,
+                   const int32_t* query_start_loc, const int32_t* positions, int32_t B, int32_t T,
+                   int32_t num_tokens, const int32_t* state_block_table, float* state_cache,
+                   int32_t num_state_blocks, int32_t state_capacity, const float* rms_gamma,
+                   float rms_eps, const float* rope_cos, const float* rope_sin,
+                   const float* tab_cos, const float* tab_sin, int32_t tab_cap,
+                   const int32_t* rope_pos, int32_t rope_dim, int32_t rope_offset,
+                   uint16_t* cmp_kv, int32_t num_cmp_blocks, const int32_t* cmp_block_table,
+                   int32_t max_cmp_blocks, int32_t* err, void* stream) {
+  const bool tables = tab_cos || tab_sin || rope_pos;
+  if (T < 0 || B < 0 || D < 0 || num_state_blocks < 0 || num_cmp_blocks < 0 ||
+      max_cmp_blocks < 0 || rope_dim < 0 || rope_offset < 0 || tab_cap < 0)
+    return CSA_ERR_SHAPE;
+  if (num_tokens < 0 || num_tokens > T || state_capacity < 1) return CSA_ERR_RANGE;
+  if ((D & 1) || D > 2048 || (rope_dim & 1) || (rope_offset & 1) ||
+      rope_offset + rope_dim > D || !(rms_eps >= 0.0f))
+    return CSA_ERR_UNSUPPORTED;
+  if (num_tokens == 0 || D == 0) return CSA_OK;
+  if (!kv_proj || !gate || !query_start_loc || !positions || !state_block_table ||
+      !rms_gamma || !cmp_block_table)
+    return CSA_ERR_NULL;
+  if (rope_dim > 0 && (tables ? (!tab_cos || !tab_sin || !rope_pos) : (!rope_cos || !rope_sin)))
+    return CSA_ERR_NULL;
+  if ((num_state_blocks > 0 && !state_cache) || (num_cmp_blocks > 0 && !cmp_kv))
+    return CSA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(kv_proj) | reinterpret_cast<uintptr_t>(gate) |
+       reinterpret_cast<uintptr_t>(state_cache) | reinterpret_cast<uintptr_t>(rms_gamma) |
+       reinterpret_cast<uintptr_t>(cmp_kv)) & 7)
+    return CSA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(num_cmp_blocks) * kPage >= (1ll << 31)) return CSA_ERR_SHAPE;
+  CompressArgs a{};
+  a.kv = kv_proj;
+  a.gate = gate;
+  a.D = D;
+  a.qsl = query_start_loc;
+  a.pos = positions;
+  a.B = B;
+  a.num_tokens = num_tokens;
+  a.sbt = state_block_table;
+  a.state = state_cache;
+  a.nsb = num_state_blocks;
+  a.cap = state_capacity;
+  a.gamma = rms_gamma;
+  a.eps = rms_eps;
+  if (tables && rope_dim > 0) {
+    a.rope_pos = rope_pos;
+    a.tab_cos = tab_cos;
+    a.tab_sin = tab_sin;
+    a.tab_cap = tab_cap;
+  } else if (!tables) {
+    a.rcos = rope_cos;
+    a.rsin = rope_sin;
+  }
+  a.half = rope_dim / 2;
+  a.rope_offset = rope_offset;
+  a.cmp = cmp_kv;
+  a.ncb = num_cmp_blocks;
+  a.cbt = cmp_block_table;
+  a.max_cb = max_cmp_blocks;
+  a.err = err;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(num_tokens)), block(kCmpLanes);
+  if (D <= 128)
+    hipLaunchKernelGGL(compress_pairs_kernel<1>, grid, block, 0, st, a);
+  else if (D <= 256)
+    hipLaunchKernelGGL(compress_pairs_kernel<2>, grid, block, 0, st, a);
+  else if (D <= 512)
+    hipLaunchKernelGGL(compress_pairs_kernel<4>, grid, block, 0, st, a);
+  else if (D <= 1024)
+    hipLaunchKernelGGL(compress_pairs_kernel<8>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(compress_pairs_kernel<16>, grid, block, 0, st, a);
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 }  // namespace csa
@@ -191,58 +287,32 @@ extern "C" int csa_compress_pairs(const float* kv_proj, const float* gate, int32
                                   uint16_t* cmp_kv, int32_t num_cmp_blocks,
                                   const int32_t* cmp_block_table, int32_t max_cmp_blocks,
                                   int32_t* err, void* stream) {
-  if (T < 0 || B < 0 || D < 0 || num_state_blocks < 0 || num_cmp_blocks < 0 ||
-      max_cmp_blocks < 0 || rope_dim < 0 || rope_offset < 0)
-    return CSA_ERR_SHAPE;
-  if (num_tokens < 0 || num_tokens > T || state_capacity < 1) return CSA_ERR_RANGE;
-  if ((D & 1) || D > 2048 || (rope_dim & 1) || (rope_offset & 1) ||
-      rope_offset + rope_dim > D || !(rms_eps >= 0.0f))
-    return CSA_ERR_UNSUPPORTED;
-  if (num_tokens == 0 || D == 0) return CSA_OK;
-  if (!kv_proj || !gate || !query_start_loc || !positions || !state_block_table ||
-      !rms_gamma || !cmp_block_table || (rope_dim > 0 && (!rope_cos || !rope_sin)))
+  return csa::compress_entry(kv_proj, gate, D, query_start_loc, positions, B, T, num_tokens,
+                             state_block_table, state_cache, num_state_blocks, state_capacity,
+                             rms_gamma, rms_eps, rope_cos, rope_sin, nullptr, nullptr, 0, nullptr,
+                             rope_dim, rope_offset, cmp_kv, num_cmp_blocks, cmp_block_table,
+                             max_cmp_blocks, err, stream);
+}
+
+extern "C" int csa_compress_pairs_rope(const float* kv_proj, const float* gate, int32_t D,
+                                       const int32_t* query_start_loc, const int32_t* positions,
+                                       int32_t B, int32_t T, int32_t num_tokens,
+                                       const int32_t* state_block_table, float* state_cache,
+                                       int32_t num_state_blocks, int32_t state_capacity,
+                                       const float* rms_gamma, float rms_eps,
+                                       const float* freqs_cos, const float* freqs_sin,
+                                       int32_t table_capacity, const int32_t* rope_position_ids,
+                                       int32_t rope_dim, int32_t rope_offset, uint16_t* cmp_kv,
+                                       int32_t num_cmp_blocks, const int32_t* cmp_block_table,
+                                       int32_t max_cmp_blocks, int32_t* err, void* stream) {
+  if (rope_dim > 0 && (!freqs_cos || !freqs_sin || !rope_position_ids)) {
+    // checked here: without a table the shared entry would read rope rows
+    if (T < 0 || B < 0 || D < 0 || table_capacity < 0) return CSA_ERR_SHAPE;
     return CSA_ERR_NULL;
-  if ((num_state_blocks > 0 && !state_cache) || (num_cmp_blocks > 0 && !cmp_kv))
-    return CSA_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(kv_proj) | reinterpret_cast<uintptr_t>(gate) |
-       reinterpret_cast<uintptr_t>(state_cache) | reinterpret_cast<uintptr_t>(rms_gamma) |
-       reinterpret_cast<uintptr_t>(cmp_kv)) & 7)
-    return CSA_ERR_UNSUPPORTED;
-  if (static_cast<long long>(num_cmp_blocks) * csa::kPage >= (1ll << 31)) return CSA_ERR_SHAPE;
-  csa::CompressArgs a{};
-  a.kv = kv_proj;
-  a.gate = gate;
-  a.D = D;
-  a.qsl = query_start_loc;
-  a.pos = positions;
-  a.B = B;
-  a.num_tokens = num_tokens;
-  a.sbt = state_block_table;
-  a.state = state_cache;
-  a.nsb = num_state_blocks;
-  a.cap = state_capacity;
-  a.gamma = rms_gamma;
-  a.eps = rms_eps;
-  a.rcos = rope_cos;
-  a.rsin = rope_sin;
-  a.half = rope_dim / 2;
-  a.rope_offset = rope_offset;
-  a.cmp = cmp_kv;
-  a.ncb = num_cmp_blocks;
-  a.cbt = cmp_block_table;
-  a.max_cb = max_cmp_blocks;
-  a.err = err;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(num_tokens)), block(csa::kCmpLanes);
-  if (D <= 128)
-    hipLaunchKernelGGL(csa::compress_pairs_kernel<1>, grid, block, 0, st, a);
-  else if (D <= 256)
-    hipLaunchKernelGGL(csa::compress_pairs_kernel<2>, grid, block, 0, st, a);
-  else if (D <= 512)
-    hipLaunchKernelGGL(csa::compress_pairs_kernel<4>, grid, block, 0, st, a);
-  else if (D <= 1024)
-    hipLaunchKernelGGL(csa::compress_pairs_kernel<8>, grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL(csa::compress_pairs_kernel<16>, grid, block, 0, st, a);
-  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
+  }
+  return csa::compress_entry(kv_proj, gate, D, query_start_loc, positions, B, T, num_tokens,
+                             state_block_table, state_cache, num_state_blocks, state_capacity,
+                             rms_gamma, rms_eps, nullptr, nullptr, freqs_cos, freqs_sin,
+                             table_capacity, rope_position_ids, rope_dim, rope_offset, cmp_kv,
+                             num_cmp_blocks, cmp_block_table, max_cmp_blocks, err, stream);
 }

@@ -5,8 +5,8 @@ workspace up front, and then runs the path as four library calls on one
 stream: RoPE rows -> indexer scores -> top-k -> sparse attention (RoPE rows ->
 attention for the layers without an indexer), with the ratio-2 compressor's
 publication after the RoPE rows when the step carries it.  Decode steps
-without the compressor gather the RoPE rows inside the attention launch
-instead (three launches).  It only moves memory and passes pointers; all
+gather the RoPE rows inside the attention launch instead, and the compressor
+inside its own launch, so only prefill keeps the separate RoPE launch.  It only moves memory and passes pointers; all
 arithmetic runs in libcsa.so.
 """
 from __future__ import annotations
@@ -74,10 +74,13 @@ class CsaStep:
         if self.compress and (kv_format != "bf16" or ratio != 2):
             raise ValueError("the compressor publishes BF16 rows at ratio 2")
         self.rms_eps = float(rms_eps)
-        # decode steps without the compressor gather their rope rows in the
-        # attention launch (csa_sparse_attn_decode_rope / _mx_rope), which
-        # also writes them out: one launch fewer per step
-        self.fuse_rope = bool(fuse_rope) and not prefill and not self.compress
+        # fuse_rope: the launches that use RoPE rows gather them from the full
+        # tables themselves -- the decode attention (csa_sparse_attn_decode_rope
+        # / _mx_rope, which also writes the query rows out) and the compressor
+        # (csa_compress_pairs_rope) -- so no separate RoPE launch remains
+        # except for prefill attention
+        self.fuse_rope = bool(fuse_rope) and not prefill and mode != "compress"
+        self.fuse_rope_cmp = bool(fuse_rope) and self.compress
         f32 = dict(dtype=torch.float32, device=dev)
         half = self.t["freqs_cos"].shape[1]
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -89,17 +92,23 @@ class CsaStep:
             self.T, self.H, self.D = T, H, D
         self.num_tokens = T if num_tokens is None else int(num_tokens)
         # RoPE rows: the queries' rows, then (with the compressor) the rows of
-        # each token's pair start, materialised by one launch when no row is
-        # padding
-        pos_ids = [] if mode == "compress" else [self.t["position_ids"]]
-        if self.compress:
-            pos_ids.append(self.t["cmp_position_ids"])
-        self.rope_pos = pos_ids[0] if len(pos_ids) == 1 else torch.cat(pos_ids)
-        self.rope_all_cos = torch.empty((len(pos_ids) * T, half), **f32)
-        self.rope_all_sin = torch.empty((len(pos_ids) * T, half), **f32)
-        if mode != "compress":
+        # each token's pair start; those that no fused launch gathers are
+        # materialised by one launch when no row is padding
+        need_q = mode != "compress" and not self.fuse_rope
+        need_c = self.compress and not self.fuse_rope_cmp
+        pos_ids = (([self.t["position_ids"]] if need_q else [])
+                   + ([self.t["cmp_position_ids"]] if need_c else []))
+        self.rope_pos = None
+        if pos_ids:
+            self.rope_pos = pos_ids[0] if len(pos_ids) == 1 else torch.cat(pos_ids)
+            self.rope_all_cos = torch.empty((len(pos_ids) * T, half), **f32)
+            self.rope_all_sin = torch.empty((len(pos_ids) * T, half), **f32)
+        if need_q:
             self.rope_cos, self.rope_sin = self.rope_all_cos[:T], self.rope_all_sin[:T]
-        if self.compress:
+        elif mode != "compress":   # written by the fused attention
+            self.rope_cos = torch.empty((T, half), **f32)
+            self.rope_sin = torch.empty((T, half), **f32)
+        if need_c:
             self.cmp_rope_cos, self.cmp_rope_sin = self.rope_all_cos[-T:], self.rope_all_sin[-T:]
         if mode == "compress":
             return
@@ -132,6 +141,8 @@ class CsaStep:
 
     # ---- the four stages -------------------------------------------------
     def rope(self, stream=None):
+        if self.rope_pos is None:   # every user gathers its own rows
+            return
         T, n = self.T, self.rope_pos.shape[0]
         if self.num_tokens == T:
             _lib.csa_materialize_rope_rows(self.t["freqs_cos"], self.t["freqs_sin"],
@@ -149,6 +160,13 @@ class CsaStep:
         """The ratio-2 compressor: every pair an odd row closes is published
         into cmp_kv, the state ring keeps the chunk's last rows."""
         t = self.t
+        if self.fuse_rope_cmp:
+            _lib.csa_compress_pairs_rope(
+                t["kv_proj"], t["gate"], t["query_start_loc"], t["positions"], self.num_tokens,
+                t["state_block_table"], t["state_cache"], t["rms_gamma"], self.rms_eps,
+                t["freqs_cos"], t["freqs_sin"], t["cmp_position_ids"], self.rope_offset,
+                t["cmp_kv"], t["cmp_block_table"], err=self.err, stream=stream)
+            return
         _lib.csa_compress_pairs(t["kv_proj"], t["gate"], t["query_start_loc"], t["positions"],
                                 self.num_tokens, t["state_block_table"], t["state_cache"],
                                 t["rms_gamma"], self.rms_eps, self.cmp_rope_cos,
@@ -232,10 +250,10 @@ class CsaStep:
 
     @property
     def stages(self):
+        pre = (("rope",) if self.rope_pos is not None else ()) + (
+            ("compress_pairs",) if self.compress else ())
         if self.mode == "compress":
-            return ("rope", "compress_pairs")
-        pre = (("rope", "compress_pairs") if self.compress
-               else () if self.fuse_rope else ("rope",))
+            return pre
         if self.mode == "hier_full":
             return pre + ("index", "topk", "cand", "attn")
         if self.mode in ("csa", "reindex"):

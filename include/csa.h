@@ -542,6 +542,34 @@ int csa_compress_pairs(const float* kv_proj, const float* gate, int32_t D,
                        void* stream);
 
 /*
+ * csa_compress_pairs_rope -- csa_compress_pairs with each token's rope row
+ * gathered from the full tables ([V41] "Serving-owned full RoPE tables") in
+ * the same launch instead of read from materialised rows: the row of token t
+ * is table row rope_position_ids[t] (the pair's start position; identity for
+ * a negative one).  A position >= table_capacity sets CSA_EFLAG_POS_RANGE, as
+ * csa_materialize_rope_rows would, and a publication of that token rotates
+ * by the identity.  Every other argument, check and flag is
+ * csa_compress_pairs's; the published rows and the ring are bit for bit
+ * those of csa_materialize_rope_rows followed by csa_compress_pairs for
+ * positions inside the tables.
+ *
+ *   freqs_cos, freqs_sin  FP32 [table_capacity, rope_dim / 2]
+ *   rope_position_ids     INT32 [T]
+ * (the three may be NULL when rope_dim = 0; CSA_ERR_SHAPE for
+ * table_capacity < 0)
+ */
+int csa_compress_pairs_rope(const float* kv_proj, const float* gate, int32_t D,
+                            const int32_t* query_start_loc, const int32_t* positions, int32_t B,
+                            int32_t T, int32_t num_tokens, const int32_t* state_block_table,
+                            float* state_cache, int32_t num_state_blocks,
+                            int32_t state_capacity, const float* rms_gamma, float rms_eps,
+                            const float* freqs_cos, const float* freqs_sin,
+                            int32_t table_capacity, const int32_t* rope_position_ids,
+                            int32_t rope_dim, int32_t rope_offset, uint16_t* cmp_kv,
+                            int32_t num_cmp_blocks, const int32_t* cmp_block_table,
+                            int32_t max_cmp_blocks, int32_t* err, void* stream);
+
+/*
  * Hierarchical selection ([V41] "Decode composition"): a full layer publishes
  * a candidate mask of blocks of `block` consecutive compressed positions
  * (2,048 blocks of eight in V4.1); a later reindex layer scores only the

@@ -282,3 +282,100 @@ def test_c17_prefill_chunk_publication():
                 "c17 published rows")
     g_st = step.t["state_cache"].cpu().numpy()
     assert np.array_equal(g_st.view(np.uint32), o_st.view(np.uint32))
+
+
+def _run_tables(a, tc, ts, rope_pos):
+    """csa_compress_pairs_rope: the rope rows gathered from full tables."""
+    csa = _csa()
+    state = _dev(a["state_cache"])
+    cmp = _bf16_dev(a["cmp_kv"])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    csa.csa_compress_pairs_rope(_dev(a["kv_proj"]), _dev(a["gate"]), _dev(a["query_start_loc"]),
+                                _dev(a["positions"]), a["num_tokens"],
+                                _dev(a["state_block_table"]), state, _dev(a["rms_gamma"]),
+                                a["rms_eps"], _dev(tc), _dev(ts), _dev(rope_pos),
+                                a["rope_offset"], cmp, _dev(a["cmp_block_table"]), err=err)
+    torch.cuda.synchronize()
+    return (cmp.view(torch.int16).cpu().numpy().view(np.uint16), state.cpu().numpy(),
+            int(err.item()))
+
+
+def _with_tables(a, rng, cap, rope_pos):
+    """Full tables of `cap` rows and the rope rows the materialisation makes
+    of them for rope_pos (identity for negative positions; rows past the
+    tables get the identity too, which the table call uses for them)."""
+    half = a["rope_cos"].shape[1]
+    ang = rng.uniform(-3, 3, (cap, half))
+    tc, ts = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    T = a["num_tokens"]
+    rc = np.full((T, half), np.nan, np.float32)
+    rs = np.full((T, half), np.nan, np.float32)
+    err = oracle.materialize_rope_rows(tc, ts, rope_pos, T, rc, rs)
+    rc = np.nan_to_num(rc, nan=1.0)
+    rs = np.nan_to_num(rs, nan=0.0)
+    return tc, ts, dict(a, rope_cos=rc, rope_sin=rs), err
+
+
+def test_table_rope_rows_equal_materialised_rows():
+    """csa_compress_pairs_rope publishes, bit for bit, what csa_compress_pairs
+    publishes from the materialised rows of the same positions (pair starts,
+    -1 rows included), and leaves the same ring."""
+    rng = np.random.default_rng(71)
+    a = _case(rng, chunks=[2, 1, 5, 7, 3, 6], starts=[10, 13, 21, 100, 6, 40], disabled=(4,),
+              neg_rows=(5,))
+    pos = a["positions"]
+    rope_pos = np.where(pos >= 0, pos - pos % 2, -1).astype(np.int32)
+    tc, ts, a_rows, e0 = _with_tables(a, rng, 256, rope_pos)
+    assert e0 == 0
+    print("[compress] table rope rows", flush=True)
+    g_cmp, g_st, g_err = _run_tables(a, tc, ts, rope_pos)
+    r_cmp, r_st, r_err = _run(a_rows)
+    assert g_err == r_err
+    assert np.array_equal(g_cmp, r_cmp), "published rows differ"
+    assert np.array_equal(g_st.view(np.uint32), r_st.view(np.uint32)), "ring differs"
+    assert _compare(a_rows, "table rope rows, against the oracle") > 0
+
+
+def test_table_rope_position_past_the_tables():
+    """A pair start past the tables flags POS_RANGE and that publication
+    rotates by the identity; the other rows are unaffected."""
+    rng = np.random.default_rng(72)
+    a = _case(rng, chunks=[4, 4], starts=[20, 61])
+    pos = a["positions"]
+    rope_pos = np.where(pos >= 0, pos - pos % 2, -1).astype(np.int32)
+    cap = 64
+    assert pos[6] == 63 and pos[2] == 22
+    rope_pos[6] = cap + 7                 # an odd row: its publication
+    rope_pos[2] = cap + 1                 # an even row: flagged, nothing published
+    tc, ts, a_rows, e0 = _with_tables(a, rng, cap, rope_pos)
+    assert e0 == oracle.EFLAG_POS_RANGE
+    g_cmp, g_st, g_err = _run_tables(a, tc, ts, rope_pos)
+    r_cmp, r_st, r_err = _run(a_rows)
+    assert g_err == r_err | oracle.EFLAG_POS_RANGE == oracle.EFLAG_POS_RANGE
+    assert np.array_equal(g_cmp, r_cmp)
+    assert np.array_equal(g_st.view(np.uint32), r_st.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["c16", "c17"])
+def test_step_with_table_rope_equals_separate_rope_launch(name):
+    """The compressor steps without a RoPE launch (the compressor and the
+    decode attention gather their rows) give the same bits as with it."""
+    csa = _csa()
+    cfg = synthetic.get(name)
+    x = synthetic.make_inputs(cfg, seed=31).t
+    sep = csa.step_for_config(cfg, x, fuse_rope=False)
+    fused = csa.step_for_config(cfg, x)
+    assert "rope" in sep.stages and "rope" not in fused.stages
+    print(f"[compress] {name}: stages {fused.stages} vs {sep.stages}", flush=True)
+    for s in (sep, fused):
+        s.run()
+    torch.cuda.synchronize()
+    assert int(fused.err.item()) == int(sep.err.item()) == 0
+    assert torch.equal(fused.t["cmp_kv"].view(torch.int16), sep.t["cmp_kv"].view(torch.int16))
+    assert torch.equal(fused.t["state_cache"].view(torch.int32),
+                       sep.t["state_cache"].view(torch.int32))
+    if cfg.mode != "compress":
+        assert torch.equal(fused.topk_idx, sep.topk_idx)
+        assert torch.equal(fused.out.view(torch.int16), sep.out.view(torch.int16))
+        assert torch.equal(fused.lse.view(torch.int32), sep.lse.view(torch.int32))
+        assert torch.equal(fused.rope_cos.view(torch.int32), sep.rope_cos.view(torch.int32))

@@ -158,6 +158,27 @@ def test_attention_mx_rope_tables_host_checks(lib):
     assert f(*bad) == 0
 
 
+def test_compress_rope_tables_host_checks(lib):
+    """The compressor with table rope rows: tables and position ids are
+    required with a rope span, then the compressor's own checks apply."""
+    f = lib.csa_compress_pairs_rope
+    base = [FAKE, FAKE, 512, FAKE, FAKE, 2, 4, 4, FAKE, FAKE, 4, 4, FAKE, 1e-6, FAKE, FAKE, 1024,
+            FAKE, 64, 448, FAKE, 8, FAKE, 2, None, None]
+    assert len(base) == 26
+    bad = list(base); bad[16] = -1                # table capacity < 0
+    assert f(*bad) == -2
+    bad = list(base); bad[14] = None              # no cos table
+    assert f(*bad) == -1
+    bad = list(base); bad[17] = None              # no position ids
+    assert f(*bad) == -1
+    bad = list(base); bad[11] = 0                 # ring capacity 0
+    assert f(*bad) == -3
+    bad = list(base); bad[2] = 511                # odd D
+    assert f(*bad) == -4
+    bad = list(base); bad[7] = 0                  # no active rows
+    assert f(*bad) == 0
+
+
 def test_attention_selection_bounds(lib):
     """A selection array holds at most 4096 entries per row; without one
     (every visible compressed row) k bounds the visible count up to 2^20, and
