@@ -946,8 +946,9 @@ __global__ void __launch_bounds__(kRingThreads, 1) attn_kernel(AttnArgs a) {
 // memory latency -- and runs one 32-key tile (S^T, softmax, P*V) for the
 // group's 16 heads; no key byte is read from LDS by more than one wave.  The
 // four per-wave softmax states are then combined in LDS.  With one span the
-// work-group writes the output rows directly; with several it writes a BF16
-// partial (16 heads x D, normalised by its own sum) with the FP32 (max, sum)
+// work-group writes the output rows directly; with several it writes an FP16
+// partial (16 heads x D, normalised by its own sum and scaled by a power of
+// two per channel quarter) with the FP32 (max, sum)
 // for the merge kernel.
 constexpr int kSpan = kAttnWaves * kTile;   // list entries per decode work-group
 
