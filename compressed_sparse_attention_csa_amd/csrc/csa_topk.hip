@@ -24,9 +24,11 @@
 // score row.  Longer rows (up to the 1,048,576-position context): three
 // kernels over the row, which the indexer has just left in L2 / MALL:
 //   sample: one work-group per row reads 8,192 scores spread over the row and
-//           takes as threshold tau the key of a sampled rank a few standard
+//           takes as threshold tau the key of a sampled rank r a few standard
 //           deviations above m * samples / span, which leaves about
-//           m * (1 + 3 / sqrt(m)) keys >= tau;
+//           m * (1 + 3 / sqrt(m)) keys >= tau (for r <= 64 the r-th best
+//           16-lane maximum bounds it from below and the few samples above
+//           that bound are ranked directly; else the selection core);
 //   filter: work-groups over 8,192-score chunks keep every key >= tau, each
 //           wave writing its (key, position) pairs in position order into the
 //           workspace slots of its own positions, with its count;
@@ -787,6 +789,76 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
 // ----------------------------------------------------------------------------
 // long rows
 // ----------------------------------------------------------------------------
+// Largest u32 of a row of 16 lanes, in every lane of the row (DPP quad swaps
+// and row mirrors: each step compares symmetric pairs).
+__device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xb1, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4e, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xf, 0xf, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xf, 0xf, false)));
+  return v;
+}
+
+// The r-th largest of the work-group's keys for a small r (r <= kRows16, the
+// number of 16-lane rows of the work-group): the r-th largest row maximum is
+// a lower bound lo for it (r rows hold a key >= lo), so it is the r-th
+// largest of the keys >= lo -- for a sample of a row's scores a few dozen --
+// which are compacted into LDS and ranked directly.  Returns false when more
+// than kSmallRCap keys reach lo (then the caller runs the selection core).
+constexpr int kSmallRCap = 1024;
+template <int THREADS, int KPT>
+__device__ bool small_r_threshold(const uint32_t (&key)[KPT], int r, SelShared<THREADS>& sh,
+                                  uint32_t* tau) {
+  constexpr int NW = THREADS / 64;
+  constexpr int kRows16 = THREADS / 16;
+  static_assert(kRows16 + kSmallRCap <= 2 * kLCap, "LDS list");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) mx = max(mx, key[j]);
+  mx = row16_max_u(mx);
+  if ((lane & 15) == 0) sh.list[wave * 4 + (lane >> 4)] = mx;
+  __syncthreads();
+  // rank the row maxima (larger first, ties by row index); the one of rank
+  // r - 1 is the bound
+  for (int g = tid; g < kRows16; g += THREADS) {
+    const uint32_t v = sh.list[g];
+    int rank = 0;
+    for (int u = 0; u < kRows16; ++u) {
+      const uint32_t o = sh.list[u];
+      rank += (o > v || (o == v && u < g)) ? 1 : 0;
+    }
+    if (rank == r - 1) sh.cut[0] = v;
+  }
+  __syncthreads();
+  const uint32_t lo = sh.cut[0];
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) c += key[j] >= lo ? 1 : 0;
+  int total = 0;
+  int o = block_excl_scan<NW>(c, sh.wsum, &total);
+  if (total > kSmallRCap) return false;
+  uint32_t* list = sh.list + kRows16;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if (key[j] >= lo) list[o++] = key[j];
+  __syncthreads();
+  for (int i = tid; i < total; i += THREADS) {
+    const uint32_t v = list[i];
+    int rank = 0;
+    for (int u = 0; u < total; ++u) {
+      const uint32_t w = list[u];
+      rank += (w > v || (w == v && u < i)) ? 1 : 0;
+    }
+    if (rank == r - 1) sh.cut[1] = v;
+  }
+  __syncthreads();
+  *tau = sh.cut[1];
+  return true;
+}
+
 // Sampled threshold of a long row: one float4 group every `span` positions
 // (span a multiple of 256 that keeps the groups within kSampleGroups), S
 // samples in all.  The key tau of the r-th best sample, with r a few standard
@@ -831,9 +903,16 @@ __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
   const int m = min(k, n);
   const float expect = static_cast<float>(m) * static_cast<float>(S) / static_cast<float>(n);
   const int r = static_cast<int>(ceilf(expect + 3.0f * sqrtf(expect) + 4.0f));
+  // keys past nmine are 0, the lowest key: with r < S they never move the
+  // r-th best, so the small-r path may take every slot.  It needs r rows of
+  // 16 lanes holding samples (threads below G hold at least one group).
   uint32_t tau = 0u;   // every key is a candidate
-  if (r < S && find_cut<kFThreads, KPT>(key, nmine, r, sh, [&](int j) { return tid * KPT + j; }))
-    tau = sh.cut[0];
+  if (r < S) {
+    const bool small_r = r <= min(G, kFThreads) / 16;
+    if (!(small_r && small_r_threshold<kFThreads, KPT>(key, r, sh, &tau)) &&
+        find_cut<kFThreads, KPT>(key, nmine, r, sh, [&](int j) { return tid * KPT + j; }))
+      tau = sh.cut[0];
+  }
   if (tid == 0) ws.meta[static_cast<size_t>(t) * kMetaWords] = tau;
 }
 

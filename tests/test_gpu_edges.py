@@ -78,6 +78,25 @@ def test_topk_ties_nan_zero_inf(stride):
     _compare_topk(sc, pos, 1, 512, f"ties stride {stride}")
 
 
+def test_topk_long_rows_with_ties():
+    """1M-position rows of few distinct values, signed zeros, infinities and
+    NaN: the sampled threshold's small-rank path sees thousands of keys at its
+    bound and hands over to the selection core; exact as the oracle."""
+    print("[edges] topk long rows with ties", flush=True)
+    rng = np.random.default_rng(77)
+    T, stride, k = 5, 1 << 20, 2048
+    sc = rng.integers(-3, 4, (T, stride)).astype(np.float32)
+    sc[1] = 2.0                                    # every key equal
+    sc[1, ::7] = -0.0
+    sc[2, ::97] = np.inf                           # more +inf keys than k
+    sc[2, 1::13] = np.nan
+    sc[3] = rng.standard_normal(stride).astype(np.float32)
+    sc[3, ::3] = np.nan                            # a third NaN
+    sc[4] = np.where(rng.random(stride) < 0.003, 5.0, sc[4])   # a tied top band near k
+    pos = np.full(T, stride - 1)
+    _compare_topk(sc, pos, 1, k, "long rows with ties")
+
+
 @pytest.mark.parametrize("case", ["ascending", "clustered", "outliers", "few_groups"])
 def test_topk_long_row_group_bound(case):
     """Long rows take a threshold from the maxima of 32-score groups: rows
