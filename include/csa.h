@@ -15,11 +15,14 @@
  *      csa_sparse_attn_prefill       window and the selected compressed rows,
  *                                    with one sink logit per head
  *      (csa_sparse_attn_decode_mx: the same over the MXFP8 window and MXFP4
- *      compressed KV planes)
+ *      compressed KV planes; csa_sparse_attn_decode_rope / _mx_rope: step 1
+ *      folded into the decode attention, which reads the full tables and
+ *      writes the rope rows out)
  *   5. csa_inverse_rope           -- the output's rope span rotated back by the
  *                                    query row's angles
  * and the step before the path: csa_compress_pairs publishes ratio-2
- * compressed rows from the projections and its FP32 state ring.
+ * compressed rows from the projections and its FP32 state ring
+ * (csa_compress_pairs_rope: with its rope rows read from the full tables).
  *
  * Pages the contracts follow (cited by title and section):
  *   [V41]  pypto-lib "DeepSeek V4.1 Flash": "Serving-owned full RoPE tables",
