@@ -1351,12 +1351,17 @@ template <int D, bool MANY>
 __global__ void __launch_bounds__(64) attn_merge_kernel(
     const uint16_t* __restrict__ part_o, const float2* __restrict__ part_ml,
     const float* __restrict__ part_mult, const float* __restrict__ sink, int splits, int H,
-    int num_tokens,
+    int num_tokens, int items_per_xcd,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int CPL = D / 64;            // channels per lane
   static_assert(CPL == 1 || CPL == 2 || CPL == 4 || CPL == 8, "channels per lane");
-  const int t = blockIdx.x / H;
-  const int h = blockIdx.x % H;
+  // (row, head) items in row-major order, consecutive items on one XCD: the
+  // same split of rows over XCDs as the span work-groups, whose partials
+  // are then still in that XCD's L2
+  const int L = blockIdx.x;
+  const int item = (L & 7) * items_per_xcd + (L >> 3);
+  const int t = item / H;
+  const int h = item % H;
   if (t >= num_tokens) return;
   const int lane = threadIdx.x;
   const float neg_inf = -__builtin_huge_valf();
@@ -1529,15 +1534,17 @@ int launch_attn(const AttnArgs& in, bool ring, bool mx, hipStream_t st) {
                        dim3(kAttnThreads), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   if (a.splits > 1) {
-    const long long mgrid = static_cast<long long>(a.num_tokens) * a.H;
+    const long long items = static_cast<long long>(a.num_tokens) * a.H;
+    const long long mpx = (items + 7) / 8;
+    const long long mgrid = 8 * mpx;
     if (a.splits <= 64)
       hipLaunchKernelGGL((attn_merge_kernel<D, false>), dim3(static_cast<unsigned>(mgrid)),
                          dim3(64), 0, st, a.part_o, a.part_ml, a.part_mult, a.sink, a.splits, a.H,
-                         a.num_tokens, a.out, a.lse);
+                         a.num_tokens, static_cast<int>(mpx), a.out, a.lse);
     else
       hipLaunchKernelGGL((attn_merge_kernel<D, true>), dim3(static_cast<unsigned>(mgrid)),
                          dim3(64), 0, st, a.part_o, a.part_ml, a.part_mult, a.sink, a.splits, a.H,
-                         a.num_tokens, a.out, a.lse);
+                         a.num_tokens, static_cast<int>(mpx), a.out, a.lse);
     if (hipGetLastError() != hipSuccess) return CSA_ERR_LAUNCH;
   }
   return CSA_OK;
