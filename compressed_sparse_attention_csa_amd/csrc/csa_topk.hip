@@ -789,6 +789,15 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
 // ----------------------------------------------------------------------------
 // long rows
 // ----------------------------------------------------------------------------
+// Long-row work is split over the XCDs in contiguous runs of rows (work-group
+// L runs on XCD L % 8): a row's sample, filter chunks and final selection
+// share one XCD's L2, so the final kernel reads its candidates (and the
+// filter its threshold) where they were written.
+__device__ __forceinline__ int xcd_item(int per_xcd) {
+  const int L = blockIdx.x;
+  return (L & 7) * per_xcd + (L >> 3);
+}
+
 // Largest u32 of a row of 16 lanes, in every lane of the row (DPP quad swaps
 // and row mirrors: each step compares symmetric pairs).
 __device__ __forceinline__ uint32_t row16_max_u(uint32_t v) {
@@ -868,9 +877,9 @@ __device__ bool small_r_threshold(const uint32_t (&key)[KPT], int r, SelShared<T
 // select when the sample misled it.
 __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
     const float* __restrict__ scores, long long stride, RowSpec rs,
-    int num_tokens, int k, Workspace ws) {
+    int num_tokens, int k, Workspace ws, int rows_per_xcd) {
   __shared__ SelShared<kFThreads> sh;
-  const int t = blockIdx.x;
+  const int t = xcd_item(rows_per_xcd);
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
   const int n = row_span(rs, t, stride, nullptr, false);
@@ -957,14 +966,16 @@ __device__ __forceinline__ bool in_span(const ChunkKeys& ck, int j, int n) {
 // into seg[].
 __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
     const float* __restrict__ scores, long long stride, RowSpec rs,
-    int num_tokens, Workspace ws) {
-  const int t = blockIdx.y;
+    int num_tokens, Workspace ws, int nchunks, int chunks_per_xcd) {
+  const int item = xcd_item(chunks_per_xcd);   // row-major (row, chunk)
+  const int t = item / nchunks;
+  const int chunk = item - t * nchunks;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   if (t >= num_tokens) return;
   const int n = row_span(rs, t, stride, nullptr, false);
-  const int c0 = blockIdx.x * kChunk;
+  const int c0 = chunk * kChunk;
   if (n <= kCap || c0 >= n) return;
   ChunkKeys ck;
   load_chunk(scores + static_cast<long long>(t) * stride, stride, n, c0, ck);
@@ -984,7 +995,7 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
              4 * __popcll(b2 & below);
     wave_total += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
   }
-  const int sidx = blockIdx.x * kLWaves + wave;
+  const int sidx = chunk * kLWaves + wave;
   if (lane == 0) ws.seg[static_cast<size_t>(t) * ws.nseg + sidx] = static_cast<uint32_t>(wave_total);
   uint2* slots = ws.cand + static_cast<size_t>(t) * stride + static_cast<size_t>(c0) + wave * kSub;
 #pragma unroll
@@ -1004,12 +1015,12 @@ __global__ void __launch_bounds__(kLThreads) topk_filter_kernel(
 __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
     const float* __restrict__ scores, long long stride, RowSpec rs,
     int num_tokens, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_val, Workspace ws, int32_t* err) {
+    float* __restrict__ topk_val, Workspace ws, int32_t* err, int rows_per_xcd) {
   __shared__ SelShared<kFThreads> sh;
   __shared__ uint32_t craw[kCap];   // candidate score bits
   __shared__ uint32_t cpos[kCap];
   __shared__ uint32_t segstart[kMaxSeg + 1];   // first candidate slot of each segment, then total
-  const int t = blockIdx.x;
+  const int t = xcd_item(rows_per_xcd);
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
   const int n = row_span(rs, t, stride, err, tid == 0);
@@ -1184,14 +1195,19 @@ int launch_topk(const float* scores, long long stride, const RowSpec& rs, int T,
     if (!workspace || workspace_bytes < ws_bytes(T, stride)) return CSA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 15) return CSA_ERR_UNSUPPORTED;
     const Workspace ws = ws_layout(workspace, T, stride);
-    const dim3 grid(static_cast<unsigned>((stride + kChunk - 1) / kChunk),
-                    static_cast<unsigned>(num_tokens));
-    hipLaunchKernelGGL(topk_sample_kernel, dim3(num_tokens), dim3(kFThreads), 0, st, scores,
-                       stride, rs, num_tokens, k, ws);
-    hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kLThreads), 0, st, scores, stride, rs,
-                       num_tokens, ws);
-    hipLaunchKernelGGL(topk_final_kernel, dim3(num_tokens), dim3(kFThreads), 0, st, scores,
-                       stride, rs, num_tokens, k, topk_idx, topk_val, ws, err);
+    // rows in contiguous runs per XCD: rpx rows, their chunks cpx = rpx * nch
+    const long long nch = (stride + kChunk - 1) / kChunk;
+    const long long rpx = (num_tokens + 7) / 8;
+    const long long cpx = rpx * nch;
+    if (8 * cpx > 0x7fffffffll) return CSA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(topk_sample_kernel, dim3(static_cast<unsigned>(8 * rpx)), dim3(kFThreads),
+                       0, st, scores, stride, rs, num_tokens, k, ws, static_cast<int>(rpx));
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(static_cast<unsigned>(8 * cpx)), dim3(kLThreads),
+                       0, st, scores, stride, rs, num_tokens, ws, static_cast<int>(nch),
+                       static_cast<int>(cpx));
+    hipLaunchKernelGGL(topk_final_kernel, dim3(static_cast<unsigned>(8 * rpx)), dim3(kFThreads),
+                       0, st, scores, stride, rs, num_tokens, k, topk_idx, topk_val, ws, err,
+                       static_cast<int>(rpx));
   }
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_ERR_LAUNCH;
 }
