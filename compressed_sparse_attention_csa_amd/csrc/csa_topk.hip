@@ -394,8 +394,10 @@ __device__ void cut_of_selection(const uint32_t (&key)[KPT], uint32_t chosen, ui
 // key[0..nmine), whose positions pos(j) ascend within a thread and across
 // threads.  One value-histogram pass over every key finds the bin holding the
 // m-th best; that bin's keys are compacted into LDS in position order and,
-// when few, ranked directly, else refined as a list.
-template <int THREADS, int KPT, typename PosFn>
+// when few, ranked directly, else refined as a list.  HOLD keeps each key's
+// bin in registers between the histogram, the count and the compaction
+// instead of recomputing it (callers short of registers leave it off).
+template <int THREADS, int KPT, bool HOLD, typename PosFn>
 __device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared<THREADS>& sh,
                          PosFn pos) {
   constexpr int NW = THREADS / 64;
@@ -411,8 +413,22 @@ __device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared
   for (int i = tid; i < kSBins + 64; i += THREADS) sh.hist[i] = 0u;
   block_minmax<NW>(fmin, fmax, sh.red, sh.mm);
   const Binner bn = make_binner(fmin, fmax, kSBins);
+  // a key's bin, -1 past nmine
+  constexpr bool kHold = HOLD;
+  int bj[kHold ? KPT : 1];
+  auto bin_of = [&](int j) {
+    if constexpr (kHold) return bj[j];
+    else return j < nmine ? bn(key[j]) : -1;
+  };
+  if constexpr (kHold) {
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) atomicAdd(&sh.hist[j < nmine ? bn(key[j]) : kSBins + lane], 1u);
+    for (int j = 0; j < KPT; ++j) bj[j] = j < nmine ? bn(key[j]) : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int bb = bin_of(j);
+    atomicAdd(&sh.hist[bb >= 0 ? bb : kSBins + lane], 1u);
+  }
   __syncthreads();
   find_bin<kSBins, THREADS>(sh.hist, m, sh.wsum, &sh.bsel[0], &sh.bsel[1]);
   const int b0 = sh.bsel[0];
@@ -421,11 +437,11 @@ __device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared
   if (cnt > kLCap) return false;   // massive ties: the caller selects on the whole row
   int c = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) c += (j < nmine && bn(key[j]) == b0) ? 1 : 0;
+  for (int j = 0; j < KPT; ++j) c += bin_of(j) == b0 ? 1 : 0;
   int o = block_excl_scan<NW>(c, sh.wsum, nullptr);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    if (j < nmine && bn(key[j]) == b0) {
+    if (bin_of(j) == b0) {
       sh.list[o] = key[j];
       sh.list[kLCap + o] = static_cast<uint32_t>(pos(j));
       ++o;
@@ -769,7 +785,7 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
         for (int j = 0; j < CPT; ++j) ck[j] = (j < cper && cbase + j < total) ? cand_k[cbase + j] : 0u;
         const int cn = max(0, min(cper, total - cbase));
         auto cpos = [&](int j) { return static_cast<int>(cand_p[cbase + j]); };
-        if (find_cut<THREADS, CPT>(ck, cn, m, sh, cpos)) {
+        if (find_cut<THREADS, CPT, false>(ck, cn, m, sh, cpos)) {
           emit_cut<THREADS, CPT>(ck, cn, m, k, [&](int j) { return row[cpos(j)]; }, out_i, out_v,
                                  sh, cpos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
           done = true;
@@ -779,7 +795,7 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
     __syncthreads();
   }
   if (done) return;
-  if (find_cut<THREADS, KPT>(key, nmine, m, sh, pos))
+  if (find_cut<THREADS, KPT, false>(key, nmine, m, sh, pos))
     emit_cut<THREADS, KPT>(key, nmine, m, k, [&](int j) { return row[pos(j)]; }, out_i, out_v, sh,
                            pos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
   else
@@ -919,7 +935,7 @@ __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
   if (r < S) {
     const bool small_r = r <= min(G, kFThreads) / 16;
     if (!(small_r && small_r_threshold<kFThreads, KPT>(key, r, sh, &tau)) &&
-        find_cut<kFThreads, KPT>(key, nmine, r, sh, [&](int j) { return tid * KPT + j; }))
+        find_cut<kFThreads, KPT, true>(key, nmine, r, sh, [&](int j) { return tid * KPT + j; }))
       tau = sh.cut[0];
   }
   if (tid == 0) ws.meta[static_cast<size_t>(t) * kMetaWords] = tau;
@@ -1023,6 +1039,29 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
   const int t = xcd_item(rows_per_xcd);
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
+  // Segment s of a row is copied by tps threads (kFThreads / nseg rounded
+  // down to a power of two, at least 1), each taking every tps-th entry in
+  // batches of kBatch loads before any is stored.  The row's span is not
+  // known until its position is read, so the counts of the first kFThreads
+  // segments and the first batch of each thread's first segment are fetched
+  // with it, laid out for a row that fills the stride (the usual case); they
+  // are used when the row's layout turns out the same, else fetched again.
+  // Slots and counts past the row's own are dropped.
+  constexpr int kBatch = 8;
+  const uint32_t* seg = ws.seg + static_cast<size_t>(t) * ws.nseg;
+  const uint2* cand = ws.cand + static_cast<size_t>(t) * stride;
+  int tps_g = 1;
+  while (tps_g * 2 * ws.nseg <= kFThreads) tps_g *= 2;
+  uint2 pre[kBatch];
+  {
+    const int s0 = tid / tps_g;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const long long slot = static_cast<long long>(s0) * kSub + tid % tps_g + u * tps_g;
+      pre[u] = (s0 < ws.nseg && slot < stride) ? cand[slot] : make_uint2(0u, 0u);
+    }
+  }
+  const uint32_t seg_g = tid < ws.nseg ? seg[tid] : 0u;
   const int n = row_span(rs, t, stride, err, tid == 0);
   const float* row = scores + static_cast<long long>(t) * stride;
   int32_t* out_i = topk_idx + static_cast<long long>(t) * k;
@@ -1043,39 +1082,40 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
     } else {
       // candidates: the positions of the keys >= tau, each wave segment's in
       // position order in the slots of its own positions
-      const int nseg = ((n + kChunk - 1) / kChunk) * kLWaves;
+      const int nseg = ((n + kChunk - 1) / kChunk) * kLWaves;   // <= ws.nseg
       const int spt = (nseg + kFThreads - 1) / kFThreads;
-      const uint32_t* seg = ws.seg + static_cast<size_t>(t) * ws.nseg;
-      const uint2* cand = ws.cand + static_cast<size_t>(t) * stride;
-      // segment s is copied by tps threads (kFThreads / nseg rounded down
-      // to a power of two, at least 1), each taking every tps-th entry in
-      // batches of kBatch loads before any is stored.  The first batch of
-      // each thread's first segment is fetched with the counts, ahead of
-      // them (slots past a count are dropped), which saves a round trip
       int tps = 1;
       while (tps * 2 * nseg <= kFThreads) tps *= 2;
-      constexpr int kBatch = 8;
       const int s0 = tid / tps;
-      uint2 pre[kBatch];
+      if (tps != tps_g) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const long long slot = static_cast<long long>(s0) * kSub + tid % tps + u * tps;
-        pre[u] = (s0 < nseg && slot < stride) ? cand[slot] : make_uint2(0u, 0u);
+        for (int u = 0; u < kBatch; ++u) {
+          const long long slot = static_cast<long long>(s0) * kSub + tid % tps + u * tps;
+          pre[u] = (s0 < nseg && slot < stride) ? cand[slot] : make_uint2(0u, 0u);
+        }
       }
       int mine = 0;
-      for (int i = 0; i < spt; ++i) {
-        const int sidx = tid * spt + i;
-        if (sidx < nseg) mine += static_cast<int>(seg[sidx]);
+      if (spt == 1) {
+        mine = tid < nseg ? static_cast<int>(seg_g) : 0;
+      } else {
+        for (int i = 0; i < spt; ++i) {
+          const int sidx = tid * spt + i;
+          if (sidx < nseg) mine += static_cast<int>(seg[sidx]);
+        }
       }
       int dst = block_excl_scan<kFThreads / 64>(mine, sh.wsum, &total);
       if (total < m || total > kCap) {
         whole_row = true;   // the sample misled: exact select over the row
       } else {
-        for (int i = 0; i < spt; ++i) {
-          const int sidx = tid * spt + i;
-          if (sidx < nseg) {
-            segstart[sidx] = static_cast<uint32_t>(dst);
-            dst += static_cast<int>(seg[sidx]);
+        if (spt == 1) {
+          if (tid < nseg) segstart[tid] = static_cast<uint32_t>(dst);
+        } else {
+          for (int i = 0; i < spt; ++i) {
+            const int sidx = tid * spt + i;
+            if (sidx < nseg) {
+              segstart[sidx] = static_cast<uint32_t>(dst);
+              dst += static_cast<int>(seg[sidx]);
+            }
           }
         }
         if (tid == 0) segstart[nseg] = static_cast<uint32_t>(total);
@@ -1129,7 +1169,7 @@ __global__ void __launch_bounds__(kFThreads) topk_final_kernel(
       auto pos = [&](int j) { return static_cast<int>(cpos[base + j]); };
       // the chosen scores come from the candidates' own bits, not the row
       auto val = [&](int j) { return __uint_as_float(craw[base + j]); };
-      if (find_cut<kFThreads, kFPer>(key, nmine, m, sh, pos))
+      if (find_cut<kFThreads, kFPer, true>(key, nmine, m, sh, pos))
         emit_cut<kFThreads, kFPer>(key, nmine, m, k, val, out_i, out_v, sh, pos,
                                    Remap{rs.remap, rs.rgroup, rs.rstride, t});
       else
