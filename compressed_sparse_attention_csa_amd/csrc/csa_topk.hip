@@ -898,13 +898,35 @@ __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
   const int t = xcd_item(rows_per_xcd);
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
+  const float* row = scores + static_cast<long long>(t) * stride;
+  // groups of 4 scores, one every `span` positions (a multiple of 256)
+  auto span_of = [](long long len) {
+    return 256ll * ((len + 256ll * kSampleGroups - 1) / (256ll * kSampleGroups));
+  };
+  constexpr int KPT = 4 * (kSampleGroups / kFThreads);
+  // The groups are read with the row's position, spaced for a row that fills
+  // the stride (the usual case), and read again only when the row's own span
+  // spaces them differently.
+  float4 v[KPT / 4];
+  const long long span_g = span_of(stride);
+#pragma unroll
+  for (int i = 0; i < KPT / 4; ++i) {
+    const long long p0 = static_cast<long long>(tid + i * kFThreads) * span_g;
+    v[i] = p0 < stride ? *reinterpret_cast<const float4*>(row + p0)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int n = row_span(rs, t, stride, nullptr, false);
   if (n <= kCap) return;
-  const float* row = scores + static_cast<long long>(t) * stride;
-  const long long span =
-      256ll * ((static_cast<long long>(n) + 256ll * kSampleGroups - 1) / (256ll * kSampleGroups));
+  const long long span = span_of(n);
   const int G = static_cast<int>((n + span - 1) / span);   // groups, <= kSampleGroups
-  constexpr int KPT = 4 * (kSampleGroups / kFThreads);
+  if (span != span_g) {
+#pragma unroll
+    for (int i = 0; i < KPT / 4; ++i) {
+      const int g = tid + i * kFThreads;
+      v[i] = g < G ? *reinterpret_cast<const float4*>(row + g * span)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
   // thread tid reads groups tid, tid + 1024, ...: its valid groups are a
   // prefix, so its keys [0, nmine) are the samples it holds (components past
   // the span take the lowest key, which never moves the r-th best)
@@ -914,12 +936,10 @@ __global__ void __launch_bounds__(kFThreads) topk_sample_kernel(
   for (int i = 0; i < KPT / 4; ++i) {
     const int g = tid + i * kFThreads;
     const long long p0 = g * span;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (g < G) v = *reinterpret_cast<const float4*>(row + p0);
-    key[4 * i] = g < G ? order_key(v.x) : 0u;
-    key[4 * i + 1] = (g < G && p0 + 1 < n) ? order_key(v.y) : 0u;
-    key[4 * i + 2] = (g < G && p0 + 2 < n) ? order_key(v.z) : 0u;
-    key[4 * i + 3] = (g < G && p0 + 3 < n) ? order_key(v.w) : 0u;
+    key[4 * i] = g < G ? order_key(v[i].x) : 0u;
+    key[4 * i + 1] = (g < G && p0 + 1 < n) ? order_key(v[i].y) : 0u;
+    key[4 * i + 2] = (g < G && p0 + 2 < n) ? order_key(v[i].z) : 0u;
+    key[4 * i + 3] = (g < G && p0 + 3 < n) ? order_key(v[i].w) : 0u;
     ng += g < G ? 1 : 0;
   }
   const int nmine = 4 * ng;
