@@ -24,11 +24,13 @@
 // score row.  Longer rows (up to the 1,048,576-position context): three
 // kernels over the row, which the indexer has just left in L2 / MALL:
 //   sample: one work-group per row reads 8,192 scores spread over the row and
-//           takes as threshold tau the key of a sampled rank r a few standard
-//           deviations above m * samples / span, which leaves about
-//           m * (1 + 3 / sqrt(m)) keys >= tau (for r <= 64 the r-th best
-//           16-lane maximum bounds it from below and the few samples above
-//           that bound are ranked directly; else the selection core);
+//           takes as threshold tau the key of sampled rank r = e + 3 sqrt(e)
+//           + 4, e = m * samples / span (three standard deviations above the
+//           expected rank of the m-th best), which leaves about
+//           r * span / samples keys >= tau (4,096 for m = 2,048 over a
+//           1,048,576-position row); for r <= 64 the r-th best 16-lane
+//           maximum bounds it from below and the few samples above that
+//           bound are ranked directly, else the selection core;
 //   filter: work-groups over 8,192-score chunks keep every key >= tau, each
 //           wave writing its (key, position) pairs in position order into the
 //           workspace slots of its own positions, with its count;
@@ -36,6 +38,11 @@
 //           into LDS and runs the selection core on them.  When the sample
 //           misled it (fewer than m keys >= tau, or more candidates than LDS
 //           holds), it selects exactly over the whole row instead.
+// All three map work-group L to XCD L mod 8 with a contiguous block of rows
+// per XCD, so a row's three kernels meet its data in one L2.  The sample and
+// final kernels fetch their first data together with the row's position,
+// laid out for a row that fills the stride, and fetch again only when the
+// row is shorter.
 // No work-group waits on another inside a kernel and no counter is shared
 // between work-groups, so the kernels need no device-scope fences or atomics
 // in global memory, and the workspace keeps nothing between calls.
@@ -66,9 +73,10 @@ constexpr uint32_t kKeyNegInf = 0x007fffffu;
 constexpr uint32_t kKeyPosInf = 0xff800000u;
 
 // Long-row workspace (no state survives a call: a word is used only after
-// this call wrote it; the final kernel may fetch a segment's slots ahead of
-// its count and then drops those past it): per row a threshold word, one
-// candidate count per wave segment, and one (score bits, position) slot per
+// this call wrote it; the final kernel may fetch counts and slots before it
+// knows which of them this call wrote, and drops the others): per row a
+// threshold word, one candidate count per wave segment, and one (score bits,
+// position) slot per
 // score (a segment owns the slots of its own positions, so no counter is
 // shared between work-groups).
 struct Workspace {
