@@ -76,9 +76,8 @@ constexpr uint32_t kKeyPosInf = 0xff800000u;
 // this call wrote it; the final kernel may fetch counts and slots before it
 // knows which of them this call wrote, and drops the others): per row a
 // threshold word, one candidate count per wave segment, and one (score bits,
-// position) slot per
-// score (a segment owns the slots of its own positions, so no counter is
-// shared between work-groups).
+// position) slot per score (a segment owns the slots of its own positions,
+// so no counter is shared between work-groups).
 struct Workspace {
   uint32_t* meta;   // [T][kMetaWords]
   uint32_t* seg;    // [T][nseg]
