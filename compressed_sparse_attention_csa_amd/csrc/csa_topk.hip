@@ -792,7 +792,7 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
         for (int j = 0; j < CPT; ++j) ck[j] = (j < cper && cbase + j < total) ? cand_k[cbase + j] : 0u;
         const int cn = max(0, min(cper, total - cbase));
         auto cpos = [&](int j) { return static_cast<int>(cand_p[cbase + j]); };
-        if (find_cut<THREADS, CPT, false>(ck, cn, m, sh, cpos)) {
+        if (find_cut<THREADS, CPT, (KPT <= 16)>(ck, cn, m, sh, cpos)) {
           emit_cut<THREADS, CPT>(ck, cn, m, k, [&](int j) { return row[cpos(j)]; }, out_i, out_v,
                                  sh, cpos, Remap{rs.remap, rs.rgroup, rs.rstride, t});
           done = true;
