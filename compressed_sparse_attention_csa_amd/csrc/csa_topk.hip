@@ -262,7 +262,6 @@ struct SelShared {
   uint32_t list[2 * kLCap];
   uint32_t red[4][THREADS / 64];
   int wsum[2 * (THREADS / 64) + 1];
-  uint32_t mm[4];                           // block min / max results
   int bsel[2];
   uint32_t cut[2];                          // key and position of the m-th best
   int sel_count;
@@ -274,10 +273,12 @@ __device__ __forceinline__ uint32_t uniform_u(uint32_t v) {
 }
 
 // Block min / max of one u32 per thread (result uniform in every thread):
-// wave partials go to red[0..1], wave 0 combines them into res[0..1].
+// wave partials go to red[0..1], and after one barrier every thread combines
+// the NW partials itself (same-address LDS reads broadcast).  A later call
+// that writes the same red rows must be separated from this one's reads by a
+// barrier; back-to-back calls use different rows.
 template <int NW>
-__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t (*red)[NW],
-                                             uint32_t* res) {
+__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t (*red)[NW]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   lo = wave_min_u(lo);
@@ -287,17 +288,14 @@ __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_
     red[1][wave] = hi;
   }
   __syncthreads();
-  if (wave == 0) {
-    const uint32_t a = wave_min_u(lane < NW ? red[0][lane] : 0xffffffffu);
-    const uint32_t b = wave_max_u(lane < NW ? red[1][lane] : 0u);
-    if (lane == 0) {
-      res[0] = a;
-      res[1] = b;
-    }
+  uint32_t a = 0xffffffffu, b = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    a = min(a, red[0][w]);
+    b = max(b, red[1][w]);
   }
-  __syncthreads();
-  lo = uniform_u(res[0]);
-  hi = uniform_u(res[1]);
+  lo = uniform_u(a);
+  hi = uniform_u(b);
 }
 
 // Refinement select (the path for a threshold bin too large for the LDS
@@ -330,8 +328,8 @@ __device__ void block_select(const uint32_t (&key)[KPT], int nmine, int m, SelSh
       fmax = max(fmax, fin ? kk : 0u);
     }
     for (int i = tid; i < kSBins + 64; i += THREADS) sh.hist[i] = 0u;
-    block_minmax<NW>(kmin, kmax, sh.red, sh.mm);
-    block_minmax<NW>(fmin, fmax, sh.red + 2, sh.mm + 2);
+    block_minmax<NW>(kmin, kmax, sh.red);
+    block_minmax<NW>(fmin, fmax, sh.red + 2);
     if (kmin == kmax) {
       // every key in play is equal: the rem lowest positions among them
       const int eq = __popc(live);
@@ -382,13 +380,13 @@ __device__ void cut_of_selection(const uint32_t (&key)[KPT], uint32_t chosen, ui
     }
     kmin = min(kmin, ((win >> j) & 1u) ? key[j] : 0xffffffffu);
   }
-  block_minmax<NW>(kmin, dummy, sh.red, sh.mm);
+  block_minmax<NW>(kmin, dummy, sh.red);
   uint32_t pmin = 0xffffffffu, pmax = 0u;
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if (((win >> j) & 1u) && key[j] == kmin) pmax = max(pmax, static_cast<uint32_t>(pos(j)));
   __syncthreads();   // red is reused
-  block_minmax<NW>(pmin, pmax, sh.red + 2, sh.mm + 2);
+  block_minmax<NW>(pmin, pmax, sh.red + 2);
   if (threadIdx.x == 0) {
     sh.cut[0] = kmin;
     sh.cut[1] = pmax;
@@ -418,7 +416,7 @@ __device__ bool find_cut(const uint32_t (&key)[KPT], int nmine, int m, SelShared
     fmax = max(fmax, fin ? key[j] : 0u);
   }
   for (int i = tid; i < kSBins + 64; i += THREADS) sh.hist[i] = 0u;
-  block_minmax<NW>(fmin, fmax, sh.red, sh.mm);
+  block_minmax<NW>(fmin, fmax, sh.red);
   const Binner bn = make_binner(fmin, fmax, kSBins);
   // a key's bin, -1 past nmine
   constexpr bool kHold = HOLD;
