@@ -202,14 +202,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   // in the same round trip as query_start_loc, and the guess is checked
   // against every entry of it.  Otherwise the groups are located by a scan
   // over query_start_loc and the rows' metadata fetched after it.
+  // Groups are taken in reverse launch order: in a causal prefill a later
+  // group sees more pages, so its work-groups are dispatched first and the
+  // short ones fill in behind them instead of trailing them.
+  const int gy = static_cast<int>(gridDim.y) - 1 - static_cast<int>(blockIdx.y);
   int row0 = 0, nrows = 0, b = -1;
   int pos_v = 0, blk_v = -1;
   bool located = false;
   if (B > 0 && B < kThreads && num_tokens % B == 0) {
     const int R = num_tokens / B;
     const int gpr = (R + kRowsPerWG - 1) / kRowsPerWG;   // groups per request
-    const int bg = static_cast<int>(blockIdx.y) / gpr;
-    const int r0 = bg * R + (static_cast<int>(blockIdx.y) % gpr) * kRowsPerWG;
+    const int bg = gy / gpr;
+    const int r0 = bg * R + (gy % gpr) * kRowsPerWG;
     const int nr = bg < B ? min(kRowsPerWG, (bg + 1) * R - r0) : 0;
     const int qv = tid <= B ? min(max(qsl[tid], 0), num_tokens) : 0;
     if (tid < nr) pos_v = positions[r0 + tid];
@@ -232,7 +236,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     }
   }
   if (!located) {
-    b = locate_group(qsl, B, num_tokens, blockIdx.y, &row0, &nrows, scratch);
+    b = locate_group(qsl, B, num_tokens, gy, &row0, &nrows, scratch);
     if (b >= 0) {
       pos_v = tid < nrows ? positions[row0 + tid] : 0;
       blk_v = -1;
@@ -252,7 +256,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
       const int hi = min(max(qsl[bb + 1], 0), num_tokens);
       gfirst += hi > lo ? (hi - lo + kRowsPerWG - 1) / kRowsPerWG : 0;
     }
-    const int u = blockIdx.y - gfirst;  // index among unowned 4-row blocks
+    const int u = gy - gfirst;  // index among unowned 4-row blocks
     const int n_unowned = owned_begin + (num_tokens - owned_end);
     if (u < 0 || u * kRowsPerWG >= n_unowned) return;
     for (int r = 0; r < kRowsPerWG; ++r) {
