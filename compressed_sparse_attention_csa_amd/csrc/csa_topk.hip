@@ -711,7 +711,9 @@ __global__ void __launch_bounds__(THREADS) topk_small_kernel(
   __shared__ SelShared<THREADS> sh;
   __shared__ uint32_t cand_k[kSmallCand];
   __shared__ uint32_t cand_p[kSmallCand];
-  const int t = blockIdx.x;
+  // rows in reverse launch order: a causal prefill's later rows span more
+  // keys, so they are dispatched first and the short rows fill in behind
+  const int t = static_cast<int>(gridDim.x) - 1 - static_cast<int>(blockIdx.x);
   const int tid = threadIdx.x;
   if (t >= num_tokens) return;
   const float* row = scores + static_cast<long long>(t) * stride;
