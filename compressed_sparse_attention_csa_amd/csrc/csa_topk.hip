@@ -31,7 +31,7 @@
 //           1,048,576-position row); for r <= 64 the r-th best 16-lane
 //           maximum bounds it from below and the few samples above that
 //           bound are ranked directly, else the selection core;
-//   filter: work-groups over 8,192-score chunks keep every key >= tau, each
+//   filter: work-groups over 4,096-score chunks keep every key >= tau, each
 //           wave writing its (key, position) pairs in position order into the
 //           workspace slots of its own positions, with its count;
 //   final:  one work-group per row gathers the segments in position order
@@ -55,7 +55,7 @@ namespace {
 constexpr int kMaxK = 4096;
 constexpr int kSmallMax = 32768;     // spans up to this use the one-group kernel
 constexpr int kSBins = 2048;         // selection-core histogram bins
-constexpr int kChunk = 8192;         // scores per work-group in the long-row kernels
+constexpr int kChunk = 4096;         // scores per work-group in the long-row kernels
 constexpr int kLThreads = 256;
 constexpr int kLWaves = kLThreads / 64;
 constexpr int kSub = kChunk / kLWaves;   // contiguous positions per wave
