@@ -320,6 +320,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   v4i qa[MT][KS];
   float ww[MT][16];
   int sa[MT][KS];   // FP4: the E8M0 byte of lane (col, half)'s 32 dims
+  // head weights (and INT8 / FP8 query scales) as 16-byte loads when every
+  // group of four heads is 16-byte aligned
+  const bool vec_w =
+      Hi % 4 == 0 &&
+      ((reinterpret_cast<uintptr_t>(head_w) | (FP4 ? 0u : reinterpret_cast<uintptr_t>(q_scale))) &
+       15u) == 0;
   auto load_query = [&]() {
     if (!active) return;
 #pragma unroll
@@ -339,18 +345,40 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) sa[mt][ks] = (qsw >> (8 * (ks * 2 + half))) & 0xff;
       }
+      // INT8: times 2^21, as the epilogue's ReLU leaves dot * 2^-21 (see the
+      // page loop); FP4: the scales are inside the MFMA.  The loads read a
+      // valid head for every lane (a head past Hi is dropped by the select),
+      // so they issue together instead of one guarded round trip each.
+      constexpr float kWScale = FP8 ? 1.0f : 2097152.0f;
+      if (vec_w) {
+        // results 4q .. 4q + 3 are four consecutive heads: one 16-byte load
+        // per array for each (and with Hi % 4 == 0 a group lies wholly
+        // inside or wholly past Hi)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-        // INT8: times 2^21, as the epilogue's ReLU leaves dot * 2^-21 (see
-        // the page loop); FP4: the scales are inside the MFMA.  The loads
-        // read a valid head for every lane (a head past Hi is dropped by the
-        // select), so they issue together instead of one guarded round trip
-        // each.
-        const long long hc = static_cast<long long>(my_t) * Hi + (hh < Hi ? hh : 0);
-        const float wv = FP4 ? head_w[hc]
-                             : head_w[hc] * q_scale[hc] * (FP8 ? 1.0f : 2097152.0f);
-        ww[mt][j] = (hh < Hi) ? wv : 0.0f;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int hh = mt * 32 + 8 * q4 + 4 * half;
+          const long long hc = static_cast<long long>(my_t) * Hi + (hh < Hi ? hh : 0);
+          const float4 hw = *reinterpret_cast<const float4*>(head_w + hc);
+          float4 wv = hw;
+          if constexpr (!FP4) {
+            const float4 qs = *reinterpret_cast<const float4*>(q_scale + hc);
+            wv = make_float4(hw.x * qs.x * kWScale, hw.y * qs.y * kWScale,
+                             hw.z * qs.z * kWScale, hw.w * qs.w * kWScale);
+          }
+          const bool in = hh < Hi;
+          ww[mt][4 * q4] = in ? wv.x : 0.0f;
+          ww[mt][4 * q4 + 1] = in ? wv.y : 0.0f;
+          ww[mt][4 * q4 + 2] = in ? wv.z : 0.0f;
+          ww[mt][4 * q4 + 3] = in ? wv.w : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+          const long long hc = static_cast<long long>(my_t) * Hi + (hh < Hi ? hh : 0);
+          const float wv = FP4 ? head_w[hc] : head_w[hc] * q_scale[hc] * kWScale;
+          ww[mt][j] = (hh < Hi) ? wv : 0.0f;
+        }
       }
     }
   };
