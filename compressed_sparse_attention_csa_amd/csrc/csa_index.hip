@@ -180,6 +180,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   __shared__ int blk_s[kMaxPPW];
   __shared__ int nvis_s[kRowsPerWG];
   __shared__ int scratch[kThreads / 64 + 2];
+  // folded head weights of the group's rows, [row][head] (w * qs * 2^21 for
+  // INT8, w * qs for FP8, w for FP4): one coalesced load per thread with the
+  // rows' metadata, read back by each wave in its MFMA result order
+  __shared__ __attribute__((aligned(16))) float ww_s[kRowsPerWG * 64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
@@ -208,6 +212,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   const int gy = static_cast<int>(gridDim.y) - 1 - static_cast<int>(blockIdx.y);
   int row0 = 0, nrows = 0, b = -1;
   int pos_v = 0, blk_v = -1;
+  // thread tid's element of ww_s: row tid / 64 of the group, head tid % 64
+  const int w_row = tid >> 6, w_head = tid & 63;
+  float hw_v = 0.0f, qs_v = 0.0f;
+  auto load_w = [&](int r0w, int nrw) {
+    if (w_row < nrw && w_head < Hi) {
+      const long long hc = static_cast<long long>(r0w + w_row) * Hi + w_head;
+      hw_v = head_w[hc];
+      if constexpr (!FP4) qs_v = q_scale[hc];
+    }
+  };
   bool located = false;
   if (B > 0 && B < kThreads && num_tokens % B == 0) {
     const int R = num_tokens / B;
@@ -217,6 +231,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     const int nr = bg < B ? min(kRowsPerWG, (bg + 1) * R - r0) : 0;
     const int qv = tid <= B ? min(max(qsl[tid], 0), num_tokens) : 0;
     if (tid < nr) pos_v = positions[r0 + tid];
+    load_w(r0, nr);
     if (bg < B && tid < npages) {
       const int page = page0 + tid;
       blk_v = (page < max_blocks) ? bt[static_cast<long long>(bg) * max_blocks + page] : -1;
@@ -239,6 +254,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
     b = locate_group(qsl, B, num_tokens, gy, &row0, &nrows, scratch);
     if (b >= 0) {
       pos_v = tid < nrows ? positions[row0 + tid] : 0;
+      hw_v = 0.0f;
+      qs_v = 0.0f;
+      load_w(row0, nrows);
       blk_v = -1;
       if (tid < npages) {
         const int page = page0 + tid;
@@ -320,12 +338,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
   v4i qa[MT][KS];
   float ww[MT][16];
   int sa[MT][KS];   // FP4: the E8M0 byte of lane (col, half)'s 32 dims
-  // head weights (and INT8 / FP8 query scales) as 16-byte loads when every
-  // group of four heads is 16-byte aligned
-  const bool vec_w =
-      Hi % 4 == 0 &&
-      ((reinterpret_cast<uintptr_t>(head_w) | (FP4 ? 0u : reinterpret_cast<uintptr_t>(q_scale))) &
-       15u) == 0;
   auto load_query = [&]() {
     if (!active) return;
 #pragma unroll
@@ -345,44 +357,28 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(k
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) sa[mt][ks] = (qsw >> (8 * (ks * 2 + half))) & 0xff;
       }
-      // INT8: times 2^21, as the epilogue's ReLU leaves dot * 2^-21 (see the
-      // page loop); FP4: the scales are inside the MFMA.  The loads read a
-      // valid head for every lane (a head past Hi is dropped by the select),
-      // so they issue together instead of one guarded round trip each.
-      constexpr float kWScale = FP8 ? 1.0f : 2097152.0f;
-      if (vec_w) {
-        // results 4q .. 4q + 3 are four consecutive heads: one 16-byte load
-        // per array for each (and with Hi % 4 == 0 a group lies wholly
-        // inside or wholly past Hi)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int hh = mt * 32 + 8 * q4 + 4 * half;
-          const long long hc = static_cast<long long>(my_t) * Hi + (hh < Hi ? hh : 0);
-          const float4 hw = *reinterpret_cast<const float4*>(head_w + hc);
-          float4 wv = hw;
-          if constexpr (!FP4) {
-            const float4 qs = *reinterpret_cast<const float4*>(q_scale + hc);
-            wv = make_float4(hw.x * qs.x * kWScale, hw.y * qs.y * kWScale,
-                             hw.z * qs.z * kWScale, hw.w * qs.w * kWScale);
-          }
-          const bool in = hh < Hi;
-          ww[mt][4 * q4] = in ? wv.x : 0.0f;
-          ww[mt][4 * q4 + 1] = in ? wv.y : 0.0f;
-          ww[mt][4 * q4 + 2] = in ? wv.z : 0.0f;
-          ww[mt][4 * q4 + 3] = in ? wv.w : 0.0f;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int hh = mt * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-          const long long hc = static_cast<long long>(my_t) * Hi + (hh < Hi ? hh : 0);
-          const float wv = FP4 ? head_w[hc] : head_w[hc] * q_scale[hc] * kWScale;
-          ww[mt][j] = (hh < Hi) ? wv : 0.0f;
-        }
-      }
     }
   };
-  __syncthreads();  // blk_s ready (no direct-to-LDS load is in flight yet)
+  // INT8: times 2^21, as the epilogue's ReLU leaves dot * 2^-21 (see the page
+  // loop); FP4: the scales are inside the MFMA
+  constexpr float kWScale = FP8 ? 1.0f : 2097152.0f;
+  ww_s[tid] = (w_row < nrows && w_head < Hi) ? (FP4 ? hw_v : hw_v * qs_v * kWScale) : 0.0f;
+  __syncthreads();  // blk_s and ww_s ready (no direct-to-LDS load is in flight yet)
+  // result 4q + i of lane (col, half) in M tile mt is head mt*32 + 8q + 4*half
+  // + i: four consecutive heads, one 16-byte LDS read (heads past Hi are 0)
+  if (active) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 wv =
+            *reinterpret_cast<const float4*>(&ww_s[wave * 64 + mt * 32 + 8 * q4 + 4 * half]);
+        ww[mt][4 * q4] = wv.x;
+        ww[mt][4 * q4 + 1] = wv.y;
+        ww[mt][4 * q4 + 2] = wv.z;
+        ww[mt][4 * q4 + 3] = wv.w;
+      }
+  }
 
   // ---- page pi -> LDS stage pi % kStages with direct-to-LDS loads.  LDS
   //      slot q of a page holds 16-byte chunk (q & 7) ^ ((key >> 1) & 7) of key
